@@ -1,0 +1,316 @@
+/*
+ * sft.h -- C ABI of the sparse-first fine-tuning hot path for AMD MI355X (gfx950).
+ *
+ * The method is the one described on the page "Sparse-First Fine-Tuning:
+ * Full-Weight Training at the Cost of the Active Set" (tensorwirelabs.com).
+ * One training step of a weight matrix W [R x C] (rows = output features):
+ *
+ *   1. masks, once per step, on the host (section 2.1): the conductor for the
+ *      embedding, a row tracker for every projection;            -> sft_conductor_window,
+ *                                                                     sft_tracker_window,
+ *                                                                     sft_plan_rows,
+ *                                                                     sft_plan_embedding,
+ *                                                                     sft_slots_update
+ *   2. the masked weight gradient dW = dY^T X, skipping 32-row tiles with no
+ *      active row (section 2.2);                                  -> sft_masked_dw,
+ *                                                                     sft_embedding_dw
+ *   3. the sparse update of the int8 weight q, per-row scale s and fp32
+ *      residual delta with fp16 Adam moments kept only for active rows
+ *      (sections 2.3 and 2.4; pairs of matrices take the coupled update);
+ *                                                                  -> sft_sparse_update,
+ *                                                                     sft_coupled_update
+ *   4. the sparse write-back of the live bf16 weights (section 2.3).
+ *                                                                  -> sft_masked_writeback
+ *                                                                     (or fused into 3)
+ *
+ * Conventions shared by every call:
+ *   - Status: every entry point returns SFT_OK (0) or a negative SFT_E* code,
+ *     never throws and never aborts.  The message of the last failure on the
+ *     calling thread is returned by sft_last_error().
+ *   - Ownership: the caller owns every buffer.  The library keeps no pointer
+ *     after a call returns and allocates no device memory.
+ *   - Host calls (section "host") run synchronously on plain host arrays.
+ *   - Device calls (section "device") take device pointers, validate host-side
+ *     scalars and pointer alignment, enqueue their kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and return
+ *     without synchronising.  They never copy anything back to the host
+ *     (section 2.6 of the page: nothing is read back in the middle of a step),
+ *     so a fault inside a kernel surfaces at the caller's next synchronisation.
+ *     Inputs must stay alive until the stream work completes.
+ *   - Layouts: row-major and contiguous.  bf16 and fp16 values are passed as
+ *     their 16-bit patterns (uint16_t).  Device base pointers must be 16-byte
+ *     aligned and C must be a multiple of 8 (16-byte vector access).
+ *   - Row lists (active_rows) are strictly ascending and < R.  Row k of a
+ *     compact gradient (dW_act, G) belongs to active_rows[k].
+ *   - Counts (n_active, n_active_tiles, nnz) are host scalars taken from the
+ *     host plan; the GPU never reports a count back.
+ *   - Thread safety: every call is re-entrant; the only per-thread state is
+ *     the last-error message.
+ */
+#ifndef SFT_H
+#define SFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFT_ABI_VERSION 1
+
+enum {
+    SFT_OK = 0,
+    SFT_EINVAL = -1,    /* null pointer, negative size, bad value, unsorted row list */
+    SFT_ESHAPE = -2,    /* inconsistent shapes (e.g. C not a multiple of 8)           */
+    SFT_EALIGN = -3,    /* a device pointer is not 16-byte aligned                     */
+    SFT_ECAPACITY = -4, /* an output or slot table is too small, or workspace too small */
+    SFT_EHIP = -5,      /* the HIP runtime reported an error at launch                 */
+    SFT_ENOTSUP = -6    /* a size beyond what the kernels support                     */
+};
+
+/* Message of the last failed call on this thread ("" if none). Never NULL. */
+const char *sft_last_error(void);
+
+/* SFT_ABI_VERSION of the built library. */
+int sft_abi_version(void);
+
+/* ======================================================================= */
+/* host: masks and plans (CPU, synchronous, plain host arrays)              */
+/* ======================================================================= */
+
+/*
+ * The conductor (section 2.1): one observation window over `rows` embedding
+ * rows.  For every row, hits_r = number of tokens equal to r; with H the
+ * largest hit count, the row's charge becomes ch_r/2 + (hits_r/H)/2 (fp32;
+ * an empty window only halves the charges) and active[r] = (ch_r >= 0.01).
+ *   ch       [rows] fp32, in/out: charges (start at 0)
+ *   tokens   [n_tokens] token ids, each in [0, rows)
+ *   active   [rows] out: 1 = active, 0 = inactive
+ * Errors: SFT_EINVAL for a null pointer, rows < 0, n_tokens < 0 or a token
+ * out of range (checked before anything is written).
+ */
+int sft_conductor_window(float *ch, int64_t rows, const int32_t *tokens, int64_t n_tokens,
+                         uint8_t *active);
+
+/*
+ * The row tracker (section 2.1): the same recurrence as the conductor with the
+ * rows' output magnitudes from the forward pass in place of hit counts.
+ *   magnitude [rows] fp32, each >= 0 and finite
+ * Errors: SFT_EINVAL for a null pointer, rows < 0, or a negative/NaN magnitude.
+ */
+int sft_tracker_window(float *ch, int64_t rows, const float *magnitude, uint8_t *active);
+
+/*
+ * Row plan of one mask (section 2.2: the mask is checked per tile of 32 rows).
+ * Caller-allocated arrays; the call fills the counts.
+ *   tile_bits    [ceil(rows/32)]  bit i of word j = mask of row 32*j+i (bits >= rows are 0)
+ *   active_rows  [rows]           ascending active rows (first n_active valid)
+ *   active_tiles [ceil(rows/32)]  ascending tiles with an active row (first n_active_tiles valid)
+ */
+typedef struct sft_plan {
+    int64_t rows;           /* in  */
+    int64_t n_active;       /* out */
+    int64_t n_active_tiles; /* out */
+    uint32_t *tile_bits;
+    int32_t *active_rows;
+    int32_t *active_tiles;
+} sft_plan;
+
+/* Errors: SFT_EINVAL for null pointers or rows < 0 or rows >= 2^31. */
+int sft_plan_rows(const uint8_t *active, sft_plan *plan);
+
+/*
+ * Token positions of the active embedding rows, as CSR: the positions t with
+ * tokens[t] == plan->active_rows[k] are positions[row_ptr[k] .. row_ptr[k+1]),
+ * ascending.  row_ptr has n_active + 1 entries; positions has capacity
+ * `positions_cap` (n_tokens always suffices); *nnz receives the total.
+ * Errors: SFT_EINVAL (null / token out of range), SFT_ECAPACITY (positions_cap).
+ */
+int sft_plan_embedding(const sft_plan *plan, const int32_t *tokens, int64_t n_tokens,
+                       int32_t *row_ptr, int32_t *positions, int64_t positions_cap,
+                       int64_t *nnz);
+
+/*
+ * Moment slots (section 2.3: m and v exist only for active rows).  row_slot
+ * [rows] is the persistent map row -> slot (-1 = none; start all -1).  Rows no
+ * longer active free their slot; rows still active keep theirs; a newly active
+ * row takes the lowest free slot and is flagged fresh (its moments and step
+ * count start from zero; the update kernels then ignore the stored values).
+ *   slot  [n_active] out, fresh [n_active] out (1 = fresh)
+ * Errors: SFT_EINVAL (null, unsorted rows), SFT_ECAPACITY (n_active > n_slots;
+ * checked before anything is written).
+ */
+int sft_slots_update(int32_t *row_slot, int64_t rows, int64_t n_slots,
+                     const int32_t *active_rows, int64_t n_active, int32_t *slot,
+                     uint8_t *fresh);
+
+/*
+ * Adam bias corrections (section 2.4, "a standard Adam step with bias
+ * correction"): bc1[t] = fl32(1 - beta1^t), bc2[t] = fl32(1 - beta2^t) for
+ * t = 1..t_max, computed in fp64 and rounded once; bc1[0] = bc2[0] = 0.
+ * The arrays hold t_max + 1 floats.  The update kernels read entry
+ * min(t, t_max); choose t_max so that the entries have reached 1.0f (about
+ * 17,000 for beta2 = 0.999) or the step count never exceeds it.
+ * Errors: SFT_EINVAL (null, t_max < 1, beta outside [0, 1)).
+ */
+int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *bc2);
+
+/* ======================================================================= */
+/* device: the masked backward pass (section 2.2)                           */
+/* ======================================================================= */
+
+/*
+ * One matrix of a masked-dW group.  dY is bf16 [T x R] (gradient at the
+ * matrix's output); the plan arrays are device copies of an sft_plan of this
+ * matrix's mask; dW_act is fp32 [n_active x C], row k = active_rows[k].
+ */
+typedef struct sft_dw_mat {
+    const uint16_t *dY;
+    int64_t R;
+    const uint32_t *tile_bits;   /* device [ceil(R/32)] */
+    const int32_t *active_rows;  /* device [n_active]  */
+    const int32_t *active_tiles; /* device [n_active_tiles] */
+    int64_t n_active;            /* host scalar */
+    int64_t n_active_tiles;      /* host scalar */
+    float *dW_act;               /* device [n_active x C] */
+} sft_dw_mat;
+
+/* Matrices that read the same layer input X (bf16 [T x C]), e.g. q/k/v. */
+typedef struct sft_dw_group {
+    const uint16_t *X;
+    int64_t T, C;
+    int32_t n_mats;
+    const sft_dw_mat *mats; /* host array of n_mats */
+} sft_dw_group;
+
+/*
+ * Workspace bytes sft_masked_dw needs for these groups (0 is possible).
+ * Returns (size_t)-1 and sets the error message on invalid groups.
+ */
+size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
+
+/*
+ * dW_act[k, c] = sum_t dY[t, r_k] * X[t, c] for every active row r_k of every
+ * matrix (bf16 inputs, fp32 accumulation on the matrix cores, fp32 output).
+ * Each 32-row tile with no active row is skipped before any load of dY or X;
+ * inside an active tile only the active rows are written (section 2.2).
+ * Matrices of one group share every load of X.
+ *   ws / ws_bytes  device workspace of at least sft_masked_dw_workspace()
+ *                  bytes.  It must be zero-filled before its first use; every
+ *                  call leaves it zero-filled again (it holds split-K
+ *                  partial sums and arrival counters).  Calls that share a
+ *                  workspace must be ordered on one stream.
+ * Limits: T >= 1, T < 2^31, C % 8 == 0, R < 2^31.  Results are deterministic
+ * (a fixed summation order for every launch configuration the same inputs
+ * produce).
+ * Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_ECAPACITY (ws too small),
+ * SFT_EHIP.
+ */
+int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/*
+ * The embedding's masked weight gradient (section 2.2: the same product with
+ * a one-hot input): dW_act[k, c] = sum over positions t of row k of dY[t, c],
+ * with the CSR from sft_plan_embedding (device copies).  Summed in fp64 and
+ * rounded to fp32 once.
+ *   dY [T x d] bf16, row_ptr [n_active+1], positions [nnz], dW_act [n_active x d] fp32
+ * Limits: d % 8 == 0.  Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_EHIP.
+ */
+int sft_embedding_dw(const uint16_t *dY, int64_t T, int64_t d, const int32_t *row_ptr,
+                     const int32_t *positions, int64_t n_active, float *dW_act, void *stream);
+
+/* ======================================================================= */
+/* device: the sparse update and write-back (sections 2.3 and 2.4)          */
+/* ======================================================================= */
+
+/* Adam hyper-parameters; bc1/bc2 are device copies of sft_bias_table(). */
+typedef struct sft_adam {
+    float lr, beta1, beta2, eps;
+    float weight_decay; /* decoupled (AdamW order: decay, then step); 0 = none */
+    const float *bc1;   /* device [t_max + 1] */
+    const float *bc2;   /* device [t_max + 1] */
+    int32_t t_max;
+} sft_adam;
+
+/*
+ * One matrix's optimizer state and the gradient of its active rows.
+ *   q      int8 [R x C], s fp32 [R], delta fp32 [R x C]: w = s*q + delta
+ *   m, v   fp16 [n_slots x C], t int32 [n_slots]: moments and step count per slot
+ *   G      fp32 [n_active x C] (row k = active_rows[k]), e.g. dW_act
+ *   slot   [n_active] slot of each active row; fresh [n_active] or NULL
+ *   w_live bf16 [R x C] live weights, or NULL for no fused write-back
+ */
+typedef struct sft_upd_mat {
+    int64_t R, C, n_active, n_slots;
+    const int32_t *active_rows;
+    const int32_t *slot;
+    const uint8_t *fresh;
+    const float *G;
+    int8_t *q;
+    float *s;
+    float *delta;
+    uint16_t *m;
+    uint16_t *v;
+    int32_t *t;
+    uint16_t *w_live;
+} sft_upd_mat;
+
+/*
+ * Plain sparse update of every active row of n_mats matrices, in one launch
+ * (section 2.3; section 2.4's plain Adam step for unpaired matrices).  Per
+ * active row: rebuild w = fl(fl(s*q) + delta) in registers, take the Adam step
+ * (fp32 moments from the stored fp16 ones, new moments stored as fp16 rounded
+ * to nearest even, bias correction from the table, step lr*mhat/(sqrt(vhat)+eps),
+ * decoupled weight decay first when weight_decay != 0), then requantise the
+ * row: s' = max|w'|/127, q' = clamp(rint(w'/s'), -127, 127),
+ * delta' = w' - s'*q' (exact, so s'*q' + delta' rebuilds w'); a row with
+ * s' = 0 stores q' = 0, delta' = w'.  With w_live set, the row's live weights
+ * are rewritten as bf16(w') in the same pass.  Rows not listed are neither
+ * read nor written.  Arithmetic is IEEE fp32 with no contraction.
+ * Limits: C % 8 == 0, C <= 65536.
+ * Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_ENOTSUP, SFT_EHIP.
+ */
+int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *hp, void *stream);
+
+/*
+ * A coupled pair (section 2.4: gate-up, query-output, key-value).  a and b
+ * have equal R and C.  Over the union of the two row lists, the effective
+ * gradients are
+ *   gA~ = a_own * (clipA * gA) + a_cross * (clipB * gB)
+ *   gB~ = a_own * (clipB * gB) + a_cross * (clipA * gA)
+ * (fp32, each product and the sum rounded), where a matrix whose row is not in
+ * its list contributes a zero gradient; then each matrix whose row is listed
+ * takes the plain update above with its effective gradient.  The blend
+ * weights a_own/a_cross come from the caller's phase schedule; clip points to
+ * a device float[2] {clipA, clipB}, or is NULL for {1, 1}.
+ */
+typedef struct sft_pair {
+    sft_upd_mat a, b;
+    float a_own, a_cross;
+    const float *clip;
+} sft_pair;
+
+/*
+ * All pairs in one launch.  hp->weight_decay is the effective decay (the page
+ * scales it by cos(alpha) of the pitch angle; the caller applies that factor).
+ * Errors: as sft_sparse_update.
+ */
+int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *hp, void *stream);
+
+/*
+ * The sparse write-back (section 2.3): w_live[r, c] = bf16(fl(fl(s[r]*q[r,c]) +
+ * delta[r,c])) for the listed rows only; every other row is left untouched.
+ *   q int8 [R x C], s fp32 [R], delta fp32 [R x C], w_live bf16 [R x C]
+ * Limits: C % 8 == 0.  Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_EHIP.
+ */
+int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, int64_t R,
+                         int64_t C, const int32_t *active_rows, int64_t n_active,
+                         uint16_t *w_live, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFT_H */

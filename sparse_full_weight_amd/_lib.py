@@ -1,0 +1,373 @@
+"""ctypes binding of ``libsft.so`` (the C ABI declared in ``include/sft.h``).
+
+Argument marshalling only: host calls take numpy arrays, device calls take
+torch tensors that live on the GPU and enqueue on torch's current stream.
+Every step of the computation runs in the library; there is no Python or CPU
+fallback -- if the library is missing the import of this module's ``lib()``
+fails loudly.
+
+Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
+Active Set" (sections 2.1-2.4); each function's C declaration states the
+passage it implements.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsft.so")
+
+SFT_OK, SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_ECAPACITY, SFT_EHIP, SFT_ENOTSUP = 0, -1, -2, -3, -4, -5, -6
+_CODES = {SFT_EINVAL: "EINVAL", SFT_ESHAPE: "ESHAPE", SFT_EALIGN: "EALIGN", SFT_ECAPACITY: "ECAPACITY",
+          SFT_EHIP: "EHIP", SFT_ENOTSUP: "ENOTSUP"}
+
+# Every symbol include/sft.h declares (checked by the test-suite).
+EXPORTS = (
+    "sft_last_error", "sft_abi_version", "sft_conductor_window", "sft_tracker_window", "sft_plan_rows",
+    "sft_plan_embedding", "sft_slots_update", "sft_bias_table", "sft_masked_dw_workspace", "sft_masked_dw",
+    "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback",
+)
+
+
+class SftError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+# ------------------------------------------------------------------ C structs
+class CPlan(C.Structure):
+    _fields_ = [("rows", C.c_int64), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
+                ("tile_bits", C.c_void_p), ("active_rows", C.c_void_p), ("active_tiles", C.c_void_p)]
+
+
+class CDwMat(C.Structure):
+    _fields_ = [("dY", C.c_void_p), ("R", C.c_int64), ("tile_bits", C.c_void_p), ("active_rows", C.c_void_p),
+                ("active_tiles", C.c_void_p), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
+                ("dW_act", C.c_void_p)]
+
+
+class CDwGroup(C.Structure):
+    _fields_ = [("X", C.c_void_p), ("T", C.c_int64), ("C", C.c_int64), ("n_mats", C.c_int32),
+                ("mats", C.POINTER(CDwMat))]
+
+
+class CAdam(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float), ("bc1", C.c_void_p), ("bc2", C.c_void_p), ("t_max", C.c_int32)]
+
+
+class CUpdMat(C.Structure):
+    _fields_ = [("R", C.c_int64), ("C", C.c_int64), ("n_active", C.c_int64), ("n_slots", C.c_int64),
+                ("active_rows", C.c_void_p), ("slot", C.c_void_p), ("fresh", C.c_void_p), ("G", C.c_void_p),
+                ("q", C.c_void_p), ("s", C.c_void_p), ("delta", C.c_void_p), ("m", C.c_void_p),
+                ("v", C.c_void_p), ("t", C.c_void_p), ("w_live", C.c_void_p)]
+
+
+class CPair(C.Structure):
+    _fields_ = [("a", CUpdMat), ("b", CUpdMat), ("a_own", C.c_float), ("a_cross", C.c_float),
+                ("clip", C.c_void_p)]
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """Load the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -c \"import __graft_entry__ as g; "
+                              f"g.build()\"` (hipcc, gfx950)")
+        L = C.CDLL(LIB_PATH)
+        p, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int32, C.c_float
+        L.sft_last_error.restype = C.c_char_p
+        L.sft_last_error.argtypes = []
+        L.sft_abi_version.restype = C.c_int
+        L.sft_conductor_window.argtypes = [p, i64, p, i64, p]
+        L.sft_tracker_window.argtypes = [p, i64, p, p]
+        L.sft_plan_rows.argtypes = [p, C.POINTER(CPlan)]
+        L.sft_plan_embedding.argtypes = [C.POINTER(CPlan), p, i64, p, p, i64, C.POINTER(C.c_int64)]
+        L.sft_slots_update.argtypes = [p, i64, i64, p, i64, p, p]
+        L.sft_bias_table.argtypes = [f32, f32, i32, p, p]
+        L.sft_masked_dw_workspace.argtypes = [C.POINTER(CDwGroup), i32]
+        L.sft_masked_dw_workspace.restype = C.c_size_t
+        L.sft_masked_dw.argtypes = [C.POINTER(CDwGroup), i32, p, C.c_size_t, p]
+        L.sft_embedding_dw.argtypes = [p, i64, i64, p, p, i64, p, p]
+        L.sft_sparse_update.argtypes = [C.POINTER(CUpdMat), i32, C.POINTER(CAdam), p]
+        L.sft_coupled_update.argtypes = [C.POINTER(CPair), i32, C.POINTER(CAdam), p]
+        L.sft_masked_writeback.argtypes = [p, p, p, i64, i64, p, i64, p, p]
+        for n in EXPORTS[2:]:
+            if n != "sft_masked_dw_workspace":
+                getattr(L, n).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != SFT_OK:
+        raise SftError(rc, lib().sft_last_error().decode())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "host arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _dev(t, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError("device argument must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ------------------------------------------------------------------ host calls
+def sft_abi_version() -> int:
+    return lib().sft_abi_version()
+
+
+def sft_conductor_window(ch: np.ndarray, tokens: np.ndarray) -> np.ndarray:
+    """Section 2.1 conductor: updates ``ch`` (fp32) in place, returns the u8 mask."""
+    assert ch.dtype == np.float32
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    active = np.zeros(ch.size, np.uint8)
+    _check(lib().sft_conductor_window(_np_ptr(ch), ch.size, _np_ptr(tokens), tokens.size, _np_ptr(active)))
+    return active
+
+
+def sft_tracker_window(ch: np.ndarray, magnitude: np.ndarray) -> np.ndarray:
+    """Section 2.1 row tracker over output magnitudes."""
+    assert ch.dtype == np.float32
+    magnitude = np.ascontiguousarray(magnitude, np.float32)
+    active = np.zeros(ch.size, np.uint8)
+    _check(lib().sft_tracker_window(_np_ptr(ch), ch.size, _np_ptr(magnitude), _np_ptr(active)))
+    return active
+
+
+@dataclass
+class Plan:
+    """Host row plan of one mask (tile bitmap, active rows, active tiles)."""
+    rows: int
+    tile_bits: np.ndarray
+    active_rows: np.ndarray
+    active_tiles: np.ndarray
+
+    @property
+    def n_active(self) -> int:
+        return int(self.active_rows.size)
+
+    @property
+    def n_active_tiles(self) -> int:
+        return int(self.active_tiles.size)
+
+    def to_device(self, device="cuda") -> "DevicePlan":
+        import torch
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device, non_blocking=False)
+        return DevicePlan(self, up(self.tile_bits), up(self.active_rows), up(self.active_tiles))
+
+
+@dataclass
+class DevicePlan:
+    host: Plan
+    tile_bits: "object"
+    active_rows: "object"
+    active_tiles: "object"
+
+    @property
+    def rows(self) -> int:
+        return self.host.rows
+
+    @property
+    def n_active(self) -> int:
+        return self.host.n_active
+
+    @property
+    def n_active_tiles(self) -> int:
+        return self.host.n_active_tiles
+
+
+def sft_plan_rows(mask: np.ndarray) -> Plan:
+    mask = np.ascontiguousarray(mask, np.uint8)
+    rows = mask.size
+    tiles = (rows + 31) // 32
+    bits = np.zeros(max(tiles, 1), np.uint32)
+    act = np.zeros(max(rows, 1), np.int32)
+    at = np.zeros(max(tiles, 1), np.int32)
+    cp = CPlan(rows, 0, 0, _np_ptr(bits), _np_ptr(act), _np_ptr(at))
+    _check(lib().sft_plan_rows(_np_ptr(mask), C.byref(cp)))
+    return Plan(rows, bits[:tiles].copy(), act[:cp.n_active].copy(), at[:cp.n_active_tiles].copy())
+
+
+def sft_plan_embedding(plan: Plan, tokens: np.ndarray):
+    """CSR (row_ptr, positions) of the active embedding rows' token positions."""
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    cp = CPlan(plan.rows, plan.n_active, plan.n_active_tiles, _np_ptr(plan.tile_bits),
+               _np_ptr(plan.active_rows), _np_ptr(plan.active_tiles))
+    row_ptr = np.zeros(plan.n_active + 1, np.int32)
+    pos = np.zeros(max(tokens.size, 1), np.int32)
+    nnz = C.c_int64()
+    _check(lib().sft_plan_embedding(C.byref(cp), _np_ptr(tokens), tokens.size, _np_ptr(row_ptr), _np_ptr(pos),
+                                    pos.size, C.byref(nnz)))
+    return row_ptr, pos[:nnz.value].copy()
+
+
+def sft_slots_update(row_slot: np.ndarray, n_slots: int, active_rows: np.ndarray):
+    assert row_slot.dtype == np.int32 and row_slot.flags["C_CONTIGUOUS"]
+    active_rows = np.ascontiguousarray(active_rows, np.int32)
+    slot = np.zeros(max(active_rows.size, 1), np.int32)
+    fresh = np.zeros(max(active_rows.size, 1), np.uint8)
+    _check(lib().sft_slots_update(_np_ptr(row_slot), row_slot.size, n_slots, _np_ptr(active_rows),
+                                  active_rows.size, _np_ptr(slot), _np_ptr(fresh)))
+    return slot[:active_rows.size].copy(), fresh[:active_rows.size].copy()
+
+
+def sft_bias_table(beta1: float, beta2: float, t_max: int):
+    bc1 = np.zeros(t_max + 1, np.float32)
+    bc2 = np.zeros(t_max + 1, np.float32)
+    _check(lib().sft_bias_table(beta1, beta2, t_max, _np_ptr(bc1), _np_ptr(bc2)))
+    return bc1, bc2
+
+
+# ------------------------------------------------------------------ device calls
+@dataclass
+class DwMat:
+    dY: "object"            # bf16 [T x R] GPU tensor
+    plan: DevicePlan
+    dW_act: "object"        # fp32 [n_active x C]
+
+
+@dataclass
+class DwGroup:
+    X: "object"             # bf16 [T x C] GPU tensor
+    mats: Sequence[DwMat]
+
+
+def _c_groups(groups: Sequence[DwGroup]):
+    import torch
+    keep = []
+    arr = (CDwGroup * max(len(groups), 1))()
+    for i, g in enumerate(groups):
+        T, Cc = g.X.shape
+        mats = (CDwMat * max(len(g.mats), 1))()
+        for j, m in enumerate(g.mats):
+            mats[j] = CDwMat(_dev(m.dY, torch.bfloat16), m.plan.rows, _dev(m.plan.tile_bits),
+                             _dev(m.plan.active_rows), _dev(m.plan.active_tiles), m.plan.n_active,
+                             m.plan.n_active_tiles, _dev(m.dW_act, torch.float32))
+        keep.append(mats)
+        arr[i] = CDwGroup(_dev(g.X, torch.bfloat16), T, Cc, len(g.mats), mats)
+    return arr, keep
+
+
+def sft_masked_dw_workspace(groups: Sequence[DwGroup]) -> int:
+    arr, keep = _c_groups(groups)
+    n = lib().sft_masked_dw_workspace(arr, len(groups))
+    if n == C.c_size_t(-1).value:
+        raise SftError(SFT_EINVAL, lib().sft_last_error().decode())
+    return n
+
+
+def sft_masked_dw(groups: Sequence[DwGroup], ws=None, stream=None) -> None:
+    """Section 2.2 masked dW for every matrix of every group (async on the stream)."""
+    arr, keep = _c_groups(groups)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sft_masked_dw(arr, len(groups), _dev(ws), nbytes, _stream(stream)))
+
+
+def sft_embedding_dw(dY, row_ptr, positions, n_active: int, dW_act, stream=None) -> None:
+    import torch
+    T, d = dY.shape
+    _check(lib().sft_embedding_dw(_dev(dY, torch.bfloat16), T, d, _dev(row_ptr, torch.int32),
+                                  _dev(positions, torch.int32), n_active, _dev(dW_act, torch.float32),
+                                  _stream(stream)))
+
+
+@dataclass
+class Adam:
+    lr: float
+    beta1: float
+    beta2: float
+    eps: float
+    bc1: "object"           # fp32 GPU tensor [t_max + 1]
+    bc2: "object"
+    weight_decay: float = 0.0
+
+    def c(self) -> CAdam:
+        return CAdam(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, _dev(self.bc1),
+                     _dev(self.bc2), self.bc1.numel() - 1)
+
+
+@dataclass
+class UpdMat:
+    """One matrix's GPU state plus the gradient of its active rows."""
+    q: "object"             # int8 [R x C]
+    s: "object"             # fp32 [R]
+    delta: "object"         # fp32 [R x C]
+    m: "object"             # fp16 bits (int16/uint16 tensor) [n_slots x C]
+    v: "object"
+    t: "object"             # int32 [n_slots]
+    active_rows: "object"   # int32 [n_active] (GPU)
+    slot: "object"          # int32 [n_active] (GPU)
+    G: "object"             # fp32 [n_active x C]
+    n_active: int
+    fresh: "object" = None  # uint8 [n_active] (GPU) or None
+    w_live: "object" = None  # bf16 [R x C] or None
+
+    def c(self) -> CUpdMat:
+        R, Cc = self.q.shape
+        return CUpdMat(R, Cc, self.n_active, self.m.shape[0], _dev(self.active_rows), _dev(self.slot),
+                       _dev(self.fresh), _dev(self.G), _dev(self.q), _dev(self.s), _dev(self.delta),
+                       _dev(self.m), _dev(self.v), _dev(self.t), _dev(self.w_live))
+
+
+def sft_sparse_update(mats: Sequence[UpdMat], hp: Adam, stream=None) -> None:
+    """Sections 2.3-2.4 plain sparse update (+ fused write-back where w_live is set)."""
+    arr = (CUpdMat * max(len(mats), 1))(*[m.c() for m in mats])
+    h = hp.c()
+    _check(lib().sft_sparse_update(arr, len(mats), C.byref(h), _stream(stream)))
+
+
+@dataclass
+class Pair:
+    a: UpdMat
+    b: UpdMat
+    a_own: float
+    a_cross: float
+    clip: "object" = None   # fp32 GPU tensor [2] or None
+
+
+def sft_coupled_update(pairs: Sequence[Pair], hp: Adam, stream=None) -> None:
+    """Section 2.4 coupled update of matrix pairs."""
+    arr = (CPair * max(len(pairs), 1))(*[CPair(p.a.c(), p.b.c(), p.a_own, p.a_cross, _dev(p.clip))
+                                         for p in pairs])
+    h = hp.c()
+    _check(lib().sft_coupled_update(arr, len(pairs), C.byref(h), _stream(stream)))
+
+
+def sft_masked_writeback(q, s, delta, active_rows, n_active: int, w_live, stream=None) -> None:
+    """Section 2.3 sparse write-back of the live bf16 weights."""
+    import torch
+    R, Cc = q.shape
+    _check(lib().sft_masked_writeback(_dev(q, torch.int8), _dev(s, torch.float32), _dev(delta, torch.float32),
+                                      R, Cc, _dev(active_rows, torch.int32), n_active, _dev(w_live),
+                                      _stream(stream)))

@@ -1,0 +1,221 @@
+// sft_host.cpp -- host side of the sparse-first step: the error channel, the
+// conductor and row tracker, row plans, embedding CSR, moment slots and the
+// Adam bias-correction table.
+//
+// Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
+// Active Set", section 2.1 (the conductor keeps one charge per row, halves it
+// at the end of every observation window and adds half of the row's share of
+// the window's hits; a row is active while its charge is at least 0.01; the
+// row tracker does the same with output magnitudes; the masks are computed
+// once a step on the CPU) and section 2.2 (the mask is checked per tile of 32
+// rows).  These run on the CPU by design: the page keeps mask decisions on the
+// host, one step ahead of the GPU.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "sft_internal.h"
+
+namespace sft {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+// Charge recurrence over `rows` given each row's window weight (hit count or
+// magnitude) and the window's largest weight.  fp32 throughout: the halving
+// and the half share are exact, the sum rounds once.
+void charge_update(float *ch, int64_t rows, const float *weight, float wmax, uint8_t *active) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float share = wmax > 0.0f ? weight[r] / wmax : 0.0f;
+        const float next = 0.5f * ch[r] + 0.5f * share;
+        ch[r] = next;
+        active[r] = next >= 0.01f;
+    }
+}
+
+}  // namespace
+}  // namespace sft
+
+using namespace sft;
+
+extern "C" {
+
+const char *sft_last_error(void) { return g_last_error.c_str(); }
+
+int sft_abi_version(void) { return SFT_ABI_VERSION; }
+
+int sft_conductor_window(float *ch, int64_t rows, const int32_t *tokens, int64_t n_tokens,
+                         uint8_t *active) {
+    clear_error();
+    SFT_CHECK(rows >= 0 && n_tokens >= 0, SFT_EINVAL, "conductor: negative size");
+    SFT_CHECK(rows == 0 || (ch && active), SFT_EINVAL, "conductor: null charge/mask array");
+    SFT_CHECK(n_tokens == 0 || tokens, SFT_EINVAL, "conductor: null tokens");
+    // Hit counts are exact in fp32 up to 2^24 tokens per window.
+    SFT_CHECK(n_tokens <= (int64_t(1) << 24), SFT_ENOTSUP, "conductor: window over 2^24 tokens");
+    std::vector<float> hits(static_cast<size_t>(rows), 0.0f);
+    for (int64_t i = 0; i < n_tokens; ++i) {
+        const int32_t tok = tokens[i];
+        SFT_CHECK(tok >= 0 && tok < rows, SFT_EINVAL, "conductor: token %d at %lld out of [0, %lld)",
+                  tok, (long long)i, (long long)rows);
+    }
+    for (int64_t i = 0; i < n_tokens; ++i) hits[tokens[i]] += 1.0f;
+    float busiest = 0.0f;
+    for (float h : hits) busiest = std::max(busiest, h);
+    charge_update(ch, rows, hits.data(), busiest, active);
+    return SFT_OK;
+}
+
+int sft_tracker_window(float *ch, int64_t rows, const float *magnitude, uint8_t *active) {
+    clear_error();
+    SFT_CHECK(rows >= 0, SFT_EINVAL, "tracker: negative size");
+    SFT_CHECK(rows == 0 || (ch && magnitude && active), SFT_EINVAL, "tracker: null array");
+    float wmax = 0.0f;
+    for (int64_t r = 0; r < rows; ++r) {
+        SFT_CHECK(magnitude[r] >= 0.0f && std::isfinite(magnitude[r]), SFT_EINVAL,
+                  "tracker: magnitude[%lld] is negative or not finite", (long long)r);
+        wmax = std::max(wmax, magnitude[r]);
+    }
+    charge_update(ch, rows, magnitude, wmax, active);
+    return SFT_OK;
+}
+
+int sft_plan_rows(const uint8_t *active, sft_plan *plan) {
+    clear_error();
+    SFT_CHECK(plan, SFT_EINVAL, "plan_rows: null plan");
+    const int64_t rows = plan->rows;
+    SFT_CHECK(rows >= 0 && rows < (int64_t(1) << 31), SFT_EINVAL, "plan_rows: rows out of range");
+    SFT_CHECK(rows == 0 || (active && plan->tile_bits && plan->active_rows && plan->active_tiles),
+              SFT_EINVAL, "plan_rows: null array");
+    const int64_t tiles = (rows + 31) / 32;
+    int64_t na = 0, nt = 0;
+    for (int64_t j = 0; j < tiles; ++j) {
+        const int64_t lo = 32 * j;
+        const int64_t hi = std::min<int64_t>(lo + 32, rows);
+        uint32_t word = 0;
+        for (int64_t r = lo; r < hi; ++r) {
+            if (active[r]) {
+                word |= 1u << (r - lo);
+                plan->active_rows[na++] = static_cast<int32_t>(r);
+            }
+        }
+        plan->tile_bits[j] = word;
+        if (word) plan->active_tiles[nt++] = static_cast<int32_t>(j);
+    }
+    plan->n_active = na;
+    plan->n_active_tiles = nt;
+    return SFT_OK;
+}
+
+int sft_plan_embedding(const sft_plan *plan, const int32_t *tokens, int64_t n_tokens,
+                       int32_t *row_ptr, int32_t *positions, int64_t positions_cap, int64_t *nnz) {
+    clear_error();
+    SFT_CHECK(plan && row_ptr && nnz, SFT_EINVAL, "plan_embedding: null argument");
+    SFT_CHECK(n_tokens >= 0 && n_tokens < (int64_t(1) << 31), SFT_EINVAL,
+              "plan_embedding: n_tokens out of range");
+    SFT_CHECK(n_tokens == 0 || tokens, SFT_EINVAL, "plan_embedding: null tokens");
+    const int64_t rows = plan->rows, na = plan->n_active;
+    SFT_CHECK(na == 0 || plan->active_rows, SFT_EINVAL, "plan_embedding: null active_rows");
+    // Row -> position in the active list (-1 = inactive), then a counting sort
+    // of the token positions by row; a stable pass keeps positions ascending.
+    std::vector<int32_t> index(static_cast<size_t>(rows), -1);
+    for (int64_t k = 0; k < na; ++k) index[plan->active_rows[k]] = static_cast<int32_t>(k);
+    std::vector<int64_t> count(static_cast<size_t>(na) + 1, 0);
+    for (int64_t t = 0; t < n_tokens; ++t) {
+        const int32_t tok = tokens[t];
+        SFT_CHECK(tok >= 0 && tok < rows, SFT_EINVAL, "plan_embedding: token %d out of range", tok);
+        if (index[tok] >= 0) ++count[index[tok] + 1];
+    }
+    for (int64_t k = 0; k < na; ++k) count[k + 1] += count[k];
+    SFT_CHECK(count[na] <= positions_cap, SFT_ECAPACITY,
+              "plan_embedding: %lld positions exceed capacity %lld", (long long)count[na],
+              (long long)positions_cap);
+    SFT_CHECK(count[na] == 0 || positions, SFT_EINVAL, "plan_embedding: null positions");
+    for (int64_t k = 0; k <= na; ++k) row_ptr[k] = static_cast<int32_t>(count[k]);
+    std::vector<int64_t> fill(count.begin(), count.end() - 1);
+    for (int64_t t = 0; t < n_tokens; ++t) {
+        const int32_t k = index[tokens[t]];
+        if (k >= 0) positions[fill[k]++] = static_cast<int32_t>(t);
+    }
+    *nnz = count[na];
+    return SFT_OK;
+}
+
+int sft_slots_update(int32_t *row_slot, int64_t rows, int64_t n_slots, const int32_t *active_rows,
+                     int64_t n_active, int32_t *slot, uint8_t *fresh) {
+    clear_error();
+    SFT_CHECK(rows >= 0 && n_slots >= 0 && n_active >= 0, SFT_EINVAL, "slots: negative size");
+    SFT_CHECK(rows == 0 || row_slot, SFT_EINVAL, "slots: null row_slot");
+    SFT_CHECK(n_active == 0 || (active_rows && slot && fresh), SFT_EINVAL, "slots: null array");
+    SFT_CHECK(n_active <= n_slots, SFT_ECAPACITY, "slots: %lld active rows exceed %lld slots",
+              (long long)n_active, (long long)n_slots);
+    for (int64_t k = 0; k < n_active; ++k) {
+        SFT_CHECK(active_rows[k] >= 0 && active_rows[k] < rows, SFT_EINVAL,
+                  "slots: active row %d out of range", active_rows[k]);
+        SFT_CHECK(k == 0 || active_rows[k] > active_rows[k - 1], SFT_EINVAL,
+                  "slots: active rows not strictly ascending at %lld", (long long)k);
+    }
+    for (int64_t r = 0; r < rows; ++r)
+        SFT_CHECK(row_slot[r] >= -1 && row_slot[r] < n_slots, SFT_EINVAL,
+                  "slots: row_slot[%lld] = %d out of range", (long long)r, row_slot[r]);
+    // Walk rows and the sorted active list together: rows that left the set
+    // free their slot; survivors mark theirs as taken.
+    std::vector<uint8_t> taken(static_cast<size_t>(n_slots), 0);
+    int64_t k = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const bool on = k < n_active && active_rows[k] == r;
+        if (on) ++k;
+        if (!on) row_slot[r] = -1;
+        else if (row_slot[r] >= 0) taken[row_slot[r]] = 1;
+    }
+    int64_t next_free = 0;
+    for (int64_t i = 0; i < n_active; ++i) {
+        const int32_t r = active_rows[i];
+        if (row_slot[r] >= 0) {
+            slot[i] = row_slot[r];
+            fresh[i] = 0;
+            continue;
+        }
+        while (taken[next_free]) ++next_free;  // lowest free slot (ascending scan)
+        taken[next_free] = 1;
+        row_slot[r] = static_cast<int32_t>(next_free);
+        slot[i] = static_cast<int32_t>(next_free);
+        fresh[i] = 1;
+    }
+    return SFT_OK;
+}
+
+int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *bc2) {
+    clear_error();
+    SFT_CHECK(bc1 && bc2, SFT_EINVAL, "bias_table: null array");
+    SFT_CHECK(t_max >= 1, SFT_EINVAL, "bias_table: t_max < 1");
+    SFT_CHECK(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f, SFT_EINVAL,
+              "bias_table: beta outside [0, 1)");
+    bc1[0] = 0.0f;
+    bc2[0] = 0.0f;
+    // Powers by repeated fp64 multiplication would drift from pow(); use pow()
+    // on the fp32 betas widened to double, then round once.
+    for (int32_t t = 1; t <= t_max; ++t) {
+        bc1[t] = static_cast<float>(1.0 - std::pow(static_cast<double>(beta1), t));
+        bc2[t] = static_cast<float>(1.0 - std::pow(static_cast<double>(beta2), t));
+    }
+    return SFT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,502 @@
+// sft_update.hip -- the sparse int8 + residual Adam update, the coupled pair
+// update and the masked write-back, for gfx950.
+//
+// Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
+// Active Set", section 2.3 (each weight is an int8 value q with a per-row
+// scale s and an fp32 residual delta; the update kernel rebuilds the fp32
+// weight in registers only, applies the update and writes back a new q and
+// delta; the fp16 moments exist only for active rows; inactive rows return at
+// once; the same mask drives the write-back of the live weights) and section
+// 2.4 (pairs of matrices blend their clipped gradients; every effective
+// gradient drives a standard Adam step with bias correction; unpaired
+// matrices take the plain step).
+//
+// Kernel shape: one workgroup per active row, all matrices of a call in one
+// launch.  A row is streamed once: each lane owns 4-column chunks
+// (16-byte loads of gradient and residual, 4 bytes of q, 8 bytes of each
+// moment), keeps the new weights in registers, reduces the row's |w'| maximum
+// across the wavefront (cross-lane shuffles) and across wavefronts (LDS),
+// then requantises and stores.  The work is bound by HBM bandwidth: per
+// active element it reads 13 bytes and writes 11 (with the fused write-back).
+//
+// Arithmetic is IEEE fp32 without contraction: every product and sum below
+// rounds on its own, divisions and square roots are correctly rounded (the
+// compiler's default for HIP), fp32->fp16 and fp32->bf16 conversions round to
+// nearest even, denormals are kept.
+#pragma clang fp contract(off)
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "sft_internal.h"
+
+namespace {
+
+constexpr int kMaxMats = 16;
+
+struct UpdMatDev {
+    const int32_t *rows;
+    const int32_t *slot;
+    const uint8_t *fresh;
+    const float *G;
+    int8_t *q;
+    float *s;
+    float *delta;
+    uint16_t *m;
+    uint16_t *v;
+    int32_t *t;
+    uint16_t *w_live;
+    int64_t C;
+    int64_t n_active;
+    int64_t row_begin;  // first workgroup of this matrix
+};
+
+struct AdamDev {
+    float lr, beta1, beta2, eps, wd;
+    float c1, c2, decay;  // 1-beta1, 1-beta2, 1-lr*wd (host fp32)
+    const float *bc1;
+    const float *bc2;
+    int32_t t_max;
+};
+
+struct UpdParams {
+    UpdMatDev mat[kMaxMats];
+    int32_t n_mats;
+    AdamDev hp;
+};
+
+// Coupled pair: the partner's gradient is looked up by row.
+struct PairDev {
+    UpdMatDev self;        // the matrix this workgroup updates
+    const int32_t *prow;   // partner's active rows
+    const float *pG;       // partner's gradient rows
+    int64_t pn;            // partner's n_active
+    float a_own, a_cross;
+    const float *clip;     // {clip_self_first? see below} device [2] or null
+    int32_t self_is_b;     // 0: self is `a` of the pair, 1: self is `b`
+};
+
+struct PairParams {
+    PairDev side[kMaxMats];
+    int32_t n_sides;
+    AdamDev hp;
+};
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint16_t f2h(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Largest value over the workgroup (non-negative floats), via the integer
+// order of their bit patterns: wave64 shuffles, then one LDS word per wave.
+template <int kThreads>
+__device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
+    uint32_t u = __float_as_uint(x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) u = max(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64)));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wave] = __uint_as_float(u);
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, lds[w]);
+    return r;
+}
+
+// Update one active row (index k of matrix M) whose effective gradient for a
+// 4-column chunk at column c is produced by grad(c, float4&).
+template <int kThreads, int kChunks, typename GradFn>
+__device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const AdamDev &hp,
+                                           GradFn grad) {
+    __shared__ float red[kThreads / 64];
+    const int64_t C = M.C;
+    const int64_t r = M.rows[k];
+    const int64_t sl = M.slot[k];
+    const bool fresh = M.fresh ? M.fresh[k] != 0 : false;
+    const int32_t step = (fresh ? 0 : M.t[sl]) + 1;
+    const int32_t ti = min(step, hp.t_max);
+    const float bc1 = hp.bc1[ti];
+    const float bc2 = hp.bc2[ti];
+    const float s_old = M.s[r];
+    const int8_t *qrow = M.q + r * C;
+    const float *drow = M.delta + r * C;
+    uint16_t *mrow = M.m + sl * C;
+    uint16_t *vrow = M.v + sl * C;
+
+    float wn[kChunks][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+        const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+        if (c < C) {
+            float g[4];
+            grad(c, g);
+            const char4 qv = *reinterpret_cast<const char4 *>(qrow + c);
+            const float4 dv = *reinterpret_cast<const float4 *>(drow + c);
+            ushort4 mv = make_ushort4(0, 0, 0, 0), vv = make_ushort4(0, 0, 0, 0);
+            if (!fresh) {
+                mv = *reinterpret_cast<const ushort4 *>(mrow + c);
+                vv = *reinterpret_cast<const ushort4 *>(vrow + c);
+            }
+            const float qf[4] = {static_cast<float>(qv.x), static_cast<float>(qv.y),
+                                 static_cast<float>(qv.z), static_cast<float>(qv.w)};
+            const float df[4] = {dv.x, dv.y, dv.z, dv.w};
+            const uint16_t mh[4] = {mv.x, mv.y, mv.z, mv.w};
+            const uint16_t vh[4] = {vv.x, vv.y, vv.z, vv.w};
+            uint16_t mo[4], vo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sq = s_old * qf[e];
+                const float w = sq + df[e];
+                const float m_a = hp.beta1 * h2f(mh[e]);
+                const float m_b = hp.c1 * g[e];
+                const float m = m_a + m_b;
+                const float gg = g[e] * g[e];
+                const float v_a = hp.beta2 * h2f(vh[e]);
+                const float v_b = hp.c2 * gg;
+                const float v = v_a + v_b;
+                mo[e] = f2h(m);
+                vo[e] = f2h(v);
+                const float mhat = m / bc1;
+                const float vhat = v / bc2;
+                const float denom = __builtin_sqrtf(vhat) + hp.eps;
+                const float ratio = mhat / denom;
+                const float u = hp.lr * ratio;
+                const float w1 = hp.wd != 0.0f ? w * hp.decay : w;
+                const float wnew = w1 - u;
+                wn[j][e] = wnew;
+                amax = fmaxf(amax, fabsf(wnew));
+            }
+            *reinterpret_cast<ushort4 *>(mrow + c) = make_ushort4(mo[0], mo[1], mo[2], mo[3]);
+            *reinterpret_cast<ushort4 *>(vrow + c) = make_ushort4(vo[0], vo[1], vo[2], vo[3]);
+        }
+    }
+    amax = block_max_nonneg<kThreads>(amax, red);
+    const float s_new = amax / 127.0f;
+    if (threadIdx.x == 0) {
+        M.s[r] = s_new;
+        M.t[sl] = step;
+    }
+    int8_t *qout = M.q + r * C;
+    float *dout = M.delta + r * C;
+    uint16_t *wl = M.w_live ? M.w_live + r * C : nullptr;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+        const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+        if (c < C) {
+            float qf[4], d[4];
+            uint16_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float qq = 0.0f;
+                if (s_new != 0.0f) {
+                    qq = __builtin_rintf(wn[j][e] / s_new);
+                    qq = fminf(fmaxf(qq, -127.0f), 127.0f);
+                }
+                const float sq = s_new * qq;
+                d[e] = wn[j][e] - sq;
+                qf[e] = qq;
+                const float back = sq + d[e];
+                b[e] = f2bf(back);
+            }
+            *reinterpret_cast<char4 *>(qout + c) =
+                make_char4(static_cast<signed char>(qf[0]), static_cast<signed char>(qf[1]),
+                           static_cast<signed char>(qf[2]), static_cast<signed char>(qf[3]));
+            *reinterpret_cast<float4 *>(dout + c) = make_float4(d[0], d[1], d[2], d[3]);
+            if (wl) *reinterpret_cast<ushort4 *>(wl + c) = make_ushort4(b[0], b[1], b[2], b[3]);
+        }
+    }
+}
+
+template <int kThreads, int kChunks>
+__global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
+    const int64_t wg = blockIdx.x;
+    int mi = 0;
+    while (mi + 1 < p.n_mats && wg >= p.mat[mi + 1].row_begin) ++mi;
+    const UpdMatDev &M = p.mat[mi];
+    const int64_t k = wg - M.row_begin;
+    const float *grow = M.G + k * M.C;
+    update_row<kThreads, kChunks>(M, k, p.hp, [&](int64_t c, float *g) {
+        const float4 gv = *reinterpret_cast<const float4 *>(grow + c);
+        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+    });
+}
+
+// Index of `row` in an ascending list, or -1.
+__device__ __forceinline__ int64_t find_row(const int32_t *rows, int64_t n, int64_t row) {
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (rows[mid] < row) lo = mid + 1;
+        else hi = mid;
+    }
+    return (lo < n && rows[lo] == row) ? lo : -1;
+}
+
+template <int kThreads, int kChunks>
+__global__ __launch_bounds__(kThreads) void k_coupled_update(const PairParams p) {
+    const int64_t wg = blockIdx.x;
+    int si = 0;
+    while (si + 1 < p.n_sides && wg >= p.side[si + 1].self.row_begin) ++si;
+    const PairDev &S = p.side[si];
+    const UpdMatDev &M = S.self;
+    const int64_t k = wg - M.row_begin;
+    const int64_t r = M.rows[k];
+    const int64_t pk = find_row(S.prow, S.pn, r);
+    const float clip_a = S.clip ? S.clip[0] : 1.0f;
+    const float clip_b = S.clip ? S.clip[1] : 1.0f;
+    const float c_self = S.self_is_b ? clip_b : clip_a;
+    const float c_part = S.self_is_b ? clip_a : clip_b;
+    const float *gs = M.G + k * M.C;
+    const float *gp = pk >= 0 ? S.pG + pk * M.C : nullptr;
+    const float a_own = S.a_own, a_cross = S.a_cross;
+    update_row<kThreads, kChunks>(M, k, p.hp, [&](int64_t c, float *g) {
+        const float4 sv = *reinterpret_cast<const float4 *>(gs + c);
+        float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gp) pv = *reinterpret_cast<const float4 *>(gp + c);
+        const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
+        const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float cs = c_self * sa[e];
+            const float cp = c_part * pa[e];
+            const float own = a_own * cs;
+            const float cross = a_cross * cp;
+            g[e] = own + cross;
+        }
+    });
+}
+
+__global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restrict__ q,
+                                                          const float *__restrict__ s,
+                                                          const float *__restrict__ delta, int64_t C,
+                                                          const int32_t *__restrict__ rows,
+                                                          uint16_t *__restrict__ w_live) {
+    const int64_t r = rows[blockIdx.x];
+    const float sr = s[r];
+    const int8_t *qr = q + r * C;
+    const float *dr = delta + r * C;
+    uint16_t *wr = w_live + r * C;
+    for (int64_t c = 8 * static_cast<int64_t>(threadIdx.x); c < C; c += 8 * 256) {
+        const int2 qv = *reinterpret_cast<const int2 *>(qr + c);
+        const float4 d0 = *reinterpret_cast<const float4 *>(dr + c);
+        const float4 d1 = *reinterpret_cast<const float4 *>(dr + c + 4);
+        const int8_t *qb = reinterpret_cast<const int8_t *>(&qv);
+        const float df[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        uint16_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sq = sr * static_cast<float>(qb[e]);
+            const float w = sq + df[e];
+            o[e] = f2bf(w);
+        }
+        uint4 pack;
+        pack.x = o[0] | (static_cast<uint32_t>(o[1]) << 16);
+        pack.y = o[2] | (static_cast<uint32_t>(o[3]) << 16);
+        pack.z = o[4] | (static_cast<uint32_t>(o[5]) << 16);
+        pack.w = o[6] | (static_cast<uint32_t>(o[7]) << 16);
+        *reinterpret_cast<uint4 *>(wr + c) = pack;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+int check_mat(const sft_upd_mat &m, const char *who) {
+    SFT_CHECK(m.R >= 0 && m.C > 0 && m.n_active >= 0 && m.n_slots >= 0, SFT_EINVAL,
+              "%s: bad sizes (R=%lld C=%lld n_active=%lld)", who, (long long)m.R, (long long)m.C,
+              (long long)m.n_active);
+    SFT_CHECK(m.C % 8 == 0, SFT_ESHAPE, "%s: C=%lld is not a multiple of 8", who, (long long)m.C);
+    SFT_CHECK(m.C <= 65536, SFT_ENOTSUP, "%s: C=%lld above 65536", who, (long long)m.C);
+    SFT_CHECK(m.n_active <= m.R && m.n_active <= m.n_slots, SFT_ECAPACITY,
+              "%s: n_active=%lld exceeds R or n_slots", who, (long long)m.n_active);
+    if (m.n_active == 0) return SFT_OK;
+    SFT_CHECK(m.active_rows && m.slot && m.G && m.q && m.s && m.delta && m.m && m.v && m.t,
+              SFT_EINVAL, "%s: null device pointer", who);
+    SFT_CHECK(sft::aligned16(m.G) && sft::aligned16(m.q) && sft::aligned16(m.delta) &&
+                  sft::aligned16(m.m) && sft::aligned16(m.v) &&
+                  (!m.w_live || sft::aligned16(m.w_live)),
+              SFT_EALIGN, "%s: a row-major device buffer is not 16-byte aligned", who);
+    return SFT_OK;
+}
+
+int check_hp(const sft_adam *hp, const char *who) {
+    SFT_CHECK(hp && hp->bc1 && hp->bc2 && hp->t_max >= 1, SFT_EINVAL,
+              "%s: missing Adam parameters or bias table", who);
+    return SFT_OK;
+}
+
+AdamDev make_adam(const sft_adam &hp) {
+    AdamDev a;
+    a.lr = hp.lr;
+    a.beta1 = hp.beta1;
+    a.beta2 = hp.beta2;
+    a.eps = hp.eps;
+    a.wd = hp.weight_decay;
+    a.c1 = 1.0f - hp.beta1;
+    a.c2 = 1.0f - hp.beta2;
+    const float lrwd = hp.lr * hp.weight_decay;
+    a.decay = 1.0f - lrwd;
+    a.bc1 = hp.bc1;
+    a.bc2 = hp.bc2;
+    a.t_max = hp.t_max;
+    return a;
+}
+
+UpdMatDev make_mat(const sft_upd_mat &m, int64_t row_begin) {
+    UpdMatDev d;
+    d.rows = m.active_rows;
+    d.slot = m.slot;
+    d.fresh = m.fresh;
+    d.G = m.G;
+    d.q = m.q;
+    d.s = m.s;
+    d.delta = m.delta;
+    d.m = m.m;
+    d.v = m.v;
+    d.t = m.t;
+    d.w_live = m.w_live;
+    d.C = m.C;
+    d.n_active = m.n_active;
+    d.row_begin = row_begin;
+    return d;
+}
+
+// Chunks of 4 columns per lane: the smallest instantiated count covering C.
+template <typename Params, template <int, int> class Launch>
+int dispatch(int64_t maxC, int64_t n_wg, const Params &p, hipStream_t stream) {
+    if (maxC <= 256 * 4 * 4) return Launch<256, 4>::go(n_wg, p, stream);
+    if (maxC <= 256 * 4 * 8) return Launch<256, 8>::go(n_wg, p, stream);
+    if (maxC <= 256 * 4 * 12) return Launch<256, 12>::go(n_wg, p, stream);
+    if (maxC <= 256 * 4 * 16) return Launch<256, 16>::go(n_wg, p, stream);
+    if (maxC <= 1024 * 4 * 8) return Launch<1024, 8>::go(n_wg, p, stream);
+    return Launch<1024, 16>::go(n_wg, p, stream);
+}
+
+int launch_status(const char *who) {
+    const hipError_t e = hipGetLastError();
+    SFT_CHECK(e == hipSuccess, SFT_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+    return SFT_OK;
+}
+
+template <int T, int N>
+struct LaunchUpd {
+    static int go(int64_t n_wg, const UpdParams &p, hipStream_t s) {
+        hipLaunchKernelGGL((k_sparse_update<T, N>), dim3(static_cast<uint32_t>(n_wg)), dim3(T), 0, s, p);
+        return launch_status("sft_sparse_update");
+    }
+};
+
+template <int T, int N>
+struct LaunchPair {
+    static int go(int64_t n_wg, const PairParams &p, hipStream_t s) {
+        hipLaunchKernelGGL((k_coupled_update<T, N>), dim3(static_cast<uint32_t>(n_wg)), dim3(T), 0, s, p);
+        return launch_status("sft_coupled_update");
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *hp, void *stream) {
+    sft::clear_error();
+    SFT_CHECK(n_mats >= 0 && (n_mats == 0 || mats), SFT_EINVAL, "sft_sparse_update: bad matrix list");
+    if (int rc = check_hp(hp, "sft_sparse_update")) return rc;
+    for (int32_t i = 0; i < n_mats; ++i)
+        if (int rc = check_mat(mats[i], "sft_sparse_update")) return rc;
+    const AdamDev a = make_adam(*hp);
+    // Matrices go out in batches of kMaxMats per launch (kernel-argument table).
+    for (int32_t base = 0; base < n_mats; base += kMaxMats) {
+        UpdParams p{};
+        p.hp = a;
+        int64_t n_wg = 0, maxC = 0;
+        int32_t n = 0;
+        for (int32_t i = base; i < std::min(n_mats, base + kMaxMats); ++i) {
+            if (mats[i].n_active == 0) continue;
+            p.mat[n++] = make_mat(mats[i], n_wg);
+            n_wg += mats[i].n_active;
+            maxC = std::max<int64_t>(maxC, mats[i].C);
+        }
+        p.n_mats = n;
+        if (n_wg == 0) continue;
+        SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_sparse_update: too many rows");
+        if (int rc = dispatch<UpdParams, LaunchUpd>(maxC, n_wg, p, static_cast<hipStream_t>(stream)))
+            return rc;
+    }
+    return SFT_OK;
+}
+
+int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *hp, void *stream) {
+    sft::clear_error();
+    SFT_CHECK(n_pairs >= 0 && (n_pairs == 0 || pairs), SFT_EINVAL, "sft_coupled_update: bad pair list");
+    if (int rc = check_hp(hp, "sft_coupled_update")) return rc;
+    for (int32_t i = 0; i < n_pairs; ++i) {
+        const sft_pair &pr = pairs[i];
+        if (int rc = check_mat(pr.a, "sft_coupled_update")) return rc;
+        if (int rc = check_mat(pr.b, "sft_coupled_update")) return rc;
+        SFT_CHECK(pr.a.R == pr.b.R && pr.a.C == pr.b.C, SFT_ESHAPE,
+                  "sft_coupled_update: pair %d has unequal shapes", i);
+    }
+    const AdamDev a = make_adam(*hp);
+    // Each side of each pair is a list of workgroups (one per active row of that
+    // side); kMaxMats sides per launch.
+    PairParams p{};
+    p.hp = a;
+    int64_t n_wg = 0, maxC = 0;
+    auto flush = [&]() -> int {
+        if (n_wg == 0) return SFT_OK;
+        SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_coupled_update: too many rows");
+        const int rc = dispatch<PairParams, LaunchPair>(maxC, n_wg, p, static_cast<hipStream_t>(stream));
+        p = PairParams{};
+        p.hp = a;
+        n_wg = 0;
+        maxC = 0;
+        return rc;
+    };
+    for (int32_t i = 0; i < n_pairs; ++i) {
+        const sft_pair &pr = pairs[i];
+        for (int side = 0; side < 2; ++side) {
+            const sft_upd_mat &self = side ? pr.b : pr.a;
+            const sft_upd_mat &partner = side ? pr.a : pr.b;
+            if (self.n_active == 0) continue;
+            if (p.n_sides == kMaxMats)
+                if (int rc = flush()) return rc;
+            PairDev &d = p.side[p.n_sides++];
+            d.self = make_mat(self, n_wg);
+            d.prow = partner.active_rows;
+            d.pG = partner.G;
+            d.pn = partner.n_active;
+            d.a_own = pr.a_own;
+            d.a_cross = pr.a_cross;
+            d.clip = pr.clip;
+            d.self_is_b = side;
+            n_wg += self.n_active;
+            maxC = std::max<int64_t>(maxC, self.C);
+        }
+    }
+    return flush();
+}
+
+int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, int64_t R, int64_t C,
+                         const int32_t *active_rows, int64_t n_active, uint16_t *w_live, void *stream) {
+    sft::clear_error();
+    SFT_CHECK(R >= 0 && C > 0 && n_active >= 0 && n_active <= R, SFT_EINVAL,
+              "sft_masked_writeback: bad sizes");
+    SFT_CHECK(C % 8 == 0, SFT_ESHAPE, "sft_masked_writeback: C=%lld is not a multiple of 8", (long long)C);
+    if (n_active == 0) return SFT_OK;
+    SFT_CHECK(q && s && delta && active_rows && w_live, SFT_EINVAL, "sft_masked_writeback: null pointer");
+    SFT_CHECK(sft::aligned16(q) && sft::aligned16(delta) && sft::aligned16(w_live), SFT_EALIGN,
+              "sft_masked_writeback: buffer not 16-byte aligned");
+    SFT_CHECK(n_active < (int64_t(1) << 31), SFT_ENOTSUP, "sft_masked_writeback: too many rows");
+    hipLaunchKernelGGL(k_masked_writeback, dim3(static_cast<uint32_t>(n_active)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), q, s, delta, C, active_rows, w_live);
+    return launch_status("sft_masked_writeback");
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+"""GPU parity of the masked weight gradient and the embedding gradient.
+
+The HIP path (sft_masked_dw, sft_embedding_dw) and the oracle get the same
+seeded bf16 inputs; dW rows of active rows must agree within the stated
+tolerance (fp32 accumulation against an fp64 sum rounded once), exactly where
+the arithmetic is exact (one token, small integers), and no byte outside the
+active rows may be written.  Method: "Sparse-First Fine-Tuning: Full-Weight
+Training at the Cost of the Active Set", section 2.2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_full_weight_amd import _lib, synth
+from tests.gpu_helpers import bf16_dev, dev, dw_close
+
+pytestmark = pytest.mark.gpu
+
+CANARY = float("nan")
+
+
+def _run(groups_np, repeat=1):
+    """groups_np: list of (X_bits [T x C], [(dY_bits [T x R], mask [R]), ...])."""
+    groups, outs, plans = [], [], []
+    for X, mats in groups_np:
+        C = X.shape[1]
+        ms = []
+        for dY, mask in mats:
+            plan = _lib.sft_plan_rows(mask)
+            buf = torch.full((plan.n_active + 3, C), CANARY, dtype=torch.float32, device="cuda")
+            ms.append(_lib.DwMat(bf16_dev(dY), plan.to_device(), buf[:plan.n_active]))
+            outs.append(buf)
+            plans.append(plan)
+        groups.append(_lib.DwGroup(bf16_dev(X), ms))
+    nbytes = _lib.sft_masked_dw_workspace(groups)
+    ws = torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device="cuda") if nbytes else None
+    results = []
+    for _ in range(repeat):
+        _lib.sft_masked_dw(groups, ws)
+        torch.cuda.synchronize()
+        results.append([b.cpu().numpy() for b in outs])
+    for res in results:
+        for b, plan in zip(res, plans):
+            assert np.all(np.isnan(b[plan.n_active:])), "write past the last active row"
+    return results[-1] if repeat == 1 else results, plans
+
+
+def _check(groups_np, exact=False, repeat=1):
+    res, plans = _run(groups_np, repeat)
+    if repeat > 1:
+        for r in res[1:]:
+            for a, b in zip(res[0], r):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "not deterministic"
+        res = res[0]
+    i = 0
+    for X, mats in groups_np:
+        for dY, mask in mats:
+            want = oracle.masked_dw(dY, X, np.nonzero(mask)[0].astype(np.int32))
+            got = res[i][:plans[i].n_active]
+            if exact:
+                assert np.array_equal(got, want)
+            else:
+                dw_close(got, want)
+            i += 1
+
+
+def _mask_rows(R, rows):
+    return synth.mask_from_rows(R, np.asarray(rows, np.int64))
+
+
+def test_dw_small_projection_10pct_clustered(gpu_lib):
+    # 512 x 512 projection, 256 tokens, 10% of rows active in clustered tiles
+    T, R, C = 256, 512, 512
+    X = synth.normal_bf16((T, C), 1.0, 1001)
+    dY = synth.normal_bf16((T, R), 0.01, 1002)
+    mask = _mask_rows(R, synth.clustered_rows(R, round(0.10 * R), 1501))
+    _check([(X, [(dY, mask)])], repeat=2)
+
+
+def test_dw_ragged_everything(gpu_lib):
+    # R % 32 != 0 and R % 8 != 0 (unaligned dY rows), C not a multiple of 128,
+    # T not a multiple of the token chunk; last row active
+    T, R, C = 100, 70, 200
+    X = synth.normal_bf16((T, C), 1.0, 1011)
+    dY = synth.normal_bf16((T, R), 0.01, 1012)
+    mask = _mask_rows(R, [0, 5, 31, 32, 40, 63, 64, 69])
+    _check([(X, [(dY, mask)])])
+
+
+def test_dw_single_token_is_exact_outer_product(gpu_lib):
+    T, R, C = 1, 96, 136
+    X = synth.normal_bf16((T, C), 1.0, 1021)
+    dY = synth.normal_bf16((T, R), 0.01, 1022)
+    mask = _mask_rows(R, [1, 2, 33, 95])
+    _check([(X, [(dY, mask)])], exact=True)
+
+
+def test_dw_integer_inputs_exact_under_split(gpu_lib):
+    # small integers: every partial sum is exact, so any order or split agrees
+    T, R, C = 2048, 64, 128
+    X = synth.integer_bf16((T, C), -3, 3, 1031)
+    dY = synth.integer_bf16((T, R), -3, 3, 1032)
+    mask = _mask_rows(R, list(range(0, 64, 3)))
+    _check([(X, [(dY, mask)])], exact=True, repeat=2)
+
+
+def test_dw_empty_full_and_one_per_tile(gpu_lib):
+    T, R, C = 128, 256, 64
+    X = synth.normal_bf16((T, C), 1.0, 1041)
+    dY = synth.normal_bf16((T, R), 0.01, 1042)
+    empty = np.zeros(R, np.uint8)
+    full = np.ones(R, np.uint8)
+    one = _mask_rows(R, synth.one_per_tile_rows(R, 1543))
+    _check([(X, [(dY, empty), (dY, full), (dY, one)])])
+
+
+def test_dw_groups_share_x_and_span_mblocks(gpu_lib):
+    # three matrices on one input with 11 active tiles (two M-blocks), plus a
+    # second group with its own input
+    T, C = 192, 264
+    X1 = synth.normal_bf16((T, C), 1.0, 1051)
+    X2 = synth.normal_bf16((T, 96), 1.0, 1052)
+    mats1 = []
+    for i, (R, k) in enumerate([(320, 100), (128, 40), (96, 10)]):
+        mats1.append((synth.normal_bf16((T, R), 0.01, 1060 + i), _mask_rows(R, synth.clustered_rows(R, k, 1560 + i))))
+    mats2 = [(synth.normal_bf16((T, 200), 0.01, 1070), _mask_rows(200, synth.clustered_rows(200, 20, 1570)))]
+    _check([(X1, mats1), (X2, mats2)])
+
+
+def test_dw_long_token_axis_split(gpu_lib):
+    # few tiles and many tokens: the launch splits the token axis many ways
+    T, R, C = 4096, 128, 128
+    X = synth.normal_bf16((T, C), 1.0, 1081)
+    dY = synth.normal_bf16((T, R), 0.01, 1082)
+    mask = _mask_rows(R, synth.clustered_rows(R, 70, 1581))
+    _check([(X, [(dY, mask)])], repeat=3)
+
+
+def test_dw_rejects_bad_shapes(gpu_lib):
+    T, R, C = 16, 32, 12
+    X = bf16_dev(synth.normal_bf16((T, C), 1.0, 1))
+    plan = _lib.sft_plan_rows(np.ones(R, np.uint8))
+    out = torch.zeros((R, C), dtype=torch.float32, device="cuda")
+    g = [_lib.DwGroup(X, [_lib.DwMat(bf16_dev(synth.normal_bf16((T, R), 0.01, 2)), plan.to_device(), out)])]
+    with pytest.raises(_lib.SftError) as e:
+        _lib.sft_masked_dw(g, None)
+    assert e.value.code == _lib.SFT_ESHAPE
+
+
+# ------------------------------------------------------------------ embedding
+
+
+def _emb_case(V, T, d, seed, integer=False):
+    toks_windows = [synth.zipf_tokens(T, V, 1.1, seed + w) for w in range(4)]
+    ch = np.zeros(V, np.float32)
+    for w in toks_windows:
+        mask = _lib.sft_conductor_window(ch, w)
+    tokens = toks_windows[-1]
+    plan = _lib.sft_plan_rows(mask)
+    row_ptr, pos = _lib.sft_plan_embedding(plan, tokens)
+    dY = synth.integer_bf16((T, d), -3, 3, seed + 9) if integer else synth.normal_bf16((T, d), 0.01, seed + 9)
+    return tokens, plan, row_ptr, pos, dY
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_embedding_dw(gpu_lib, integer):
+    V, T, d = 2000, 1024, 264
+    tokens, plan, row_ptr, pos, dY = _emb_case(V, T, d, 1100, integer)
+    assert plan.n_active > 0
+    out = torch.full((plan.n_active + 2, d), CANARY, dtype=torch.float32, device="cuda")
+    _lib.sft_embedding_dw(bf16_dev(dY), dev(row_ptr), dev(pos if pos.size else np.zeros(1, np.int32)),
+                          plan.n_active, out[:plan.n_active])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[plan.n_active:]))
+    want = oracle.embedding_dw(dY, tokens, plan.active_rows)
+    if integer:
+        assert np.array_equal(got[:plan.n_active], want)
+    else:
+        dw_close(got[:plan.n_active], want)

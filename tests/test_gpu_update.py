@@ -1,0 +1,157 @@
+"""GPU parity of the sparse update, the coupled update and the write-back.
+
+The HIP kernels and the oracle receive the same state and the same gradient
+rows; every stored result (q, s, delta, fp16 m and v, step counts, live bf16
+weights) must match bit for bit, and rows outside the list must keep their
+canary bytes.  Method: "Sparse-First Fine-Tuning: Full-Weight Training at the
+Cost of the Active Set", sections 2.3 (int8 + residual state, fp16 moments
+for active rows, sparse write-back) and 2.4 (Adam with bias correction,
+coupled pairs).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_full_weight_amd import _lib, synth
+from tests.gpu_helpers import GpuMat, adam_dev, assert_state_equal, dev, make_state
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+
+
+def _case(R, C, n_rows, n_slots, seed, mid_run, fresh_frac=0.0, gstd=0.16):
+    g = synth.rng(seed)
+    st = make_state(R, C, seed, n_slots, mid_run)
+    rows = np.sort(g.choice(R, size=n_rows, replace=False)).astype(np.int32)
+    slot = g.choice(n_slots, size=n_rows, replace=False).astype(np.int32)
+    fresh = (g.random(n_rows) < fresh_frac).astype(np.uint8) if fresh_frac else None
+    G = synth.gradient_rows(n_rows, C, gstd, seed + 7)
+    return st, rows, slot, fresh, G
+
+
+@pytest.mark.parametrize("mid_run", [False, True])
+def test_sparse_update_bit_exact_many_shapes(gpu_lib, mid_run):
+    # one launch over matrices of several widths: exercises every chunk count
+    shapes = [(512, 512, 51), (40, 8, 5), (33, 24, 33), (300, 4096, 7), (64, 11008, 3), (50, 6000, 4)]
+    cases = [_case(R, C, n, n + 3, 100 + i, mid_run, fresh_frac=0.3 if mid_run else 0.0)
+             for i, (R, C, n) in enumerate(shapes)]
+    gm = [GpuMat(st, G, rows, slot, fresh) for st, rows, slot, fresh, G in cases]
+    hp = adam_dev(**HP)
+    _lib.sft_sparse_update([m.upd() for m in gm], hp)
+    torch.cuda.synchronize()
+    for i, ((st, rows, slot, fresh, G), m) in enumerate(zip(cases, gm)):
+        want = st.copy()
+        oracle.sparse_update(want, G, rows, slot, fresh, **HP)
+        assert_state_equal(m.to_state(), want, f"shape {shapes[i]}")
+
+
+@pytest.mark.parametrize("C", [20000, 40000])
+def test_sparse_update_wide_rows(gpu_lib, C):
+    st, rows, slot, fresh, G = _case(6, C, 3, 3, 200 + C, True)
+    m = GpuMat(st, G, rows, slot, fresh)
+    _lib.sft_sparse_update([m.upd()], adam_dev(**HP))
+    torch.cuda.synchronize()
+    want = st.copy()
+    oracle.sparse_update(want, G, rows, slot, fresh, **HP)
+    assert_state_equal(m.to_state(), want, f"C={C}")
+
+
+def test_sparse_update_weight_decay_and_no_writeback(gpu_lib):
+    st, rows, slot, fresh, G = _case(96, 256, 20, 24, 300, True)
+    wd = float(np.float32(0.01 * math.cos(math.radians(28.4))))
+    m = GpuMat(st, G, rows, slot, fresh, with_live=False)
+    empty = GpuMat(make_state(32, 64, 301, 2, False), np.zeros((0, 64), np.float32), np.zeros(0, np.int32),
+                   np.zeros(0, np.int32), None)
+    _lib.sft_sparse_update([empty.upd(), m.upd()], adam_dev(weight_decay=wd, **HP))
+    torch.cuda.synchronize()
+    want = st.copy()
+    want.w_live = None
+    oracle.sparse_update(want, G, rows, slot, fresh, weight_decay=wd, **HP)
+    got = m.to_state()
+    assert_state_equal(got, want, "wd")
+
+
+def test_sparse_update_second_step_and_large_lr(gpu_lib):
+    # Two consecutive steps (t goes 1 -> 2) with a step size that moves rows far.
+    st, rows, slot, fresh, G = _case(128, 128, 16, 16, 400, False)
+    hp = dict(HP, lr=0.05)
+    m = GpuMat(st, G, rows, slot, fresh)
+    want = st.copy()
+    for step in range(2):
+        Gs = synth.gradient_rows(rows.size, 128, 0.5, 410 + step)
+        m.G.copy_(dev(Gs))
+        _lib.sft_sparse_update([m.upd()], adam_dev(**hp))
+        oracle.sparse_update(want, Gs, rows, slot, fresh, **hp)
+    torch.cuda.synchronize()
+    assert_state_equal(m.to_state(), want, "two steps")
+
+
+def test_sparse_update_zero_row(gpu_lib):
+    st, rows, slot, fresh, G = _case(32, 64, 2, 2, 500, False)
+    st.q[rows[0]] = 0
+    st.delta[rows[0]] = 0
+    G[0] = 0
+    m = GpuMat(st, G, rows, slot, fresh)
+    _lib.sft_sparse_update([m.upd()], adam_dev(**HP))
+    torch.cuda.synchronize()
+    want = st.copy()
+    oracle.sparse_update(want, G, rows, slot, fresh, **HP)
+    assert_state_equal(m.to_state(), want, "zero row")
+
+
+def test_coupled_update_bit_exact(gpu_lib):
+    R, C = 200, 512
+    g = synth.rng(600)
+    pairs_np = []
+    for pi, (a_own, a_cross) in enumerate([(1.0, 0.0), (0.9, 0.37), (0.0, 1.0)]):
+        A = make_state(R, C, 610 + pi, 40, True)
+        B = make_state(R, C, 620 + pi, 40, True)
+        ra = np.sort(g.choice(R, 25, replace=False)).astype(np.int32)
+        rb = np.sort(np.unique(np.concatenate([ra[:10], g.choice(R, 15, replace=False)]))).astype(np.int32)
+        sa = g.choice(40, ra.size, replace=False).astype(np.int32)
+        sb = g.choice(40, rb.size, replace=False).astype(np.int32)
+        fa = (g.random(ra.size) < 0.2).astype(np.uint8)
+        GA = synth.gradient_rows(ra.size, C, 0.2, 630 + pi)
+        GB = synth.gradient_rows(rb.size, C, 0.2, 640 + pi)
+        clip = np.array([0.75, 1.0], np.float32) if pi == 1 else None
+        pairs_np.append((A, B, ra, rb, sa, sb, fa, GA, GB, a_own, a_cross, clip))
+    wd = float(np.float32(0.01 * math.cos(math.radians(28.4))))
+    gpu_pairs, mats = [], []
+    for A, B, ra, rb, sa, sb, fa, GA, GB, a_own, a_cross, clip in pairs_np:
+        ma, mb = GpuMat(A, GA, ra, sa, fa), GpuMat(B, GB, rb, sb, None)
+        mats.append((ma, mb))
+        gpu_pairs.append(_lib.Pair(ma.upd(), mb.upd(), a_own, a_cross, None if clip is None else dev(clip)))
+    _lib.sft_coupled_update(gpu_pairs, adam_dev(weight_decay=wd, **HP))
+    torch.cuda.synchronize()
+    for (A, B, ra, rb, sa, sb, fa, GA, GB, a_own, a_cross, clip), (ma, mb) in zip(pairs_np, mats):
+        wa, wb = A.copy(), B.copy()
+        ca, cb = (1.0, 1.0) if clip is None else (float(clip[0]), float(clip[1]))
+        oracle.coupled_update(wa, GA, ra, sa, fa, wb, GB, rb, sb, None, a_own=a_own, a_cross=a_cross,
+                              clip_a=ca, clip_b=cb, weight_decay=wd, **HP)
+        assert_state_equal(ma.to_state(), wa, f"pair A ({a_own},{a_cross})")
+        assert_state_equal(mb.to_state(), wb, f"pair B ({a_own},{a_cross})")
+
+
+def test_masked_writeback_bit_exact(gpu_lib):
+    R, C = 333, 1032
+    q, s, delta = synth.quant_state(R, C, 700)
+    rows = np.sort(synth.rng(701).choice(R, 40, replace=False)).astype(np.int32)
+    w0 = np.full((R, C), 0x5A5A, np.uint16)
+    wl = torch.from_numpy(w0.view(np.int16)).cuda()
+    _lib.sft_masked_writeback(dev(q), dev(s), dev(delta), dev(rows), rows.size, wl)
+    torch.cuda.synchronize()
+    want = w0.copy()
+    oracle.masked_writeback(q, s, delta, rows, want)
+    assert np.array_equal(wl.cpu().numpy().view(np.uint16), want)
+
+
+def test_update_rejects_bad_arguments(gpu_lib):
+    st, rows, slot, fresh, G = _case(16, 12, 2, 2, 800, False)   # C = 12: not a multiple of 8
+    m = GpuMat(st, G, rows, slot, fresh)
+    with pytest.raises(_lib.SftError) as e:
+        _lib.sft_sparse_update([m.upd()], adam_dev(**HP))
+    assert e.value.code == _lib.SFT_ESHAPE

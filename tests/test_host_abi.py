@@ -1,0 +1,123 @@
+"""CPU tests of the C-ABI library: every declared symbol is exported, and the
+host-side logic (conductor, row tracker, row plans, embedding CSR, moment
+slots, bias table, argument checks) matches the oracle bit for bit.
+
+No GPU is needed: these calls run on the host.  Method: "Sparse-First
+Fine-Tuning: Full-Weight Training at the Cost of the Active Set", sections
+2.1 (conductor and tracker, masks once a step on the CPU) and 2.2 (32-row
+tiles).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_full_weight_amd import _lib, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sft.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sft_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    declared = _declared()
+    assert len(declared) >= 14
+    missing = [n for n in declared if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(_lib.EXPORTS) == declared
+    assert _lib.sft_abi_version() == 1
+
+
+def test_conductor_matches_oracle_over_windows():
+    V = 32000
+    ch_l = np.zeros(V, np.float32)
+    ch_o = np.zeros(V, np.float32)
+    for w in range(4):
+        toks = synth.zipf_tokens(4096, V, 1.1, 2000 + w)
+        a_l = _lib.sft_conductor_window(ch_l, toks)
+        a_o = oracle.conductor_window(ch_o, toks)
+        assert np.array_equal(ch_l.view(np.uint32), ch_o.view(np.uint32))
+        assert np.array_equal(a_l, a_o)
+    # the embedding config's conductor yields a sparse mask (about 0.2% of rows)
+    assert 20 <= a_l.sum() <= 200
+
+
+def test_tracker_matches_oracle():
+    R = 11008
+    hot = synth.clustered_rows(R, 110, 2100)
+    ch_l = np.zeros(R, np.float32)
+    ch_o = np.zeros(R, np.float32)
+    for w in range(3):
+        a = synth.tracker_magnitudes(R, hot, 2101 + w)
+        a_l = _lib.sft_tracker_window(ch_l, a)
+        a_o = oracle.tracker_window(ch_o, a)
+        assert np.array_equal(ch_l.view(np.uint32), ch_o.view(np.uint32))
+        assert np.array_equal(a_l, a_o)
+    with pytest.raises(_lib.SftError):
+        _lib.sft_tracker_window(ch_l, -np.ones(R, np.float32))
+
+
+@pytest.mark.parametrize("R", [1, 31, 33, 512, 4097, 11008])
+def test_plan_rows_matches_oracle(R):
+    mask = (synth.rng(R).random(R) < 0.05).astype(np.uint8)
+    mask[-1] = 1
+    p = _lib.sft_plan_rows(mask)
+    o = oracle.plan_rows(mask)
+    assert np.array_equal(p.tile_bits, o["bits"])
+    assert np.array_equal(p.active_rows, o["active_rows"])
+    assert np.array_equal(p.active_tiles, o["active_tiles"])
+
+
+def test_plan_embedding_matches_oracle():
+    V = 5000
+    toks = synth.zipf_tokens(4096, V, 1.1, 2200)
+    mask = np.zeros(V, np.uint8)
+    mask[np.unique(toks)[:40]] = 1
+    mask[V - 1] = 1                       # an active row with no hits
+    p = _lib.sft_plan_rows(mask)
+    rp, pos = _lib.sft_plan_embedding(p, toks)
+    orp, opos = oracle.plan_embedding(p.active_rows, toks)
+    assert np.array_equal(rp, orp) and np.array_equal(pos, opos)
+
+
+def test_slots_match_oracle_over_steps():
+    g = synth.rng(2300)
+    R, n_slots = 500, 60
+    rs_l = np.full(R, -1, np.int32)
+    rs_o = np.full(R, -1, np.int32)
+    for _ in range(40):
+        rows = np.sort(g.choice(R, size=int(g.integers(0, n_slots + 1)), replace=False)).astype(np.int32)
+        s_l, f_l = _lib.sft_slots_update(rs_l, n_slots, rows)
+        s_o, f_o = oracle.slots_update(rs_o, n_slots, rows)
+        assert np.array_equal(s_l, s_o) and np.array_equal(f_l, f_o) and np.array_equal(rs_l, rs_o)
+    with pytest.raises(_lib.SftError) as e:
+        _lib.sft_slots_update(rs_l, 2, np.arange(3, dtype=np.int32))
+    assert e.value.code == _lib.SFT_ECAPACITY
+
+
+def test_bias_table_matches_oracle():
+    for b1, b2 in [(0.9, 0.999), (0.8, 0.95), (0.0, 0.5)]:
+        l1, l2 = _lib.sft_bias_table(b1, b2, 20000)
+        o1, o2 = oracle.bias_table(b1, b2, 20000)
+        assert np.array_equal(l1.view(np.uint32), o1.view(np.uint32))
+        assert np.array_equal(l2.view(np.uint32), o2.view(np.uint32))
+    assert _lib.sft_bias_table(0.9, 0.999, 20000)[1][-1] == 1.0   # table reaches 1.0f
+
+
+def test_host_calls_reject_bad_input_before_writing():
+    ch = np.full(4, 0.5, np.float32)
+    with pytest.raises(_lib.SftError) as e:
+        _lib.sft_conductor_window(ch, np.array([0, 4], np.int32))
+    assert e.value.code == _lib.SFT_EINVAL
+    assert np.all(ch == 0.5)
+    with pytest.raises(_lib.SftError):
+        _lib.sft_bias_table(1.0, 0.9, 10)
+    assert "beta" in _lib.lib().sft_last_error().decode()
