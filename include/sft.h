@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 1
+#define SFT_ABI_VERSION 2
 
 enum {
     SFT_OK = 0,
@@ -107,6 +107,8 @@ int sft_tracker_window(float *ch, int64_t rows, const float *magnitude, uint8_t 
  *   tile_bits    [ceil(rows/32)]  bit i of word j = mask of row 32*j+i (bits >= rows are 0)
  *   active_rows  [rows]           ascending active rows (first n_active valid)
  *   active_tiles [ceil(rows/32)]  ascending tiles with an active row (first n_active_tiles valid)
+ *   active_bits  [ceil(rows/32)]  tile_bits of each active tile (first n_active_tiles valid)
+ *   tile_first   [ceil(rows/32)]  index in active_rows of each active tile's first active row
  */
 typedef struct sft_plan {
     int64_t rows;           /* in  */
@@ -115,9 +117,12 @@ typedef struct sft_plan {
     uint32_t *tile_bits;
     int32_t *active_rows;
     int32_t *active_tiles;
+    uint32_t *active_bits;
+    int32_t *tile_first;
 } sft_plan;
 
-/* Errors: SFT_EINVAL for null pointers or rows < 0 or rows >= 2^31. */
+/* Errors: SFT_EINVAL for null pointers or rows < 0 or rows >= 2^31.
+ * active_bits and tile_first may be NULL (not filled). */
 int sft_plan_rows(const uint8_t *active, sft_plan *plan);
 
 /*
@@ -162,15 +167,16 @@ int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *b
 
 /*
  * One matrix of a masked-dW group.  dY is bf16 [T x R] (gradient at the
- * matrix's output); the plan arrays are device copies of an sft_plan of this
- * matrix's mask; dW_act is fp32 [n_active x C], row k = active_rows[k].
+ * matrix's output); the plan arrays are device copies of the active-tile part
+ * of an sft_plan of this matrix's mask; dW_act is fp32 [n_active x C], row k
+ * = the k-th active row.
  */
 typedef struct sft_dw_mat {
     const uint16_t *dY;
     int64_t R;
-    const uint32_t *tile_bits;   /* device [ceil(R/32)] */
-    const int32_t *active_rows;  /* device [n_active]  */
     const int32_t *active_tiles; /* device [n_active_tiles] */
+    const uint32_t *active_bits; /* device [n_active_tiles] */
+    const int32_t *tile_first;   /* device [n_active_tiles] */
     int64_t n_active;            /* host scalar */
     int64_t n_active_tiles;      /* host scalar */
     float *dW_act;               /* device [n_active x C] */
@@ -185,7 +191,8 @@ typedef struct sft_dw_group {
 } sft_dw_group;
 
 /*
- * Workspace bytes sft_masked_dw needs for these groups (0 is possible).
+ * Workspace bytes sft_masked_dw needs for these groups (0 is possible): the
+ * split-K partial rows when the token axis is split to fill the GPU.
  * Returns (size_t)-1 and sets the error message on invalid groups.
  */
 size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
@@ -196,11 +203,9 @@ size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
  * Each 32-row tile with no active row is skipped before any load of dY or X;
  * inside an active tile only the active rows are written (section 2.2).
  * Matrices of one group share every load of X.
- *   ws / ws_bytes  device workspace of at least sft_masked_dw_workspace()
- *                  bytes.  It must be zero-filled before its first use; every
- *                  call leaves it zero-filled again (it holds split-K
- *                  partial sums and arrival counters).  Calls that share a
- *                  workspace must be ordered on one stream.
+ *   ws / ws_bytes  device scratch of at least sft_masked_dw_workspace()
+ *                  bytes (16-byte aligned; no initialisation needed).  Calls
+ *                  that share a workspace must be ordered on one stream.
  * Limits: T >= 1, T < 2^31, C % 8 == 0, R < 2^31.  Results are deterministic
  * (a fixed summation order for every launch configuration the same inputs
  * produce).

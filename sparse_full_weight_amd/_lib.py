@@ -43,12 +43,13 @@ class SftError(RuntimeError):
 # ------------------------------------------------------------------ C structs
 class CPlan(C.Structure):
     _fields_ = [("rows", C.c_int64), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
-                ("tile_bits", C.c_void_p), ("active_rows", C.c_void_p), ("active_tiles", C.c_void_p)]
+                ("tile_bits", C.c_void_p), ("active_rows", C.c_void_p), ("active_tiles", C.c_void_p),
+                ("active_bits", C.c_void_p), ("tile_first", C.c_void_p)]
 
 
 class CDwMat(C.Structure):
-    _fields_ = [("dY", C.c_void_p), ("R", C.c_int64), ("tile_bits", C.c_void_p), ("active_rows", C.c_void_p),
-                ("active_tiles", C.c_void_p), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
+    _fields_ = [("dY", C.c_void_p), ("R", C.c_int64), ("active_tiles", C.c_void_p), ("active_bits", C.c_void_p),
+                ("tile_first", C.c_void_p), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
                 ("dW_act", C.c_void_p)]
 
 
@@ -166,11 +167,14 @@ def sft_tracker_window(ch: np.ndarray, magnitude: np.ndarray) -> np.ndarray:
 
 @dataclass
 class Plan:
-    """Host row plan of one mask (tile bitmap, active rows, active tiles)."""
+    """Host row plan of one mask (tile bitmap, active rows, active tiles and,
+    per active tile, its row bits and the index of its first active row)."""
     rows: int
     tile_bits: np.ndarray
     active_rows: np.ndarray
     active_tiles: np.ndarray
+    active_bits: np.ndarray
+    tile_first: np.ndarray
 
     @property
     def n_active(self) -> int:
@@ -184,15 +188,17 @@ class Plan:
         import torch
         def up(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device, non_blocking=False)
-        return DevicePlan(self, up(self.tile_bits), up(self.active_rows), up(self.active_tiles))
+        return DevicePlan(self, up(self.active_rows), up(self.active_tiles), up(self.active_bits),
+                          up(self.tile_first))
 
 
 @dataclass
 class DevicePlan:
     host: Plan
-    tile_bits: "object"
     active_rows: "object"
     active_tiles: "object"
+    active_bits: "object"
+    tile_first: "object"
 
     @property
     def rows(self) -> int:
@@ -214,16 +220,20 @@ def sft_plan_rows(mask: np.ndarray) -> Plan:
     bits = np.zeros(max(tiles, 1), np.uint32)
     act = np.zeros(max(rows, 1), np.int32)
     at = np.zeros(max(tiles, 1), np.int32)
-    cp = CPlan(rows, 0, 0, _np_ptr(bits), _np_ptr(act), _np_ptr(at))
+    ab = np.zeros(max(tiles, 1), np.uint32)
+    tf = np.zeros(max(tiles, 1), np.int32)
+    cp = CPlan(rows, 0, 0, _np_ptr(bits), _np_ptr(act), _np_ptr(at), _np_ptr(ab), _np_ptr(tf))
     _check(lib().sft_plan_rows(_np_ptr(mask), C.byref(cp)))
-    return Plan(rows, bits[:tiles].copy(), act[:cp.n_active].copy(), at[:cp.n_active_tiles].copy())
+    nt = cp.n_active_tiles
+    return Plan(rows, bits[:tiles].copy(), act[:cp.n_active].copy(), at[:nt].copy(), ab[:nt].copy(), tf[:nt].copy())
 
 
 def sft_plan_embedding(plan: Plan, tokens: np.ndarray):
     """CSR (row_ptr, positions) of the active embedding rows' token positions."""
     tokens = np.ascontiguousarray(tokens, np.int32)
     cp = CPlan(plan.rows, plan.n_active, plan.n_active_tiles, _np_ptr(plan.tile_bits),
-               _np_ptr(plan.active_rows), _np_ptr(plan.active_tiles))
+               _np_ptr(plan.active_rows), _np_ptr(plan.active_tiles), _np_ptr(plan.active_bits),
+               _np_ptr(plan.tile_first))
     row_ptr = np.zeros(plan.n_active + 1, np.int32)
     pos = np.zeros(max(tokens.size, 1), np.int32)
     nnz = C.c_int64()
@@ -271,8 +281,8 @@ def _c_groups(groups: Sequence[DwGroup]):
         T, Cc = g.X.shape
         mats = (CDwMat * max(len(g.mats), 1))()
         for j, m in enumerate(g.mats):
-            mats[j] = CDwMat(_dev(m.dY, torch.bfloat16), m.plan.rows, _dev(m.plan.tile_bits),
-                             _dev(m.plan.active_rows), _dev(m.plan.active_tiles), m.plan.n_active,
+            mats[j] = CDwMat(_dev(m.dY, torch.bfloat16), m.plan.rows, _dev(m.plan.active_tiles),
+                             _dev(m.plan.active_bits), _dev(m.plan.tile_first), m.plan.n_active,
                              m.plan.n_active_tiles, _dev(m.dW_act, torch.float32))
         keep.append(mats)
         arr[i] = CDwGroup(_dev(g.X, torch.bfloat16), T, Cc, len(g.mats), mats)
@@ -371,3 +381,38 @@ def sft_masked_writeback(q, s, delta, active_rows, n_active: int, w_live, stream
     _check(lib().sft_masked_writeback(_dev(q, torch.int8), _dev(s, torch.float32), _dev(delta, torch.float32),
                                       R, Cc, _dev(active_rows, torch.int32), n_active, _dev(w_live),
                                       _stream(stream)))
+
+
+# ------------------------------------------------------------------ prepared calls
+class Prepared:
+    """A device call with its ctypes arguments built once (for tight loops).
+
+    Calling it enqueues the same launch again on the given stream; the tensors
+    it refers to must stay alive (the object keeps references to them)."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def prepare_masked_dw(groups: Sequence[DwGroup], ws=None) -> Prepared:
+    arr, keep = _c_groups(groups)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return Prepared(lib().sft_masked_dw, (arr, len(groups), _dev(ws), nbytes), (arr, keep, groups, ws))
+
+
+def prepare_sparse_update(mats: Sequence[UpdMat], hp: Adam) -> Prepared:
+    arr = (CUpdMat * max(len(mats), 1))(*[m.c() for m in mats])
+    h = hp.c()
+    return Prepared(lib().sft_sparse_update, (arr, len(mats), C.byref(h)), (arr, h, mats, hp))
+
+
+def prepare_coupled_update(pairs: Sequence[Pair], hp: Adam) -> Prepared:
+    arr = (CPair * max(len(pairs), 1))(*[CPair(p.a.c(), p.b.c(), p.a_own, p.a_cross, _dev(p.clip))
+                                         for p in pairs])
+    h = hp.c()
+    return Prepared(lib().sft_coupled_update, (arr, len(pairs), C.byref(h)), (arr, h, pairs, hp))

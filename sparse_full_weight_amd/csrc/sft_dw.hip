@@ -10,30 +10,37 @@
 // so a row's gradient is the sum of dY over the positions of its token.
 //
 // Masked dW design (MI355X):
-//   * Only active tiles are ever scheduled: the grid is built from the active
-//     tile lists, so a skipped tile is never even visited.
+//   * Only active tiles are ever scheduled: the work list is built from the
+//     active tile lists, so a skipped tile is never visited.
 //   * Matrices that read the same input X (q/k/v; gate/up) form one group; up
-//     to 8 active tiles of a group (256 rows) share every load of an X block,
-//     which is what makes the product cheap at ~1% density: X is the dominant
-//     HBM stream and is read once per group instead of once per matrix.
-//   * A workgroup (4 wave64s) owns an M-block of up to 8 tiles x 128 columns
-//     of C and a range of tokens.  Per 64-token chunk each lane loads 8x8
-//     bf16 blocks (eight 16-byte rows), transposes them in registers so that
-//     tokens (the reduction axis) become contiguous, and writes them to LDS
-//     with 16-byte stores; the MFMA v_mfma_f32_32x32x16_bf16 then reads its
-//     operand fragments as 16-byte LDS loads.  The next chunk's global loads
-//     are in flight while the current chunk is multiplied.
-//   * Few active tiles means few workgroups, so the token axis is split
-//     (split-K) until the launch fills the 256 CUs.  Partial tiles go to a
-//     workspace; the last workgroup of a tile to arrive (an atomic counter)
-//     adds all partials in split order, so the result does not depend on
-//     timing, and resets the counter for the next call.
-//   * Units are ordered so that consecutive ones, which share the same dY
-//     slice, land on the same XCD (its private L2): the hardware dispatches
-//     workgroup i to XCD i mod 8, and unit = (i mod 8) * per_xcd + i / 8.
+//     to 8 active tiles of a group (an M-block of 256 rows) share every load
+//     of an X block.  X is the dominant HBM stream at ~1% density and is read
+//     once per M-block instead of once per matrix.
+//   * Output tiles are (M-block, 128 columns of C); each is a sequence of
+//     64-token chunks.  The launch is persistent and stream-K: one 8-wave
+//     workgroup per CU takes an equal contiguous slice of the whole
+//     (tile, chunk) iteration space, so every CU streams the same number of X
+//     bytes whatever the tile counts.  Tiles cut by a slice boundary are
+//     written as partial sums to scratch and combined by a second small
+//     kernel in slice order (deterministic; the kernel boundary orders the
+//     stores, so no device-scope fence is needed -- such a fence writes back
+//     and invalidates an XCD's L2, and one per workgroup serialised badly).
+//   * Per chunk each lane loads one 8x8 bf16 block (eight 16-byte rows of
+//     tokens), transposes it in registers so that tokens (the reduction
+//     axis) become contiguous, and stores it to LDS with 16-byte writes.  The
+//     LDS row pitch is 9 granules of 16 bytes: the 8 lanes of a store phase
+//     (same columns, token groups 0..7) and the 8 lanes of an operand read
+//     phase (8 consecutive rows) then hit 8 distinct bank groups.  LDS is
+//     double-buffered and two further chunks are in flight in registers.
+//   * v_mfma_f32_32x32x16_bf16 consumes 16-byte LDS fragments; wave w owns
+//     columns 32*(w%4) and half of the M-block's tiles.
+//   * Slices are laid out so that the 32 workgroups of one XCD (the hardware
+//     dispatches workgroup i to XCD i mod 8) take neighbouring slices, which
+//     share the M-block's dY columns in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "sft_internal.h"
@@ -42,69 +49,77 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const uint16_t gu16;
 
-constexpr int kBK = 32;              // tokens per chunk
-constexpr int kBN = 128;             // columns per N-block (4 waves x 32)
-constexpr int kMaxTiles = 8;         // 32-row tiles per M-block
-constexpr int kLdk = kBK + 8;        // LDS pitch (elements): 80-B rows keep 16-B fragment reads conflict-free
-constexpr int kThreads = 256;
+constexpr int kBN = 128;           // columns per output tile (4 column slices of 32)
+constexpr int kMaxTiles = 8;       // 32-row tiles per M-block
+constexpr int kBK = 64;            // tokens per chunk
+constexpr int kLdk = 72;           // LDS row pitch (elements): 9 granules of 16 B
+constexpr int kThreads = 512;      // 8 waves
+constexpr int kStageRows = kMaxTiles * 32 + kBN;
+constexpr int kStageElems = kStageRows * kLdk;
 constexpr int kMaxGroups = 8;
 constexpr int kMaxMats = 16;
+constexpr int kMaxSegs = 16;       // tiles touched by one slice
 constexpr int kXcds = 8;
-constexpr int64_t kPartStride = int64_t(kMaxTiles) * 32 * kBN;  // floats per partial tile
+constexpr int64_t kSlotFloats = int64_t(kMaxTiles) * 32 * kBN;  // one partial tile
 
 struct DwMatDev {
     const uint16_t *dY;
     int64_t R;
-    const uint32_t *bits;
-    const int32_t *rows;
-    const int32_t *tiles;
+    const int32_t *tiles;   // active tiles
+    const uint32_t *abits;  // their row bits
+    const int32_t *first;   // index of their first active row
     int64_t n_active;
     float *out;
     int32_t n_tiles;
     int32_t tile_begin;  // offset in the group's concatenated tile list
-    int32_t vec;         // R % 8 == 0: 16-byte loads of dY
 };
 
 struct DwGroupDev {
     const uint16_t *X;
     int64_t T, C;
     int32_t mat_begin, n_mats;
-    int32_t n_tiles, n_mblk, n_nblk, n_split, chunks;
-    int64_t unit_begin;      // first unit of this group
-    int64_t out_tile_begin;  // first (mblock, nblock) output tile of this group (counter index)
-    int64_t part_offset;     // floats: this group's partial tiles in the workspace
+    int32_t n_tiles;     // active 32-row tiles of the group
+    int32_t n_mblk, n_nblk, chunks;
+    int64_t it_begin;    // first global iteration of this group
+    int64_t otile_begin; // first output tile (global numbering)
 };
 
 struct DwParams {
     DwGroupDev g[kMaxGroups];
     DwMatDev m[kMaxMats];
     int32_t n_groups;
-    int64_t n_units;
-    int64_t per_xcd;
-    uint32_t *counters;  // [output tiles of the call], zero between calls
-    float *partials;     // per split group: [mblk*nblk][n_split][kPartStride]
+    int32_t n_wg;        // slices (= workgroups of the main launch)
+    int64_t iters;       // total (tile, chunk) iterations
+    float *part;         // [2 * n_wg] partial tiles of kSlotFloats
 };
 
 struct TileDesc {
     const uint16_t *dY;
-    int64_t R;
     float *out;
     int64_t col0;   // first dY column (= first row of W) of the tile
+    uint32_t R;
     uint32_t bits;
     int32_t first;  // index in the matrix's active-row list of the tile's first active row
-    int32_t vec;
 };
 
-// First index k with rows[k] >= key.
-__device__ __forceinline__ int32_t lower_bound_rows(const int32_t *rows, int64_t n, int64_t key) {
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (rows[mid] < key) lo = mid + 1;
-        else hi = mid;
-    }
-    return static_cast<int32_t>(lo);
+struct Seg {
+    int32_t g, mb, nb, mt;
+    int32_t k0;     // first chunk of the tile in this slice
+    int32_t j0;     // first local iteration of the segment
+    int32_t len;    // chunks
+    int32_t slot;   // -1: whole tile (final output); else partial slot
+};
+
+__device__ __forceinline__ uint4 gload16(const uint16_t *p) {
+    const u32x4 v = *reinterpret_cast<gu32x4 *>(reinterpret_cast<uintptr_t>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t gload2(const uint16_t *p) {
+    return *reinterpret_cast<gu16 *>(reinterpret_cast<uintptr_t>(p));
 }
 
 // 8x8 transpose of bf16: in[i] holds 8 consecutive columns of token row i;
@@ -125,210 +140,352 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
     }
 }
 
-template <bool kVecA>
-__global__ __launch_bounds__(kThreads, 2) void k_masked_dw(const DwParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[kMaxTiles * 32 * kLdk];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdk];
-    __shared__ TileDesc tdesc[kMaxTiles];
-    __shared__ int32_t s_last;
+// Descriptor of tile `t` (0..mt-1) of M-block mb of group G.
+__device__ TileDesc make_tile_desc(const DwParams &p, const DwGroupDev &G, int32_t mb, int t) {
+    const int32_t gt = mb * kMaxTiles + t;
+    int mi = G.mat_begin;
+    while (mi + 1 < G.mat_begin + G.n_mats && gt >= p.m[mi + 1].tile_begin) ++mi;
+    const DwMatDev &M = p.m[mi];
+    const int32_t lt = gt - M.tile_begin;
+    TileDesc d;
+    d.dY = M.dY;
+    d.out = M.out;
+    d.col0 = 32 * static_cast<int64_t>(M.tiles[lt]);
+    d.R = static_cast<uint32_t>(M.R);
+    d.bits = M.abits[lt];
+    d.first = M.first[lt];
+    return d;
+}
 
-    // ---- which unit: XCD-contiguous order
-    const int64_t b = blockIdx.x;
-    const int64_t unit = (b % kXcds) * p.per_xcd + b / kXcds;
-    if (unit >= p.n_units) return;
-    int gi = 0;
-    while (gi + 1 < p.n_groups && unit >= p.g[gi + 1].unit_begin) ++gi;
-    const DwGroupDev &G = p.g[gi];
-    int64_t u = unit - G.unit_begin;
-    const int32_t nb = static_cast<int32_t>(u % G.n_nblk);
-    u /= G.n_nblk;
-    const int32_t sp = static_cast<int32_t>(u % G.n_split);
-    const int32_t mb = static_cast<int32_t>(u / G.n_split);
-    const int32_t t_lo = mb * kMaxTiles;
-    const int32_t mt = min(kMaxTiles, G.n_tiles - t_lo);
-    const int64_t n0 = static_cast<int64_t>(nb) * kBN;
-    const int32_t c_begin = static_cast<int32_t>((static_cast<int64_t>(sp) * G.chunks) / G.n_split);
-    const int32_t c_end = static_cast<int32_t>((static_cast<int64_t>(sp + 1) * G.chunks) / G.n_split);
+// Slice of workgroup v: global iterations [lo, hi).  Boundaries fall on
+// even iterations (chunk counts are even too), so every segment is a whole
+// number of chunk pairs -- the unit of the software pipeline below.
+__device__ __forceinline__ int64_t slice_lo(const DwParams &p, int64_t v) {
+    return 2 * (v * (p.iters / 2) / p.n_wg);
+}
+
+// One lane's share of a chunk: which 8 columns and 8 tokens it loads and
+// where the transposed block goes in the stage buffer.  Offsets are 32-bit
+// element counts (the host checks T*R and T*C < 2^31).
+struct Task {
+    const uint16_t *base;     // matrix base; masked-off lanes use X (>= 16 bytes, C % 8 == 0)
+    uint32_t col;             // first column of the block (0 for masked-off lanes)
+    uint32_t pitch;           // row pitch (elements)
+    uint32_t t0;              // first token row
+    uint32_t t_last;          // last valid token row (T - 1)
+    uint32_t valid_cols;      // columns of the block inside the matrix (0: no task)
+    int32_t dst;              // element offset in the stage buffer
+};
+
+// What a store needs to know about a block in flight.  The loaded registers
+// are never touched before the store: masking them at load time would make
+// the compiler wait for the loads right after issuing them.
+struct Pending {
+    int32_t dst;        // -1: no task
+    uint32_t row_ok;    // bit i: token row i of the block is inside the matrix
+    uint32_t valid_cols;
+};
+
+template <bool kVec>
+__device__ __forceinline__ Pending load_task(const Task &k, uint4 (&ld)[8]) {
+    Pending pd;
+    pd.dst = k.valid_cols ? k.dst : -1;
+    pd.valid_cols = k.valid_cols;
+    pd.row_ok = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t t = k.t0 + i;
+        pd.row_ok |= (t <= k.t_last) ? (1u << i) : 0u;
+        // rows past the end re-read the last row; the store masks them
+        const uint32_t off = min(t, k.t_last) * k.pitch + k.col;
+        if (kVec) {
+            ld[i] = gload16(k.base + off);
+        } else {
+            // rows not 16-byte aligned: element loads (this path packs at once)
+            uint16_t e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                e[q] = gload2(k.base + off + (static_cast<uint32_t>(q) < k.valid_cols ? q : 0));
+            ld[i] = make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                               e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+        }
+    }
+    return pd;
+}
+
+__device__ __forceinline__ void store_task(uint4 (&ld)[8], const Pending &pd, uint16_t *stage) {
+    if (pd.dst < 0) return;
+    // zero what lies outside the matrix: token rows past T, columns past R
+    uint32_t cm[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        cm[w] = (2u * w < pd.valid_cols ? 0x0000ffffu : 0u) | (2u * w + 1 < pd.valid_cols ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t rm = ((pd.row_ok >> i) & 1u) ? 0xffffffffu : 0u;
+        ld[i].x &= rm & cm[0];
+        ld[i].y &= rm & cm[1];
+        ld[i].z &= rm & cm[2];
+        ld[i].w &= rm & cm[3];
+    }
+    uint4 tr[8];
+    transpose8x8(ld, tr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4 *>(stage + pd.dst + e * kLdk) = tr[e];
+}
+
+// MFMAs of one chunk for one wave: NT tiles (from tile tb) x 32 columns.
+template <int NT>
+__device__ __forceinline__ void mma_chunk(const uint16_t *stage, int tb, int wave, int lane,
+                                          floatx16 (&acc)[4]) {
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 8;
+    const uint16_t *bptr = stage + (kMaxTiles * 32 + (wave & 3) * 32 + frag_row) * kLdk + frag_k;
+    const uint16_t *aptr = stage + (tb * 32 + frag_row) * kLdk + frag_k;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(bptr + kk * 16);
+        bf16x8 a[NT > 0 ? NT : 1];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) a[t] = *reinterpret_cast<const bf16x8 *>(aptr + t * 32 * kLdk + kk * 16);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], b, acc[t], 0, 0, 0);
+    }
+}
+
+template <bool kVecA>
+__global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t stage[2][kStageElems];
+    __shared__ Seg segs[kMaxSegs];
+    __shared__ TileDesc tdesc[kMaxSegs][kMaxTiles];
+    __shared__ int32_t s_nseg;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    // Slice of this workgroup: the 32 workgroups of an XCD take neighbouring slices.
+    const int64_t b = blockIdx.x;
+    const int64_t v = (p.n_wg % kXcds == 0) ? (b % kXcds) * (p.n_wg / kXcds) + b / kXcds : b;
+    const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
+    if (it_lo >= it_hi) return;
 
-    if (tid < mt) {
-        const int32_t gt = t_lo + tid;
-        int mi = G.mat_begin;
-        while (mi + 1 < G.mat_begin + G.n_mats && gt >= p.m[mi + 1].tile_begin) ++mi;
-        const DwMatDev &M = p.m[mi];
-        const int32_t j = M.tiles[gt - M.tile_begin];
-        TileDesc d;
-        d.dY = M.dY;
-        d.R = M.R;
-        d.out = M.out;
-        d.col0 = 32 * static_cast<int64_t>(j);
-        d.bits = M.bits[j];
-        d.first = lower_bound_rows(M.rows, M.n_active, d.col0);
-        d.vec = M.vec;
-        tdesc[tid] = d;
-    }
-    __syncthreads();
-
-    const int64_t T = G.T, C = G.C;
-    const uint16_t *X = G.X;
-    // One 8x8 (8 columns x 8 tokens) block per lane and chunk: the A side has
-    // mt tiles x 4 column groups x 4 token groups, the B side 16 x 4.
-    const int n_a = 16 * mt;
-    const int n_tasks = n_a + 64;
-    const int task = tid;
-    const bool has_task = task < n_tasks;
-    const int tg = task & 3;  // token group fastest: LDS stores spread over banks
-    const bool is_a = task < n_a;
-    const int cg = is_a ? (task >> 2) : ((task - n_a) >> 2);
-    // Element offsets fit 32 bits (the host checks T*R and T*C < 2^31).
-    const uint16_t *src_base;
-    uint32_t src_pitch;
-    bool col_ok;
-    uint32_t valid_cols = 8;  // unaligned dY rows: columns of the granule inside R
-    if (is_a) {
-        const TileDesc &d = tdesc[cg >> 2];
-        const int64_t col = d.col0 + (cg & 3) * 8;
-        src_base = d.dY + col;
-        src_pitch = static_cast<uint32_t>(d.R);
-        col_ok = col < d.R;
-        if (!kVecA && col_ok) valid_cols = static_cast<uint32_t>(min<int64_t>(8, d.R - col));
-    } else {
-        const int64_t col = n0 + cg * 8;
-        src_base = X + col;
-        src_pitch = static_cast<uint32_t>(C);
-        col_ok = col < C;
-    }
-    uint16_t *lds_dst = (is_a ? As : Bs) + (cg * 8) * kLdk + tg * 8;
-
-    uint4 ld[8];
-    auto load_chunk = [&](int32_t chunk) {
-        const uint32_t t0 = static_cast<uint32_t>(chunk) * kBK + tg * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t t = t0 + i;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (has_task && col_ok && t < T) {
-                const uint16_t *src = src_base + t * src_pitch;
-                if (kVecA || !is_a) {
-                    v = *reinterpret_cast<const uint4 *>(src);
-                } else {
-                    uint16_t e[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) e[q] = (static_cast<uint32_t>(q) < valid_cols) ? src[q] : 0;
-                    v.x = e[0] | (uint32_t(e[1]) << 16);
-                    v.y = e[2] | (uint32_t(e[3]) << 16);
-                    v.z = e[4] | (uint32_t(e[5]) << 16);
-                    v.w = e[6] | (uint32_t(e[7]) << 16);
-                }
-            }
-            ld[i] = v;
-        }
-    };
-    auto store_chunk = [&]() {
-        if (!has_task) return;
-        uint4 tr[8];
-        transpose8x8(ld, tr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4 *>(lds_dst + e * kLdk) = tr[e];
-    };
-
-    floatx16 acc[kMaxTiles];
-#pragma unroll
-    for (int tm = 0; tm < kMaxTiles; ++tm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tm][r] = 0.0f;
-
-    const int frag_row = lane & 31;           // row (A) / column (B) of the fragment
-    const int frag_k = (lane >> 5) * 8;       // first of the lane's 8 tokens
-    if (c_begin < c_end) load_chunk(c_begin);
-    for (int32_t chunk = c_begin; chunk < c_end; ++chunk) {
-        __syncthreads();
-        store_chunk();
-        __syncthreads();
-        if (chunk + 1 < c_end) load_chunk(chunk + 1);
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const bf16x8 bfrag = *reinterpret_cast<const bf16x8 *>(
-                Bs + (wave * 32 + frag_row) * kLdk + kk * 16 + frag_k);
-#pragma unroll
-            for (int tm = 0; tm < kMaxTiles; ++tm) {
-                if (tm < mt) {
-                    const bf16x8 afrag = *reinterpret_cast<const bf16x8 *>(
-                        As + (tm * 32 + frag_row) * kLdk + kk * 16 + frag_k);
-                    acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[tm], 0, 0, 0);
-                }
-            }
-        }
-    }
-
-    // ---- epilogue.  Accumulator layout of the 32x32 MFMA: lane l, register r
-    // holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the tile.
-    const int64_t col = n0 + wave * 32 + (lane & 31);
-    const int row_base = 4 * (lane >> 5);
-    if (G.n_split == 1) {
-#pragma unroll
-        for (int tm = 0; tm < kMaxTiles; ++tm) {
-            if (tm >= mt) continue;
-            const TileDesc &d = tdesc[tm];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 8 * (r >> 2) + row_base + (r & 3);
-                if (((d.bits >> i) & 1u) && col < C) {
-                    const int k = d.first + __builtin_popcount(d.bits & ((1u << i) - 1u));
-                    d.out[static_cast<int64_t>(k) * C + col] = acc[tm][r];
-                }
-            }
-        }
-        return;
-    }
-
-    // split-K: publish the partial tile, count arrivals, the last one reduces.
-    const int64_t out_tile = G.out_tile_begin + static_cast<int64_t>(mb) * G.n_nblk + nb;
-    float *part = p.partials + G.part_offset +
-                  (static_cast<int64_t>(mb) * G.n_nblk + nb) * G.n_split * kPartStride;
-    const int pcol = wave * 32 + (lane & 31);
-#pragma unroll
-    for (int tm = 0; tm < kMaxTiles; ++tm) {
-        if (tm >= mt) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 8 * (r >> 2) + row_base + (r & 3);
-            part[sp * kPartStride + (tm * 32 + i) * kBN + pcol] = acc[tm][r];
-        }
-    }
-    __threadfence();
-    __syncthreads();
+    // ---- the slice's segments (one per tile it touches)
     if (tid == 0) {
-        const uint32_t prev = atomicAdd(p.counters + out_tile, 1u);
-        s_last = (prev == static_cast<uint32_t>(G.n_split - 1)) ? 1 : 0;
+        int64_t it = it_lo;
+        int n = 0;
+        int32_t j = 0;
+        while (it < it_hi && n < kMaxSegs) {
+            int gi = 0;
+            while (gi + 1 < p.n_groups && it >= p.g[gi + 1].it_begin) ++gi;
+            const DwGroupDev &G = p.g[gi];
+            const int64_t rel = it - G.it_begin;
+            const int32_t tile = static_cast<int32_t>(rel / G.chunks);
+            const int32_t k0 = static_cast<int32_t>(rel % G.chunks);
+            const int64_t tile_end = G.it_begin + static_cast<int64_t>(tile + 1) * G.chunks;
+            const int64_t end = min(tile_end, it_hi);
+            Seg s;
+            s.g = gi;
+            s.mb = tile / G.n_nblk;
+            s.nb = tile % G.n_nblk;
+            s.mt = min(kMaxTiles, G.n_tiles - s.mb * kMaxTiles);
+            s.k0 = k0;
+            s.j0 = j;
+            s.len = static_cast<int32_t>(end - it);
+            const bool whole = (k0 == 0 && end == tile_end);
+            s.slot = whole ? -1 : (n == 0 ? static_cast<int32_t>(2 * v) : static_cast<int32_t>(2 * v + 1));
+            segs[n++] = s;
+            j += s.len;
+            it = end;
+        }
+        s_nseg = n;
     }
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-#pragma unroll
-    for (int tm = 0; tm < kMaxTiles; ++tm) {
-        if (tm >= mt) continue;
-        const TileDesc &d = tdesc[tm];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 8 * (r >> 2) + row_base + (r & 3);
-            float sum = 0.0f;
-            for (int s = 0; s < G.n_split; ++s) {
-                const float v = (s == sp) ? acc[tm][r]
-                                          : __builtin_nontemporal_load(
-                                                part + s * kPartStride + (tm * 32 + i) * kBN + pcol);
-                sum = (s == 0) ? v : sum + v;
+    const int nseg = s_nseg;
+    for (int x = tid; x < nseg * kMaxTiles; x += kThreads) {
+        const int s = x / kMaxTiles, t = x % kMaxTiles;
+        if (t < segs[s].mt) tdesc[s][t] = make_tile_desc(p, p.g[segs[s].g], segs[s].mb, t);
+    }
+    __syncthreads();
+    const int32_t J = segs[nseg - 1].j0 + segs[nseg - 1].len;
+
+    // ---- this lane's load task for local iteration j
+    const int tg = tid & 7;   // token group: the 8 lanes of a store phase cover tokens 0..63
+    const int cg = tid >> 3;  // column group (8 columns)
+    // j lies in segment s0 or in one of the next two (lookahead is at most 4
+    // chunks and segments are at least 2 long); no loop here, so that the
+    // compiler keeps exact counts of the loads in flight.
+    auto make_task = [&](int32_t j, int s0) {
+        int s = s0;
+        s += (s + 1 < nseg && j >= segs[s + 1].j0) ? 1 : 0;
+        s += (s + 1 < nseg && j >= segs[s + 1].j0) ? 1 : 0;
+        const Seg &S = segs[s];
+        const DwGroupDev &G = p.g[S.g];
+        Task k;
+        k.base = G.X;
+        k.col = 0;
+        k.pitch = 0;
+        k.t_last = static_cast<uint32_t>(G.T) - 1;
+        k.t0 = static_cast<uint32_t>(S.k0 + (j - S.j0)) * kBK + tg * 8;
+        k.valid_cols = 0;
+        k.dst = -1;
+        if (j < J) {
+            if (cg < 4 * S.mt) {
+                const TileDesc &d = tdesc[s][cg >> 2];
+                const uint32_t col = static_cast<uint32_t>(d.col0) + (cg & 3) * 8;
+                if (col < d.R) {
+                    k.base = d.dY;
+                    k.col = col;
+                    k.pitch = d.R;
+                    k.valid_cols = min(8u, d.R - col);
+                    k.dst = (cg * 8) * kLdk + tg * 8;
+                }
+            } else if (cg < 4 * S.mt + kBN / 8) {
+                const int cb = cg - 4 * S.mt;
+                const uint32_t col = static_cast<uint32_t>(S.nb) * kBN + cb * 8;
+                if (col < static_cast<uint32_t>(G.C)) {
+                    k.col = col;
+                    k.pitch = static_cast<uint32_t>(G.C);
+                    k.valid_cols = 8;
+                    k.dst = (kMaxTiles * 32 + cb * 8) * kLdk + tg * 8;
+                }
             }
-            if (((d.bits >> i) & 1u) && col < C) {
-                const int k = d.first + __builtin_popcount(d.bits & ((1u << i) - 1u));
-                d.out[static_cast<int64_t>(k) * C + col] = sum;
+        }
+        return k;
+    };
+
+    floatx16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+    // ---- software pipeline, one chunk pair at a time: both chunks of a pair
+    // are transposed into the two stage buffers, then the loads of the next
+    // pair are issued, then both chunks are multiplied while those loads are
+    // in flight.  Loads are issued unconditionally (past the end of the slice
+    // they read a safe address and are masked), and sched_barrier keeps every
+    // group of loads in place, so the only wait on loads is the one at the
+    // stores, which needs them all.
+    uint4 ld0[8], ld1[8];
+    Pending pd0 = load_task<kVecA>(make_task(0, 0), ld0);
+    __builtin_amdgcn_sched_barrier(0);
+    Pending pd1 = load_task<kVecA>(make_task(1, 0), ld1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto pairs = [&](auto nt_tag, int tb, int seg, int32_t j, int32_t n) {
+        constexpr int NT = decltype(nt_tag)::value;
+        for (int32_t c = 0; c < n; c += 2, j += 2) {
+            store_task(ld0, pd0, stage[0]);
+            store_task(ld1, pd1, stage[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            pd0 = load_task<kVecA>(make_task(j + 2, seg), ld0);
+            __builtin_amdgcn_sched_barrier(0);
+            pd1 = load_task<kVecA>(make_task(j + 3, seg), ld1);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            mma_chunk<NT>(stage[0], tb, wave, lane, acc);
+            mma_chunk<NT>(stage[1], tb, wave, lane, acc);
+            __syncthreads();
+        }
+    };
+
+    for (int s = 0; s < nseg; ++s) {
+        const Seg &S = segs[s];
+        const int half = wave >> 2;
+        const int nt = half ? S.mt / 2 : (S.mt + 1) / 2;   // this wave's tiles
+        const int tb = half ? (S.mt + 1) / 2 : 0;
+        switch (nt) {
+            // Two loop bodies only (more instantiations make the register
+            // allocator spill): a wave with fewer tiles multiplies rows it
+            // then ignores -- cheap, as such blocks are bound by HBM anyway.
+            case 0:
+            case 1:
+            case 2: pairs(std::integral_constant<int, 2>{}, tb, s, S.j0, S.len); break;
+            default: pairs(std::integral_constant<int, 4>{}, tb, s, S.j0, S.len); break;
+        }
+        // ---- epilogue of the segment.  Accumulator layout of the 32x32 MFMA:
+        // lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+        // A whole tile goes to dW_act; a partial one to its slot, as compact
+        // active rows (row c = c-th active row of the M-block).
+        const DwGroupDev &G = p.g[S.g];
+        const int cl = (wave & 3) * 32 + (lane & 31);        // column inside the tile
+        const int64_t col = static_cast<int64_t>(S.nb) * kBN + cl;
+        const int row_base = 4 * (lane >> 5);
+        int prefix = 0;                                       // active rows of tiles before tb
+        for (int t = 0; t < tb; ++t) prefix += __builtin_popcount(tdesc[s][t].bits);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < nt) {
+                const TileDesc &d = tdesc[s][tb + t];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 8 * (r >> 2) + row_base + (r & 3);
+                    if ((d.bits >> i) & 1u) {
+                        const int below = __builtin_popcount(d.bits & ((1u << i) - 1u));
+                        if (S.slot < 0) {
+                            if (col < G.C) d.out[static_cast<int64_t>(d.first + below) * G.C + col] = acc[t][r];
+                        } else {
+                            p.part[S.slot * kSlotFloats + (prefix + below) * kBN + cl] = acc[t][r];
+                        }
+                    }
+                    acc[t][r] = 0.0f;
+                }
+                prefix += __builtin_popcount(d.bits);
             }
         }
     }
-    if (tid == 0) atomicExch(p.counters + out_tile, 0u);
+}
+
+// Combination of the partial tiles: an output tile cut by slice boundaries
+// is the sum of its slices' partial rows, added in slice order.  One
+// workgroup per (tile, 8 compact rows); a lane adds 4 columns.
+__global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
+    const int64_t ot = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < p.n_groups && ot >= p.g[gi + 1].otile_begin) ++gi;
+    const DwGroupDev &G = p.g[gi];
+    const int32_t tile = static_cast<int32_t>(ot - G.otile_begin);
+    const int64_t A = G.it_begin + static_cast<int64_t>(tile) * G.chunks;   // first iteration
+    const int64_t B = A + G.chunks;                                           // one past the last
+    // slices covering [A, B): slice v starts at 2*floor(v*PI/P), PI = iters/2
+    // (A and B are even)
+    const int64_t PI = p.iters / 2, P = p.n_wg;
+    const int64_t v_first = ((A / 2 + 1) * P - 1) / PI;
+    const int64_t v_last = ((B / 2) * P - 1) / PI;
+    if (v_first == v_last) return;  // the tile lies inside one slice: written directly
+    const int32_t mb = tile / G.n_nblk, nb = tile % G.n_nblk;
+    const int32_t mt = min(kMaxTiles, G.n_tiles - mb * kMaxTiles);
+    __shared__ TileDesc td[kMaxTiles];
+    __shared__ int32_t pre[kMaxTiles + 1];
+    if (threadIdx.x < mt) td[threadIdx.x] = make_tile_desc(p, G, mb, threadIdx.x);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        pre[0] = 0;
+        for (int t = 0; t < mt; ++t) pre[t + 1] = pre[t] + __builtin_popcount(td[t].bits);
+    }
+    __syncthreads();
+    const int c = blockIdx.y * 8 + (threadIdx.x >> 5);   // compact active row of the M-block
+    if (c >= pre[mt]) return;
+    const int cl = (threadIdx.x & 31) * 4;                // first of this lane's 4 columns
+    const int64_t col = static_cast<int64_t>(nb) * kBN + cl;
+    if (col >= G.C) return;
+    int t = 0;
+    while (t + 1 < mt && c >= pre[t + 1]) ++t;
+    const int64_t k = td[t].first + (c - pre[t]);        // output row in dW_act
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t vv = v_first; vv <= v_last; ++vv) {
+        const int64_t slot = (slice_lo(p, vv) >= A) ? 2 * vv : 2 * vv + 1;
+        const float4 x = *reinterpret_cast<const float4 *>(p.part + slot * kSlotFloats + c * kBN + cl);
+        if (vv == v_first) {
+            sum = x;
+        } else {
+            sum.x += x.x;
+            sum.y += x.y;
+            sum.z += x.z;
+            sum.w += x.w;
+        }
+    }
+    *reinterpret_cast<float4 *>(td[t].out + k * G.C + col) = sum;
 }
 
 // ---------------------------------------------------------------- embedding
@@ -377,10 +534,22 @@ __global__ __launch_bounds__(kEmbThreads) void k_embedding_dw(const uint16_t *__
 
 struct Plan {
     std::vector<DwParams> launches;
-    std::vector<int64_t> grid;
-    size_t cnt_bytes = 0;
+    std::vector<int64_t> out_tiles;
     size_t ws_bytes = 0;
 };
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 int validate(const sft_dw_group *groups, int32_t n_groups) {
     SFT_CHECK(n_groups >= 0 && (n_groups == 0 || groups), SFT_EINVAL, "sft_masked_dw: bad group list");
@@ -406,7 +575,7 @@ int validate(const sft_dw_group *groups, int32_t n_groups) {
                           m.n_active >= m.n_active_tiles && (m.n_active == 0) == (m.n_active_tiles == 0),
                       SFT_EINVAL, "sft_masked_dw: matrix %d/%d has inconsistent counts", gi, mi);
             if (m.n_active_tiles == 0) continue;
-            SFT_CHECK(m.dY && m.tile_bits && m.active_rows && m.active_tiles && m.dW_act, SFT_EINVAL,
+            SFT_CHECK(m.dY && m.active_tiles && m.active_bits && m.tile_first && m.dW_act, SFT_EINVAL,
                       "sft_masked_dw: matrix %d/%d has a null pointer", gi, mi);
             SFT_CHECK(g.T * m.R < (int64_t(1) << 31) && g.T * g.C < (int64_t(1) << 31), SFT_ENOTSUP,
                       "sft_masked_dw: matrix %d/%d: T*R or T*C reaches 2^31 elements", gi, mi);
@@ -418,86 +587,78 @@ int validate(const sft_dw_group *groups, int32_t n_groups) {
 }
 
 // Launch decomposition, shared by the workspace query and the launch.
-Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
+Plan make_plan(const sft_dw_group *groups, int32_t n_groups, void *ws) {
     Plan plan;
-    struct G {
-        const sft_dw_group *g;
-        int64_t tiles, mblk, nblk, chunks;
-    };
-    std::vector<G> live;
-    int64_t pairs = 0;
-    for (int32_t gi = 0; gi < n_groups; ++gi) {
-        int64_t tiles = 0;
-        for (int32_t mi = 0; mi < groups[gi].n_mats; ++mi) tiles += groups[gi].mats[mi].n_active_tiles;
-        if (tiles == 0) continue;
-        G g{&groups[gi], tiles, (tiles + kMaxTiles - 1) / kMaxTiles, (groups[gi].C + kBN - 1) / kBN,
-            (groups[gi].T + kBK - 1) / kBK};
-        pairs += g.mblk * g.nblk;
-        live.push_back(g);
-    }
-    if (live.empty()) return plan;
-    // Split the token axis until ~2 workgroups per CU exist (two fit at once),
-    // keeping at least 4 chunks (256 tokens) per split.
-    const int64_t target = 2 * 256;
-    int64_t max_chunks = 0;
-    for (const G &g : live) max_chunks = std::max(max_chunks, g.chunks);
-    int64_t split = std::max<int64_t>(1, (target + pairs - 1) / pairs);
-    split = std::min(split, std::max<int64_t>(1, max_chunks / 4));
-
-    size_t part_floats = 0;
-    int64_t out_tiles = 0;
-    size_t gidx = 0;
-    while (gidx < live.size()) {
+    const int cus = num_cus();
+    int32_t gi = 0;
+    while (gi < n_groups) {
         DwParams p{};
-        int64_t units = 0;
         int32_t nm = 0;
-        while (gidx < live.size() && p.n_groups < kMaxGroups &&
-               nm + live[gidx].g->n_mats <= kMaxMats) {
-            const G &g = live[gidx++];
+        int64_t iters = 0, otiles = 0, min_chunks = INT64_MAX;
+        while (gi < n_groups && p.n_groups < kMaxGroups) {
+            const sft_dw_group &g = groups[gi];
+            int32_t live_mats = 0;
+            int64_t tiles = 0;
+            for (int32_t mi = 0; mi < g.n_mats; ++mi)
+                if (g.mats[mi].n_active_tiles) {
+                    ++live_mats;
+                    tiles += g.mats[mi].n_active_tiles;
+                }
+            if (tiles == 0) {
+                ++gi;
+                continue;
+            }
+            if (nm + live_mats > kMaxMats) break;
+            ++gi;
             DwGroupDev &d = p.g[p.n_groups++];
-            d.X = g.g->X;
-            d.T = g.g->T;
-            d.C = g.g->C;
+            d.X = g.X;
+            d.T = g.T;
+            d.C = g.C;
             d.mat_begin = nm;
             d.n_mats = 0;
             int32_t tb = 0;
-            for (int32_t mi = 0; mi < g.g->n_mats; ++mi) {
-                const sft_dw_mat &m = g.g->mats[mi];
+            for (int32_t mi = 0; mi < g.n_mats; ++mi) {
+                const sft_dw_mat &m = g.mats[mi];
                 if (m.n_active_tiles == 0) continue;
                 DwMatDev &dm = p.m[nm++];
                 ++d.n_mats;
                 dm.dY = m.dY;
                 dm.R = m.R;
-                dm.bits = m.tile_bits;
-                dm.rows = m.active_rows;
                 dm.tiles = m.active_tiles;
+                dm.abits = m.active_bits;
+                dm.first = m.tile_first;
                 dm.n_active = m.n_active;
                 dm.out = m.dW_act;
                 dm.n_tiles = static_cast<int32_t>(m.n_active_tiles);
                 dm.tile_begin = tb;
-                dm.vec = (m.R % 8 == 0) ? 1 : 0;
                 tb += dm.n_tiles;
             }
             d.n_tiles = tb;
-            d.n_mblk = static_cast<int32_t>(g.mblk);
-            d.n_nblk = static_cast<int32_t>(g.nblk);
-            d.chunks = static_cast<int32_t>(g.chunks);
-            d.n_split = static_cast<int32_t>(std::min<int64_t>(split, g.chunks));
-            d.unit_begin = units;
-            d.out_tile_begin = out_tiles;
-            d.part_offset = static_cast<int64_t>(part_floats);
-            units += g.mblk * g.nblk * d.n_split;
-            if (d.n_split > 1) part_floats += size_t(g.mblk * g.nblk) * d.n_split * kPartStride;
-            out_tiles += g.mblk * g.nblk;
+            d.n_mblk = (tb + kMaxTiles - 1) / kMaxTiles;
+            d.n_nblk = static_cast<int32_t>((g.C + kBN - 1) / kBN);
+            d.chunks = static_cast<int32_t>(((g.T + 2 * kBK - 1) / (2 * kBK)) * 2);  // even
+            d.it_begin = iters;
+            d.otile_begin = otiles;
+            const int64_t ot = int64_t(d.n_mblk) * d.n_nblk;
+            otiles += ot;
+            iters += ot * d.chunks;
+            min_chunks = std::min<int64_t>(min_chunks, d.chunks);
         }
-        p.n_units = units;
-        p.per_xcd = (units + kXcds - 1) / kXcds;
+        if (p.n_groups == 0) break;
+        // One workgroup per CU; more (whole rounds) only if a slice would cross
+        // more tiles than the kernel tracks; never more slices than iterations.
+        int64_t P = cus;
+        const int64_t need = (iters + (kMaxSegs - 2) * min_chunks - 1) / ((kMaxSegs - 2) * min_chunks);
+        if (need > P) P = ((need + cus - 1) / cus) * cus;
+        P = std::min<int64_t>(P, iters / 2);
+        if (P >= kXcds) P -= P % kXcds;
+        p.n_wg = static_cast<int32_t>(P);
+        p.iters = iters;
         plan.launches.push_back(p);
-        plan.grid.push_back(p.per_xcd * kXcds);
+        plan.out_tiles.push_back(otiles);
+        plan.ws_bytes = std::max(plan.ws_bytes, size_t(2 * P) * size_t(kSlotFloats) * sizeof(float));
     }
-    // Workspace: counters for every output tile (256-B aligned), then partials.
-    plan.cnt_bytes = ((size_t(out_tiles) * 4 + 255) / 256) * 256;
-    plan.ws_bytes = part_floats == 0 ? 0 : plan.cnt_bytes + part_floats * sizeof(float);
+    for (DwParams &p : plan.launches) p.part = static_cast<float *>(ws);
     return plan;
 }
 
@@ -508,37 +669,35 @@ extern "C" {
 size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups) {
     sft::clear_error();
     if (validate(groups, n_groups) != SFT_OK) return static_cast<size_t>(-1);
-    return make_plan(groups, n_groups).ws_bytes;
+    return make_plan(groups, n_groups, nullptr).ws_bytes;
 }
 
 int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream) {
     sft::clear_error();
     if (int rc = validate(groups, n_groups)) return rc;
-    Plan plan = make_plan(groups, n_groups);
+    Plan plan = make_plan(groups, n_groups, ws);
     SFT_CHECK(ws_bytes >= plan.ws_bytes, SFT_ECAPACITY, "sft_masked_dw: workspace %zu < %zu bytes",
               ws_bytes, plan.ws_bytes);
+    SFT_CHECK(plan.ws_bytes == 0 || (ws && sft::aligned16(ws)), SFT_EINVAL,
+              "sft_masked_dw: workspace null or not 16-byte aligned");
     bool all_vec = true;
     for (int32_t gi = 0; gi < n_groups; ++gi)
         for (int32_t mi = 0; mi < groups[gi].n_mats; ++mi)
             if (groups[gi].mats[mi].n_active_tiles && groups[gi].mats[mi].R % 8) all_vec = false;
-    SFT_CHECK(plan.ws_bytes == 0 || (ws && sft::aligned16(ws)), SFT_EINVAL,
-              "sft_masked_dw: workspace null or not 16-byte aligned");
-    uint32_t *counters = plan.ws_bytes ? static_cast<uint32_t *>(ws) : nullptr;
-    float *partials =
-        plan.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(ws) + plan.cnt_bytes) : nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
     for (size_t li = 0; li < plan.launches.size(); ++li) {
-        DwParams &p = plan.launches[li];
-        p.counters = counters;
-        p.partials = partials;
-        SFT_CHECK(plan.grid[li] < (int64_t(1) << 31), SFT_ENOTSUP, "sft_masked_dw: grid too large");
+        const DwParams &p = plan.launches[li];
+        const dim3 grid(static_cast<uint32_t>(p.n_wg));
         if (all_vec)
-            hipLaunchKernelGGL(k_masked_dw<true>, dim3(static_cast<uint32_t>(plan.grid[li])), dim3(kThreads),
-                               0, static_cast<hipStream_t>(stream), p);
+            hipLaunchKernelGGL(k_masked_dw<true>, grid, dim3(kThreads), 0, st, p);
         else
-            hipLaunchKernelGGL(k_masked_dw<false>, dim3(static_cast<uint32_t>(plan.grid[li])), dim3(kThreads),
-                               0, static_cast<hipStream_t>(stream), p);
-        const hipError_t e = hipGetLastError();
+            hipLaunchKernelGGL(k_masked_dw<false>, grid, dim3(kThreads), 0, st, p);
+        hipError_t e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
+        hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(plan.out_tiles[li]), kMaxTiles * 32 / 8), dim3(256),
+                           0, st, p);
+        e = hipGetLastError();
+        SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: fix-up launch failed: %s", hipGetErrorString(e));
     }
     return SFT_OK;
 }

@@ -116,7 +116,11 @@ int sft_plan_rows(const uint8_t *active, sft_plan *plan) {
             }
         }
         plan->tile_bits[j] = word;
-        if (word) plan->active_tiles[nt++] = static_cast<int32_t>(j);
+        if (word) {
+            if (plan->active_bits) plan->active_bits[nt] = word;
+            if (plan->tile_first) plan->tile_first[nt] = static_cast<int32_t>(na - __builtin_popcount(word));
+            plan->active_tiles[nt++] = static_cast<int32_t>(j);
+        }
     }
     plan->n_active = na;
     plan->n_active_tiles = nt;

@@ -1,0 +1,54 @@
+"""The byte accounting against the page's printed worked example (section 3,
+tests/golden/memory_model.txt) and against hand-counted kernel traffic."""
+import os
+
+import pytest
+
+from sparse_full_weight_amd import accounting as acc
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "memory_model.txt")
+
+
+def _golden():
+    vals = {}
+    for line in open(GOLDEN):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = (x.strip() for x in line.split("=", 1))
+            vals[k] = float(v)
+    return vals
+
+
+def test_memory_model_matches_page_example():
+    g = _golden()
+    base, active = acc.state_bytes(g["n_params"], g["active_share"])
+    assert base == pytest.approx(g["helix_base_bytes"])
+    assert active == pytest.approx(g["helix_active_bytes"])
+    full = acc.full_ft_bytes(g["n_params"])
+    assert full == pytest.approx(g["full_ft_bytes"])
+    assert full / (base + active) == pytest.approx(g["full_ft_over_helix"], rel=0.05)
+    lora = acc.lora_bytes(g["n_params"], g["lora_adapter_params"])
+    assert lora / (base + active) == pytest.approx(g["lora_over_helix"], rel=0.1)
+    _, one_more = acc.state_bytes(g["n_params"], 0.01)
+    assert one_more == pytest.approx(g["per_percent_bytes"])
+
+
+def test_update_bytes_per_element():
+    # 24 bytes per active element with the fused write-back, 22 without
+    assert acc.update_work([(1, 1)]).bytes == 24 + 8
+    assert acc.update_work([(1, 1)], fused_writeback=False).bytes == 22 + 8
+
+
+def test_masked_dw_work_llama_layer():
+    T = 4096
+    groups = [(T, 4096, [(41, 2)] * 3), (T, 4096, [(41, 2)]), (T, 4096, [(110, 4)] * 2),
+              (T, 11008, [(41, 2)])]
+    w = acc.masked_dw_work(groups)
+    x = T * (3 * 4096 + 11008) * 2
+    dy = 18 * T * 32 * 2
+    dw = (41 * 4 * 4096 + 110 * 2 * 4096 + 41 * 11008) * 4
+    assert w.bytes == x + dy + dw
+    assert w.flops_useful == pytest.approx(16.58e9, rel=1e-3)
+    assert w.flops_issued == pytest.approx(22.95e9, rel=1e-3)
+    # a group with no active tile costs nothing (the tile skip)
+    assert acc.masked_dw_work([(T, 4096, [(0, 0)])]).bytes == 0

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     missing = [n for n in declared if not hasattr(L, n)]
     assert not missing, missing
     assert sorted(_lib.EXPORTS) == declared
-    assert _lib.sft_abi_version() == 1
+    assert _lib.sft_abi_version() == 2
 
 
 def test_conductor_matches_oracle_over_windows():
@@ -74,6 +74,9 @@ def test_plan_rows_matches_oracle(R):
     assert np.array_equal(p.tile_bits, o["bits"])
     assert np.array_equal(p.active_rows, o["active_rows"])
     assert np.array_equal(p.active_tiles, o["active_tiles"])
+    # per active tile: its bits, and where its first active row sits in the row list
+    assert np.array_equal(p.active_bits, o["bits"][o["active_tiles"]])
+    assert np.array_equal(p.tile_first, np.searchsorted(o["active_rows"], 32 * o["active_tiles"]))
 
 
 def test_plan_embedding_matches_oracle():
