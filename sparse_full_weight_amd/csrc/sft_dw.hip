@@ -253,23 +253,13 @@ __device__ __forceinline__ void mma_chunk(const uint16_t *stage, int tb, int wav
     }
 }
 
-template <bool kVecA>
-__global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t stage[2][kStageElems];
-    __shared__ Seg segs[kMaxSegs];
-    __shared__ TileDesc tdesc[kMaxSegs][kMaxTiles];
-    __shared__ int32_t s_nseg;
+// ---- shared by both masked-dW kernels -----------------------------------
 
+// The slice's segments (one per tile it touches) and their tile descriptors,
+// built once per workgroup into LDS.  Returns the slice's chunk count.
+__device__ int32_t build_segments(const DwParams &p, int64_t v, int64_t it_lo, int64_t it_hi, Seg *segs,
+                                  TileDesc (*tdesc)[kMaxTiles], int32_t *s_nseg) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    // Slice of this workgroup: the 32 workgroups of an XCD take neighbouring slices.
-    const int64_t b = blockIdx.x;
-    const int64_t v = (p.n_wg % kXcds == 0) ? (b % kXcds) * (p.n_wg / kXcds) + b / kXcds : b;
-    const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
-    if (it_lo >= it_hi) return;
-
-    // ---- the slice's segments (one per tile it touches)
     if (tid == 0) {
         int64_t it = it_lo;
         int n = 0;
@@ -283,30 +273,93 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             const int32_t k0 = static_cast<int32_t>(rel % G.chunks);
             const int64_t tile_end = G.it_begin + static_cast<int64_t>(tile + 1) * G.chunks;
             const int64_t end = min(tile_end, it_hi);
-            Seg s;
-            s.g = gi;
-            s.mb = tile / G.n_nblk;
-            s.nb = tile % G.n_nblk;
-            s.mt = min(kMaxTiles, G.n_tiles - s.mb * kMaxTiles);
-            s.k0 = k0;
-            s.j0 = j;
-            s.len = static_cast<int32_t>(end - it);
+            Seg sg;
+            sg.g = gi;
+            sg.mb = tile / G.n_nblk;
+            sg.nb = tile % G.n_nblk;
+            sg.mt = min(kMaxTiles, G.n_tiles - sg.mb * kMaxTiles);
+            sg.k0 = k0;
+            sg.j0 = j;
+            sg.len = static_cast<int32_t>(end - it);
             const bool whole = (k0 == 0 && end == tile_end);
-            s.slot = whole ? -1 : (n == 0 ? static_cast<int32_t>(2 * v) : static_cast<int32_t>(2 * v + 1));
-            segs[n++] = s;
-            j += s.len;
+            sg.slot = whole ? -1 : (n == 0 ? static_cast<int32_t>(2 * v) : static_cast<int32_t>(2 * v + 1));
+            segs[n++] = sg;
+            j += sg.len;
             it = end;
         }
-        s_nseg = n;
+        *s_nseg = n;
     }
     __syncthreads();
+    const int nseg = *s_nseg;
+    for (int x = tid; x < nseg * kMaxTiles; x += blockDim.x) {
+        const int sg = x / kMaxTiles, t = x % kMaxTiles;
+        if (t < segs[sg].mt) tdesc[sg][t] = make_tile_desc(p, p.g[segs[sg].g], segs[sg].mb, t);
+    }
+    __syncthreads();
+    return segs[nseg - 1].j0 + segs[nseg - 1].len;
+}
+
+// Epilogue of a segment for one wave: nt tiles (from tile tb) x 32 columns.
+// Accumulator layout of the 32x32 MFMA: lane l, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32.  A whole tile goes to dW_act; a
+// partial one to its slot, as compact active rows (row c = c-th active row of
+// the M-block).  The accumulators are cleared for the next segment.
+__device__ __forceinline__ void segment_epilogue(const DwParams &p, const Seg &S, const TileDesc *td, int nt,
+                                                 int tb, int wave, int lane, floatx16 (&acc)[4]) {
+    const DwGroupDev &G = p.g[S.g];
+    const int cl = (wave & 3) * 32 + (lane & 31);        // column inside the tile
+    const int64_t col = static_cast<int64_t>(S.nb) * kBN + cl;
+    const int row_base = 4 * (lane >> 5);
+    int prefix = 0;                                       // active rows of tiles before tb
+    for (int t = 0; t < tb; ++t) prefix += __builtin_popcount(td[t].bits);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if (t < nt) {
+            const TileDesc &d = td[tb + t];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r >> 2) + row_base + (r & 3);
+                if ((d.bits >> i) & 1u) {
+                    const int below = __builtin_popcount(d.bits & ((1u << i) - 1u));
+                    if (S.slot < 0) {
+                        if (col < G.C) d.out[static_cast<int64_t>(d.first + below) * G.C + col] = acc[t][r];
+                    } else {
+                        p.part[S.slot * kSlotFloats + (prefix + below) * kBN + cl] = acc[t][r];
+                    }
+                }
+            }
+            prefix += __builtin_popcount(d.bits);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+    }
+}
+
+// Slice of workgroup b: the 32 workgroups of an XCD take neighbouring slices.
+__device__ __forceinline__ int64_t slice_of(const DwParams &p) {
+    const int64_t b = blockIdx.x;
+    return (p.n_wg % kXcds == 0) ? (b % kXcds) * (p.n_wg / kXcds) + b / kXcds : b;
+}
+
+// ---- register-staged kernel: rows of dY that are not 16-byte aligned ------
+// (R % 8 != 0).  Each lane loads an 8x8 block into registers (element loads),
+// transposes it and writes it to LDS.
+
+template <bool kVecA>
+__global__ __launch_bounds__(kThreads, 1) void k_masked_dw_reg(const DwParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t stage[2][kStageElems];
+    __shared__ Seg segs[kMaxSegs];
+    __shared__ TileDesc tdesc[kMaxSegs][kMaxTiles];
+    __shared__ int32_t s_nseg;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t v = slice_of(p);
+    const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
+    if (it_lo >= it_hi) return;
+    const int32_t J = build_segments(p, v, it_lo, it_hi, segs, tdesc, &s_nseg);
     const int nseg = s_nseg;
-    for (int x = tid; x < nseg * kMaxTiles; x += kThreads) {
-        const int s = x / kMaxTiles, t = x % kMaxTiles;
-        if (t < segs[s].mt) tdesc[s][t] = make_tile_desc(p, p.g[segs[s].g], segs[s].mb, t);
-    }
-    __syncthreads();
-    const int32_t J = segs[nseg - 1].j0 + segs[nseg - 1].len;
 
     // ---- this lane's load task for local iteration j
     const int tg = tid & 7;   // token group: the 8 lanes of a store phase cover tokens 0..63
@@ -403,36 +456,289 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             case 2: pairs(std::integral_constant<int, 2>{}, tb, s, S.j0, S.len); break;
             default: pairs(std::integral_constant<int, 4>{}, tb, s, S.j0, S.len); break;
         }
-        // ---- epilogue of the segment.  Accumulator layout of the 32x32 MFMA:
-        // lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-        // A whole tile goes to dW_act; a partial one to its slot, as compact
-        // active rows (row c = c-th active row of the M-block).
+        segment_epilogue(p, S, tdesc[s], nt, tb, wave, lane, acc);
+    }
+}
+
+// ---- DMA kernel (every dY row 16-byte aligned, the common case) ----------
+//
+// Chunks go from HBM straight into a 3-stage LDS ring with the gfx950
+// global_load_lds_dwordx4 (lane l's 16 bytes land at base + 16*l), without
+// passing through registers, so two chunks are always in flight.  The MFMA
+// operands are read from the untransposed [token][column] layout with
+// ds_read_b64_tr_b16: in each group of 16 lanes, output lane 4a+b receives
+// element b of source lane 4e+a as its element e; when the 16 lanes point at
+// a 4-token x 16-column block, lane i receives column i for 4 consecutive
+// tokens, and two such reads give the 32x32x16 operand of a lane (column
+// l%32, tokens 8*(l/32) + 0..7).
+//
+// Stage layout (48 KB): 8 dY tiles x [64 tokens][32 columns] (4 KB each),
+// then X as [64 tokens][128 columns] (16 KB) with the 16-byte column groups
+// of token row r stored at group g ^ (2*(r%4)), which makes the transposing
+// reads of 4 consecutive rows hit distinct banks.  Lanes outside the
+// matrices (tokens >= T, columns >= R or C) copy 16 zero bytes.
+//
+// Per chunk j each wave: waits for its own copies of chunk j (vmcnt), joins a
+// barrier (all copies of chunk j landed; all reads of chunk j-1 finished),
+// issues the copies of chunk j+2 into the stage of chunk j-1, then multiplies
+// chunk j.  The waits are explicit (s_waitcnt with an immediate count) and the
+// barrier is a bare s_barrier: __syncthreads() carries a release fence that
+// would wait for every copy in flight.
+
+constexpr int kStages = 3;
+constexpr int kStageBytes = 48 * 1024;
+constexpr int kXOff = kMaxTiles * 4096;   // byte offset of the X block in a stage
+
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0, 0, 0, 0};
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const __attribute__((address_space(1))) void *>(reinterpret_cast<uintptr_t>(src)),
+        reinterpret_cast<__attribute__((address_space(3))) void *>(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds))),
+        16, 0, 0);
+}
+
+// Wave-uniform copies of values every lane holds alike (so that they live in
+// scalar registers and buffer resources need no per-lane loop).
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// 16 bytes per lane from a raw buffer [base, base + size) at byte offset
+// voff into LDS at lds + 16*lane; offsets at or beyond size read as zero.
+__device__ __forceinline__ void dma16_buf(const uint8_t *base, int32_t size, uint32_t voff, void *lds) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), static_cast<short>(0), size, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, reinterpret_cast<__attribute__((address_space(3))) void *>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds))),
+        16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) short4v *>(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p))));
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters free (gfx9 encoding).
+#define SFT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+// s_waitcnt lgkmcnt(0) leaving vmcnt and expcnt free.
+#define SFT_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+        case 0: SFT_WAIT_VMCNT(0); break;
+        case 1: SFT_WAIT_VMCNT(1); break;
+        case 2: SFT_WAIT_VMCNT(2); break;
+        case 3: SFT_WAIT_VMCNT(3); break;
+        case 4: SFT_WAIT_VMCNT(4); break;
+        case 5: SFT_WAIT_VMCNT(5); break;
+        default: SFT_WAIT_VMCNT(6); break;
+    }
+}
+
+// Copies one wave issues for a chunk of an M-block of mt tiles: the chunk is
+// 4*mt + 16 copies of 1 KB, dealt round-robin to the 8 waves.
+__device__ __forceinline__ int copies_of_wave(int mt, int wave) { return (4 * mt + 16 - wave + 7) / 8; }
+
+// MFMAs of one chunk for one wave: NT tiles (from tile tb) x 32 columns.
+template <int NT>
+__device__ __forceinline__ void mma_chunk_tr(const uint8_t *st, int tb, int wave, int lane, floatx16 (&acc)[4]) {
+    const int s16 = lane & 15;
+    const int half_col = ((lane >> 4) & 1) * 16;          // 16-column half of the 32
+    const int trow = 8 * (lane >> 5) + (s16 >> 2);          // token row inside a k-step, before +4h
+    const int c4 = 4 * (s16 & 3);
+    const uint16_t *A = reinterpret_cast<const uint16_t *>(st);
+    const uint16_t *X = reinterpret_cast<const uint16_t *>(st + kXOff);
+    // X: logical column = 32*(wave%4) + half_col + c4, group g = column / 8,
+    // stored at group g ^ (2*(row%4)); row%4 = s16 >> 2 for every row read here.
+    const int xcol = 32 * (wave & 3) + half_col + c4;
+    const int xoff = 8 * ((xcol >> 3) ^ (2 * (s16 >> 2))) + (xcol & 7);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int r0 = 16 * kk + trow;                      // tokens r0 (h = 0) and r0 + 4 (h = 1)
+        bf16x8 b;
+        {
+            const short4v lo = lds_tr16(X + r0 * kBN + xoff);
+            const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xoff);
+            b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint16_t *At = A + (tb + t) * 2048;       // [64 tokens][32 columns]
+            const short4v lo = lds_tr16(At + r0 * 32 + half_col + c4);
+            const short4v hi = lds_tr16(At + (r0 + 4) * 32 + half_col + c4);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_masked_dw_dma(const DwParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageBytes];
+    __shared__ Seg segs[kMaxSegs];
+    __shared__ TileDesc tdesc[kMaxSegs][kMaxTiles];
+    __shared__ int32_t s_nseg;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t v = slice_of(p);
+    const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
+    if (it_lo >= it_hi) return;
+    const int32_t J = build_segments(p, v, it_lo, it_hi, segs, tdesc, &s_nseg);
+    const int nseg = s_nseg;
+
+    // Copies of local chunk j (segment hint s0: j is in s0 or the next segment).
+    // Returns the number of copies this wave issued.
+    auto issue = [&](int32_t j, int s0) -> int {
+        if (j >= J) return 0;
+        int sg = s0;
+        sg += (sg + 1 < nseg && j >= segs[sg + 1].j0) ? 1 : 0;
+        const Seg &S = segs[sg];
         const DwGroupDev &G = p.g[S.g];
-        const int cl = (wave & 3) * 32 + (lane & 31);        // column inside the tile
-        const int64_t col = static_cast<int64_t>(S.nb) * kBN + cl;
-        const int row_base = 4 * (lane >> 5);
-        int prefix = 0;                                       // active rows of tiles before tb
-        for (int t = 0; t < tb; ++t) prefix += __builtin_popcount(tdesc[s][t].bits);
+        const uint32_t T = static_cast<uint32_t>(G.T);
+        const uint32_t t0 = static_cast<uint32_t>(S.k0 + (j - S.j0)) * kBK;
+        uint8_t *st = ring + (j % kStages) * kStageBytes;
+        const int nq = 4 * S.mt + 16;
+        int n = 0;
+        for (int q = wave; q < nq; q += 8, ++n) {
+            const void *src = g_zero16;
+            uint8_t *dst;
+            if (q < 4 * S.mt) {
+                // dY tile q/4, token rows 16*(q%4) + lane/4, 16-byte quarter lane%4
+                const TileDesc &d = tdesc[sg][q >> 2];
+                const uint32_t row = t0 + 16 * (q & 3) + (lane >> 2);
+                const int64_t col = d.col0 + 8 * (lane & 3);
+                if (row < T && col < d.R) src = d.dY + static_cast<uint64_t>(row) * d.R + col;
+                dst = st + (q >> 2) * 4096 + (q & 3) * 1024;
+            } else {
+                // X rows 4*b + lane/16; lane's slot lane%16 holds column group (lane%16) ^ 2*(row%4)
+                const int bq = q - 4 * S.mt;
+                const uint32_t row = t0 + 4 * bq + (lane >> 4);
+                const int grp = (lane & 15) ^ (2 * (lane >> 4));
+                const int64_t col = static_cast<int64_t>(S.nb) * kBN + 8 * grp;
+                if (row < T && col < G.C) src = G.X + static_cast<uint64_t>(row) * static_cast<uint64_t>(G.C) + col;
+                dst = st + kXOff + bq * 1024;
+            }
+            dma16(src, dst);   // lane l lands at dst + 16*l
+        }
+        return n;
+    };
+
+    // Per-segment copy descriptors of this wave.  Each copy reads through a
+    // buffer resource whose base and size advance by one chunk per chunk
+    // (scalar work only); a lane's offset inside the chunk is fixed for the
+    // segment.  Rows past T fall beyond the resource's size and columns past
+    // R or C get an offset beyond any size, so the hardware range check turns
+    // them into zeros.
+    constexpr int kMaxCopies = (4 * kMaxTiles + 16 + 7) / 8;   // per wave and chunk
+    constexpr uint32_t kOutside = 0x80000000u;                   // >= every resource size
+    const uint8_t *cp_base[kMaxCopies];   // uniform: chunk 0 of the segment
+    int64_t cp_rem[kMaxCopies];           // uniform: bytes from cp_base to the end of the matrix
+    int64_t cp_stride[kMaxCopies];        // uniform: bytes per chunk
+    uint32_t cp_dst[kMaxCopies];          // uniform: byte offset in the stage
+    uint32_t cp_voff[kMaxCopies];         // per lane: byte offset inside the chunk
+    int n_cp = 0;
+    auto describe = [&](int sg) {
+        const Seg &S = segs[sg];
+        const DwGroupDev &G = p.g[S.g];
+        const int64_t T = G.T;
+        const int64_t r0 = static_cast<int64_t>(S.k0) * kBK;
+        const int nq = 4 * S.mt + 16;
+        n_cp = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t < nt) {
-                const TileDesc &d = tdesc[s][tb + t];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = 8 * (r >> 2) + row_base + (r & 3);
-                    if ((d.bits >> i) & 1u) {
-                        const int below = __builtin_popcount(d.bits & ((1u << i) - 1u));
-                        if (S.slot < 0) {
-                            if (col < G.C) d.out[static_cast<int64_t>(d.first + below) * G.C + col] = acc[t][r];
-                        } else {
-                            p.part[S.slot * kSlotFloats + (prefix + below) * kBN + cl] = acc[t][r];
-                        }
-                    }
-                    acc[t][r] = 0.0f;
+        for (int k = 0; k < kMaxCopies; ++k) {
+            const int q = wave + 8 * k;
+            cp_base[k] = reinterpret_cast<const uint8_t *>(G.X);
+            cp_rem[k] = 0;
+            cp_stride[k] = 0;
+            cp_dst[k] = 0;
+            cp_voff[k] = kOutside;
+            if (q < nq) {
+                ++n_cp;
+                if (q < 4 * S.mt) {
+                    const TileDesc &d = tdesc[sg][q >> 2];
+                    const int64_t R = d.R;
+                    const int row_in = 16 * (q & 3) + (lane >> 2);
+                    const int col_in = 8 * (lane & 3);
+                    cp_base[k] = reinterpret_cast<const uint8_t *>(d.dY + r0 * R + d.col0);
+                    cp_rem[k] = (T - r0) * R * 2 - d.col0 * 2;
+                    cp_stride[k] = static_cast<int64_t>(kBK) * R * 2;
+                    cp_dst[k] = (q >> 2) * 4096 + (q & 3) * 1024;
+                    if (d.col0 + col_in < R) cp_voff[k] = static_cast<uint32_t>((row_in * R + col_in) * 2);
+                } else {
+                    const int bq = q - 4 * S.mt;
+                    const int64_t C = G.C;
+                    const int64_t c0 = static_cast<int64_t>(S.nb) * kBN;
+                    const int row_in = 4 * bq + (lane >> 4);
+                    const int grp = (lane & 15) ^ (2 * (lane >> 4));   // X swizzle
+                    cp_base[k] = reinterpret_cast<const uint8_t *>(G.X + r0 * C + c0);
+                    cp_rem[k] = (T - r0) * C * 2 - c0 * 2;
+                    cp_stride[k] = static_cast<int64_t>(kBK) * C * 2;
+                    cp_dst[k] = kXOff + bq * 1024;
+                    if (c0 + 8 * grp < C) cp_voff[k] = static_cast<uint32_t>((row_in * C + 8 * grp) * 2);
                 }
-                prefix += __builtin_popcount(d.bits);
+            }
+            cp_base[k] = reinterpret_cast<const uint8_t *>(uniform64(reinterpret_cast<uint64_t>(cp_base[k])));
+            cp_rem[k] = static_cast<int64_t>(uniform64(static_cast<uint64_t>(cp_rem[k])));
+            cp_stride[k] = static_cast<int64_t>(uniform64(static_cast<uint64_t>(cp_stride[k])));
+            cp_dst[k] = __builtin_amdgcn_readfirstlane(cp_dst[k]);
+        }
+        n_cp = __builtin_amdgcn_readfirstlane(n_cp);
+    };
+    // Copies of chunk c (0-based inside the described segment) into stage `st`.
+    auto issue_fast = [&](int32_t c, uint8_t *st) -> int {
+#pragma unroll
+        for (int k = 0; k < kMaxCopies; ++k) {
+            if (k < n_cp) {
+                const int64_t off = static_cast<int64_t>(c) * cp_stride[k];
+                const int64_t rem = cp_rem[k] - off;
+                const int32_t size = static_cast<int32_t>(rem <= 0 ? 0 : (rem > 0x7fffffff ? 0x7fffffff : rem));
+                dma16_buf(cp_base[k] + off, size, cp_voff[k], st + cp_dst[k]);
             }
         }
+        return n_cp;
+    };
+
+    floatx16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+    int n_next = issue(0, 0);      // copies of chunk j+1 still allowed in flight at the wait
+    n_next = issue(1, 0);
+    auto run = [&](auto nt_tag, int tb, int sg, int32_t j0, int32_t len) {
+        constexpr int NT = decltype(nt_tag)::value;
+        for (int32_t j = j0; j < j0 + len; ++j) {
+            // chunk j landed for this wave (only chunk j+1's copies may remain), and
+            // every read of chunk j-1 done; then the whole workgroup agrees.
+            SFT_WAIT_LGKM0();
+            wait_vmcnt(n_next);
+            __builtin_amdgcn_s_barrier();
+            uint8_t *st2 = ring + ((j + 2) % kStages) * kStageBytes;
+            n_next = (j + 2 < j0 + len) ? issue_fast(j + 2 - j0, st2) : issue(j + 2, sg);
+            mma_chunk_tr<NT>(ring + (j % kStages) * kStageBytes, tb, wave, lane, acc);
+        }
+    };
+    for (int sg = 0; sg < nseg; ++sg) {
+        const Seg &S = segs[sg];
+        describe(sg);
+        const int half = wave >> 2;
+        const int nt = half ? S.mt / 2 : (S.mt + 1) / 2;   // this wave's tiles
+        const int tb = half ? (S.mt + 1) / 2 : 0;
+        switch (nt) {
+            case 0:
+            case 1:
+            case 2: run(std::integral_constant<int, 2>{}, tb, sg, S.j0, S.len); break;
+            default: run(std::integral_constant<int, 4>{}, tb, sg, S.j0, S.len); break;
+        }
+        segment_epilogue(p, S, tdesc[sg], nt, tb, wave, lane, acc);
     }
 }
 
@@ -689,9 +995,9 @@ int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t
         const DwParams &p = plan.launches[li];
         const dim3 grid(static_cast<uint32_t>(p.n_wg));
         if (all_vec)
-            hipLaunchKernelGGL(k_masked_dw<true>, grid, dim3(kThreads), 0, st, p);
+            hipLaunchKernelGGL(k_masked_dw_dma, grid, dim3(kThreads), 0, st, p);
         else
-            hipLaunchKernelGGL(k_masked_dw<false>, grid, dim3(kThreads), 0, st, p);
+            hipLaunchKernelGGL(k_masked_dw_reg<false>, grid, dim3(kThreads), 0, st, p);
         hipError_t e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
         hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(plan.out_tiles[li]), kMaxTiles * 32 / 8), dim3(256),
