@@ -546,8 +546,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 __device__ __forceinline__ int copies_of_wave(int mt, int wave) { return (4 * mt + 16 - wave + 7) / 8; }
 
 // MFMAs of one chunk for one wave: NT tiles (from tile tb) x 32 columns.
-template <int NT>
-__device__ __forceinline__ void mma_chunk_tr(const uint8_t *st, int tb, int wave, int lane, floatx16 (&acc)[4]) {
+// after_step(kk) runs after the MFMAs of k-step kk are issued: the caller
+// issues the next chunks' copies there, so that the vector-memory pipe and
+// the matrix cores work at the same time.
+template <int NT, typename AfterStep>
+__device__ __forceinline__ void mma_chunk_tr(const uint8_t *st, int tb, int wave, int lane, floatx16 (&acc)[4],
+                                             AfterStep after_step) {
     const int s16 = lane & 15;
     const int half_col = ((lane >> 4) & 1) * 16;          // 16-column half of the 32
     const int trow = 8 * (lane >> 5) + (s16 >> 2);          // token row inside a k-step, before +4h
@@ -558,22 +562,34 @@ __device__ __forceinline__ void mma_chunk_tr(const uint8_t *st, int tb, int wave
     // stored at group g ^ (2*(row%4)); row%4 = s16 >> 2 for every row read here.
     const int xcol = 32 * (wave & 3) + half_col + c4;
     const int xoff = 8 * ((xcol >> 3) ^ (2 * (s16 >> 2))) + (xcol & 7);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+    const uint16_t *Ab = A + tb * 2048 + half_col + c4;
+    auto frags = [&](int kk, bf16x8 &b, bf16x8 (&a)[NT > 0 ? NT : 1]) {
         const int r0 = 16 * kk + trow;                      // tokens r0 (h = 0) and r0 + 4 (h = 1)
-        bf16x8 b;
-        {
-            const short4v lo = lds_tr16(X + r0 * kBN + xoff);
-            const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xoff);
-            b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+        const short4v blo = lds_tr16(X + r0 * kBN + xoff);
+        const short4v bhi = lds_tr16(X + (r0 + 4) * kBN + xoff);
+        b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const uint16_t *At = A + (tb + t) * 2048;       // [64 tokens][32 columns]
-            const short4v lo = lds_tr16(At + r0 * 32 + half_col + c4);
-            const short4v hi = lds_tr16(At + (r0 + 4) * 32 + half_col + c4);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+            const short4v lo = lds_tr16(Ab + t * 2048 + r0 * 32);
+            const short4v hi = lds_tr16(Ab + t * 2048 + (r0 + 4) * 32);
+            a[t] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    bf16x8 b_cur, a_cur[NT > 0 ? NT : 1];
+    frags(0, b_cur, a_cur);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        bf16x8 b_nxt, a_nxt[NT > 0 ? NT : 1];
+        if (kk + 1 < kBK / 16) frags(kk + 1, b_nxt, a_nxt);   // next k-step's fragments in flight
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[t], b_cur, acc[t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        after_step(kk);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < kBK / 16) {
+            b_cur = b_nxt;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) a_cur[t] = a_nxt[t];
         }
     }
 }
@@ -691,11 +707,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw_dma(const DwParams p)
         }
         n_cp = __builtin_amdgcn_readfirstlane(n_cp);
     };
-    // Copies of chunk c (0-based inside the described segment) into stage `st`.
-    auto issue_fast = [&](int32_t c, uint8_t *st) -> int {
+    // Copies [k_lo, k_hi) of chunk c (0-based inside the described segment) into stage `st`.
+    auto issue_fast = [&](int32_t c, uint8_t *st, int k_lo, int k_hi) -> int {
 #pragma unroll
         for (int k = 0; k < kMaxCopies; ++k) {
-            if (k < n_cp) {
+            if (k >= k_lo && k < k_hi && k < n_cp) {
                 const int64_t off = static_cast<int64_t>(c) * cp_stride[k];
                 const int64_t rem = cp_rem[k] - off;
                 const int32_t size = static_cast<int32_t>(rem <= 0 ? 0 : (rem > 0x7fffffff ? 0x7fffffff : rem));
@@ -722,8 +738,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw_dma(const DwParams p)
             wait_vmcnt(n_next);
             __builtin_amdgcn_s_barrier();
             uint8_t *st2 = ring + ((j + 2) % kStages) * kStageBytes;
-            n_next = (j + 2 < j0 + len) ? issue_fast(j + 2 - j0, st2) : issue(j + 2, sg);
-            mma_chunk_tr<NT>(ring + (j % kStages) * kStageBytes, tb, wave, lane, acc);
+            const bool fast = j + 2 < j0 + len;
+            if (!fast) n_next = issue(j + 2, sg);   // crosses into the next segment (rare)
+            // copies of chunk j+2 spread over the four k-steps: 2, 2, 1, 1
+            mma_chunk_tr<NT>(ring + (j % kStages) * kStageBytes, tb, wave, lane, acc, [&](int kk) {
+                if (!fast) return;
+                const int lo = kk < 2 ? 2 * kk : kk + 2, hi = kk < 2 ? 2 * kk + 2 : kk + 3;
+                issue_fast(j + 2 - j0, st2, lo, hi);
+            });
+            if (fast) n_next = n_cp;
         }
     };
     for (int sg = 0; sg < nseg; ++sg) {
