@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 2
+#define SFT_ABI_VERSION 3
 
 enum {
     SFT_OK = 0,
@@ -167,13 +167,15 @@ int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *b
 
 /*
  * One matrix of a masked-dW group.  dY is bf16 [T x R] (gradient at the
- * matrix's output); the plan arrays are device copies of the active-tile part
- * of an sft_plan of this matrix's mask; dW_act is fp32 [n_active x C], row k
- * = the k-th active row.
+ * matrix's output); the plan arrays are device copies of an sft_plan of this
+ * matrix's mask; dW_act is fp32 [n_active x C], row k = the k-th active row.
+ * active_rows is read by the packed layout only, the tile arrays by the tile
+ * layout only (the other pointers may be NULL).
  */
 typedef struct sft_dw_mat {
     const uint16_t *dY;
     int64_t R;
+    const int32_t *active_rows;  /* device [n_active] */
     const int32_t *active_tiles; /* device [n_active_tiles] */
     const uint32_t *active_bits; /* device [n_active_tiles] */
     const int32_t *tile_first;   /* device [n_active_tiles] */
@@ -182,17 +184,33 @@ typedef struct sft_dw_mat {
     float *dW_act;               /* device [n_active x C] */
 } sft_dw_mat;
 
+/*
+ * How a group's rows are laid out on the matrix cores (the result is the
+ * same, bit for bit, for integer-exact inputs and within fp32 summation order
+ * otherwise):
+ *   SFT_DW_TILES   every active 32-row tile is multiplied whole and its
+ *                  inactive rows are dropped at the store (section 2.2 as
+ *                  the page states it);
+ *   SFT_DW_PACKED  the active rows of the group are packed 32 to a tile
+ *                  before the product, so a tile with one active row costs
+ *                  1/32 of a whole tile.  Inactive tiles are skipped in both.
+ */
+enum { SFT_DW_TILES = 0, SFT_DW_PACKED = 1 };
+
 /* Matrices that read the same layer input X (bf16 [T x C]), e.g. q/k/v. */
 typedef struct sft_dw_group {
     const uint16_t *X;
     int64_t T, C;
     int32_t n_mats;
+    int32_t layout;         /* SFT_DW_TILES or SFT_DW_PACKED */
     const sft_dw_mat *mats; /* host array of n_mats */
 } sft_dw_group;
 
 /*
- * Workspace bytes sft_masked_dw needs for these groups (0 is possible): the
- * split-K partial rows when the token axis is split to fill the GPU.
+ * Workspace bytes sft_masked_dw needs for these groups: the gathered dY
+ * columns of the active rows (the matrix-core operand, token-contiguous),
+ * their output map, and the split-K partial rows when the token axis is
+ * split to fill the GPU.
  * Returns (size_t)-1 and sets the error message on invalid groups.
  */
 size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
@@ -206,7 +224,8 @@ size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
  *   ws / ws_bytes  device scratch of at least sft_masked_dw_workspace()
  *                  bytes (16-byte aligned; no initialisation needed).  Calls
  *                  that share a workspace must be ordered on one stream.
- * Limits: T >= 1, T < 2^31, C % 8 == 0, R < 2^31.  Results are deterministic
+ * Limits: T >= 1, T < 2^31, C % 8 == 0, R < 2^31, n_active < 2^24, at most
+ * 16 matrices per group.  Results are deterministic
  * (a fixed summation order for every launch configuration the same inputs
  * produce).
  * Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_ECAPACITY (ws too small),

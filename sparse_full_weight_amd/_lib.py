@@ -48,14 +48,18 @@ class CPlan(C.Structure):
 
 
 class CDwMat(C.Structure):
-    _fields_ = [("dY", C.c_void_p), ("R", C.c_int64), ("active_tiles", C.c_void_p), ("active_bits", C.c_void_p),
-                ("tile_first", C.c_void_p), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
-                ("dW_act", C.c_void_p)]
+    _fields_ = [("dY", C.c_void_p), ("R", C.c_int64), ("active_rows", C.c_void_p), ("active_tiles", C.c_void_p),
+                ("active_bits", C.c_void_p), ("tile_first", C.c_void_p), ("n_active", C.c_int64),
+                ("n_active_tiles", C.c_int64), ("dW_act", C.c_void_p)]
+
+
+SFT_DW_TILES = 0    # whole active 32-row tiles on the matrix cores, inactive rows dropped at the store
+SFT_DW_PACKED = 1   # active rows packed 32 to a tile before the product
 
 
 class CDwGroup(C.Structure):
     _fields_ = [("X", C.c_void_p), ("T", C.c_int64), ("C", C.c_int64), ("n_mats", C.c_int32),
-                ("mats", C.POINTER(CDwMat))]
+                ("layout", C.c_int32), ("mats", C.POINTER(CDwMat))]
 
 
 class CAdam(C.Structure):
@@ -271,6 +275,7 @@ class DwMat:
 class DwGroup:
     X: "object"             # bf16 [T x C] GPU tensor
     mats: Sequence[DwMat]
+    layout: int = SFT_DW_PACKED
 
 
 def _c_groups(groups: Sequence[DwGroup]):
@@ -281,11 +286,11 @@ def _c_groups(groups: Sequence[DwGroup]):
         T, Cc = g.X.shape
         mats = (CDwMat * max(len(g.mats), 1))()
         for j, m in enumerate(g.mats):
-            mats[j] = CDwMat(_dev(m.dY, torch.bfloat16), m.plan.rows, _dev(m.plan.active_tiles),
-                             _dev(m.plan.active_bits), _dev(m.plan.tile_first), m.plan.n_active,
-                             m.plan.n_active_tiles, _dev(m.dW_act, torch.float32))
+            mats[j] = CDwMat(_dev(m.dY, torch.bfloat16), m.plan.rows, _dev(m.plan.active_rows),
+                             _dev(m.plan.active_tiles), _dev(m.plan.active_bits), _dev(m.plan.tile_first),
+                             m.plan.n_active, m.plan.n_active_tiles, _dev(m.dW_act, torch.float32))
         keep.append(mats)
-        arr[i] = CDwGroup(_dev(g.X, torch.bfloat16), T, Cc, len(g.mats), mats)
+        arr[i] = CDwGroup(_dev(g.X, torch.bfloat16), T, Cc, len(g.mats), g.layout, mats)
     return arr, keep
 
 

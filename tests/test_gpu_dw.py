@@ -20,7 +20,10 @@ pytestmark = pytest.mark.gpu
 CANARY = float("nan")
 
 
-def _run(groups_np, repeat=1):
+LAYOUTS = pytest.mark.parametrize("layout", [_lib.SFT_DW_TILES, _lib.SFT_DW_PACKED], ids=["tiles", "packed"])
+
+
+def _run(groups_np, repeat=1, layout=_lib.SFT_DW_PACKED):
     """groups_np: list of (X_bits [T x C], [(dY_bits [T x R], mask [R]), ...])."""
     groups, outs, plans = [], [], []
     for X, mats in groups_np:
@@ -32,7 +35,7 @@ def _run(groups_np, repeat=1):
             ms.append(_lib.DwMat(bf16_dev(dY), plan.to_device(), buf[:plan.n_active]))
             outs.append(buf)
             plans.append(plan)
-        groups.append(_lib.DwGroup(bf16_dev(X), ms))
+        groups.append(_lib.DwGroup(bf16_dev(X), ms, layout))
     nbytes = _lib.sft_masked_dw_workspace(groups)
     ws = torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device="cuda") if nbytes else None
     results = []
@@ -46,8 +49,8 @@ def _run(groups_np, repeat=1):
     return results[-1] if repeat == 1 else results, plans
 
 
-def _check(groups_np, exact=False, repeat=1):
-    res, plans = _run(groups_np, repeat)
+def _check(groups_np, exact=False, repeat=1, layout=_lib.SFT_DW_PACKED):
+    res, plans = _run(groups_np, repeat, layout)
     if repeat > 1:
         for r in res[1:]:
             for a, b in zip(res[0], r):
@@ -69,53 +72,59 @@ def _mask_rows(R, rows):
     return synth.mask_from_rows(R, np.asarray(rows, np.int64))
 
 
-def test_dw_small_projection_10pct_clustered(gpu_lib):
+@LAYOUTS
+def test_dw_small_projection_10pct_clustered(gpu_lib, layout):
     # 512 x 512 projection, 256 tokens, 10% of rows active in clustered tiles
     T, R, C = 256, 512, 512
     X = synth.normal_bf16((T, C), 1.0, 1001)
     dY = synth.normal_bf16((T, R), 0.01, 1002)
     mask = _mask_rows(R, synth.clustered_rows(R, round(0.10 * R), 1501))
-    _check([(X, [(dY, mask)])], repeat=2)
+    _check([(X, [(dY, mask)])], repeat=2, layout=layout)
 
 
-def test_dw_ragged_everything(gpu_lib):
+@LAYOUTS
+def test_dw_ragged_everything(gpu_lib, layout):
     # R % 32 != 0 and R % 8 != 0 (unaligned dY rows), C not a multiple of 128,
     # T not a multiple of the token chunk; last row active
     T, R, C = 100, 70, 200
     X = synth.normal_bf16((T, C), 1.0, 1011)
     dY = synth.normal_bf16((T, R), 0.01, 1012)
     mask = _mask_rows(R, [0, 5, 31, 32, 40, 63, 64, 69])
-    _check([(X, [(dY, mask)])])
+    _check([(X, [(dY, mask)])], layout=layout)
 
 
-def test_dw_single_token_is_exact_outer_product(gpu_lib):
+@LAYOUTS
+def test_dw_single_token_is_exact_outer_product(gpu_lib, layout):
     T, R, C = 1, 96, 136
     X = synth.normal_bf16((T, C), 1.0, 1021)
     dY = synth.normal_bf16((T, R), 0.01, 1022)
     mask = _mask_rows(R, [1, 2, 33, 95])
-    _check([(X, [(dY, mask)])], exact=True)
+    _check([(X, [(dY, mask)])], exact=True, layout=layout)
 
 
-def test_dw_integer_inputs_exact_under_split(gpu_lib):
+@LAYOUTS
+def test_dw_integer_inputs_exact_under_split(gpu_lib, layout):
     # small integers: every partial sum is exact, so any order or split agrees
     T, R, C = 2048, 64, 128
     X = synth.integer_bf16((T, C), -3, 3, 1031)
     dY = synth.integer_bf16((T, R), -3, 3, 1032)
     mask = _mask_rows(R, list(range(0, 64, 3)))
-    _check([(X, [(dY, mask)])], exact=True, repeat=2)
+    _check([(X, [(dY, mask)])], exact=True, repeat=2, layout=layout)
 
 
-def test_dw_empty_full_and_one_per_tile(gpu_lib):
+@LAYOUTS
+def test_dw_empty_full_and_one_per_tile(gpu_lib, layout):
     T, R, C = 128, 256, 64
     X = synth.normal_bf16((T, C), 1.0, 1041)
     dY = synth.normal_bf16((T, R), 0.01, 1042)
     empty = np.zeros(R, np.uint8)
     full = np.ones(R, np.uint8)
     one = _mask_rows(R, synth.one_per_tile_rows(R, 1543))
-    _check([(X, [(dY, empty), (dY, full), (dY, one)])])
+    _check([(X, [(dY, empty), (dY, full), (dY, one)])], layout=layout)
 
 
-def test_dw_groups_share_x_and_span_mblocks(gpu_lib):
+@LAYOUTS
+def test_dw_groups_share_x_and_span_mblocks(gpu_lib, layout):
     # three matrices on one input with 11 active tiles (two M-blocks), plus a
     # second group with its own input
     T, C = 192, 264
@@ -125,16 +134,44 @@ def test_dw_groups_share_x_and_span_mblocks(gpu_lib):
     for i, (R, k) in enumerate([(320, 100), (128, 40), (96, 10)]):
         mats1.append((synth.normal_bf16((T, R), 0.01, 1060 + i), _mask_rows(R, synth.clustered_rows(R, k, 1560 + i))))
     mats2 = [(synth.normal_bf16((T, 200), 0.01, 1070), _mask_rows(200, synth.clustered_rows(200, 20, 1570)))]
-    _check([(X1, mats1), (X2, mats2)])
+    _check([(X1, mats1), (X2, mats2)], layout=layout)
 
 
-def test_dw_long_token_axis_split(gpu_lib):
+@LAYOUTS
+def test_dw_long_token_axis_split(gpu_lib, layout):
     # few tiles and many tokens: the launch splits the token axis many ways
     T, R, C = 4096, 128, 128
     X = synth.normal_bf16((T, C), 1.0, 1081)
     dY = synth.normal_bf16((T, R), 0.01, 1082)
     mask = _mask_rows(R, synth.clustered_rows(R, 70, 1581))
-    _check([(X, [(dY, mask)])], repeat=3)
+    _check([(X, [(dY, mask)])], repeat=3, layout=layout)
+
+
+def test_dw_layouts_agree_bitwise_on_integer_inputs(gpu_lib):
+    # packed and whole-tile layouts sum the same exact products: bit-identical
+    T, R, C = 640, 200, 136
+    X = synth.integer_bf16((T, C), -3, 3, 1091)
+    dY = synth.integer_bf16((T, R), -3, 3, 1092)
+    mask = _mask_rows(R, synth.one_per_tile_rows(R, 1591))
+    a, plans = _run([(X, [(dY, mask)])], layout=_lib.SFT_DW_TILES)
+    b, _ = _run([(X, [(dY, mask)])], layout=_lib.SFT_DW_PACKED)
+    n = plans[0].n_active
+    assert np.array_equal(a[0][:n], b[0][:n])
+    assert np.array_equal(a[0][:n], oracle.masked_dw(dY, X, plans[0].active_rows))
+
+
+@LAYOUTS
+def test_dw_more_groups_than_one_launch(gpu_lib, layout):
+    # ten groups of one matrix: the call splits into two launches that reuse
+    # one workspace in stream order
+    T = 320
+    groups = []
+    for i in range(10):
+        C, R = 64 + 8 * i, 40 + 13 * i
+        X = synth.normal_bf16((T, C), 1.0, 1200 + i)
+        dY = synth.normal_bf16((T, R), 0.01, 1300 + i)
+        groups.append((X, [(dY, _mask_rows(R, synth.clustered_rows(R, 5 + i, 1400 + i)))]))
+    _check(groups, layout=layout)
 
 
 def test_dw_rejects_bad_shapes(gpu_lib):
