@@ -18,14 +18,15 @@
 //      is 1 KB and lane l reads bytes 16l..16l+15.  Each packed row's
 //      destination (matrix, row of dW_act) or -1 goes to a row map.
 //   2. Product.  Matrices that read the same X (q/k/v; gate/up) form a group;
-//      up to 8 packed tiles of a group (an M-block) share every load of an X
+//      up to 4 packed tiles of a group (an M-block) share every load of an X
 //      block of 64 tokens x 128 columns.  X is the dominant HBM stream.  It
 //      goes from HBM straight into an 8-stage LDS ring (buffer_load ... lds,
 //      16 bytes per lane), so 7 chunks (112 KB) are in flight per CU, and the
 //      MFMA operand is read from the [token][column] layout with
 //      ds_read_b64_tr_b16.  The dY operand goes from the gather buffer
-//      straight into registers, 3 chunks ahead.  Wave w owns packed tile w of
-//      the M-block and all 128 columns.  The launch is persistent and
+//      straight into registers, 3 chunks ahead.  Two or four waves share a
+//      packed tile, each taking two or one of its four 32-column blocks, so
+//      that every SIMD runs two waves.  The launch is persistent and
 //      stream-K: one 8-wave workgroup per CU takes an equal slice of the
 //      (output tile, chunk) iteration space.
 //   3. Fix-up.  Output tiles cut by slice boundaries leave partial sums in
@@ -49,7 +50,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
 
 constexpr int kBN = 128;             // columns per output tile: 4 MFMA column blocks of 32
-constexpr int kMaxTiles = 8;         // packed tiles per M-block, one per wave
+constexpr int kMaxTiles = 4;         // packed tiles per M-block
 constexpr int kBK = 64;              // tokens per chunk: 4 MFMA k-steps of 16
 constexpr int kRound = 8;            // chunks per pipeline round (segments are whole rounds)
 constexpr int kThreads = 512;        // 8 waves
@@ -66,8 +67,8 @@ constexpr int kGatherTokens = 256;
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset beyond every resource size
 // Memory instructions a wave issues per chunk: 4 operand loads + 2 X copies.
 constexpr int kLoadsA = 4, kCopiesX = 2;
-// Stores a wave issues per segment epilogue: 4 column blocks x 4 float4.
-constexpr int kEpiStores = 16;
+// Stores a wave issues per segment epilogue: up to 2 column blocks x 4 float4.
+constexpr int kEpiStores = 8;
 // Loads a wave may leave in flight when chunk j's operands must have landed:
 // the copies issued after the operand loads of chunk j, in the same round,
 // and the two rounds that follow.
@@ -252,7 +253,7 @@ __device__ __forceinline__ void dma16_buf(const uint8_t *base, int32_t size, uin
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), static_cast<short>(0), size, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)(lds), 16, voff, 0, 0, 0);
+        r, (__attribute__((address_space(3))) void *)(lds), 16, voff, 0, 0, 2);
 }
 
 __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
@@ -276,6 +277,7 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 // the compiler's own waits stay exact as well.
 __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     __shared__ int32_t codes[kMaxSegs][kMaxTiles * 32];
+    __shared__ DwGroupDev gs[kMaxGroups];   // the group table, indexable at run time
     __shared__ float *outp[kMaxMats];
     __shared__ Seg segs[kMaxSegs];
     __shared__ int32_t s_nseg;
@@ -287,6 +289,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
     if (it_lo >= it_hi) return;
 
+    // ---- the group table (constant indices only: a run-time index into the
+    // kernel argument would make the compiler copy it to scratch)
+    if (tid == 0) {
+#pragma unroll
+        for (int g = 0; g < kMaxGroups; ++g)
+            if (g < p.n_groups) gs[g] = p.g[g];
+#pragma unroll
+        for (int m = 0; m < kMaxMats; ++m) outp[m] = p.m[m].out;
+    }
+    __syncthreads();
+
     // ---- the slice's segments (one per output tile it touches)
     if (tid == 0) {
         int64_t it = it_lo;
@@ -294,8 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         int32_t j = 0;
         while (it < it_hi && n < kMaxSegs) {
             int gi = 0;
-            while (gi + 1 < p.n_groups && it >= p.g[gi + 1].it_begin) ++gi;
-            const DwGroupDev &G = p.g[gi];
+            while (gi + 1 < p.n_groups && it >= gs[gi + 1].it_begin) ++gi;
+            const DwGroupDev &G = gs[gi];
             const int64_t rel = it - G.it_begin;
             const int32_t tile = static_cast<int32_t>(rel / G.chunks);
             const int32_t k0 = static_cast<int32_t>(rel % G.chunks);
@@ -318,13 +331,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         }
         s_nseg = n;
     }
-    if (tid == 0)
-        for (int m = 0; m < kMaxMats; ++m) outp[m] = p.m[m].out;
     __syncthreads();
     const int nseg = s_nseg;
     for (int sg = 0; sg < nseg; ++sg) {
         const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[sg].g);
-        const int32_t *map = p.g[gsg].rowmap + segs[sg].p0 * 32;
+        const int32_t *map = gs[gsg].rowmap + segs[sg].p0 * 32;
         const int32_t n = segs[sg].mt * 32;
         for (int r = tid; r < kMaxTiles * 32; r += kThreads) codes[sg][r] = r < n ? map[r] : -1;
     }
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     uint32_t x_voff[kCopiesX];
     auto describe_x = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
-        const DwGroupDev &G = p.g[S.g];
+        const DwGroupDev &G = gs[S.g];
         const int64_t C = G.C, c0 = static_cast<int64_t>(S.nb) * kBN, r0 = static_cast<int64_t>(S.k0) * kBK;
         x_base = reinterpret_cast<const uint8_t *>(uniform64(reinterpret_cast<uint64_t>(G.X + r0 * C + c0)));
         x_rem = static_cast<int64_t>(uniform64(static_cast<uint64_t>((G.T - r0) * C * 2 - c0 * 2)));
@@ -372,64 +383,67 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         dma16_buf(x_base + (jx < J ? off : 0), size, x_voff[k], stage + (wave + 8 * k) * 1024);
     };
 
+    // ---- wave layout of a segment with mt packed tiles: NC = 1 or 2 column
+    // blocks per wave, so that 4/NC waves share a tile and the SIMDs run two
+    // waves each (one wave per SIMD is bound by the latency of its operand
+    // reads).  Wave w takes tile w / (4/NC) and column blocks
+    // (w % (4/NC)) * NC .. + NC - 1; waves past the tiles only copy.  (Four
+    // column blocks per wave and 8-tile M-blocks would need more than the 256
+    // registers a wave has at two waves per SIMD.)
+    auto nc_of = [](int mt) __attribute__((always_inline)) { return mt <= 2 ? 1 : 2; };
+
     // ---- dY operand: 4 KB per (packed tile, chunk); k-step kk is the 1 KB
-    // at 512*kk elements, lane l's 16 bytes at 8*l.  Waves past the M-block's
-    // tiles load tile 0 again (and ignore it); chunks past the slice reload
-    // its last chunk, so every wave issues the same loads every chunk.
+    // at 512*kk elements, lane l's 16 bytes at 8*l.  Loads go through a buffer
+    // resource whose size is 0 for waves without a tile and for chunks past
+    // the slice: the load is still issued (every wave issues the same memory
+    // instructions every chunk) but touches no memory.
     int sa = 0;
     const uint16_t *a_base = nullptr;
-    int32_t a_j0 = 0, a_last = 0;
+    int32_t a_j0 = 0;
+    bool a_live = false;
     auto describe_a = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
-        const DwGroupDev &G = p.g[S.g];
-        const int t = wave < S.mt ? wave : 0;
+        const DwGroupDev &G = gs[S.g];
+        const int t = wave / (4 / nc_of(S.mt));
+        a_live = t < S.mt;
         a_base = reinterpret_cast<const uint16_t *>(uniform64(reinterpret_cast<uint64_t>(
-            G.at + (static_cast<int64_t>(S.p0 + t) * (G.Tp / 8) + 8 * static_cast<int64_t>(S.k0)) * 256)));
+            G.at + (static_cast<int64_t>(S.p0 + (a_live ? t : 0)) * (G.Tp / 8) + 8 * static_cast<int64_t>(S.k0)) * 256)));
         a_j0 = __builtin_amdgcn_readfirstlane(S.j0);
-        a_last = __builtin_amdgcn_readfirstlane(S.len - 1);
     };
     auto issue_a = [&](int32_t ja, bf16x8 (&buf)[4]) __attribute__((always_inline)) {
         if (ja < J && sa + 1 < nseg && ja >= segs[sa + 1].j0) {
             ++sa;
             describe_a(sa);
         }
-        const int32_t c = min(ja - a_j0, a_last);
-        const uint16_t *ptr = a_base + static_cast<int64_t>(c) * 2048 + 8 * lane;
+        const bool live = a_live && ja < J;
+        const uint16_t *base = a_base + (live ? static_cast<int64_t>(ja - a_j0) * 2048 : 0);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(base), static_cast<short>(0), live ? 4096 : 0, 0x00020000);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            buf[kk] = *reinterpret_cast<gbf16x8 *>(reinterpret_cast<uintptr_t>(ptr + 512 * kk));
+            buf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane + 1024 * kk, 0, 0));
     };
 
     // ---- operand reads of X: lane l takes column l%32 of a 32-column block,
     // tokens 8*(l/32) + 0..7 of a k-step, by two transposing reads of 4 rows.
+    // Column group g of token row r sits at group g ^ 2*(r%4); here r%4 =
+    // (l%16)/4 for every row a lane reads.
     const int s16 = lane & 15;
     const int trow = 8 * (lane >> 5) + (s16 >> 2);
-    int xoff[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const int xcol = 32 * cb + ((lane >> 4) & 1) * 16 + 4 * (s16 & 3);
-        xoff[cb] = 8 * ((xcol >> 3) ^ (2 * (s16 >> 2))) + (xcol & 7);
-    }
-
-    // Accumulators: acc[cb] = X-block^T . dY-tile, so lane l register r holds
-    // column 32*cb + 8*(r/4) + 4*(l/32) + r%4 of packed row l%32: four
-    // consecutive columns per register quad, stored as one float4.
-    floatx16 acc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
-
-    // Transposing reads of the X operand of k-step kk (4 column blocks).
-    auto bfrag = [&](const uint16_t *X, int kk, bf16x8 (&b)[4]) __attribute__((always_inline)) {
-        const int r0 = 16 * kk + trow;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const short4v lo = lds_tr16(X + r0 * kBN + xoff[cb]);
-            const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xoff[cb]);
-            b[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+    const int xcp = ((lane >> 4) & 1) * 16 + 4 * (s16 & 3);   // column inside a 32-column block
+    auto xoff_of = [&](int cb) __attribute__((always_inline)) {
+        return 8 * ((4 * cb + (xcp >> 3)) ^ (2 * (s16 >> 2))) + (xcp & 7);
     };
+
+    // Accumulators: acc[c] = X-block^T . dY-tile for the wave's c-th column
+    // block, so lane l register r holds column 8*(r/4) + 4*(l/32) + r%4 of the
+    // block for packed row l%32: four consecutive columns per register quad,
+    // stored as one float4.
+    floatx16 acc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
     auto wait_vm = [](int n) __attribute__((always_inline)) {
         if (n == kInFlight) SFT_WAIT_VMCNT(kInFlight);
@@ -438,9 +452,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
 
     // One chunk, u = jj mod 8 (a constant): reads stage u and A buffer u%4;
     // the operand loads of chunk jj+3 go to buffer (u+3)%4 (chunk jj-1's) and
-    // the copies of chunk jj+7 to stage (u+7)%8 (chunk jj-1's).
+    // the copies of chunk jj+7 to stage (u+7)%8 (chunk jj-1's).  `two` (wave
+    // uniform) selects the second column block; one code path serves both
+    // layouts, so the registers of loads in flight never move.
     bf16x8 ab[kAAhead + 1][4];
-    auto step = [&](auto u_tag, int32_t jj, int n_wait, bool active) __attribute__((always_inline)) {
+    auto step = [&](auto u_tag, int32_t jj, int n_wait, bool active, bool two, const int (&xo)[2])
+                    __attribute__((always_inline)) {
         constexpr int U = decltype(u_tag)::value;
         const uint16_t *X = reinterpret_cast<const uint16_t *>(xstage<U>());
         uint8_t *st_dma = xstage<(U + kXAhead) % kXStages>();
@@ -451,21 +468,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         issue_a(jj + kAAhead, ab[(U + kAAhead) % (kAAhead + 1)]);
         const int32_t jx = jj + kXAhead;
         advance_x(jx);
+        auto bfrag = [&](int kk, int c) __attribute__((always_inline)) {
+            const int r0 = 16 * kk + trow;
+            const short4v lo = lds_tr16(X + r0 * kBN + xo[c]);
+            const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xo[c]);
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
         // The X copies are issued on every path (only the MFMA work is
         // conditional), so the compiler's count of operations in flight is
         // exact; they sit between k-steps to overlap the matrix cores.
-        bf16x8 bc[4], bn[4];
-        if (active) bfrag(X, 0, bc);
+        bf16x8 bc0, bc1, bn0, bn1;
+        if (active) {
+            bc0 = bfrag(0, 0);
+            if (two) bc1 = bfrag(0, 1);
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if (active) {
-                if (kk < 3) bfrag(X, kk + 1, bn);
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[cb], a[kk], acc[cb], 0, 0, 0);
                 if (kk < 3) {
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) bc[cb] = bn[cb];
+                    bn0 = bfrag(kk + 1, 0);
+                    if (two) bn1 = bfrag(kk + 1, 1);
+                }
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc0, a[kk], acc[0], 0, 0, 0);
+                if (two) acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc1, a[kk], acc[1], 0, 0, 0);
+                if (kk < 3) {
+                    bc0 = bn0;
+                    bc1 = bn1;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -474,47 +502,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         }
     };
     // A round of 8 chunks; the first three wait for `extra` more operations.
-    auto round8 = [&](int32_t jq, bool active, int extra) __attribute__((always_inline)) {
-        step(ic<0>{}, jq + 0, kInFlight + extra, active);
-        step(ic<1>{}, jq + 1, kInFlight + extra, active);
-        step(ic<2>{}, jq + 2, kInFlight + extra, active);
-        step(ic<3>{}, jq + 3, kInFlight, active);
-        step(ic<4>{}, jq + 4, kInFlight, active);
-        step(ic<5>{}, jq + 5, kInFlight, active);
-        step(ic<6>{}, jq + 6, kInFlight, active);
-        step(ic<7>{}, jq + 7, kInFlight, active);
+    auto round8 = [&](int32_t jq, bool active, bool two, const int (&xo)[2], int extra)
+                      __attribute__((always_inline)) {
+        step(ic<0>{}, jq + 0, kInFlight + extra, active, two, xo);
+        step(ic<1>{}, jq + 1, kInFlight + extra, active, two, xo);
+        step(ic<2>{}, jq + 2, kInFlight + extra, active, two, xo);
+        step(ic<3>{}, jq + 3, kInFlight, active, two, xo);
+        step(ic<4>{}, jq + 4, kInFlight, active, two, xo);
+        step(ic<5>{}, jq + 5, kInFlight, active, two, xo);
+        step(ic<6>{}, jq + 6, kInFlight, active, two, xo);
+        step(ic<7>{}, jq + 7, kInFlight, active, two, xo);
     };
 
-    // Segment epilogue: every wave stores 16 float4 (masked-off lanes to the
+    // Segment epilogue: every wave issues 8 float4 stores whatever its
+    // layout (masked-off lanes and an unused second block write to the
     // sink).  A whole tile goes to dW_act through the row map; a partial one
-    // to its slot, row = wave*32 + packed row.
-    auto epilogue = [&](int sg) __attribute__((always_inline)) {
+    // to its slot, row = tile*32 + packed row.
+    auto epilogue = [&](int sg, int t, int cb0, bool two) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
-        const DwGroupDev &G = p.g[S.g];
+        const DwGroupDev &G = gs[S.g];
         const int i = lane & 31, h = lane >> 5;
-        const int32_t code = wave < S.mt ? codes[sg][wave * 32 + i] : -1;
+        const int32_t code = t < S.mt ? codes[sg][t * 32 + i] : -1;
         const int64_t c0 = static_cast<int64_t>(S.nb) * kBN;
         float *rowp = sink;
         if (code >= 0)
             rowp = S.slot < 0 ? outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C + c0
-                              : p.part + S.slot * kSlotFloats + (wave * 32 + i) * kBN;
+                              : p.part + S.slot * kSlotFloats + (t * 32 + i) * kBN;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int cl = 32 * cb + 8 * a + 4 * h;
-                const bool ok = code >= 0 && (S.slot >= 0 || c0 + cl < G.C);
-                auto *dst = reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(
-                    reinterpret_cast<uintptr_t>(ok ? rowp + cl : sink));
-                *dst = f32x4{acc[cb][4 * a], acc[cb][4 * a + 1], acc[cb][4 * a + 2], acc[cb][4 * a + 3]};
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+        for (int q = 0; q < kEpiStores; ++q) {
+            const int c = q / 4, a = q % 4;
+            const int cl = 32 * (cb0 + c) + 8 * a + 4 * h;
+            const bool ok = (c == 0 || two) && code >= 0 && (S.slot >= 0 || c0 + cl < G.C);
+            auto *dst = reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(
+                reinterpret_cast<uintptr_t>(ok ? rowp + cl : sink));
+            *dst = f32x4{acc[c][4 * a], acc[c][4 * a + 1], acc[c][4 * a + 2], acc[c][4 * a + 3]};
         }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
     };
 
     // ---- prologue: X copies of chunks 0..6 and operands of chunks 0..2, in
-    // the order the steady state issues them.
+    // the order the steady state issues them, then 8 stores to the sink so
+    // that every segment, the first included, starts behind an epilogue.
     describe_x(0);
     describe_a(0);
     auto prologue_x = [&](auto s_tag) __attribute__((always_inline)) {
@@ -534,21 +565,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     prologue_x(ic<5>{});
     issue_a(2, ab[2]);
     prologue_x(ic<6>{});
+#pragma unroll
+    for (int q = 0; q < kEpiStores; ++q)
+        *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(reinterpret_cast<uintptr_t>(sink)) = f32x4{};
 
-    // ---- segment 0, then the others.  The first round after an epilogue is
-    // peeled: its first three chunks wait for 16 more memory operations (the
-    // epilogue's stores sit behind their operand loads).
-    {
-        const bool active = wave < segs[0].mt;
-        for (int32_t jq = 0; jq < segs[0].len; jq += kRound) round8(jq, active, 0);
-        epilogue(0);
-    }
-    for (int sg = 1; sg < nseg; ++sg) {
+    // ---- the segments.  The first round of each waits for 8 more memory
+    // operations in its first three chunks (the epilogue's stores sit behind
+    // their operand loads).
+    for (int sg = 0; sg < nseg; ++sg) {
         const int32_t j0 = segs[sg].j0, len = segs[sg].len;
-        const bool active = wave < segs[sg].mt;
-        round8(j0, active, kEpiStores);
-        for (int32_t jq = j0 + kRound; jq < j0 + len; jq += kRound) round8(jq, active, 0);
-        epilogue(sg);
+        const bool two = nc_of(segs[sg].mt) == 2;
+        const int wpt = two ? 2 : 4;
+        const int t = wave / wpt, cb0 = (wave % wpt) * (two ? 2 : 1);
+        const bool active = t < segs[sg].mt;
+        int xo[2];
+        xo[0] = xoff_of(cb0);
+        xo[1] = xoff_of(two ? cb0 + 1 : cb0);
+        round8(j0, active, two, xo, kEpiStores);
+        for (int32_t jq = j0 + kRound; jq < j0 + len; jq += kRound) round8(jq, active, two, xo, 0);
+        epilogue(sg, t, cb0, two);
     }
     // Copies past the slice are still in flight (they write zeros to LDS):
     // drain before the workgroup's LDS can be handed to another.
@@ -557,7 +592,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
 
 // Combination of the partial tiles: an output tile cut by slice boundaries
 // is the sum of its slices' partial rows, added in slice order.  One
-// workgroup per (output tile, 8 packed rows); a lane adds 4 columns.
+// workgroup per (output tile, 8 packed rows); a lane adds 4 columns.  The
+// tile bookkeeping is wave-uniform (scalar); a lane issues its partial loads
+// and its row-map load together, so the kernel is one memory round trip.
 __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     const int64_t ot = blockIdx.x;
     int gi = 0;
@@ -569,31 +606,46 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     // slices covering [A, B): slice v starts at 8*floor(v*Q/P), Q = iters/8
     // (A and B are multiples of 8)
     const int64_t Q = p.iters / kRound, P = p.n_wg;
-    const int64_t v_first = ((A / kRound + 1) * P - 1) / Q;
-    const int64_t v_last = ((B / kRound) * P - 1) / Q;
+    const int32_t v_first = static_cast<int32_t>(((A / kRound + 1) * P - 1) / Q);
+    const int32_t v_last = static_cast<int32_t>(((B / kRound) * P - 1) / Q);
     if (v_first == v_last) return;  // the tile lies inside one slice: written directly
     const int32_t mb = tile / G.n_nblk, nb = tile % G.n_nblk;
     const int32_t p0 = mblk_lo(G, mb), mt = mblk_lo(G, mb + 1) - p0;
     const int prow = blockIdx.y * 8 + (threadIdx.x >> 5);
     if (prow >= mt * 32) return;
-    const int32_t code = G.rowmap[p0 * 32 + prow];
-    if (code < 0) return;
     const int cl = (threadIdx.x & 31) * 4;
     const int64_t col = static_cast<int64_t>(nb) * kBN + cl;
     if (col >= G.C) return;
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t vv = v_first; vv <= v_last; ++vv) {
-        const int64_t slot = (slice_lo(p, vv) >= A) ? 2 * vv : 2 * vv + 1;
-        const float4 x = *reinterpret_cast<const float4 *>(p.part + slot * kSlotFloats + prow * kBN + cl);
-        if (vv == v_first) {
-            sum = x;
-        } else {
-            sum.x += x.x;
-            sum.y += x.y;
-            sum.z += x.z;
-            sum.w += x.w;
+    // The first slice started before the tile (its last segment: odd slot);
+    // every later one starts inside it (first segment: even slot).
+    const bool first_odd = slice_lo(p, v_first) < A;
+    const float *part = p.part + prow * kBN + cl;
+    const int32_t code = G.rowmap[p0 * 32 + prow];
+    float4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t vv = v_first + i;
+        const int64_t slot = (i == 0 && first_odd) ? 2 * static_cast<int64_t>(vv) + 1 : 2 * static_cast<int64_t>(vv);
+        if (vv <= v_last) x[i] = *reinterpret_cast<const float4 *>(part + slot * kSlotFloats);
+    }
+    float4 sum = x[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        if (v_first + i <= v_last) {
+            sum.x += x[i].x;
+            sum.y += x[i].y;
+            sum.z += x[i].z;
+            sum.w += x[i].w;
         }
     }
+    for (int32_t vv = v_first + 4; vv <= v_last; ++vv) {
+        const float4 y = *reinterpret_cast<const float4 *>(part + 2 * static_cast<int64_t>(vv) * kSlotFloats);
+        sum.x += y.x;
+        sum.y += y.y;
+        sum.z += y.z;
+        sum.w += y.w;
+    }
+    if (code < 0) return;
     float *out = p.m[code >> 24].out;
     *reinterpret_cast<float4 *>(out + static_cast<int64_t>(code & 0xFFFFFF) * G.C + col) = sum;
 }

@@ -109,72 +109,101 @@ __device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
     return r;
 }
 
-// Update one active row (index k of matrix M) whose effective gradient for a
-// 4-column chunk at column c is produced by grad(c, float4&).
-template <int kThreads, int kChunks, typename GradFn>
-__device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const AdamDev &hp,
-                                           GradFn grad) {
+// Update one active row (index k of matrix M).  `gr` supplies the effective
+// gradient of a 4-column chunk in two parts: gr.load(c) issues the chunk's
+// gradient loads, gr.combine(raw, g) forms the gradient from them.  Every
+// load of the row is issued before any arithmetic (one memory round trip for
+// the whole row; rows wider than 16384 columns take two to four); the moments
+// are stored as soon as they are computed, q, delta and the live weights
+// after the row's |w'| maximum.
+template <int kThreads, int kChunks, typename Grad>
+__device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const AdamDev &hp, const Grad &gr) {
     __shared__ float red[kThreads / 64];
     const int64_t C = M.C;
     const int64_t r = M.rows[k];
     const int64_t sl = M.slot[k];
     const bool fresh = M.fresh ? M.fresh[k] != 0 : false;
-    const int32_t step = (fresh ? 0 : M.t[sl]) + 1;
-    const int32_t ti = min(step, hp.t_max);
-    const float bc1 = hp.bc1[ti];
-    const float bc2 = hp.bc2[ti];
     const float s_old = M.s[r];
-    const int8_t *qrow = M.q + r * C;
-    const float *drow = M.delta + r * C;
+    const int32_t t_old = fresh ? 0 : M.t[sl];
+    const int8_t *__restrict__ qrow = M.q + r * C;
+    const float *__restrict__ drow = M.delta + r * C;
     uint16_t *mrow = M.m + sl * C;
     uint16_t *vrow = M.v + sl * C;
 
+    const int32_t step = t_old + 1;
+    const int32_t ti = min(step, hp.t_max);
+    float bc1 = 0.0f, bc2 = 0.0f;
+
+    // Wide rows on 1024-lane workgroups go in batches of chunks (registers).
+    constexpr int kBatch = kThreads >= 1024 ? (kChunks >= 16 ? 2 : 4) : kChunks;
+    static_assert(kChunks % kBatch == 0, "batch");
     float wn[kChunks][4];
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-        const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
-        if (c < C) {
-            float g[4];
-            grad(c, g);
-            const char4 qv = *reinterpret_cast<const char4 *>(qrow + c);
-            const float4 dv = *reinterpret_cast<const float4 *>(drow + c);
-            ushort4 mv = make_ushort4(0, 0, 0, 0), vv = make_ushort4(0, 0, 0, 0);
-            if (!fresh) {
-                mv = *reinterpret_cast<const ushort4 *>(mrow + c);
-                vv = *reinterpret_cast<const ushort4 *>(vrow + c);
-            }
-            const float qf[4] = {static_cast<float>(qv.x), static_cast<float>(qv.y),
-                                 static_cast<float>(qv.z), static_cast<float>(qv.w)};
-            const float df[4] = {dv.x, dv.y, dv.z, dv.w};
-            const uint16_t mh[4] = {mv.x, mv.y, mv.z, mv.w};
-            const uint16_t vh[4] = {vv.x, vv.y, vv.z, vv.w};
-            uint16_t mo[4], vo[4];
+    for (int b0 = 0; b0 < kChunks; b0 += kBatch) {
+        typename Grad::Raw graw[kBatch];
+        char4 qv[kBatch];
+        float4 dv[kBatch];
+        ushort4 mv[kBatch], vv[kBatch];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float sq = s_old * qf[e];
-                const float w = sq + df[e];
-                const float m_a = hp.beta1 * h2f(mh[e]);
-                const float m_b = hp.c1 * g[e];
-                const float m = m_a + m_b;
-                const float gg = g[e] * g[e];
-                const float v_a = hp.beta2 * h2f(vh[e]);
-                const float v_b = hp.c2 * gg;
-                const float v = v_a + v_b;
-                mo[e] = f2h(m);
-                vo[e] = f2h(v);
-                const float mhat = m / bc1;
-                const float vhat = v / bc2;
-                const float denom = __builtin_sqrtf(vhat) + hp.eps;
-                const float ratio = mhat / denom;
-                const float u = hp.lr * ratio;
-                const float w1 = hp.wd != 0.0f ? w * hp.decay : w;
-                const float wnew = w1 - u;
-                wn[j][e] = wnew;
-                amax = fmaxf(amax, fabsf(wnew));
+        for (int jb = 0; jb < kBatch; ++jb) {
+            const int j = b0 + jb;
+            const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+            mv[jb] = make_ushort4(0, 0, 0, 0);
+            vv[jb] = make_ushort4(0, 0, 0, 0);
+            if (c < C) {
+                graw[jb] = gr.load(c);
+                qv[jb] = *reinterpret_cast<const char4 *>(qrow + c);
+                dv[jb] = *reinterpret_cast<const float4 *>(drow + c);
+                if (!fresh) {
+                    mv[jb] = *reinterpret_cast<const ushort4 *>(mrow + c);
+                    vv[jb] = *reinterpret_cast<const ushort4 *>(vrow + c);
+                }
             }
-            *reinterpret_cast<ushort4 *>(mrow + c) = make_ushort4(mo[0], mo[1], mo[2], mo[3]);
-            *reinterpret_cast<ushort4 *>(vrow + c) = make_ushort4(vo[0], vo[1], vo[2], vo[3]);
+        }
+        if (b0 == 0) {
+            bc1 = hp.bc1[ti];
+            bc2 = hp.bc2[ti];
+        }
+#pragma unroll
+        for (int jb = 0; jb < kBatch; ++jb) {
+            const int j = b0 + jb;
+            const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+            if (c < C) {
+                float g[4];
+                gr.combine(graw[jb], g);
+                const float qf[4] = {static_cast<float>(qv[jb].x), static_cast<float>(qv[jb].y),
+                                     static_cast<float>(qv[jb].z), static_cast<float>(qv[jb].w)};
+                const float df[4] = {dv[jb].x, dv[jb].y, dv[jb].z, dv[jb].w};
+                const uint16_t mh[4] = {mv[jb].x, mv[jb].y, mv[jb].z, mv[jb].w};
+                const uint16_t vh[4] = {vv[jb].x, vv[jb].y, vv[jb].z, vv[jb].w};
+                uint16_t mo[4], vo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sq = s_old * qf[e];
+                    const float w = sq + df[e];
+                    const float m_a = hp.beta1 * h2f(mh[e]);
+                    const float m_b = hp.c1 * g[e];
+                    const float m = m_a + m_b;
+                    const float gg = g[e] * g[e];
+                    const float v_a = hp.beta2 * h2f(vh[e]);
+                    const float v_b = hp.c2 * gg;
+                    const float v = v_a + v_b;
+                    mo[e] = f2h(m);
+                    vo[e] = f2h(v);
+                    const float mhat = m / bc1;
+                    const float vhat = v / bc2;
+                    const float denom = __builtin_sqrtf(vhat) + hp.eps;
+                    const float ratio = mhat / denom;
+                    const float u = hp.lr * ratio;
+                    const float w1 = hp.wd != 0.0f ? w * hp.decay : w;
+                    const float wnew = w1 - u;
+                    wn[j][e] = wnew;
+                    amax = fmaxf(amax, fabsf(wnew));
+                }
+                *reinterpret_cast<ushort4 *>(mrow + c) = make_ushort4(mo[0], mo[1], mo[2], mo[3]);
+                *reinterpret_cast<ushort4 *>(vrow + c) = make_ushort4(vo[0], vo[1], vo[2], vo[3]);
+            }
         }
     }
     amax = block_max_nonneg<kThreads>(amax, red);
@@ -214,6 +243,19 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
     }
 }
 
+// Plain update: the gradient is the matrix's own dW row.
+struct OwnGrad {
+    typedef float4 Raw;
+    const float *row;
+    __device__ __forceinline__ Raw load(int64_t c) const { return *reinterpret_cast<const float4 *>(row + c); }
+    __device__ __forceinline__ void combine(const Raw &x, float *g) const {
+        g[0] = x.x;
+        g[1] = x.y;
+        g[2] = x.z;
+        g[3] = x.w;
+    }
+};
+
 template <int kThreads, int kChunks>
 __global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
     const int64_t wg = blockIdx.x;
@@ -221,12 +263,37 @@ __global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
     while (mi + 1 < p.n_mats && wg >= p.mat[mi + 1].row_begin) ++mi;
     const UpdMatDev &M = p.mat[mi];
     const int64_t k = wg - M.row_begin;
-    const float *grow = M.G + k * M.C;
-    update_row<kThreads, kChunks>(M, k, p.hp, [&](int64_t c, float *g) {
-        const float4 gv = *reinterpret_cast<const float4 *>(grow + c);
-        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
-    });
+    update_row<kThreads, kChunks>(M, k, p.hp, OwnGrad{M.G + k * M.C});
 }
+
+// Coupled update: the blend of the clipped own and partner gradients (a row
+// missing from the partner's active set contributes zero).
+struct PairGrad {
+    struct Raw {
+        float4 own, part;
+    };
+    const float *own_row;
+    const float *part_row;   // null: the partner's row is inactive
+    float c_self, c_part, a_own, a_cross;
+    __device__ __forceinline__ Raw load(int64_t c) const {
+        Raw x;
+        x.own = *reinterpret_cast<const float4 *>(own_row + c);
+        x.part = part_row ? *reinterpret_cast<const float4 *>(part_row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        return x;
+    }
+    __device__ __forceinline__ void combine(const Raw &x, float *g) const {
+        const float sa[4] = {x.own.x, x.own.y, x.own.z, x.own.w};
+        const float pa[4] = {x.part.x, x.part.y, x.part.z, x.part.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float cs = c_self * sa[e];
+            const float cp = c_part * pa[e];
+            const float own = a_own * cs;
+            const float cross = a_cross * cp;
+            g[e] = own + cross;
+        }
+    }
+};
 
 // Index of `row` in an ascending list, or -1.
 __device__ __forceinline__ int64_t find_row(const int32_t *rows, int64_t n, int64_t row) {
@@ -251,26 +318,14 @@ __global__ __launch_bounds__(kThreads) void k_coupled_update(const PairParams p)
     const int64_t pk = find_row(S.prow, S.pn, r);
     const float clip_a = S.clip ? S.clip[0] : 1.0f;
     const float clip_b = S.clip ? S.clip[1] : 1.0f;
-    const float c_self = S.self_is_b ? clip_b : clip_a;
-    const float c_part = S.self_is_b ? clip_a : clip_b;
-    const float *gs = M.G + k * M.C;
-    const float *gp = pk >= 0 ? S.pG + pk * M.C : nullptr;
-    const float a_own = S.a_own, a_cross = S.a_cross;
-    update_row<kThreads, kChunks>(M, k, p.hp, [&](int64_t c, float *g) {
-        const float4 sv = *reinterpret_cast<const float4 *>(gs + c);
-        float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gp) pv = *reinterpret_cast<const float4 *>(gp + c);
-        const float sa[4] = {sv.x, sv.y, sv.z, sv.w};
-        const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float cs = c_self * sa[e];
-            const float cp = c_part * pa[e];
-            const float own = a_own * cs;
-            const float cross = a_cross * cp;
-            g[e] = own + cross;
-        }
-    });
+    PairGrad gr;
+    gr.own_row = M.G + k * M.C;
+    gr.part_row = pk >= 0 ? S.pG + pk * M.C : nullptr;
+    gr.c_self = S.self_is_b ? clip_b : clip_a;
+    gr.c_part = S.self_is_b ? clip_a : clip_b;
+    gr.a_own = S.a_own;
+    gr.a_cross = S.a_cross;
+    update_row<kThreads, kChunks>(M, k, p.hp, gr);
 }
 
 __global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restrict__ q,
@@ -373,7 +428,7 @@ int dispatch(int64_t maxC, int64_t n_wg, const Params &p, hipStream_t stream) {
     if (maxC <= 256 * 4 * 4) return Launch<256, 4>::go(n_wg, p, stream);
     if (maxC <= 256 * 4 * 8) return Launch<256, 8>::go(n_wg, p, stream);
     if (maxC <= 256 * 4 * 12) return Launch<256, 12>::go(n_wg, p, stream);
-    if (maxC <= 256 * 4 * 16) return Launch<256, 16>::go(n_wg, p, stream);
+    if (maxC <= 1024 * 4 * 4) return Launch<1024, 4>::go(n_wg, p, stream);
     if (maxC <= 1024 * 4 * 8) return Launch<1024, 8>::go(n_wg, p, stream);
     return Launch<1024, 16>::go(n_wg, p, stream);
 }
