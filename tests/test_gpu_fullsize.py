@@ -135,3 +135,160 @@ def test_llama7b_layer_dw_and_update_sampled(gpu_lib, layer, layout):
         assert np.array_equal(s[idle].view(np.uint32), m["s"][idle].view(np.uint32)), name
         assert np.array_equal(delta[idle].view(np.uint32), m["delta"][idle].view(np.uint32)), name
         assert not host_u16(st["w"])[idle].any(), name
+
+
+def _sub_state(m, rows, C):
+    """Oracle state holding only the given rows (fresh moments)."""
+    n = rows.size
+    return oracle.MatState(m["q"][rows].copy(), m["s"][rows].copy(), m["delta"][rows].copy(),
+                           np.zeros((n, C), np.uint16), np.zeros((n, C), np.uint16), np.zeros(n, np.int32),
+                           np.zeros((n, C), np.uint16))
+
+
+def _assert_rows(st, rows, pos, sub, what):
+    """GPU state rows `rows` (moment slots `pos`) equal the oracle sub-state."""
+    assert np.array_equal(st["q"].cpu().numpy()[rows], sub.q), what
+    assert np.array_equal(st["s"].cpu().numpy()[rows].view(np.uint32), sub.s.view(np.uint32)), what
+    assert np.array_equal(st["delta"].cpu().numpy()[rows].view(np.uint32), sub.delta.view(np.uint32)), what
+    assert np.array_equal(host_u16(st["m"])[pos], sub.m), what
+    assert np.array_equal(host_u16(st["v"])[pos], sub.v), what
+    assert np.array_equal(host_u16(st["w"])[rows], sub.w_live), what
+
+
+def _dev_state(m, n):
+    return {"q": dev(m["q"]), "s": dev(m["s"]), "delta": dev(m["delta"]),
+            "m": torch.zeros((n, m["C"]), dtype=torch.int16, device="cuda"),
+            "v": torch.zeros((n, m["C"]), dtype=torch.int16, device="cuda"),
+            "t": torch.zeros(n, dtype=torch.int32, device="cuda"),
+            "w": torch.zeros((m["R"], m["C"]), dtype=torch.int16, device="cuda"),
+            "slot": dev(np.arange(n, dtype=np.int32)), "fresh": dev(np.ones(n, np.uint8))}
+
+
+def test_llama7b_adversarial_one_row_per_tile_coupled(gpu_lib, layer):
+    """Exactly one active row in every 32-row tile (no tile can be skipped),
+    packed dW, then the coupled update of (gate, up), (q, o), (k, v) and the
+    plain update of down.  A pair's masks share the row of every other tile,
+    so that rows active in both, in one only, and the blend all occur."""
+    import math
+    X, base = layer
+    rng = synth.rng(7100)
+    mats = {}
+    for mi, name in enumerate(synth.LLAMA7B):
+        mats[name] = dict(base[name])
+        rows = synth.one_per_tile_rows(base[name]["R"], 7200 + mi)
+        mats[name]["rows"] = rows
+    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
+    for a, b in pairs:
+        ra, rb = mats[a]["rows"].copy(), mats[b]["rows"].copy()
+        rb[::2] = ra[::2]                       # same row in every other tile
+        mats[b]["rows"] = rb
+    for name, m in mats.items():
+        m["mask"] = synth.mask_from_rows(m["R"], m["rows"])
+
+    groups, gpu = [], {}
+    for gname, members in synth.LLAMA7B_GROUPS:
+        ms = []
+        for name in members:
+            m = mats[name]
+            plan = _lib.sft_plan_rows(m["mask"])
+            assert plan.n_active_tiles == (m["R"] + 31) // 32 == plan.n_active
+            out = torch.empty((plan.n_active, m["C"]), dtype=torch.float32, device="cuda")
+            gpu[name] = {"plan": plan, "dplan": plan.to_device(), "out": out}
+            ms.append(_lib.DwMat(bf16_dev(m["dY"]), gpu[name]["dplan"], out))
+        groups.append(_lib.DwGroup(bf16_dev(X[gname]), ms, _lib.SFT_DW_PACKED))
+    ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device="cuda")
+    _lib.sft_masked_dw(groups, ws)
+    torch.cuda.synchronize()
+    G = {}
+    for name, m in mats.items():
+        plan = gpu[name]["plan"]
+        G[name] = gpu[name]["out"].cpu().numpy()
+        pick = np.sort(rng.choice(plan.n_active, size=ROWS_PER_MAT, replace=False))
+        dw_close(G[name][pick], oracle.masked_dw(m["dY"], X[m["group"]], plan.active_rows[pick]))
+
+    wd = float(np.float32(0.01 * math.cos(math.radians(28.4))))
+    hp = adam_dev(weight_decay=wd)
+    a_own, a_cross = 1.0, 0.4
+    st = {name: _dev_state(m, gpu[name]["plan"].n_active) for name, m in mats.items()}
+
+    def upd(name):
+        s_ = st[name]
+        return _lib.UpdMat(s_["q"], s_["s"], s_["delta"], s_["m"], s_["v"], s_["t"], gpu[name]["dplan"].active_rows,
+                           s_["slot"], gpu[name]["out"], gpu[name]["plan"].n_active, s_["fresh"], s_["w"])
+    _lib.sft_coupled_update([_lib.Pair(upd(a), upd(b), a_own, a_cross) for a, b in pairs], hp)
+    _lib.sft_sparse_update([upd("down")], hp)
+    torch.cuda.synchronize()
+
+    for a, b in pairs:
+        ra, rb = gpu[a]["plan"].active_rows, gpu[b]["plan"].active_rows
+        union = np.union1d(ra, rb)
+        S = np.sort(rng.choice(union, size=6, replace=False)).astype(np.int32)
+        C = mats[a]["C"]
+        ia = np.searchsorted(ra, S)
+        ib = np.searchsorted(rb, S)
+        in_a = (ia < ra.size) & (ra[np.minimum(ia, ra.size - 1)] == S)
+        in_b = (ib < rb.size) & (rb[np.minimum(ib, rb.size - 1)] == S)
+        sa, sb = _sub_state(mats[a], S, C), _sub_state(mats[b], S, C)
+        la, lb = np.nonzero(in_a)[0].astype(np.int32), np.nonzero(in_b)[0].astype(np.int32)
+        oracle.coupled_update(sa, G[a][ia[in_a]], la, la, np.ones(la.size, np.uint8),
+                              sb, G[b][ib[in_b]], lb, lb, np.ones(lb.size, np.uint8),
+                              a_own=a_own, a_cross=a_cross, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8,
+                              weight_decay=wd)
+        # rows active in one side only are left untouched on the other
+        for side, (name, sub, inside, idx) in enumerate([(a, sa, in_a, ia), (b, sb, in_b, ib)]):
+            rows = S[inside]
+            got = {k: v for k, v in st[name].items()}
+            sub_rows = oracle.MatState(sub.q[inside], sub.s[inside], sub.delta[inside],
+                                       sub.m[np.nonzero(inside)[0]], sub.v[np.nonzero(inside)[0]],
+                                       sub.t[np.nonzero(inside)[0]], sub.w_live[inside])
+            _assert_rows(got, rows, idx[inside], sub_rows, f"{name} (pair {a},{b})")
+            untouched = S[~inside]
+            assert np.array_equal(got["q"].cpu().numpy()[untouched], mats[name]["q"][untouched])
+            assert not host_u16(got["w"])[untouched].any()
+
+    # down: the plain step
+    plan = gpu["down"]["plan"]
+    pick = np.sort(rng.choice(plan.n_active, size=ROWS_PER_MAT, replace=False))
+    rows = plan.active_rows[pick]
+    sub = _sub_state(mats["down"], rows, mats["down"]["C"])
+    oracle.sparse_update(sub, G["down"][pick], np.arange(pick.size, dtype=np.int32),
+                         np.arange(pick.size, dtype=np.int32), np.ones(pick.size, np.uint8),
+                         lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd)
+    _assert_rows(st["down"], rows, pick, sub, "down")
+
+
+def test_embedding_32000x4096_conductor_gradient_update(gpu_lib):
+    """The embedding workload: a 32000 x 4096 table, batches of 8 x 512 token
+    ids drawn Zipf(1.1), the conductor over 4 windows sets the row mask, then
+    the masked scatter-gradient (every active row, against the oracle), the
+    sparse update with fused write-back (sampled rows, bit for bit)."""
+    V, d, Tb = 32000, 4096, 8 * 512
+    ch = np.zeros(V, np.float32)
+    for w in range(4):
+        tokens = synth.zipf_tokens(Tb, V, 1.1, 7300 + w)
+        mask = _lib.sft_conductor_window(ch, tokens)
+    plan = _lib.sft_plan_rows(mask)
+    assert 20 <= plan.n_active <= 400
+    row_ptr, pos = _lib.sft_plan_embedding(plan, tokens)
+    dY = synth.normal_bf16((Tb, d), 0.01, 7310)
+    out = torch.full((plan.n_active + 1, d), float("nan"), dtype=torch.float32, device="cuda")
+    _lib.sft_embedding_dw(bf16_dev(dY), dev(row_ptr), dev(pos), plan.n_active, out[:plan.n_active])
+    torch.cuda.synchronize()
+    G = out.cpu().numpy()
+    assert np.all(np.isnan(G[plan.n_active:]))
+    G = G[:plan.n_active]
+    dw_close(G, oracle.embedding_dw(dY, tokens, plan.active_rows))
+
+    q, s, delta = synth.quant_state(V, d, 7320)
+    m = {"q": q, "s": s, "delta": delta, "R": V, "C": d}
+    st = _dev_state(m, plan.n_active)
+    dplan = plan.to_device()
+    _lib.sft_sparse_update([_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], dplan.active_rows,
+                                        st["slot"], dev(G), plan.n_active, st["fresh"], st["w"])], adam_dev())
+    torch.cuda.synchronize()
+    pick = np.sort(synth.rng(7330).choice(plan.n_active, size=6, replace=False))
+    rows = plan.active_rows[pick]
+    sub = _sub_state(m, rows, d)
+    oracle.sparse_update(sub, G[pick], np.arange(pick.size, dtype=np.int32), np.arange(pick.size, dtype=np.int32),
+                         np.ones(pick.size, np.uint8), lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+    _assert_rows(st, rows, pick, sub, "embedding")
