@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+COUNTERS_SUMMARY = "masked_dw_llama7b_layer_1pct_counters.txt"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
@@ -43,6 +44,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=6, help="ring of distinct layers cycled by the steps")
     ap.add_argument("--density", type=float, default=0.01)
+    ap.add_argument("--layout", choices=["packed", "tiles"], default="packed",
+                    help="masked-dW row layout: active rows packed 32 to a tile, or whole active tiles")
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-every", type=int, default=4,
@@ -55,7 +58,7 @@ def parse_args():
 class Layer:
     """Device buffers, plans and prepared launches of one layer."""
 
-    def __init__(self, idx: int, T: int, density: float, seed0: int):
+    def __init__(self, idx: int, T: int, density: float, seed0: int, layout: str = "packed"):
         import torch
 
         from sparse_full_weight_amd import _lib, synth
@@ -127,7 +130,8 @@ class Layer:
                 m["t"] = torch.zeros(n, dtype=torch.int32, device=dev)
                 upd.append(_lib.UpdMat(m["q"], m["s"], m["delta"], m["m"], m["v"], m["t"], view("rows"),
                                        view("slot"), m["dW"], n, view("fresh", n, torch.uint8), m["w_live"]))
-            groups.append(_lib.DwGroup(self.X[gname], dw_mats))
+            groups.append(_lib.DwGroup(self.X[gname], dw_mats,
+                                       _lib.SFT_DW_PACKED if layout == "packed" else _lib.SFT_DW_TILES))
         self.groups = groups
         self.upd = upd
         nbytes = _lib.sft_masked_dw_workspace(groups)
@@ -216,7 +220,7 @@ def main():
     print(f"[bench] building {args.layers} layers (T={args.tokens}, density={args.density})", file=sys.stderr,
           flush=True)
     t0 = time.perf_counter()
-    layers = [Layer(i, args.tokens, args.density, 5000) for i in range(args.layers)]
+    layers = [Layer(i, args.tokens, args.density, 5000, args.layout) for i in range(args.layers)]
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
 
@@ -282,6 +286,14 @@ def main():
     n_act = sum(m["plan"].n_active for m in L0.mats.values())
     n_tiles = sum(m["plan"].n_active_tiles for m in L0.mats.values())
 
+    # HBM bytes per masked-dW call from the committed counter summary, if it
+    # was taken on the current kernel source (else null).
+    from sparse_full_weight_amd import profsum
+    rec = profsum.read_traffic(os.path.join(ROOT, "profiles", COUNTERS_SUMMARY))
+    traffic = None
+    if rec and rec.get("sft_dw_sha256") == profsum.source_hash("sft_dw.hip"):
+        traffic = rec["masked_dw_call_bytes"]
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
@@ -306,12 +318,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama7b_layer_masked_step", "tokens": args.tokens, "density": args.density,
                    "matrices": {k: list(v) for k, v in synth.LLAMA7B.items()}, "active_rows": n_act,
-                   "active_tiles": n_tiles, "ring_layers": args.layers,
+                   "active_tiles": n_tiles, "ring_layers": args.layers, "dw_layout": args.layout,
                    "step": "plan upload + masked dW (7 matrices, 1 launch) + sparse update with fused "
                            "write-back (7 matrices, 1 launch)"},
-        "roofline": {"bound": "hbm", "kernel": "k_masked_dw", "achieved": round(dw_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dw_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": dw.bytes, "avg_ms": round(dw_avg, 5)},
+        "roofline": {"bound": "hbm", "kernel": "sft_masked_dw (k_dw_gather + k_masked_dw + k_dw_fixup)",
+                     "achieved": round(dw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": dw.bytes, "avg_ms": round(dw_avg, 5)},
         "cpu_baseline": cpu,
         "kernels": {
             "k_masked_dw": {"avg_ms": round(dw_avg, 5), "GB_s": round(dw_gbs, 1),

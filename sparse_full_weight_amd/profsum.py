@@ -1,0 +1,163 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+Two summaries, both plain text meant to be kept next to the numbers they
+support:
+
+* ``stats``: per-kernel call count and average/min/max duration from a
+  ``--kernel-trace --stats --output-format csv`` run, plus the sum over the
+  kernels of one masked-dW call (gather, product, fix-up);
+* ``counters``: HBM bytes per dispatch from two ``--pmc`` runs of the same
+  program (``FETCH_SIZE``, then ``WRITE_SIZE``, both in KiB), each scaled by
+  what the same counter reads for a plain device copy of known size (a
+  ``bench.py --copy-calibration`` run under the same counter).  The last line
+  is machine-readable (``traffic-json: {...}``) and carries the SHA-256 of the
+  kernel source the counters were taken on, so that a reader can tell when
+  they no longer describe the code.
+
+Usage:
+  python -m sparse_full_weight_amd.profsum stats <kernel_stats.csv> --cmd "<command>" > out.txt
+  python -m sparse_full_weight_amd.profsum counters --fetch <dir> --write <dir> \\
+      --copy-fetch <dir> --copy-write <dir> --cmd "<commands>" > out.txt
+(each <dir> holds the ``*_counter_collection.csv`` of one run).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DW_KERNELS = ("k_dw_gather", "k_masked_dw", "k_dw_fixup")
+UPDATE_KERNELS = ("k_sparse_update", "k_coupled_update")
+COPY_BYTES = 1 << 30            # bench.py --copy-calibration copies 1 GiB per launch
+
+
+def source_hash(name: str = "sft_dw.hip") -> str:
+    with open(os.path.join(ROOT, "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def short(name: str) -> str:
+    """Kernel name without namespace and parameter list."""
+    base = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return base.split("(")[0].strip()
+
+
+def kernel_of(name: str, kernels) -> str | None:
+    s = short(name)
+    for k in kernels:
+        if s == k or s.startswith(k + "<"):
+            return k
+    return None
+
+
+def stats(path: str, cmd: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["# rocprofv3 kernel-trace statistics", f"# command: {cmd}", "",
+           f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    dw_sum = 0.0
+    for r in rows:
+        s = short(r["Name"])
+        if s.startswith("at::") or "at::native" in r["Name"]:
+            continue
+        avg = float(r["AverageNs"]) / 1e3
+        out.append(f"{s[:40]:40s} {int(r['Calls']):6d} {avg:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                   f"{float(r['MaxNs']) / 1e3:9.2f}")
+        if kernel_of(r["Name"], DW_KERNELS):
+            dw_sum += avg
+    out += ["", f"sft_masked_dw call (k_dw_gather + k_masked_dw + k_dw_fixup), sum of averages: {dw_sum:.2f} us"]
+    return "\n".join(out) + "\n"
+
+
+def _counter(dirname: str, counter: str) -> dict:
+    files = glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {dirname}")
+    per: dict = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def counters(fetch: str, write: str, copy_fetch: str, copy_write: str, cmd: str) -> str:
+    f = _counter(fetch, "FETCH_SIZE")
+    w = _counter(write, "WRITE_SIZE")
+    cf = _counter(copy_fetch, "FETCH_SIZE")
+    cw = _counter(copy_write, "WRITE_SIZE")
+
+    def copy_kib(per):
+        vals = [v for k, vs in per.items() if "copyBuffer" in k or "copy" in short(k).lower() for v in vs]
+        vals = [v for v in vals if v > 1024]     # the 1 GiB copies, not small blits
+        return sum(vals) / len(vals)
+
+    f_scale = (COPY_BYTES / 1024) / copy_kib(cf)
+    w_scale = (COPY_BYTES / 1024) / copy_kib(cw)
+
+    def avg_kib(per, kernels):
+        res = {}
+        for name, vals in per.items():
+            k = kernel_of(name, kernels)
+            if k:
+                res.setdefault(k, []).extend(vals)
+        return {k: sum(v) / len(v) for k, v in res.items()}
+
+    out = ["# HBM traffic per dispatch from rocprofv3 counters",
+           f"# commands: {cmd}", "",
+           f"calibration: a 1 GiB device copy reads FETCH_SIZE {copy_kib(cf):.0f} KiB and WRITE_SIZE "
+           f"{copy_kib(cw):.0f} KiB per launch -> scale FETCH_SIZE x{f_scale:.4f}, WRITE_SIZE x{w_scale:.4f}", "",
+           f"{'kernel':20s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'read MB':>10s} {'written MB':>11s}"]
+    fk = avg_kib(f, DW_KERNELS + UPDATE_KERNELS)
+    wk = avg_kib(w, DW_KERNELS + UPDATE_KERNELS)
+    total = {}
+    for k in DW_KERNELS + UPDATE_KERNELS:
+        if k not in fk:
+            continue
+        rd = fk[k] * 1024 * f_scale
+        wr = wk.get(k, 0.0) * 1024 * w_scale
+        total[k] = {"read_bytes": round(rd), "write_bytes": round(wr)}
+        out.append(f"{k:20s} {fk[k]:12.1f} {wk.get(k, 0.0):12.1f} {rd / 1e6:10.2f} {wr / 1e6:11.2f}")
+    dw = sum(v["read_bytes"] + v["write_bytes"] for k, v in total.items() if k in DW_KERNELS)
+    out += ["", f"sft_masked_dw call (gather + product + fix-up): {dw / 1e6:.2f} MB of HBM traffic per call"]
+    rec = {"kernels": total, "masked_dw_call_bytes": dw, "fetch_scale": f_scale, "write_scale": w_scale,
+           "sft_dw_sha256": source_hash("sft_dw.hip"), "sft_update_sha256": source_hash("sft_update.hip")}
+    out.append("traffic-json: " + json.dumps(rec, sort_keys=True))
+    return "\n".join(out) + "\n"
+
+
+def read_traffic(path: str) -> dict | None:
+    """The traffic record of a counters summary, or None if missing."""
+    try:
+        for line in open(path):
+            if line.startswith("traffic-json: "):
+                return json.loads(line[len("traffic-json: "):])
+    except OSError:
+        return None
+    return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--cmd", required=True)
+    b = sub.add_parser("counters")
+    for k in ("fetch", "write", "copy-fetch", "copy-write"):
+        b.add_argument("--" + k, required=True)
+    b.add_argument("--cmd", required=True)
+    args = ap.parse_args(argv)
+    if args.what == "stats":
+        sys.stdout.write(stats(args.csv, args.cmd))
+    else:
+        sys.stdout.write(counters(args.fetch, args.write, args.copy_fetch, args.copy_write, args.cmd))
+
+
+if __name__ == "__main__":
+    main()
