@@ -19,14 +19,14 @@
 //      destination (matrix, row of dW_act) or -1 goes to a row map.
 //   2. Product.  Matrices that read the same X (q/k/v; gate/up) form a group;
 //      up to 4 packed tiles of a group (an M-block) share every load of an X
-//      block of 64 tokens x 128 columns.  X is the dominant HBM stream.  It
-//      goes from HBM straight into an 8-stage LDS ring (buffer_load ... lds,
-//      16 bytes per lane), so 7 chunks (112 KB) are in flight per CU, and the
-//      MFMA operand is read from the [token][column] layout with
-//      ds_read_b64_tr_b16.  The dY operand goes from the gather buffer
-//      straight into registers, 3 chunks ahead.  Two or four waves share a
-//      packed tile, each taking two or one of its four 32-column blocks, so
-//      that every SIMD runs two waves.  The launch is persistent and
+//      block of 64 tokens x 256 columns.  X is the dominant HBM stream.  It
+//      goes from HBM straight into a 4-stage LDS ring (buffer_load ... lds,
+//      16 bytes per lane, 512 contiguous bytes a row), so 3 chunks (96 KB)
+//      are in flight per CU, and the MFMA operand is read from the
+//      [token][column] layout with ds_read_b64_tr_b16.  The dY operand goes
+//      from the gather buffer straight into registers, 3 chunks ahead.  Two
+//      waves share a packed tile, each taking four of its eight 32-column
+//      blocks.  The launch is persistent and
 //      stream-K: one 8-wave workgroup per CU takes an equal slice of the
 //      (output tile, chunk) iteration space.
 //   3. Fix-up.  Output tiles cut by slice boundaries leave partial sums in
@@ -49,14 +49,14 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
 
-constexpr int kBN = 128;             // columns per output tile: 4 MFMA column blocks of 32
+constexpr int kBN = 256;             // columns per output tile: 8 MFMA column blocks of 32
 constexpr int kMaxTiles = 4;         // packed tiles per M-block
 constexpr int kBK = 64;              // tokens per chunk: 4 MFMA k-steps of 16
-constexpr int kRound = 8;            // chunks per pipeline round (segments are whole rounds)
+constexpr int kRound = 4;            // chunks per pipeline round (segments are whole rounds)
 constexpr int kThreads = 512;        // 8 waves
-constexpr int kXStages = 8;          // X ring depth
+constexpr int kXStages = 4;          // X ring depth
 constexpr int kXAhead = kXStages - 1;
-constexpr int kXStageBytes = kBK * kBN * 2;   // 16 KB
+constexpr int kXStageBytes = kBK * kBN * 2;   // 32 KB
 constexpr int kAAhead = 3;           // chunks of the dY operand in flight (registers)
 constexpr int kMaxGroups = 8;
 constexpr int kMaxMats = 16;
@@ -65,14 +65,16 @@ constexpr int kXcds = 8;
 constexpr int64_t kSlotFloats = int64_t(kMaxTiles) * 32 * kBN;   // one partial output tile
 constexpr int kGatherTokens = 256;
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset beyond every resource size
-// Memory instructions a wave issues per chunk: 4 operand loads + 2 X copies.
-constexpr int kLoadsA = 4, kCopiesX = 2;
-// Stores a wave issues per segment epilogue: up to 2 column blocks x 4 float4.
-constexpr int kEpiStores = 8;
-// Loads a wave may leave in flight when chunk j's operands must have landed:
-// the copies issued after the operand loads of chunk j, in the same round,
-// and the two rounds that follow.
-constexpr int kInFlight = kCopiesX + (kAAhead - 1) * (kLoadsA + kCopiesX);
+// Memory instructions a wave issues per chunk: 4 operand loads + 4 X copies.
+constexpr int kLoadsA = 4, kCopiesX = 4;
+// Stores a wave issues per segment epilogue: 4 column blocks x 4 float4.
+constexpr int kEpiStores = 16;
+// Loads a wave may leave in flight when chunk j's data must have landed: the
+// operand loads and copies of chunks j+1 and j+2 (issued after those of
+// chunk j, which go out together, operands first, kAAhead = kXAhead chunks
+// ahead).
+static_assert(kAAhead == kXAhead, "operands and X travel together");
+constexpr int kInFlight = (kXAhead - 1) * (kLoadsA + kCopiesX);
 
 struct DwMatDev {
     const uint16_t *dY;
@@ -210,10 +212,6 @@ __shared__ __attribute__((aligned(1024))) uint8_t xs0[kXStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t xs1[kXStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t xs2[kXStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t xs3[kXStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t xs4[kXStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t xs5[kXStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t xs6[kXStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t xs7[kXStageBytes];
 
 template <int S>
 __device__ __forceinline__ uint8_t *xstage() {
@@ -221,11 +219,7 @@ __device__ __forceinline__ uint8_t *xstage() {
     if constexpr (S == 0) return xs0;
     else if constexpr (S == 1) return xs1;
     else if constexpr (S == 2) return xs2;
-    else if constexpr (S == 3) return xs3;
-    else if constexpr (S == 4) return xs4;
-    else if constexpr (S == 5) return xs5;
-    else if constexpr (S == 6) return xs6;
-    else return xs7;
+    else return xs3;
 }
 
 template <int V>
@@ -291,38 +285,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
 
     // ---- the group table (constant indices only: a run-time index into the
     // kernel argument would make the compiler copy it to scratch)
-    if (tid == 0) {
+    // (one wave per entry: each wave's copy is independent of the others)
 #pragma unroll
-        for (int g = 0; g < kMaxGroups; ++g)
-            if (g < p.n_groups) gs[g] = p.g[g];
+    for (int g = 0; g < kMaxGroups; ++g)
+        if (wave == g && lane == 0) gs[g] = p.g[g];
 #pragma unroll
-        for (int m = 0; m < kMaxMats; ++m) outp[m] = p.m[m].out;
-    }
+    for (int m = 0; m < kMaxMats; ++m)
+        if (wave == (m & 7) && lane == 1 + (m >> 3)) outp[m] = p.m[m].out;
     __syncthreads();
 
-    // ---- the slice's segments (one per output tile it touches)
+    // ---- the slice's segments (one per output tile it touches); 32-bit
+    // arithmetic (the host keeps the iteration count below 2^31)
     if (tid == 0) {
-        int64_t it = it_lo;
+        int32_t it = static_cast<int32_t>(it_lo);
+        const int32_t hi = static_cast<int32_t>(it_hi);
         int n = 0;
         int32_t j = 0;
-        while (it < it_hi && n < kMaxSegs) {
+        while (it < hi && n < kMaxSegs) {
             int gi = 0;
-            while (gi + 1 < p.n_groups && it >= gs[gi + 1].it_begin) ++gi;
+            while (gi + 1 < p.n_groups && it >= static_cast<int32_t>(gs[gi + 1].it_begin)) ++gi;
             const DwGroupDev &G = gs[gi];
-            const int64_t rel = it - G.it_begin;
-            const int32_t tile = static_cast<int32_t>(rel / G.chunks);
-            const int32_t k0 = static_cast<int32_t>(rel % G.chunks);
-            const int64_t tile_end = G.it_begin + static_cast<int64_t>(tile + 1) * G.chunks;
-            const int64_t end = min(tile_end, it_hi);
+            const int32_t rel = it - static_cast<int32_t>(G.it_begin);
+            const int32_t tile = rel / G.chunks;
+            const int32_t k0 = rel - tile * G.chunks;
+            const int32_t tile_end = static_cast<int32_t>(G.it_begin) + (tile + 1) * G.chunks;
+            const int32_t end = min(tile_end, hi);
             const int32_t mb = tile / G.n_nblk;
             Seg sg;
             sg.g = gi;
-            sg.nb = tile % G.n_nblk;
-            sg.p0 = mblk_lo(G, mb);
-            sg.mt = mblk_lo(G, mb + 1) - sg.p0;
+            sg.nb = tile - mb * G.n_nblk;
+            sg.p0 = mb * G.n_ptiles / G.n_mblk;
+            sg.mt = (mb + 1) * G.n_ptiles / G.n_mblk - sg.p0;
             sg.k0 = k0;
             sg.j0 = j;
-            sg.len = static_cast<int32_t>(end - it);
+            sg.len = end - it;
             const bool whole = (k0 == 0 && end == tile_end);
             sg.slot = whole ? -1 : (n == 0 ? static_cast<int32_t>(2 * v) : static_cast<int32_t>(2 * v + 1));
             segs[n++] = sg;
@@ -333,20 +329,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     }
     __syncthreads();
     const int nseg = s_nseg;
-    for (int sg = 0; sg < nseg; ++sg) {
-        const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[sg].g);
-        const int32_t *map = gs[gsg].rowmap + segs[sg].p0 * 32;
-        const int32_t n = segs[sg].mt * 32;
-        for (int r = tid; r < kMaxTiles * 32; r += kThreads) codes[sg][r] = r < n ? map[r] : -1;
-    }
-    __syncthreads();
     const int32_t J = segs[nseg - 1].j0 + segs[nseg - 1].len;
     float *const sink = p.sink + (v * 8 + wave) * 16;
 
-    // ---- X copies.  Copy k of a chunk (k = 0, 1) holds token rows 4q..4q+3,
-    // q = wave + 8k; lane slot l%16 of row 4q + l/16 holds the 16-byte column
-    // group (l%16) ^ 2*(row%4) (a swizzle that makes the transposing reads of
-    // 4 consecutive rows hit distinct banks).  The buffer resource's base
+    // ---- X copies.  A chunk is 64 token rows x 256 columns (512 bytes a
+    // row); copy k (k = 0..3) of a wave holds rows 2q, 2q+1, q = wave + 8k.
+    // Lane slot l%32 of row 2q + l/32 holds the 16-byte column group
+    // (l%32) ^ 2*(row%4) (a swizzle that makes the transposing reads of 4
+    // consecutive rows hit distinct banks).  The buffer resource's base
     // advances by one chunk per chunk (scalar work); rows past T fall beyond
     // its size and columns past C get an offset beyond any size, so the range
     // check turns them into zeros.
@@ -363,10 +353,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         x_rem = static_cast<int64_t>(uniform64(static_cast<uint64_t>((G.T - r0) * C * 2 - c0 * 2)));
         x_stride = static_cast<int64_t>(uniform64(static_cast<uint64_t>(kBK * C * 2)));
         x_j0 = __builtin_amdgcn_readfirstlane(S.j0);
-        const int grp = (lane & 15) ^ (2 * (lane >> 4));
 #pragma unroll
         for (int k = 0; k < kCopiesX; ++k) {
-            const int row_in = 4 * (wave + 8 * k) + (lane >> 4);
+            const int row_in = 2 * (wave + 8 * k) + (lane >> 5);
+            const int grp = (lane & 31) ^ (2 * (row_in & 3));
             x_voff[k] = (c0 + 8 * grp < C) ? static_cast<uint32_t>((row_in * C + 8 * grp) * 2) : kOutside;
         }
     };
@@ -383,14 +373,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         dma16_buf(x_base + (jx < J ? off : 0), size, x_voff[k], stage + (wave + 8 * k) * 1024);
     };
 
-    // ---- wave layout of a segment with mt packed tiles: NC = 1 or 2 column
-    // blocks per wave, so that 4/NC waves share a tile and the SIMDs run two
-    // waves each (one wave per SIMD is bound by the latency of its operand
-    // reads).  Wave w takes tile w / (4/NC) and column blocks
-    // (w % (4/NC)) * NC .. + NC - 1; waves past the tiles only copy.  (Four
-    // column blocks per wave and 8-tile M-blocks would need more than the 256
-    // registers a wave has at two waves per SIMD.)
-    auto nc_of = [](int mt) __attribute__((always_inline)) { return mt <= 2 ? 1 : 2; };
+    // ---- wave layout: wave w takes packed tile w/2 of the M-block and the
+    // column half w%2 (four 32-column blocks); waves past the M-block's tiles
+    // only copy.
+    const int tw = wave >> 1, ch = wave & 1;
 
     // ---- dY operand: 4 KB per (packed tile, chunk); k-step kk is the 1 KB
     // at 512*kk elements, lane l's 16 bytes at 8*l.  Loads go through a buffer
@@ -404,10 +390,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     auto describe_a = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
-        const int t = wave / (4 / nc_of(S.mt));
-        a_live = t < S.mt;
+        a_live = tw < S.mt;
         a_base = reinterpret_cast<const uint16_t *>(uniform64(reinterpret_cast<uint64_t>(
-            G.at + (static_cast<int64_t>(S.p0 + (a_live ? t : 0)) * (G.Tp / 8) + 8 * static_cast<int64_t>(S.k0)) * 256)));
+            G.at + (static_cast<int64_t>(S.p0 + (a_live ? tw : 0)) * (G.Tp / 8) + 8 * static_cast<int64_t>(S.k0)) * 256)));
         a_j0 = __builtin_amdgcn_readfirstlane(S.j0);
     };
     auto issue_a = [&](int32_t ja, bf16x8 (&buf)[4]) __attribute__((always_inline)) {
@@ -431,17 +416,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int s16 = lane & 15;
     const int trow = 8 * (lane >> 5) + (s16 >> 2);
     const int xcp = ((lane >> 4) & 1) * 16 + 4 * (s16 & 3);   // column inside a 32-column block
-    auto xoff_of = [&](int cb) __attribute__((always_inline)) {
-        return 8 * ((4 * cb + (xcp >> 3)) ^ (2 * (s16 >> 2))) + (xcp & 7);
-    };
+    int xo[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int cb = 4 * ch + c;
+        xo[c] = 8 * ((4 * cb + (xcp >> 3)) ^ (2 * (s16 >> 2))) + (xcp & 7);
+    }
 
     // Accumulators: acc[c] = X-block^T . dY-tile for the wave's c-th column
     // block, so lane l register r holds column 8*(r/4) + 4*(l/32) + r%4 of the
     // block for packed row l%32: four consecutive columns per register quad,
     // stored as one float4.
-    floatx16 acc[2];
+    floatx16 acc[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
@@ -450,14 +438,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         else SFT_WAIT_VMCNT(kInFlight + kEpiStores);
     };
 
-    // One chunk, u = jj mod 8 (a constant): reads stage u and A buffer u%4;
-    // the operand loads of chunk jj+3 go to buffer (u+3)%4 (chunk jj-1's) and
-    // the copies of chunk jj+7 to stage (u+7)%8 (chunk jj-1's).  `two` (wave
-    // uniform) selects the second column block; one code path serves both
-    // layouts, so the registers of loads in flight never move.
+    // One chunk, u = jj mod 4 (a constant): reads stage u and A buffer u; the
+    // operand loads and copies of chunk jj+3 go to buffer (u+3)%4 and stage
+    // (u+3)%4 (chunk jj-1's), one copy after each k-step.
     bf16x8 ab[kAAhead + 1][4];
-    auto step = [&](auto u_tag, int32_t jj, int n_wait, bool active, bool two, const int (&xo)[2])
-                    __attribute__((always_inline)) {
+    auto step = [&](auto u_tag, int32_t jj, int n_wait, bool active) __attribute__((always_inline)) {
         constexpr int U = decltype(u_tag)::value;
         const uint16_t *X = reinterpret_cast<const uint16_t *>(xstage<U>());
         uint8_t *st_dma = xstage<(U + kXAhead) % kXStages>();
@@ -468,131 +453,123 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         issue_a(jj + kAAhead, ab[(U + kAAhead) % (kAAhead + 1)]);
         const int32_t jx = jj + kXAhead;
         advance_x(jx);
-        auto bfrag = [&](int kk, int c) __attribute__((always_inline)) {
+        auto bfrag = [&](int kk, bf16x8 (&b)[4]) __attribute__((always_inline)) {
             const int r0 = 16 * kk + trow;
-            const short4v lo = lds_tr16(X + r0 * kBN + xo[c]);
-            const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xo[c]);
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const short4v lo = lds_tr16(X + r0 * kBN + xo[c]);
+                const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xo[c]);
+                b[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
         };
         // The X copies are issued on every path (only the MFMA work is
         // conditional), so the compiler's count of operations in flight is
         // exact; they sit between k-steps to overlap the matrix cores.
-        bf16x8 bc0, bc1, bn0, bn1;
-        if (active) {
-            bc0 = bfrag(0, 0);
-            if (two) bc1 = bfrag(0, 1);
-        }
+        bf16x8 bc[4], bn[4];
+        if (active) bfrag(0, bc);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if (active) {
+                if (kk < 3) bfrag(kk + 1, bn);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[c], a[kk], acc[c], 0, 0, 0);
                 if (kk < 3) {
-                    bn0 = bfrag(kk + 1, 0);
-                    if (two) bn1 = bfrag(kk + 1, 1);
-                }
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc0, a[kk], acc[0], 0, 0, 0);
-                if (two) acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc1, a[kk], acc[1], 0, 0, 0);
-                if (kk < 3) {
-                    bc0 = bn0;
-                    bc1 = bn1;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) bc[c] = bn[c];
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (kk < kCopiesX) issue_x(jx, kk, st_dma);
+            issue_x(jx, kk, st_dma);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // A round of 8 chunks; the first three wait for `extra` more operations.
-    auto round8 = [&](int32_t jq, bool active, bool two, const int (&xo)[2], int extra)
-                      __attribute__((always_inline)) {
-        step(ic<0>{}, jq + 0, kInFlight + extra, active, two, xo);
-        step(ic<1>{}, jq + 1, kInFlight + extra, active, two, xo);
-        step(ic<2>{}, jq + 2, kInFlight + extra, active, two, xo);
-        step(ic<3>{}, jq + 3, kInFlight, active, two, xo);
-        step(ic<4>{}, jq + 4, kInFlight, active, two, xo);
-        step(ic<5>{}, jq + 5, kInFlight, active, two, xo);
-        step(ic<6>{}, jq + 6, kInFlight, active, two, xo);
-        step(ic<7>{}, jq + 7, kInFlight, active, two, xo);
+    static_assert(kCopiesX == 4 && kRound == kXStages, "one copy per k-step; stages rotate once a round");
+    // A round of 4 chunks; the first three wait for `extra` more operations.
+    auto round4 = [&](int32_t jq, bool active, int extra) __attribute__((always_inline)) {
+        step(ic<0>{}, jq + 0, kInFlight + extra, active);
+        step(ic<1>{}, jq + 1, kInFlight + extra, active);
+        step(ic<2>{}, jq + 2, kInFlight + extra, active);
+        step(ic<3>{}, jq + 3, kInFlight, active);
     };
 
-    // Segment epilogue: every wave issues 8 float4 stores whatever its
-    // layout (masked-off lanes and an unused second block write to the
-    // sink).  A whole tile goes to dW_act through the row map; a partial one
-    // to its slot, row = tile*32 + packed row.
-    auto epilogue = [&](int sg, int t, int cb0, bool two) __attribute__((always_inline)) {
+    // Segment epilogue: every wave issues 16 float4 stores (masked-off lanes
+    // write to the sink).  A whole tile goes to dW_act through the row map; a
+    // partial one to its slot, row = tile*32 + packed row.
+    auto epilogue = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
         const int i = lane & 31, h = lane >> 5;
-        const int32_t code = t < S.mt ? codes[sg][t * 32 + i] : -1;
+        const int32_t code = tw < S.mt ? codes[sg][tw * 32 + i] : -1;
         const int64_t c0 = static_cast<int64_t>(S.nb) * kBN;
         float *rowp = sink;
         if (code >= 0)
             rowp = S.slot < 0 ? outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C + c0
-                              : p.part + S.slot * kSlotFloats + (t * 32 + i) * kBN;
+                              : p.part + S.slot * kSlotFloats + (tw * 32 + i) * kBN;
 #pragma unroll
         for (int q = 0; q < kEpiStores; ++q) {
             const int c = q / 4, a = q % 4;
-            const int cl = 32 * (cb0 + c) + 8 * a + 4 * h;
-            const bool ok = (c == 0 || two) && code >= 0 && (S.slot >= 0 || c0 + cl < G.C);
+            const int cl = 32 * (4 * ch + c) + 8 * a + 4 * h;
+            const bool ok = code >= 0 && (S.slot >= 0 || c0 + cl < G.C);
             auto *dst = reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(
                 reinterpret_cast<uintptr_t>(ok ? rowp + cl : sink));
             *dst = f32x4{acc[c][4 * a], acc[c][4 * a + 1], acc[c][4 * a + 2], acc[c][4 * a + 3]};
         }
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
     };
 
-    // ---- prologue: X copies of chunks 0..6 and operands of chunks 0..2, in
-    // the order the steady state issues them, then 8 stores to the sink so
-    // that every segment, the first included, starts behind an epilogue.
+    // ---- prologue: operands and X copies of chunks 0..2, in the order the
+    // steady state issues them, then 16 stores to the sink so that every
+    // segment, the first included, starts behind an epilogue.
     describe_x(0);
     describe_a(0);
-    auto prologue_x = [&](auto s_tag) __attribute__((always_inline)) {
+    auto prologue = [&](auto s_tag) __attribute__((always_inline)) {
         constexpr int S = decltype(s_tag)::value;
+        issue_a(S, ab[S]);
         advance_x(S);
 #pragma unroll
         for (int k = 0; k < kCopiesX; ++k) issue_x(S, k, xstage<S>());
     };
-    static_assert(kXAhead == 7 && kAAhead == 3, "prologue order");
-    prologue_x(ic<0>{});
-    prologue_x(ic<1>{});
-    prologue_x(ic<2>{});
-    prologue_x(ic<3>{});
-    issue_a(0, ab[0]);
-    prologue_x(ic<4>{});
-    issue_a(1, ab[1]);
-    prologue_x(ic<5>{});
-    issue_a(2, ab[2]);
-    prologue_x(ic<6>{});
+    static_assert(kXAhead == 3, "prologue order");
+    prologue(ic<0>{});
+    prologue(ic<1>{});
+    prologue(ic<2>{});
 #pragma unroll
     for (int q = 0; q < kEpiStores; ++q)
         *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(reinterpret_cast<uintptr_t>(sink)) = f32x4{};
 
-    // ---- the segments.  The first round of each waits for 8 more memory
+    // ---- the output map of the slice's tiles, fetched while the first
+    // chunks are in flight (the wait for it covers them too)
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[sg].g);
+        const int32_t *map = gs[gsg].rowmap + segs[sg].p0 * 32;
+        const int32_t n = segs[sg].mt * 32;
+        for (int r = tid; r < kMaxTiles * 32; r += kThreads) codes[sg][r] = r < n ? map[r] : -1;
+    }
+    __syncthreads();
+
+    // ---- the segments.  The first round of each waits for 16 more memory
     // operations in its first three chunks (the epilogue's stores sit behind
-    // their operand loads).
+    // their loads).
     for (int sg = 0; sg < nseg; ++sg) {
         const int32_t j0 = segs[sg].j0, len = segs[sg].len;
-        const bool two = nc_of(segs[sg].mt) == 2;
-        const int wpt = two ? 2 : 4;
-        const int t = wave / wpt, cb0 = (wave % wpt) * (two ? 2 : 1);
-        const bool active = t < segs[sg].mt;
-        int xo[2];
-        xo[0] = xoff_of(cb0);
-        xo[1] = xoff_of(two ? cb0 + 1 : cb0);
-        round8(j0, active, two, xo, kEpiStores);
-        for (int32_t jq = j0 + kRound; jq < j0 + len; jq += kRound) round8(jq, active, two, xo, 0);
-        epilogue(sg, t, cb0, two);
+        const bool active = tw < segs[sg].mt;
+        round4(j0, active, kEpiStores);
+        for (int32_t jq = j0 + kRound; jq < j0 + len; jq += kRound) round4(jq, active, 0);
+        epilogue(sg);
     }
     // Copies past the slice are still in flight (they write zeros to LDS):
-    // drain before the workgroup's LDS can be handed to another.
-    SFT_WAIT_VMCNT(0);
+    // drain them before the workgroup's LDS can be handed to another (the
+    // last epilogue's stores, issued after them, may stay in flight).
+    SFT_WAIT_VMCNT(kEpiStores);
 }
 
 // Combination of the partial tiles: an output tile cut by slice boundaries
 // is the sum of its slices' partial rows, added in slice order.  One
-// workgroup per (output tile, 8 packed rows); a lane adds 4 columns.  The
+// workgroup per (output tile, 4 packed rows); a lane adds 4 columns.  The
 // tile bookkeeping is wave-uniform (scalar); a lane issues its partial loads
 // and its row-map load together, so the kernel is one memory round trip.
 __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
@@ -611,9 +588,9 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     if (v_first == v_last) return;  // the tile lies inside one slice: written directly
     const int32_t mb = tile / G.n_nblk, nb = tile % G.n_nblk;
     const int32_t p0 = mblk_lo(G, mb), mt = mblk_lo(G, mb + 1) - p0;
-    const int prow = blockIdx.y * 8 + (threadIdx.x >> 5);
+    const int prow = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (prow >= mt * 32) return;
-    const int cl = (threadIdx.x & 31) * 4;
+    const int cl = (threadIdx.x & 63) * 4;
     const int64_t col = static_cast<int64_t>(nb) * kBN + cl;
     if (col >= G.C) return;
     // The first slice started before the tile (its last segment: odd slot);
@@ -705,6 +682,7 @@ struct Launch {
 
 struct Plan {
     std::vector<Launch> launches;
+    bool too_big = false;      // a launch would exceed 2^31 (tile, chunk) iterations
     size_t part_bytes = 0, sink_bytes = 0, at_bytes = 0;
     size_t ws_bytes() const { return part_bytes + sink_bytes + at_bytes; }
 };
@@ -839,6 +817,10 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             L.gather_blocks = std::max(L.gather_blocks, d.Tp / kGatherTokens);
         }
         if (p.n_groups == 0) break;
+        if (iters >= (int64_t(1) << 31)) {
+            plan.too_big = true;
+            break;
+        }
         // One workgroup per CU; more (whole rounds) only if a slice would cross
         // more output tiles than the kernel tracks; never more slices than rounds.
         int64_t P = cus;
@@ -879,13 +861,19 @@ extern "C" {
 size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups) {
     sft::clear_error();
     if (validate(groups, n_groups) != SFT_OK) return static_cast<size_t>(-1);
-    return make_plan(groups, n_groups).ws_bytes();
+    const Plan plan = make_plan(groups, n_groups);
+    if (plan.too_big) {
+        sft::fail(SFT_ENOTSUP, "sft_masked_dw: more than 2^31 (tile, chunk) iterations in one launch");
+        return static_cast<size_t>(-1);
+    }
+    return plan.ws_bytes();
 }
 
 int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream) {
     sft::clear_error();
     if (int rc = validate(groups, n_groups)) return rc;
     Plan plan = make_plan(groups, n_groups);
+    SFT_CHECK(!plan.too_big, SFT_ENOTSUP, "sft_masked_dw: more than 2^31 (tile, chunk) iterations in one launch");
     if (plan.launches.empty()) return SFT_OK;
     SFT_CHECK(ws_bytes >= plan.ws_bytes(), SFT_ECAPACITY, "sft_masked_dw: workspace %zu < %zu bytes", ws_bytes,
               plan.ws_bytes());
@@ -900,7 +888,7 @@ int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t
         hipLaunchKernelGGL(k_masked_dw, dim3(static_cast<uint32_t>(L.p.n_wg)), dim3(kThreads), 0, st, L.p);
         e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
-        hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(L.out_tiles), kMaxTiles * 32 / 8), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(L.out_tiles), kMaxTiles * 32 / 4), dim3(256), 0, st,
                            L.p);
         e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: fix-up launch failed: %s", hipGetErrorString(e));
