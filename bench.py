@@ -68,7 +68,7 @@ class Layer:
         shapes = synth.LLAMA7B
         self.mats = {}
         host_chunks = []   # packed plan: int32 words, uploaded once per step
-        layout = {}
+        offsets = {}      # per matrix: word offset and length of each plan part
         off = 0
         for mi, (name, (R, C)) in enumerate(shapes.items()):
             k = round(density * R)
@@ -82,9 +82,9 @@ class Layer:
             parts = {"rows": plan.active_rows, "tiles": plan.active_tiles,
                      "abits": plan.active_bits.view(np.int32), "first": plan.tile_first, "slot": slot,
                      "fresh": np.frombuffer(np.pad(fresh, (0, (-fresh.size) % 4)).tobytes(), np.int32)}
-            layout[name] = {}
+            offsets[name] = {}
             for key, arr in parts.items():
-                layout[name][key] = (off, arr.size)
+                offsets[name][key] = (off, arr.size)
                 host_chunks.append(arr.astype(np.int32, copy=False))
                 off += arr.size
             self.mats[name] = {"R": R, "C": C, "plan": plan}
@@ -107,7 +107,7 @@ class Layer:
             for name in members:
                 m = self.mats[name]
                 R, C, plan = m["R"], m["C"], m["plan"]
-                lay = layout[name]
+                lay = offsets[name]
 
                 def view(key, n=None, dtype=None):
                     o, sz = lay[key]
