@@ -225,11 +225,12 @@ size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
  *                  bytes (16-byte aligned; no initialisation needed).  Calls
  *                  that share a workspace must be ordered on one stream.
  * Limits: T >= 1, T < 2^31, C % 8 == 0, R < 2^31, n_active < 2^24, at most
- * 16 matrices per group.  Results are deterministic
+ * 16 matrices per group, fewer than 2^31 (output tile, 64-token chunk)
+ * iterations per launch of 8 groups.  Results are deterministic
  * (a fixed summation order for every launch configuration the same inputs
  * produce).
  * Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_ECAPACITY (ws too small),
- * SFT_EHIP.
+ * SFT_ENOTSUP (beyond the limits above), SFT_EHIP.
  */
 int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes,
                   void *stream);

@@ -106,7 +106,7 @@ struct DwParams {
     DwMatDev m[kMaxMats];
     int32_t n_groups;
     int32_t n_wg;           // slices (= workgroups of the product)
-    int64_t iters;          // total (output tile, chunk) iterations, a multiple of 8
+    int64_t iters;          // total (output tile, chunk) iterations, a multiple of kRound
     float *part;            // [2 * n_wg] partial tiles of kSlotFloats
     float *sink;            // [n_wg * 8] x 16 floats: target of masked-off stores
 };
@@ -115,7 +115,7 @@ struct Seg {
     int32_t g, nb, mt, p0;
     int32_t k0;     // first chunk of the output tile in this slice
     int32_t j0;     // first local iteration of the segment
-    int32_t len;    // chunks (a multiple of 8)
+    int32_t len;    // chunks (whole rounds)
     int32_t slot;   // -1: whole tile (final output); else partial slot
 };
 
@@ -199,8 +199,17 @@ __global__ __launch_bounds__(256) void k_dw_gather(const DwParams p) {
 
 // Slice of workgroup v: global iterations [lo, hi), on whole rounds (output
 // tiles are whole rounds too, so every segment is whole rounds).
+// floor(n / d) for 0 <= n, d < 2^53 through one correctly rounded fp64
+// division (a few instructions where a 64-bit integer division is a long
+// scalar routine): n/d = k + f with f <= 1 - 1/d, and the rounding error is
+// at most (n/d)*2^-53 < 1/d, so the rounded quotient stays below k + 1.
+__device__ __forceinline__ int64_t floordiv53(int64_t n, int64_t d) {
+    return static_cast<int64_t>(static_cast<double>(n) / static_cast<double>(d));
+}
+
+// Slice v starts at round floor(v * Q / n_wg), Q = iters / kRound rounds.
 __device__ __forceinline__ int64_t slice_lo(const DwParams &p, int64_t v) {
-    return kRound * (v * (p.iters / kRound) / p.n_wg);
+    return kRound * floordiv53(v * (p.iters / kRound), p.n_wg);
 }
 
 // The X ring: one LDS variable per stage.  The compiler's wait insertion can
@@ -259,14 +268,14 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 // s_waitcnt lgkmcnt(0) leaving vmcnt and expcnt free.
 #define SFT_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-// Output tile = (M-block, 128 columns) of a group; a chunk is 64 tokens.
+// Output tile = (M-block, 256 columns) of a group; a chunk is 64 tokens.
 //
 // Per chunk j every wave: waits until its own copies and operand loads of
 // chunk j have landed (an exact s_waitcnt: every wave issues the same memory
 // instructions in the same order every chunk, masked-off work included), joins
 // a bare s_barrier (all copies of chunk j landed; all reads of chunk j-1
 // done), issues the operand loads of chunk j+3 and, between its MFMA k-steps,
-// the X copies of chunk j+7 into the stage chunk j-1 used.  Segment epilogues
+// the X copies of chunk j+3 into the stage chunk j-1 used.  Segment epilogues
 // store unconditionally too (masked-off lanes write to a per-wave sink), so
 // the compiler's own waits stay exact as well.
 __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
@@ -494,25 +503,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     };
 
     // Segment epilogue: every wave issues 16 float4 stores (masked-off lanes
-    // write to the sink).  A whole tile goes to dW_act through the row map; a
-    // partial one to its slot, row = tile*32 + packed row.
+    // write to the sink).  A whole tile goes to dW_act through the row map,
+    // row-major.  A partial one goes to its slot in fragment order: store q
+    // of wave (tw, ch) fills the 1 KB fragment (tw*2 + ch)*16 + q, lane l's
+    // 16 bytes at 16*l, so each of those stores is one contiguous kilobyte.
     auto epilogue = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
-        const int i = lane & 31, h = lane >> 5;
-        const int32_t code = tw < S.mt ? codes[sg][tw * 32 + i] : -1;
+        const int h = lane >> 5;
+        const int32_t code = tw < S.mt ? codes[sg][tw * 32 + (lane & 31)] : -1;
         const int64_t c0 = static_cast<int64_t>(S.nb) * kBN;
-        float *rowp = sink;
+        const bool part = S.slot >= 0;
+        float *base = sink;
         if (code >= 0)
-            rowp = S.slot < 0 ? outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C + c0
-                              : p.part + S.slot * kSlotFloats + (tw * 32 + i) * kBN;
+            base = part ? p.part + S.slot * kSlotFloats + ((tw * 2 + ch) * kEpiStores * 64 + lane) * 4
+                        : outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C + c0 + 128 * ch + 4 * h;
 #pragma unroll
         for (int q = 0; q < kEpiStores; ++q) {
             const int c = q / 4, a = q % 4;
-            const int cl = 32 * (4 * ch + c) + 8 * a + 4 * h;
-            const bool ok = code >= 0 && (S.slot >= 0 || c0 + cl < G.C);
+            const bool ok = code >= 0 && (part || c0 + 32 * (4 * ch + c) + 8 * a + 4 * h < G.C);
+            const int off = part ? 256 * q : 32 * c + 8 * a;
             auto *dst = reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(
-                reinterpret_cast<uintptr_t>(ok ? rowp + cl : sink));
+                reinterpret_cast<uintptr_t>(ok ? base + off : sink));
             *dst = f32x4{acc[c][4 * a], acc[c][4 * a + 1], acc[c][4 * a + 2], acc[c][4 * a + 3]};
         }
 #pragma unroll
@@ -569,9 +581,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
 
 // Combination of the partial tiles: an output tile cut by slice boundaries
 // is the sum of its slices' partial rows, added in slice order.  One
-// workgroup per (output tile, 4 packed rows); a lane adds 4 columns.  The
-// tile bookkeeping is wave-uniform (scalar); a lane issues its partial loads
-// and its row-map load together, so the kernel is one memory round trip.
+// workgroup per (output tile, 32 packed rows); a lane adds 4 columns of 8
+// rows.  The tile bookkeeping is wave-uniform; a lane issues its row-map
+// loads and the partial loads of its rows for the first four slices
+// together, so the kernel is one memory round trip for tiles cut up to
+// four ways.
 __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     const int64_t ot = blockIdx.x;
     int gi = 0;
@@ -579,52 +593,73 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     const DwGroupDev &G = p.g[gi];
     const int32_t tile = static_cast<int32_t>(ot - G.otile_begin);
     const int64_t A = G.it_begin + static_cast<int64_t>(tile) * G.chunks;   // first iteration
-    const int64_t B = A + G.chunks;                                           // one past the last
-    // slices covering [A, B): slice v starts at 8*floor(v*Q/P), Q = iters/8
-    // (A and B are multiples of 8)
-    const int64_t Q = p.iters / kRound, P = p.n_wg;
-    const int32_t v_first = static_cast<int32_t>(((A / kRound + 1) * P - 1) / Q);
-    const int32_t v_last = static_cast<int32_t>(((B / kRound) * P - 1) / Q);
-    if (v_first == v_last) return;  // the tile lies inside one slice: written directly
+    const int64_t a = A / kRound, b = a + G.chunks / kRound;                  // its rounds [a, b)
     const int32_t mb = tile / G.n_nblk, nb = tile % G.n_nblk;
+    // Slices covering rounds [a, b): slice v starts at or before round r
+    // exactly when floor(v * Q / P) < r + 1, i.e. when v <= ((r + 1) * P - 1) / Q.
+    const int64_t Q = p.iters / kRound, P = p.n_wg;
+    const int32_t v_first = static_cast<int32_t>(floordiv53((a + 1) * P - 1, Q));
+    const int32_t v_last = static_cast<int32_t>(floordiv53(b * P - 1, Q));
+    if (v_first == v_last) return;  // the tile lies inside one slice: written directly
     const int32_t p0 = mblk_lo(G, mb), mt = mblk_lo(G, mb + 1) - p0;
-    const int prow = blockIdx.y * 4 + (threadIdx.x >> 6);
-    if (prow >= mt * 32) return;
-    const int cl = (threadIdx.x & 63) * 4;
-    const int64_t col = static_cast<int64_t>(nb) * kBN + cl;
-    if (col >= G.C) return;
-    // The first slice started before the tile (its last segment: odd slot);
-    // every later one starts inside it (first segment: even slot).
-    const bool first_odd = slice_lo(p, v_first) < A;
-    const float *part = p.part + prow * kBN + cl;
-    const int32_t code = G.rowmap[p0 * 32 + prow];
-    float4 x[4];
+    const int tw = blockIdx.y;
+    if (tw >= mt) return;   // past the M-block's packed tiles
+    // The first slice started before the tile (its last segment: odd slot)
+    // unless it starts at round a; every later one starts inside the tile
+    // (first segment: even slot).
+    const bool first_odd = floordiv53(static_cast<int64_t>(v_first) * Q, P) < a;
+    // Partial slots hold the product's fragments: fragment f = (tw*2 + ch)*16
+    // + 4*c + a (1 KB), lane l's 4 floats at 4*l, are columns
+    // 32*(4*ch + c) + 8*a + 4*(l/32) .. +3 of packed row tw*32 + l%32.  Thread
+    // t takes lane t%64 of fragments tw*32 + t/64 + 4*i, i = 0..7: one row,
+    // eight 4-column pieces, all loads before the sums.
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int32_t code = G.rowmap[p0 * 32 + tw * 32 + (lane & 31)];
+    const float *part = p.part + (tw * 32 + (threadIdx.x >> 6)) * 256 + lane * 4;
+    constexpr int kRows = 8;
+    float4 x[4][kRows];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int32_t vv = v_first + i;
-        const int64_t slot = (i == 0 && first_odd) ? 2 * static_cast<int64_t>(vv) + 1 : 2 * static_cast<int64_t>(vv);
-        if (vv <= v_last) x[i] = *reinterpret_cast<const float4 *>(part + slot * kSlotFloats);
+    for (int c = 0; c < 4; ++c) {
+        const int32_t vv = v_first + c;
+        const int64_t slot = (c == 0 && first_odd) ? 2 * static_cast<int64_t>(vv) + 1 : 2 * static_cast<int64_t>(vv);
+        if (vv <= v_last) {
+#pragma unroll
+            for (int i = 0; i < kRows; ++i)
+                x[c][i] = *reinterpret_cast<const float4 *>(part + slot * kSlotFloats + 4 * i * 256);
+        }
     }
-    float4 sum = x[0];
+    float4 sum[kRows];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) {
-        if (v_first + i <= v_last) {
-            sum.x += x[i].x;
-            sum.y += x[i].y;
-            sum.z += x[i].z;
-            sum.w += x[i].w;
+    for (int i = 0; i < kRows; ++i) {
+        sum[i] = x[0][i];
+#pragma unroll
+        for (int c = 1; c < 4; ++c) {
+            if (v_first + c <= v_last) {
+                sum[i].x += x[c][i].x;
+                sum[i].y += x[c][i].y;
+                sum[i].z += x[c][i].z;
+                sum[i].w += x[c][i].w;
+            }
         }
     }
     for (int32_t vv = v_first + 4; vv <= v_last; ++vv) {
-        const float4 y = *reinterpret_cast<const float4 *>(part + 2 * static_cast<int64_t>(vv) * kSlotFloats);
-        sum.x += y.x;
-        sum.y += y.y;
-        sum.z += y.z;
-        sum.w += y.w;
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const float4 y = *reinterpret_cast<const float4 *>(part + 2 * static_cast<int64_t>(vv) * kSlotFloats + 4 * i * 256);
+            sum[i].x += y.x;
+            sum[i].y += y.y;
+            sum[i].z += y.z;
+            sum[i].w += y.w;
+        }
     }
     if (code < 0) return;
-    float *out = p.m[code >> 24].out;
-    *reinterpret_cast<float4 *>(out + static_cast<int64_t>(code & 0xFFFFFF) * G.C + col) = sum;
+    float *out = p.m[code >> 24].out + static_cast<int64_t>(code & 0xFFFFFF) * G.C + static_cast<int64_t>(nb) * kBN;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        const int f = (threadIdx.x >> 6) + 4 * i;   // (ch*4 + c)*4 + a
+        const int cl = 32 * (f >> 2) + 8 * (f & 3) + 4 * h;   // block ch*4 + c, piece a, half h
+        if (static_cast<int64_t>(nb) * kBN + cl < G.C) *reinterpret_cast<float4 *>(out + cl) = sum[i];
+    }
 }
 
 // ---------------------------------------------------------------- embedding
@@ -822,12 +857,18 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             break;
         }
         // One workgroup per CU; more (whole rounds) only if a slice would cross
-        // more output tiles than the kernel tracks; never more slices than rounds.
+        // more output tiles than the kernel tracks; never more slices than
+        // rounds (so none is empty).  The slice arithmetic runs in fp64 on the
+        // GPU, exact while P * Q < 2^53.
         int64_t P = cus;
         const int64_t need = (iters + (kMaxSegs - 2) * min_chunks - 1) / ((kMaxSegs - 2) * min_chunks);
         if (need > P) P = ((need + cus - 1) / cus) * cus;
         P = std::min<int64_t>(P, iters / kRound);
         if (P >= kXcds) P -= P % kXcds;
+        if (P * (iters / kRound) >= (int64_t(1) << 53)) {
+            plan.too_big = true;
+            break;
+        }
         p.n_wg = static_cast<int32_t>(P);
         p.iters = iters;
         L.out_tiles = otiles;
@@ -863,7 +904,7 @@ size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups) {
     if (validate(groups, n_groups) != SFT_OK) return static_cast<size_t>(-1);
     const Plan plan = make_plan(groups, n_groups);
     if (plan.too_big) {
-        sft::fail(SFT_ENOTSUP, "sft_masked_dw: more than 2^31 (tile, chunk) iterations in one launch");
+        sft::fail(SFT_ENOTSUP, "sft_masked_dw: a launch beyond 2^31 (tile, chunk) iterations");
         return static_cast<size_t>(-1);
     }
     return plan.ws_bytes();
@@ -873,7 +914,7 @@ int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t
     sft::clear_error();
     if (int rc = validate(groups, n_groups)) return rc;
     Plan plan = make_plan(groups, n_groups);
-    SFT_CHECK(!plan.too_big, SFT_ENOTSUP, "sft_masked_dw: more than 2^31 (tile, chunk) iterations in one launch");
+    SFT_CHECK(!plan.too_big, SFT_ENOTSUP, "sft_masked_dw: a launch beyond 2^31 (tile, chunk) iterations");
     if (plan.launches.empty()) return SFT_OK;
     SFT_CHECK(ws_bytes >= plan.ws_bytes(), SFT_ECAPACITY, "sft_masked_dw: workspace %zu < %zu bytes", ws_bytes,
               plan.ws_bytes());
@@ -888,7 +929,7 @@ int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t
         hipLaunchKernelGGL(k_masked_dw, dim3(static_cast<uint32_t>(L.p.n_wg)), dim3(kThreads), 0, st, L.p);
         e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
-        hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(L.out_tiles), kMaxTiles * 32 / 4), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(L.out_tiles), kMaxTiles), dim3(256), 0, st,
                            L.p);
         e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: fix-up launch failed: %s", hipGetErrorString(e));
