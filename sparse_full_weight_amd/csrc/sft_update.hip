@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <numeric>
+#include <vector>
 
 #include "sft_internal.h"
 
@@ -466,13 +468,19 @@ int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *h
     for (int32_t i = 0; i < n_mats; ++i)
         if (int rc = check_mat(mats[i], "sft_sparse_update")) return rc;
     const AdamDev a = make_adam(*hp);
+    // Widest rows first: they are the longest workgroups, and going out
+    // first they get CUs of their own before the narrow rows fill the rest.
+    std::vector<int32_t> order(static_cast<size_t>(n_mats));
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return mats[x].C > mats[y].C; });
     // Matrices go out in batches of kMaxMats per launch (kernel-argument table).
     for (int32_t base = 0; base < n_mats; base += kMaxMats) {
         UpdParams p{};
         p.hp = a;
         int64_t n_wg = 0, maxC = 0;
         int32_t n = 0;
-        for (int32_t i = base; i < std::min(n_mats, base + kMaxMats); ++i) {
+        for (int32_t oi = base; oi < std::min(n_mats, base + kMaxMats); ++oi) {
+            const int32_t i = order[static_cast<size_t>(oi)];
             if (mats[i].n_active == 0) continue;
             p.mat[n++] = make_mat(mats[i], n_wg);
             n_wg += mats[i].n_active;
@@ -514,9 +522,15 @@ int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *h
         maxC = 0;
         return rc;
     };
-    for (int32_t i = 0; i < n_pairs; ++i) {
-        const sft_pair &pr = pairs[i];
-        for (int side = 0; side < 2; ++side) {
+    // Sides with the widest rows first (as in sft_sparse_update).
+    std::vector<int32_t> order(static_cast<size_t>(2 * n_pairs));
+    std::iota(order.begin(), order.end(), 0);
+    auto width = [&](int32_t k) { return (k & 1) ? pairs[k >> 1].b.C : pairs[k >> 1].a.C; };
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return width(x) > width(y); });
+    for (const int32_t k : order) {
+        const sft_pair &pr = pairs[k >> 1];
+        {
+            const int side = k & 1;
             const sft_upd_mat &self = side ? pr.b : pr.a;
             const sft_upd_mat &partner = side ? pr.a : pr.b;
             if (self.n_active == 0) continue;
