@@ -327,13 +327,13 @@ def main():
                      "algorithmic_bytes": dw.bytes, "avg_ms": round(dw_avg, 5)},
         "cpu_baseline": cpu,
         "kernels": {
-            "k_masked_dw": {"avg_ms": round(dw_avg, 5), "GB_s": round(dw_gbs, 1),
+            "sft_masked_dw": {"avg_ms": round(dw_avg, 5), "GB_s": round(dw_gbs, 1),
                             "hbm_frac": round(dw_gbs / HBM_PEAK_GBS, 4),
                             "useful_TFLOP_s": round(dw.flops_useful / (dw_avg * 1e-3) / 1e12, 1),
                             "issued_TFLOP_s": round(dw.flops_issued / (dw_avg * 1e-3) / 1e12, 1),
                             "mfma_frac_issued": round(dw.flops_issued / (dw_avg * 1e-3) / 1e12 /
                                                       MFMA_BF16_PEAK_TFLOPS, 4)},
-            "k_sparse_update": {"avg_ms": round(up_avg, 5), "GB_s": round(up_gbs, 1),
+            "sft_sparse_update": {"avg_ms": round(up_avg, 5), "GB_s": round(up_gbs, 1),
                                 "hbm_frac": round(up_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": up.bytes},
         },
         "host_plan_us_per_layer": round(host_plan_us, 1),

@@ -224,7 +224,7 @@ size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups);
  *   ws / ws_bytes  device scratch of at least sft_masked_dw_workspace()
  *                  bytes (16-byte aligned; no initialisation needed).  Calls
  *                  that share a workspace must be ordered on one stream.
- * Limits: T >= 1, T < 2^31, C % 8 == 0, R < 2^31, n_active < 2^24, at most
+ * Limits: 1 <= T <= 2^24, C % 8 == 0, R < 2^31, n_active < 2^24, at most
  * 16 matrices per group, fewer than 2^31 (output tile, 64-token chunk)
  * iterations per launch of 8 groups.  Results are deterministic
  * (a fixed summation order for every launch configuration the same inputs
