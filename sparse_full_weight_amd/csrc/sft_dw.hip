@@ -292,28 +292,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
     if (it_lo >= it_hi) return;
 
-    // ---- the group table (constant indices only: a run-time index into the
-    // kernel argument would make the compiler copy it to scratch)
-    // (one wave per entry: each wave's copy is independent of the others)
+    // ---- the group table, for run-time indexing (one wave per entry, constant
+    // indices only: a run-time index into the kernel argument would make the
+    // compiler copy it to scratch)
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g)
         if (wave == g && lane == 0) gs[g] = p.g[g];
 #pragma unroll
     for (int m = 0; m < kMaxMats; ++m)
         if (wave == (m & 7) && lane == 1 + (m >> 3)) outp[m] = p.m[m].out;
-    __syncthreads();
 
-    // ---- the slice's segments (one per output tile it touches); 32-bit
-    // arithmetic (the host keeps the iteration count below 2^31)
-    if (tid == 0) {
+    // ---- meanwhile wave 0 builds the slice's segments (one per output tile it
+    // touches) from the kernel argument: wave-uniform control flow, so the
+    // table reads are scalar loads.  32-bit arithmetic (the host keeps the
+    // iteration count below 2^31).
+    if (wave == 0) {
         int32_t it = static_cast<int32_t>(it_lo);
         const int32_t hi = static_cast<int32_t>(it_hi);
         int n = 0;
         int32_t j = 0;
         while (it < hi && n < kMaxSegs) {
             int gi = 0;
-            while (gi + 1 < p.n_groups && it >= static_cast<int32_t>(gs[gi + 1].it_begin)) ++gi;
-            const DwGroupDev &G = gs[gi];
+            while (gi + 1 < p.n_groups && it >= static_cast<int32_t>(p.g[gi + 1].it_begin)) ++gi;
+            const DwGroupDev &G = p.g[gi];
             const int32_t rel = it - static_cast<int32_t>(G.it_begin);
             const int32_t tile = rel / G.chunks;
             const int32_t k0 = rel - tile * G.chunks;
@@ -330,11 +331,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             sg.len = end - it;
             const bool whole = (k0 == 0 && end == tile_end);
             sg.slot = whole ? -1 : (n == 0 ? static_cast<int32_t>(2 * v) : static_cast<int32_t>(2 * v + 1));
-            segs[n++] = sg;
+            if (lane == 0) segs[n] = sg;
+            ++n;
             j += sg.len;
             it = end;
         }
-        s_nseg = n;
+        if (lane == 0) s_nseg = n;
     }
     __syncthreads();
     const int nseg = s_nseg;
@@ -533,9 +535,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
     };
 
+    // ---- the output map of the slice's first four segments (thread t: entry
+    // t%128 of segment t/128), loaded ahead of the prologue so that the wait
+    // for it covers these loads only; written to LDS behind the prologue, and
+    // read only by epilogues, after the first chunk's barrier.
+    const int csg = tid >> 7, crow = tid & 127;
+    int32_t cval = -1;
+    if (csg < nseg) {
+        const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[csg].g);
+        // (a global, not flat, load: flat loads count in lgkmcnt too, and every
+        // LDS access of the prologue would then wait for this one)
+        if (crow < segs[csg].mt * 32)
+            cval = *reinterpret_cast<__attribute__((address_space(1))) const int32_t *>(
+                reinterpret_cast<uintptr_t>(gs[gsg].rowmap + segs[csg].p0 * 32 + crow));
+    }
+
     // ---- prologue: operands and X copies of chunks 0..2, in the order the
-    // steady state issues them, then 16 stores to the sink so that every
-    // segment, the first included, starts behind an epilogue.
+    // steady state issues them.
     describe_x(0);
     describe_a(0);
     auto prologue = [&](auto s_tag) __attribute__((always_inline)) {
@@ -549,30 +565,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     prologue(ic<0>{});
     prologue(ic<1>{});
     prologue(ic<2>{});
-#pragma unroll
-    for (int q = 0; q < kEpiStores; ++q)
-        *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(reinterpret_cast<uintptr_t>(sink)) = f32x4{};
 
-    // ---- the output map of the slice's tiles, fetched while the first
-    // chunks are in flight (the wait for it covers them too)
-    for (int sg = 0; sg < nseg; ++sg) {
-        const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[sg].g);
-        const int32_t *map = gs[gsg].rowmap + segs[sg].p0 * 32;
-        const int32_t n = segs[sg].mt * 32;
-        for (int r = tid; r < kMaxTiles * 32; r += kThreads) codes[sg][r] = r < n ? map[r] : -1;
+    static_assert(kThreads / (kMaxTiles * 32) == 4 && kMaxSegs >= 4, "four segments' output map per pass");
+    codes[csg][crow] = cval;
+    if (nseg > 4) {   // rare: slices across more than four output tiles
+        for (int sg = 4; sg < nseg; ++sg) {
+            const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[sg].g);
+            const int32_t *map = gs[gsg].rowmap + segs[sg].p0 * 32;
+            const int32_t n = segs[sg].mt * 32;
+            for (int r = tid; r < kMaxTiles * 32; r += kThreads) codes[sg][r] = r < n ? map[r] : -1;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // ---- the segments.  The first round of each waits for 16 more memory
-    // operations in its first three chunks (the epilogue's stores sit behind
-    // their loads).
-    for (int sg = 0; sg < nseg; ++sg) {
+    // ---- the segments.  The first round of every segment but the first waits
+    // for 16 more memory operations in its first three chunks (the previous
+    // epilogue's stores sit behind their loads); the first segment's code is
+    // separate, so that each loop sees one state of the operations in flight.
+    auto segment = [&](int sg, auto first_tag) __attribute__((always_inline)) {
         const int32_t j0 = segs[sg].j0, len = segs[sg].len;
         const bool active = tw < segs[sg].mt;
-        round4(j0, active, kEpiStores);
+        round4(j0, active, decltype(first_tag)::value ? 0 : kEpiStores);
         for (int32_t jq = j0 + kRound; jq < j0 + len; jq += kRound) round4(jq, active, 0);
         epilogue(sg);
-    }
+    };
+    segment(0, ic<1>{});
+    for (int sg = 1; sg < nseg; ++sg) segment(sg, ic<0>{});
     // Copies past the slice are still in flight (they write zeros to LDS):
     // drain them before the workgroup's LDS can be handed to another (the
     // last epilogue's stores, issued after them, may stay in flight).
