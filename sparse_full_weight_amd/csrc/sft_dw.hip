@@ -119,9 +119,18 @@ struct Seg {
     int32_t slot;   // -1: whole tile (final output); else partial slot
 };
 
-// Packed tiles [lo(b), lo(b+1)) form M-block b: balanced blocks of <= 8.
+// floor(n / d) for 0 <= n, d < 2^53 through one correctly rounded fp64
+// division (a few instructions where a 64-bit integer division is a long
+// scalar routine): n/d = k + f with f <= 1 - 1/d, and the rounding error is
+// at most (n/d)*2^-53 < 1/d, so the rounded quotient stays below k + 1.
+__device__ __forceinline__ int64_t floordiv53(int64_t n, int64_t d) {
+    return static_cast<int64_t>(static_cast<double>(n) / static_cast<double>(d));
+}
+
+// Packed tiles [lo(b), lo(b+1)) form M-block b: balanced blocks of at most
+// kMaxTiles (b * n_ptiles < 2^48).
 __device__ __forceinline__ int32_t mblk_lo(const DwGroupDev &G, int32_t b) {
-    return static_cast<int32_t>((static_cast<int64_t>(b) * G.n_ptiles) / G.n_mblk);
+    return static_cast<int32_t>(floordiv53(static_cast<int64_t>(b) * G.n_ptiles, G.n_mblk));
 }
 
 // ---------------------------------------------------------------- gather
@@ -199,14 +208,6 @@ __global__ __launch_bounds__(256) void k_dw_gather(const DwParams p) {
 
 // Slice of workgroup v: global iterations [lo, hi), on whole rounds (output
 // tiles are whole rounds too, so every segment is whole rounds).
-// floor(n / d) for 0 <= n, d < 2^53 through one correctly rounded fp64
-// division (a few instructions where a 64-bit integer division is a long
-// scalar routine): n/d = k + f with f <= 1 - 1/d, and the rounding error is
-// at most (n/d)*2^-53 < 1/d, so the rounded quotient stays below k + 1.
-__device__ __forceinline__ int64_t floordiv53(int64_t n, int64_t d) {
-    return static_cast<int64_t>(static_cast<double>(n) / static_cast<double>(d));
-}
-
 // Slice v starts at round floor(v * Q / n_wg), Q = iters / kRound rounds.
 __device__ __forceinline__ int64_t slice_lo(const DwParams &p, int64_t v) {
     return kRound * floordiv53(v * (p.iters / kRound), p.n_wg);
@@ -324,8 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             Seg sg;
             sg.g = gi;
             sg.nb = tile - mb * G.n_nblk;
-            sg.p0 = mb * G.n_ptiles / G.n_mblk;
-            sg.mt = (mb + 1) * G.n_ptiles / G.n_mblk - sg.p0;
+            sg.p0 = mblk_lo(G, mb);
+            sg.mt = mblk_lo(G, mb + 1) - sg.p0;
             sg.k0 = k0;
             sg.j0 = j;
             sg.len = end - it;

@@ -174,6 +174,18 @@ def test_dw_more_groups_than_one_launch(gpu_lib, layout):
     _check(groups, layout=layout)
 
 
+@LAYOUTS
+def test_dw_many_rows_tiny_shape(gpu_lib, layout):
+    # 2^22 + 96 active rows of one token and 8 columns: 131075 packed tiles in
+    # 32769 M-blocks, so an M-block's first packed tile (block * packed tiles /
+    # blocks) needs more than 32 bits on the way; one token of small integers
+    # makes the product exact
+    T, R, C = 1, (1 << 22) + 96, 8
+    X = synth.integer_bf16((T, C), -3, 3, 1501)
+    dY = synth.integer_bf16((T, R), -3, 3, 1502)
+    _check([(X, [(dY, np.ones(R, np.uint8))])], exact=True, layout=layout)
+
+
 def test_dw_rejects_bad_shapes(gpu_lib):
     T, R, C = 16, 32, 12
     X = bf16_dev(synth.normal_bf16((T, C), 1.0, 1))
