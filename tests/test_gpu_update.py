@@ -90,8 +90,11 @@ def test_sparse_update_second_step_and_large_lr(gpu_lib):
     assert_state_equal(m.to_state(), want, "two steps")
 
 
-def test_sparse_update_zero_row(gpu_lib):
-    st, rows, slot, fresh, G = _case(32, 64, 2, 2, 500, False)
+@pytest.mark.parametrize("C", [64, 8200])
+def test_sparse_update_zero_row(gpu_lib, C):
+    # an all-zero row keeps a zero scale (at 8200 columns also through the
+    # piecewise update and its requantisation)
+    st, rows, slot, fresh, G = _case(32, C, 2, 2, 500, False)
     st.q[rows[0]] = 0
     st.delta[rows[0]] = 0
     G[0] = 0
@@ -103,8 +106,11 @@ def test_sparse_update_zero_row(gpu_lib):
     assert_state_equal(m.to_state(), want, "zero row")
 
 
-def test_coupled_update_bit_exact(gpu_lib):
-    R, C = 200, 512
+@pytest.mark.parametrize("C", [512, 8200, 11008])
+def test_coupled_update_bit_exact(gpu_lib, C):
+    # 8200 and 11008 columns go in 4096-column pieces (the last one 8 and 2816
+    # columns wide) and a separate requantisation
+    R = 200
     g = synth.rng(600)
     pairs_np = []
     for pi, (a_own, a_cross) in enumerate([(1.0, 0.0), (0.9, 0.37), (0.0, 1.0)]):
