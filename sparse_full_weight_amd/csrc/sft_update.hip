@@ -425,11 +425,13 @@ UpdMatDev make_mat(const sft_upd_mat &m, int64_t row_begin) {
 }
 
 // Chunks of 4 columns per lane: the smallest instantiated count covering C.
+// Rows up to 4096 columns take 256 lanes (several workgroups share a CU);
+// wider ones take 1024 lanes, one workgroup a CU, so that a wide row's
+// arithmetic has all four SIMDs to itself (with 256 lanes it shared its CU
+// with a narrow row and set the kernel's length).
 template <typename Params, template <int, int> class Launch>
 int dispatch(int64_t maxC, int64_t n_wg, const Params &p, hipStream_t stream) {
     if (maxC <= 256 * 4 * 4) return Launch<256, 4>::go(n_wg, p, stream);
-    if (maxC <= 256 * 4 * 8) return Launch<256, 8>::go(n_wg, p, stream);
-    if (maxC <= 256 * 4 * 12) return Launch<256, 12>::go(n_wg, p, stream);
     if (maxC <= 1024 * 4 * 4) return Launch<1024, 4>::go(n_wg, p, stream);
     if (maxC <= 1024 * 4 * 8) return Launch<1024, 8>::go(n_wg, p, stream);
     return Launch<1024, 16>::go(n_wg, p, stream);
