@@ -48,6 +48,8 @@ def parse_args():
                     help="masked-dW row layout: active rows packed 32 to a tile, or whole active tiles")
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step with sft_masked_dw + sft_sparse_update instead of the fused sft_masked_dw_update")
     ap.add_argument("--cpu-sample-every", type=int, default=4,
                     help="oracle timing uses every n-th active row of each matrix")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -138,6 +140,8 @@ class Layer:
         self.ws = torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device=dev)
         self.dw_call = _lib.prepare_masked_dw(groups, self.ws)
         self.upd_call = _lib.prepare_sparse_update(upd, self.hp)
+        # the update matrices follow the groups' matrices in order
+        self.fused_call = _lib.prepare_masked_dw_update(groups, self.ws, upd, self.hp)
         self.T = T
 
     def upload_plan(self):
@@ -238,8 +242,11 @@ def main():
 
     def step(L):
         L.upload_plan()
-        L.dw_call(stream)
-        L.upd_call(stream)
+        if args.unfused:
+            L.dw_call(stream)
+            L.upd_call(stream)
+        else:
+            L.fused_call(stream)
 
     for i in range(args.warmup):
         step(layers[i % len(layers)])
@@ -277,12 +284,14 @@ def main():
         L.upload_plan()
     dw_avg = timed(lambda L: L.dw_call(stream))
     up_avg = timed(lambda L: L.upd_call(stream))
+    fu_avg = timed(lambda L: L.fused_call(stream))
 
     L0 = layers[0]
     dw = L0.dw_work()
     up = L0.upd_work()
     dw_gbs = dw.bytes / (dw_avg * 1e-3) / 1e9
     up_gbs = up.bytes / (up_avg * 1e-3) / 1e9
+    fu_gbs = (dw.bytes + up.bytes) / (fu_avg * 1e-3) / 1e9
     n_act = sum(m["plan"].n_active for m in L0.mats.values())
     n_tiles = sum(m["plan"].n_active_tiles for m in L0.mats.values())
 
@@ -319,8 +328,10 @@ def main():
         "config": {"workload": "llama7b_layer_masked_step", "tokens": args.tokens, "density": args.density,
                    "matrices": {k: list(v) for k, v in synth.LLAMA7B.items()}, "active_rows": n_act,
                    "active_tiles": n_tiles, "ring_layers": args.layers, "dw_layout": args.layout,
-                   "step": "plan upload + masked dW (7 matrices, 1 launch) + sparse update with fused "
-                           "write-back (7 matrices, 1 launch)"},
+                   "step": ("plan upload + masked dW (7 matrices) + sparse update with fused write-back "
+                            "(7 matrices), " + ("two calls" if args.unfused else
+                                                "one call: sft_masked_dw_update, the split tiles' fix-up "
+                                                "done by the update"))},
         "roofline": {"bound": "hbm", "kernel": "sft_masked_dw (k_dw_gather + k_masked_dw + k_dw_fixup)",
                      "achieved": round(dw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -335,6 +346,9 @@ def main():
                                                       MFMA_BF16_PEAK_TFLOPS, 4)},
             "sft_sparse_update": {"avg_ms": round(up_avg, 5), "GB_s": round(up_gbs, 1),
                                 "hbm_frac": round(up_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": up.bytes},
+            "sft_masked_dw_update": {"avg_ms": round(fu_avg, 5), "GB_s": round(fu_gbs, 1),
+                                     "hbm_frac": round(fu_gbs / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": dw.bytes + up.bytes},
         },
         "host_plan_us_per_layer": round(host_plan_us, 1),
     }

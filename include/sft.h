@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 3
+#define SFT_ABI_VERSION 4
 
 enum {
     SFT_OK = 0,
@@ -298,6 +298,27 @@ typedef struct sft_upd_mat {
  * Errors: SFT_EINVAL, SFT_ESHAPE, SFT_EALIGN, SFT_ENOTSUP, SFT_EHIP.
  */
 int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *hp, void *stream);
+
+/*
+ * sft_masked_dw followed by sft_sparse_update on its gradients, with the
+ * fix-up of split output tiles folded into the update (sections 2.2, 2.3):
+ * each updated row reads its gradient as the sum, in slice order, of the
+ * partial rows the product left in the workspace -- the same additions as
+ * sft_masked_dw's -- so every result is bit-identical to the two calls.
+ *   groups, ws, ws_bytes  as for sft_masked_dw (the same workspace size)
+ *   mats / n_mats         one update matrix per dW matrix, in the order of
+ *                         the groups and their matrices; mats[i].G must be
+ *                         the dW matrix's dW_act, and active_rows, n_active,
+ *                         R and C must be the same
+ * On return dW_act holds only the tiles that one slice computed whole (the
+ * rest stayed in the workspace); its contents are otherwise unspecified.
+ * When the groups need more than one product launch, the call runs
+ * sft_masked_dw and sft_sparse_update instead.
+ * Errors: those of sft_masked_dw and sft_sparse_update; SFT_EINVAL when the
+ * update matrices do not match the dW matrices.
+ */
+int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes,
+                         const sft_upd_mat *mats, int32_t n_mats, const sft_adam *hp, void *stream);
 
 /*
  * A coupled pair (section 2.4: gate-up, query-output, key-value).  a and b

@@ -30,7 +30,7 @@ _CODES = {SFT_EINVAL: "EINVAL", SFT_ESHAPE: "ESHAPE", SFT_EALIGN: "EALIGN", SFT_
 EXPORTS = (
     "sft_last_error", "sft_abi_version", "sft_conductor_window", "sft_tracker_window", "sft_plan_rows",
     "sft_plan_embedding", "sft_slots_update", "sft_bias_table", "sft_masked_dw_workspace", "sft_masked_dw",
-    "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback",
+    "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback", "sft_masked_dw_update",
 )
 
 
@@ -106,6 +106,8 @@ def lib() -> C.CDLL:
         L.sft_embedding_dw.argtypes = [p, i64, i64, p, p, i64, p, p]
         L.sft_sparse_update.argtypes = [C.POINTER(CUpdMat), i32, C.POINTER(CAdam), p]
         L.sft_coupled_update.argtypes = [C.POINTER(CPair), i32, C.POINTER(CAdam), p]
+        L.sft_masked_dw_update.argtypes = [C.POINTER(CDwGroup), i32, p, C.c_size_t, C.POINTER(CUpdMat), i32,
+                                           C.POINTER(CAdam), p]
         L.sft_masked_writeback.argtypes = [p, p, p, i64, i64, p, i64, p, p]
         for n in EXPORTS[2:]:
             if n != "sft_masked_dw_workspace":
@@ -362,6 +364,18 @@ def sft_sparse_update(mats: Sequence[UpdMat], hp: Adam, stream=None) -> None:
     _check(lib().sft_sparse_update(arr, len(mats), C.byref(h), _stream(stream)))
 
 
+def sft_masked_dw_update(groups: Sequence[DwGroup], ws, mats: Sequence[UpdMat], hp: Adam, stream=None) -> None:
+    """Masked dW with the update of every matrix fused in (the split tiles' fix-up
+    is done by the update); mats follow the groups' matrices in order, each
+    with G = that matrix's dW_act."""
+    arr, keep = _c_groups(groups)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    u = (CUpdMat * max(len(mats), 1))(*[m.c() for m in mats])
+    h = hp.c()
+    _check(lib().sft_masked_dw_update(arr, len(groups), _dev(ws), nbytes, u, len(mats), C.byref(h),
+                                      _stream(stream)))
+
+
 @dataclass
 class Pair:
     a: UpdMat
@@ -414,6 +428,15 @@ def prepare_sparse_update(mats: Sequence[UpdMat], hp: Adam) -> Prepared:
     arr = (CUpdMat * max(len(mats), 1))(*[m.c() for m in mats])
     h = hp.c()
     return Prepared(lib().sft_sparse_update, (arr, len(mats), C.byref(h)), (arr, h, mats, hp))
+
+
+def prepare_masked_dw_update(groups: Sequence[DwGroup], ws, mats: Sequence[UpdMat], hp: Adam) -> Prepared:
+    arr, keep = _c_groups(groups)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    u = (CUpdMat * max(len(mats), 1))(*[m.c() for m in mats])
+    h = hp.c()
+    return Prepared(lib().sft_masked_dw_update, (arr, len(groups), _dev(ws), nbytes, u, len(mats), C.byref(h)),
+                    (arr, keep, u, h, groups, ws, mats, hp))
 
 
 def prepare_coupled_update(pairs: Sequence[Pair], hp: Adam) -> Prepared:

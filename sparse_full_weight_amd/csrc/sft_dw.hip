@@ -108,6 +108,7 @@ struct DwParams {
     int32_t n_wg;           // slices (= workgroups of the product)
     int64_t iters;          // total (output tile, chunk) iterations, a multiple of kRound
     float *part;            // [2 * n_wg] partial tiles of kSlotFloats
+    int32_t part_rows;      // partial tiles row-major (1) or in MFMA fragment order (0)
     float *sink;            // [n_wg * 8] x 16 floats: target of masked-off stores
 };
 
@@ -509,7 +510,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // write to the sink).  A whole tile goes to dW_act through the row map,
     // row-major.  A partial one goes to its slot in fragment order: store q
     // of wave (tw, ch) fills the 1 KB fragment (tw*2 + ch)*16 + q, lane l's
-    // 16 bytes at 16*l, so each of those stores is one contiguous kilobyte.
+    // 16 bytes at 16*l, so each of those stores is one contiguous kilobyte;
+    // or, for an update that reads its rows from the slots, row-major.
     auto epilogue = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
@@ -517,15 +519,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         const int32_t code = tw < S.mt ? codes[sg][tw * 32 + (lane & 31)] : -1;
         const int64_t c0 = static_cast<int64_t>(S.nb) * kBN;
         const bool part = S.slot >= 0;
+        const bool frag = part && !p.part_rows;
         float *base = sink;
         if (code >= 0)
-            base = part ? p.part + S.slot * kSlotFloats + ((tw * 2 + ch) * kEpiStores * 64 + lane) * 4
+            base = frag ? p.part + S.slot * kSlotFloats + ((tw * 2 + ch) * kEpiStores * 64 + lane) * 4
+                 : part ? p.part + S.slot * kSlotFloats + (tw * 32 + (lane & 31)) * kBN + 128 * ch + 4 * h
                         : outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C + c0 + 128 * ch + 4 * h;
 #pragma unroll
         for (int q = 0; q < kEpiStores; ++q) {
             const int c = q / 4, a = q % 4;
             const bool ok = code >= 0 && (part || c0 + 32 * (4 * ch + c) + 8 * a + 4 * h < G.C);
-            const int off = part ? 256 * q : 32 * c + 8 * a;
+            const int off = frag ? 256 * q : 32 * c + 8 * a;
             auto *dst = reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(
                 reinterpret_cast<uintptr_t>(ok ? base + off : sink));
             *dst = f32x4{acc[c][4 * a], acc[c][4 * a + 1], acc[c][4 * a + 2], acc[c][4 * a + 3]};
@@ -915,6 +919,66 @@ void bind_workspace(Plan &plan, void *ws) {
 }
 
 }  // namespace
+
+namespace sft {
+
+int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream,
+                       DwRowSrc *src, bool *done) {
+    *done = false;
+    if (int rc = validate(groups, n_groups)) return rc;
+    Plan plan = make_plan(groups, n_groups);
+    SFT_CHECK(!plan.too_big, SFT_ENOTSUP, "sft_masked_dw: a launch beyond 2^31 (tile, chunk) iterations");
+    if (plan.launches.size() != 1) return SFT_OK;
+    SFT_CHECK(ws_bytes >= plan.ws_bytes(), SFT_ECAPACITY, "sft_masked_dw: workspace %zu < %zu bytes", ws_bytes,
+              plan.ws_bytes());
+    SFT_CHECK(ws && aligned16(ws), SFT_EINVAL, "sft_masked_dw: workspace null or not 16-byte aligned");
+    bind_workspace(plan, ws);
+    Launch &L = plan.launches[0];
+    L.p.part_rows = 1;
+    // the matrices in input order: live groups and their matrices with active
+    // tiles were taken in this order by the plan
+    int32_t dg = 0, dm = 0, i = 0;
+    for (int32_t gi = 0; gi < n_groups; ++gi) {
+        const sft_dw_group &g = groups[gi];
+        const bool live = group_live(g);
+        for (int32_t mi = 0; mi < g.n_mats; ++mi, ++i) {
+            DwRowSrc &r = src[i];
+            r = DwRowSrc{};
+            if (!live || g.mats[mi].n_active_tiles == 0) continue;
+            const DwGroupDev &G = L.p.g[dg];
+            const DwMatDev &M = L.p.m[dm++];
+            r.part = L.p.part;
+            r.dW = M.out;
+            r.tiles = g.layout == SFT_DW_TILES ? g.mats[mi].active_tiles : nullptr;
+            r.n_tiles = g.mats[mi].n_active_tiles;
+            r.slot_floats = kSlotFloats;
+            r.it_begin = G.it_begin;
+            r.P = L.p.n_wg;
+            r.Q = L.p.iters / kRound;
+            r.bn = kBN;
+            r.rnd = kRound;
+            r.chunks = G.chunks;
+            r.n_nblk = G.n_nblk;
+            r.n_ptiles = G.n_ptiles;
+            r.n_mblk = G.n_mblk;
+            r.row_begin = M.row_begin;
+            r.layout = G.layout;
+        }
+        if (live) ++dg;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(k_dw_gather, dim3(static_cast<uint32_t>(L.gather_tiles), static_cast<uint32_t>(L.gather_blocks)),
+                       dim3(256), 0, st, L.p);
+    hipError_t e = hipGetLastError();
+    SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: gather launch failed: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(k_masked_dw, dim3(static_cast<uint32_t>(L.p.n_wg)), dim3(kThreads), 0, st, L.p);
+    e = hipGetLastError();
+    SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
+    *done = true;
+    return SFT_OK;
+}
+
+}  // namespace sft
 
 extern "C" {
 

@@ -36,6 +36,7 @@
 namespace {
 
 constexpr int kMaxMats = 16;
+constexpr int kMaxFused = 8;   // matrices per fused-update launch (kernel-argument size)
 
 struct UpdMatDev {
     const int32_t *rows;
@@ -113,7 +114,7 @@ __device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
 
 // Update one active row (index k of matrix M).  `gr` supplies the effective
 // gradient of a 4-column chunk in two parts: gr.load(c) issues the chunk's
-// gradient loads, gr.combine(raw, g) forms the gradient from them.  Every
+// gradient loads, gr.combine(raw, c, g) forms the gradient from them.  Every
 // load of the row is issued before any arithmetic (one memory round trip for
 // the whole row; rows wider than 16384 columns take two to four); the moments
 // are stored as soon as they are computed, q, delta and the live weights
@@ -137,7 +138,7 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
     float bc1 = 0.0f, bc2 = 0.0f;
 
     // Wide rows on 1024-lane workgroups go in batches of chunks (registers).
-    constexpr int kBatch = kThreads >= 1024 ? (kChunks >= 16 ? 2 : 4) : kChunks;
+    constexpr int kBatch = Grad::template batch<kThreads, kChunks>();
     static_assert(kChunks % kBatch == 0, "batch");
     float wn[kChunks][4];
     float amax = 0.0f;
@@ -173,7 +174,7 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
             const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
             if (c < C) {
                 float g[4];
-                gr.combine(graw[jb], g);
+                gr.combine(graw[jb], c, g);
                 const float qf[4] = {static_cast<float>(qv[jb].x), static_cast<float>(qv[jb].y),
                                      static_cast<float>(qv[jb].z), static_cast<float>(qv[jb].w)};
                 const float df[4] = {dv[jb].x, dv[jb].y, dv[jb].z, dv[jb].w};
@@ -246,11 +247,18 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
 }
 
 // Plain update: the gradient is the matrix's own dW row.
+// Chunks whose loads go out together, within the register budget (1024-lane
+// workgroups have at most 128 registers a lane).
+template <int kThreads, int kChunks>
+constexpr int plain_batch() { return kThreads >= 1024 ? (kChunks >= 16 ? 2 : 4) : kChunks; }
+
 struct OwnGrad {
+    template <int kThreads, int kChunks>
+    static constexpr int batch() { return plain_batch<kThreads, kChunks>(); }
     typedef float4 Raw;
     const float *row;
     __device__ __forceinline__ Raw load(int64_t c) const { return *reinterpret_cast<const float4 *>(row + c); }
-    __device__ __forceinline__ void combine(const Raw &x, float *g) const {
+    __device__ __forceinline__ void combine(const Raw &x, int64_t, float *g) const {
         g[0] = x.x;
         g[1] = x.y;
         g[2] = x.z;
@@ -271,6 +279,8 @@ __global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
 // Coupled update: the blend of the clipped own and partner gradients (a row
 // missing from the partner's active set contributes zero).
 struct PairGrad {
+    template <int kThreads, int kChunks>
+    static constexpr int batch() { return plain_batch<kThreads, kChunks>(); }
     struct Raw {
         float4 own, part;
     };
@@ -283,7 +293,7 @@ struct PairGrad {
         x.part = part_row ? *reinterpret_cast<const float4 *>(part_row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
         return x;
     }
-    __device__ __forceinline__ void combine(const Raw &x, float *g) const {
+    __device__ __forceinline__ void combine(const Raw &x, int64_t, float *g) const {
         const float sa[4] = {x.own.x, x.own.y, x.own.z, x.own.w};
         const float pa[4] = {x.part.x, x.part.y, x.part.z, x.part.w};
 #pragma unroll
@@ -360,6 +370,132 @@ __global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restri
         pack.w = o[6] | (static_cast<uint32_t>(o[7]) << 16);
         *reinterpret_cast<uint4 *>(wr + c) = pack;
     }
+}
+
+// Update fused with the masked-dW fix-up: the gradient of a 256-column block
+// of the row is the sum, in slice order, of the partial rows the slices that
+// cut its output tile left (the same additions as the fix-up kernel's), or
+// the dW_act row where one slice covered the tile.  tab[nb] = (first slice,
+// slices | first-slot-odd << 16), built per workgroup.
+struct FusedGrad {
+    // (up to four partial loads per chunk)
+    template <int kThreads, int kChunks>
+    static constexpr int batch() { return kThreads >= 1024 ? (kChunks >= 8 ? 2 : 4) : kChunks; }
+    struct Raw {
+        float4 x[4];
+    };
+    const float *part;
+    const float *dw_row;      // the row in dW_act
+    const int2 *tab;          // LDS
+    int64_t slot_floats;
+    int32_t bn, prow;
+    __device__ __forceinline__ const float *slot_row(int32_t v0, int32_t i, bool odd) const {
+        const int64_t slot = (i == 0 && odd) ? 2 * static_cast<int64_t>(v0) + 1 : 2 * static_cast<int64_t>(v0 + i);
+        return part + slot * slot_floats + static_cast<int64_t>(prow) * bn;
+    }
+    __device__ __forceinline__ Raw load(int64_t c) const {
+        const int nb = static_cast<int>(c / bn), cl = static_cast<int>(c - static_cast<int64_t>(nb) * bn);
+        const int2 t = tab[nb];
+        const int n = t.y & 0xFFFF;
+        const bool odd = (t.y >> 16) != 0;
+        Raw r;
+        if (n == 1) {
+            r.x[0] = *reinterpret_cast<const float4 *>(dw_row + c);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < n) r.x[i] = *reinterpret_cast<const float4 *>(slot_row(t.x, i, odd) + cl);
+        }
+        return r;
+    }
+    __device__ __forceinline__ void combine(const Raw &r, int64_t c, float *g) const {
+        const int nb = static_cast<int>(c / bn), cl = static_cast<int>(c - static_cast<int64_t>(nb) * bn);
+        const int2 t = tab[nb];
+        const int n = t.y & 0xFFFF;
+        float4 sum = r.x[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            if (i < n) {
+                sum.x += r.x[i].x;
+                sum.y += r.x[i].y;
+                sum.z += r.x[i].z;
+                sum.w += r.x[i].w;
+            }
+        }
+        for (int i = 4; i < n; ++i) {
+            const float4 y = *reinterpret_cast<const float4 *>(slot_row(t.x, i, false) + cl);
+            sum.x += y.x;
+            sum.y += y.y;
+            sum.z += y.z;
+            sum.w += y.w;
+        }
+        g[0] = sum.x;
+        g[1] = sum.y;
+        g[2] = sum.z;
+        g[3] = sum.w;
+    }
+};
+
+struct FusedParams {
+    UpdMatDev mat[kMaxFused];
+    sft::DwRowSrc src[kMaxFused];
+    int32_t n_mats;
+    AdamDev hp;
+};
+
+// floor(n / d) for 0 <= n, d < 2^53 (one correctly rounded fp64 division:
+// the rounding error stays below the distance 1/d to the next integer).
+__device__ __forceinline__ int64_t floordiv53(int64_t n, int64_t d) {
+    return static_cast<int64_t>(static_cast<double>(n) / static_cast<double>(d));
+}
+
+template <int kThreads, int kChunks>
+__global__ __launch_bounds__(kThreads) void k_fused_update(const FusedParams p) {
+    __shared__ int2 tab[256];
+    const int64_t wg = blockIdx.x;
+    int mi = 0;
+    while (mi + 1 < p.n_mats && wg >= p.mat[mi + 1].row_begin) ++mi;
+    const UpdMatDev &M = p.mat[mi];
+    const sft::DwRowSrc &S = p.src[mi];
+    const int64_t k = wg - M.row_begin;
+    // the row's packed row j in its group, its M-block and its row in the
+    // M-block's packed rows
+    int64_t j = S.row_begin + k;
+    if (S.tiles) {   // tile layout: 32 rows per active tile
+        const int32_t r = M.rows[k];
+        int64_t lo = 0, hi = S.n_tiles;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (S.tiles[mid] < (r >> 5)) lo = mid + 1;
+            else hi = mid;
+        }
+        j = S.row_begin + 32 * lo + (r & 31);
+    }
+    const int64_t ptile = j >> 5;
+    auto mlo = [&](int64_t b) __attribute__((always_inline)) { return floordiv53(b * S.n_ptiles, S.n_mblk); };
+    int64_t mb = floordiv53(ptile * S.n_mblk, S.n_ptiles);
+    while (mb > 0 && mlo(mb) > ptile) --mb;
+    while (mb + 1 < S.n_mblk && mlo(mb + 1) <= ptile) ++mb;
+    const int32_t prow = static_cast<int32_t>(j - 32 * mlo(mb));
+    // slices over each output tile (M-block mb, column block nb): slice v
+    // starts at round floor(v * Q / P)
+    for (int nb = threadIdx.x; nb < S.n_nblk; nb += kThreads) {
+        const int64_t a = (S.it_begin + (mb * S.n_nblk + nb) * static_cast<int64_t>(S.chunks)) / S.rnd;
+        const int64_t b = a + S.chunks / S.rnd;
+        const int64_t v0 = floordiv53((a + 1) * S.P - 1, S.Q);
+        const int64_t v1 = floordiv53(b * S.P - 1, S.Q);
+        const bool odd = floordiv53(v0 * S.Q, S.P) < a;
+        tab[nb] = make_int2(static_cast<int>(v0), static_cast<int>(v1 - v0 + 1) | (odd ? 0x10000 : 0));
+    }
+    __syncthreads();
+    FusedGrad gr;
+    gr.part = S.part;
+    gr.dw_row = S.dW + k * M.C;
+    gr.tab = tab;
+    gr.slot_floats = S.slot_floats;
+    gr.bn = S.bn;
+    gr.prow = prow;
+    update_row<kThreads, kChunks>(M, k, p.hp, gr);
 }
 
 // ---------------------------------------------------------------- host side
@@ -448,6 +584,14 @@ struct LaunchUpd {
     static int go(int64_t n_wg, const UpdParams &p, hipStream_t s) {
         hipLaunchKernelGGL((k_sparse_update<T, N>), dim3(static_cast<uint32_t>(n_wg)), dim3(T), 0, s, p);
         return launch_status("sft_sparse_update");
+    }
+};
+
+template <int T, int N>
+struct LaunchFused {
+    static int go(int64_t n_wg, const FusedParams &p, hipStream_t s) {
+        hipLaunchKernelGGL((k_fused_update<T, N>), dim3(static_cast<uint32_t>(n_wg)), dim3(T), 0, s, p);
+        return launch_status("sft_masked_dw_update");
     }
 };
 
@@ -552,6 +696,62 @@ int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *h
         }
     }
     return flush();
+}
+
+int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes,
+                         const sft_upd_mat *mats, int32_t n_mats, const sft_adam *hp, void *stream) {
+    sft::clear_error();
+    SFT_CHECK(n_groups >= 0 && (n_groups == 0 || groups), SFT_EINVAL, "sft_masked_dw_update: bad group list");
+    int32_t total = 0;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        SFT_CHECK(groups[g].n_mats >= 0 && (groups[g].n_mats == 0 || groups[g].mats), SFT_EINVAL,
+                  "sft_masked_dw_update: group %d has a bad matrix list", g);
+        total += groups[g].n_mats;
+    }
+    SFT_CHECK(n_mats == total && (n_mats == 0 || mats), SFT_EINVAL,
+              "sft_masked_dw_update: %d update matrices for %d dW matrices", n_mats, total);
+    if (int rc = check_hp(hp, "sft_masked_dw_update")) return rc;
+    for (int32_t i = 0, g = 0; g < n_groups; ++g) {
+        for (int32_t m = 0; m < groups[g].n_mats; ++m, ++i) {
+            if (int rc = check_mat(mats[i], "sft_masked_dw_update")) return rc;
+            const sft_dw_mat &d = groups[g].mats[m];
+            SFT_CHECK(mats[i].C == groups[g].C && mats[i].n_active == d.n_active && mats[i].R == d.R &&
+                          (d.n_active == 0 || (mats[i].G == d.dW_act && mats[i].active_rows == d.active_rows)),
+                      SFT_EINVAL, "sft_masked_dw_update: update matrix %d does not match its dW matrix", i);
+        }
+    }
+    std::vector<sft::DwRowSrc> src(static_cast<size_t>(total));
+    bool done = false;
+    if (int rc = sft::masked_dw_partials(groups, n_groups, ws, ws_bytes, stream, src.data(), &done)) return rc;
+    if (!done) {   // the product needs more than one launch: the two calls
+        if (int rc = sft_masked_dw(groups, n_groups, ws, ws_bytes, stream)) return rc;
+        return sft_sparse_update(mats, n_mats, hp, stream);
+    }
+    const AdamDev a = make_adam(*hp);
+    std::vector<int32_t> order(static_cast<size_t>(n_mats));
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return mats[x].C > mats[y].C; });
+    for (int32_t base = 0; base < n_mats; base += kMaxFused) {
+        FusedParams p{};
+        p.hp = a;
+        int64_t n_wg = 0, maxC = 0;
+        int32_t n = 0;
+        for (int32_t oi = base; oi < std::min(n_mats, base + kMaxFused); ++oi) {
+            const int32_t i = order[static_cast<size_t>(oi)];
+            if (mats[i].n_active == 0) continue;
+            p.mat[n] = make_mat(mats[i], n_wg);
+            p.src[n] = src[static_cast<size_t>(i)];
+            ++n;
+            n_wg += mats[i].n_active;
+            maxC = std::max<int64_t>(maxC, mats[i].C);
+        }
+        p.n_mats = n;
+        if (n_wg == 0) continue;
+        SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_masked_dw_update: too many rows");
+        if (int rc = dispatch<FusedParams, LaunchFused>(maxC, n_wg, p, static_cast<hipStream_t>(stream)))
+            return rc;
+    }
+    return SFT_OK;
 }
 
 int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, int64_t R, int64_t C,
