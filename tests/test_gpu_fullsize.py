@@ -137,6 +137,49 @@ def test_llama7b_layer_dw_and_update_sampled(gpu_lib, layer, layout):
         assert not host_u16(st["w"])[idle].any(), name
 
 
+@pytest.mark.parametrize("layout", [_lib.SFT_DW_PACKED, _lib.SFT_DW_TILES], ids=["packed", "tiles"])
+def test_llama7b_layer_fused_update_matches_two_calls(gpu_lib, layer, layout):
+    # sft_masked_dw_update on the whole layer leaves every state array (all
+    # rows, compared on the device) bit-identical to sft_masked_dw followed by
+    # sft_sparse_update
+    X, mats = layer
+    Xd = {g: bf16_dev(x) for g, x in X.items()}
+    plans = {name: _lib.sft_plan_rows(m["mask"]) for name, m in mats.items()}
+
+    def run(fused):
+        groups, upd, states = [], [], {}
+        for gname, members in synth.LLAMA7B_GROUPS:
+            ms = []
+            for name in members:
+                m, plan = mats[name], plans[name]
+                n = plan.n_active
+                dplan = plan.to_device()
+                out = torch.zeros((n, m["C"]), dtype=torch.float32, device="cuda")
+                ms.append(_lib.DwMat(bf16_dev(m["dY"]), dplan, out))
+                st = _dev_state(m, n)
+                states[name] = st
+                upd.append(_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], dplan.active_rows,
+                                       st["slot"], out, n, st["fresh"], st["w"]))
+            groups.append(_lib.DwGroup(Xd[gname], ms, layout))
+        ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device="cuda")
+        hp = adam_dev()
+        if fused:
+            _lib.sft_masked_dw_update(groups, ws, upd, hp)
+        else:
+            _lib.sft_masked_dw(groups, ws)
+            _lib.sft_sparse_update(upd, hp)
+        torch.cuda.synchronize()
+        return states
+
+    a, b = run(True), run(False)
+    for name in mats:
+        for key in ("q", "s", "delta", "m", "v", "t", "w"):
+            x, y = a[name][key], b[name][key]
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), f"{name} {key}"
+
+
 def _sub_state(m, rows, C):
     """Oracle state holding only the given rows (fresh moments)."""
     n = rows.size
