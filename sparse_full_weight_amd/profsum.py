@@ -32,7 +32,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 DW_KERNELS = ("k_dw_gather", "k_masked_dw", "k_dw_fixup")
-UPDATE_KERNELS = ("k_sparse_update", "k_coupled_update")
+UPDATE_KERNELS = ("k_sparse_update", "k_coupled_update", "k_fused_update")
 COPY_BYTES = 1 << 30            # bench.py --copy-calibration copies 1 GiB per launch
 
 
