@@ -747,18 +747,6 @@ struct Plan {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int num_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 bool group_live(const sft_dw_group &g) {
     for (int32_t mi = 0; mi < g.n_mats; ++mi)
@@ -812,7 +800,7 @@ int validate(const sft_dw_group *groups, int32_t n_groups) {
 // launch] (launches run in stream order, so they reuse the last region).
 Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
     Plan plan;
-    const int cus = num_cus();
+    const int cus = sft::num_cus();
     int32_t gi = 0;
     while (gi < n_groups) {
         Launch L;
@@ -921,6 +909,19 @@ void bind_workspace(Plan &plan, void *ws) {
 }  // namespace
 
 namespace sft {
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream,
                        DwRowSrc *src, bool *done) {

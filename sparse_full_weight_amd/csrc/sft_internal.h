@@ -17,6 +17,9 @@ void clear_error();
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Compute units of the current device (256 if the runtime cannot say).
+int num_cus();
+
 // Where one matrix's dW rows are after a masked-dW launch that left its cut
 // output tiles as partial sums (for the update that adds them itself).
 // Partial slot s holds rows [prow][col] of an output tile, row-major, at

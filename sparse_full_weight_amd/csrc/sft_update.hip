@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <numeric>
 #include <vector>
 
@@ -53,6 +54,7 @@ struct UpdMatDev {
     int64_t C;
     int64_t n_active;
     int64_t row_begin;  // first workgroup of this matrix
+    int32_t per_wg;     // rows per workgroup (1, or 2 on the halves of a 1024-lane workgroup)
 };
 
 struct AdamDev {
@@ -98,7 +100,9 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 
 // Largest value over the workgroup (non-negative floats), via the integer
 // order of their bit patterns: wave64 shuffles, then one LDS word per wave.
-template <int kThreads>
+// The workgroup may hold several rows of kLanes lanes each: the maximum is
+// taken over the waves of the calling lane's row.
+template <int kThreads, int kLanes>
 __device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
     uint32_t u = __float_as_uint(x);
 #pragma unroll
@@ -106,9 +110,10 @@ __device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) lds[wave] = __uint_as_float(u);
     __syncthreads();
-    float r = lds[0];
+    const int w0 = (static_cast<int>(threadIdx.x) / kLanes) * (kLanes / 64);
+    float r = lds[w0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, lds[w]);
+    for (int w = 1; w < kLanes / 64; ++w) r = fmaxf(r, lds[w0 + w]);
     return r;
 }
 
@@ -119,15 +124,22 @@ __device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
 // the whole row; rows wider than 16384 columns take two to four); the moments
 // are stored as soon as they are computed, q, delta and the live weights
 // after the row's |w'| maximum.
-template <int kThreads, int kChunks, typename Grad>
-__device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const AdamDev &hp, const Grad &gr) {
+//
+// The workgroup holds kPer rows, each on kThreads/kPer consecutive lanes; in
+// a workgroup of two rows whose second one does not exist (odd row count)
+// those lanes pass valid = false and only take part in the barrier.
+template <int kThreads, int kChunks, int kPer, typename Grad>
+__device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool valid, const AdamDev &hp,
+                                           const Grad &gr) {
+    constexpr int kLanes = kThreads / kPer;
+    const int lt = static_cast<int>(threadIdx.x) % kLanes;
     __shared__ float red[kThreads / 64];
-    const int64_t C = M.C;
-    const int64_t r = M.rows[k];
-    const int64_t sl = M.slot[k];
-    const bool fresh = M.fresh ? M.fresh[k] != 0 : false;
-    const float s_old = M.s[r];
-    const int32_t t_old = fresh ? 0 : M.t[sl];
+    const int64_t C = valid ? M.C : 0;
+    const int64_t r = valid ? M.rows[k] : 0;
+    const int64_t sl = valid ? M.slot[k] : 0;
+    const bool fresh = (valid && M.fresh) ? M.fresh[k] != 0 : false;
+    const float s_old = valid ? M.s[r] : 0.0f;
+    const int32_t t_old = (fresh || !valid) ? 0 : M.t[sl];
     const int8_t *__restrict__ qrow = M.q + r * C;
     const float *__restrict__ drow = M.delta + r * C;
     uint16_t *mrow = M.m + sl * C;
@@ -151,7 +163,7 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
 #pragma unroll
         for (int jb = 0; jb < kBatch; ++jb) {
             const int j = b0 + jb;
-            const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+            const int64_t c = 4 * (static_cast<int64_t>(lt) + static_cast<int64_t>(j) * kLanes);
             mv[jb] = make_ushort4(0, 0, 0, 0);
             vv[jb] = make_ushort4(0, 0, 0, 0);
             if (c < C) {
@@ -164,14 +176,14 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
                 }
             }
         }
-        if (b0 == 0) {
+        if (b0 == 0 && valid) {
             bc1 = hp.bc1[ti];
             bc2 = hp.bc2[ti];
         }
 #pragma unroll
         for (int jb = 0; jb < kBatch; ++jb) {
             const int j = b0 + jb;
-            const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+            const int64_t c = 4 * (static_cast<int64_t>(lt) + static_cast<int64_t>(j) * kLanes);
             if (c < C) {
                 float g[4];
                 gr.combine(graw[jb], c, g);
@@ -209,9 +221,9 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
             }
         }
     }
-    amax = block_max_nonneg<kThreads>(amax, red);
+    amax = block_max_nonneg<kThreads, kLanes>(amax, red);
     const float s_new = amax / 127.0f;
-    if (threadIdx.x == 0) {
+    if (lt == 0 && valid) {
         M.s[r] = s_new;
         M.t[sl] = step;
     }
@@ -220,7 +232,7 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
     uint16_t *wl = M.w_live ? M.w_live + r * C : nullptr;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
-        const int64_t c = 4 * (static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(j) * kThreads);
+        const int64_t c = 4 * (static_cast<int64_t>(lt) + static_cast<int64_t>(j) * kLanes);
         if (c < C) {
             float qf[4], d[4];
             uint16_t b[4];
@@ -247,6 +259,22 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, const 
 }
 
 // Plain update: the gradient is the matrix's own dW row.
+// Launch shapes that may take rows two to a workgroup (see assign_wgs).
+template <int kThreads, int kChunks>
+constexpr bool kPairs = kThreads == 1024 && kChunks == 4;
+
+// Runs fn(integral_constant<kPer>) with the matrix's rows per workgroup.
+template <int kThreads, int kChunks, typename Fn>
+__device__ __forceinline__ void with_rows_per_wg(const UpdMatDev &M, Fn &&fn) {
+    if constexpr (kPairs<kThreads, kChunks>) {
+        if (M.per_wg == 2) {
+            fn(std::integral_constant<int, 2>{});
+            return;
+        }
+    }
+    fn(std::integral_constant<int, 1>{});
+}
+
 // Chunks whose loads go out together, within the register budget (1024-lane
 // workgroups have at most 128 registers a lane).
 template <int kThreads, int kChunks>
@@ -272,8 +300,12 @@ __global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
     int mi = 0;
     while (mi + 1 < p.n_mats && wg >= p.mat[mi + 1].row_begin) ++mi;
     const UpdMatDev &M = p.mat[mi];
-    const int64_t k = wg - M.row_begin;
-    update_row<kThreads, kChunks>(M, k, p.hp, OwnGrad{M.G + k * M.C});
+    with_rows_per_wg<kThreads, kChunks>(M, [&](auto per) __attribute__((always_inline)) {
+        constexpr int kPer = decltype(per)::value;
+        const int64_t k = (wg - M.row_begin) * kPer + static_cast<int>(threadIdx.x) / (kThreads / kPer);
+        const bool valid = k < M.n_active;
+        update_row<kThreads, kChunks, kPer>(M, k, valid, p.hp, OwnGrad{M.G + (valid ? k : 0) * M.C});
+    });
 }
 
 // Coupled update: the blend of the clipped own and partner gradients (a row
@@ -325,19 +357,23 @@ __global__ __launch_bounds__(kThreads) void k_coupled_update(const PairParams p)
     while (si + 1 < p.n_sides && wg >= p.side[si + 1].self.row_begin) ++si;
     const PairDev &S = p.side[si];
     const UpdMatDev &M = S.self;
-    const int64_t k = wg - M.row_begin;
-    const int64_t r = M.rows[k];
-    const int64_t pk = find_row(S.prow, S.pn, r);
-    const float clip_a = S.clip ? S.clip[0] : 1.0f;
-    const float clip_b = S.clip ? S.clip[1] : 1.0f;
-    PairGrad gr;
-    gr.own_row = M.G + k * M.C;
-    gr.part_row = pk >= 0 ? S.pG + pk * M.C : nullptr;
-    gr.c_self = S.self_is_b ? clip_b : clip_a;
-    gr.c_part = S.self_is_b ? clip_a : clip_b;
-    gr.a_own = S.a_own;
-    gr.a_cross = S.a_cross;
-    update_row<kThreads, kChunks>(M, k, p.hp, gr);
+    with_rows_per_wg<kThreads, kChunks>(M, [&](auto per) __attribute__((always_inline)) {
+        constexpr int kPer = decltype(per)::value;
+        const int64_t k = (wg - M.row_begin) * kPer + static_cast<int>(threadIdx.x) / (kThreads / kPer);
+        const bool valid = k < M.n_active;
+        const int64_t r = valid ? M.rows[k] : 0;
+        const int64_t pk = valid ? find_row(S.prow, S.pn, r) : -1;
+        const float clip_a = S.clip ? S.clip[0] : 1.0f;
+        const float clip_b = S.clip ? S.clip[1] : 1.0f;
+        PairGrad gr;
+        gr.own_row = M.G + (valid ? k : 0) * M.C;
+        gr.part_row = pk >= 0 ? S.pG + pk * M.C : nullptr;
+        gr.c_self = S.self_is_b ? clip_b : clip_a;
+        gr.c_part = S.self_is_b ? clip_a : clip_b;
+        gr.a_own = S.a_own;
+        gr.a_cross = S.a_cross;
+        update_row<kThreads, kChunks, kPer>(M, k, valid, p.hp, gr);
+    });
 }
 
 __global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restrict__ q,
@@ -380,7 +416,7 @@ __global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restri
 struct FusedGrad {
     // (up to four partial loads per chunk)
     template <int kThreads, int kChunks>
-    static constexpr int batch() { return kThreads >= 1024 ? (kChunks >= 8 ? 2 : 4) : kChunks; }
+    static constexpr int batch() { return kThreads >= 1024 ? 2 : kChunks; }
     struct Raw {
         float4 x[4];
     };
@@ -451,51 +487,57 @@ __device__ __forceinline__ int64_t floordiv53(int64_t n, int64_t d) {
 
 template <int kThreads, int kChunks>
 __global__ __launch_bounds__(kThreads) void k_fused_update(const FusedParams p) {
-    __shared__ int2 tab[256];
+    __shared__ int2 tab[2][256];
     const int64_t wg = blockIdx.x;
     int mi = 0;
     while (mi + 1 < p.n_mats && wg >= p.mat[mi + 1].row_begin) ++mi;
     const UpdMatDev &M = p.mat[mi];
     const sft::DwRowSrc &S = p.src[mi];
-    const int64_t k = wg - M.row_begin;
-    // the row's packed row j in its group, its M-block and its row in the
-    // M-block's packed rows
-    int64_t j = S.row_begin + k;
-    if (S.tiles) {   // tile layout: 32 rows per active tile
-        const int32_t r = M.rows[k];
-        int64_t lo = 0, hi = S.n_tiles;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (S.tiles[mid] < (r >> 5)) lo = mid + 1;
-            else hi = mid;
+    with_rows_per_wg<kThreads, kChunks>(M, [&](auto per) __attribute__((always_inline)) {
+        constexpr int kPer = decltype(per)::value, kLanes = kThreads / kPer;
+        const int sub = static_cast<int>(threadIdx.x) / kLanes, lt = static_cast<int>(threadIdx.x) % kLanes;
+        const int64_t k = (wg - M.row_begin) * kPer + sub;
+        const bool valid = k < M.n_active;
+        const int64_t kk = valid ? k : 0;
+        // the row's packed row j in its group, its M-block and its row in the
+        // M-block's packed rows
+        int64_t j = S.row_begin + kk;
+        if (S.tiles) {   // tile layout: 32 rows per active tile
+            const int32_t r = M.rows[kk];
+            int64_t lo = 0, hi = S.n_tiles;
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (S.tiles[mid] < (r >> 5)) lo = mid + 1;
+                else hi = mid;
+            }
+            j = S.row_begin + 32 * lo + (r & 31);
         }
-        j = S.row_begin + 32 * lo + (r & 31);
-    }
-    const int64_t ptile = j >> 5;
-    auto mlo = [&](int64_t b) __attribute__((always_inline)) { return floordiv53(b * S.n_ptiles, S.n_mblk); };
-    int64_t mb = floordiv53(ptile * S.n_mblk, S.n_ptiles);
-    while (mb > 0 && mlo(mb) > ptile) --mb;
-    while (mb + 1 < S.n_mblk && mlo(mb + 1) <= ptile) ++mb;
-    const int32_t prow = static_cast<int32_t>(j - 32 * mlo(mb));
-    // slices over each output tile (M-block mb, column block nb): slice v
-    // starts at round floor(v * Q / P)
-    for (int nb = threadIdx.x; nb < S.n_nblk; nb += kThreads) {
-        const int64_t a = (S.it_begin + (mb * S.n_nblk + nb) * static_cast<int64_t>(S.chunks)) / S.rnd;
-        const int64_t b = a + S.chunks / S.rnd;
-        const int64_t v0 = floordiv53((a + 1) * S.P - 1, S.Q);
-        const int64_t v1 = floordiv53(b * S.P - 1, S.Q);
-        const bool odd = floordiv53(v0 * S.Q, S.P) < a;
-        tab[nb] = make_int2(static_cast<int>(v0), static_cast<int>(v1 - v0 + 1) | (odd ? 0x10000 : 0));
-    }
-    __syncthreads();
-    FusedGrad gr;
-    gr.part = S.part;
-    gr.dw_row = S.dW + k * M.C;
-    gr.tab = tab;
-    gr.slot_floats = S.slot_floats;
-    gr.bn = S.bn;
-    gr.prow = prow;
-    update_row<kThreads, kChunks>(M, k, p.hp, gr);
+        const int64_t ptile = j >> 5;
+        auto mlo = [&](int64_t bb) __attribute__((always_inline)) { return floordiv53(bb * S.n_ptiles, S.n_mblk); };
+        int64_t mb = floordiv53(ptile * S.n_mblk, S.n_ptiles);
+        while (mb > 0 && mlo(mb) > ptile) --mb;
+        while (mb + 1 < S.n_mblk && mlo(mb + 1) <= ptile) ++mb;
+        const int32_t prow = static_cast<int32_t>(j - 32 * mlo(mb));
+        // slices over each output tile (M-block mb, column block nb): slice v
+        // starts at round floor(v * Q / P)
+        for (int nb = lt; nb < S.n_nblk; nb += kLanes) {
+            const int64_t a = (S.it_begin + (mb * S.n_nblk + nb) * static_cast<int64_t>(S.chunks)) / S.rnd;
+            const int64_t b = a + S.chunks / S.rnd;
+            const int64_t v0 = floordiv53((a + 1) * S.P - 1, S.Q);
+            const int64_t v1 = floordiv53(b * S.P - 1, S.Q);
+            const bool odd = floordiv53(v0 * S.Q, S.P) < a;
+            tab[sub][nb] = make_int2(static_cast<int>(v0), static_cast<int>(v1 - v0 + 1) | (odd ? 0x10000 : 0));
+        }
+        __syncthreads();
+        FusedGrad gr;
+        gr.part = S.part;
+        gr.dw_row = S.dW + kk * M.C;
+        gr.tab = tab[sub];
+        gr.slot_floats = S.slot_floats;
+        gr.bn = S.bn;
+        gr.prow = prow;
+        update_row<kThreads, kChunks, kPer>(M, k, valid, p.hp, gr);
+    });
 }
 
 // ---------------------------------------------------------------- host side
@@ -557,7 +599,27 @@ UpdMatDev make_mat(const sft_upd_mat &m, int64_t row_begin) {
     d.C = m.C;
     d.n_active = m.n_active;
     d.row_begin = row_begin;
+    d.per_wg = 1;
     return d;
+}
+
+// Rows per workgroup and workgroup offsets of a launch's matrices.  With
+// 1024 lanes (some row wider than 4096 columns) a workgroup holds a CU by
+// itself; when single rows would outnumber the CUs, rows of up to 8192
+// columns go two to a workgroup (512 lanes each), so that the launch is one
+// wave of workgroups.  Returns the workgroup count.
+int64_t assign_wgs(UpdMatDev *const *mats, int32_t n, int64_t maxC) {
+    int64_t rows = 0;
+    for (int32_t i = 0; i < n; ++i) rows += mats[i]->n_active;
+    const bool pair = maxC > 256 * 4 * 4 && maxC <= 1024 * 4 * 4 && rows > sft::num_cus();
+    int64_t n_wg = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        UpdMatDev &d = *mats[i];
+        d.per_wg = (pair && d.C <= 512 * 4 * 4) ? 2 : 1;
+        d.row_begin = n_wg;
+        n_wg += (d.n_active + d.per_wg - 1) / d.per_wg;
+    }
+    return n_wg;
 }
 
 // Chunks of 4 columns per lane: the smallest instantiated count covering C.
@@ -625,14 +687,17 @@ int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *h
         p.hp = a;
         int64_t n_wg = 0, maxC = 0;
         int32_t n = 0;
+        UpdMatDev *list[kMaxMats];
         for (int32_t oi = base; oi < std::min(n_mats, base + kMaxMats); ++oi) {
             const int32_t i = order[static_cast<size_t>(oi)];
             if (mats[i].n_active == 0) continue;
-            p.mat[n++] = make_mat(mats[i], n_wg);
-            n_wg += mats[i].n_active;
+            p.mat[n] = make_mat(mats[i], 0);
+            list[n] = &p.mat[n];
+            ++n;
             maxC = std::max<int64_t>(maxC, mats[i].C);
         }
         p.n_mats = n;
+        n_wg = assign_wgs(list, n, maxC);
         if (n_wg == 0) continue;
         SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_sparse_update: too many rows");
         if (int rc = dispatch<UpdParams, LaunchUpd>(maxC, n_wg, p, static_cast<hipStream_t>(stream)))
@@ -660,6 +725,9 @@ int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *h
     int64_t n_wg = 0, maxC = 0;
     auto flush = [&]() -> int {
         if (n_wg == 0) return SFT_OK;
+        UpdMatDev *list[kMaxMats];
+        for (int32_t i = 0; i < p.n_sides; ++i) list[i] = &p.side[i].self;
+        n_wg = assign_wgs(list, p.n_sides, maxC);
         SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_coupled_update: too many rows");
         const int rc = dispatch<PairParams, LaunchPair>(maxC, n_wg, p, static_cast<hipStream_t>(stream));
         p = PairParams{};
@@ -736,16 +804,18 @@ int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws,
         p.hp = a;
         int64_t n_wg = 0, maxC = 0;
         int32_t n = 0;
+        UpdMatDev *list[kMaxFused];
         for (int32_t oi = base; oi < std::min(n_mats, base + kMaxFused); ++oi) {
             const int32_t i = order[static_cast<size_t>(oi)];
             if (mats[i].n_active == 0) continue;
-            p.mat[n] = make_mat(mats[i], n_wg);
+            p.mat[n] = make_mat(mats[i], 0);
             p.src[n] = src[static_cast<size_t>(i)];
+            list[n] = &p.mat[n];
             ++n;
-            n_wg += mats[i].n_active;
             maxC = std::max<int64_t>(maxC, mats[i].C);
         }
         p.n_mats = n;
+        n_wg = assign_wgs(list, n, maxC);
         if (n_wg == 0) continue;
         SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_masked_dw_update: too many rows");
         if (int rc = dispatch<FusedParams, LaunchFused>(maxC, n_wg, p, static_cast<hipStream_t>(stream)))

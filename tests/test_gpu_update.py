@@ -49,6 +49,21 @@ def test_sparse_update_bit_exact_many_shapes(gpu_lib, mid_run):
         assert_state_equal(m.to_state(), want, f"shape {shapes[i]}")
 
 
+def test_sparse_update_two_rows_per_workgroup(gpu_lib):
+    # more rows than CUs with one row wider than 4096 columns: rows of up to
+    # 8192 columns go two to a 1024-lane workgroup (odd counts leave a
+    # workgroup's second half without a row)
+    shapes = [(64, 6000, 21), (700, 4096, 301), (300, 2048, 33)]
+    cases = [_case(R, C, n, n + 5, 900 + i, True, fresh_frac=0.2) for i, (R, C, n) in enumerate(shapes)]
+    gm = [GpuMat(st, G, rows, slot, fresh) for st, rows, slot, fresh, G in cases]
+    _lib.sft_sparse_update([m.upd() for m in gm], adam_dev(**HP))
+    torch.cuda.synchronize()
+    for i, ((st, rows, slot, fresh, G), m) in enumerate(zip(cases, gm)):
+        want = st.copy()
+        oracle.sparse_update(want, G, rows, slot, fresh, **HP)
+        assert_state_equal(m.to_state(), want, f"shape {shapes[i]}")
+
+
 @pytest.mark.parametrize("C", [20000, 40000])
 def test_sparse_update_wide_rows(gpu_lib, C):
     st, rows, slot, fresh, G = _case(6, C, 3, 3, 200 + C, True)
@@ -140,6 +155,37 @@ def test_coupled_update_bit_exact(gpu_lib, C):
                               clip_a=ca, clip_b=cb, weight_decay=wd, **HP)
         assert_state_equal(ma.to_state(), wa, f"pair A ({a_own},{a_cross})")
         assert_state_equal(mb.to_state(), wb, f"pair B ({a_own},{a_cross})")
+
+
+def test_coupled_update_two_rows_per_workgroup(gpu_lib):
+    # a wide pair and a 4096-column pair with more rows than CUs: the narrow
+    # pair's rows go two to a 1024-lane workgroup
+    g = synth.rng(950)
+    specs = [(300, 8200, 31), (700, 4096, 163)]
+    pairs_np = []
+    for pi, (R, C, k) in enumerate(specs):
+        A = make_state(R, C, 960 + pi, k + 4, True)
+        B = make_state(R, C, 970 + pi, k + 4, True)
+        ra = np.sort(g.choice(R, k, replace=False)).astype(np.int32)
+        rb = np.sort(g.choice(R, k, replace=False)).astype(np.int32)
+        sa = g.choice(k + 4, ra.size, replace=False).astype(np.int32)
+        sb = g.choice(k + 4, rb.size, replace=False).astype(np.int32)
+        GA = synth.gradient_rows(ra.size, C, 0.2, 980 + pi)
+        GB = synth.gradient_rows(rb.size, C, 0.2, 990 + pi)
+        pairs_np.append((A, B, ra, rb, sa, sb, GA, GB))
+    gpu_pairs, mats = [], []
+    for A, B, ra, rb, sa, sb, GA, GB in pairs_np:
+        ma, mb = GpuMat(A, GA, ra, sa, None), GpuMat(B, GB, rb, sb, None)
+        mats.append((ma, mb))
+        gpu_pairs.append(_lib.Pair(ma.upd(), mb.upd(), 0.8, 0.3, None))
+    _lib.sft_coupled_update(gpu_pairs, adam_dev(**HP))
+    torch.cuda.synchronize()
+    for (A, B, ra, rb, sa, sb, GA, GB), (ma, mb) in zip(pairs_np, mats):
+        wa, wb = A.copy(), B.copy()
+        oracle.coupled_update(wa, GA, ra, sa, None, wb, GB, rb, sb, None, a_own=0.8, a_cross=0.3,
+                              clip_a=1.0, clip_b=1.0, weight_decay=0.0, **HP)
+        assert_state_equal(ma.to_state(), wa, f"pair A C={A.q.shape[1]}")
+        assert_state_equal(mb.to_state(), wb, f"pair B C={A.q.shape[1]}")
 
 
 def test_masked_writeback_bit_exact(gpu_lib):
