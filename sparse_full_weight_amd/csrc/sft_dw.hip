@@ -106,6 +106,7 @@ struct DwParams {
     DwMatDev m[kMaxMats];
     int32_t n_groups;
     int32_t n_wg;           // slices (= workgroups of the product)
+    int32_t xcd_blocked;    // neighbouring slices on one XCD (else slice = workgroup index)
     int64_t iters;          // total (output tile, chunk) iterations, a multiple of kRound
     float *part;            // [2 * n_wg] partial tiles of kSlotFloats
     int32_t part_rows;      // partial tiles row-major (1) or in MFMA fragment order (0)
@@ -241,7 +242,7 @@ using ic = std::integral_constant<int, V>;
 // operand rows and X blocks in that XCD's L2.
 __device__ __forceinline__ int64_t slice_of(const DwParams &p) {
     const int64_t b = blockIdx.x;
-    return (p.n_wg % kXcds == 0) ? (b % kXcds) * (p.n_wg / kXcds) + b / kXcds : b;
+    return (p.xcd_blocked && p.n_wg % kXcds == 0) ? (b % kXcds) * (p.n_wg / kXcds) + b / kXcds : b;
 }
 
 // Wave-uniform copy of a value every lane holds alike (so that it lives in
@@ -867,15 +868,36 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             plan.too_big = true;
             break;
         }
-        // One workgroup per CU; more (whole rounds) only if a slice would cross
-        // more output tiles than the kernel tracks; never more slices than
-        // rounds (so none is empty).  The slice arithmetic runs in fp64 on the
-        // GPU, exact while P * Q < 2^53.
-        int64_t P = cus;
-        const int64_t need = (iters + (kMaxSegs - 2) * min_chunks - 1) / ((kMaxSegs - 2) * min_chunks);
-        if (need > P) P = ((need + cus - 1) / cus) * cus;
-        P = std::min<int64_t>(P, iters / kRound);
-        if (P >= kXcds) P -= P % kXcds;
+        // Slices aligned to the output tiles when that keeps most CUs busy:
+        // if every tile has the same number of rounds and f (dividing it) times
+        // the tile count fits the CUs with at least 3/4 of them at work, each
+        // workgroup takes exactly 1/f of one tile -- every tile cut f ways at
+        // the same places, the fewest partial sums for that many workgroups,
+        // one segment each, equal work -- with workgroup index = slice (on
+        // MI355X this spread of the groups over the XCDs measured faster than
+        // keeping neighbouring slices on one XCD).  Otherwise one workgroup per
+        // CU over the whole (tile, chunk) space (stream-K), neighbouring
+        // slices on one XCD; more workgroups (whole rounds) only if a slice
+        // would cross more output tiles than the kernel tracks; never more
+        // slices than rounds (so none is empty).  The slice arithmetic runs in
+        // fp64 on the GPU, exact while P * Q < 2^53.
+        int64_t P = 0;
+        int64_t rt = p.g[0].chunks / kRound;
+        for (int32_t g = 1; g < p.n_groups; ++g)
+            if (p.g[g].chunks / kRound != rt) rt = 0;
+        for (int64_t f = rt; f >= 1; --f) {
+            if (rt % f || f * otiles > cus) continue;
+            if (4 * f * otiles >= 3 * int64_t(cus)) P = f * otiles;
+            break;
+        }
+        p.xcd_blocked = P == 0;
+        if (P == 0) {
+            P = cus;
+            const int64_t need = (iters + (kMaxSegs - 2) * min_chunks - 1) / ((kMaxSegs - 2) * min_chunks);
+            if (need > P) P = ((need + cus - 1) / cus) * cus;
+            P = std::min<int64_t>(P, iters / kRound);
+            if (P >= kXcds) P -= P % kXcds;
+        }
         if (P * (iters / kRound) >= (int64_t(1) << 53)) {
             plan.too_big = true;
             break;

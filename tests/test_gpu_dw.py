@@ -147,6 +147,28 @@ def test_dw_long_token_axis_split(gpu_lib, layout):
     _check([(X, [(dY, mask)])], repeat=3, layout=layout)
 
 
+@LAYOUTS
+def test_dw_tile_aligned_half_slices(gpu_lib, layout):
+    # 100 output tiles of 2 rounds: 200 workgroups each take exactly half a
+    # tile (slices aligned to the tiles)
+    T, R, C = 512, 96, 100 * 256
+    X = synth.normal_bf16((T, C), 1.0, 1601)
+    dY = synth.normal_bf16((T, R), 0.01, 1602)
+    mask = _mask_rows(R, synth.clustered_rows(R, 40, 1603))
+    _check([(X, [(dY, mask)])], repeat=2, layout=layout)
+
+
+@LAYOUTS
+def test_dw_one_tile_per_workgroup(gpu_lib, layout):
+    # 200 output tiles of one round: every workgroup computes one whole tile
+    # (no partial sums at all)
+    T, R, C = 256, 64, 200 * 256
+    X = synth.normal_bf16((T, C), 1.0, 1611)
+    dY = synth.normal_bf16((T, R), 0.01, 1612)
+    mask = _mask_rows(R, synth.clustered_rows(R, 30, 1613))
+    _check([(X, [(dY, mask)])], layout=layout)
+
+
 def test_dw_layouts_agree_bitwise_on_integer_inputs(gpu_lib):
     # packed and whole-tile layouts sum the same exact products: bit-identical
     T, R, C = 640, 200, 136

@@ -95,6 +95,13 @@ def test_fused_wide_and_narrow_rows(gpu_lib):
     _check_equal(case, _lib.SFT_DW_PACKED)
 
 
+@LAYOUTS
+def test_fused_tile_aligned_slices(gpu_lib, layout):
+    # 100 output tiles of 2 rounds, each cut in half by the slices
+    case = _case([(512, 100 * 256, [(96, 40)])], 2350)
+    _check_equal(case, layout)
+
+
 def test_fused_falls_back_beyond_one_launch(gpu_lib):
     # ten groups need two product launches: the call runs the two calls
     case = _case([(128, 64 + 8 * i, [(40 + 13 * i, 5 + i)]) for i in range(10)], 2400)
