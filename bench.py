@@ -52,6 +52,8 @@ def parse_args():
                     help="step with sft_masked_dw + sft_sparse_update instead of the fused sft_masked_dw_update")
     ap.add_argument("--cpu-sample-every", type=int, default=4,
                     help="oracle timing uses every n-th active row of each matrix")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the timings of the other hot-path calls (embedding, coupled pairs, write-back)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -197,6 +199,143 @@ def cpu_baseline(layer: "Layer", every: int):
     return t_total * scale * 1e3, rows_done, rows_all, t_total
 
 
+def _time_calls(fns, K, stream):
+    """Average ms of one pass over fns (each enqueued on stream), over K back-to-back passes after 5 warm-ups."""
+    import torch
+    for _ in range(5):
+        for f in fns:
+            f(stream)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        for f in fns:
+            f(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / K
+
+
+def _hbm(work_bytes, ms):
+    gbs = work_bytes / (ms * 1e-3) / 1e9
+    return {"avg_ms": round(ms, 5), "algorithmic_bytes": work_bytes, "GB_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def other_rows(L0: "Layer", K: int, stream):
+    """Timings of the hot-path calls the layer step does not run: the embedding
+    scatter-gradient and its update, the coupled pair update (with the packed
+    masked dW feeding it) on one-active-row-per-tile masks, and the standalone
+    masked write-back.  Same event bracketing as the step: K back-to-back
+    passes over prepared calls."""
+    import torch
+
+    from sparse_full_weight_amd import _lib, accounting, synth
+    dev = "cuda"
+    out = {}
+
+    def state(R, C, n, seed):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        st = {"q": torch.randint(-127, 128, (R, C), dtype=torch.int8, device=dev, generator=gen),
+              "s": torch.empty(R, dtype=torch.float32, device=dev).uniform_(1e-4, 1e-3, generator=gen)}
+        st["delta"] = (torch.rand((R, C), dtype=torch.float32, device=dev, generator=gen) - 0.5) * st["s"][:, None]
+        st["w"] = torch.zeros((R, C), dtype=torch.bfloat16, device=dev)
+        st["m"] = torch.zeros((n, C), dtype=torch.int16, device=dev)
+        st["v"] = torch.zeros((n, C), dtype=torch.int16, device=dev)
+        st["t"] = torch.zeros(n, dtype=torch.int32, device=dev)
+        st["slot"] = torch.arange(n, dtype=torch.int32, device=dev)
+        return st
+
+    def upd(st, rows_dev, G, n):
+        return _lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], rows_dev, st["slot"], G, n,
+                           None, st["w"])
+
+    hp = L0.hp
+
+    # ---- embedding: a 32000 x 4096 table, 4 windows of 8 x 512 Zipf(1.1) ids
+    V, d, Tb = 32000, 4096, 8 * 512
+    windows = [synth.zipf_tokens(Tb, V, 1.1, 9000 + w) for w in range(4)]
+    ch = np.zeros(V, np.float32)
+    t0 = time.perf_counter()
+    for tokens in windows:
+        mask = _lib.sft_conductor_window(ch, tokens)
+    plan = _lib.sft_plan_rows(mask)
+    row_ptr, pos = _lib.sft_plan_embedding(plan, tokens)
+    host_us = (time.perf_counter() - t0) * 1e6
+    n = plan.n_active
+    dY = synth.normal_bf16_device((Tb, d), 0.01, 9010, dev)
+    G = torch.empty((max(n, 1), d), dtype=torch.float32, device=dev)
+    st = state(V, d, n, 9020)
+    dplan = plan.to_device()
+    rp, ps = torch.from_numpy(row_ptr).to(dev), torch.from_numpy(pos).to(dev)
+    emb = _lib.prepare_embedding_dw(dY, rp, ps, n, G)
+    eup = _lib.prepare_sparse_update([upd(st, dplan.active_rows, G, n)], hp)
+    w_emb = accounting.embedding_dw_work(d, int(pos.size), n).bytes
+    w_eup = accounting.update_work([(d, n)]).bytes
+    out["a3_embedding_dw"] = dict(_hbm(w_emb, _time_calls([emb], K, stream)), active_rows=n, hit_tokens=int(pos.size),
+                                  table=[V, d], tokens=Tb)
+    out["a3_embedding_dw_and_update"] = dict(_hbm(w_emb + w_eup, _time_calls([emb, eup], K, stream)),
+                                             host_conductor_plan_us=round(host_us, 1))
+    del st, dY, G
+
+    # ---- coupled pairs on one active row per 32-row tile (every tile active)
+    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
+    rows = {name: synth.one_per_tile_rows(L0.mats[name]["R"], 9100 + mi) for mi, name in enumerate(L0.mats)}
+    for a, b in pairs:
+        rows[b][::2] = rows[a][::2]   # a pair shares the row of every other tile
+    groups, plans, G = [], {}, {}
+    for gname, members in synth.LLAMA7B_GROUPS:
+        ms = []
+        for name in members:
+            m = L0.mats[name]
+            plan = _lib.sft_plan_rows(synth.mask_from_rows(m["R"], rows[name]))
+            plans[name] = plan.to_device()
+            G[name] = torch.empty((plan.n_active, m["C"]), dtype=torch.float32, device=dev)
+            ms.append(_lib.DwMat(m["dY"], plans[name], G[name]))
+        groups.append(_lib.DwGroup(L0.X[gname], ms, _lib.SFT_DW_PACKED))
+    ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device=dev)
+    dw = _lib.prepare_masked_dw(groups, ws)
+    sts = {name: state(L0.mats[name]["R"], L0.mats[name]["C"], plans[name].n_active, 9200 + i)
+           for i, name in enumerate(L0.mats)}
+    cp = _lib.prepare_coupled_update([_lib.Pair(upd(sts[a], plans[a].active_rows, G[a], plans[a].n_active),
+                                                upd(sts[b], plans[b].active_rows, G[b], plans[b].n_active), 1.0, 0.4)
+                                      for a, b in pairs], hp)
+    dn = _lib.prepare_sparse_update([upd(sts["down"], plans["down"].active_rows, G["down"], plans["down"].n_active)],
+                                    hp)
+    dw_groups = [(L0.T, L0.mats[mm[0]]["C"], [(plans[n].n_active, plans[n].n_active_tiles) for n in mm])
+                 for _, mm in synth.LLAMA7B_GROUPS]
+    w_dw = accounting.masked_dw_work(dw_groups)
+    sides = []
+    for a, b in pairs:
+        shared = int(np.intersect1d(rows[a], rows[b]).size)
+        sides += [(L0.mats[a]["C"], rows[a].size, shared), (L0.mats[b]["C"], rows[b].size, shared)]
+    w_cp = accounting.coupled_update_work(sides).bytes
+    t_dw = _time_calls([dw], K, stream)
+    out["f1_packed_dw_one_row_per_tile"] = dict(
+        _hbm(w_dw.bytes, t_dw), active_rows=int(sum(p.n_active for p in plans.values())),
+        useful_TFLOP_s=round(w_dw.flops_useful / (t_dw * 1e-3) / 1e12, 1),
+        whole_tile_TFLOP=round(w_dw.flops_issued / 1e12, 3))
+    out["a5_coupled_update"] = dict(_hbm(w_cp, _time_calls([cp], K, stream)), pairs=[list(p) for p in pairs],
+                                    a_own=1.0, a_cross=0.4)
+    out["a5_coupled_and_down_update"] = _hbm(
+        w_cp + accounting.update_work([(L0.mats["down"]["C"], plans["down"].n_active)]).bytes,
+        _time_calls([cp, dn], K, stream))
+    del sts, G, ws
+
+    # ---- standalone write-back of the 1% layer's active rows (7 matrices)
+    wb, w_wb = [], 0.0
+    for name, m in L0.mats.items():
+        plan = m["plan"]
+        rows_dev = torch.from_numpy(plan.active_rows).to(dev)
+        wb.append(_lib.prepare_masked_writeback(m["q"], m["s"], m["delta"], rows_dev, plan.n_active, m["w_live"]))
+        w_wb += accounting.writeback_work(m["C"], plan.n_active).bytes
+    out["a6_masked_writeback"] = dict(_hbm(w_wb, _time_calls(wb, K, stream)), calls=len(wb))
+    torch.cuda.synchronize()
+    return out
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -303,6 +442,11 @@ def main():
     if rec and rec.get("sft_dw_sha256") == profsum.source_hash("sft_dw.hip"):
         traffic = rec["masked_dw_call_bytes"]
 
+    rows = None
+    if not args.no_rows:
+        print("[bench] timing the other hot-path calls", file=sys.stderr, flush=True)
+        rows = other_rows(L0, min(K, 100), stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
@@ -350,6 +494,7 @@ def main():
                                      "hbm_frac": round(fu_gbs / HBM_PEAK_GBS, 4),
                                      "algorithmic_bytes": dw.bytes + up.bytes},
         },
+        "rows": rows,
         "host_plan_us_per_layer": round(host_plan_us, 1),
     }
     print(json.dumps(out), flush=True)

@@ -444,3 +444,19 @@ def prepare_coupled_update(pairs: Sequence[Pair], hp: Adam) -> Prepared:
                                          for p in pairs])
     h = hp.c()
     return Prepared(lib().sft_coupled_update, (arr, len(pairs), C.byref(h)), (arr, h, pairs, hp))
+
+
+def prepare_embedding_dw(dY, row_ptr, positions, n_active: int, dW_act) -> Prepared:
+    import torch
+    T, d = dY.shape
+    args = (_dev(dY, torch.bfloat16), T, d, _dev(row_ptr, torch.int32), _dev(positions, torch.int32), n_active,
+            _dev(dW_act, torch.float32))
+    return Prepared(lib().sft_embedding_dw, args, (dY, row_ptr, positions, dW_act))
+
+
+def prepare_masked_writeback(q, s, delta, active_rows, n_active: int, w_live) -> Prepared:
+    import torch
+    R, Cc = q.shape
+    args = (_dev(q, torch.int8), _dev(s, torch.float32), _dev(delta, torch.float32), R, Cc,
+            _dev(active_rows, torch.int32), n_active, _dev(w_live))
+    return Prepared(lib().sft_masked_writeback, args, (q, s, delta, active_rows, w_live))

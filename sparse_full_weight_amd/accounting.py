@@ -63,6 +63,17 @@ def update_work(mats: Iterable[Tuple[int, int]], fused_writeback: bool = True) -
     return Work(b)
 
 
+def coupled_update_work(sides: Iterable[Tuple[int, int, int]]) -> Work:
+    """sides: (C, n_active_rows, n_rows_also_listed_by_the_partner) per matrix
+    of every pair.  Each listed row takes the update with fused write-back and
+    reads its partner's gradient row where the partner lists the row too."""
+    b = 0.0
+    for C, n, n_shared in sides:
+        b += n * C * (UPDATE_BYTES_PER_ELEMENT + WRITEBACK_BYTES_PER_ELEMENT) + n * UPDATE_BYTES_PER_ROW
+        b += n_shared * C * F32
+    return Work(b)
+
+
 def embedding_dw_work(d: int, nnz: int, n_active: int) -> Work:
     """Reads the bf16 dY row of every hit position, writes fp32 rows."""
     return Work(nnz * d * BF16 + n_active * d * F32 + (nnz + n_active + 1) * 4)

@@ -688,9 +688,18 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
 
 // ---------------------------------------------------------------- embedding
 
-constexpr int kEmbThreads = 1024;  // 16 waves split a row's positions
-constexpr int kEmbCols = 512;      // columns per workgroup: 64 lanes x 8
+constexpr int kEmbThreads = 512;   // 8 waves split a row's positions (measured faster than 4 or 16)
+constexpr int kEmbVec = 4;         // columns per lane (8-byte loads)
+constexpr int kEmbCols = 64 * kEmbVec;   // columns per workgroup
+constexpr int kEmbBatch = 32;      // positions whose dY loads a wave keeps in flight
 
+// One workgroup per (active row, 256 columns).  Wave w sums the w-th of 8
+// contiguous shares of the row's positions (fp64, in position order).  The
+// wave reads up to 64 of its positions with one vector load, takes them from
+// the lanes one by one (wave-uniform), and issues the dY loads of 32
+// positions together before adding them, so a hot row (hundreds of hits)
+// costs a few memory round trips per wave rather than one per position.
+// The 8 wave sums are added in wave order and rounded to fp32 once.
 __global__ __launch_bounds__(kEmbThreads) void k_embedding_dw(const uint16_t *__restrict__ dY,
                                                               int64_t d,
                                                               const int32_t *__restrict__ row_ptr,
@@ -700,26 +709,42 @@ __global__ __launch_bounds__(kEmbThreads) void k_embedding_dw(const uint16_t *__
     const int64_t k = blockIdx.y;
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kEmbCols;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t col = c0 + lane * 8;
-    const int32_t lo = row_ptr[k], hi = row_ptr[k + 1];
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col < d) {
-        for (int32_t i = lo + wave; i < hi; i += kEmbThreads / 64) {
-            const int64_t t = positions[i];
-            const uint4 v = *reinterpret_cast<const uint4 *>(dY + t * d + col);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t col = c0 + lane * kEmbVec;
+    const bool in = col < d;
+    const int64_t lo = row_ptr[k], n = row_ptr[k + 1] - lo;
+    const int64_t a = lo + n * wave / (kEmbThreads / 64), b = lo + n * (wave + 1) / (kEmbThreads / 64);
+    double acc[kEmbVec] = {0, 0, 0, 0};
+    for (int64_t base = a; base < b; base += 64) {
+        const int m = static_cast<int>(b - base < 64 ? b - base : 64);
+        const int32_t pv = lane < m ? positions[base + lane] : 0;
+        for (int j0 = 0; j0 < m; j0 += kEmbBatch) {
+            uint2 v[kEmbBatch];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
-                acc[e] += static_cast<double>(__uint_as_float(bits));
+            for (int j = 0; j < kEmbBatch; ++j) {
+                v[j] = make_uint2(0, 0);
+                if (j0 + j < m) {
+                    const int64_t t = __builtin_amdgcn_readlane(pv, j0 + j);
+                    if (in) v[j] = *reinterpret_cast<const uint2 *>(dY + t * d + col);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kEmbBatch; ++j) {
+                if (j0 + j < m) {
+                    const uint32_t w[2] = {v[j].x, v[j].y};
+#pragma unroll
+                    for (int e = 0; e < kEmbVec; ++e) {
+                        const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+                        acc[e] += static_cast<double>(__uint_as_float(bits));
+                    }
+                }
             }
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = acc[e];
+    for (int e = 0; e < kEmbVec; ++e) part[wave][lane * kEmbVec + e] = acc[e];
     __syncthreads();
-    // Fixed-order combination of the 16 wave partials (fp64), one rounding.
+    // Fixed-order combination of the wave partials (fp64), one rounding.
     for (int c = threadIdx.x; c < kEmbCols; c += kEmbThreads) {
         if (c0 + c >= d) continue;
         double s = part[0][c];

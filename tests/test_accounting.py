@@ -52,3 +52,19 @@ def test_masked_dw_work_llama_layer():
     assert w.flops_issued == pytest.approx(22.95e9, rel=1e-3)
     # a group with no active tile costs nothing (the tile skip)
     assert acc.masked_dw_work([(T, 4096, [(0, 0)])]).bytes == 0
+
+
+def test_coupled_update_bytes():
+    # one pair of 64-column matrices: 3 rows listed by a, 2 by b, 1 by both.
+    # Per listed row element: read g 4, q 1, delta 4, m 2, v 2; write q 1,
+    # delta 4, m 2, v 2, live bf16 2 (24 in all); per row s read + write (8);
+    # a shared row also reads the partner's fp32 gradient row.
+    w = acc.coupled_update_work([(64, 3, 1), (64, 2, 1)])
+    assert w.bytes == (3 + 2) * 64 * 24 + (3 + 2) * 8 + 2 * 64 * 4
+
+
+def test_writeback_and_embedding_bytes():
+    assert acc.writeback_work(16, 3).bytes == 3 * 16 * 7 + 3 * 4
+    # 10 hit tokens of a 32-wide table into 4 rows: bf16 dY rows read, fp32
+    # rows written, CSR (positions + row pointers) read
+    assert acc.embedding_dw_work(32, 10, 4).bytes == 10 * 32 * 2 + 4 * 32 * 4 + (10 + 5) * 4

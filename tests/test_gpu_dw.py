@@ -250,3 +250,19 @@ def test_embedding_dw(gpu_lib, integer):
         assert np.array_equal(got[:plan.n_active], want)
     else:
         dw_close(got[:plan.n_active], want)
+
+
+def test_embedding_dw_hot_rows(gpu_lib):
+    # a 50-row vocabulary and 2048 tokens: the hottest row has more than 512
+    # positions, so each of its 8 position shares spans two 64-position reads
+    # and more than one batch of 32 loads (and the 520 columns leave a ragged
+    # 8-column slab); integer values make every sum exact
+    V, T, d = 50, 2048, 520
+    tokens, plan, row_ptr, pos, dY = _emb_case(V, T, d, 1200, integer=True)
+    assert np.diff(row_ptr).max() > 8 * 64
+    out = torch.full((plan.n_active + 2, d), CANARY, dtype=torch.float32, device="cuda")
+    _lib.sft_embedding_dw(bf16_dev(dY), dev(row_ptr), dev(pos), plan.n_active, out[:plan.n_active])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[plan.n_active:]))
+    assert np.array_equal(got[:plan.n_active], oracle.embedding_dw(dY, tokens, plan.active_rows))
