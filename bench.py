@@ -226,8 +226,8 @@ def _hbm(work_bytes, ms):
 def other_rows(L0: "Layer", K: int, stream):
     """Timings of the hot-path calls the layer step does not run: the embedding
     scatter-gradient and its update, the coupled pair update (with the packed
-    masked dW feeding it) on one-active-row-per-tile masks, and the standalone
-    masked write-back.  Same event bracketing as the step: K back-to-back
+    masked dW feeding it) on one-active-row-per-tile masks, the standalone
+    masked write-back, and the active-row checkpoint save and restore.  Same event bracketing as the step: K back-to-back
     passes over prepared calls."""
     import torch
 
@@ -332,6 +332,17 @@ def other_rows(L0: "Layer", K: int, stream):
         wb.append(_lib.prepare_masked_writeback(m["q"], m["s"], m["delta"], rows_dev, plan.n_active, m["w_live"]))
         w_wb += accounting.writeback_work(m["C"], plan.n_active).bytes
     out["a6_masked_writeback"] = dict(_hbm(w_wb, _time_calls(wb, K, stream)), calls=len(wb))
+
+    # ---- active-row checkpoint of the 1% layer (7 matrices, one call each way)
+    cks = [_lib.CkptMat.alloc(u.q, u.s, u.delta, u.m, u.v, u.t, u.active_rows, u.slot, u.n_active, u.w_live)
+           for u in L0.upd]
+    dims = [(u.q.shape[1], u.n_active) for u in L0.upd]
+    save = _lib.prepare_rows_save(cks)
+    restore = _lib.prepare_rows_restore(cks)
+    out["f2_rows_save"] = dict(_hbm(accounting.checkpoint_work(dims).bytes, _time_calls([save], K, stream)),
+                               rows=int(sum(n for _, n in dims)))
+    out["f2_rows_restore"] = _hbm(accounting.checkpoint_work(dims, restore=True).bytes,
+                                  _time_calls([restore], K, stream))
     torch.cuda.synchronize()
     return out
 

@@ -22,6 +22,12 @@
  *   4. the sparse write-back of the live bf16 weights (section 2.3).
  *                                                                  -> sft_masked_writeback
  *                                                                     (or fused into 3)
+ *   5. checkpoint and rewind (section 2.6): a host controller decides from
+ *      the loss when to save the active rows and when to restore them;
+ *                                                                  -> sft_rewind_init,
+ *                                                                     sft_rewind_observe,
+ *                                                                     sft_rows_save,
+ *                                                                     sft_rows_restore
  *
  * Conventions shared by every call:
  *   - Status: every entry point returns SFT_OK (0) or a negative SFT_E* code,
@@ -57,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 4
+#define SFT_ABI_VERSION 5
 
 enum {
     SFT_OK = 0,
@@ -160,6 +166,63 @@ int sft_slots_update(int32_t *row_slot, int64_t rows, int64_t n_slots,
  * Errors: SFT_EINVAL (null, t_max < 1, beta outside [0, 1)).
  */
 int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *bc2);
+
+/*
+ * Checkpoint-and-rewind controller (section 2.6).  A copy of the active rows
+ * is refreshed while the loss stays close (10%) to the loss of the last copy;
+ * each new lowest loss is watched for 10 steps, and a loss more than 15%
+ * above it when the watch ends brings the copy back, restarts the phase
+ * stride at 1 and drops the step (up to 3 times for one minimum); a minimum
+ * that survives its watch becomes the reference for later copies.
+ * Readings of the prose, exactly as implemented (loss = the loss the caller
+ * has for the latest step, a double; comparisons in double):
+ *   - save when there is no checkpoint yet or
+ *     loss <= (1 + save_within) * checkpoint_loss; a save sets
+ *     checkpoint_loss = loss;
+ *   - a new minimum is a loss below every loss seen so far (min_loss); it
+ *     sets watch_left = watch_steps and recoveries = 0;
+ *   - each later step decrements watch_left; the step that brings it to 0
+ *     ends the watch: if loss > (1 + rise_above) * min_loss and
+ *     recoveries < max_recoveries, the action is SFT_REWIND_RESTORE,
+ *     recoveries grows by one and the watch re-opens on the same minimum
+ *     (nothing else happens on that step: it is skipped); otherwise the
+ *     minimum is accepted (checkpoint_loss = min_loss, watch closed) and the
+ *     step goes on;
+ *   - order within a step: end of watch, then new minimum, then save;
+ *   - a NaN or infinite loss counts as +infinity: never a minimum, never
+ *     saved, always a rise.
+ * sft_rewind_init sets the page's values (0.10, 0.15, 10 steps, 3 recoveries)
+ * and an empty state; the settings may be changed before the first
+ * observation.  On SFT_REWIND_RESTORE the caller restores the rows saved last
+ * (sft_rows_restore), resets its phase stride to 1 and does not apply the
+ * step's update; on SFT_REWIND_SAVE it saves the active rows (sft_rows_save)
+ * after the step's update.
+ */
+enum { SFT_REWIND_SAVE = 1, SFT_REWIND_RESTORE = 2 };
+
+typedef struct sft_rewind {
+    double save_within;       /* 0.10 */
+    double rise_above;        /* 0.15 */
+    int32_t watch_steps;      /* 10 */
+    int32_t max_recoveries;   /* 3 */
+    /* state */
+    int32_t has_checkpoint;
+    int32_t watch_left;       /* 0 = no watch open */
+    int32_t recoveries;       /* restores since the current minimum */
+    int32_t reserved;
+    double checkpoint_loss;
+    double min_loss;          /* +inf before the first finite loss */
+} sft_rewind;
+
+/* Errors: SFT_EINVAL (null). */
+int sft_rewind_init(sft_rewind *st);
+
+/*
+ * Feeds one step's loss; *action = 0, SFT_REWIND_SAVE or SFT_REWIND_RESTORE.
+ * Errors: SFT_EINVAL (null pointers, save_within or rise_above negative or
+ * NaN, watch_steps < 1, max_recoveries < 0); the state is then unchanged.
+ */
+int sft_rewind_observe(sft_rewind *st, double loss, int32_t *action);
 
 /* ======================================================================= */
 /* device: the masked backward pass (section 2.2)                           */
@@ -354,6 +417,67 @@ int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *h
 int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, int64_t R,
                          int64_t C, const int32_t *active_rows, int64_t n_active,
                          uint16_t *w_live, void *stream);
+
+/* ======================================================================= */
+/* device: active-row checkpoints (section 2.6)                             */
+/* ======================================================================= */
+
+/*
+ * One matrix's part of a checkpoint (section 2.6: the copy holds the active
+ * rows only, so it is the size of the active set).  The live state
+ * is laid out as in sft_upd_mat; the checkpoint buffers are caller-owned
+ * device arrays whose row k belongs to rows[k].
+ *   rows  [n_rows] strictly ascending, < R (device)
+ *   slot  [n_rows] the moment slot of each row, in [0, n_slots) (device):
+ *         at save the slot the moments are read from, at restore the slot
+ *         they are written to (the same array unless slots were reassigned)
+ *   q, s, delta, m, v, t   live state: int8 [R x C], fp32 [R], fp32 [R x C],
+ *                          fp16 [n_slots x C] twice, int32 [n_slots]
+ *   w_live                 bf16 [R x C]; restore rebuilds the restored rows
+ *                          as in sft_masked_writeback; NULL = no live copy
+ *   ck_q [n_rows x C] int8, ck_s [n_rows] fp32, ck_delta [n_rows x C] fp32,
+ *   ck_m, ck_v [n_rows x C] fp16, ck_t [n_rows] int32
+ */
+typedef struct sft_ckpt_mat {
+    int64_t R, C, n_rows, n_slots;
+    const int32_t *rows;
+    const int32_t *slot;
+    int8_t *q;
+    float *s;
+    float *delta;
+    uint16_t *m;
+    uint16_t *v;
+    int32_t *t;
+    uint16_t *w_live;
+    int8_t *ck_q;
+    float *ck_s;
+    float *ck_delta;
+    uint16_t *ck_m;
+    uint16_t *ck_v;
+    int32_t *ck_t;
+} sft_ckpt_mat;
+
+/*
+ * Copies the listed rows of every matrix (q, s, delta and the moments and
+ * step count of their slots) into the checkpoint buffers, bit for bit; one
+ * launch for all matrices.  Rows not listed and the live state are not
+ * touched.
+ * Limits: C % 8 == 0, fewer than 2^31 rows in all.
+ * Errors: SFT_EINVAL (null pointers, negative sizes, n_rows above R or
+ * n_slots), SFT_ESHAPE (C % 8), SFT_EALIGN (a row-major buffer not 16-byte
+ * aligned), SFT_ENOTSUP (beyond the limits), SFT_EHIP.  Nothing is launched
+ * when a check fails.
+ */
+int sft_rows_save(const sft_ckpt_mat *mats, int32_t n_mats, void *stream);
+
+/*
+ * The inverse copy: writes the checkpointed q, s, delta rows back to their
+ * rows and the moments and step counts back to slot[k], bit for bit, and
+ * rebuilds those rows of w_live (bf16 of fl(s*q) + delta, as
+ * sft_masked_writeback) when w_live is set.  Rows not listed are not
+ * touched.  Limits and errors: as sft_rows_save.
+ */
+int sft_rows_restore(const sft_ckpt_mat *mats, int32_t n_mats, void *stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,7 @@ EXPORTS = (
     "sft_last_error", "sft_abi_version", "sft_conductor_window", "sft_tracker_window", "sft_plan_rows",
     "sft_plan_embedding", "sft_slots_update", "sft_bias_table", "sft_masked_dw_workspace", "sft_masked_dw",
     "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback", "sft_masked_dw_update",
+    "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
 )
 
 
@@ -79,6 +80,21 @@ class CPair(C.Structure):
                 ("clip", C.c_void_p)]
 
 
+class CRewind(C.Structure):
+    _fields_ = [("save_within", C.c_double), ("rise_above", C.c_double), ("watch_steps", C.c_int32),
+                ("max_recoveries", C.c_int32), ("has_checkpoint", C.c_int32), ("watch_left", C.c_int32),
+                ("recoveries", C.c_int32), ("reserved", C.c_int32), ("checkpoint_loss", C.c_double),
+                ("min_loss", C.c_double)]
+
+
+class CCkptMat(C.Structure):
+    _fields_ = [("R", C.c_int64), ("C", C.c_int64), ("n_rows", C.c_int64), ("n_slots", C.c_int64),
+                ("rows", C.c_void_p), ("slot", C.c_void_p), ("q", C.c_void_p), ("s", C.c_void_p),
+                ("delta", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p), ("t", C.c_void_p),
+                ("w_live", C.c_void_p), ("ck_q", C.c_void_p), ("ck_s", C.c_void_p), ("ck_delta", C.c_void_p),
+                ("ck_m", C.c_void_p), ("ck_v", C.c_void_p), ("ck_t", C.c_void_p)]
+
+
 _lib: Optional[C.CDLL] = None
 
 
@@ -109,6 +125,10 @@ def lib() -> C.CDLL:
         L.sft_masked_dw_update.argtypes = [C.POINTER(CDwGroup), i32, p, C.c_size_t, C.POINTER(CUpdMat), i32,
                                            C.POINTER(CAdam), p]
         L.sft_masked_writeback.argtypes = [p, p, p, i64, i64, p, i64, p, p]
+        L.sft_rewind_init.argtypes = [C.POINTER(CRewind)]
+        L.sft_rewind_observe.argtypes = [C.POINTER(CRewind), C.c_double, C.POINTER(C.c_int32)]
+        L.sft_rows_save.argtypes = [C.POINTER(CCkptMat), i32, p]
+        L.sft_rows_restore.argtypes = [C.POINTER(CCkptMat), i32, p]
         for n in EXPORTS[2:]:
             if n != "sft_masked_dw_workspace":
                 getattr(L, n).restype = C.c_int
@@ -460,3 +480,89 @@ def prepare_masked_writeback(q, s, delta, active_rows, n_active: int, w_live) ->
     args = (_dev(q, torch.int8), _dev(s, torch.float32), _dev(delta, torch.float32), R, Cc,
             _dev(active_rows, torch.int32), n_active, _dev(w_live))
     return Prepared(lib().sft_masked_writeback, args, (q, s, delta, active_rows, w_live))
+
+
+# ------------------------------------------------------------------ checkpoint and rewind
+SFT_REWIND_SAVE = 1
+SFT_REWIND_RESTORE = 2
+
+
+class Rewind:
+    """Section 2.6 controller (host, C library): observe(loss) -> 0,
+    SFT_REWIND_SAVE or SFT_REWIND_RESTORE.  ``st`` is the C state (its
+    settings may be changed before the first observation)."""
+
+    def __init__(self):
+        self.st = CRewind()
+        _check(lib().sft_rewind_init(C.byref(self.st)))
+
+    def observe(self, loss: float) -> int:
+        act = C.c_int32(0)
+        _check(lib().sft_rewind_observe(C.byref(self.st), float(loss), C.byref(act)))
+        return act.value
+
+    def state(self) -> CRewind:
+        return self.st
+
+
+@dataclass
+class CkptMat:
+    """One matrix's live state, its checkpointed rows and the checkpoint buffers."""
+    q: "object"             # int8 [R x C]
+    s: "object"             # fp32 [R]
+    delta: "object"         # fp32 [R x C]
+    m: "object"             # fp16 bits [n_slots x C]
+    v: "object"
+    t: "object"             # int32 [n_slots]
+    rows: "object"          # int32 [n_rows] (GPU)
+    slot: "object"          # int32 [n_rows] (GPU)
+    ck_q: "object"          # int8 [n_rows x C]
+    ck_s: "object"          # fp32 [n_rows]
+    ck_delta: "object"      # fp32 [n_rows x C]
+    ck_m: "object"          # fp16 bits [n_rows x C]
+    ck_v: "object"
+    ck_t: "object"          # int32 [n_rows]
+    n_rows: int
+    w_live: "object" = None  # bf16 [R x C] or None
+
+    def c(self) -> CCkptMat:
+        R, Cc = self.q.shape
+        return CCkptMat(R, Cc, self.n_rows, self.m.shape[0], _dev(self.rows), _dev(self.slot), _dev(self.q),
+                        _dev(self.s), _dev(self.delta), _dev(self.m), _dev(self.v), _dev(self.t),
+                        _dev(self.w_live), _dev(self.ck_q), _dev(self.ck_s), _dev(self.ck_delta),
+                        _dev(self.ck_m), _dev(self.ck_v), _dev(self.ck_t))
+
+    @staticmethod
+    def alloc(q, s, delta, m, v, t, rows, slot, n_rows: int, w_live=None) -> "CkptMat":
+        """Checkpoint buffers for n_rows rows of this state (device tensors)."""
+        import torch
+        Cc = q.shape[1]
+        dev = q.device
+        n = max(n_rows, 1)
+        return CkptMat(q, s, delta, m, v, t, rows, slot, torch.empty((n, Cc), dtype=torch.int8, device=dev),
+                       torch.empty(n, dtype=torch.float32, device=dev),
+                       torch.empty((n, Cc), dtype=torch.float32, device=dev),
+                       torch.empty((n, Cc), dtype=m.dtype, device=dev), torch.empty((n, Cc), dtype=v.dtype, device=dev),
+                       torch.empty(n, dtype=torch.int32, device=dev), n_rows, w_live)
+
+
+def sft_rows_save(mats: Sequence[CkptMat], stream=None) -> None:
+    """Section 2.6: copy the listed rows of every matrix into its checkpoint buffers."""
+    arr = (CCkptMat * max(len(mats), 1))(*[m.c() for m in mats])
+    _check(lib().sft_rows_save(arr, len(mats), _stream(stream)))
+
+
+def sft_rows_restore(mats: Sequence[CkptMat], stream=None) -> None:
+    """Section 2.6: write the checkpointed rows back (and rebuild their live bf16 rows)."""
+    arr = (CCkptMat * max(len(mats), 1))(*[m.c() for m in mats])
+    _check(lib().sft_rows_restore(arr, len(mats), _stream(stream)))
+
+
+def prepare_rows_save(mats: Sequence[CkptMat]) -> Prepared:
+    arr = (CCkptMat * max(len(mats), 1))(*[m.c() for m in mats])
+    return Prepared(lib().sft_rows_save, (arr, len(mats)), (arr, mats))
+
+
+def prepare_rows_restore(mats: Sequence[CkptMat]) -> Prepared:
+    arr = (CCkptMat * max(len(mats), 1))(*[m.c() for m in mats])
+    return Prepared(lib().sft_rows_restore, (arr, len(mats)), (arr, mats))

@@ -74,6 +74,19 @@ def coupled_update_work(sides: Iterable[Tuple[int, int, int]]) -> Work:
     return Work(b)
 
 
+# Section 2.6 checkpoint of one row element: q (1), delta (4), m (2), v (2),
+# read on one side and written on the other; a restore also writes the live
+# bf16 weight (2).  Per row: s and the slot's step count, read and written.
+CHECKPOINT_BYTES_PER_ELEMENT = 2 * (1 + 4 + 2 + 2)
+CHECKPOINT_BYTES_PER_ROW = 2 * (4 + 4)
+
+
+def checkpoint_work(mats: Iterable[Tuple[int, int]], restore: bool = False, live: bool = True) -> Work:
+    """mats: (C, n_rows) per matrix; restore adds the rebuilt live rows."""
+    per = CHECKPOINT_BYTES_PER_ELEMENT + (WRITEBACK_BYTES_PER_ELEMENT if restore and live else 0)
+    return Work(sum(n * C * per + n * CHECKPOINT_BYTES_PER_ROW for C, n in mats))
+
+
 def embedding_dw_work(d: int, nnz: int, n_active: int) -> Work:
     """Reads the bf16 dY row of every hit position, writes fp32 rows."""
     return Work(nnz * d * BF16 + n_active * d * F32 + (nnz + n_active + 1) * 4)

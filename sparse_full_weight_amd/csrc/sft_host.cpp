@@ -222,4 +222,50 @@ int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *b
     return SFT_OK;
 }
 
+// Checkpoint-and-rewind controller (section 2.6); the readings it implements
+// are stated with the declaration.  All arithmetic in double.
+int sft_rewind_init(sft_rewind *st) {
+    clear_error();
+    SFT_CHECK(st, SFT_EINVAL, "rewind_init: null state");
+    std::memset(st, 0, sizeof(*st));
+    st->save_within = 0.10;
+    st->rise_above = 0.15;
+    st->watch_steps = 10;
+    st->max_recoveries = 3;
+    st->min_loss = HUGE_VAL;
+    return SFT_OK;
+}
+
+int sft_rewind_observe(sft_rewind *st, double loss, int32_t *action) {
+    clear_error();
+    SFT_CHECK(st && action, SFT_EINVAL, "rewind_observe: null pointer");
+    SFT_CHECK(st->save_within >= 0.0 && st->rise_above >= 0.0, SFT_EINVAL,
+              "rewind_observe: save_within and rise_above must be >= 0");
+    SFT_CHECK(st->watch_steps >= 1 && st->max_recoveries >= 0, SFT_EINVAL,
+              "rewind_observe: watch_steps < 1 or max_recoveries < 0");
+    const double x = std::isfinite(loss) ? loss : HUGE_VAL;
+    *action = 0;
+    if (st->watch_left > 0 && --st->watch_left == 0) {
+        // the watch on min_loss ends with this step
+        if (x > (1.0 + st->rise_above) * st->min_loss && st->recoveries < st->max_recoveries) {
+            ++st->recoveries;
+            st->watch_left = st->watch_steps;
+            *action = SFT_REWIND_RESTORE;
+            return SFT_OK;
+        }
+        st->checkpoint_loss = st->min_loss;
+    }
+    if (x < st->min_loss) {
+        st->min_loss = x;
+        st->watch_left = st->watch_steps;
+        st->recoveries = 0;
+    }
+    if (x != HUGE_VAL && (!st->has_checkpoint || x <= (1.0 + st->save_within) * st->checkpoint_loss)) {
+        st->has_checkpoint = 1;
+        st->checkpoint_loss = x;
+        *action = SFT_REWIND_SAVE;
+    }
+    return SFT_OK;
+}
+
 }  // extern "C"

@@ -408,6 +408,111 @@ __global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restri
     }
 }
 
+// ---- Active-row checkpoints (section 2.6: only the active rows are copied).
+constexpr int kCkMats = 16;      // matrices per launch (kernel-argument size)
+constexpr int kCkThreads = 256;
+constexpr int kCkBatch = 4;      // 8-column chunks per lane whose loads are in flight together
+
+struct CkMatDev {
+    sft_ckpt_mat m;
+    int64_t row_begin;   // first workgroup (= checkpointed row) of this matrix
+};
+
+struct CkParams {
+    CkMatDev mat[kCkMats];
+    int32_t n_mats;
+};
+
+// One workgroup per checkpointed row.  Per 8-column chunk the row's q
+// (8 bytes) and delta (32 bytes) and its slot's m and v (16 bytes each) go
+// live -> checkpoint (save) or back (restore); a restore also rebuilds the
+// row's live bf16 weights from the restored values, as the write-back does.
+// Lane l takes chunks l, l + 256, ...; it issues the loads of 4 chunks before
+// its stores.  The row's s and its slot's t are copied by lane 0.
+template <bool kRestore>
+__global__ __launch_bounds__(kCkThreads) void k_rows_copy(const CkParams p) {
+    const int64_t wg = blockIdx.x;
+    int mi = 0;
+    while (mi + 1 < p.n_mats && wg >= p.mat[mi + 1].row_begin) ++mi;
+    const sft_ckpt_mat &M = p.mat[mi].m;
+    const int64_t k = wg - p.mat[mi].row_begin;
+    const int64_t r = M.rows[k], sl = M.slot[k], C = M.C;
+    int8_t *const lq = M.q + r * C, *const cq = M.ck_q + k * C;
+    float *const ld = M.delta + r * C, *const cd = M.ck_delta + k * C;
+    uint16_t *const lm = M.m + sl * C, *const cm = M.ck_m + k * C;
+    uint16_t *const lv = M.v + sl * C, *const cv = M.ck_v + k * C;
+    const int8_t *const q_src = kRestore ? cq : lq;
+    int8_t *const q_dst = kRestore ? lq : cq;
+    const float *const d_src = kRestore ? cd : ld;
+    float *const d_dst = kRestore ? ld : cd;
+    const uint16_t *const m_src = kRestore ? cm : lm;
+    uint16_t *const m_dst = kRestore ? lm : cm;
+    const uint16_t *const v_src = kRestore ? cv : lv;
+    uint16_t *const v_dst = kRestore ? lv : cv;
+    uint16_t *const w = (kRestore && M.w_live) ? M.w_live + r * C : nullptr;
+    const float s_row = kRestore ? M.ck_s[k] : 0.0f;
+    if (threadIdx.x == 0) {
+        if (kRestore) {
+            M.s[r] = s_row;
+            M.t[sl] = M.ck_t[k];
+        } else {
+            M.ck_s[k] = M.s[r];
+            M.ck_t[k] = M.t[sl];
+        }
+    }
+    // One 8-column chunk in registers.  The four chunks of a batch are named
+    // variables, not an array: an array here was placed in LDS and scratch.
+    struct Chunk {
+        uint2 q;
+        float4 d0, d1;
+        uint4 m, v;
+    };
+    auto load = [&](int64_t c) __attribute__((always_inline)) {
+        Chunk x;
+        x.q = *reinterpret_cast<const uint2 *>(q_src + c);
+        x.d0 = *reinterpret_cast<const float4 *>(d_src + c);
+        x.d1 = *reinterpret_cast<const float4 *>(d_src + c + 4);
+        x.m = *reinterpret_cast<const uint4 *>(m_src + c);
+        x.v = *reinterpret_cast<const uint4 *>(v_src + c);
+        return x;
+    };
+    auto store = [&](int64_t c, const Chunk &x) __attribute__((always_inline)) {
+        if (c >= C) return;
+        *reinterpret_cast<uint2 *>(q_dst + c) = x.q;
+        *reinterpret_cast<float4 *>(d_dst + c) = x.d0;
+        *reinterpret_cast<float4 *>(d_dst + c + 4) = x.d1;
+        *reinterpret_cast<uint4 *>(m_dst + c) = x.m;
+        *reinterpret_cast<uint4 *>(v_dst + c) = x.v;
+        if (w) {
+            const float df[8] = {x.d0.x, x.d0.y, x.d0.z, x.d0.w, x.d1.x, x.d1.y, x.d1.z, x.d1.w};
+            uint32_t o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t word = e < 4 ? x.q.x : x.q.y;
+                const int8_t qe = static_cast<int8_t>((word >> (8 * (e & 3))) & 0xffu);
+                const float sq = s_row * static_cast<float>(qe);
+                o[e] = f2bf(sq + df[e]);
+            }
+            *reinterpret_cast<uint4 *>(w + c) =
+                make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16));
+        }
+    };
+    static_assert(kCkBatch == 4, "the batch below is spelled out for four chunks");
+    constexpr int64_t kStep = 8 * kCkThreads;
+    for (int64_t c0 = 8 * static_cast<int64_t>(threadIdx.x); c0 < C; c0 += kStep * kCkBatch) {
+        // chunks past the row read chunk c0 again (in bounds) and store nothing
+        const int64_t c1 = c0 + kStep, c2 = c0 + 2 * kStep, c3 = c0 + 3 * kStep;
+        const Chunk x0 = load(c0);
+        const Chunk x1 = load(c1 < C ? c1 : c0);
+        const Chunk x2 = load(c2 < C ? c2 : c0);
+        const Chunk x3 = load(c3 < C ? c3 : c0);
+        store(c0, x0);
+        store(c1, x1);
+        store(c2, x2);
+        store(c3, x3);
+    }
+}
+
 // Update fused with the masked-dW fix-up: the gradient of a 256-column block
 // of the row is the sum, in slice order, of the partial rows the slices that
 // cut its output tile left (the same additions as the fix-up kernel's), or
@@ -838,6 +943,73 @@ int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, in
     hipLaunchKernelGGL(k_masked_writeback, dim3(static_cast<uint32_t>(n_active)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), q, s, delta, C, active_rows, w_live);
     return launch_status("sft_masked_writeback");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation and batched launches shared by sft_rows_save / sft_rows_restore.
+int rows_copy(const sft_ckpt_mat *mats, int32_t n_mats, void *stream, bool restore, const char *who) {
+    sft::clear_error();
+    SFT_CHECK(n_mats >= 0 && (n_mats == 0 || mats), SFT_EINVAL, "%s: bad matrix list", who);
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const sft_ckpt_mat &m = mats[i];
+        SFT_CHECK(m.R >= 0 && m.C > 0 && m.n_rows >= 0 && m.n_slots >= 0, SFT_EINVAL,
+                  "%s: matrix %d: bad sizes (R=%lld C=%lld n_rows=%lld)", who, i, (long long)m.R,
+                  (long long)m.C, (long long)m.n_rows);
+        SFT_CHECK(m.n_rows <= m.R && m.n_rows <= m.n_slots, SFT_EINVAL,
+                  "%s: matrix %d: n_rows=%lld exceeds R or n_slots", who, i, (long long)m.n_rows);
+        SFT_CHECK(m.C % 8 == 0, SFT_ESHAPE, "%s: matrix %d: C=%lld is not a multiple of 8", who, i,
+                  (long long)m.C);
+        if (m.n_rows == 0) continue;
+        SFT_CHECK(m.rows && m.slot && m.q && m.s && m.delta && m.m && m.v && m.t && m.ck_q && m.ck_s &&
+                      m.ck_delta && m.ck_m && m.ck_v && m.ck_t,
+                  SFT_EINVAL, "%s: matrix %d: null device pointer", who, i);
+        SFT_CHECK(sft::aligned16(m.q) && sft::aligned16(m.delta) && sft::aligned16(m.m) && sft::aligned16(m.v) &&
+                      sft::aligned16(m.ck_q) && sft::aligned16(m.ck_delta) && sft::aligned16(m.ck_m) &&
+                      sft::aligned16(m.ck_v) && (!m.w_live || sft::aligned16(m.w_live)),
+                  SFT_EALIGN, "%s: matrix %d: a row-major buffer is not 16-byte aligned", who, i);
+        total += m.n_rows;
+    }
+    SFT_CHECK(total < (int64_t(1) << 31), SFT_ENOTSUP, "%s: %lld rows in one call", who, (long long)total);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    CkParams p{};
+    int64_t rows = 0;
+    auto flush = [&]() -> int {
+        if (p.n_mats == 0) return SFT_OK;
+        if (restore)
+            hipLaunchKernelGGL(k_rows_copy<true>, dim3(static_cast<uint32_t>(rows)), dim3(kCkThreads), 0, st, p);
+        else
+            hipLaunchKernelGGL(k_rows_copy<false>, dim3(static_cast<uint32_t>(rows)), dim3(kCkThreads), 0, st, p);
+        const int rc = launch_status(who);
+        p = CkParams{};
+        rows = 0;
+        return rc;
+    };
+    for (int32_t i = 0; i < n_mats; ++i) {
+        if (mats[i].n_rows == 0) continue;
+        if (p.n_mats == kCkMats)
+            if (int rc = flush()) return rc;
+        p.mat[p.n_mats].m = mats[i];
+        p.mat[p.n_mats].row_begin = rows;
+        ++p.n_mats;
+        rows += mats[i].n_rows;
+    }
+    return flush();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sft_rows_save(const sft_ckpt_mat *mats, int32_t n_mats, void *stream) {
+    return rows_copy(mats, n_mats, stream, false, "sft_rows_save");
+}
+
+int sft_rows_restore(const sft_ckpt_mat *mats, int32_t n_mats, void *stream) {
+    return rows_copy(mats, n_mats, stream, true, "sft_rows_restore");
 }
 
 }  // extern "C"

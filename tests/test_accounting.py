@@ -68,3 +68,11 @@ def test_writeback_and_embedding_bytes():
     # 10 hit tokens of a 32-wide table into 4 rows: bf16 dY rows read, fp32
     # rows written, CSR (positions + row pointers) read
     assert acc.embedding_dw_work(32, 10, 4).bytes == 10 * 32 * 2 + 4 * 32 * 4 + (10 + 5) * 4
+
+
+def test_checkpoint_bytes():
+    # 3 rows of 16 columns: q 1 + delta 4 + m 2 + v 2 read and written per
+    # element, s and t read and written per row; a restore writes bf16 too
+    assert acc.checkpoint_work([(16, 3)]).bytes == 3 * 16 * 18 + 3 * 16
+    assert acc.checkpoint_work([(16, 3)], restore=True).bytes == 3 * 16 * 20 + 3 * 16
+    assert acc.checkpoint_work([(16, 3)], restore=True, live=False).bytes == 3 * 16 * 18 + 3 * 16

@@ -1,0 +1,60 @@
+"""The library's checkpoint-and-rewind controller (host code, section 2.6 of
+"Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the Active
+Set") against the oracle: on the hand-worked pin sequences and on long
+seeded loss runs with spikes and NaNs, every action and every state field
+must agree exactly (both compare in double precision)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import rewind as rw
+from sparse_full_weight_amd import _lib
+
+
+def _run(losses):
+    c = rw.Rewind()
+    return [c.observe(x) for x in losses]
+
+
+def _random_losses(seed, n):
+    g = np.random.default_rng(seed)
+    x, out = 5.0, []
+    for _ in range(n):
+        x *= math.exp(g.normal(-0.01, 0.04))
+        y = x * (1.0 + (g.random() < 0.05) * g.uniform(0.1, 0.6))   # occasional spikes
+        if g.random() < 0.01:
+            y = float("nan")
+        out.append(y)
+    return out
+
+
+def test_library_controller_matches_the_pins():
+    cases = [[10.0, 9.0, 8.0, 7.0], [10.0, 8.0] + [8.5] * 9 + [9.3],
+             [10.0, 8.0] + [8.5] * 9 + [9.3] + [9.3] * 40,
+             [10.0, 8.0] + [9.0] * 5 + [7.0] + [9.0] * 10, [10.0, float("nan")] + [math.inf] * 9]
+    for losses in cases:
+        want = _run(losses)
+        ctl = _lib.Rewind()
+        assert [ctl.observe(x) for x in losses] == want
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_library_controller_matches_oracle_on_long_runs(seed):
+    losses = _random_losses(seed, 3000)
+    o = rw.Rewind()
+    c = _lib.Rewind()
+    for x in losses:
+        assert c.observe(x) == o.observe(x)
+        st = c.state()
+        assert (st.has_checkpoint, st.watch_left, st.recoveries) == (int(o.has_checkpoint), o.watch_left,
+                                                                     o.recoveries)
+        assert st.checkpoint_loss == o.checkpoint_loss and st.min_loss == o.min_loss
+
+
+def test_library_controller_rejects_bad_settings():
+    c = _lib.Rewind()
+    c.st.watch_steps = 0
+    with pytest.raises(_lib.SftError) as e:
+        c.observe(1.0)
+    assert e.value.code == _lib.SFT_EINVAL
