@@ -53,7 +53,11 @@ def parse_args():
     ap.add_argument("--cpu-sample-every", type=int, default=4,
                     help="oracle timing uses every n-th active row of each matrix")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the timings of the other hot-path calls (embedding, coupled pairs, write-back)")
+                    help="skip the timings of the other hot-path calls (embedding, coupled pairs, write-back, "
+                         "checkpoint)")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time only the other hot-path calls (prints their JSON object), for profiling them apart "
+                         "from the layer step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -389,6 +393,9 @@ def main():
     host_plan_us = (time.perf_counter() - th0) * 1e6
 
     stream = torch.cuda.current_stream()
+    if args.rows_only:
+        print(json.dumps({"rows": other_rows(layers[0], min(args.steps, 100), stream)}), flush=True)
+        return
 
     def step(L):
         L.upload_plan()

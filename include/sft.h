@@ -40,7 +40,7 @@
  *     scalars and pointer alignment, enqueue their kernels on `stream` (a
  *     hipStream_t passed as void*, NULL = the default stream) and return
  *     without synchronising.  They never copy anything back to the host
- *     (section 2.6 of the page: nothing is read back in the middle of a step),
+ *     (section 2.6 of the page: no readback happens while a step runs),
  *     so a fault inside a kernel surfaces at the caller's next synchronisation.
  *     Inputs must stay alive until the stream work completes.
  *   - Layouts: row-major and contiguous.  bf16 and fp16 values are passed as
@@ -108,7 +108,7 @@ int sft_conductor_window(float *ch, int64_t rows, const int32_t *tokens, int64_t
 int sft_tracker_window(float *ch, int64_t rows, const float *magnitude, uint8_t *active);
 
 /*
- * Row plan of one mask (section 2.2: the mask is checked per tile of 32 rows).
+ * Row plan of one mask (section 2.2: the mask is tested 32 rows at a time).
  * Caller-allocated arrays; the call fills the counts.
  *   tile_bits    [ceil(rows/32)]  bit i of word j = mask of row 32*j+i (bits >= rows are 0)
  *   active_rows  [rows]           ascending active rows (first n_active valid)
@@ -157,8 +157,8 @@ int sft_slots_update(int32_t *row_slot, int64_t rows, int64_t n_slots,
                      uint8_t *fresh);
 
 /*
- * Adam bias corrections (section 2.4, "a standard Adam step with bias
- * correction"): bc1[t] = fl32(1 - beta1^t), bc2[t] = fl32(1 - beta2^t) for
+ * Adam bias corrections (section 2.4: Adam with its bias correction):
+ * bc1[t] = fl32(1 - beta1^t), bc2[t] = fl32(1 - beta2^t) for
  * t = 1..t_max, computed in fp64 and rounded once; bc1[0] = bc2[0] = 0.
  * The arrays hold t_max + 1 floats.  The update kernels read entry
  * min(t, t_max); choose t_max so that the entries have reached 1.0f (about
@@ -185,9 +185,9 @@ int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *b
  *     ends the watch: if loss > (1 + rise_above) * min_loss and
  *     recoveries < max_recoveries, the action is SFT_REWIND_RESTORE,
  *     recoveries grows by one and the watch re-opens on the same minimum
- *     (nothing else happens on that step: it is skipped); otherwise the
- *     minimum is accepted (checkpoint_loss = min_loss, watch closed) and the
- *     step goes on;
+ *     (nothing else happens on that step: it is skipped); in every other
+ *     case the minimum stands (checkpoint_loss = min_loss, watch closed) and
+ *     the step goes on;
  *   - order within a step: end of watch, then new minimum, then save;
  *   - a NaN or infinite loss counts as +infinity: never a minimum, never
  *     saved, always a rise.

@@ -17,8 +17,8 @@ in prose only; the readings taken here are:
      (1 + 0.15) times the minimum and fewer than 3 recoveries were made for
      this minimum, the rows are restored, the stride restarts and the step
      is dropped (nothing else happens on it), and the watch starts again on
-     the same minimum; otherwise the minimum is accepted and becomes the loss
-     that later copies are compared with;
+     the same minimum; in every other case the minimum stands and later
+     copies are compared with it;
   4. within one step: end of watch first, then the new-minimum test, then
      the copy test;
   5. a NaN or infinite loss is taken as +infinity.

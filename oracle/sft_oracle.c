@@ -376,9 +376,9 @@ typedef struct {
 /*
  * Update one active row of a matrix with the (effective) gradient g[C].
  *
- * Section 2.3: the weight is stored as int8 q with a per-row scale s and an
- * fp32 residual delta; the fp32 weight w = s*q + delta is rebuilt, updated
- * and stored back as a new q and delta; m and v are stored in fp16.  The
+ * Section 2.3: storage is an int8 code q, a scale s per row and an fp32
+ * residual delta; the fp32 weight w = s*q + delta is rebuilt, stepped and
+ * split again into q and delta; m and v live in fp16.  The
  * equation of the quantiser is lost; the reading is: w is rebuilt with two
  * roundings (product, then sum), the new scale is the row's largest |w'| over
  * 127, q' = clamp(rint(w'/s'), -127, 127) and delta' = w' - s'*q' (exact by
@@ -489,7 +489,7 @@ ORACLE_API int oracle_sparse_update(oracle_mat *M, const oracle_adam *hp)
 
 /*
  * Coupled update of a pair (A, B) of equally shaped matrices, section 2.4:
- * each matrix's gradient informs its partner's step.  The lost equations give
+ * the step of each matrix also sees its partner's gradient.  The lost equations give
  * the effective gradients as a blend of the two clipped gradients; with the
  * blend weights given as inputs (own weight a_own, cross weight a_cross, clip
  * factors clip_a and clip_b) the reading is

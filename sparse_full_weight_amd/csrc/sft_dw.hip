@@ -2,10 +2,10 @@
 // cores, and the embedding's masked gradient.
 //
 // Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
-// Active Set", section 2.2: the weight gradient of a projection is the
-// transposed product of the output gradient and the layer input; the mask is
-// checked per tile of 32 output rows, a tile with no active row costs no load,
-// no accumulation and no write, and inside an active tile the inactive rows
+// Active Set", section 2.2: dW of a linear layer is dY^T times the layer's
+// input; the row mask is tested 32 output rows at a time, 32 rows with no
+// active one are skipped before any load, multiply or store, and inside an
+// active tile the inactive rows
 // are dropped before the final write.  For the embedding the input is one-hot,
 // so a row's gradient is the sum of dY over the positions of its token.
 //

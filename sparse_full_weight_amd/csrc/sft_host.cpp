@@ -3,12 +3,12 @@
 // Adam bias-correction table.
 //
 // Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
-// Active Set", section 2.1 (the conductor keeps one charge per row, halves it
-// at the end of every observation window and adds half of the row's share of
-// the window's hits; a row is active while its charge is at least 0.01; the
-// row tracker does the same with output magnitudes; the masks are computed
-// once a step on the CPU) and section 2.2 (the mask is checked per tile of 32
-// rows).  These run on the CPU by design: the page keeps mask decisions on the
+// Active Set", section 2.1 (the conductor holds a charge per row; at each
+// window's end the charge is halved and half of the row's hit count relative
+// to the window's busiest row is added; a row counts as active while its
+// charge is at least 0.01; the row tracker runs the same recurrence on output
+// magnitudes; the CPU derives the masks once per step) and section 2.2 (the
+// mask is tested 32 rows at a time).  These run on the CPU by design: the page keeps mask decisions on the
 // host, one step ahead of the GPU.
 #include <algorithm>
 #include <cmath>

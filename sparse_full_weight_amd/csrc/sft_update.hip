@@ -2,14 +2,14 @@
 // update and the masked write-back, for gfx950.
 //
 // Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
-// Active Set", section 2.3 (each weight is an int8 value q with a per-row
-// scale s and an fp32 residual delta; the update kernel rebuilds the fp32
-// weight in registers only, applies the update and writes back a new q and
-// delta; the fp16 moments exist only for active rows; inactive rows return at
-// once; the same mask drives the write-back of the live weights) and section
-// 2.4 (pairs of matrices blend their clipped gradients; every effective
-// gradient drives a standard Adam step with bias correction; unpaired
-// matrices take the plain step).
+// Active Set", section 2.3 (storage is an int8 code q per weight, a scale s
+// per row and an fp32 residual delta; the fp32 weight exists only in
+// registers while the update steps it, and leaves as a fresh q and delta;
+// fp16 moments are kept for active rows alone; rows outside the mask are not
+// touched; the mask also selects the live rows to rebuild) and section 2.4
+// (paired matrices mix their clipped gradients; each mixed gradient takes a
+// textbook Adam step with bias correction; matrices without a partner take
+// the plain step).
 //
 // Kernel shape: one workgroup per active row, all matrices of a call in one
 // launch.  A row is streamed once: each lane owns 4-column chunks

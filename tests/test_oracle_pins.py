@@ -257,7 +257,7 @@ def test_masked_dw_integer_inputs_exact():
 
 
 def test_masked_dw_single_token_is_outer_product():
-    # One example: the weight gradient is an outer product (SparseLeaf post,
+    # One token: dW is the outer product of dY and X (SparseLeaf post,
     # Appendix B); a bf16 x bf16 product is exact in fp32.
     dY = synth.normal_bf16((1, 50), 0.01, 7)
     X = synth.normal_bf16((1, 8), 1.0, 8)

@@ -2,11 +2,11 @@
 Weight Training at the Cost of the Active Set", section 2.6).
 
 The expected action sequences below were worked out by hand from the rule
-the section states (copy while the loss is within 10% of the last copy's
-loss, 10-step watch after a new minimum, restore on a rise of more than 15%
-at the end of the watch, at most 3 restores per minimum, otherwise accept
-the minimum), under the readings listed in oracle/rewind.py; each case names
-the step that decides it.
+the section states (copy while the loss stays within a 10% margin of the
+last copy's loss, a 10-step watch after each new minimum, restore when the
+watch closes with a loss over 1.15 times the minimum, at most 3 restores per
+minimum, else keep the minimum), under the readings listed in
+oracle/rewind.py; each case names the step that decides it.
 """
 import math
 
@@ -36,7 +36,7 @@ def test_steady_descent_saves_every_step():
 
 
 def test_rise_above_15_percent_at_end_of_watch_restores():
-    # minimum 8 at step 1; steps 2..10 at 8.5 are within 10% of the last copy
+    # minimum 8 at step 1; steps 2..10 at 8.5 stay under 1.1 times the last copy
     # (8.8, then 9.35) and are saved; step 11 is the 10th after the minimum and
     # 9.3 > 1.15 * 8 = 9.2
     acts, c = _run([10.0, 8.0] + [8.5] * 9 + [9.3])
