@@ -7,8 +7,9 @@ library.  Inputs and outputs are numpy arrays; bf16/fp16 tensors travel as
 ``uint16`` bit patterns.
 
 Method source: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of
-the Active Set", sections 2.1-2.4 (each C function names the passage it
-follows).
+the Active Set", sections 2.1-2.4, and the blog post "SparseLeaf: synaptic
+sparse fine-tuning" for the gradients and Adam step of K selected
+connections (each C function names the passage it follows).
 """
 from __future__ import annotations
 
@@ -89,6 +90,10 @@ def _declare(L: C.CDLL) -> None:
     L.oracle_coupled_update.restype = C.c_int
     L.oracle_masked_writeback.argtypes = [p, p, p, i64, i64, p, i64, p]
     L.oracle_masked_writeback.restype = None
+    L.oracle_leaf_grad.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
+    L.oracle_leaf_grad.restype = None
+    L.oracle_leaf_adam.argtypes = [i64, p, p, p, p, p, i32, f32, f32, f32, f32]
+    L.oracle_leaf_adam.restype = None
 
 
 def _ptr(a: np.ndarray | None):
@@ -284,3 +289,29 @@ def masked_writeback(q, s, delta, active_rows, w_live: np.ndarray) -> None:
     R, Cc = q.shape
     lib().oracle_masked_writeback(_ptr(q), _ptr(s), _ptr(delta), R, Cc, _ptr(active_rows),
                                   active_rows.size, _ptr(w_live))
+
+
+def leaf_grad(D_bits: np.ndarray, X_bits: np.ndarray, rows, cols) -> np.ndarray:
+    """SparseLeaf connection gradients: g[k] = sum_t D[t, rows[k]] * X[t, cols[k]]
+    (bf16 inputs as uint16 bits, fp64 sum, one rounding)."""
+    D = _arr(D_bits, np.uint16)
+    X = _arr(X_bits, np.uint16)
+    rows = _arr(rows, np.int32)
+    cols = _arr(cols, np.int32)
+    T, m = D.shape
+    assert X.shape[0] == T and rows.size == cols.size
+    g = np.zeros(rows.size, np.float32)
+    lib().oracle_leaf_grad(_ptr(D), _ptr(X), T, m, X.shape[1], _ptr(rows), _ptr(cols), rows.size, _ptr(g))
+    return g
+
+
+def leaf_adam(g, theta: np.ndarray, m: np.ndarray, v: np.ndarray, theta_bf16, step: int, *, lr, beta1, beta2,
+              eps) -> None:
+    """SparseLeaf Adam step on K coordinates (theta, m, v fp32, updated in place)."""
+    g = _arr(g, np.float32)
+    for a in (theta, m, v):
+        assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"] and a.size == g.size
+    if theta_bf16 is not None:
+        assert theta_bf16.dtype == np.uint16 and theta_bf16.size == g.size
+    lib().oracle_leaf_adam(g.size, _ptr(g), _ptr(theta), _ptr(m), _ptr(v), _ptr(theta_bf16), step, lr, beta1,
+                           beta2, eps)

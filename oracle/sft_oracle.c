@@ -25,6 +25,9 @@
  *   - the weight-gradient sums (a plain dot product over tokens) are taken in
  *     fp64 and rounded to fp32 once.
  *
+ * The element-sparse variant of the SparseLeaf blog post (gradients of K
+ * selected connections and their coordinate Adam step) is stated at the end.
+ *
  * Parity pins: every exported function is checked in tests/test_oracle_pins.py
  * against closed forms, library routines or brute force.  The coupled mixing
  * schedule (the lost equations of section 2.4) is not part of this file: the
@@ -558,6 +561,70 @@ ORACLE_API void oracle_masked_writeback(const int8_t *q, const float *s, const f
             float w = sq + delta[r * C + c];
             w_live[r * C + c] = oracle_f32_to_bf16(w);
         }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* SparseLeaf: gradients and Adam of K selected connections.                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The blog post "SparseLeaf: synaptic sparse fine-tuning" (di-zhang-llm.github
+ * .io), section "Weight gradients: write the selected results directly": for
+ * Y = X W^T and D = dL/dY, each selected connection (i_k, j_k) receives the
+ * dot product over token positions of column i_k of D and column j_k of X,
+ * written into a length-K buffer.  D is bf16 [T x m], X bf16 [T x n]; summed
+ * in fp64 and rounded to fp32 once, like the masked dW above.
+ */
+ORACLE_API void oracle_leaf_grad(const uint16_t *D, const uint16_t *X, int64_t T, int64_t m,
+                                 int64_t n, const int32_t *rows, const int32_t *cols, int64_t K,
+                                 float *g)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        int64_t i = rows[k], j = cols[k];
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            acc += (double)oracle_bf16_to_f32(D[t * m + i]) * (double)oracle_bf16_to_f32(X[t * n + j]);
+        g[k] = (float)acc;
+    }
+}
+
+/*
+ * SparseLeaf Adam (same post, section "The optimizer"): theta, m and v start
+ * at zero; at step t >= 1 the moments of each selected coordinate follow
+ * Adam, are bias-corrected with 1 - beta^t and move theta by
+ * lr * mhat / (sqrt(vhat) + eps), all elementwise.  The post's memory ledger
+ * keeps an fp32 master theta and fp32 moments and computes with a bf16 copy
+ * of theta.  Reading: the same fp32 rounding steps as update_row above (no
+ * weight decay, which the post's step does not have), theta_bf16 = RNE(theta).
+ */
+ORACLE_API void oracle_leaf_adam(int64_t K, const float *g, float *theta, float *m, float *v,
+                                 uint16_t *theta_bf16, int32_t step, float lr, float beta1,
+                                 float beta2, float eps)
+{
+    float bc1 = (float)(1.0 - pow((double)beta1, (double)step));
+    float bc2 = (float)(1.0 - pow((double)beta2, (double)step));
+    float c1 = 1.0f - beta1;
+    float c2 = 1.0f - beta2;
+    for (int64_t k = 0; k < K; ++k) {
+        float gk = g[k];
+        float m_a = beta1 * m[k];
+        float m_b = c1 * gk;
+        float mk = m_a + m_b;
+        float gg = gk * gk;
+        float v_a = beta2 * v[k];
+        float v_b = c2 * gg;
+        float vk = v_a + v_b;
+        float mhat = mk / bc1;
+        float vhat = vk / bc2;
+        float denom = sqrtf(vhat) + eps;
+        float ratio = mhat / denom;
+        float u = lr * ratio;
+        m[k] = mk;
+        v[k] = vk;
+        theta[k] = theta[k] - u;
+        if (theta_bf16)
+            theta_bf16[k] = oracle_f32_to_bf16(theta[k]);
     }
 }
 
