@@ -203,6 +203,18 @@ def cpu_baseline(layer: "Layer", every: int):
     return t_total * scale * 1e3, rows_done, rows_all, t_total
 
 
+LEAF_DENSITY = 0.001
+
+
+def leaf_support(m: int, n: int, seed: int):
+    """SparseLeaf support: round(0.1% of m*n) distinct coordinates, uniform,
+    sorted by (row, column)."""
+    from sparse_full_weight_amd import synth
+    g = synth.rng(seed)
+    flat = np.sort(g.choice(m * n, size=round(LEAF_DENSITY * m * n), replace=False))
+    return (flat // n).astype(np.int32), (flat % n).astype(np.int32)
+
+
 def _time_calls(fns, K, stream):
     """Average ms of one pass over fns (each enqueued on stream), over K back-to-back passes after 5 warm-ups."""
     import torch
@@ -231,7 +243,8 @@ def other_rows(L0: "Layer", K: int, stream):
     """Timings of the hot-path calls the layer step does not run: the embedding
     scatter-gradient and its update, the coupled pair update (with the packed
     masked dW feeding it) on one-active-row-per-tile masks, the standalone
-    masked write-back, and the active-row checkpoint save and restore.  Same event bracketing as the step: K back-to-back
+    masked write-back, the active-row checkpoint save and restore, and the
+    SparseLeaf connection gradients and Adam step.  Same event bracketing as the step: K back-to-back
     passes over prepared calls."""
     import torch
 
@@ -347,6 +360,27 @@ def other_rows(L0: "Layer", K: int, stream):
                                rows=int(sum(n for _, n in dims)))
     out["f2_rows_restore"] = _hbm(accounting.checkpoint_work(dims, restore=True).bytes,
                                   _time_calls([restore], K, stream))
+
+    # ---- SparseLeaf connections: 0.1% of each matrix's entries, uniform random
+    # coordinates (sorted), on the layer's own dY and X
+    leaf, lvecs, dims = [], [], []
+    for mi, (name, m) in enumerate(L0.mats.items()):
+        rows, cols = leaf_support(m["R"], m["C"], 9300 + mi)
+        g = torch.empty(rows.size, dtype=torch.float32, device=dev)
+        X = L0.X[[gn for gn, mm in synth.LLAMA7B_GROUPS if name in mm][0]]
+        leaf.append(_lib.LeafMat(m["dY"], X, torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev), g))
+        z = [torch.zeros(rows.size, dtype=torch.float32, device=dev) for _ in range(3)]
+        lvecs.append(_lib.LeafVec(g, z[0], z[1], z[2], torch.zeros(rows.size, dtype=torch.int16, device=dev)))
+        dims.append((int(np.unique(rows).size), int(np.unique(cols).size), int(rows.size)))
+    lws = torch.zeros(max(_lib.sft_leaf_grad_workspace(leaf) // 4, 1), dtype=torch.int32, device=dev)
+    lgrad = _lib.prepare_leaf_grad(leaf, lws)
+    ladam = _lib.prepare_leaf_adam(lvecs, 1, hp)
+    wl = accounting.leaf_grad_work(L0.T, dims)
+    t_l = _time_calls([lgrad], K, stream)
+    out["f4_leaf_grad"] = dict(_hbm(wl.bytes, t_l), coordinates=int(sum(d[2] for d in dims)), density=LEAF_DENSITY,
+                               useful_TFLOP_s=round(wl.flops_useful / (t_l * 1e-3) / 1e12, 2))
+    out["f4_leaf_adam"] = _hbm(accounting.leaf_adam_work(sum(d[2] for d in dims)).bytes,
+                               _time_calls([ladam], K, stream))
     torch.cuda.synchronize()
     return out
 

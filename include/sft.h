@@ -28,6 +28,12 @@
  *                                                                     sft_rewind_observe,
  *                                                                     sft_rows_save,
  *                                                                     sft_rows_restore
+ *   The element-sparse variant of the blog post "SparseLeaf: synaptic sparse
+ *   fine-tuning" (K selected connections of a frozen weight train their own
+ *   increments): their gradients and their Adam step.
+ *                                                                  -> sft_leaf_grad,
+ *                                                                     sft_leaf_grad_workspace,
+ *                                                                     sft_leaf_adam
  *
  * Conventions shared by every call:
  *   - Status: every entry point returns SFT_OK (0) or a negative SFT_E* code,
@@ -63,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 5
+#define SFT_ABI_VERSION 6
 
 enum {
     SFT_OK = 0,
@@ -478,6 +484,75 @@ int sft_rows_save(const sft_ckpt_mat *mats, int32_t n_mats, void *stream);
  * touched.  Limits and errors: as sft_rows_save.
  */
 int sft_rows_restore(const sft_ckpt_mat *mats, int32_t n_mats, void *stream);
+
+/* ======================================================================= */
+/* device: SparseLeaf connection gradients and Adam                          */
+/* ======================================================================= */
+
+/*
+ * One weight of the SparseLeaf variant (blog post "SparseLeaf: synaptic
+ * sparse fine-tuning", section "Weight gradients: write the selected results
+ * directly"): for Y = X W^T, D = dL/dY and K selected coordinates (i_k, j_k)
+ * of the m x n weight, grad[k] = sum over tokens t of D[t, i_k] * X[t, j_k].
+ *   dY   bf16 [T x m], X bf16 [T x n] (row-major, 16-byte aligned)
+ *   rows [K] i_k in [0, m), cols [K] j_k in [0, n) (device; any order,
+ *        coordinates distinct)
+ *   grad [K] fp32 out
+ * Summed in fp32 over token ranges (any association), the ranges added in a
+ * fixed order: deterministic for a given launch configuration.
+ */
+typedef struct sft_leaf_mat {
+    const uint16_t *dY;
+    const uint16_t *X;
+    int64_t m, n, K;
+    const int32_t *rows;
+    const int32_t *cols;
+    float *grad;
+} sft_leaf_mat;
+
+/* Workspace bytes sft_leaf_grad needs for these matrices and T tokens, or
+ * (size_t)-1 on invalid input (message in sft_last_error). */
+size_t sft_leaf_grad_workspace(const sft_leaf_mat *mats, int32_t n_mats, int64_t T);
+
+/*
+ * The gradients of every matrix's selected connections, all matrices in one
+ * launch (plus one short reduction launch).  T = 0 gives zero gradients.
+ *   ws / ws_bytes  device scratch of at least sft_leaf_grad_workspace()
+ *                  bytes (16-byte aligned; no initialisation needed); calls
+ *                  sharing it must be ordered on one stream.
+ * Limits: m and n multiples of 8, m <= 65536, n <= 65536, m + n <= 65536,
+ * K < 2^31.
+ * Errors: SFT_EINVAL (null pointers, negative sizes), SFT_ESHAPE (m or n not
+ * a multiple of 8), SFT_EALIGN, SFT_ECAPACITY (workspace too small),
+ * SFT_ENOTSUP (beyond the limits), SFT_EHIP.
+ */
+int sft_leaf_grad(const sft_leaf_mat *mats, int32_t n_mats, int64_t T, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/*
+ * SparseLeaf Adam (same post, section "The optimizer") on the K increments of
+ * one or more weights at step `step` (>= 1, the same for every coordinate: the
+ * support is fixed and trains every step); theta, m, v start at zero.
+ *   m = beta1*m + (1-beta1)*g,  v = beta2*v + (1-beta2)*g^2,
+ *   theta -= lr * (m / bc1[step]) / (sqrt(v / bc2[step]) + eps)
+ * in fp32 with every product, sum, quotient and square root rounded on its
+ * own (bc1/bc2 from sft_bias_table); theta_bf16 (optional) receives
+ * RNE-bf16(theta), the copy used for computation.
+ *   grad, theta, m, v [K] fp32; theta_bf16 [K] bf16 or NULL
+ * Errors: SFT_EINVAL (null pointers, step outside [1, t_max], nonzero
+ * weight_decay: this step has none), SFT_EHIP.
+ */
+typedef struct sft_leaf_vec {
+    int64_t K;
+    const float *grad;
+    float *theta;
+    float *m;
+    float *v;
+    uint16_t *theta_bf16;
+} sft_leaf_vec;
+
+int sft_leaf_adam(const sft_leaf_vec *vecs, int32_t n_vecs, int32_t step, const sft_adam *hp,
+                  void *stream);
 
 #ifdef __cplusplus
 }

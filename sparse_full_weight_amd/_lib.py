@@ -32,6 +32,7 @@ EXPORTS = (
     "sft_plan_embedding", "sft_slots_update", "sft_bias_table", "sft_masked_dw_workspace", "sft_masked_dw",
     "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback", "sft_masked_dw_update",
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
+    "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam",
 )
 
 
@@ -95,6 +96,16 @@ class CCkptMat(C.Structure):
                 ("ck_m", C.c_void_p), ("ck_v", C.c_void_p), ("ck_t", C.c_void_p)]
 
 
+class CLeafMat(C.Structure):
+    _fields_ = [("dY", C.c_void_p), ("X", C.c_void_p), ("m", C.c_int64), ("n", C.c_int64), ("K", C.c_int64),
+                ("rows", C.c_void_p), ("cols", C.c_void_p), ("grad", C.c_void_p)]
+
+
+class CLeafVec(C.Structure):
+    _fields_ = [("K", C.c_int64), ("grad", C.c_void_p), ("theta", C.c_void_p), ("m", C.c_void_p),
+                ("v", C.c_void_p), ("theta_bf16", C.c_void_p)]
+
+
 _lib: Optional[C.CDLL] = None
 
 
@@ -129,8 +140,12 @@ def lib() -> C.CDLL:
         L.sft_rewind_observe.argtypes = [C.POINTER(CRewind), C.c_double, C.POINTER(C.c_int32)]
         L.sft_rows_save.argtypes = [C.POINTER(CCkptMat), i32, p]
         L.sft_rows_restore.argtypes = [C.POINTER(CCkptMat), i32, p]
+        L.sft_leaf_grad_workspace.argtypes = [C.POINTER(CLeafMat), i32, i64]
+        L.sft_leaf_grad_workspace.restype = C.c_size_t
+        L.sft_leaf_grad.argtypes = [C.POINTER(CLeafMat), i32, i64, p, C.c_size_t, p]
+        L.sft_leaf_adam.argtypes = [C.POINTER(CLeafVec), i32, i32, C.POINTER(CAdam), p]
         for n in EXPORTS[2:]:
-            if n != "sft_masked_dw_workspace":
+            if n not in ("sft_masked_dw_workspace", "sft_leaf_grad_workspace"):
                 getattr(L, n).restype = C.c_int
         _lib = L
     return _lib
@@ -566,3 +581,79 @@ def prepare_rows_save(mats: Sequence[CkptMat]) -> Prepared:
 def prepare_rows_restore(mats: Sequence[CkptMat]) -> Prepared:
     arr = (CCkptMat * max(len(mats), 1))(*[m.c() for m in mats])
     return Prepared(lib().sft_rows_restore, (arr, len(mats)), (arr, mats))
+
+
+# ------------------------------------------------------------------ SparseLeaf connections
+@dataclass
+class LeafMat:
+    """One weight's K selected connections: dY bf16 [T x m], X bf16 [T x n],
+    rows/cols int32 [K] (GPU), grad fp32 [K] (GPU, written)."""
+    dY: "object"
+    X: "object"
+    rows: "object"
+    cols: "object"
+    grad: "object"
+
+    def c(self) -> CLeafMat:
+        import torch
+        T, m = self.dY.shape
+        n = self.X.shape[1]
+        return CLeafMat(_dev(self.dY, torch.bfloat16), _dev(self.X, torch.bfloat16), m, n, self.rows.numel(),
+                        _dev(self.rows, torch.int32), _dev(self.cols, torch.int32), _dev(self.grad, torch.float32))
+
+
+def _leaf_arr(mats: Sequence[LeafMat]):
+    return (CLeafMat * max(len(mats), 1))(*[m.c() for m in mats])
+
+
+def _leaf_T(mats: Sequence[LeafMat]) -> int:
+    Ts = {m.dY.shape[0] for m in mats} | {m.X.shape[0] for m in mats}
+    if len(Ts) > 1:
+        raise SftError(SFT_EINVAL, f"sft_leaf_grad: matrices with different token counts {sorted(Ts)}")
+    return Ts.pop() if Ts else 0
+
+
+def sft_leaf_grad_workspace(mats: Sequence[LeafMat]) -> int:
+    n = lib().sft_leaf_grad_workspace(_leaf_arr(mats), len(mats), _leaf_T(mats))
+    if n == C.c_size_t(-1).value:
+        raise SftError(SFT_EINVAL, lib().sft_last_error().decode())
+    return n
+
+
+def sft_leaf_grad(mats: Sequence[LeafMat], ws, stream=None) -> None:
+    """SparseLeaf: gradients of the selected connections of every matrix (async)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sft_leaf_grad(_leaf_arr(mats), len(mats), _leaf_T(mats), _dev(ws), nbytes, _stream(stream)))
+
+
+@dataclass
+class LeafVec:
+    """One weight's increments and their Adam state (fp32 [K] each, GPU)."""
+    grad: "object"
+    theta: "object"
+    m: "object"
+    v: "object"
+    theta_bf16: "object" = None
+
+    def c(self) -> CLeafVec:
+        return CLeafVec(self.theta.numel(), _dev(self.grad), _dev(self.theta), _dev(self.m), _dev(self.v),
+                        _dev(self.theta_bf16))
+
+
+def sft_leaf_adam(vecs: Sequence[LeafVec], step: int, hp: Adam, stream=None) -> None:
+    """SparseLeaf Adam step on every vector's increments (async)."""
+    arr = (CLeafVec * max(len(vecs), 1))(*[v.c() for v in vecs])
+    h = hp.c()
+    _check(lib().sft_leaf_adam(arr, len(vecs), int(step), C.byref(h), _stream(stream)))
+
+
+def prepare_leaf_grad(mats: Sequence[LeafMat], ws) -> Prepared:
+    arr = _leaf_arr(mats)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return Prepared(lib().sft_leaf_grad, (arr, len(mats), _leaf_T(mats), _dev(ws), nbytes), (arr, mats, ws))
+
+
+def prepare_leaf_adam(vecs: Sequence[LeafVec], step: int, hp: Adam) -> Prepared:
+    arr = (CLeafVec * max(len(vecs), 1))(*[v.c() for v in vecs])
+    h = hp.c()
+    return Prepared(lib().sft_leaf_adam, (arr, len(vecs), int(step), C.byref(h)), (arr, h, vecs, hp))

@@ -87,6 +87,27 @@ def checkpoint_work(mats: Iterable[Tuple[int, int]], restore: bool = False, live
     return Work(sum(n * C * per + n * CHECKPOINT_BYTES_PER_ROW for C, n in mats))
 
 
+def leaf_grad_work(T: int, mats: Iterable[Tuple[int, int, int]]) -> Work:
+    """SparseLeaf connection gradients. mats: (distinct rows, distinct columns,
+    K) per weight.  Bytes: the bf16 columns of D and X the support touches (T
+    values each), the two int32 indices and the fp32 gradient per coordinate;
+    FLOPs: 2*T per coordinate."""
+    b = f = 0.0
+    for n_rows, n_cols, K in mats:
+        b += T * BF16 * (n_rows + n_cols) + K * (4 + 4 + F32)
+        f += 2.0 * T * K
+    return Work(b, f, f)
+
+
+# SparseLeaf Adam per coordinate: read g, theta, m, v (fp32); write theta, m,
+# v (fp32) and the bf16 copy of theta.
+LEAF_ADAM_BYTES = 4 * F32 + 3 * F32 + BF16
+
+
+def leaf_adam_work(K: int) -> Work:
+    return Work(K * LEAF_ADAM_BYTES)
+
+
 def embedding_dw_work(d: int, nnz: int, n_active: int) -> Work:
     """Reads the bf16 dY row of every hit position, writes fp32 rows."""
     return Work(nnz * d * BF16 + n_active * d * F32 + (nnz + n_active + 1) * 4)

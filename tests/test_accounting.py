@@ -76,3 +76,13 @@ def test_checkpoint_bytes():
     assert acc.checkpoint_work([(16, 3)]).bytes == 3 * 16 * 18 + 3 * 16
     assert acc.checkpoint_work([(16, 3)], restore=True).bytes == 3 * 16 * 20 + 3 * 16
     assert acc.checkpoint_work([(16, 3)], restore=True, live=False).bytes == 3 * 16 * 18 + 3 * 16
+
+
+def test_leaf_bytes():
+    # 10 tokens, a support touching 3 rows and 5 columns with 7 coordinates:
+    # 10 bf16 values per touched row of D and column of X, two int32 indices
+    # and one fp32 gradient per coordinate
+    w = acc.leaf_grad_work(10, [(3, 5, 7)])
+    assert w.bytes == 10 * 2 * (3 + 5) + 7 * 12
+    assert w.flops_useful == 2 * 10 * 7
+    assert acc.leaf_adam_work(7).bytes == 7 * 30

@@ -335,3 +335,39 @@ def test_embedding_32000x4096_conductor_gradient_update(gpu_lib):
     oracle.sparse_update(sub, G[pick], np.arange(pick.size, dtype=np.int32), np.arange(pick.size, dtype=np.int32),
                          np.ones(pick.size, np.uint8), lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
     _assert_rows(st, rows, pick, sub, "embedding")
+
+
+def test_llama7b_layer_leaf_gradients_and_adam(gpu_lib, layer):
+    """SparseLeaf on the whole layer in one call, as the benchmark launches it:
+    0.1% of every matrix's entries as uniform random coordinates, T = 4096;
+    every coordinate's gradient against the oracle, then the Adam step of all
+    seven increment vectors bit for bit."""
+    X, mats = layer
+    leaf, want, vecs = [], [], []
+    for mi, (name, m) in enumerate(mats.items()):
+        R, C = m["R"], m["C"]
+        g = synth.rng(7400 + mi)
+        flat = np.sort(g.choice(R * C, size=round(0.001 * R * C), replace=False))
+        rows, cols = (flat // C).astype(np.int32), (flat % C).astype(np.int32)
+        out = torch.full((rows.size,), float("nan"), dtype=torch.float32, device="cuda")
+        leaf.append(_lib.LeafMat(bf16_dev(m["dY"]), bf16_dev(X[m["group"]]), dev(rows), dev(cols), out))
+        want.append(oracle.leaf_grad(m["dY"], X[m["group"]], rows, cols))
+    ws = torch.zeros(max(_lib.sft_leaf_grad_workspace(leaf) // 4, 1), dtype=torch.int32, device="cuda")
+    _lib.sft_leaf_grad(leaf, ws)
+    torch.cuda.synchronize()
+    for L, w in zip(leaf, want):
+        dw_close(L.grad.cpu().numpy()[None, :], w[None, :])
+    hp = adam_dev(lr=1e-3)
+    host = []
+    for L in leaf:
+        K = L.grad.numel()
+        z = [torch.zeros(K, dtype=torch.float32, device="cuda") for _ in range(3)]
+        vecs.append(_lib.LeafVec(L.grad, z[0], z[1], z[2], torch.zeros(K, dtype=torch.int16, device="cuda")))
+        host.append([np.zeros(K, np.float32) for _ in range(3)] + [np.zeros(K, np.uint16)])
+    _lib.sft_leaf_adam(vecs, 1, hp)
+    torch.cuda.synchronize()
+    for L, v, (th, mm, vv, bf) in zip(leaf, vecs, host):
+        oracle.leaf_adam(L.grad.cpu().numpy(), th, mm, vv, bf, 1, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+        assert np.array_equal(v.theta.cpu().numpy().view(np.uint32), th.view(np.uint32))
+        assert np.array_equal(v.v.cpu().numpy().view(np.uint32), vv.view(np.uint32))
+        assert np.array_equal(host_u16(v.theta_bf16), bf)
