@@ -22,6 +22,10 @@
  *   4. the sparse write-back of the live bf16 weights (section 2.3).
  *                                                                  -> sft_masked_writeback
  *                                                                     (or fused into 3)
+ *   The mixing coefficients of the coupled update come from a host schedule
+ *   (sections 2.4, 2.5):                                         -> sft_helix_init,
+ *                                                                     sft_helix_step,
+ *                                                                     sft_helix_coupling
  *   5. checkpoint and rewind (section 2.6): a host controller decides from
  *      the loss when to save the active rows and when to restore them;
  *                                                                  -> sft_rewind_init,
@@ -69,7 +73,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 6
+#define SFT_ABI_VERSION 7
 
 enum {
     SFT_OK = 0,
@@ -229,6 +233,47 @@ int sft_rewind_init(sft_rewind *st);
  * NaN, watch_steps < 1, max_recoveries < 0); the state is then unchanged.
  */
 int sft_rewind_observe(sft_rewind *st, double loss, int32_t *action);
+
+/*
+ * The coupled update's scalar schedule (sections 2.4, 2.5, 2.6, 2.8), host
+ * side: a loss trend, a Fibonacci stride, the phase it advances, and the
+ * mixing coefficients a_own / a_cross that sft_coupled_update takes.  The
+ * page's equations are lost; the readings implemented are:
+ *   - trend = sum_i r^i dL(t-i) / sum_i r^i over the steps seen, r =
+ *     exp(-1/decay_len), dL(t) = L(t-1) - L(t) (none for the first loss);
+ *     smooth = the same mean over the series of trends;
+ *   - each step the rung (0..7 on 1, 1, 2, 3, 5, 8, 13, 21) goes up by one if
+ *     smooth > up_threshold, down by one if smooth < 0, else stays; a rewind
+ *     sets it to 0 instead; stride = the rung's Fibonacci number;
+ *   - rotation += rung_deg * stride (degrees); phase = fmod(rotation, 360);
+ *   - channel weights w+ = 1 + mod_plus cos(2 pi rotation / 360) and
+ *     w- = 1 + mod_minus cos(2 pi rotation / 3600);
+ *   - exposure e = (1 + cos(phase + psi)) / 2 (psi, the slow phase term, is
+ *     the caller's: the page's elliptic-curve walk is not specified),
+ *     a_own = 1, a_cross = b mu w- (1 - e) / (M w+ e + mu w- (1 - e));
+ *   - double precision throughout.
+ * sft_helix_init sets decay_len 10, up_threshold 1e-4 (loss units), rung_deg
+ * 36, M 1.833, mu 1, mod_plus 0.10, mod_minus 0.05 and an empty state.
+ */
+typedef struct sft_helix {
+    double decay_len, up_threshold, rung_deg, M, mu, mod_plus, mod_minus;
+    /* state */
+    double trend_sum, trend_w, smooth_sum, smooth_w, last_loss, rotation;
+    int32_t has_loss, rung;
+} sft_helix;
+
+/* Errors: SFT_EINVAL (null). */
+int sft_helix_init(sft_helix *h);
+
+/* One step with the loss the caller has (rewind != 0: the step was dropped by
+ * a restore); *stride and *phase_deg (either may be NULL) receive the new
+ * values.  Errors: SFT_EINVAL (null state, non-finite loss, decay_len <= 0). */
+int sft_helix_step(sft_helix *h, double loss, int32_t rewind, int32_t *stride, double *phase_deg);
+
+/* The pair coefficients at the current phase for coupling strength b (0.6
+ * gate-up, 0.4 attention pairs on the page).  Errors: SFT_EINVAL (null
+ * pointers, b or psi not finite, M, mu or a channel weight not positive). */
+int sft_helix_coupling(const sft_helix *h, double b, double psi_deg, double *a_own, double *a_cross);
 
 /* ======================================================================= */
 /* device: the masked backward pass (section 2.2)                           */

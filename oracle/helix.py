@@ -6,14 +6,14 @@ library's schedule calls must return.  The GPU library never imports it, and
 it imports nothing from the GPU library.
 
 Source: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
-Active Set", sections 2.4 (a phase advancing by 36 degrees times a stride
-each step splits the update between a primary and a secondary channel with
-weights in the ratio 1.833 : 1; a slow non-periodic phase term), 2.5 (an
-exponentially weighted mean of loss changes with a decay length of ten steps;
-a smoothed copy of it moves the stride along the Fibonacci ladder 1, 1, 2,
-3, 5, ... capped at 21; slower counters modulate the channel weights by 10%
-and 5%), 2.6 (a rewind restarts the stride at 1) and 2.8 (a pair's blend
-runs from mostly its own gradient to strongly shared over each turn).  The
+Active Set", sections 2.4 (each step a phase moves on by 36 degrees per unit
+of stride and divides the update between a primary and a secondary channel,
+weighted 1.833 to 1, with a slow phase term that never repeats), 2.5 (the
+loss changes are averaged with exponential weights that fall off over ten
+steps; a smoothed copy of that average moves the stride over the Fibonacci
+numbers up to 21; slower counters vary the channel weights by 10% and 5%),
+2.6 (a rewind starts the stride again at 1) and 2.8 (over a turn a pair's
+mix goes from nearly its own gradient to fully coupled).  The
 page's equations are lost; the readings taken here are:
   1. trend C_t = sum_i r^i dL_{t-i} / sum_i r^i over the steps seen so far,
      r = exp(-1/10), dL_t = L_{t-1} - L_t (positive while the loss falls); no

@@ -32,7 +32,8 @@ EXPORTS = (
     "sft_plan_embedding", "sft_slots_update", "sft_bias_table", "sft_masked_dw_workspace", "sft_masked_dw",
     "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback", "sft_masked_dw_update",
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
-    "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam",
+    "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
+    "sft_helix_coupling",
 )
 
 
@@ -96,6 +97,12 @@ class CCkptMat(C.Structure):
                 ("ck_m", C.c_void_p), ("ck_v", C.c_void_p), ("ck_t", C.c_void_p)]
 
 
+class CHelix(C.Structure):
+    _fields_ = [(n, C.c_double) for n in ("decay_len", "up_threshold", "rung_deg", "M", "mu", "mod_plus",
+                                          "mod_minus", "trend_sum", "trend_w", "smooth_sum", "smooth_w",
+                                          "last_loss", "rotation")] + [("has_loss", C.c_int32), ("rung", C.c_int32)]
+
+
 class CLeafMat(C.Structure):
     _fields_ = [("dY", C.c_void_p), ("X", C.c_void_p), ("m", C.c_int64), ("n", C.c_int64), ("K", C.c_int64),
                 ("rows", C.c_void_p), ("cols", C.c_void_p), ("grad", C.c_void_p)]
@@ -144,6 +151,11 @@ def lib() -> C.CDLL:
         L.sft_leaf_grad_workspace.restype = C.c_size_t
         L.sft_leaf_grad.argtypes = [C.POINTER(CLeafMat), i32, i64, p, C.c_size_t, p]
         L.sft_leaf_adam.argtypes = [C.POINTER(CLeafVec), i32, i32, C.POINTER(CAdam), p]
+        L.sft_helix_init.argtypes = [C.POINTER(CHelix)]
+        L.sft_helix_step.argtypes = [C.POINTER(CHelix), C.c_double, i32, C.POINTER(C.c_int32),
+                                     C.POINTER(C.c_double)]
+        L.sft_helix_coupling.argtypes = [C.POINTER(CHelix), C.c_double, C.c_double, C.POINTER(C.c_double),
+                                         C.POINTER(C.c_double)]
         for n in EXPORTS[2:]:
             if n not in ("sft_masked_dw_workspace", "sft_leaf_grad_workspace"):
                 getattr(L, n).restype = C.c_int
@@ -657,3 +669,27 @@ def prepare_leaf_adam(vecs: Sequence[LeafVec], step: int, hp: Adam) -> Prepared:
     arr = (CLeafVec * max(len(vecs), 1))(*[v.c() for v in vecs])
     h = hp.c()
     return Prepared(lib().sft_leaf_adam, (arr, len(vecs), int(step), C.byref(h)), (arr, h, vecs, hp))
+
+
+# ------------------------------------------------------------------ coupled-update schedule
+class Helix:
+    """The coupled update's scalar schedule (host, C library): step(loss,
+    rewind) -> (stride, phase in degrees); coupling(b, psi) -> (a_own, a_cross)."""
+
+    def __init__(self):
+        self.st = CHelix()
+        _check(lib().sft_helix_init(C.byref(self.st)))
+
+    def step(self, loss: float, rewind: bool = False):
+        stride = C.c_int32(0)
+        phase = C.c_double(0.0)
+        _check(lib().sft_helix_step(C.byref(self.st), float(loss), int(bool(rewind)), C.byref(stride),
+                                    C.byref(phase)))
+        return stride.value, phase.value
+
+    def coupling(self, b: float, psi_deg: float = 0.0):
+        a_own = C.c_double(0.0)
+        a_cross = C.c_double(0.0)
+        _check(lib().sft_helix_coupling(C.byref(self.st), float(b), float(psi_deg), C.byref(a_own),
+                                        C.byref(a_cross)))
+        return a_own.value, a_cross.value

@@ -268,4 +268,68 @@ int sft_rewind_observe(sft_rewind *st, double loss, int32_t *action) {
     return SFT_OK;
 }
 
+// The coupled update's scalar schedule; the readings it implements are
+// stated with the declaration.  Double precision throughout.
+namespace {
+constexpr int32_t kFib[8] = {1, 1, 2, 3, 5, 8, 13, 21};
+}
+
+int sft_helix_init(sft_helix *h) {
+    clear_error();
+    SFT_CHECK(h, SFT_EINVAL, "helix_init: null state");
+    std::memset(h, 0, sizeof(*h));
+    h->decay_len = 10.0;
+    h->up_threshold = 1e-4;
+    h->rung_deg = 36.0;
+    h->M = 1.833;
+    h->mu = 1.0;
+    h->mod_plus = 0.10;
+    h->mod_minus = 0.05;
+    return SFT_OK;
+}
+
+int sft_helix_step(sft_helix *h, double loss, int32_t rewind, int32_t *stride, double *phase_deg) {
+    clear_error();
+    SFT_CHECK(h && std::isfinite(loss), SFT_EINVAL, "helix_step: null state or non-finite loss");
+    SFT_CHECK(h->decay_len > 0.0 && h->rung >= 0 && h->rung < 8, SFT_EINVAL, "helix_step: bad settings or rung");
+    const double r = std::exp(-1.0 / h->decay_len);
+    if (h->has_loss) {
+        const double d = h->last_loss - loss;
+        h->trend_sum = d + r * h->trend_sum;
+        h->trend_w = 1.0 + r * h->trend_w;
+        const double trend = h->trend_sum / h->trend_w;
+        h->smooth_sum = trend + r * h->smooth_sum;
+        h->smooth_w = 1.0 + r * h->smooth_w;
+    }
+    h->last_loss = loss;
+    h->has_loss = 1;
+    const double smooth = h->smooth_w > 0.0 ? h->smooth_sum / h->smooth_w : 0.0;
+    if (rewind)
+        h->rung = 0;
+    else if (smooth > h->up_threshold)
+        h->rung = std::min(h->rung + 1, 7);
+    else if (smooth < 0.0)
+        h->rung = std::max(h->rung - 1, 0);
+    h->rotation += h->rung_deg * kFib[h->rung];
+    if (stride) *stride = kFib[h->rung];
+    if (phase_deg) *phase_deg = std::fmod(h->rotation, 360.0);
+    return SFT_OK;
+}
+
+int sft_helix_coupling(const sft_helix *h, double b, double psi_deg, double *a_own, double *a_cross) {
+    clear_error();
+    SFT_CHECK(h && a_own && a_cross && std::isfinite(b) && std::isfinite(psi_deg), SFT_EINVAL,
+              "helix_coupling: null pointer or non-finite b / psi");
+    const double R = h->rotation;
+    const double wp = 1.0 + h->mod_plus * std::cos(2.0 * M_PI * R / 360.0);
+    const double wm = 1.0 + h->mod_minus * std::cos(2.0 * M_PI * R / 3600.0);
+    SFT_CHECK(h->M > 0.0 && h->mu > 0.0 && wp > 0.0 && wm > 0.0, SFT_EINVAL,
+              "helix_coupling: channel weights must be positive");
+    const double e = (1.0 + std::cos((std::fmod(R, 360.0) + psi_deg) * (M_PI / 180.0))) / 2.0;
+    const double sec = h->mu * wm * (1.0 - e);
+    *a_own = 1.0;
+    *a_cross = b * sec / (h->M * wp * e + sec);
+    return SFT_OK;
+}
+
 }  // extern "C"

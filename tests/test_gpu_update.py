@@ -207,3 +207,41 @@ def test_update_rejects_bad_arguments(gpu_lib):
     with pytest.raises(_lib.SftError) as e:
         _lib.sft_sparse_update([m.upd()], adam_dev(**HP))
     assert e.value.code == _lib.SFT_ESHAPE
+
+
+def test_coupled_update_driven_by_the_schedule(gpu_lib):
+    """Six steps of a gate-up-like pair (b = 0.6) whose a_own / a_cross come
+    from the library's schedule at each step (falling loss, so the stride
+    climbs and the phase sweeps part of a turn): the GPU state equals the
+    oracle's after every step, both fed the schedule's coefficients rounded
+    to fp32 and the same gradients."""
+    import oracle.helix as hx
+    R, C = 160, 264
+    g = synth.rng(1500)
+    A = make_state(R, C, 1510, 40, True)
+    B = make_state(R, C, 1520, 40, True)
+    ra = np.sort(g.choice(R, 30, replace=False)).astype(np.int32)
+    rb = np.sort(np.unique(np.concatenate([ra[:12], g.choice(R, 18, replace=False)]))).astype(np.int32)
+    sa = g.choice(40, ra.size, replace=False).astype(np.int32)
+    sb = g.choice(40, rb.size, replace=False).astype(np.int32)
+    wa, wb = A.copy(), B.copy()
+    ma = GpuMat(A, np.zeros((ra.size, C), np.float32), ra, sa, None)
+    mb = GpuMat(B, np.zeros((rb.size, C), np.float32), rb, sb, None)
+    sched, ref = _lib.Helix(), hx.Helix()
+    hp = adam_dev(**HP)
+    for step in range(6):
+        loss = 5.0 - 0.2 * step
+        sched.step(loss)
+        ref.step(loss)
+        a_own, a_cross = sched.coupling(0.6)
+        assert (a_own, a_cross) == ref.coupling(0.6)
+        GA = synth.gradient_rows(ra.size, C, 0.2, 1530 + step)
+        GB = synth.gradient_rows(rb.size, C, 0.2, 1540 + step)
+        ma.G.copy_(torch.from_numpy(GA))
+        mb.G.copy_(torch.from_numpy(GB))
+        _lib.sft_coupled_update([_lib.Pair(ma.upd(), mb.upd(), a_own, a_cross, None)], hp)
+        torch.cuda.synchronize()
+        oracle.coupled_update(wa, GA, ra, sa, None, wb, GB, rb, sb, None, a_own=float(np.float32(a_own)),
+                              a_cross=float(np.float32(a_cross)), clip_a=1.0, clip_b=1.0, weight_decay=0.0, **HP)
+        assert_state_equal(ma.to_state(), wa, f"step {step} A")
+        assert_state_equal(mb.to_state(), wb, f"step {step} B")
