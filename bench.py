@@ -58,6 +58,8 @@ def parse_args():
     ap.add_argument("--rows-only", action="store_true",
                     help="time only the other hot-path calls (prints their JSON object), for profiling them apart "
                          "from the layer step")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the probes of the HBM and matrix-core rates this device sustains")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -385,6 +387,32 @@ def other_rows(L0: "Layer", K: int, stream):
     return out
 
 
+def ceilings(stream):
+    """What this device sustains beside the published peaks: an HBM read stream
+    and copy over 2 GiB buffers (16-byte non-temporal accesses, 8 workgroups per
+    CU) and back-to-back bf16 MFMA on register operands."""
+    import torch
+
+    from sparse_full_weight_amd import _lib
+    n = 1 << 31
+    a = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    sink = torch.empty(_lib.sft_probe_grid() * 256, dtype=torch.int32, device="cuda")
+    t_read = _time_calls([_lib.prepare_probe_read(a, sink)], 20, stream)
+    t_copy = _time_calls([_lib.prepare_probe_copy(a, b)], 20, stream)
+    del a, b
+    iters = 4096
+    out = torch.empty(_lib.sft_probe_grid() * 256, dtype=torch.float32, device="cuda")
+    t_mfma = _time_calls([_lib.prepare_probe_mfma(iters, out)], 10, stream)
+    flops = _lib.sft_probe_grid() * 4 * 4 * iters * 32768
+    return {"hbm_read_GB_s": round(n / (t_read * 1e-3) / 1e9, 1),
+            "hbm_copy_GB_s": round(2 * n / (t_copy * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOP_s": round(flops / (t_mfma * 1e-3) / 1e12, 1),
+            "peaks": {"hbm_GB_s": HBM_PEAK_GBS, "mfma_bf16_TFLOP_s": MFMA_BF16_PEAK_TFLOPS},
+            "note": "read and copy over 2 GiB buffers (copy counts read + write bytes); MFMA 32x32x16 bf16 "
+                    "back to back, 8 workgroups per CU"}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -499,6 +527,11 @@ def main():
         print("[bench] timing the other hot-path calls", file=sys.stderr, flush=True)
         rows = other_rows(L0, min(K, 100), stream)
 
+    ceil = None
+    if not args.no_ceilings:
+        print("[bench] probing the sustained HBM and matrix-core rates", file=sys.stderr, flush=True)
+        ceil = ceilings(stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
@@ -547,6 +580,7 @@ def main():
                                      "algorithmic_bytes": dw.bytes + up.bytes},
         },
         "rows": rows,
+        "ceilings": ceil,
         "host_plan_us_per_layer": round(host_plan_us, 1),
     }
     print(json.dumps(out), flush=True)

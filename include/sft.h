@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 7
+#define SFT_ABI_VERSION 8
 
 enum {
     SFT_OK = 0,
@@ -598,6 +598,30 @@ typedef struct sft_leaf_vec {
 
 int sft_leaf_adam(const sft_leaf_vec *vecs, int32_t n_vecs, int32_t step, const sft_adam *hp,
                   void *stream);
+
+/* ======================================================================= */
+/* measurement probes                                                        */
+/* ======================================================================= */
+
+/*
+ * What this device sustains, measured beside the published peaks that the
+ * kernels' roofline fractions use.  Each launches sft_probe_grid()
+ * workgroups of 256 lanes (8 per CU) and returns without synchronising.
+ *   sft_probe_read: streams `bytes` (a multiple of 16, 16-byte aligned) with
+ *     16-byte non-temporal loads and writes one XOR per lane to sink
+ *     [sft_probe_grid() * 256] (the XOR of sink equals the XOR of the buffer's
+ *     32-bit words);
+ *   sft_probe_copy: copies `bytes` from src to dst the same way;
+ *   sft_probe_mfma: each wave issues 4 * iters v_mfma_f32_32x32x16_bf16 on
+ *     register operands (every input 1/16) and writes each lane's sum to out
+ *     [sft_probe_grid() * 256], which equals 4 * iters (iters < 2^22 keeps it
+ *     exact); work = sft_probe_grid() * 4 waves * 4 * iters * 32768 FLOP.
+ * Errors: SFT_EINVAL (null or unaligned pointers, bad sizes), SFT_EHIP.
+ */
+int sft_probe_grid(void);
+int sft_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+int sft_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+int sft_probe_mfma(int64_t iters, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ EXPORTS = (
     "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback", "sft_masked_dw_update",
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
     "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
-    "sft_helix_coupling",
+    "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma",
 )
 
 
@@ -151,6 +151,10 @@ def lib() -> C.CDLL:
         L.sft_leaf_grad_workspace.restype = C.c_size_t
         L.sft_leaf_grad.argtypes = [C.POINTER(CLeafMat), i32, i64, p, C.c_size_t, p]
         L.sft_leaf_adam.argtypes = [C.POINTER(CLeafVec), i32, i32, C.POINTER(CAdam), p]
+        L.sft_probe_grid.argtypes = []
+        L.sft_probe_read.argtypes = [p, C.c_size_t, p, p]
+        L.sft_probe_copy.argtypes = [p, p, C.c_size_t, p]
+        L.sft_probe_mfma.argtypes = [i64, p, p]
         L.sft_helix_init.argtypes = [C.POINTER(CHelix)]
         L.sft_helix_step.argtypes = [C.POINTER(CHelix), C.c_double, i32, C.POINTER(C.c_int32),
                                      C.POINTER(C.c_double)]
@@ -693,3 +697,22 @@ class Helix:
         _check(lib().sft_helix_coupling(C.byref(self.st), float(b), float(psi_deg), C.byref(a_own),
                                         C.byref(a_cross)))
         return a_own.value, a_cross.value
+
+
+# ------------------------------------------------------------------ measurement probes
+def sft_probe_grid() -> int:
+    return lib().sft_probe_grid()
+
+
+def prepare_probe_read(buf, sink) -> Prepared:
+    nbytes = buf.numel() * buf.element_size()
+    return Prepared(lib().sft_probe_read, (_dev(buf), nbytes, _dev(sink)), (buf, sink))
+
+
+def prepare_probe_copy(src, dst) -> Prepared:
+    nbytes = src.numel() * src.element_size()
+    return Prepared(lib().sft_probe_copy, (_dev(src), _dev(dst), nbytes), (src, dst))
+
+
+def prepare_probe_mfma(iters: int, out) -> Prepared:
+    return Prepared(lib().sft_probe_mfma, (int(iters), _dev(out)), (out,))
