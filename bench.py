@@ -245,8 +245,9 @@ def other_rows(L0: "Layer", K: int, stream):
     """Timings of the hot-path calls the layer step does not run: the embedding
     scatter-gradient and its update, the coupled pair update (with the packed
     masked dW feeding it) on one-active-row-per-tile masks, the standalone
-    masked write-back, the active-row checkpoint save and restore, and the
-    SparseLeaf connection gradients and Adam step.  Same event bracketing as the step: K back-to-back
+    masked write-back, the active-row checkpoint save and restore, the
+    SparseLeaf connection gradients and Adam step, and the layer step at the
+    full step's other row densities (0.5%, 2%, 5%).  Same event bracketing as the step: K back-to-back
     passes over prepared calls."""
     import torch
 
@@ -383,6 +384,34 @@ def other_rows(L0: "Layer", K: int, stream):
                                useful_TFLOP_s=round(wl.flops_useful / (t_l * 1e-3) / 1e12, 2))
     out["f4_leaf_adam"] = _hbm(accounting.leaf_adam_work(sum(d[2] for d in dims)).bytes,
                                _time_calls([ladam], K, stream))
+    del leaf, lvecs, lws
+
+    # ---- the full step's other row densities: the same layer step (plan upload
+    # + fused masked dW and update) over a ring of 3 layers at each density
+    sweep = {}
+    for density in (0.005, 0.02, 0.05):
+        ring = [Layer(100 + i, L0.T, density, 6000, "packed") for i in range(3)]
+
+        def step(L):
+            L.upload_plan()
+            L.fused_call(stream)
+        for i in range(5):
+            step(ring[i % 3])
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            step(ring[i % 3])
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / K
+        work = ring[0].dw_work().bytes + ring[0].upd_work().bytes
+        sweep[f"{density:g}"] = dict(_hbm(work, ms), active_rows=int(sum(m["plan"].n_active
+                                                                        for m in ring[0].mats.values())))
+        del ring
+        torch.cuda.empty_cache()
+    out["c_density_sweep_step"] = sweep
     torch.cuda.synchronize()
     return out
 

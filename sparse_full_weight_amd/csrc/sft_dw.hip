@@ -97,6 +97,7 @@ struct DwGroupDev {
     int32_t mat_begin, n_mats;
     int32_t n_rows, n_ptiles, n_mblk, n_nblk, chunks;
     int32_t ptile_begin;    // first packed tile in the launch's numbering
+    int32_t nb_major;       // output tiles numbered column block by column block (3+ M-blocks)
     int64_t it_begin;       // first global iteration of this group
     int64_t otile_begin;    // first output tile (launch numbering)
 };
@@ -133,6 +134,18 @@ __device__ __forceinline__ int64_t floordiv53(int64_t n, int64_t d) {
 // kMaxTiles (b * n_ptiles < 2^48).
 __device__ __forceinline__ int32_t mblk_lo(const DwGroupDev &G, int32_t b) {
     return static_cast<int32_t>(floordiv53(static_cast<int64_t>(b) * G.n_ptiles, G.n_mblk));
+}
+
+// M-block and column block of output tile t of a group.  A group of three or
+// more M-blocks numbers its tiles column block by column block, so that all
+// M-blocks of one column block take neighbouring slices (one XCD, at about
+// the same time) and read its X from that XCD's L2 after the first; other
+// groups number them M-block by M-block.
+// Returns (M-block, column block).
+__device__ __forceinline__ int2 tile_pos(const DwGroupDev &G, int32_t t) {
+    const int32_t q = t / (G.nb_major ? G.n_mblk : G.n_nblk);
+    const int32_t r = t - q * (G.nb_major ? G.n_mblk : G.n_nblk);
+    return G.nb_major ? make_int2(r, q) : make_int2(q, r);
 }
 
 // ---------------------------------------------------------------- gather
@@ -255,11 +268,15 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 
 // 16 bytes per lane from a raw buffer [base, base + size) at byte offset
 // voff into LDS at lds + 16*lane; offsets at or beyond size read as zero.
-__device__ __forceinline__ void dma16_buf(const uint8_t *base, int32_t size, uint32_t voff, void *lds) {
+// keep: an ordinary cached load (X that other M-blocks read again soon);
+// otherwise non-temporal (X read once).
+__device__ __forceinline__ void dma16_buf(const uint8_t *base, int32_t size, uint32_t voff, void *lds, bool keep) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), static_cast<short>(0), size, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)(lds), 16, voff, 0, 0, 2);
+    if (keep)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(lds), 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(lds), 16, voff, 0, 0, 2);
 }
 
 __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
@@ -323,10 +340,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             const int32_t k0 = rel - tile * G.chunks;
             const int32_t tile_end = static_cast<int32_t>(G.it_begin) + (tile + 1) * G.chunks;
             const int32_t end = min(tile_end, hi);
-            const int32_t mb = tile / G.n_nblk;
+            const int2 pos = tile_pos(G, tile);
+            const int32_t mb = pos.x;
             Seg sg;
             sg.g = gi;
-            sg.nb = tile - mb * G.n_nblk;
+            sg.nb = pos.y;
             sg.p0 = mblk_lo(G, mb);
             sg.mt = mblk_lo(G, mb + 1) - sg.p0;
             sg.k0 = k0;
@@ -358,6 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const uint8_t *x_base = nullptr;
     int64_t x_rem = 0, x_stride = 0;
     int32_t x_j0 = 0;
+    bool x_keep = false;
     uint32_t x_voff[kCopiesX];
     auto describe_x = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
@@ -367,6 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         x_rem = static_cast<int64_t>(uniform64(static_cast<uint64_t>((G.T - r0) * C * 2 - c0 * 2)));
         x_stride = static_cast<int64_t>(uniform64(static_cast<uint64_t>(kBK * C * 2)));
         x_j0 = __builtin_amdgcn_readfirstlane(S.j0);
+        x_keep = __builtin_amdgcn_readfirstlane(G.nb_major) != 0;
 #pragma unroll
         for (int k = 0; k < kCopiesX; ++k) {
             const int row_in = 2 * (wave + 8 * k) + (lane >> 5);
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         const int64_t off = static_cast<int64_t>(jx - x_j0) * x_stride;
         const int64_t rem = jx < J ? x_rem - off : 0;
         const int32_t size = static_cast<int32_t>(rem <= 0 ? 0 : (rem > 0x7fffffff ? 0x7fffffff : rem));
-        dma16_buf(x_base + (jx < J ? off : 0), size, x_voff[k], stage + (wave + 8 * k) * 1024);
+        dma16_buf(x_base + (jx < J ? off : 0), size, x_voff[k], stage + (wave + 8 * k) * 1024, x_keep);
     };
 
     // ---- wave layout: wave w takes packed tile w/2 of the M-block and the
@@ -618,7 +638,8 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     const int32_t tile = static_cast<int32_t>(ot - G.otile_begin);
     const int64_t A = G.it_begin + static_cast<int64_t>(tile) * G.chunks;   // first iteration
     const int64_t a = A / kRound, b = a + G.chunks / kRound;                  // its rounds [a, b)
-    const int32_t mb = tile / G.n_nblk, nb = tile % G.n_nblk;
+    const int2 pos = tile_pos(G, tile);
+    const int32_t mb = pos.x, nb = pos.y;
     // Slices covering rounds [a, b): slice v starts at or before round r
     // exactly when floor(v * Q / P) < r + 1, i.e. when v <= ((r + 1) * P - 1) / Q.
     const int64_t Q = p.iters / kRound, P = p.n_wg;
@@ -872,6 +893,7 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             d.n_ptiles = static_cast<int32_t>((rows + 31) / 32);
             d.n_mblk = (d.n_ptiles + kMaxTiles - 1) / kMaxTiles;
             d.n_nblk = static_cast<int32_t>((g.C + kBN - 1) / kBN);
+            d.nb_major = d.n_mblk >= 3 ? 1 : 0;
             d.chunks = static_cast<int32_t>(((g.T + kRound * kBK - 1) / (kRound * kBK)) * kRound);
             d.Tp = d.chunks * kBK;
             d.ptile_begin = ptiles;
@@ -1007,6 +1029,7 @@ int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, s
             r.rnd = kRound;
             r.chunks = G.chunks;
             r.n_nblk = G.n_nblk;
+            r.nb_major = G.nb_major;
             r.n_ptiles = G.n_ptiles;
             r.n_mblk = G.n_mblk;
             r.row_begin = M.row_begin;

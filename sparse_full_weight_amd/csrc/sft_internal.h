@@ -37,6 +37,7 @@ struct DwRowSrc {
     int32_t chunks, n_nblk, n_ptiles, n_mblk;
     int32_t row_begin;        // first packed row of the matrix in its group
     int32_t layout;           // SFT_DW_TILES or SFT_DW_PACKED
+    int32_t nb_major;         // output tiles numbered column block by column block
 };
 
 // Gather and product of sft_masked_dw without the fix-up, partial tiles

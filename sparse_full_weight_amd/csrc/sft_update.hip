@@ -626,7 +626,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_update(const FusedParams p) 
         // slices over each output tile (M-block mb, column block nb): slice v
         // starts at round floor(v * Q / P)
         for (int nb = lt; nb < S.n_nblk; nb += kLanes) {
-            const int64_t a = (S.it_begin + (mb * S.n_nblk + nb) * static_cast<int64_t>(S.chunks)) / S.rnd;
+            const int64_t tile = S.nb_major ? nb * static_cast<int64_t>(S.n_mblk) + mb : mb * S.n_nblk + nb;
+            const int64_t a = (S.it_begin + tile * static_cast<int64_t>(S.chunks)) / S.rnd;
             const int64_t b = a + S.chunks / S.rnd;
             const int64_t v0 = floordiv53((a + 1) * S.P - 1, S.Q);
             const int64_t v1 = floordiv53(b * S.P - 1, S.Q);

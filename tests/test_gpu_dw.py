@@ -266,3 +266,22 @@ def test_embedding_dw_hot_rows(gpu_lib):
     got = out.cpu().numpy()
     assert np.all(np.isnan(got[plan.n_active:]))
     assert np.array_equal(got[:plan.n_active], oracle.embedding_dw(dY, tokens, plan.active_rows))
+
+
+@LAYOUTS
+def test_dw_many_mblocks_column_major_tiles(gpu_lib, layout):
+    # groups of three and more M-blocks number their output tiles column block
+    # by column block and keep X in L2: 450 active rows of two matrices on one
+    # input (15 packed tiles, 4 M-blocks; tile layout more), ragged C and T,
+    # beside a 2-M-block group, repeated for determinism; and an integer case
+    # that must be exact
+    T, C = 200, 520
+    X1 = synth.normal_bf16((T, C), 1.0, 1900)
+    mats1 = [(synth.normal_bf16((T, R), 0.01, 1901 + i), _mask_rows(R, synth.clustered_rows(R, k, 1910 + i)))
+             for i, (R, k) in enumerate([(700, 300), (400, 150)])]
+    X2 = synth.normal_bf16((T, 136), 1.0, 1920)
+    mats2 = [(synth.normal_bf16((T, 300), 0.01, 1921), _mask_rows(300, synth.clustered_rows(300, 170, 1922)))]
+    _check([(X1, mats1), (X2, mats2)], repeat=2, layout=layout)
+    Xi = synth.integer_bf16((T, C), -3, 3, 1930)
+    matsi = [(synth.integer_bf16((T, 900), -2, 2, 1931), _mask_rows(900, synth.clustered_rows(900, 420, 1932)))]
+    _check([(Xi, matsi)], exact=True, layout=layout)

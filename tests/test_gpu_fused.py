@@ -144,3 +144,10 @@ def test_fused_rejects_mismatched_gradient(gpu_lib):
     with pytest.raises(_lib.SftError) as e:
         _lib.sft_masked_dw_update(groups, ws, [m.upd()], adam_dev(**HP))
     assert e.value.code == _lib.SFT_EINVAL
+
+
+@LAYOUTS
+def test_fused_many_mblocks(gpu_lib, layout):
+    # 4 and more M-blocks (output tiles numbered column block by column block)
+    case = _case([(256, 520, [(700, 300), (400, 150)]), (256, 136, [(300, 170)])], 2700)
+    _check_equal(case, layout)
