@@ -62,6 +62,7 @@ constexpr int kMaxGroups = 8;
 constexpr int kMaxMats = 16;
 constexpr int kMaxSegs = 16;         // output tiles touched by one slice
 constexpr int kXcds = 8;
+constexpr int kTeamMblk = 3;         // team slicing when a group has this many M-blocks (2 measured slower)
 constexpr int64_t kSlotFloats = int64_t(kMaxTiles) * 32 * kBN;   // one partial output tile
 constexpr int kGatherTokens = 256;
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset beyond every resource size
@@ -98,6 +99,9 @@ struct DwGroupDev {
     int32_t n_rows, n_ptiles, n_mblk, n_nblk, chunks;
     int32_t ptile_begin;    // first packed tile in the launch's numbering
     int32_t nb_major;       // output tiles numbered column block by column block (3+ M-blocks)
+    int32_t keep_x;         // X copies allocate in L2 (other M-blocks read the same X soon)
+    int32_t wg_begin;       // team slicing: first slice of the group's teams
+    int32_t n_team;         // team slicing: teams of n_mblk slices each
     int64_t it_begin;       // first global iteration of this group
     int64_t otile_begin;    // first output tile (launch numbering)
 };
@@ -108,6 +112,7 @@ struct DwParams {
     int32_t n_groups;
     int32_t n_wg;           // slices (= workgroups of the product)
     int32_t xcd_blocked;    // neighbouring slices on one XCD (else slice = workgroup index)
+    int32_t teams;          // team slicing (per group) instead of slices of the iteration space
     int64_t iters;          // total (output tile, chunk) iterations, a multiple of kRound
     float *part;            // [2 * n_wg] partial tiles of kSlotFloats
     int32_t part_rows;      // partial tiles row-major (1) or in MFMA fragment order (0)
@@ -137,10 +142,12 @@ __device__ __forceinline__ int32_t mblk_lo(const DwGroupDev &G, int32_t b) {
 }
 
 // M-block and column block of output tile t of a group.  A group of three or
-// more M-blocks numbers its tiles column block by column block, so that all
-// M-blocks of one column block take neighbouring slices (one XCD, at about
-// the same time) and read its X from that XCD's L2 after the first; other
-// groups number them M-block by M-block.
+// more M-blocks numbers its tiles column block by column block (under
+// stream-K slicing, which such groups fall back to when their teams do not
+// fit the CUs, all M-blocks of one column block then take neighbouring
+// slices: one XCD, at about the same time, X from L2 after the first); other
+// groups number them M-block by M-block.  The fix-up's grid follows the
+// same numbering.
 // Returns (M-block, column block).
 __device__ __forceinline__ int2 tile_pos(const DwGroupDev &G, int32_t t) {
     const int32_t q = t / (G.nb_major ? G.n_mblk : G.n_nblk);
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int64_t v = slice_of(p);
-    const int64_t it_lo = slice_lo(p, v), it_hi = slice_lo(p, v + 1);
+    const int64_t it_lo = p.teams ? 0 : slice_lo(p, v), it_hi = p.teams ? 1 : slice_lo(p, v + 1);
     if (it_lo >= it_hi) return;
 
     // ---- the group table, for run-time indexing (one wave per entry, constant
@@ -326,7 +333,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // touches) from the kernel argument: wave-uniform control flow, so the
     // table reads are scalar loads.  32-bit arithmetic (the host keeps the
     // iteration count below 2^31).
-    if (wave == 0) {
+    if (wave == 0 && p.teams) {
+        // Team slicing: the slices of group g form n_team teams of n_mblk;
+        // member mb of team t takes M-block mb over the team's share
+        // [floor(t*Q/n_team), floor((t+1)*Q/n_team)) of the group's Q =
+        // n_nblk * R column-block rounds, column block by column block, so
+        // the members read the same X at about the same time.
+        int gi = 0;
+        while (gi + 1 < p.n_groups && v >= p.g[gi + 1].wg_begin) ++gi;
+        const DwGroupDev &G = p.g[gi];
+        const int32_t w = static_cast<int32_t>(v) - G.wg_begin;
+        int n = 0;
+        if (w < G.n_team * G.n_mblk) {
+            const int32_t t = w / G.n_mblk, mb = w - t * G.n_mblk;
+            const int32_t R = G.chunks / kRound;
+            const int64_t Q = static_cast<int64_t>(G.n_nblk) * R;
+            int32_t u = static_cast<int32_t>(floordiv53(t * Q, G.n_team));
+            const int32_t hi = static_cast<int32_t>(floordiv53((t + 1) * Q, G.n_team));
+            const int32_t p0 = mblk_lo(G, mb), mt = mblk_lo(G, mb + 1) - p0;
+            int32_t j = 0;
+            while (u < hi && n < kMaxSegs) {
+                const int32_t nb = u / R, r0 = u - nb * R;
+                const int32_t end = min((nb + 1) * R, hi);
+                Seg sg;
+                sg.g = gi;
+                sg.nb = nb;
+                sg.p0 = p0;
+                sg.mt = mt;
+                sg.k0 = r0 * kRound;
+                sg.j0 = j;
+                sg.len = (end - u) * kRound;
+                const bool whole = (r0 == 0 && end == (nb + 1) * R);
+                sg.slot = whole ? -1 : (n == 0 ? static_cast<int32_t>(2 * v) : static_cast<int32_t>(2 * v + 1));
+                if (lane == 0) segs[n] = sg;
+                ++n;
+                j += sg.len;
+                u = end;
+            }
+        }
+        if (lane == 0) s_nseg = n;
+    } else if (wave == 0) {
         int32_t it = static_cast<int32_t>(it_lo);
         const int32_t hi = static_cast<int32_t>(it_hi);
         int n = 0;
@@ -361,6 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     }
     __syncthreads();
     const int nseg = s_nseg;
+    if (nseg == 0) return;   // an idle slice (team slicing pads the grid to whole XCDs)
     const int32_t J = segs[nseg - 1].j0 + segs[nseg - 1].len;
     float *const sink = p.sink + (v * 8 + wave) * 16;
 
@@ -386,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         x_rem = static_cast<int64_t>(uniform64(static_cast<uint64_t>((G.T - r0) * C * 2 - c0 * 2)));
         x_stride = static_cast<int64_t>(uniform64(static_cast<uint64_t>(kBK * C * 2)));
         x_j0 = __builtin_amdgcn_readfirstlane(S.j0);
-        x_keep = __builtin_amdgcn_readfirstlane(G.nb_major) != 0;
+        x_keep = __builtin_amdgcn_readfirstlane(G.keep_x) != 0;
 #pragma unroll
         for (int k = 0; k < kCopiesX; ++k) {
             const int row_in = 2 * (wave + 8 * k) + (lane >> 5);
@@ -636,16 +683,32 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     while (gi + 1 < p.n_groups && ot >= p.g[gi + 1].otile_begin) ++gi;
     const DwGroupDev &G = p.g[gi];
     const int32_t tile = static_cast<int32_t>(ot - G.otile_begin);
-    const int64_t A = G.it_begin + static_cast<int64_t>(tile) * G.chunks;   // first iteration
-    const int64_t a = A / kRound, b = a + G.chunks / kRound;                  // its rounds [a, b)
     const int2 pos = tile_pos(G, tile);
     const int32_t mb = pos.x, nb = pos.y;
-    // Slices covering rounds [a, b): slice v starts at or before round r
-    // exactly when floor(v * Q / P) < r + 1, i.e. when v <= ((r + 1) * P - 1) / Q.
-    const int64_t Q = p.iters / kRound, P = p.n_wg;
+    // The tile is rounds [a, b) of a space of Q rounds cut into P equal
+    // ranges: the launch's iterations and its slices, or (team slicing) the
+    // group's column-block rounds and its teams, range i being slice
+    // base + i * stride.  Range i starts at or before round r exactly when
+    // floor(i * Q / P) < r + 1, i.e. when i <= ((r + 1) * P - 1) / Q.
+    int64_t a, b, Q, P;
+    int32_t base = 0, stride = 1;
+    if (p.teams) {
+        const int32_t R = G.chunks / kRound;
+        a = static_cast<int64_t>(nb) * R;
+        b = a + R;
+        Q = static_cast<int64_t>(G.n_nblk) * R;
+        P = G.n_team;
+        base = G.wg_begin + mb;
+        stride = G.n_mblk;
+    } else {
+        a = (G.it_begin + static_cast<int64_t>(tile) * G.chunks) / kRound;
+        b = a + G.chunks / kRound;
+        Q = p.iters / kRound;
+        P = p.n_wg;
+    }
     const int32_t v_first = static_cast<int32_t>(floordiv53((a + 1) * P - 1, Q));
     const int32_t v_last = static_cast<int32_t>(floordiv53(b * P - 1, Q));
-    if (v_first == v_last) return;  // the tile lies inside one slice: written directly
+    if (v_first == v_last) return;  // the tile lies inside one range: written directly
     const int32_t p0 = mblk_lo(G, mb), mt = mblk_lo(G, mb + 1) - p0;
     const int tw = blockIdx.y;
     if (tw >= mt) return;   // past the M-block's packed tiles
@@ -666,7 +729,8 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int32_t vv = v_first + c;
-        const int64_t slot = (c == 0 && first_odd) ? 2 * static_cast<int64_t>(vv) + 1 : 2 * static_cast<int64_t>(vv);
+        const int64_t sv = base + static_cast<int64_t>(vv) * stride;
+        const int64_t slot = (c == 0 && first_odd) ? 2 * sv + 1 : 2 * sv;
         if (vv <= v_last) {
 #pragma unroll
             for (int i = 0; i < kRows; ++i)
@@ -690,7 +754,8 @@ __global__ __launch_bounds__(256) void k_dw_fixup(const DwParams p) {
     for (int32_t vv = v_first + 4; vv <= v_last; ++vv) {
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
-            const float4 y = *reinterpret_cast<const float4 *>(part + 2 * static_cast<int64_t>(vv) * kSlotFloats + 4 * i * 256);
+            const float4 y = *reinterpret_cast<const float4 *>(
+                part + 2 * (base + static_cast<int64_t>(vv) * stride) * kSlotFloats + 4 * i * 256);
             sum[i].x += y.x;
             sum[i].y += y.y;
             sum[i].z += y.z;
@@ -928,16 +993,59 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         // would cross more output tiles than the kernel tracks; never more
         // slices than rounds (so none is empty).  The slice arithmetic runs in
         // fp64 on the GPU, exact while P * Q < 2^53.
+        //
+        // Team slicing when a group has three or more M-blocks: group g gets
+        // n_team teams of n_mblk workgroups, member mb of a team doing
+        // M-block mb over the team's range of column-block rounds, so the
+        // members read each X chunk together (one XCD, neighbouring slices)
+        // and all but the first find it in L2.  Each group starts with the
+        // fewest teams whose ranges touch at most kMaxSegs - 1 column blocks;
+        // a team is then added, while the CUs last, to the group whose
+        // members have the most rounds each (never more teams than rounds).
         int64_t P = 0;
+        bool teams = false;
+        for (int32_t g = 0; g < p.n_groups; ++g) teams = teams || p.g[g].n_mblk >= kTeamMblk;
+        if (teams) {
+            int64_t T[kMaxGroups], Qg[kMaxGroups], tot = 0;
+            for (int32_t g = 0; g < p.n_groups; ++g) {
+                const DwGroupDev &d = p.g[g];
+                Qg[g] = int64_t(d.n_nblk) * (d.chunks / kRound);
+                T[g] = std::min<int64_t>(Qg[g], (d.n_nblk + kMaxSegs - 3) / (kMaxSegs - 2));
+                tot += T[g] * d.n_mblk;
+            }
+            teams = tot <= cus;
+            while (teams) {
+                int32_t best = -1;
+                for (int32_t g = 0; g < p.n_groups; ++g) {
+                    if (T[g] >= Qg[g] || tot + p.g[g].n_mblk > cus) continue;
+                    if (best < 0 || Qg[g] * T[best] > Qg[best] * T[g]) best = g;
+                }
+                if (best < 0) break;
+                ++T[best];
+                tot += p.g[best].n_mblk;
+            }
+            if (teams) {
+                int32_t wb = 0;
+                for (int32_t g = 0; g < p.n_groups; ++g) {
+                    p.g[g].wg_begin = wb;
+                    p.g[g].n_team = static_cast<int32_t>(T[g]);
+                    wb += static_cast<int32_t>(T[g]) * p.g[g].n_mblk;
+                }
+                P = ((tot + kXcds - 1) / kXcds) * kXcds;   // idle slices up to whole XCDs
+            }
+        }
+        p.teams = teams ? 1 : 0;
+        for (int32_t g = 0; g < p.n_groups; ++g)
+            p.g[g].keep_x = teams ? (p.g[g].n_mblk >= 2) : p.g[g].nb_major;
         int64_t rt = p.g[0].chunks / kRound;
         for (int32_t g = 1; g < p.n_groups; ++g)
             if (p.g[g].chunks / kRound != rt) rt = 0;
-        for (int64_t f = rt; f >= 1; --f) {
+        for (int64_t f = rt; f >= 1 && !teams; --f) {
             if (rt % f || f * otiles > cus) continue;
             if (4 * f * otiles >= 3 * int64_t(cus)) P = f * otiles;
             break;
         }
-        p.xcd_blocked = P == 0;
+        p.xcd_blocked = teams || P == 0;
         if (P == 0) {
             P = cus;
             const int64_t need = (iters + (kMaxSegs - 2) * min_chunks - 1) / ((kMaxSegs - 2) * min_chunks);
@@ -1030,6 +1138,9 @@ int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, s
             r.chunks = G.chunks;
             r.n_nblk = G.n_nblk;
             r.nb_major = G.nb_major;
+            r.team = L.p.teams;
+            r.wg_begin = G.wg_begin;
+            r.n_team = G.n_team;
             r.n_ptiles = G.n_ptiles;
             r.n_mblk = G.n_mblk;
             r.row_begin = M.row_begin;

@@ -38,6 +38,8 @@ struct DwRowSrc {
     int32_t row_begin;        // first packed row of the matrix in its group
     int32_t layout;           // SFT_DW_TILES or SFT_DW_PACKED
     int32_t nb_major;         // output tiles numbered column block by column block
+    int32_t team;             // team slicing: slices wg_begin + t * n_mblk + M-block, t < n_team
+    int32_t wg_begin, n_team;
 };
 
 // Gather and product of sft_masked_dw without the fix-up, partial tiles

@@ -517,7 +517,8 @@ __global__ __launch_bounds__(kCkThreads) void k_rows_copy(const CkParams p) {
 // of the row is the sum, in slice order, of the partial rows the slices that
 // cut its output tile left (the same additions as the fix-up kernel's), or
 // the dW_act row where one slice covered the tile.  tab[nb] = (first slice,
-// slices | first-slot-odd << 16), built per workgroup.
+// slices | first-slot-odd << 16), built per workgroup; the slices are
+// `stride` apart (team slicing: one per team).
 struct FusedGrad {
     // (up to four partial loads per chunk)
     template <int kThreads, int kChunks>
@@ -529,9 +530,10 @@ struct FusedGrad {
     const float *dw_row;      // the row in dW_act
     const int2 *tab;          // LDS
     int64_t slot_floats;
-    int32_t bn, prow;
+    int32_t bn, prow, stride;
     __device__ __forceinline__ const float *slot_row(int32_t v0, int32_t i, bool odd) const {
-        const int64_t slot = (i == 0 && odd) ? 2 * static_cast<int64_t>(v0) + 1 : 2 * static_cast<int64_t>(v0 + i);
+        const int64_t sv = v0 + static_cast<int64_t>(i) * stride;
+        const int64_t slot = (i == 0 && odd) ? 2 * sv + 1 : 2 * sv;
         return part + slot * slot_floats + static_cast<int64_t>(prow) * bn;
     }
     __device__ __forceinline__ Raw load(int64_t c) const {
@@ -623,16 +625,23 @@ __global__ __launch_bounds__(kThreads) void k_fused_update(const FusedParams p) 
         while (mb > 0 && mlo(mb) > ptile) --mb;
         while (mb + 1 < S.n_mblk && mlo(mb + 1) <= ptile) ++mb;
         const int32_t prow = static_cast<int32_t>(j - 32 * mlo(mb));
-        // slices over each output tile (M-block mb, column block nb): slice v
-        // starts at round floor(v * Q / P)
+        // slices over each output tile (M-block mb, column block nb): the
+        // tile is rounds [a, b) of Q rounds cut into P equal ranges, range i
+        // starting at round floor(i * Q / P) -- the launch's iterations and
+        // slices, or (team slicing) the group's column-block rounds and teams,
+        // range i being slice wg_begin + i * n_mblk + mb
+        const int64_t R = S.chunks / S.rnd;
+        const int64_t Q = S.team ? S.n_nblk * R : S.Q, P = S.team ? S.n_team : S.P;
+        const int64_t base = S.team ? S.wg_begin + mb : 0, stride = S.team ? S.n_mblk : 1;
         for (int nb = lt; nb < S.n_nblk; nb += kLanes) {
             const int64_t tile = S.nb_major ? nb * static_cast<int64_t>(S.n_mblk) + mb : mb * S.n_nblk + nb;
-            const int64_t a = (S.it_begin + tile * static_cast<int64_t>(S.chunks)) / S.rnd;
-            const int64_t b = a + S.chunks / S.rnd;
-            const int64_t v0 = floordiv53((a + 1) * S.P - 1, S.Q);
-            const int64_t v1 = floordiv53(b * S.P - 1, S.Q);
-            const bool odd = floordiv53(v0 * S.Q, S.P) < a;
-            tab[sub][nb] = make_int2(static_cast<int>(v0), static_cast<int>(v1 - v0 + 1) | (odd ? 0x10000 : 0));
+            const int64_t a = S.team ? nb * R : (S.it_begin + tile * static_cast<int64_t>(S.chunks)) / S.rnd;
+            const int64_t b = a + R;
+            const int64_t v0 = floordiv53((a + 1) * P - 1, Q);
+            const int64_t v1 = floordiv53(b * P - 1, Q);
+            const bool odd = floordiv53(v0 * Q, P) < a;
+            tab[sub][nb] = make_int2(static_cast<int>(base + v0 * stride),
+                                     static_cast<int>(v1 - v0 + 1) | (odd ? 0x10000 : 0));
         }
         __syncthreads();
         FusedGrad gr;
@@ -642,6 +651,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_update(const FusedParams p) 
         gr.slot_floats = S.slot_floats;
         gr.bn = S.bn;
         gr.prow = prow;
+        gr.stride = S.team ? S.n_mblk : 1;
         update_row<kThreads, kChunks, kPer>(M, k, valid, p.hp, gr);
     });
 }

@@ -285,3 +285,19 @@ def test_dw_many_mblocks_column_major_tiles(gpu_lib, layout):
     Xi = synth.integer_bf16((T, C), -3, 3, 1930)
     matsi = [(synth.integer_bf16((T, 900), -2, 2, 1931), _mask_rows(900, synth.clustered_rows(900, 420, 1932)))]
     _check([(Xi, matsi)], exact=True, layout=layout)
+
+
+@LAYOUTS
+def test_dw_team_slices_cut_tiles(gpu_lib, layout):
+    # a group of three or more M-blocks puts the launch on team slicing: a
+    # 5-M-block and a 2-M-block group (packed; more in the tile layout), 8
+    # column blocks each, 4096 tokens (16 rounds a tile), share the CUs in
+    # teams of 3-4 rounds, so most tiles are cut at ragged rounds into up to
+    # five partial sums added by the fix-up; repeated for determinism
+    T, C = 4096, 2000
+    X1 = synth.normal_bf16((T, C), 1.0, 2100)
+    mats1 = [(synth.normal_bf16((T, R), 0.01, 2101 + i), _mask_rows(R, synth.clustered_rows(R, k, 2110 + i)))
+             for i, (R, k) in enumerate([(900, 330), (600, 200)])]
+    X2 = synth.normal_bf16((T, C), 1.0, 2120)
+    mats2 = [(synth.normal_bf16((T, 512), 0.01, 2121), _mask_rows(512, synth.clustered_rows(512, 200, 2122)))]
+    _check([(X1, mats1), (X2, mats2)], repeat=2, layout=layout)

@@ -151,3 +151,12 @@ def test_fused_many_mblocks(gpu_lib, layout):
     # 4 and more M-blocks (output tiles numbered column block by column block)
     case = _case([(256, 520, [(700, 300), (400, 150)]), (256, 136, [(300, 170)])], 2700)
     _check_equal(case, layout)
+
+
+@LAYOUTS
+def test_fused_team_slices_cut_tiles(gpu_lib, layout):
+    # team slicing with tiles cut at ragged rounds (5- and 2-M-block groups,
+    # 16 rounds a tile, teams of 3-4 rounds): the update adds each cut tile's
+    # partial rows, one slice per team, in the fix-up's order
+    case = _case([(4096, 2000, [(900, 330), (600, 200)]), (4096, 2000, [(512, 200)])], 2800)
+    _check_equal(case, layout)
