@@ -64,7 +64,7 @@ constexpr int kMaxSegs = 16;         // output tiles touched by one slice
 constexpr int kXcds = 8;
 constexpr int kTeamMblk = 3;         // team slicing when a group has this many M-blocks (2 measured slower)
 constexpr int64_t kSlotFloats = int64_t(kMaxTiles) * 32 * kBN;   // one partial output tile
-constexpr int kGatherTokens = 256;
+constexpr int kGatherTokens = 64;
 constexpr uint32_t kOutside = 0x80000000u;   // buffer offset beyond every resource size
 // Memory instructions a wave issues per chunk: 4 operand loads + 4 X copies.
 constexpr int kLoadsA = 4, kCopiesX = 4;
@@ -157,7 +157,8 @@ __device__ __forceinline__ int2 tile_pos(const DwGroupDev &G, int32_t t) {
 
 // ---------------------------------------------------------------- gather
 
-// One workgroup per (packed tile, 256 tokens).  Thread (row i, token t%8)
+// One workgroup per (packed tile, 64 tokens) (measured faster than 128 or
+// 256: more waves in flight for the scattered 2-byte reads).  Thread (row i, token t%8)
 // loads one bf16 per 8 tokens; the block is transposed through LDS and
 // written as 16-byte runs of 8 tokens.  Rows without a source, tokens past T
 // and the padding up to Tp are zero.
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(256) void k_dw_gather(const DwParams p) {
     __syncthreads();
     uint16_t *dst = G.at + (static_cast<int64_t>(pt) * (G.Tp / 8) + t0 / 8) * 256;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kGatherTokens / 64; ++u) {
         const int gidx = tid + 256 * u;
         const int oct = gidx >> 5, r = gidx & 31;
         if (t0 + 8 * oct < G.Tp)
