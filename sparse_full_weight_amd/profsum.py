@@ -12,12 +12,21 @@ support:
   ``bench.py --copy-calibration`` run under the same counter).  The last line
   is machine-readable (``traffic-json: {...}``) and carries the SHA-256 of the
   kernel source the counters were taken on, so that a reader can tell when
-  they no longer describe the code.
+  they no longer describe the code;
+* ``units``: how busy the texture address (TA) and texture data (TD) units,
+  the matrix cores and the L2 read path were during one kernel, from a
+  ``--pmc`` run of ``GRBM_GUI_ACTIVE TA_TA_BUSY_sum TD_TD_BUSY_sum
+  SQ_VALU_MFMA_BUSY_CYCLES`` (and a second of ``TCP_TCC_READ_REQ_LATENCY_sum
+  TCP_TCC_READ_REQ_sum``).  On MI355X ``GRBM_GUI_ACTIVE`` adds the 8 XCDs'
+  active cycles, the TA and TD sums add the 256 CUs' and the MFMA-busy sum
+  the 1024 SIMDs' busy cycles; the fractions divide by those counts.
 
 Usage:
   python -m sparse_full_weight_amd.profsum stats <kernel_stats.csv> --cmd "<command>" > out.txt
   python -m sparse_full_weight_amd.profsum counters --fetch <dir> --write <dir> \\
       --copy-fetch <dir> --copy-write <dir> --cmd "<commands>" > out.txt
+  python -m sparse_full_weight_amd.profsum units --runs <dir> [<dir> ...] --kernel k_masked_dw \\
+      --label "<workload>" ... --cmd "<commands>" > out.txt
 (each <dir> holds the ``*_counter_collection.csv`` of one run).
 """
 from __future__ import annotations
@@ -131,6 +140,42 @@ def counters(fetch: str, write: str, copy_fetch: str, copy_write: str, cmd: str)
     return "\n".join(out) + "\n"
 
 
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def _kernel_avgs(dirname: str, kernel: str) -> dict:
+    """Average per dispatch of every counter a run collected for `kernel`."""
+    files = glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {dirname}")
+    per: dict = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if kernel_of(r["Kernel_Name"], (kernel,)):
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {c: sum(v) / len(v) for c, v in per.items()}
+
+
+def units(groups, labels, kernel: str, cmd: str) -> str:
+    """groups: per workload, the run directories whose counters it combines."""
+    out = [f"# unit activity of {kernel} from rocprofv3 counters", f"# commands: {cmd}",
+           f"# fractions: TA and TD busy cycles / ({CUS} CUs x active cycles per XCD), MFMA busy cycles / "
+           f"({SIMDS} SIMDs x active cycles per XCD), active cycles per XCD = GRBM_GUI_ACTIVE / {XCDS}", "",
+           f"{'workload':28s} {'cycles/XCD':>11s} {'TA busy':>8s} {'TD busy':>8s} {'MFMA busy':>10s} "
+           f"{'L2 read latency (cyc)':>22s}"]
+    for label, dirs in zip(labels, groups):
+        v: dict = {}
+        for d in dirs:
+            v.update(_kernel_avgs(d, kernel))
+        g = v.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        frac = lambda c, n: f"{v[c] / (n * g):8.3f}" if c in v and g else f"{'-':>8s}"
+        lat = (f"{v['TCP_TCC_READ_REQ_LATENCY_sum'] / v['TCP_TCC_READ_REQ_sum']:22.0f}"
+               if v.get("TCP_TCC_READ_REQ_sum") else f"{'-':>22s}")
+        out.append(f"{label:28s} {g:11.0f} {frac('TA_TA_BUSY_sum', CUS)} {frac('TD_TD_BUSY_sum', CUS)} "
+                   f"{frac('SQ_VALU_MFMA_BUSY_CYCLES', SIMDS):>10s} {lat}")
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str) -> dict | None:
     """The traffic record of a counters summary, or None if missing."""
     try:
@@ -152,9 +197,19 @@ def main(argv=None):
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         b.add_argument("--" + k, required=True)
     b.add_argument("--cmd", required=True)
+    c = sub.add_parser("units")
+    c.add_argument("--runs", nargs="+", action="append", required=True,
+                   help="run directories of one workload (repeat the flag per workload)")
+    c.add_argument("--label", action="append", required=True)
+    c.add_argument("--kernel", default="k_masked_dw")
+    c.add_argument("--cmd", required=True)
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(stats(args.csv, args.cmd))
+    elif args.what == "units":
+        if len(args.runs) != len(args.label):
+            raise SystemExit("one --label per --runs")
+        sys.stdout.write(units(args.runs, args.label, args.kernel, args.cmd))
     else:
         sys.stdout.write(counters(args.fetch, args.write, args.copy_fetch, args.copy_write, args.cmd))
 
