@@ -344,14 +344,18 @@ def other_rows(L0: "Layer", K: int, stream):
         _time_calls([cp, dn], K, stream))
     del sts, G, ws
 
-    # ---- standalone write-back of the 1% layer's active rows (7 matrices)
-    wb, w_wb = [], 0.0
+    # ---- standalone write-back of the 1% layer's active rows (7 matrices):
+    # one batched call, and the seven single-matrix calls beside it
+    wb, wb_mats, w_wb = [], [], 0.0
     for name, m in L0.mats.items():
         plan = m["plan"]
         rows_dev = torch.from_numpy(plan.active_rows).to(dev)
         wb.append(_lib.prepare_masked_writeback(m["q"], m["s"], m["delta"], rows_dev, plan.n_active, m["w_live"]))
+        wb_mats.append((m["q"], m["s"], m["delta"], rows_dev, plan.n_active, m["w_live"]))
         w_wb += accounting.writeback_work(m["C"], plan.n_active).bytes
-    out["a6_masked_writeback"] = dict(_hbm(w_wb, _time_calls(wb, K, stream)), calls=len(wb))
+    out["a6_masked_writeback"] = dict(_hbm(w_wb, _time_calls([_lib.prepare_masked_writeback_many(wb_mats)], K,
+                                                             stream)), calls=1)
+    out["a6_masked_writeback_single_calls"] = dict(_hbm(w_wb, _time_calls(wb, K, stream)), calls=len(wb))
 
     # ---- active-row checkpoint of the 1% layer (7 matrices, one call each way)
     cks = [_lib.CkptMat.alloc(u.q, u.s, u.delta, u.m, u.v, u.t, u.active_rows, u.slot, u.n_active, u.w_live)

@@ -20,7 +20,8 @@
  *                                                                  -> sft_sparse_update,
  *                                                                     sft_coupled_update
  *   4. the sparse write-back of the live bf16 weights (section 2.3).
- *                                                                  -> sft_masked_writeback
+ *                                                                  -> sft_masked_writeback,
+ *                                                                     sft_masked_writeback_many
  *                                                                     (or fused into 3)
  *   The mixing coefficients of the coupled update come from a host schedule
  *   (sections 2.4, 2.5):                                         -> sft_helix_init,
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 8
+#define SFT_ABI_VERSION 9
 
 enum {
     SFT_OK = 0,
@@ -468,6 +469,29 @@ int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *h
 int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, int64_t R,
                          int64_t C, const int32_t *active_rows, int64_t n_active,
                          uint16_t *w_live, void *stream);
+
+/* One matrix of sft_masked_writeback_many: the arguments of
+ * sft_masked_writeback, with the same layouts and limits. */
+typedef struct {
+    const int8_t *q;            /* int8 [R x C]                     */
+    const float *s;             /* fp32 [R]                         */
+    const float *delta;         /* fp32 [R x C]                     */
+    int64_t R, C;
+    const int32_t *active_rows; /* device, ascending, [n_active]    */
+    int64_t n_active;
+    uint16_t *w_live;           /* bf16 [R x C], written on the listed rows only */
+} sft_wb_mat;
+
+/*
+ * The sparse write-back (section 2.3) of several matrices in one launch (16
+ * matrices per launch; more take more launches): each matrix's listed rows
+ * get exactly what sft_masked_writeback writes.  Matrices with no active row
+ * are skipped.  The caller owns every buffer; the library keeps no pointer.
+ * Errors: SFT_EINVAL (bad sizes, null pointer), SFT_ESHAPE (C % 8 != 0),
+ * SFT_EALIGN, SFT_ENOTSUP (2^31 rows or more in one launch), SFT_EHIP; a
+ * failed check launches nothing.
+ */
+int sft_masked_writeback_many(const sft_wb_mat *mats, int32_t n_mats, void *stream);
 
 /* ======================================================================= */
 /* device: active-row checkpoints (section 2.6)                             */

@@ -31,6 +31,7 @@ EXPORTS = (
     "sft_last_error", "sft_abi_version", "sft_conductor_window", "sft_tracker_window", "sft_plan_rows",
     "sft_plan_embedding", "sft_slots_update", "sft_bias_table", "sft_masked_dw_workspace", "sft_masked_dw",
     "sft_embedding_dw", "sft_sparse_update", "sft_coupled_update", "sft_masked_writeback", "sft_masked_dw_update",
+    "sft_masked_writeback_many",
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
     "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
     "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma",
@@ -75,6 +76,11 @@ class CUpdMat(C.Structure):
                 ("active_rows", C.c_void_p), ("slot", C.c_void_p), ("fresh", C.c_void_p), ("G", C.c_void_p),
                 ("q", C.c_void_p), ("s", C.c_void_p), ("delta", C.c_void_p), ("m", C.c_void_p),
                 ("v", C.c_void_p), ("t", C.c_void_p), ("w_live", C.c_void_p)]
+
+
+class CWbMat(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("s", C.c_void_p), ("delta", C.c_void_p), ("R", C.c_int64), ("C", C.c_int64),
+                ("active_rows", C.c_void_p), ("n_active", C.c_int64), ("w_live", C.c_void_p)]
 
 
 class CPair(C.Structure):
@@ -143,6 +149,7 @@ def lib() -> C.CDLL:
         L.sft_masked_dw_update.argtypes = [C.POINTER(CDwGroup), i32, p, C.c_size_t, C.POINTER(CUpdMat), i32,
                                            C.POINTER(CAdam), p]
         L.sft_masked_writeback.argtypes = [p, p, p, i64, i64, p, i64, p, p]
+        L.sft_masked_writeback_many.argtypes = [C.POINTER(CWbMat), i32, p]
         L.sft_rewind_init.argtypes = [C.POINTER(CRewind)]
         L.sft_rewind_observe.argtypes = [C.POINTER(CRewind), C.c_double, C.POINTER(C.c_int32)]
         L.sft_rows_save.argtypes = [C.POINTER(CCkptMat), i32, p]
@@ -453,6 +460,21 @@ def sft_masked_writeback(q, s, delta, active_rows, n_active: int, w_live, stream
                                       _stream(stream)))
 
 
+def _c_wb_mats(mats):
+    """mats: (q, s, delta, active_rows, n_active, w_live) per matrix."""
+    import torch
+    return (CWbMat * max(len(mats), 1))(*[
+        CWbMat(_dev(q, torch.int8), _dev(s, torch.float32), _dev(d, torch.float32), q.shape[0], q.shape[1],
+               _dev(rows, torch.int32), n, _dev(w)) for q, s, d, rows, n, w in mats])
+
+
+def sft_masked_writeback_many(mats, stream=None) -> None:
+    """Section 2.3 sparse write-back of several matrices in one launch; mats
+    holds (q, s, delta, active_rows, n_active, w_live) per matrix."""
+    arr = _c_wb_mats(mats)
+    _check(lib().sft_masked_writeback_many(arr, len(mats), _stream(stream)))
+
+
 # ------------------------------------------------------------------ prepared calls
 class Prepared:
     """A device call with its ctypes arguments built once (for tight loops).
@@ -511,6 +533,11 @@ def prepare_masked_writeback(q, s, delta, active_rows, n_active: int, w_live) ->
     args = (_dev(q, torch.int8), _dev(s, torch.float32), _dev(delta, torch.float32), R, Cc,
             _dev(active_rows, torch.int32), n_active, _dev(w_live))
     return Prepared(lib().sft_masked_writeback, args, (q, s, delta, active_rows, w_live))
+
+
+def prepare_masked_writeback_many(mats) -> Prepared:
+    arr = _c_wb_mats(mats)
+    return Prepared(lib().sft_masked_writeback_many, (arr, len(mats)), (arr, mats))
 
 
 # ------------------------------------------------------------------ checkpoint and rewind

@@ -376,12 +376,11 @@ __global__ __launch_bounds__(kThreads) void k_coupled_update(const PairParams p)
     });
 }
 
-__global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restrict__ q,
-                                                          const float *__restrict__ s,
-                                                          const float *__restrict__ delta, int64_t C,
-                                                          const int32_t *__restrict__ rows,
-                                                          uint16_t *__restrict__ w_live) {
-    const int64_t r = rows[blockIdx.x];
+// One live row r: w_live[r, c] = bf16(fl(fl(s[r] * q[r, c]) + delta[r, c])),
+// 8 columns per lane and step, 256 lanes.
+__device__ __forceinline__ void writeback_row(const int8_t *__restrict__ q, const float *__restrict__ s,
+                                              const float *__restrict__ delta, int64_t C, int64_t r,
+                                              uint16_t *__restrict__ w_live) {
     const float sr = s[r];
     const int8_t *qr = q + r * C;
     const float *dr = delta + r * C;
@@ -406,6 +405,39 @@ __global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restri
         pack.w = o[6] | (static_cast<uint32_t>(o[7]) << 16);
         *reinterpret_cast<uint4 *>(wr + c) = pack;
     }
+}
+
+__global__ __launch_bounds__(256) void k_masked_writeback(const int8_t *__restrict__ q,
+                                                          const float *__restrict__ s,
+                                                          const float *__restrict__ delta, int64_t C,
+                                                          const int32_t *__restrict__ rows,
+                                                          uint16_t *__restrict__ w_live) {
+    writeback_row(q, s, delta, C, rows[blockIdx.x], w_live);
+}
+
+// Several matrices in one launch: workgroup b takes row b - row_begin of the
+// matrix whose range [row_begin, row_begin + n_active) holds b.
+struct WbMatDev {
+    const int8_t *q;
+    const float *s;
+    const float *delta;
+    const int32_t *rows;
+    uint16_t *w_live;
+    int64_t C;
+    int64_t row_begin;
+};
+
+struct WbParams {
+    WbMatDev mat[kMaxMats];
+    int32_t n_mats;
+};
+
+__global__ __launch_bounds__(256) void k_masked_writeback_many(const WbParams p) {
+    const int64_t b = blockIdx.x;
+    int mi = 0;
+    while (mi + 1 < p.n_mats && b >= p.mat[mi + 1].row_begin) ++mi;
+    const WbMatDev &M = p.mat[mi];
+    writeback_row(M.q, M.s, M.delta, M.C, M.rows[b - M.row_begin], M.w_live);
 }
 
 // ---- Active-row checkpoints (section 2.6: only the active rows are copied).
@@ -954,6 +986,40 @@ int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, in
     hipLaunchKernelGGL(k_masked_writeback, dim3(static_cast<uint32_t>(n_active)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), q, s, delta, C, active_rows, w_live);
     return launch_status("sft_masked_writeback");
+}
+
+int sft_masked_writeback_many(const sft_wb_mat *mats, int32_t n_mats, void *stream) {
+    sft::clear_error();
+    SFT_CHECK(n_mats >= 0 && (n_mats == 0 || mats), SFT_EINVAL, "sft_masked_writeback_many: bad matrix list");
+    for (int32_t i = 0; i < n_mats; ++i) {
+        const sft_wb_mat &m = mats[i];
+        SFT_CHECK(m.R >= 0 && m.C > 0 && m.n_active >= 0 && m.n_active <= m.R, SFT_EINVAL,
+                  "sft_masked_writeback_many: matrix %d: bad sizes", i);
+        SFT_CHECK(m.C % 8 == 0, SFT_ESHAPE, "sft_masked_writeback_many: matrix %d: C=%lld is not a multiple of 8", i,
+                  (long long)m.C);
+        if (m.n_active == 0) continue;
+        SFT_CHECK(m.q && m.s && m.delta && m.active_rows && m.w_live, SFT_EINVAL,
+                  "sft_masked_writeback_many: matrix %d: null pointer", i);
+        SFT_CHECK(sft::aligned16(m.q) && sft::aligned16(m.delta) && sft::aligned16(m.w_live), SFT_EALIGN,
+                  "sft_masked_writeback_many: matrix %d: buffer not 16-byte aligned", i);
+    }
+    // Matrices go out in batches of kMaxMats per launch (kernel-argument table).
+    for (int32_t base = 0; base < n_mats; base += kMaxMats) {
+        WbParams p{};
+        int64_t n_wg = 0;
+        for (int32_t i = base; i < std::min(n_mats, base + kMaxMats); ++i) {
+            const sft_wb_mat &m = mats[i];
+            if (m.n_active == 0) continue;
+            p.mat[p.n_mats++] = WbMatDev{m.q, m.s, m.delta, m.active_rows, m.w_live, m.C, n_wg};
+            n_wg += m.n_active;
+        }
+        if (n_wg == 0) continue;
+        SFT_CHECK(n_wg < (int64_t(1) << 31), SFT_ENOTSUP, "sft_masked_writeback_many: too many rows");
+        hipLaunchKernelGGL(k_masked_writeback_many, dim3(static_cast<uint32_t>(n_wg)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), p);
+        if (int rc = launch_status("sft_masked_writeback_many")) return rc;
+    }
+    return SFT_OK;
 }
 
 }  // extern "C"

@@ -201,6 +201,48 @@ def test_masked_writeback_bit_exact(gpu_lib):
     assert np.array_equal(wl.cpu().numpy().view(np.uint16), want)
 
 
+def _wb_case(R, C, k, seed):
+    q, s, delta = synth.quant_state(R, C, seed)
+    rows = np.sort(synth.rng(seed + 1).choice(R, k, replace=False)).astype(np.int32)
+    w0 = np.full((R, C), 0x5A5A, np.uint16)
+    return q, s, delta, rows, w0
+
+
+def test_masked_writeback_many_bit_exact(gpu_lib):
+    # 19 matrices (two launches of at most 16), mixed widths, one with no
+    # active row and one with every row active; every listed row bit-exact
+    # against the oracle and every other row untouched
+    shapes = [(333, 1032, 40), (64, 8, 64), (500, 4096, 0), (40, 2056, 7)] + [(96, 264, 5 + i) for i in range(15)]
+    cases = [_wb_case(R, C, k, 900 + 10 * i) for i, (R, C, k) in enumerate(shapes)]
+    dev_wl = [torch.from_numpy(w0.view(np.int16)).cuda() for *_, w0 in cases]
+    mats = [(dev(q), dev(s), dev(d), dev(rows), rows.size, wl) for (q, s, d, rows, _), wl in zip(cases, dev_wl)]
+    _lib.sft_masked_writeback_many(mats)
+    torch.cuda.synchronize()
+    for i, ((q, s, d, rows, w0), wl) in enumerate(zip(cases, dev_wl)):
+        want = w0.copy()
+        oracle.masked_writeback(q, s, d, rows, want)
+        assert np.array_equal(wl.cpu().numpy().view(np.uint16), want), f"matrix {i}"
+
+
+def test_masked_writeback_many_matches_single_calls_and_rejects(gpu_lib):
+    cases = [_wb_case(200, 520, 30, 960), _wb_case(120, 1000, 120, 970)]
+    one = [torch.from_numpy(w0.view(np.int16)).cuda() for *_, w0 in cases]
+    many = [torch.from_numpy(w0.view(np.int16)).cuda() for *_, w0 in cases]
+    for (q, s, d, rows, _), wl in zip(cases, one):
+        _lib.sft_masked_writeback(dev(q), dev(s), dev(d), dev(rows), rows.size, wl)
+    _lib.sft_masked_writeback_many([(dev(q), dev(s), dev(d), dev(rows), rows.size, wl)
+                                    for (q, s, d, rows, _), wl in zip(cases, many)])
+    torch.cuda.synchronize()
+    for a, b in zip(one, many):
+        assert torch.equal(a, b)
+    _lib.sft_masked_writeback_many([])
+    q, s, d, rows, w0 = _wb_case(16, 12, 2, 980)       # C = 12: not a multiple of 8
+    with pytest.raises(_lib.SftError) as e:
+        _lib.sft_masked_writeback_many([(dev(q), dev(s), dev(d), dev(rows), rows.size,
+                                         torch.zeros((16, 12), dtype=torch.int16, device="cuda"))])
+    assert e.value.code == _lib.SFT_ESHAPE
+
+
 def test_update_rejects_bad_arguments(gpu_lib):
     st, rows, slot, fresh, G = _case(16, 12, 2, 2, 800, False)   # C = 12: not a multiple of 8
     m = GpuMat(st, G, rows, slot, fresh)

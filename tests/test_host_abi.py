@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     missing = [n for n in declared if not hasattr(L, n)]
     assert not missing, missing
     assert sorted(_lib.EXPORTS) == declared
-    assert _lib.sft_abi_version() == 8
+    assert _lib.sft_abi_version() == 9
 
 
 def test_conductor_matches_oracle_over_windows():
