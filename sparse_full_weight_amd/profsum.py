@@ -19,7 +19,10 @@ support:
   SQ_VALU_MFMA_BUSY_CYCLES`` (and a second of ``TCP_TCC_READ_REQ_LATENCY_sum
   TCP_TCC_READ_REQ_sum``).  On MI355X ``GRBM_GUI_ACTIVE`` adds the 8 XCDs'
   active cycles, the TA and TD sums add the 256 CUs' and the MFMA-busy sum
-  the 1024 SIMDs' busy cycles; the fractions divide by those counts.
+  the 1024 SIMDs' busy cycles; the fractions divide by those counts.  With
+  ``SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS`` collected too it
+  adds the LDS's busy fraction (the 256 CUs' LDS cycles) and the bank-conflict
+  cycles per LDS instruction.
 
 Usage:
   python -m sparse_full_weight_amd.profsum stats <kernel_stats.csv> --cmd "<command>" > out.txt
@@ -162,7 +165,7 @@ def units(groups, labels, kernel: str, cmd: str) -> str:
            f"# fractions: TA and TD busy cycles / ({CUS} CUs x active cycles per XCD), MFMA busy cycles / "
            f"({SIMDS} SIMDs x active cycles per XCD), active cycles per XCD = GRBM_GUI_ACTIVE / {XCDS}", "",
            f"{'workload':28s} {'cycles/XCD':>11s} {'TA busy':>8s} {'TD busy':>8s} {'MFMA busy':>10s} "
-           f"{'L2 read latency (cyc)':>22s}"]
+           f"{'L2 read latency (cyc)':>22s} {'LDS busy':>9s} {'conflict cyc/LDS inst':>22s}"]
     for label, dirs in zip(labels, groups):
         v: dict = {}
         for d in dirs:
@@ -171,8 +174,10 @@ def units(groups, labels, kernel: str, cmd: str) -> str:
         frac = lambda c, n: f"{v[c] / (n * g):8.3f}" if c in v and g else f"{'-':>8s}"
         lat = (f"{v['TCP_TCC_READ_REQ_LATENCY_sum'] / v['TCP_TCC_READ_REQ_sum']:22.0f}"
                if v.get("TCP_TCC_READ_REQ_sum") else f"{'-':>22s}")
+        conf = (f"{v['SQ_LDS_BANK_CONFLICT'] / v['SQ_INSTS_LDS']:22.2f}"
+                if v.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in v else f"{'-':>22s}")
         out.append(f"{label:28s} {g:11.0f} {frac('TA_TA_BUSY_sum', CUS)} {frac('TD_TD_BUSY_sum', CUS)} "
-                   f"{frac('SQ_VALU_MFMA_BUSY_CYCLES', SIMDS):>10s} {lat}")
+                   f"{frac('SQ_VALU_MFMA_BUSY_CYCLES', SIMDS):>10s} {lat} {frac('SQ_LDS_IDX_ACTIVE', CUS):>9s} {conf}")
     return "\n".join(out) + "\n"
 
 

@@ -31,7 +31,7 @@ def test_units_fractions(tmp_path):
     _write_run(b, [(k, "TCP_TCC_READ_REQ_LATENCY_sum", 5000.0), (k, "TCP_TCC_READ_REQ_sum", 10.0)])
     text = profsum.units([[a, b]], ["layer"], "k_masked_dw", "cmd")
     row = [ln for ln in text.splitlines() if ln.startswith("layer")][0].split()
-    assert row[1:] == ["1000", "0.500", "0.800", "0.100", "500"]
+    assert row[1:] == ["1000", "0.500", "0.800", "0.100", "500", "-", "-"]
 
 
 def test_units_missing_counters_print_dashes(tmp_path):
@@ -39,4 +39,13 @@ def test_units_missing_counters_print_dashes(tmp_path):
     a = str(tmp_path / "a")
     _write_run(a, [(k, "GRBM_GUI_ACTIVE", 8000.0)])
     row = [ln for ln in profsum.units([[a]], ["x"], "k_masked_dw", "c").splitlines() if ln.startswith("x")][0]
-    assert row.split()[1:] == ["1000", "-", "-", "-", "-"]
+    assert row.split()[1:] == ["1000", "-", "-", "-", "-", "-", "-"]
+
+
+def test_units_lds_columns(tmp_path):
+    k = "void (anonymous namespace)::k_leaf_grad<28>((anonymous namespace)::LeafParams)"
+    a = str(tmp_path / "a")
+    _write_run(a, [(k, "GRBM_GUI_ACTIVE", 8000.0), (k, "SQ_LDS_IDX_ACTIVE", 256 * 1000 * 0.4),
+                   (k, "SQ_LDS_BANK_CONFLICT", 300.0), (k, "SQ_INSTS_LDS", 100.0)])
+    row = [ln for ln in profsum.units([[a]], ["leaf"], "k_leaf_grad", "c").splitlines() if ln.startswith("leaf")][0]
+    assert row.split()[-2:] == ["0.400", "3.00"]
