@@ -75,6 +75,7 @@ class Layer:
 
         from sparse_full_weight_amd import _lib, synth
         self.idx = idx
+        self.density = density
         dev = "cuda"
         seed = seed0 + 100 * idx
         shapes = synth.LLAMA7B
@@ -417,6 +418,33 @@ def other_rows(L0: "Layer", K: int, stream):
         del ring
         torch.cuda.empty_cache()
     out["c_density_sweep_step"] = sweep
+
+    # ---- one GPU's share of a token-sharded step: the same 1% layer step (fused
+    # call, plans resident) on T/N tokens, the shape each of N GPUs would run
+    # before the dW exchange (which is not built here)
+    share = {}
+    for n_gpu in (2, 4, 8):
+        T = L0.T // n_gpu
+        ring = [Layer(200 + i, T, L0.density, 7000, "packed") for i in range(3)]
+
+        def ring_ms(fn):
+            for i in range(5):
+                fn(ring[i % 3])
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(K):
+                fn(ring[i % 3])
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / K
+        dw_b, up_b = ring[0].dw_work().bytes, ring[0].upd_work().bytes
+        share[f"T{T}"] = dict(_hbm(dw_b + up_b, ring_ms(lambda L: L.fused_call(stream))), n_gpus_sharing=n_gpu,
+                              tokens=T, masked_dw=_hbm(dw_b, ring_ms(lambda L: L.dw_call(stream))))
+        del ring
+        torch.cuda.empty_cache()
+    out["e_token_share_step"] = share
     torch.cuda.synchronize()
     return out
 
