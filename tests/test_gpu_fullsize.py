@@ -379,8 +379,21 @@ def test_llama7b_layer_density_sweep(gpu_lib, layer, density):
     tests above) on the same layer: the benchmark's fused call leaves every
     state array bit-identical to the two calls; sampled dW rows of every matrix
     match the oracle and their update matches it bit for bit."""
-    X, base = layer
-    rng = synth.rng(7500 + int(density * 1000))
+    _check_step(layer, density, T, 7500 + int(density * 1000))
+
+
+@pytest.mark.parametrize("n_gpus", [2, 4, 8])
+def test_llama7b_layer_token_share(gpu_lib, layer, n_gpus):
+    """One GPU's share of a token-sharded step, as the benchmark times it: the
+    1% layer on its first T/N tokens (2048, 1024, 512; at 512 every output tile
+    has two rounds and each workgroup one), checked as the density sweep is."""
+    _check_step(layer, DENSITY, T // n_gpus, 7900 + n_gpus)
+
+
+def _check_step(layer, density, tokens, seed):
+    X = {g: np.ascontiguousarray(x[:tokens]) for g, x in layer[0].items()}
+    base = {name: dict(m, dY=np.ascontiguousarray(m["dY"][:tokens])) for name, m in layer[1].items()}
+    rng = synth.rng(seed)
     mats = {}
     for mi, (name, m) in enumerate(base.items()):
         R = m["R"]
@@ -425,7 +438,7 @@ def test_llama7b_layer_density_sweep(gpu_lib, layer, density):
             x, y = a[name][key], b[name][key]
             if x.dtype == torch.float32:
                 x, y = x.view(torch.int32), y.view(torch.int32)
-            assert torch.equal(x, y), f"{density} {name} {key}"
+            assert torch.equal(x, y), f"{density} T={tokens} {name} {key}"
     for name, m in mats.items():
         plan = plans[name]
         n, C = plan.n_active, m["C"]
@@ -437,4 +450,4 @@ def test_llama7b_layer_density_sweep(gpu_lib, layer, density):
         sub = _sub_state(m, rows, C)
         oracle.sparse_update(sub, g[pick], np.arange(pick.size, dtype=np.int32), np.arange(pick.size, dtype=np.int32),
                              np.ones(pick.size, np.uint8), lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
-        _assert_rows(b[name], rows, pick, sub, f"{density} {name}")
+        _assert_rows(b[name], rows, pick, sub, f"{density} T={tokens} {name}")
