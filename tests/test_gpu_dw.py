@@ -301,3 +301,16 @@ def test_dw_team_slices_cut_tiles(gpu_lib, layout):
     X2 = synth.normal_bf16((T, C), 1.0, 2120)
     mats2 = [(synth.normal_bf16((T, 512), 0.01, 2121), _mask_rows(512, synth.clustered_rows(512, 200, 2122)))]
     _check([(X1, mats1), (X2, mats2)], repeat=2, layout=layout)
+
+
+@LAYOUTS
+def test_dw_million_token_axis_exact(gpu_lib, layout):
+    # T = 2^20 tokens, one 32-row tile, 8 columns: the one output tile is cut
+    # into one slice per CU (256 partial tiles, added by the fix-up in slice
+    # order); small integers keep every partial sum exact, so the result is
+    # bit for bit the oracle's
+    T, R, C = 1 << 20, 32, 8
+    X = synth.integer_bf16((T, C), -2, 2, 2201)
+    dY = synth.integer_bf16((T, R), -2, 2, 2202)
+    mask = _mask_rows(R, [0, 3, 4, 5, 17, 30, 31])
+    _check([(X, [(dY, mask)])], exact=True, layout=layout)
