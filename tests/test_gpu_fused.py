@@ -160,3 +160,10 @@ def test_fused_team_slices_cut_tiles(gpu_lib, layout):
     # partial rows, one slice per team, in the fix-up's order
     case = _case([(4096, 2000, [(900, 330), (600, 200)]), (4096, 2000, [(512, 200)])], 2800)
     _check_equal(case, layout)
+
+
+def test_fused_million_token_axis(gpu_lib):
+    # 2^20 tokens over one 32-row tile and 8 columns: every output tile is cut
+    # into one slice per CU, so each updated row adds 256 partial rows
+    case = _case([(1 << 20, 8, [(32, 7)])], 2900)
+    _check_equal(case, _lib.SFT_DW_PACKED)
