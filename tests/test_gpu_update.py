@@ -64,7 +64,7 @@ def test_sparse_update_two_rows_per_workgroup(gpu_lib):
         assert_state_equal(m.to_state(), want, f"shape {shapes[i]}")
 
 
-@pytest.mark.parametrize("C", [20000, 40000])
+@pytest.mark.parametrize("C", [20000, 40000, 65536])
 def test_sparse_update_wide_rows(gpu_lib, C):
     st, rows, slot, fresh, G = _case(6, C, 3, 3, 200 + C, True)
     m = GpuMat(st, G, rows, slot, fresh)
