@@ -56,8 +56,8 @@ class OracleMat(C.Structure):
         ("R", C.c_int64), ("C", C.c_int64), ("n_active", C.c_int64),
         ("active_rows", C.c_void_p), ("slot", C.c_void_p), ("fresh", C.c_void_p),
         ("G", C.c_void_p), ("q", C.c_void_p), ("s", C.c_void_p), ("delta", C.c_void_p),
-        ("m", C.c_void_p), ("v", C.c_void_p), ("t", C.c_void_p), ("n_slots", C.c_int64),
-        ("w_live", C.c_void_p),
+        ("m", C.c_void_p), ("v", C.c_void_p), ("t", C.c_void_p), ("mv_exp", C.c_void_p),
+        ("n_slots", C.c_int64), ("w_live", C.c_void_p),
     ]
 
 
@@ -72,6 +72,11 @@ def _declare(L: C.CDLL) -> None:
     L.oracle_f16_to_f32.argtypes = [C.c_uint16]; L.oracle_f16_to_f32.restype = f32
     L.oracle_f32_to_f16.argtypes = [f32]; L.oracle_f32_to_f16.restype = C.c_uint16
     L.oracle_f32_to_bf16.argtypes = [f32]; L.oracle_f32_to_bf16.restype = C.c_uint16
+    L.oracle_moment_exponent.argtypes = [f32]; L.oracle_moment_exponent.restype = C.c_int
+    L.oracle_moment_encode.argtypes = [f32, C.c_int]; L.oracle_moment_encode.restype = C.c_uint16
+    L.oracle_moment_decode.argtypes = [C.c_uint16, C.c_int]; L.oracle_moment_decode.restype = f32
+    L.oracle_moment_encode_array.argtypes = [p, i64, C.c_int, p]; L.oracle_moment_encode_array.restype = None
+    L.oracle_moment_decode_array.argtypes = [p, i64, C.c_int, p]; L.oracle_moment_decode_array.restype = None
     for n in ("oracle_f32_to_f16_array", "oracle_f32_to_bf16_array", "oracle_f16_to_f32_array",
               "oracle_bf16_to_f32_array"):
         getattr(L, n).argtypes = [p, i64, p]; getattr(L, n).restype = None
@@ -133,6 +138,28 @@ def bf16_to_f32(h) -> np.ndarray:
     h = _arr(h, np.uint16)
     out = np.empty(h.shape, np.float32)
     lib().oracle_bf16_to_f32_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- scaled fp16 moments
+def moment_exponent(amax: float) -> int:
+    """The exponent a moment row with largest magnitude ``amax`` is stored with."""
+    return int(lib().oracle_moment_exponent(float(amax)))
+
+
+def moment_encode(x, e: int) -> np.ndarray:
+    """fp16 bits of x * 2^e (round to nearest even, saturating)."""
+    x = _arr(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_moment_encode_array(_ptr(x), x.size, int(e), _ptr(out))
+    return out
+
+
+def moment_decode(h, e: int) -> np.ndarray:
+    """The fp32 values fp16(h) * 2^-e."""
+    h = _arr(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().oracle_moment_decode_array(_ptr(h), h.size, int(e), _ptr(out))
     return out
 
 
@@ -229,9 +256,11 @@ def bias_table(beta1: float, beta2: float, t_max: int):
 
 
 class MatState:
-    """Host copy of one matrix's optimizer state (all numpy, updated in place)."""
+    """Host copy of one matrix's optimizer state (all numpy, updated in place).
+    ``e`` holds each slot's moment exponents (int8 [n_slots, 2]: m's, v's);
+    the stored fp16 value h of a moment stands for h * 2^-e."""
 
-    def __init__(self, q, s, delta, m, v, t, w_live=None):
+    def __init__(self, q, s, delta, m, v, t, w_live=None, e=None):
         self.q = _arr(q, np.int8)
         self.s = _arr(s, np.float32)
         self.delta = _arr(delta, np.float32)
@@ -239,10 +268,19 @@ class MatState:
         self.v = _arr(v, np.uint16)
         self.t = _arr(t, np.int32)
         self.w_live = None if w_live is None else _arr(w_live, np.uint16)
+        self.e = np.zeros((self.m.shape[0], 2), np.int8) if e is None else _arr(e, np.int8).reshape(-1, 2)
+        assert self.e.shape[0] == self.m.shape[0]
 
     def copy(self) -> "MatState":
         return MatState(self.q.copy(), self.s.copy(), self.delta.copy(), self.m.copy(),
-                        self.v.copy(), self.t.copy(), None if self.w_live is None else self.w_live.copy())
+                        self.v.copy(), self.t.copy(), None if self.w_live is None else self.w_live.copy(),
+                        self.e.copy())
+
+    def moments(self):
+        """The fp32 moments the stored rows stand for (m, v), slot by slot."""
+        m = np.stack([moment_decode(self.m[k], self.e[k, 0]) for k in range(self.m.shape[0])])
+        v = np.stack([moment_decode(self.v[k], self.e[k, 1]) for k in range(self.v.shape[0])])
+        return m.reshape(self.m.shape), v.reshape(self.v.shape)
 
 
 def _mat(st: MatState, G, active_rows, slot, fresh, keep):
@@ -254,7 +292,7 @@ def _mat(st: MatState, G, active_rows, slot, fresh, keep):
     keep.extend([active_rows, slot, fresh, G])
     return OracleMat(R, Cc, active_rows.size, _ptr(active_rows), _ptr(slot), _ptr(fresh), _ptr(G),
                      _ptr(st.q), _ptr(st.s), _ptr(st.delta), _ptr(st.m), _ptr(st.v), _ptr(st.t),
-                     st.m.shape[0], _ptr(st.w_live))
+                     _ptr(st.e), st.m.shape[0], _ptr(st.w_live))
 
 
 def sparse_update(st: MatState, G, active_rows, slot, fresh=None, *, lr, beta1, beta2, eps,

@@ -125,17 +125,17 @@ class Rewind:
 class RowCopy:
     """The saved rows of one matrix: row k belongs to rows[k]."""
 
-    def __init__(self, q, s, delta, m, v, t):
-        self.q, self.s, self.delta, self.m, self.v, self.t = q, s, delta, m, v, t
+    def __init__(self, q, s, delta, m, v, t, e):
+        self.q, self.s, self.delta, self.m, self.v, self.t, self.e = q, s, delta, m, v, t, e
 
 
 def rows_save(st, rows, slot) -> RowCopy:
-    """Copies rows (q, s, delta) and the moment slots (m, v, t) of a matrix
-    state (an ``oracle.MatState``)."""
+    """Copies rows (q, s, delta) and the moment slots (m, v, t and the
+    moments' exponents) of a matrix state (an ``oracle.MatState``)."""
     rows = np.asarray(rows, np.int64)
     slot = np.asarray(slot, np.int64)
     return RowCopy(st.q[rows].copy(), st.s[rows].copy(), st.delta[rows].copy(), st.m[slot].copy(),
-                   st.v[slot].copy(), st.t[slot].copy())
+                   st.v[slot].copy(), st.t[slot].copy(), st.e[slot].copy())
 
 
 def rows_restore(st, ck: RowCopy, rows, slot) -> None:
@@ -150,5 +150,6 @@ def rows_restore(st, ck: RowCopy, rows, slot) -> None:
     st.m[slot] = ck.m
     st.v[slot] = ck.v
     st.t[slot] = ck.t
+    st.e[slot] = ck.e
     if st.w_live is not None:
         oracle.masked_writeback(st.q, st.s, st.delta, rows.astype(np.int32), st.w_live)

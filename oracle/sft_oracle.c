@@ -132,6 +132,57 @@ ORACLE_API uint16_t oracle_f32_to_bf16(float x)
     return sign | (uint16_t)(((exp2 + 127) << 7) | ((int)n - 128));
 }
 
+/*
+ * Scaled fp16 storage of a row of Adam moments (section 2.3 keeps m and v in
+ * fp16).  Plain fp16 loses small moments: (1 - beta2) g^2 falls below the
+ * smallest fp16 subnormal (2^-24) once |g| is under about 5e-3 and large ones
+ * overflow (v above 65504 once |g| passes about 256).  Reading: each slot
+ * stores its row of m (and of v) as fp16 values of m * 2^e with one exponent
+ * e per row and moment, e chosen at every update so that the row's largest
+ * magnitude lands in [2^14, 2^15): the row keeps fp16's 11 significant bits
+ * across any range of gradients.  e = 15 - k for the row maximum in
+ * [2^(k-1), 2^k), limited to [-112, 125] so that both 2^e and 2^-e are
+ * normal binary32 numbers; an all-zero row takes e = 0.  Scaling by a power
+ * of two is exact in double; the fp16 rounding is to nearest even and
+ * saturates at the largest finite value (65504) instead of overflowing.
+ */
+#define MOMENT_EXP_MIN (-112)
+#define MOMENT_EXP_MAX 125
+
+ORACLE_API int oracle_moment_exponent(float amax)
+{
+    if (!(amax > 0.0f))
+        return 0;
+    int k;
+    frexp((double)amax, &k);       /* amax in [2^(k-1), 2^k) */
+    int e = 15 - k;
+    if (e < MOMENT_EXP_MIN)
+        e = MOMENT_EXP_MIN;
+    if (e > MOMENT_EXP_MAX)
+        e = MOMENT_EXP_MAX;
+    return e;
+}
+
+/* fp16 bits of x * 2^e (round to nearest even, saturating at +-65504). */
+ORACLE_API uint16_t oracle_moment_encode(float x, int e)
+{
+    double y = ldexp((double)x, e);
+    uint16_t h;
+    if (y >= 65504.0)
+        h = 0x7bff;
+    else if (y <= -65504.0)
+        h = 0xfbff;
+    else
+        h = oracle_f32_to_f16((float)y);   /* y is a binary32 value or rounds to f16 zero below 2^-126 */
+    return h;
+}
+
+/* The stored moment: fp16 value times 2^-e (exact in binary32 for e in range). */
+ORACLE_API float oracle_moment_decode(uint16_t h, int e)
+{
+    return (float)ldexp((double)oracle_f16_to_f32(h), -e);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Section 2.1: the conductor and the row tracker.                           */
 /* ------------------------------------------------------------------------ */
@@ -366,8 +417,9 @@ typedef struct {
     int8_t *q;                  /* [R x C] */
     float *s;                   /* [R] */
     float *delta;               /* [R x C] */
-    uint16_t *m, *v;            /* fp16 [n_slots x C] */
+    uint16_t *m, *v;            /* fp16 [n_slots x C], scaled by 2^mv_exp (see above) */
     int32_t *t;                 /* [n_slots] */
+    int8_t *mv_exp;             /* [n_slots x 2]: exponent of the slot's m row, of its v row */
     int64_t n_slots;
     uint16_t *w_live;           /* bf16 [R x C] or NULL */
 } oracle_mat;
@@ -388,13 +440,14 @@ typedef struct {
  * Sterbenz's lemma, so s'*q' + delta' gives w' back); a zero row keeps q' = 0
  * and delta' = w'.
  *
- * Section 2.4 / Kingma-Ba Adam with bias correction: fp32 moments from the
- * stored fp16 values drive the step, the new moments are stored rounded to
- * fp16; the step is lr * mhat / (sqrt(vhat) + eps); decoupled weight decay
+ * Section 2.4 / Kingma-Ba Adam with bias correction: fp32 moments decoded
+ * from the stored scaled fp16 rows drive the step, the new moments are
+ * stored as scaled fp16 rows (exponents from the new rows' maxima); the step
+ * is lr * mhat / (sqrt(vhat) + eps); decoupled weight decay
  * (w * (1 - lr*lambda)) is applied before the step when lambda != 0.
  */
 static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_adam *hp,
-                       float *wnew)
+                       float *wnew, float *mnew, float *vnew)
 {
     int64_t C = M->C;
     int64_t r = M->active_rows[k];
@@ -407,13 +460,15 @@ static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_ad
     float c2 = 1.0f - hp->beta2;
     float decay = 1.0f - hp->lr * hp->weight_decay;
     float s_old = M->s[r];
+    int em_old = fresh ? 0 : M->mv_exp[2 * sl];
+    int ev_old = fresh ? 0 : M->mv_exp[2 * sl + 1];
 
     for (int64_t c = 0; c < C; ++c) {
         int64_t e = r * C + c;
         float sq = s_old * (float)M->q[e];
         float w = sq + M->delta[e];
-        float m_old = fresh ? 0.0f : oracle_f16_to_f32(M->m[sl * C + c]);
-        float v_old = fresh ? 0.0f : oracle_f16_to_f32(M->v[sl * C + c]);
+        float m_old = fresh ? 0.0f : oracle_moment_decode(M->m[sl * C + c], em_old);
+        float v_old = fresh ? 0.0f : oracle_moment_decode(M->v[sl * C + c], ev_old);
         float gc = g[c];
         float m_a = hp->beta1 * m_old;
         float m_b = c1 * gc;
@@ -422,8 +477,8 @@ static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_ad
         float v_a = hp->beta2 * v_old;
         float v_b = c2 * gg;
         float v = v_a + v_b;
-        M->m[sl * C + c] = oracle_f32_to_f16(m);
-        M->v[sl * C + c] = oracle_f32_to_f16(v);
+        mnew[c] = m;
+        vnew[c] = v;
         float mhat = m / bc1;
         float vhat = v / bc2;
         float denom = sqrtf(vhat) + hp->eps;
@@ -433,6 +488,23 @@ static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_ad
         wnew[c] = w1 - u;
     }
     M->t[sl] = step;
+
+    /* the moments leave as scaled fp16 rows */
+    float mmax = 0.0f, vmax = 0.0f;
+    for (int64_t c = 0; c < C; ++c) {
+        if (fabsf(mnew[c]) > mmax)
+            mmax = fabsf(mnew[c]);
+        if (fabsf(vnew[c]) > vmax)
+            vmax = fabsf(vnew[c]);
+    }
+    int em = oracle_moment_exponent(mmax);
+    int ev = oracle_moment_exponent(vmax);
+    M->mv_exp[2 * sl] = (int8_t)em;
+    M->mv_exp[2 * sl + 1] = (int8_t)ev;
+    for (int64_t c = 0; c < C; ++c) {
+        M->m[sl * C + c] = oracle_moment_encode(mnew[c], em);
+        M->v[sl * C + c] = oracle_moment_encode(vnew[c], ev);
+    }
 
     float amax = 0.0f;
     for (int64_t c = 0; c < C; ++c)
@@ -482,11 +554,15 @@ ORACLE_API int oracle_sparse_update(oracle_mat *M, const oracle_adam *hp)
     if (check_mat(M))
         return -1;
     float *wnew = malloc((size_t)M->C * sizeof(float));
-    if (!wnew)
+    float *mnew = malloc((size_t)M->C * sizeof(float));
+    float *vnew = malloc((size_t)M->C * sizeof(float));
+    if (!wnew || !mnew || !vnew) {
+        free(wnew); free(mnew); free(vnew);
         return -2;
+    }
     for (int64_t k = 0; k < M->n_active; ++k)
-        update_row(M, k, M->G + k * M->C, hp, wnew);
-    free(wnew);
+        update_row(M, k, M->G + k * M->C, hp, wnew, mnew, vnew);
+    free(wnew); free(mnew); free(vnew);
     return 0;
 }
 
@@ -513,8 +589,10 @@ ORACLE_API int oracle_coupled_update(oracle_mat *A, oracle_mat *B, float a_own, 
     float *ea = malloc((size_t)C * sizeof(float));
     float *eb = malloc((size_t)C * sizeof(float));
     float *wnew = malloc((size_t)C * sizeof(float));
-    if (!ga || !gb || !ea || !eb || !wnew) {
-        free(ga); free(gb); free(ea); free(eb); free(wnew);
+    float *mnew = malloc((size_t)C * sizeof(float));
+    float *vnew = malloc((size_t)C * sizeof(float));
+    if (!ga || !gb || !ea || !eb || !wnew || !mnew || !vnew) {
+        free(ga); free(gb); free(ea); free(eb); free(wnew); free(mnew); free(vnew);
         return -2;
     }
     int64_t ia = 0, ib = 0;
@@ -536,11 +614,11 @@ ORACLE_API int oracle_coupled_update(oracle_mat *A, oracle_mat *B, float a_own, 
             eb[c] = own_b + cross_b;
         }
         if (has_a)
-            update_row(A, ia++, ea, hp, wnew);
+            update_row(A, ia++, ea, hp, wnew, mnew, vnew);
         if (has_b)
-            update_row(B, ib++, eb, hp, wnew);
+            update_row(B, ib++, eb, hp, wnew, mnew, vnew);
     }
-    free(ga); free(gb); free(ea); free(eb); free(wnew);
+    free(ga); free(gb); free(ea); free(eb); free(wnew); free(mnew); free(vnew);
     return 0;
 }
 
@@ -629,6 +707,18 @@ ORACLE_API void oracle_leaf_adam(int64_t K, const float *g, float *theta, float 
 }
 
 /* Array forms of the conversions above (for tests that convert many values). */
+ORACLE_API void oracle_moment_encode_array(const float *x, int64_t n, int e, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_moment_encode(x[i], e);
+}
+
+ORACLE_API void oracle_moment_decode_array(const uint16_t *h, int64_t n, int e, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_moment_decode(h[i], e);
+}
+
 ORACLE_API void oracle_f32_to_f16_array(const float *x, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i)

@@ -12,7 +12,9 @@ Llama-7B-shaped projections.  Value distributions:
   * activations X ~ N(0, 1) and output gradients dY ~ N(0, 0.01) read as a
     standard deviation of 0.01, both rounded to bf16 (round to nearest even);
   * q ~ U{-127..127}, s_r ~ U(1e-4, 1e-3), delta ~ U(-s_r/2, s_r/2);
-  * mid-run moments m ~ N(0, 1e-3), v ~ U(1e-6, 1e-4) stored as fp16;
+  * mid-run moments m ~ N(0, 1e-3), v ~ U(1e-6, 1e-4) stored as fp16 rows
+    scaled by a per-slot power of two (m by 2^em, em ~ U{8..12}; v by 2^ev,
+    ev ~ U{16..22}), the exponents stored beside them;
   * embedding tokens from a Zipf(1.1) law bounded to the vocabulary.
 Every generator takes an explicit integer seed (numpy PCG64).  Bulk tensors for
 timing can also be drawn on the GPU with torch's seeded generator
@@ -140,15 +142,22 @@ def quant_state(R: int, C: int, seed: int):
 
 
 def moments(n_slots: int, C: int, seed: int, mid_run: bool):
-    """fp16 moment bit patterns and per-slot step counts."""
+    """Stored moments: fp16 bit patterns of m and v rows, per-slot step
+    counts, and per-slot exponents e (int8 [n_slots, 2]); a stored value h
+    stands for h * 2^-e of its row."""
     if not mid_run:
         return (np.zeros((n_slots, C), np.uint16), np.zeros((n_slots, C), np.uint16),
-                np.zeros(n_slots, np.int32))
+                np.zeros(n_slots, np.int32), np.zeros((n_slots, 2), np.int8))
     g = rng(seed)
-    m = to_f16_bits(g.standard_normal((n_slots, C), dtype=np.float32) * np.float32(1e-3))
-    v = to_f16_bits(g.uniform(1e-6, 1e-4, size=(n_slots, C)).astype(np.float32))
+    em = g.integers(8, 13, size=n_slots)
+    ev = g.integers(16, 23, size=n_slots)
+    m = to_f16_bits(g.standard_normal((n_slots, C), dtype=np.float32) * np.float32(1e-3)
+                    * np.exp2(em).astype(np.float32)[:, None])
+    v = to_f16_bits(g.uniform(1e-6, 1e-4, size=(n_slots, C)).astype(np.float32)
+                    * np.exp2(ev).astype(np.float32)[:, None])
     t = np.full(n_slots, 6, np.int32)
-    return m, v, t
+    e = np.stack([em, ev], axis=1).astype(np.int8)
+    return m, v, t, e
 
 
 def gradient_rows(n: int, C: int, std: float, seed: int) -> np.ndarray:

@@ -303,9 +303,9 @@ HP = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
 
 def _state(R, Cc, seed, n_slots, mid_run):
     q, s, delta = synth.quant_state(R, Cc, seed)
-    m, v, t = synth.moments(n_slots, Cc, seed + 1, mid_run)
+    m, v, t, e = synth.moments(n_slots, Cc, seed + 1, mid_run)
     w_live = np.full((R, Cc), 0xA5A5, np.uint16)
-    return oracle.MatState(q, s, delta, m, v, t, w_live)
+    return oracle.MatState(q, s, delta, m, v, t, w_live, e=e)
 
 
 def _rebuild(st):
@@ -357,19 +357,19 @@ def test_update_matches_torch_adam(mid_run):
     w0 = _rebuild(before)
     oracle.sparse_update(st, G, rows, slot, None, **HP)
     w1 = _check_quantised(st, rows)
+    m_before, v_before = before.moments()
+    m_after, v_after = st.moments()
     for k, r in enumerate(rows):
         sl = slot[k]
-        m0 = oracle.f16_to_f32(before.m[sl])
-        v0 = oracle.f16_to_f32(before.v[sl])
-        wt, mt, vt = _torch_adam(w0[r], G[k], m0, v0, int(before.t[sl]), **HP)
+        wt, mt, vt = _torch_adam(w0[r], G[k], m_before[sl], v_before[sl], int(before.t[sl]), **HP)
         tol = 2 * np.spacing(np.abs(wt)) + 1e-6 * HP["lr"]
         assert np.all(np.abs(w1[r] - wt) <= tol)
-        # stored fp16 moments: torch's fp32 moments rounded to fp16 (1 fp16 ulp slack
-        # for torch's different operation order)
-        mh = oracle.f16_to_f32(st.m[sl]).astype(np.float64)
-        vh = oracle.f16_to_f32(st.v[sl]).astype(np.float64)
-        assert np.all(np.abs(mh - mt) <= np.spacing(np.abs(mt.astype(np.float16))).astype(np.float64) + 2 ** -24)
-        assert np.all(np.abs(vh - vt) <= np.spacing(np.abs(vt.astype(np.float16))).astype(np.float64) + 2 ** -24)
+        # stored moments: torch's fp32 moments as fp16 rows scaled by 2^e (1 ulp
+        # of the scaled fp16 value as slack for torch's operation order)
+        for got, want, e in ((m_after[sl], mt, st.e[sl, 0]), (v_after[sl], vt, st.e[sl, 1])):
+            scaled = np.abs(want.astype(np.float64)) * 2.0 ** int(e)
+            ulp = (np.spacing(scaled.astype(np.float16)).astype(np.float64) + 2 ** -24) * 2.0 ** -int(e)
+            assert np.all(np.abs(got.astype(np.float64) - want) <= ulp)
         assert st.t[sl] == before.t[sl] + 1
         assert np.array_equal(st.w_live[r], synth.to_bf16_bits(w1[r]))
 
@@ -400,10 +400,9 @@ def test_update_decoupled_weight_decay_matches_adamw():
     wd = 0.01 * math.cos(math.radians(28.4))
     oracle.sparse_update(st, G, rows, np.array([0, 1], np.int32), None, weight_decay=wd, **HP)
     w1 = _rebuild(st)
+    m_before, v_before = before.moments()
     for k, r in enumerate(rows):
-        m0 = oracle.f16_to_f32(before.m[k])
-        v0 = oracle.f16_to_f32(before.v[k])
-        wt, _, _ = _torch_adam(w0[r], G[k], m0, v0, int(before.t[k]), wd=wd, **HP)
+        wt, _, _ = _torch_adam(w0[r], G[k], m_before[k], v_before[k], int(before.t[k]), wd=wd, **HP)
         assert np.all(np.abs(w1[r] - wt) <= 2 * np.spacing(np.abs(wt)) + 1e-6 * HP["lr"])
 
 
@@ -435,7 +434,7 @@ def test_update_leaves_inactive_rows_and_slots_untouched():
     assert np.array_equal(st.s[others], before.s[others])
     free = np.setdiff1d(np.arange(8), [1, 4, 6])
     assert np.array_equal(st.m[free], before.m[free]) and np.array_equal(st.v[free], before.v[free])
-    assert np.array_equal(st.t[free], before.t[free])
+    assert np.array_equal(st.t[free], before.t[free]) and np.array_equal(st.e[free], before.e[free])
 
 
 def test_update_fresh_slot_ignores_stale_moments():
@@ -446,10 +445,11 @@ def test_update_fresh_slot_ignores_stale_moments():
     b.m[:] = 0
     b.v[:] = 0
     b.t[:] = 0
+    b.e[:] = 0
     G = synth.gradient_rows(1, Cc, 0.1, 62)
     oracle.sparse_update(a, G, rows, np.array([0], np.int32), np.array([1], np.uint8), **HP)
     oracle.sparse_update(b, G, rows, np.array([0], np.int32), None, **HP)
-    for x, y in ((a.q, b.q), (a.s, b.s), (a.delta, b.delta), (a.m, b.m), (a.v, b.v), (a.t, b.t)):
+    for x, y in ((a.q, b.q), (a.s, b.s), (a.delta, b.delta), (a.m, b.m), (a.v, b.v), (a.t, b.t), (a.e, b.e)):
         assert np.array_equal(x, y)
 
 
@@ -461,6 +461,90 @@ def test_update_zero_row_edge():
     oracle.sparse_update(st, np.zeros((1, Cc), np.float32), np.array([3], np.int32),
                          np.array([0], np.int32), None, **HP)
     assert st.s[3] == 0 and not st.q[3].any() and not st.delta[3].any()
+
+
+# ---------------------------------------------------------------- scaled fp16 moment rows
+
+
+def test_moment_row_maximum_lands_in_the_top_binade():
+    """A stored row's largest moment is an fp16 value in [2^14, 2^15] whatever
+    the row's magnitude (numpy's float16 decodes the stored bits)."""
+    g = synth.rng(80)
+    for amax in np.concatenate([[1.0, 2.0 ** -20, 3.0e4, 1e-30, 5e30],
+                                np.exp(g.uniform(-60, 60, 200))]).astype(np.float32):
+        e = oracle.moment_exponent(amax)
+        h = oracle.moment_encode(np.array([amax, -amax], np.float32), e)
+        top = np.abs(h.view(np.float16).astype(np.float64))
+        assert np.all((2.0 ** 14 <= top) & (top <= 2.0 ** 15)), (amax, e, top)
+    assert oracle.moment_exponent(0.0) == 0
+
+
+def test_moment_encoding_is_fp16_of_the_power_of_two_scaled_value():
+    """Encode and decode against numpy's float16 rounding of x * 2^e (round to
+    nearest even), with saturation at 65504 where numpy overflows to inf."""
+    g = synth.rng(81)
+    x = (g.standard_normal(4000) * np.exp(g.uniform(-20, 10, 4000))).astype(np.float32)
+    for e in (-30, -5, 0, 7, 19, 60):
+        scaled = x.astype(np.float64) * 2.0 ** e
+        with np.errstate(over="ignore"):
+            want = scaled.astype(np.float16)
+            want = np.where(np.isinf(want), np.copysign(np.float16(65504), scaled), want).astype(np.float16)
+        got = oracle.moment_encode(x, e)
+        assert np.array_equal(got, want.view(np.uint16)), e
+        back = oracle.moment_decode(got, e)
+        assert np.array_equal(back, (want.astype(np.float64) * 2.0 ** -e).astype(np.float32))
+
+
+def _adam_fp32_displacement(g, steps, **hp):
+    """Displacement of a weight row after `steps` Adam steps with fp32 moments
+    (numpy, every operation rounded to fp32)."""
+    f = np.float32
+    b1, b2, lr, eps = f(hp["beta1"]), f(hp["beta2"]), f(hp["lr"]), f(hp["eps"])
+    m = np.zeros_like(g)
+    v = np.zeros_like(g)
+    d = np.zeros(g.shape, np.float64)
+    for t in range(1, steps + 1):
+        m = b1 * m + (f(1) - b1) * g
+        v = b2 * v + (f(1) - b2) * (g * g)
+        bc1 = f(1.0 - float(b1) ** t)
+        bc2 = f(1.0 - float(b2) ** t)
+        d += lr * ((m / bc1) / (np.sqrt(v / bc2) + eps))
+    return d
+
+
+@pytest.mark.parametrize("gmag", [1e-5, 1e-3, 300.0])
+def test_thousand_steps_follow_fp32_moment_adam(gmag):
+    """With the moments stored as scaled fp16 rows, 1000 steps on a constant
+    gradient move every weight within 2% of what Adam with fp32 moments moves
+    it, at gradients far below and far above fp16's comfortable range (plain
+    fp16 moments move the |g| = 1e-5 and 1e-3 rows about 17x too far, and
+    overflow v to infinity near |g| = 300 after a few thousand steps)."""
+    R, Cc, steps = 32, 64, 1000
+    g = synth.rng(82)
+    grad = (gmag * np.where(g.random(Cc) < 0.5, -1.0, 1.0) * g.uniform(0.5, 1.0, Cc)).astype(np.float32)
+    st = _state(R, Cc, 83, 1, False)
+    st.s[5] = np.float32(1.0)           # a weight row of order 1 keeps the displacement visible
+    rows, slot = np.array([5], np.int32), np.array([0], np.int32)
+    w0 = _rebuild(st)[5].astype(np.float64)
+    for _ in range(steps):
+        oracle.sparse_update(st, grad[None, :], rows, slot, None, **HP)
+    got = w0 - _rebuild(st)[5].astype(np.float64)
+    want = _adam_fp32_displacement(grad, steps, **HP)
+    assert np.all(np.abs(got / want - 1.0) <= 0.02), (gmag, np.abs(got / want - 1.0).max())
+    m, v = st.moments()
+    assert np.all(np.isfinite(m)) and np.all(np.isfinite(v)) and np.all(v > 0)
+
+
+def test_huge_gradient_moments_saturate_nowhere_and_stay_finite():
+    R, Cc = 32, 16
+    st = _state(R, Cc, 84, 1, False)
+    grad = np.full((1, Cc), 3.0e4, np.float32)
+    grad[0, ::2] *= -1
+    for _ in range(20):
+        oracle.sparse_update(st, grad, np.array([2], np.int32), np.array([0], np.int32), None, **HP)
+    m, v = st.moments()
+    assert np.all(np.isfinite(v)) and np.all(np.abs(v - 9.0e8 * (1 - 0.999 ** 20)) <= 1e-3 * 9.0e8)
+    assert np.all(np.abs(np.abs(m) - 3.0e4 * (1 - 0.9 ** 20)) <= 1e-3 * 3.0e4)
 
 
 def test_bias_table_closed_form():
@@ -490,7 +574,7 @@ def _pair_inputs(seed, R=64, Cc=32):
 def _same(x: oracle.MatState, y: oracle.MatState):
     return all(np.array_equal(a, b) for a, b in
                ((x.q, y.q), (x.s, y.s), (x.delta, y.delta), (x.m, y.m), (x.v, y.v), (x.t, y.t),
-                (x.w_live, y.w_live)))
+                (x.e, y.e), (x.w_live, y.w_live)))
 
 
 def test_coupled_without_cross_term_is_two_plain_updates():

@@ -170,9 +170,9 @@ def test_every_copy_and_restore_respects_the_rise_bound_on_long_runs():
 
 def _state(R_, C, n_slots, seed):
     q, s, delta = synth.quant_state(R_, C, seed)
-    m, v, t = synth.moments(n_slots, C, seed + 1, mid_run=True)
+    m, v, t, e = synth.moments(n_slots, C, seed + 1, mid_run=True)
     w = np.zeros((R_, C), np.uint16)
-    return oracle.MatState(q, s, delta, m, v, t, w)
+    return oracle.MatState(q, s, delta, m, v, t, w, e=e)
 
 
 def test_rows_save_restore_round_trip():
@@ -189,12 +189,14 @@ def test_rows_save_restore_round_trip():
     st.m[:] = 7
     st.v[:] = 9
     st.t[:] = 99
+    st.e[:] = -3
     rw.rows_restore(st, ck, rows, slot)
     assert np.array_equal(st.q[rows], before.q[rows])
     assert np.array_equal(st.s[rows], before.s[rows])
     assert np.array_equal(st.delta[rows].view(np.uint32), before.delta[rows].view(np.uint32))
     assert np.array_equal(st.m[slot], before.m[slot]) and np.array_equal(st.v[slot], before.v[slot])
-    assert np.array_equal(st.t[slot], before.t[slot])
+    assert np.array_equal(st.t[slot], before.t[slot]) and np.array_equal(st.e[slot], before.e[slot])
+    assert np.all(np.delete(st.e, slot, axis=0) == -3)
     others = np.setdiff1d(np.arange(40), rows)
     assert np.all(st.q[others] == 0) and np.all(st.s[others] == 1.0)
     assert np.all(np.delete(st.m, slot, axis=0) == 7)
