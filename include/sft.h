@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 9
+#define SFT_ABI_VERSION 10
 
 enum {
     SFT_OK = 0,
@@ -179,37 +179,54 @@ int sft_slots_update(int32_t *row_slot, int64_t rows, int64_t n_slots,
 int sft_bias_table(float beta1, float beta2, int32_t t_max, float *bc1, float *bc2);
 
 /*
- * Checkpoint-and-rewind controller (section 2.6).  A copy of the active rows
- * is refreshed while the loss stays close (10%) to the loss of the last copy;
- * each new lowest loss is watched for 10 steps, and a loss more than 15%
- * above it when the watch ends brings the copy back, restarts the phase
- * stride at 1 and drops the step (up to 3 times for one minimum); a minimum
- * that survives its watch becomes the reference for later copies.
- * Readings of the prose, exactly as implemented (loss = the loss the caller
- * has for the latest step, a double; comparisons in double):
- *   - save when there is no checkpoint yet or
- *     loss <= (1 + save_within) * checkpoint_loss; a save sets
- *     checkpoint_loss = loss;
- *   - a new minimum is a loss below every loss seen so far (min_loss); it
- *     sets watch_left = watch_steps and recoveries = 0;
- *   - each later step decrements watch_left; the step that brings it to 0
- *     ends the watch: if loss > (1 + rise_above) * min_loss and
- *     recoveries < max_recoveries, the action is SFT_REWIND_RESTORE,
- *     recoveries grows by one and the watch re-opens on the same minimum
- *     (nothing else happens on that step: it is skipped); in every other
- *     case the minimum stands (checkpoint_loss = min_loss, watch closed) and
- *     the step goes on;
- *   - order within a step: end of watch, then new minimum, then save;
+ * Checkpoint-and-rewind controller (section 2.6; section 4.2 reports its one
+ * rewind: at step 356 the loss had rebounded past the threshold and the
+ * checkpoint of step 336 came back).  Two row copies are kept: the checkpoint
+ * (what a restore brings back) and the copy of the lowest loss so far (the
+ * minimum), which becomes the checkpoint once the minimum is accepted.  Each
+ * new minimum is watched for 10 steps; a loss more than 15% above it when the
+ * watch ends brings the checkpoint back, restarts the phase stride at 1 and
+ * drops the step (up to 3 times for one minimum); otherwise the minimum is
+ * accepted and becomes the checkpoint.  Outside a watch the checkpoint is
+ * refreshed while the loss stays within 10% of the checkpoint's loss.
+ * Readings of the prose, exactly as implemented (loss = the loss the rows
+ * held by the caller produced, a double; comparisons in double; the step
+ * counter k counts observations from 0):
+ *   - the end of a watch comes first: each step decrements watch_left; the
+ *     step that brings it to 0 ends the watch: if loss > (1 + rise_above) *
+ *     min_loss and recoveries < max_recoveries, the action is
+ *     SFT_REWIND_RESTORE alone, recoveries grows by one and the watch
+ *     re-opens on the same minimum (the step is dropped: nothing else
+ *     happens on it); otherwise the minimum is accepted (SFT_REWIND_PROMOTE:
+ *     checkpoint_loss = min_loss, checkpoint_step = min_step);
+ *   - then a new minimum, a loss below every loss seen so far: if a watch is
+ *     still open its minimum is accepted first (SFT_REWIND_PROMOTE: the loss
+ *     fell below it, so it did not rise); then min_loss = loss, min_step = k,
+ *     watch_left = watch_steps, recoveries = 0, action SFT_REWIND_SAVE_MIN;
+ *   - then the refresh, SFT_REWIND_SAVE (checkpoint_loss = loss,
+ *     checkpoint_step = k): when there is no checkpoint yet, or when no watch
+ *     is open, loss <= (1 + save_within) * checkpoint_loss and
+ *     loss <= (1 + rise_above) * min_loss;
  *   - a NaN or infinite loss counts as +infinity: never a minimum, never
- *     saved, always a rise.
+ *     copied, always a rise.
+ * The caller keeps two copy buffers (sft_ckpt_mat) and applies a step's
+ * bits before the step's update, in this order: SFT_REWIND_PROMOTE (the
+ * minimum's buffer, with its row list, becomes the checkpoint's and the old
+ * checkpoint buffer becomes the minimum's: no copy is made),
+ * SFT_REWIND_SAVE_MIN (sft_rows_save of the active rows into the minimum's
+ * buffer), SFT_REWIND_SAVE (sft_rows_save into the checkpoint's buffer).  On
+ * SFT_REWIND_RESTORE it calls sft_rows_restore with the checkpoint's buffer,
+ * resets its phase stride to 1 and does not apply the step's update.
  * sft_rewind_init sets the page's values (0.10, 0.15, 10 steps, 3 recoveries)
  * and an empty state; the settings may be changed before the first
- * observation.  On SFT_REWIND_RESTORE the caller restores the rows saved last
- * (sft_rows_restore), resets its phase stride to 1 and does not apply the
- * step's update; on SFT_REWIND_SAVE it saves the active rows (sft_rows_save)
- * after the step's update.
+ * observation.
  */
-enum { SFT_REWIND_SAVE = 1, SFT_REWIND_RESTORE = 2 };
+enum {
+    SFT_REWIND_SAVE = 1,      /* copy the rows into the checkpoint              */
+    SFT_REWIND_RESTORE = 2,   /* bring the checkpoint back, drop the step       */
+    SFT_REWIND_SAVE_MIN = 4,  /* copy the rows into the minimum's copy          */
+    SFT_REWIND_PROMOTE = 8    /* the minimum's copy becomes the checkpoint      */
+};
 
 typedef struct sft_rewind {
     double save_within;       /* 0.10 */
@@ -221,15 +238,18 @@ typedef struct sft_rewind {
     int32_t watch_left;       /* 0 = no watch open */
     int32_t recoveries;       /* restores since the current minimum */
     int32_t reserved;
-    double checkpoint_loss;
+    double checkpoint_loss;   /* loss of the rows the checkpoint holds */
     double min_loss;          /* +inf before the first finite loss */
+    int64_t step;             /* observations so far */
+    int64_t checkpoint_step;  /* step whose rows the checkpoint holds (-1: none) */
+    int64_t min_step;         /* step whose rows the minimum's copy holds (-1: none) */
 } sft_rewind;
 
 /* Errors: SFT_EINVAL (null). */
 int sft_rewind_init(sft_rewind *st);
 
 /*
- * Feeds one step's loss; *action = 0, SFT_REWIND_SAVE or SFT_REWIND_RESTORE.
+ * Feeds one step's loss; *action = an OR of the SFT_REWIND_* bits (0 = none).
  * Errors: SFT_EINVAL (null pointers, save_within or rise_above negative or
  * NaN, watch_steps < 1, max_recoveries < 0); the state is then unchanged.
  */

@@ -92,7 +92,8 @@ class CRewind(C.Structure):
     _fields_ = [("save_within", C.c_double), ("rise_above", C.c_double), ("watch_steps", C.c_int32),
                 ("max_recoveries", C.c_int32), ("has_checkpoint", C.c_int32), ("watch_left", C.c_int32),
                 ("recoveries", C.c_int32), ("reserved", C.c_int32), ("checkpoint_loss", C.c_double),
-                ("min_loss", C.c_double)]
+                ("min_loss", C.c_double), ("step", C.c_int64), ("checkpoint_step", C.c_int64),
+                ("min_step", C.c_int64)]
 
 
 class CCkptMat(C.Structure):
@@ -543,12 +544,14 @@ def prepare_masked_writeback_many(mats) -> Prepared:
 # ------------------------------------------------------------------ checkpoint and rewind
 SFT_REWIND_SAVE = 1
 SFT_REWIND_RESTORE = 2
+SFT_REWIND_SAVE_MIN = 4
+SFT_REWIND_PROMOTE = 8
 
 
 class Rewind:
-    """Section 2.6 controller (host, C library): observe(loss) -> 0,
-    SFT_REWIND_SAVE or SFT_REWIND_RESTORE.  ``st`` is the C state (its
-    settings may be changed before the first observation)."""
+    """Section 2.6 controller (host, C library): observe(loss) -> an OR of
+    the SFT_REWIND_* bits.  ``st`` is the C state (its settings may be
+    changed before the first observation)."""
 
     def __init__(self):
         self.st = CRewind()

@@ -233,8 +233,20 @@ int sft_rewind_init(sft_rewind *st) {
     st->watch_steps = 10;
     st->max_recoveries = 3;
     st->min_loss = HUGE_VAL;
+    st->checkpoint_step = -1;
+    st->min_step = -1;
     return SFT_OK;
 }
+
+namespace {
+// The minimum's copy becomes the checkpoint, with the minimum's loss.
+int32_t rewind_accept(sft_rewind *st) {
+    st->has_checkpoint = 1;
+    st->checkpoint_loss = st->min_loss;
+    st->checkpoint_step = st->min_step;
+    return SFT_REWIND_PROMOTE;
+}
+}  // namespace
 
 int sft_rewind_observe(sft_rewind *st, double loss, int32_t *action) {
     clear_error();
@@ -244,27 +256,37 @@ int sft_rewind_observe(sft_rewind *st, double loss, int32_t *action) {
     SFT_CHECK(st->watch_steps >= 1 && st->max_recoveries >= 0, SFT_EINVAL,
               "rewind_observe: watch_steps < 1 or max_recoveries < 0");
     const double x = std::isfinite(loss) ? loss : HUGE_VAL;
-    *action = 0;
+    const int64_t k = st->step++;
+    int32_t act = 0;
+    // the end of an open watch
     if (st->watch_left > 0 && --st->watch_left == 0) {
-        // the watch on min_loss ends with this step
         if (x > (1.0 + st->rise_above) * st->min_loss && st->recoveries < st->max_recoveries) {
             ++st->recoveries;
             st->watch_left = st->watch_steps;
             *action = SFT_REWIND_RESTORE;
             return SFT_OK;
         }
-        st->checkpoint_loss = st->min_loss;
+        act |= rewind_accept(st);
     }
+    // a new minimum; one still being watched is accepted first
     if (x < st->min_loss) {
+        if (st->watch_left > 0) act |= rewind_accept(st);
         st->min_loss = x;
+        st->min_step = k;
         st->watch_left = st->watch_steps;
         st->recoveries = 0;
+        act |= SFT_REWIND_SAVE_MIN;
     }
-    if (x != HUGE_VAL && (!st->has_checkpoint || x <= (1.0 + st->save_within) * st->checkpoint_loss)) {
+    // the refresh: never during a watch, never above the rise bound
+    if (x != HUGE_VAL &&
+        (!st->has_checkpoint || (st->watch_left == 0 && x <= (1.0 + st->save_within) * st->checkpoint_loss &&
+                                 x <= (1.0 + st->rise_above) * st->min_loss))) {
         st->has_checkpoint = 1;
         st->checkpoint_loss = x;
-        *action = SFT_REWIND_SAVE;
+        st->checkpoint_step = k;
+        act |= SFT_REWIND_SAVE;
     }
+    *action = act;
     return SFT_OK;
 }
 

@@ -32,11 +32,35 @@ def _random_losses(seed, n):
 def test_library_controller_matches_the_pins():
     cases = [[10.0, 9.0, 8.0, 7.0], [10.0, 8.0] + [8.5] * 9 + [9.3],
              [10.0, 8.0] + [8.5] * 9 + [9.3] + [9.3] * 40,
-             [10.0, 8.0] + [9.0] * 5 + [7.0] + [9.0] * 10, [10.0, float("nan")] + [math.inf] * 9]
+             [10.0, 8.0] + [8.5] * 9 + [9.1, 8.7, 9.5, 8.0],
+             [10.0, 8.0] + [9.0] * 5 + [7.0] + [9.0] * 10, [10.0, float("nan")] + [math.inf] * 9,
+             [math.inf, 5.0]]
     for losses in cases:
         want = _run(losses)
         ctl = _lib.Rewind()
         assert [ctl.observe(x) for x in losses] == want
+
+
+def test_library_controller_reproduces_the_page_rewind():
+    """Section 4.2's event: the first restore of the run comes at step 356
+    and brings back the checkpoint of step 336."""
+    losses = [6.17 * math.exp(-0.00322 * k) for k in range(336)]
+    l336 = losses[-1] * 0.99
+    l346 = l336 * 0.98
+    losses += [l336] + [l336 * 1.03] * 9 + [l346] + [l346 * 1.05] * 9 + [l346 * 1.2]
+    c = _lib.Rewind()
+    acts = [c.observe(x) for x in losses]
+    assert acts.index(_lib.SFT_REWIND_RESTORE) == 356
+    assert c.state().checkpoint_step == 336 and c.state().min_step == 346
+
+
+def _fields(c, o):
+    st = c.state()
+    got = (st.has_checkpoint, st.watch_left, st.recoveries, st.checkpoint_loss, st.min_loss, st.step,
+           st.checkpoint_step, st.min_step)
+    want = (int(o.has_checkpoint), o.watch_left, o.recoveries, o.checkpoint_loss, o.min_loss, o.step,
+            o.checkpoint_step, o.min_step)
+    return got, want
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
@@ -44,12 +68,15 @@ def test_library_controller_matches_oracle_on_long_runs(seed):
     losses = _random_losses(seed, 3000)
     o = rw.Rewind()
     c = _lib.Rewind()
+    seen = set()
     for x in losses:
-        assert c.observe(x) == o.observe(x)
-        st = c.state()
-        assert (st.has_checkpoint, st.watch_left, st.recoveries) == (int(o.has_checkpoint), o.watch_left,
-                                                                     o.recoveries)
-        assert st.checkpoint_loss == o.checkpoint_loss and st.min_loss == o.min_loss
+        a = c.observe(x)
+        assert a == o.observe(x)
+        seen.add(a)
+        got, want = _fields(c, o)
+        assert got == want
+    # the runs exercise every kind of step
+    assert {0, rw.RESTORE, rw.PROMOTE, rw.PROMOTE | rw.SAVE_MIN, rw.SAVE} <= seen
 
 
 def test_library_controller_rejects_bad_settings():
