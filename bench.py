@@ -1,20 +1,29 @@
 """Benchmark of the sparse-first step on one MI355X.
 
-Workload: one Llama-7B-shaped decoder layer (q, k, v, o 4096x4096; gate, up
-11008x4096; down 4096x11008), 4096 tokens, bf16 X ~ N(0,1) and dY ~ N(0,0.01),
-row-tracker masks from seeded output magnitudes with 1% of each matrix's rows
-active (clustered in 32-row tiles), int8 q + fp32 residual resident, fp16
-moments for the active rows.  One step = the masked dW of all seven
-matrices (one launch; q/k/v and gate/up share their input) and the sparse
-update with fused write-back of all seven (one launch), every input (the
-packed plan included) resident in HBM when the timed region starts.  The same
-steps with the plan's host->device copy in front of each are timed too and
-reported beside the value (PCIe-inclusive, never the value).  Method: "Sparse-First Fine-Tuning: Full-Weight
-Training at the Cost of the Active Set", sections 2.1-2.3.
+Headline workload: one Llama-7B-shaped decoder layer (q, k, v, o 4096x4096;
+gate, up 11008x4096; down 4096x11008), 4096 tokens, bf16 X ~ N(0,1) and
+dY ~ N(0,0.01), row-tracker masks from seeded output magnitudes with 1% of
+each matrix's rows active (clustered in 32-row tiles), int8 q + fp32 residual
+resident, scaled fp16 moments for the active rows.  One step = the copy of
+the step's packed plan (active rows, tiles, slots; a few KB made on the host,
+section 2.6 and Figure 2 of the page) to the device, then the masked dW of
+all seven matrices and the sparse update with fused write-back of all seven
+(one call, sft_masked_dw_update).  Every other input (activations, output
+gradients, optimizer state) is resident in HBM when the timed region starts.
+The same steps with the plan already resident are reported beside the value.
+Method: "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the
+Active Set", sections 2.1-2.6.
 
 Steps cycle through a ring of distinct layers (like the layers of one model
 step), so that every step reads its inputs from HBM rather than from the
 256 MB last-level cache.
+
+Besides the headline, the JSON line carries (``rows``) the other workloads
+timed as steps: the 512x512 projection (10% rows), the whole 7B-shaped model
+(32 distinct layers plus the 32000x4096 embedding) at 0.5%, 1%, 2% and 5%
+rows, the adversarial one-row-per-tile layer with the coupled update, and the
+separate calls of the path; the oracle timed on the host on one thread and on
+several; the a1 host calls timed alone.
 
 Prints one JSON line (rank 0).  ``--gpus`` above 1 is refused: this build
 measures one GPU.
@@ -25,6 +34,7 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -37,6 +47,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 COUNTERS_SUMMARY = "masked_dw_llama7b_layer_1pct_counters.txt"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HP = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+CPU_THREADS = 16               # the host share of one GPU on the box
 
 
 def parse_args():
@@ -44,6 +56,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--block", type=int, default=10,
+                    help="steps between the timing events whose block means give the median and percentiles")
     ap.add_argument("--layers", type=int, default=6, help="ring of distinct layers cycled by the steps")
     ap.add_argument("--density", type=float, default=0.01)
     ap.add_argument("--layout", choices=["packed", "tiles"], default="packed",
@@ -52,14 +66,13 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="step with sft_masked_dw + sft_sparse_update instead of the fused sft_masked_dw_update")
-    ap.add_argument("--cpu-sample-every", type=int, default=4,
-                    help="oracle timing uses every n-th active row of each matrix")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the timings of the other hot-path calls (embedding, coupled pairs, write-back, "
-                         "checkpoint)")
+                    help="skip the other workloads and calls (model step, adversarial step, embedding, ...)")
     ap.add_argument("--rows-only", action="store_true",
-                    help="time only the other hot-path calls (prints their JSON object), for profiling them apart "
+                    help="time only the other calls (prints their JSON object), for profiling them apart "
                          "from the layer step")
+    ap.add_argument("--no-model", action="store_true", help="skip the 32-layer model step")
+    ap.add_argument("--model-steps", type=int, default=10)
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probes of the HBM and matrix-core rates this device sustains")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -67,28 +80,63 @@ def parse_args():
     return ap.parse_args()
 
 
-class Layer:
-    """Device buffers, plans and prepared launches of one layer."""
+# ---------------------------------------------------------------------- workloads
+def _mask_plan(R, k, seed, clustered=True):
+    """Row-tracker mask with exactly k hot rows (clustered in 32-row tiles)."""
+    from sparse_full_weight_amd import _lib, synth
+    hot = synth.clustered_rows(R, k, seed)
+    mag = synth.tracker_magnitudes(R, hot, seed + 1)
+    return _lib.sft_plan_rows(_lib.sft_tracker_window(np.zeros(R, np.float32), mag))
 
-    def __init__(self, idx: int, T: int, density: float, seed0: int, layout: str = "packed"):
+
+def layer_buffers(T, seed, dev="cuda", shapes=None, groups=None):
+    """Activations, output gradients and resident state of one layer, drawn
+    on the device (torch's seeded generator)."""
+    import torch
+
+    from sparse_full_weight_amd import synth
+    shapes = shapes or synth.LLAMA7B
+    groups = groups or synth.LLAMA7B_GROUPS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 7)
+    X = {}
+    for gi, (gname, members) in enumerate(groups):
+        X[gname] = synth.normal_bf16_device((T, shapes[members[0]][1]), 1.0, seed + 1000 + gi, dev)
+    mats = {}
+    for mi, (name, (R, C)) in enumerate(shapes.items()):
+        m = {"R": R, "C": C, "dY": synth.normal_bf16_device((T, R), 0.01, seed + 2000 + mi, dev),
+             "q": torch.randint(-127, 128, (R, C), dtype=torch.int8, device=dev, generator=gen),
+             "s": torch.empty(R, dtype=torch.float32, device=dev).uniform_(1e-4, 1e-3, generator=gen),
+             "w_live": torch.zeros((R, C), dtype=torch.bfloat16, device=dev)}
+        m["delta"] = (torch.rand((R, C), dtype=torch.float32, device=dev, generator=gen) - 0.5) * m["s"][:, None]
+        mats[name] = m
+    return X, mats
+
+
+class Layer:
+    """Plans, moments and prepared launches of one layer over its buffers."""
+
+    def __init__(self, idx: int, T: int, density: float, seed0: int, layout: str = "packed", buffers=None,
+                 rows=None, shapes=None, groups=None):
         import torch
 
         from sparse_full_weight_amd import _lib, synth
         self.idx = idx
         self.density = density
+        self.T = T
         dev = "cuda"
         seed = seed0 + 100 * idx
-        shapes = synth.LLAMA7B
+        self.shapes = shapes or synth.LLAMA7B
+        self.groups_def = groups or synth.LLAMA7B_GROUPS
+        X, bufs = buffers if buffers is not None else layer_buffers(T, seed, dev, self.shapes, self.groups_def)
+        self.X = X
         self.mats = {}
-        host_chunks = []   # packed plan: int32 words, uploaded once per step
-        offsets = {}      # per matrix: word offset and length of each plan part
-        off = 0
-        for mi, (name, (R, C)) in enumerate(shapes.items()):
-            k = round(density * R)
-            hot = synth.clustered_rows(R, k, seed + 10 * mi + 1)
-            mag = synth.tracker_magnitudes(R, hot, seed + 10 * mi + 2)
-            mask = _lib.sft_tracker_window(np.zeros(R, np.float32), mag)
-            plan = _lib.sft_plan_rows(mask)
+        host_chunks, offsets, off = [], {}, 0
+        for mi, (name, (R, C)) in enumerate(self.shapes.items()):
+            if rows is not None:
+                plan = _lib.sft_plan_rows(synth.mask_from_rows(R, rows[name]))
+            else:
+                plan = _mask_plan(R, round(density * R), seed + 10 * mi + 1)
             row_slot = np.full(R, -1, np.int32)
             slot, fresh = _lib.sft_slots_update(row_slot, plan.n_active, plan.active_rows)
             fresh[:] = 0          # steady state: the moments already exist
@@ -100,49 +148,40 @@ class Layer:
                 offsets[name][key] = (off, arr.size)
                 host_chunks.append(arr.astype(np.int32, copy=False))
                 off += arr.size
-            self.mats[name] = {"R": R, "C": C, "plan": plan}
+            self.mats[name] = dict(bufs[name], plan=plan)
         packed = np.concatenate(host_chunks) if host_chunks else np.zeros(1, np.int32)
         self.plan_host = torch.from_numpy(packed).pin_memory()
         self.plan_dev = torch.empty_like(self.plan_host, device=dev)
         self.plan_dev.copy_(self.plan_host)
-
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(seed + 7)
-        self.X = {}
-        for gname, members in synth.LLAMA7B_GROUPS:
-            C = shapes[members[0]][1]
-            self.X[gname] = synth.normal_bf16_device((T, C), 1.0, seed + 1000 + len(self.X), dev)
         bc1, bc2 = _lib.sft_bias_table(0.9, 0.999, 20000)
-        self.hp = _lib.Adam(1e-4, 0.9, 0.999, 1e-8, torch.from_numpy(bc1).to(dev), torch.from_numpy(bc2).to(dev))
+        self.hp = _lib.Adam(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], torch.from_numpy(bc1).to(dev),
+                            torch.from_numpy(bc2).to(dev))
         groups, upd = [], []
-        for gi, (gname, members) in enumerate(synth.LLAMA7B_GROUPS):
+        self.views = {}
+        for gname, members in self.groups_def:
             dw_mats = []
             for name in members:
                 m = self.mats[name]
-                R, C, plan = m["R"], m["C"], m["plan"]
+                C, plan = m["C"], m["plan"]
                 lay = offsets[name]
 
-                def view(key, n=None, dtype=None):
+                def view(key, n=None, dtype=None, lay=lay):
                     o, sz = lay[key]
                     t = self.plan_dev[o:o + sz]
                     if dtype is not None:
                         t = t.view(dtype)[: n]
                     return t
-                dplan = _lib.DevicePlan(plan, view("rows"), view("tiles"), view("abits"), view("first"))
-                m["dY"] = synth.normal_bf16_device((T, R), 0.01, seed + 2000 + R + len(dw_mats) + 17 * gi, dev)
                 n = plan.n_active
-                m["dW"] = torch.empty((n, C), dtype=torch.float32, device=dev)
-                dw_mats.append(_lib.DwMat(m["dY"], dplan, m["dW"]))
-                # resident state
-                m["q"] = torch.randint(-127, 128, (R, C), dtype=torch.int8, device=dev, generator=gen)
-                m["s"] = torch.empty(R, dtype=torch.float32, device=dev).uniform_(1e-4, 1e-3, generator=gen)
-                m["delta"] = (torch.rand((R, C), dtype=torch.float32, device=dev, generator=gen) - 0.5) * m["s"][:, None]
-                m["w_live"] = torch.zeros((R, C), dtype=torch.bfloat16, device=dev)
+                self.views[name] = {"rows": view("rows"), "slot": view("slot")}
+                dplan = _lib.DevicePlan(plan, view("rows"), view("tiles"), view("abits"), view("first"))
+                m["dW"] = torch.empty((max(n, 1), C), dtype=torch.float32, device=dev)
+                dw_mats.append(_lib.DwMat(m["dY"], dplan, m["dW"][:n]))
                 m["m"] = torch.zeros((n, C), dtype=torch.int16, device=dev)
                 m["v"] = torch.zeros((n, C), dtype=torch.int16, device=dev)
                 m["t"] = torch.zeros(n, dtype=torch.int32, device=dev)
-                upd.append(_lib.UpdMat(m["q"], m["s"], m["delta"], m["m"], m["v"], m["t"], view("rows"),
-                                       view("slot"), m["dW"], n, view("fresh", n, torch.uint8), m["w_live"]))
+                m["e"] = torch.zeros((n, 2), dtype=torch.int8, device=dev)
+                upd.append(_lib.UpdMat(m["q"], m["s"], m["delta"], m["m"], m["v"], m["t"], m["e"], view("rows"),
+                                       view("slot"), m["dW"][:n], n, view("fresh", n, torch.uint8), m["w_live"]))
             groups.append(_lib.DwGroup(self.X[gname], dw_mats,
                                        _lib.SFT_DW_PACKED if layout == "packed" else _lib.SFT_DW_TILES))
         self.groups = groups
@@ -153,15 +192,17 @@ class Layer:
         self.upd_call = _lib.prepare_sparse_update(upd, self.hp)
         # the update matrices follow the groups' matrices in order
         self.fused_call = _lib.prepare_masked_dw_update(groups, self.ws, upd, self.hp)
-        self.T = T
 
     def upload_plan(self):
         self.plan_dev.copy_(self.plan_host, non_blocking=True)
 
+    def n_active(self):
+        return int(sum(m["plan"].n_active for m in self.mats.values()))
+
     def dw_work(self):
-        from sparse_full_weight_amd import accounting, synth
+        from sparse_full_weight_amd import accounting
         groups = []
-        for gname, members in synth.LLAMA7B_GROUPS:
+        for gname, members in self.groups_def:
             C = self.mats[members[0]]["C"]
             groups.append((self.T, C, [(self.mats[n]["plan"].n_active, self.mats[n]["plan"].n_active_tiles)
                                        for n in members]))
@@ -172,52 +213,97 @@ class Layer:
         return accounting.update_work([(m["C"], m["plan"].n_active) for m in self.mats.values()])
 
 
-def cpu_baseline(layer: "Layer", every: int):
-    """Time the oracle (plain C, one thread) on every n-th active row of each
-    matrix of one layer: its masked dW rows and their update; scale to the
-    whole layer."""
-    import oracle
+class Embedding:
+    """The 32000 x 4096 embedding: the conductor over four windows of 8 x 512
+    Zipf(1.1) token ids sets the mask; one step uploads the step's plan (active
+    rows, slots, the CSR of token positions), takes the masked scatter-gradient
+    and the sparse update with fused write-back."""
+
+    def __init__(self, seed, hp, dev="cuda"):
+        import torch
+
+        from sparse_full_weight_amd import _lib, synth
+        V, d, Tb = 32000, 4096, 8 * 512
+        self.V, self.d, self.Tb = V, d, Tb
+        ch = np.zeros(V, np.float32)
+        t0 = time.perf_counter()
+        for w in range(4):
+            tokens = synth.zipf_tokens(Tb, V, 1.1, seed + w)
+            mask = _lib.sft_conductor_window(ch, tokens)
+        plan = _lib.sft_plan_rows(mask)
+        row_ptr, pos = _lib.sft_plan_embedding(plan, tokens)
+        self.host_us = (time.perf_counter() - t0) * 1e6
+        n = plan.n_active
+        self.n, self.nnz = n, int(pos.size)
+        slot = np.arange(n, dtype=np.int32)
+        packed = np.concatenate([plan.active_rows, slot, row_ptr, pos]).astype(np.int32)
+        self.plan_host = torch.from_numpy(packed).pin_memory()
+        self.plan_dev = self.plan_host.to(dev)
+        o1, o2, o3 = n, 2 * n, 2 * n + n + 1
+        rows_d, slot_d = self.plan_dev[:o1], self.plan_dev[o1:o2]
+        rp_d, pos_d = self.plan_dev[o2:o3], self.plan_dev[o3:]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed + 20)
+        self.dY = synth.normal_bf16_device((Tb, d), 0.01, seed + 10, dev)
+        self.G = torch.empty((max(n, 1), d), dtype=torch.float32, device=dev)
+        st = {"q": torch.randint(-127, 128, (V, d), dtype=torch.int8, device=dev, generator=gen),
+              "s": torch.empty(V, dtype=torch.float32, device=dev).uniform_(1e-4, 1e-3, generator=gen),
+              "w": torch.zeros((V, d), dtype=torch.bfloat16, device=dev),
+              "m": torch.zeros((n, d), dtype=torch.int16, device=dev),
+              "v": torch.zeros((n, d), dtype=torch.int16, device=dev),
+              "t": torch.zeros(n, dtype=torch.int32, device=dev),
+              "e": torch.zeros((n, 2), dtype=torch.int8, device=dev)}
+        st["delta"] = (torch.rand((V, d), dtype=torch.float32, device=dev, generator=gen) - 0.5) * st["s"][:, None]
+        self.st = st
+        self.emb_call = _lib.prepare_embedding_dw(self.dY, rp_d, pos_d, n, self.G[:n])
+        self.upd_call = _lib.prepare_sparse_update(
+            [_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], st["e"], rows_d, slot_d,
+                         self.G[:n], n, None, st["w"])], hp)
+
+    def upload_plan(self):
+        self.plan_dev.copy_(self.plan_host, non_blocking=True)
+
+    def step(self, stream):
+        self.upload_plan()
+        self.emb_call(stream)
+        self.upd_call(stream)
+
+    def work(self):
+        from sparse_full_weight_amd import accounting
+        return (accounting.embedding_dw_work(self.d, self.nnz, self.n).bytes
+                + accounting.update_work([(self.d, self.n)]).bytes)
+
+
+# ---------------------------------------------------------------------- timing
+def _ev():
     import torch
-
-    from sparse_full_weight_amd import synth
-    t_total = 0.0
-    rows_done = rows_all = 0
-    for gname, members in synth.LLAMA7B_GROUPS:
-        Xb = layer.X[gname].view(torch.int16).cpu().numpy().view(np.uint16)
-        for name in members:
-            m = layer.mats[name]
-            plan = m["plan"]
-            rows = plan.active_rows[::every].copy()
-            dY = m["dY"].view(torch.int16).cpu().numpy().view(np.uint16)
-            R, C = m["R"], m["C"]
-            sub = np.searchsorted(plan.active_rows, rows)
-            q = m["q"].cpu().numpy()
-            s = m["s"].cpu().numpy()
-            delta = m["delta"].cpu().numpy()
-            st = oracle.MatState(q, s, delta, np.zeros((rows.size, C), np.uint16), np.zeros((rows.size, C), np.uint16),
-                                 np.zeros(rows.size, np.int32), np.zeros((R, C), np.uint16))
-            t0 = time.perf_counter()
-            G = oracle.masked_dw(dY, Xb, rows)
-            oracle.sparse_update(st, G, rows, np.arange(rows.size, dtype=np.int32), None, lr=1e-4, beta1=0.9,
-                                 beta2=0.999, eps=1e-8)
-            t_total += time.perf_counter() - t0
-            rows_done += rows.size
-            rows_all += plan.n_active
-            del sub
-    scale = rows_all / max(rows_done, 1)
-    return t_total * scale * 1e3, rows_done, rows_all, t_total
+    return torch.cuda.Event(enable_timing=True)
 
 
-LEAF_DENSITY = 0.001
+def timed_blocks(fn, K: int, block: int, stream):
+    """K calls of fn(i) back to back on `stream`, with an event pair around
+    the whole run and an event between every `block` calls.  Returns the mean
+    ms per call over all K and the block means (ms per call)."""
+    import torch
+    block = max(1, min(block, K))
+    n_blocks = max(1, K // block)
+    K = n_blocks * block
+    evs = [_ev() for _ in range(n_blocks + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for b in range(n_blocks):
+        for j in range(block):
+            fn(b * block + j)
+        evs[b + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[b].elapsed_time(evs[b + 1]) / block for b in range(n_blocks)]
+    return evs[0].elapsed_time(evs[-1]) / K, per
 
 
-def leaf_support(m: int, n: int, seed: int):
-    """SparseLeaf support: round(0.1% of m*n) distinct coordinates, uniform,
-    sorted by (row, column)."""
-    from sparse_full_weight_amd import synth
-    g = synth.rng(seed)
-    flat = np.sort(g.choice(m * n, size=round(LEAF_DENSITY * m * n), replace=False))
-    return (flat // n).astype(np.int32), (flat % n).astype(np.int32)
+def _stats(per):
+    a = np.asarray(per, np.float64)
+    return {"median_ms": round(float(np.median(a)), 5), "p10_ms": round(float(np.percentile(a, 10)), 5),
+            "p90_ms": round(float(np.percentile(a, 90)), 5), "blocks": int(a.size)}
 
 
 def _time_calls(fns, K, stream):
@@ -227,8 +313,7 @@ def _time_calls(fns, K, stream):
         for f in fns:
             f(stream)
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
+    a, b = _ev(), _ev()
     a.record(stream)
     for _ in range(K):
         for f in fns:
@@ -244,19 +329,242 @@ def _hbm(work_bytes, ms):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def other_rows(L0: "Layer", K: int, stream):
-    """Timings of the hot-path calls the layer step does not run: the embedding
-    scatter-gradient and its update, the coupled pair update (with the packed
-    masked dW feeding it) on one-active-row-per-tile masks, the standalone
-    masked write-back, the active-row checkpoint save and restore, the
-    SparseLeaf connection gradients and Adam step, and the layer step at the
-    full step's other row densities (0.5%, 2%, 5%).  Same event bracketing as the step: K back-to-back
-    passes over prepared calls."""
+# ---------------------------------------------------------------------- host side
+def host_plan_us(density: float, reps: int = 30):
+    """The a1 host calls of one layer timed alone (C calls only: the row
+    tracker's window, the row plan and the moment slots of the seven
+    matrices), median over `reps` repetitions; the magnitudes are drawn
+    before the clock starts."""
+    from sparse_full_weight_amd import _lib, synth
+    inputs = []
+    for mi, (name, (R, C)) in enumerate(synth.LLAMA7B.items()):
+        mag = synth.tracker_magnitudes(R, synth.clustered_rows(R, round(density * R), 7 + mi), 8 + mi)
+        inputs.append((R, mag))
+    times = []
+    for _ in range(reps):
+        chs = [np.zeros(R, np.float32) for R, _ in inputs]
+        slots = [np.full(R, -1, np.int32) for R, _ in inputs]
+        t0 = time.perf_counter()
+        for (R, mag), ch, rs in zip(inputs, chs, slots):
+            mask = _lib.sft_tracker_window(ch, mag)
+            plan = _lib.sft_plan_rows(mask)
+            _lib.sft_slots_update(rs, plan.n_active, plan.active_rows)
+        times.append((time.perf_counter() - t0) * 1e6)
+    return {"median_us": round(float(np.median(times)), 1), "p10_us": round(float(np.percentile(times, 10)), 1),
+            "p90_us": round(float(np.percentile(times, 90)), 1), "reps": reps,
+            "calls": "sft_tracker_window + sft_plan_rows + sft_slots_update on the 7 matrices (42,496 rows), "
+                     "through the ctypes binding"}
+
+
+def host_info():
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def cpu_baseline(L0: "Layer", threads: int):
+    """Time the oracle (plain C) on samples of one layer's active rows: their
+    masked dW rows (fp64 sums over the 4096 tokens) and their update, scaled
+    to the whole layer.  Once on one thread (every 8th active row of each
+    matrix) and once on `threads` host threads, each taking a share of the
+    rows (every 2nd active row; the C oracle releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import torch
+    host = {}
+    for gname, members in L0.groups_def:
+        Xb = L0.X[gname].view(torch.int16).cpu().numpy().view(np.uint16)
+        for name in members:
+            m = L0.mats[name]
+            host[name] = (Xb, m["dY"].view(torch.int16).cpu().numpy().view(np.uint16), m["q"].cpu().numpy(),
+                          m["s"].cpu().numpy(), m["delta"].cpu().numpy())
+
+    def rows_work(name, rows):
+        Xb, dY, q, s, delta = host[name]
+        C = q.shape[1]
+        st = oracle.MatState(q[rows], s[rows], delta[rows], np.zeros((rows.size, C), np.uint16),
+                             np.zeros((rows.size, C), np.uint16), np.zeros(rows.size, np.int32),
+                             np.zeros((rows.size, C), np.uint16))
+        G = oracle.masked_dw(dY, Xb, rows)
+        k = np.arange(rows.size, dtype=np.int32)
+        oracle.sparse_update(st, G, k, k, None, **HP)
+
+    def run(every, n_threads):
+        jobs, done, total = [], 0, 0
+        for name, m in L0.mats.items():
+            rows = m["plan"].active_rows[::every].copy()
+            total += m["plan"].n_active
+            done += rows.size
+            for part in np.array_split(rows, max(1, min(rows.size, 4 * n_threads))):
+                if part.size:
+                    jobs.append((name, part))
+        t0 = time.perf_counter()
+        if n_threads == 1:
+            for j in jobs:
+                rows_work(*j)
+        else:
+            with ThreadPoolExecutor(max_workers=n_threads) as ex:
+                list(ex.map(lambda j: rows_work(*j), jobs))
+        dt = time.perf_counter() - t0
+        return dt * total / done * 1e3, done, total, dt
+
+    one_ms, one_done, total, one_s = run(8, 1)
+    many_ms, many_done, _, many_s = run(2, threads)
+    info = host_info()
+    return {"value": round(many_ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
+            "sample": (f"every 2nd active row of each of the 7 matrices of one layer ({many_done} of {total} rows: "
+                       f"masked dW rows + their update, {many_s:.1f} s on {threads} threads), scaled to the "
+                       f"whole layer"),
+            "single_thread": {"value": round(one_ms, 1), "unit": "ms", "cores": 1,
+                              "sample": f"every 8th active row ({one_done} of {total} rows, {one_s:.1f} s), scaled"},
+            "host": info}
+
+
+# ---------------------------------------------------------------------- other workloads
+LEAF_DENSITY = 0.001
+
+
+def leaf_support(m: int, n: int, seed: int):
+    """SparseLeaf support: round(0.1% of m*n) distinct coordinates, uniform,
+    sorted by (row, column)."""
+    from sparse_full_weight_amd import synth
+    g = synth.rng(seed)
+    flat = np.sort(g.choice(m * n, size=round(LEAF_DENSITY * m * n), replace=False))
+    return (flat // n).astype(np.int32), (flat % n).astype(np.int32)
+
+
+def _ring_step_ms(ring, fn, K, stream, block=10):
+    for i in range(5):
+        fn(ring[i % len(ring)])
+    mean, per = timed_blocks(lambda i: fn(ring[i % len(ring)]), K, block, stream)
+    return mean, per
+
+
+def small_projection_step(K, stream):
+    """The 512 x 512 projection, 256 tokens, 10% of the rows active (51, in
+    two clustered tiles): plan upload, masked dW and update in one call."""
+    shapes = {"w": (512, 512)}
+    groups = (("x", ("w",)),)
+    ring = [Layer(300 + i, 256, 0.10, 8000, "packed", shapes=shapes, groups=groups) for i in range(4)]
+
+    def fn(L):
+        L.upload_plan()
+        L.fused_call(stream)
+    mean, per = _ring_step_ms(ring, fn, K, stream)
+    work = ring[0].dw_work().bytes + ring[0].upd_work().bytes
+    return dict(_hbm(work, mean), **_stats(per), active_rows=ring[0].n_active(), tokens=256,
+                note="launch-latency bound (about 1 MB of work)")
+
+
+def adversarial_coupled_step(L0, K, stream):
+    """One active row in every 32-row tile of every matrix (a pair's second
+    matrix shares the first one's row in every other tile): plan upload, packed
+    masked dW of the seven matrices, the coupled update of (gate, up), (q, o),
+    (k, v) at coupling strength 0.6 with the schedule's coefficients at its
+    first step, weight decay 0.01 cos(28.4 deg), and the plain update of down."""
+    import torch
+
+    from sparse_full_weight_amd import _lib, accounting, synth
+    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
+    rows = {name: synth.one_per_tile_rows(L0.mats[name]["R"], 9100 + mi) for mi, name in enumerate(L0.mats)}
+    for a, b in pairs:
+        rows[b][::2] = rows[a][::2]
+    bufs = (L0.X, {n: {k: m[k] for k in ("R", "C", "dY", "q", "s", "delta", "w_live")} for n, m in L0.mats.items()})
+    L = Layer(0, L0.T, 0.0, 9000, "packed", buffers=bufs, rows=rows)
+    helix = _lib.Helix()
+    helix.step(6.17)
+    a_own, a_cross = helix.coupling(0.6, 0.0)
+    wd = float(np.float32(0.01 * math.cos(math.radians(28.4))))
+    bc1, bc2 = L.hp.bc1, L.hp.bc2
+    hp = _lib.Adam(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], bc1, bc2, wd)
+    by_name = {name: u for name, u in zip([n for _, mm in L.groups_def for n in mm], L.upd)}
+    cp = _lib.prepare_coupled_update([_lib.Pair(by_name[a], by_name[b], a_own, a_cross) for a, b in pairs], hp)
+    dn = _lib.prepare_sparse_update([by_name["down"]], hp)
+
+    def step(_):
+        L.upload_plan()
+        L.dw_call(stream)
+        cp(stream)
+        dn(stream)
+    for i in range(3):
+        step(i)
+    mean, per = timed_blocks(step, K, 10, stream)
+    w_dw = L.dw_work()
+    sides = []
+    for a, b in pairs:
+        shared = int(np.intersect1d(rows[a], rows[b]).size)
+        sides += [(L.mats[a]["C"], rows[a].size, shared), (L.mats[b]["C"], rows[b].size, shared)]
+    w_up = (accounting.coupled_update_work(sides).bytes
+            + accounting.update_work([(L.mats["down"]["C"], rows["down"].size)]).bytes)
+    t_dw = _time_calls([L.dw_call], K, stream)
+    t_cp = _time_calls([cp, dn], K, stream)
+    out = dict(_hbm(w_dw.bytes + w_up, mean), **_stats(per), active_rows=L.n_active(), a_own=a_own,
+               a_cross=round(a_cross, 6), coupling_strength=0.6, weight_decay=wd,
+               useful_TFLOP_s=round(w_dw.flops_useful / (mean * 1e-3) / 1e12, 1),
+               whole_tile_TFLOP=round(w_dw.flops_issued / 1e12, 3),
+               packed_dw=dict(_hbm(w_dw.bytes, t_dw),
+                              useful_TFLOP_s=round(w_dw.flops_useful / (t_dw * 1e-3) / 1e12, 1)),
+               coupled_and_down_update=_hbm(w_up, t_cp))
+    del L
+    torch.cuda.empty_cache()
+    return out
+
+
+def model_step(T, K, stream, densities=(0.005, 0.01, 0.02, 0.05), n_layers=32):
+    """The whole 7B-shaped model: 32 layers with distinct activations,
+    gradients and state, and the 32000 x 4096 embedding; fresh seeded masks
+    per layer at each density.  One step = every layer's plan upload and fused
+    call, then the embedding's plan upload, scatter-gradient and update."""
+    import torch
+    t0 = time.perf_counter()
+    bufs = [layer_buffers(T, 11000 + 100 * i) for i in range(n_layers)]
+    torch.cuda.synchronize()
+    setup = time.perf_counter() - t0
+    out = {"layers": n_layers, "tokens": T, "setup_s": round(setup, 1)}
+    emb = None
+    for density in densities:
+        layers = [Layer(i, T, density, 12000 + int(density * 1e4) * 1000, "packed", buffers=bufs[i])
+                  for i in range(n_layers)]
+        if emb is None:
+            emb = Embedding(13000, layers[0].hp)
+
+        def step(_):
+            for L in layers:
+                L.upload_plan()
+                L.fused_call(stream)
+            emb.step(stream)
+        for i in range(2):
+            step(i)
+        mean, per = timed_blocks(step, K, 1, stream)
+        work = sum(L.dw_work().bytes + L.upd_work().bytes for L in layers) + emb.work()
+        out[f"{density:g}"] = dict(_hbm(work, mean), **_stats(per),
+                                   ms_per_layer=round(mean / n_layers, 5),
+                                   active_rows_per_layer=round(float(np.mean([L.n_active() for L in layers])), 1),
+                                   embedding_active_rows=emb.n,
+                                   hbm_roofline_ms=round(work / (HBM_PEAK_GBS * 1e9) * 1e3, 4))
+        del layers
+        torch.cuda.empty_cache()
+    del bufs, emb
+    torch.cuda.empty_cache()
+    return out
+
+
+def other_rows(L0: "Layer", K: int, stream, with_model=True, model_steps=10):
+    """The other workloads and calls, each timed over back-to-back prepared
+    calls on the stream (see the module docstring)."""
     import torch
 
     from sparse_full_weight_amd import _lib, accounting, synth
     dev = "cuda"
     out = {}
+    hp = L0.hp
 
     def state(R, C, n, seed):
         gen = torch.Generator(device=dev)
@@ -268,84 +576,30 @@ def other_rows(L0: "Layer", K: int, stream):
         st["m"] = torch.zeros((n, C), dtype=torch.int16, device=dev)
         st["v"] = torch.zeros((n, C), dtype=torch.int16, device=dev)
         st["t"] = torch.zeros(n, dtype=torch.int32, device=dev)
+        st["e"] = torch.zeros((n, 2), dtype=torch.int8, device=dev)
         st["slot"] = torch.arange(n, dtype=torch.int32, device=dev)
         return st
 
     def upd(st, rows_dev, G, n):
-        return _lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], rows_dev, st["slot"], G, n,
-                           None, st["w"])
+        return _lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], st["e"], rows_dev, st["slot"],
+                           G, n, None, st["w"])
 
-    hp = L0.hp
+    # ---- cfg 1: the 512 x 512 projection
+    out["cfg1_small_projection_step"] = small_projection_step(K, stream)
 
-    # ---- embedding: a 32000 x 4096 table, 4 windows of 8 x 512 Zipf(1.1) ids
-    V, d, Tb = 32000, 4096, 8 * 512
-    windows = [synth.zipf_tokens(Tb, V, 1.1, 9000 + w) for w in range(4)]
-    ch = np.zeros(V, np.float32)
-    t0 = time.perf_counter()
-    for tokens in windows:
-        mask = _lib.sft_conductor_window(ch, tokens)
-    plan = _lib.sft_plan_rows(mask)
-    row_ptr, pos = _lib.sft_plan_embedding(plan, tokens)
-    host_us = (time.perf_counter() - t0) * 1e6
-    n = plan.n_active
-    dY = synth.normal_bf16_device((Tb, d), 0.01, 9010, dev)
-    G = torch.empty((max(n, 1), d), dtype=torch.float32, device=dev)
-    st = state(V, d, n, 9020)
-    dplan = plan.to_device()
-    rp, ps = torch.from_numpy(row_ptr).to(dev), torch.from_numpy(pos).to(dev)
-    emb = _lib.prepare_embedding_dw(dY, rp, ps, n, G)
-    eup = _lib.prepare_sparse_update([upd(st, dplan.active_rows, G, n)], hp)
-    w_emb = accounting.embedding_dw_work(d, int(pos.size), n).bytes
-    w_eup = accounting.update_work([(d, n)]).bytes
-    out["a3_embedding_dw"] = dict(_hbm(w_emb, _time_calls([emb], K, stream)), active_rows=n, hit_tokens=int(pos.size),
-                                  table=[V, d], tokens=Tb)
-    out["a3_embedding_dw_and_update"] = dict(_hbm(w_emb + w_eup, _time_calls([emb, eup], K, stream)),
-                                             host_conductor_plan_us=round(host_us, 1))
-    del st, dY, G
+    # ---- cfg 5: the adversarial layer with the coupled update, as one step
+    out["cfg5_adversarial_coupled_step"] = adversarial_coupled_step(L0, K, stream)
 
-    # ---- coupled pairs on one active row per 32-row tile (every tile active)
-    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
-    rows = {name: synth.one_per_tile_rows(L0.mats[name]["R"], 9100 + mi) for mi, name in enumerate(L0.mats)}
-    for a, b in pairs:
-        rows[b][::2] = rows[a][::2]   # a pair shares the row of every other tile
-    groups, plans, G = [], {}, {}
-    for gname, members in synth.LLAMA7B_GROUPS:
-        ms = []
-        for name in members:
-            m = L0.mats[name]
-            plan = _lib.sft_plan_rows(synth.mask_from_rows(m["R"], rows[name]))
-            plans[name] = plan.to_device()
-            G[name] = torch.empty((plan.n_active, m["C"]), dtype=torch.float32, device=dev)
-            ms.append(_lib.DwMat(m["dY"], plans[name], G[name]))
-        groups.append(_lib.DwGroup(L0.X[gname], ms, _lib.SFT_DW_PACKED))
-    ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device=dev)
-    dw = _lib.prepare_masked_dw(groups, ws)
-    sts = {name: state(L0.mats[name]["R"], L0.mats[name]["C"], plans[name].n_active, 9200 + i)
-           for i, name in enumerate(L0.mats)}
-    cp = _lib.prepare_coupled_update([_lib.Pair(upd(sts[a], plans[a].active_rows, G[a], plans[a].n_active),
-                                                upd(sts[b], plans[b].active_rows, G[b], plans[b].n_active), 1.0, 0.4)
-                                      for a, b in pairs], hp)
-    dn = _lib.prepare_sparse_update([upd(sts["down"], plans["down"].active_rows, G["down"], plans["down"].n_active)],
-                                    hp)
-    dw_groups = [(L0.T, L0.mats[mm[0]]["C"], [(plans[n].n_active, plans[n].n_active_tiles) for n in mm])
-                 for _, mm in synth.LLAMA7B_GROUPS]
-    w_dw = accounting.masked_dw_work(dw_groups)
-    sides = []
-    for a, b in pairs:
-        shared = int(np.intersect1d(rows[a], rows[b]).size)
-        sides += [(L0.mats[a]["C"], rows[a].size, shared), (L0.mats[b]["C"], rows[b].size, shared)]
-    w_cp = accounting.coupled_update_work(sides).bytes
-    t_dw = _time_calls([dw], K, stream)
-    out["f1_packed_dw_one_row_per_tile"] = dict(
-        _hbm(w_dw.bytes, t_dw), active_rows=int(sum(p.n_active for p in plans.values())),
-        useful_TFLOP_s=round(w_dw.flops_useful / (t_dw * 1e-3) / 1e12, 1),
-        whole_tile_TFLOP=round(w_dw.flops_issued / 1e12, 3))
-    out["a5_coupled_update"] = dict(_hbm(w_cp, _time_calls([cp], K, stream)), pairs=[list(p) for p in pairs],
-                                    a_own=1.0, a_cross=0.4)
-    out["a5_coupled_and_down_update"] = _hbm(
-        w_cp + accounting.update_work([(L0.mats["down"]["C"], plans["down"].n_active)]).bytes,
-        _time_calls([cp, dn], K, stream))
-    del sts, G, ws
+    # ---- cfg 2: the embedding workload as one step, and its scatter-gradient alone
+    emb = Embedding(9000, hp)
+    w_emb = accounting.embedding_dw_work(emb.d, emb.nnz, emb.n).bytes
+    out["a3_embedding_dw"] = dict(_hbm(w_emb, _time_calls([emb.emb_call], K, stream)), active_rows=emb.n,
+                                  hit_tokens=emb.nnz, table=[emb.V, emb.d], tokens=emb.Tb)
+    mean, per = timed_blocks(lambda i: emb.step(stream), K, 10, stream)
+    out["cfg2_embedding_step"] = dict(_hbm(emb.work(), mean), **_stats(per),
+                                      host_conductor_plan_us=round(emb.host_us, 1),
+                                      note="plan upload + scatter-gradient + sparse update with write-back")
+    del emb
 
     # ---- standalone write-back of the 1% layer's active rows (7 matrices):
     # one batched call, and the seven single-matrix calls beside it
@@ -361,8 +615,8 @@ def other_rows(L0: "Layer", K: int, stream):
     out["a6_masked_writeback_single_calls"] = dict(_hbm(w_wb, _time_calls(wb, K, stream)), calls=len(wb))
 
     # ---- active-row checkpoint of the 1% layer (7 matrices, one call each way)
-    cks = [_lib.CkptMat.alloc(u.q, u.s, u.delta, u.m, u.v, u.t, u.active_rows, u.slot, u.n_active, u.w_live)
-           for u in L0.upd]
+    cks = [_lib.CkptMat.alloc(u.q, u.s, u.delta, u.m, u.v, u.t, u.mv_exp, u.active_rows, u.slot, u.n_active,
+                              u.w_live) for u in L0.upd]
     dims = [(u.q.shape[1], u.n_active) for u in L0.upd]
     save = _lib.prepare_rows_save(cks)
     restore = _lib.prepare_rows_restore(cks)
@@ -393,58 +647,45 @@ def other_rows(L0: "Layer", K: int, stream):
                                _time_calls([ladam], K, stream))
     del leaf, lvecs, lws
 
-    # ---- the full step's other row densities: the same layer step (fused
-    # masked dW and update, plan resident) over a ring of 3 layers at each density
+    # ---- the layer step at the model's other row densities (0.5%, 2%, 5%),
+    # plan upload included, over a ring of 3 layers at each density
     sweep = {}
     for density in (0.005, 0.02, 0.05):
         ring = [Layer(100 + i, L0.T, density, 6000, "packed") for i in range(3)]
 
-        def step(L):
+        def fn(L):
+            L.upload_plan()
             L.fused_call(stream)
-        for i in range(5):
-            step(ring[i % 3])
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(K):
-            step(ring[i % 3])
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / K
+        mean, per = _ring_step_ms(ring, fn, K, stream)
         work = ring[0].dw_work().bytes + ring[0].upd_work().bytes
-        sweep[f"{density:g}"] = dict(_hbm(work, ms), active_rows=int(sum(m["plan"].n_active
-                                                                        for m in ring[0].mats.values())))
+        sweep[f"{density:g}"] = dict(_hbm(work, mean), **_stats(per), active_rows=ring[0].n_active())
         del ring
         torch.cuda.empty_cache()
     out["c_density_sweep_step"] = sweep
 
     # ---- one GPU's share of a token-sharded step: the same 1% layer step (fused
-    # call, plans resident) on T/N tokens, the shape each of N GPUs would run
-    # before the dW exchange (which is not built here)
+    # call, plan upload included) on T/N tokens, the shape each of N GPUs would
+    # run before the dW exchange (which is not built here)
     share = {}
     for n_gpu in (2, 4, 8):
         T = L0.T // n_gpu
         ring = [Layer(200 + i, T, L0.density, 7000, "packed") for i in range(3)]
-
-        def ring_ms(fn):
-            for i in range(5):
-                fn(ring[i % 3])
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for i in range(K):
-                fn(ring[i % 3])
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / K
         dw_b, up_b = ring[0].dw_work().bytes, ring[0].upd_work().bytes
-        share[f"T{T}"] = dict(_hbm(dw_b + up_b, ring_ms(lambda L: L.fused_call(stream))), n_gpus_sharing=n_gpu,
-                              tokens=T, masked_dw=_hbm(dw_b, ring_ms(lambda L: L.dw_call(stream))))
+
+        def fn(L):
+            L.upload_plan()
+            L.fused_call(stream)
+        mean, _ = _ring_step_ms(ring, fn, K, stream)
+        dw_ms, _ = _ring_step_ms(ring, lambda L: L.dw_call(stream), K, stream)
+        share[f"T{T}"] = dict(_hbm(dw_b + up_b, mean), n_gpus_sharing=n_gpu, tokens=T, masked_dw=_hbm(dw_b, dw_ms))
         del ring
         torch.cuda.empty_cache()
     out["e_token_share_step"] = share
+
+    # ---- cfg 4: the whole model (32 layers + embedding) at four densities
+    if with_model:
+        print("[bench] timing the 32-layer model step", file=sys.stderr, flush=True)
+        out["cfg4_model_step"] = model_step(L0.T, model_steps, stream)
     torch.cuda.synchronize()
     return out
 
@@ -506,82 +747,54 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    # host plan cost of one layer (tracker windows + plans + slots), for the record
-    from sparse_full_weight_amd import _lib, synth
-    th0 = time.perf_counter()
-    for mi, (name, (R, C)) in enumerate(synth.LLAMA7B.items()):
-        mag = synth.tracker_magnitudes(R, synth.clustered_rows(R, round(args.density * R), 7 + mi), 8 + mi)
-        mask = _lib.sft_tracker_window(np.zeros(R, np.float32), mag)
-        plan = _lib.sft_plan_rows(mask)
-        _lib.sft_slots_update(np.full(R, -1, np.int32), plan.n_active, plan.active_rows)
-    host_plan_us = (time.perf_counter() - th0) * 1e6
-
+    from sparse_full_weight_amd import synth
     stream = torch.cuda.current_stream()
     if args.rows_only:
-        print(json.dumps({"rows": other_rows(layers[0], min(args.steps, 100), stream)}), flush=True)
+        print(json.dumps({"rows": other_rows(layers[0], min(args.steps, 100), stream, not args.no_model,
+                                             args.model_steps)}), flush=True)
         return
 
-    def step(L):
+    def call(L):
         if args.unfused:
             L.dw_call(stream)
             L.upd_call(stream)
         else:
             L.fused_call(stream)
 
-    def step_with_upload(L):
+    def step(i):
+        # the step: this step's plan to the device, then the masked dW and update
+        L = layers[i % len(layers)]
         L.upload_plan()
-        step(L)
+        call(L)
+
+    def step_resident(i):
+        call(layers[i % len(layers)])
 
     # Untimed: about 0.1 s of steps so that the clocks have settled, then the
     # W warmup steps.
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < 0.1:
         for i in range(len(layers)):
-            step(layers[i])
+            step(i)
         torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(layers[i % len(layers)])
+        step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    # The timed loop: K whole steps back to back, bracketed by one event pair
-    # (per-step events would put markers between the kernels); every plan is
-    # resident (uploaded when its layer was built).
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-
-    def timed_steps(fn):
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(K):
-            fn(layers[i % len(layers)])
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / K
-
-    ms_per_step = timed_steps(step)
-    # the same steps, each behind its plan's host->device copy (PCIe-inclusive)
-    ms_with_upload = timed_steps(step_with_upload)
+    # The timed loop: K whole steps back to back, with an event pair around the
+    # run and an event every `block` steps (between steps, never inside one).
+    ms_per_step, per_block = timed_blocks(step, K, args.block, stream)
+    ms_resident, per_block_res = timed_blocks(step_resident, K, args.block, stream)
 
     # Per-call durations, each timed over its own back-to-back run of K calls
     # on the same stream and inputs (the masked-dW call is the gather, product
     # and fix-up kernels; the update call is one kernel).
-    def timed(fn):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(K):
-            fn(layers[i % len(layers)])
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / K
-
     for L in layers:
         L.upload_plan()
-    dw_avg = timed(lambda L: L.dw_call(stream))
-    up_avg = timed(lambda L: L.upd_call(stream))
-    fu_avg = timed(lambda L: L.fused_call(stream))
+    dw_avg, _ = timed_blocks(lambda i: layers[i % len(layers)].dw_call(stream), K, K, stream)
+    up_avg, _ = timed_blocks(lambda i: layers[i % len(layers)].upd_call(stream), K, K, stream)
+    fu_avg, _ = timed_blocks(lambda i: layers[i % len(layers)].fused_call(stream), K, K, stream)
 
     L0 = layers[0]
     dw = L0.dw_work()
@@ -589,7 +802,8 @@ def main():
     dw_gbs = dw.bytes / (dw_avg * 1e-3) / 1e9
     up_gbs = up.bytes / (up_avg * 1e-3) / 1e9
     fu_gbs = (dw.bytes + up.bytes) / (fu_avg * 1e-3) / 1e9
-    n_act = sum(m["plan"].n_active for m in L0.mats.values())
+    step_gbs = (dw.bytes + up.bytes) / (ms_per_step * 1e-3) / 1e9
+    n_act = L0.n_active()
     n_tiles = sum(m["plan"].n_active_tiles for m in L0.mats.values())
 
     # HBM bytes per masked-dW call from the committed counter summary, if it
@@ -600,10 +814,13 @@ def main():
     if rec and rec.get("sft_dw_sha256") == profsum.source_hash("sft_dw.hip"):
         traffic = rec["masked_dw_call_bytes"]
 
+    print("[bench] timing the a1 host calls", file=sys.stderr, flush=True)
+    host_plan = host_plan_us(args.density)
+
     rows = None
     if not args.no_rows:
-        print("[bench] timing the other hot-path calls", file=sys.stderr, flush=True)
-        rows = other_rows(L0, min(K, 100), stream)
+        print("[bench] timing the other workloads and calls", file=sys.stderr, flush=True)
+        rows = other_rows(L0, min(K, 100), stream, not args.no_model, args.model_steps)
 
     ceil = None
     if not args.no_ceilings:
@@ -612,12 +829,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
-        cpu_ms, rows_done, rows_all, t_sample = cpu_baseline(L0, args.cpu_sample_every)
-        cpu = {"value": round(cpu_ms, 1), "unit": "ms", "cores": 1, "kind": "oracle",
-               "sample": f"every {args.cpu_sample_every}th active row of each of the 7 matrices of one layer "
-                         f"({rows_done} of {rows_all} rows: masked dW rows + their update, "
-                         f"{t_sample:.1f} s), scaled to the whole layer"}
+        print("[bench] timing the oracle on samples", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(L0, CPU_THREADS)
 
     out = {
         "metric": "masked step ms per 7B-shape layer at 1% active rows; MFMA util + HBM GB/s",
@@ -635,11 +848,16 @@ def main():
         "config": {"workload": "llama7b_layer_masked_step", "tokens": args.tokens, "density": args.density,
                    "matrices": {k: list(v) for k, v in synth.LLAMA7B.items()}, "active_rows": n_act,
                    "active_tiles": n_tiles, "ring_layers": args.layers, "dw_layout": args.layout,
-                   "step": ("masked dW (7 matrices) + sparse update with fused write-back (7 matrices), "
+                   "step": ("the step's packed plan copied host -> device (a few KB, pinned), then masked dW "
+                            "(7 matrices) + sparse update with fused write-back (7 matrices), "
                             + ("two calls" if args.unfused else
                                "one call: sft_masked_dw_update, the split tiles' fix-up done by the update")
-                            + "; inputs and plans resident in HBM"),
-                   "ms_per_step_with_plan_upload": round(ms_with_upload, 5)},
+                            + "; activations, gradients and state resident in HBM"),
+                   "step_stats": _stats(per_block),
+                   "ms_per_step_plan_resident": round(ms_resident, 5),
+                   "step_stats_plan_resident": _stats(per_block_res),
+                   "step_GB_s": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "hbm_roofline_ms": round((dw.bytes + up.bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 5)},
         "roofline": {"bound": "hbm", "kernel": "sft_masked_dw (k_dw_gather + k_masked_dw + k_dw_fixup)",
                      "achieved": round(dw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -660,7 +878,7 @@ def main():
         },
         "rows": rows,
         "ceilings": ceil,
-        "host_plan_us_per_layer": round(host_plan_us, 1),
+        "host_plan_us_per_layer": host_plan,
     }
     print(json.dumps(out), flush=True)
 

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 10
+#define SFT_ABI_VERSION 11
 
 enum {
     SFT_OK = 0,
@@ -398,6 +398,15 @@ typedef struct sft_adam {
  * One matrix's optimizer state and the gradient of its active rows.
  *   q      int8 [R x C], s fp32 [R], delta fp32 [R x C]: w = s*q + delta
  *   m, v   fp16 [n_slots x C], t int32 [n_slots]: moments and step count per slot
+ *   mv_exp int8 [n_slots x 2]: the exponents of each slot's m row and v row.
+ *          The fp16 moments (section 2.3) are stored scaled: the value h of
+ *          a row with exponent e stands for h * 2^-e.  Every update picks e
+ *          from the new row's largest magnitude so that it lands in
+ *          [2^14, 2^15) (e = 15 - k for a maximum in [2^(k-1), 2^k), limited
+ *          to [-112, 125]; 0 for an all-zero row), rounds to nearest even and
+ *          saturates at 65504, so that small and large gradients alike keep
+ *          fp16's 11 significant bits instead of flushing to zero or
+ *          overflowing.  A fresh slot ignores the stored values.
  *   G      fp32 [n_active x C] (row k = active_rows[k]), e.g. dW_act
  *   slot   [n_active] slot of each active row; fresh [n_active] or NULL
  *   w_live bf16 [R x C] live weights, or NULL for no fused write-back
@@ -414,6 +423,7 @@ typedef struct sft_upd_mat {
     uint16_t *m;
     uint16_t *v;
     int32_t *t;
+    int8_t *mv_exp;
     uint16_t *w_live;
 } sft_upd_mat;
 
@@ -421,8 +431,9 @@ typedef struct sft_upd_mat {
  * Plain sparse update of every active row of n_mats matrices, in one launch
  * (section 2.3; section 2.4's plain Adam step for unpaired matrices).  Per
  * active row: rebuild w = fl(fl(s*q) + delta) in registers, take the Adam step
- * (fp32 moments from the stored fp16 ones, new moments stored as fp16 rounded
- * to nearest even, bias correction from the table, step lr*mhat/(sqrt(vhat)+eps),
+ * (fp32 moments decoded from the stored scaled fp16 rows, new moments stored
+ * as scaled fp16 rows with new exponents, bias correction from the table,
+ * step lr*mhat/(sqrt(vhat)+eps),
  * decoupled weight decay first when weight_decay != 0), then requantise the
  * row: s' = max|w'|/127, q' = clamp(rint(w'/s'), -127, 127),
  * delta' = w' - s'*q' (exact, so s'*q' + delta' rebuilds w'); a row with
@@ -526,12 +537,13 @@ int sft_masked_writeback_many(const sft_wb_mat *mats, int32_t n_mats, void *stre
  *   slot  [n_rows] the moment slot of each row, in [0, n_slots) (device):
  *         at save the slot the moments are read from, at restore the slot
  *         they are written to (the same array unless slots were reassigned)
- *   q, s, delta, m, v, t   live state: int8 [R x C], fp32 [R], fp32 [R x C],
- *                          fp16 [n_slots x C] twice, int32 [n_slots]
+ *   q, s, delta, m, v, t, mv_exp   live state: int8 [R x C], fp32 [R],
+ *                          fp32 [R x C], fp16 [n_slots x C] twice, int32
+ *                          [n_slots], int8 [n_slots x 2] (as in sft_upd_mat)
  *   w_live                 bf16 [R x C]; restore rebuilds the restored rows
  *                          as in sft_masked_writeback; NULL = no live copy
  *   ck_q [n_rows x C] int8, ck_s [n_rows] fp32, ck_delta [n_rows x C] fp32,
- *   ck_m, ck_v [n_rows x C] fp16, ck_t [n_rows] int32
+ *   ck_m, ck_v [n_rows x C] fp16, ck_t [n_rows] int32, ck_mv_exp [n_rows x 2] int8
  */
 typedef struct sft_ckpt_mat {
     int64_t R, C, n_rows, n_slots;
@@ -543,6 +555,7 @@ typedef struct sft_ckpt_mat {
     uint16_t *m;
     uint16_t *v;
     int32_t *t;
+    int8_t *mv_exp;
     uint16_t *w_live;
     int8_t *ck_q;
     float *ck_s;
@@ -550,11 +563,12 @@ typedef struct sft_ckpt_mat {
     uint16_t *ck_m;
     uint16_t *ck_v;
     int32_t *ck_t;
+    int8_t *ck_mv_exp;
 } sft_ckpt_mat;
 
 /*
- * Copies the listed rows of every matrix (q, s, delta and the moments and
- * step count of their slots) into the checkpoint buffers, bit for bit; one
+ * Copies the listed rows of every matrix (q, s, delta and the moments, step
+ * count and moment exponents of their slots) into the checkpoint buffers, bit for bit; one
  * launch for all matrices.  Rows not listed and the live state are not
  * touched.
  * Limits: C % 8 == 0, fewer than 2^31 rows in all.
@@ -567,7 +581,7 @@ int sft_rows_save(const sft_ckpt_mat *mats, int32_t n_mats, void *stream);
 
 /*
  * The inverse copy: writes the checkpointed q, s, delta rows back to their
- * rows and the moments and step counts back to slot[k], bit for bit, and
+ * rows and the moments, step counts and exponents back to slot[k], bit for bit, and
  * rebuilds those rows of w_live (bf16 of fl(s*q) + delta, as
  * sft_masked_writeback) when w_live is set.  Rows not listed are not
  * touched.  Limits and errors: as sft_rows_save.

@@ -75,7 +75,7 @@ class CUpdMat(C.Structure):
     _fields_ = [("R", C.c_int64), ("C", C.c_int64), ("n_active", C.c_int64), ("n_slots", C.c_int64),
                 ("active_rows", C.c_void_p), ("slot", C.c_void_p), ("fresh", C.c_void_p), ("G", C.c_void_p),
                 ("q", C.c_void_p), ("s", C.c_void_p), ("delta", C.c_void_p), ("m", C.c_void_p),
-                ("v", C.c_void_p), ("t", C.c_void_p), ("w_live", C.c_void_p)]
+                ("v", C.c_void_p), ("t", C.c_void_p), ("mv_exp", C.c_void_p), ("w_live", C.c_void_p)]
 
 
 class CWbMat(C.Structure):
@@ -100,8 +100,9 @@ class CCkptMat(C.Structure):
     _fields_ = [("R", C.c_int64), ("C", C.c_int64), ("n_rows", C.c_int64), ("n_slots", C.c_int64),
                 ("rows", C.c_void_p), ("slot", C.c_void_p), ("q", C.c_void_p), ("s", C.c_void_p),
                 ("delta", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p), ("t", C.c_void_p),
-                ("w_live", C.c_void_p), ("ck_q", C.c_void_p), ("ck_s", C.c_void_p), ("ck_delta", C.c_void_p),
-                ("ck_m", C.c_void_p), ("ck_v", C.c_void_p), ("ck_t", C.c_void_p)]
+                ("mv_exp", C.c_void_p), ("w_live", C.c_void_p), ("ck_q", C.c_void_p), ("ck_s", C.c_void_p),
+                ("ck_delta", C.c_void_p), ("ck_m", C.c_void_p), ("ck_v", C.c_void_p), ("ck_t", C.c_void_p),
+                ("ck_mv_exp", C.c_void_p)]
 
 
 class CHelix(C.Structure):
@@ -198,6 +199,23 @@ def _dev(t, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"expected {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def _shape(t, want, what):
+    """Raise unless tensor ``t`` has shape ``want`` (entries None match any size)."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        raise ValueError(f"{what}: shape {got}, expected {tuple('*' if w is None else w for w in want)}")
+
+
+def _numel_at_least(t, n, what):
+    if t.numel() < n:
+        raise ValueError(f"{what}: {t.numel()} elements, need at least {n}")
+
+
+def _is16(t) -> bool:
+    import torch
+    return t.dtype in (torch.int16, torch.uint16, torch.float16, torch.bfloat16)
 
 
 def _stream(stream):
@@ -347,6 +365,10 @@ def _c_groups(groups: Sequence[DwGroup]):
         T, Cc = g.X.shape
         mats = (CDwMat * max(len(g.mats), 1))()
         for j, m in enumerate(g.mats):
+            _shape(m.dY, (T, m.plan.rows), f"group {i} matrix {j} dY")
+            if m.plan.n_active:
+                _shape(m.dW_act, (None, Cc), f"group {i} matrix {j} dW_act")
+                _numel_at_least(m.dW_act, m.plan.n_active * Cc, f"group {i} matrix {j} dW_act")
             mats[j] = CDwMat(_dev(m.dY, torch.bfloat16), m.plan.rows, _dev(m.plan.active_rows),
                              _dev(m.plan.active_tiles), _dev(m.plan.active_bits), _dev(m.plan.tile_first),
                              m.plan.n_active, m.plan.n_active_tiles, _dev(m.dW_act, torch.float32))
@@ -402,6 +424,7 @@ class UpdMat:
     m: "object"             # fp16 bits (int16/uint16 tensor) [n_slots x C]
     v: "object"
     t: "object"             # int32 [n_slots]
+    mv_exp: "object"        # int8 [n_slots x 2]: exponents of the slot's m row and v row
     active_rows: "object"   # int32 [n_active] (GPU)
     slot: "object"          # int32 [n_active] (GPU)
     G: "object"             # fp32 [n_active x C]
@@ -410,10 +433,36 @@ class UpdMat:
     w_live: "object" = None  # bf16 [R x C] or None
 
     def c(self) -> CUpdMat:
+        """The C struct, after checking every tensor's dtype and shape (the
+        kernels trust the sizes: a wrong one would read or write out of
+        bounds on the GPU)."""
+        import torch
+        _shape(self.q, (None, None), "q")
         R, Cc = self.q.shape
-        return CUpdMat(R, Cc, self.n_active, self.m.shape[0], _dev(self.active_rows), _dev(self.slot),
-                       _dev(self.fresh), _dev(self.G), _dev(self.q), _dev(self.s), _dev(self.delta),
-                       _dev(self.m), _dev(self.v), _dev(self.t), _dev(self.w_live))
+        n_slots = self.m.shape[0]
+        n = int(self.n_active)
+        _shape(self.s, (R,), "s")
+        _shape(self.delta, (R, Cc), "delta")
+        _shape(self.m, (n_slots, Cc), "m")
+        _shape(self.v, (n_slots, Cc), "v")
+        _shape(self.t, (n_slots,), "t")
+        _shape(self.mv_exp, (n_slots, 2), "mv_exp")
+        if not (_is16(self.m) and _is16(self.v)):
+            raise TypeError("m and v must be 16-bit tensors (fp16 bit patterns)")
+        _shape(self.G, (None, Cc), "G")
+        for t_, what in ((self.active_rows, "active_rows"), (self.slot, "slot")):
+            _numel_at_least(t_, n, what)
+        _numel_at_least(self.G, n * Cc, "G")
+        if self.fresh is not None:
+            _numel_at_least(self.fresh, n, "fresh")
+        if self.w_live is not None:
+            _shape(self.w_live, (R, Cc), "w_live")
+            if not _is16(self.w_live):
+                raise TypeError("w_live must be a 16-bit tensor (bf16 bit patterns)")
+        return CUpdMat(R, Cc, n, n_slots, _dev(self.active_rows, torch.int32), _dev(self.slot, torch.int32),
+                       _dev(self.fresh, torch.uint8), _dev(self.G, torch.float32), _dev(self.q, torch.int8),
+                       _dev(self.s, torch.float32), _dev(self.delta, torch.float32), _dev(self.m), _dev(self.v),
+                       _dev(self.t, torch.int32), _dev(self.mv_exp, torch.int8), _dev(self.w_live))
 
 
 def sft_sparse_update(mats: Sequence[UpdMat], hp: Adam, stream=None) -> None:
@@ -575,6 +624,7 @@ class CkptMat:
     m: "object"             # fp16 bits [n_slots x C]
     v: "object"
     t: "object"             # int32 [n_slots]
+    mv_exp: "object"        # int8 [n_slots x 2]
     rows: "object"          # int32 [n_rows] (GPU)
     slot: "object"          # int32 [n_rows] (GPU)
     ck_q: "object"          # int8 [n_rows x C]
@@ -583,28 +633,50 @@ class CkptMat:
     ck_m: "object"          # fp16 bits [n_rows x C]
     ck_v: "object"
     ck_t: "object"          # int32 [n_rows]
+    ck_mv_exp: "object"     # int8 [n_rows x 2]
     n_rows: int
     w_live: "object" = None  # bf16 [R x C] or None
 
     def c(self) -> CCkptMat:
+        import torch
         R, Cc = self.q.shape
-        return CCkptMat(R, Cc, self.n_rows, self.m.shape[0], _dev(self.rows), _dev(self.slot), _dev(self.q),
+        n_slots = self.m.shape[0]
+        n = int(self.n_rows)
+        if n > 0:
+            # the sizes the C checks cannot see (n_rows within R and n_slots is checked there)
+            _shape(self.s, (R,), "s")
+            _shape(self.t, (n_slots,), "t")
+            _shape(self.mv_exp, (n_slots, 2), "mv_exp")
+            for t_, what in ((self.rows, "rows"), (self.slot, "slot"), (self.ck_s, "ck_s"), (self.ck_t, "ck_t")):
+                _numel_at_least(t_, n, what)
+            _numel_at_least(self.ck_mv_exp, 2 * n, "ck_mv_exp")
+            for t_, what in ((self.ck_q, "ck_q"), (self.ck_delta, "ck_delta"), (self.ck_m, "ck_m"),
+                             (self.ck_v, "ck_v")):
+                _numel_at_least(t_, n * Cc, what)
+            _shape(self.delta, (R, Cc), "delta")
+            _shape(self.m, (n_slots, Cc), "m")
+            _shape(self.v, (n_slots, Cc), "v")
+            if self.w_live is not None:
+                _shape(self.w_live, (R, Cc), "w_live")
+        return CCkptMat(R, Cc, n, n_slots, _dev(self.rows), _dev(self.slot), _dev(self.q),
                         _dev(self.s), _dev(self.delta), _dev(self.m), _dev(self.v), _dev(self.t),
-                        _dev(self.w_live), _dev(self.ck_q), _dev(self.ck_s), _dev(self.ck_delta),
-                        _dev(self.ck_m), _dev(self.ck_v), _dev(self.ck_t))
+                        _dev(self.mv_exp, torch.int8), _dev(self.w_live), _dev(self.ck_q), _dev(self.ck_s),
+                        _dev(self.ck_delta), _dev(self.ck_m), _dev(self.ck_v), _dev(self.ck_t),
+                        _dev(self.ck_mv_exp, torch.int8))
 
     @staticmethod
-    def alloc(q, s, delta, m, v, t, rows, slot, n_rows: int, w_live=None) -> "CkptMat":
+    def alloc(q, s, delta, m, v, t, mv_exp, rows, slot, n_rows: int, w_live=None) -> "CkptMat":
         """Checkpoint buffers for n_rows rows of this state (device tensors)."""
         import torch
         Cc = q.shape[1]
         dev = q.device
         n = max(n_rows, 1)
-        return CkptMat(q, s, delta, m, v, t, rows, slot, torch.empty((n, Cc), dtype=torch.int8, device=dev),
+        return CkptMat(q, s, delta, m, v, t, mv_exp, rows, slot, torch.empty((n, Cc), dtype=torch.int8, device=dev),
                        torch.empty(n, dtype=torch.float32, device=dev),
                        torch.empty((n, Cc), dtype=torch.float32, device=dev),
                        torch.empty((n, Cc), dtype=m.dtype, device=dev), torch.empty((n, Cc), dtype=v.dtype, device=dev),
-                       torch.empty(n, dtype=torch.int32, device=dev), n_rows, w_live)
+                       torch.empty(n, dtype=torch.int32, device=dev), torch.empty((n, 2), dtype=torch.int8, device=dev),
+                       n_rows, w_live)
 
 
 def sft_rows_save(mats: Sequence[CkptMat], stream=None) -> None:

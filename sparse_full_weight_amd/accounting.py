@@ -48,10 +48,11 @@ def masked_dw_work(groups: Sequence[Tuple[int, int, Sequence[Tuple[int, int]]]])
 
 # Per active element of the update: read g (4), q (1), delta (4), m (2), v (2);
 # write q (1), delta (4), m (2), v (2); plus the bf16 live weight (2) when the
-# write-back is fused.  Per active row: the scale s (read 4, write 4).
+# write-back is fused.  Per active row: the scale s (read 4, write 4) and the
+# two moment exponents of its slot (read 2, write 2).
 UPDATE_BYTES_PER_ELEMENT = 4 + 1 + 4 + 2 + 2 + 1 + 4 + 2 + 2
 WRITEBACK_BYTES_PER_ELEMENT = 2
-UPDATE_BYTES_PER_ROW = 8
+UPDATE_BYTES_PER_ROW = 8 + 4
 
 
 def update_work(mats: Iterable[Tuple[int, int]], fused_writeback: bool = True) -> Work:
@@ -76,9 +77,10 @@ def coupled_update_work(sides: Iterable[Tuple[int, int, int]]) -> Work:
 
 # Section 2.6 checkpoint of one row element: q (1), delta (4), m (2), v (2),
 # read on one side and written on the other; a restore also writes the live
-# bf16 weight (2).  Per row: s and the slot's step count, read and written.
+# bf16 weight (2).  Per row: s, the slot's step count and its two moment
+# exponents, read and written.
 CHECKPOINT_BYTES_PER_ELEMENT = 2 * (1 + 4 + 2 + 2)
-CHECKPOINT_BYTES_PER_ROW = 2 * (4 + 4)
+CHECKPOINT_BYTES_PER_ROW = 2 * (4 + 4 + 2)
 
 
 def checkpoint_work(mats: Iterable[Tuple[int, int]], restore: bool = False, live: bool = True) -> Work:

@@ -14,10 +14,11 @@
 // Kernel shape: one workgroup per active row, all matrices of a call in one
 // launch.  A row is streamed once: each lane owns 4-column chunks
 // (16-byte loads of gradient and residual, 4 bytes of q, 8 bytes of each
-// moment), keeps the new weights in registers, reduces the row's |w'| maximum
-// across the wavefront (cross-lane shuffles) and across wavefronts (LDS),
-// then requantises and stores.  The work is bound by HBM bandwidth: per
-// active element it reads 13 bytes and writes 11 (with the fused write-back).
+// moment), keeps the new weights and moments in registers, reduces the row's
+// maxima of |w'|, |m| and v across the wavefront (cross-lane shuffles) and
+// across wavefronts (LDS), then requantises, scales the moments and stores.
+// The work is bound by HBM bandwidth: per active element it reads 13 bytes
+// and writes 11 (with the fused write-back).
 //
 // Arithmetic is IEEE fp32 without contraction: every product and sum below
 // rounds on its own, divisions and square roots are correctly rounded (the
@@ -50,6 +51,7 @@ struct UpdMatDev {
     uint16_t *m;
     uint16_t *v;
     int32_t *t;
+    int8_t *mv_exp;
     uint16_t *w_live;
     int64_t C;
     int64_t n_active;
@@ -98,32 +100,71 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Largest value over the workgroup (non-negative floats), via the integer
-// order of their bit patterns: wave64 shuffles, then one LDS word per wave.
-// The workgroup may hold several rows of kLanes lanes each: the maximum is
-// taken over the waves of the calling lane's row.
+// Largest values over the workgroup (three non-negative floats at once), via
+// the integer order of their bit patterns: wave64 shuffles, then one LDS word
+// per wave and value.  The workgroup may hold several rows of kLanes lanes
+// each: the maxima are taken over the waves of the calling lane's row.
 template <int kThreads, int kLanes>
-__device__ __forceinline__ float block_max_nonneg(float x, float *lds) {
-    uint32_t u = __float_as_uint(x);
+__device__ __forceinline__ void block_max3_nonneg(float &x0, float &x1, float &x2, float (*lds)[kThreads / 64]) {
+    uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1), u2 = __float_as_uint(x2);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) u = max(u, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u), off, 64)));
+    for (int off = 32; off >= 1; off >>= 1) {
+        u0 = max(u0, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u0), off, 64)));
+        u1 = max(u1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u1), off, 64)));
+        u2 = max(u2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(u2), off, 64)));
+    }
     const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[wave] = __uint_as_float(u);
+    if ((threadIdx.x & 63) == 0) {
+        lds[0][wave] = __uint_as_float(u0);
+        lds[1][wave] = __uint_as_float(u1);
+        lds[2][wave] = __uint_as_float(u2);
+    }
     __syncthreads();
     const int w0 = (static_cast<int>(threadIdx.x) / kLanes) * (kLanes / 64);
-    float r = lds[w0];
+    float r0 = lds[0][w0], r1 = lds[1][w0], r2 = lds[2][w0];
 #pragma unroll
-    for (int w = 1; w < kLanes / 64; ++w) r = fmaxf(r, lds[w0 + w]);
-    return r;
+    for (int w = 1; w < kLanes / 64; ++w) {
+        r0 = fmaxf(r0, lds[0][w0 + w]);
+        r1 = fmaxf(r1, lds[1][w0 + w]);
+        r2 = fmaxf(r2, lds[2][w0 + w]);
+    }
+    x0 = r0;
+    x1 = r1;
+    x2 = r2;
+}
+
+// Scaled fp16 moment rows (the storage of section 2.3's fp16 moments): a row
+// is stored as fp16 values of x * 2^e, one exponent e per row and moment,
+// chosen from the new row's largest magnitude so that it lands in
+// [2^14, 2^15): e = 141 - (biased exponent of the maximum), limited to
+// [-112, 125] so that 2^e and 2^-e are normal floats; an all-zero row takes
+// e = 0.  Scaling by 2^e is exact (a result below 2^-126 rounds to fp16 zero
+// either way), the fp16 rounding is to nearest even, saturating at 65504.
+constexpr int kExpMin = -112, kExpMax = 125;
+
+__device__ __forceinline__ float pow2f(int e) {   // e in [-126, 127]
+    return __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+}
+__device__ __forceinline__ int moment_exp(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    const int biased = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+    return min(kExpMax, max(kExpMin, 141 - biased));
+}
+__device__ __forceinline__ uint16_t moment_enc(float x, float scale) {
+    return f2h(fminf(fmaxf(x * scale, -65504.0f), 65504.0f));
 }
 
 // Update one active row (index k of matrix M).  `gr` supplies the effective
 // gradient of a 4-column chunk in two parts: gr.load(c) issues the chunk's
-// gradient loads, gr.combine(raw, c, g) forms the gradient from them.  Every
-// load of the row is issued before any arithmetic (one memory round trip for
-// the whole row; rows wider than 16384 columns take two to four); the moments
-// are stored as soon as they are computed, q, delta and the live weights
-// after the row's |w'| maximum.
+// gradient loads, gr.combine(raw, c, g) forms the gradient from them.
+//
+// Pass 1 loads the row (every load of a batch of chunks before any
+// arithmetic), takes the Adam step and reduces the row's maxima of |w'|,
+// |m| and v; pass 2 requantises w' and stores q, delta, the live weights and
+// the moments scaled by their new exponents.  Rows of up to 16384 columns
+// keep w', m and v in registers between the passes; wider rows (kChunks > 4)
+// load and compute the row again in pass 2 (the same operations, so the same
+// values).
 //
 // The workgroup holds kPer rows, each on kThreads/kPer consecutive lanes; in
 // a workgroup of two rows whose second one does not exist (odd row count)
@@ -132,14 +173,19 @@ template <int kThreads, int kChunks, int kPer, typename Grad>
 __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool valid, const AdamDev &hp,
                                            const Grad &gr) {
     constexpr int kLanes = kThreads / kPer;
+    constexpr bool kKeep = kChunks <= 4;
+    constexpr int kKept = kKeep ? kChunks : 1;
     const int lt = static_cast<int>(threadIdx.x) % kLanes;
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[3][kThreads / 64];
     const int64_t C = valid ? M.C : 0;
     const int64_t r = valid ? M.rows[k] : 0;
     const int64_t sl = valid ? M.slot[k] : 0;
     const bool fresh = (valid && M.fresh) ? M.fresh[k] != 0 : false;
     const float s_old = valid ? M.s[r] : 0.0f;
     const int32_t t_old = (fresh || !valid) ? 0 : M.t[sl];
+    const int em_old = (fresh || !valid) ? 0 : static_cast<int>(M.mv_exp[2 * sl]);
+    const int ev_old = (fresh || !valid) ? 0 : static_cast<int>(M.mv_exp[2 * sl + 1]);
+    const float dec_m = pow2f(-em_old), dec_v = pow2f(-ev_old);
     const int8_t *__restrict__ qrow = M.q + r * C;
     const float *__restrict__ drow = M.delta + r * C;
     uint16_t *mrow = M.m + sl * C;
@@ -147,15 +193,17 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
 
     const int32_t step = t_old + 1;
     const int32_t ti = min(step, hp.t_max);
-    float bc1 = 0.0f, bc2 = 0.0f;
+    const float bc1 = valid ? hp.bc1[ti] : 1.0f;
+    const float bc2 = valid ? hp.bc2[ti] : 1.0f;
 
     // Wide rows on 1024-lane workgroups go in batches of chunks (registers).
     constexpr int kBatch = Grad::template batch<kThreads, kChunks>();
     static_assert(kChunks % kBatch == 0, "batch");
-    float wn[kChunks][4];
-    float amax = 0.0f;
-#pragma unroll
-    for (int b0 = 0; b0 < kChunks; b0 += kBatch) {
+    float wn[kKept][4], mn[kKept][4], vn[kKept][4];
+    float amax = 0.0f, mmax = 0.0f, vmax = 0.0f;
+
+    // Loads and Adam step of chunks [b0, b0 + kBatch): fn(j, e, w', m, v) per element.
+    auto step_batch = [&](int b0, auto &&fn) __attribute__((always_inline)) {
         typename Grad::Raw graw[kBatch];
         char4 qv[kBatch];
         float4 dv[kBatch];
@@ -176,10 +224,6 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
                 }
             }
         }
-        if (b0 == 0 && valid) {
-            bc1 = hp.bc1[ti];
-            bc2 = hp.bc2[ti];
-        }
 #pragma unroll
         for (int jb = 0; jb < kBatch; ++jb) {
             const int j = b0 + jb;
@@ -192,68 +236,104 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
                 const float df[4] = {dv[jb].x, dv[jb].y, dv[jb].z, dv[jb].w};
                 const uint16_t mh[4] = {mv[jb].x, mv[jb].y, mv[jb].z, mv[jb].w};
                 const uint16_t vh[4] = {vv[jb].x, vv[jb].y, vv[jb].z, vv[jb].w};
-                uint16_t mo[4], vo[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float sq = s_old * qf[e];
                     const float w = sq + df[e];
-                    const float m_a = hp.beta1 * h2f(mh[e]);
+                    const float m_old = h2f(mh[e]) * dec_m;
+                    const float v_old = h2f(vh[e]) * dec_v;
+                    const float m_a = hp.beta1 * m_old;
                     const float m_b = hp.c1 * g[e];
                     const float m = m_a + m_b;
                     const float gg = g[e] * g[e];
-                    const float v_a = hp.beta2 * h2f(vh[e]);
+                    const float v_a = hp.beta2 * v_old;
                     const float v_b = hp.c2 * gg;
                     const float v = v_a + v_b;
-                    mo[e] = f2h(m);
-                    vo[e] = f2h(v);
                     const float mhat = m / bc1;
                     const float vhat = v / bc2;
                     const float denom = __builtin_sqrtf(vhat) + hp.eps;
                     const float ratio = mhat / denom;
                     const float u = hp.lr * ratio;
                     const float w1 = hp.wd != 0.0f ? w * hp.decay : w;
-                    const float wnew = w1 - u;
-                    wn[j][e] = wnew;
-                    amax = fmaxf(amax, fabsf(wnew));
+                    fn(j, e, w1 - u, m, v);
                 }
-                *reinterpret_cast<ushort4 *>(mrow + c) = make_ushort4(mo[0], mo[1], mo[2], mo[3]);
-                *reinterpret_cast<ushort4 *>(vrow + c) = make_ushort4(vo[0], vo[1], vo[2], vo[3]);
             }
         }
-    }
-    amax = block_max_nonneg<kThreads, kLanes>(amax, red);
+    };
+
+    // pass 1
+#pragma unroll
+    for (int b0 = 0; b0 < kChunks; b0 += kBatch)
+        step_batch(b0, [&](int j, int e, float w, float m, float v) __attribute__((always_inline)) {
+            if constexpr (kKeep) {
+                wn[j][e] = w;
+                mn[j][e] = m;
+                vn[j][e] = v;
+            }
+            amax = fmaxf(amax, fabsf(w));
+            mmax = fmaxf(mmax, fabsf(m));
+            vmax = fmaxf(vmax, fabsf(v));
+        });
+    block_max3_nonneg<kThreads, kLanes>(amax, mmax, vmax, red);
     const float s_new = amax / 127.0f;
+    const int em = moment_exp(mmax), ev = moment_exp(vmax);
+    const float enc_m = pow2f(em), enc_v = pow2f(ev);
     if (lt == 0 && valid) {
         M.s[r] = s_new;
         M.t[sl] = step;
+        M.mv_exp[2 * sl] = static_cast<int8_t>(em);
+        M.mv_exp[2 * sl + 1] = static_cast<int8_t>(ev);
     }
+
+    // pass 2
     int8_t *qout = M.q + r * C;
     float *dout = M.delta + r * C;
     uint16_t *wl = M.w_live ? M.w_live + r * C : nullptr;
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
+    auto store_chunk = [&](int j, const float (&w4)[4], const float (&m4)[4], const float (&v4)[4])
+        __attribute__((always_inline)) {
         const int64_t c = 4 * (static_cast<int64_t>(lt) + static_cast<int64_t>(j) * kLanes);
-        if (c < C) {
-            float qf[4], d[4];
-            uint16_t b[4];
+        if (c >= C) return;
+        float qf[4], d[4];
+        uint16_t b[4], mo[4], vo[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float qq = 0.0f;
-                if (s_new != 0.0f) {
-                    qq = __builtin_rintf(wn[j][e] / s_new);
-                    qq = fminf(fmaxf(qq, -127.0f), 127.0f);
-                }
-                const float sq = s_new * qq;
-                d[e] = wn[j][e] - sq;
-                qf[e] = qq;
-                const float back = sq + d[e];
-                b[e] = f2bf(back);
+        for (int e = 0; e < 4; ++e) {
+            float qq = 0.0f;
+            if (s_new != 0.0f) {
+                qq = __builtin_rintf(w4[e] / s_new);
+                qq = fminf(fmaxf(qq, -127.0f), 127.0f);
             }
-            *reinterpret_cast<char4 *>(qout + c) =
-                make_char4(static_cast<signed char>(qf[0]), static_cast<signed char>(qf[1]),
-                           static_cast<signed char>(qf[2]), static_cast<signed char>(qf[3]));
-            *reinterpret_cast<float4 *>(dout + c) = make_float4(d[0], d[1], d[2], d[3]);
-            if (wl) *reinterpret_cast<ushort4 *>(wl + c) = make_ushort4(b[0], b[1], b[2], b[3]);
+            const float sq = s_new * qq;
+            d[e] = w4[e] - sq;
+            qf[e] = qq;
+            const float back = sq + d[e];
+            b[e] = f2bf(back);
+            mo[e] = moment_enc(m4[e], enc_m);
+            vo[e] = moment_enc(v4[e], enc_v);
+        }
+        *reinterpret_cast<char4 *>(qout + c) =
+            make_char4(static_cast<signed char>(qf[0]), static_cast<signed char>(qf[1]),
+                       static_cast<signed char>(qf[2]), static_cast<signed char>(qf[3]));
+        *reinterpret_cast<float4 *>(dout + c) = make_float4(d[0], d[1], d[2], d[3]);
+        if (wl) *reinterpret_cast<ushort4 *>(wl + c) = make_ushort4(b[0], b[1], b[2], b[3]);
+        *reinterpret_cast<ushort4 *>(mrow + c) = make_ushort4(mo[0], mo[1], mo[2], mo[3]);
+        *reinterpret_cast<ushort4 *>(vrow + c) = make_ushort4(vo[0], vo[1], vo[2], vo[3]);
+    };
+    if constexpr (kKeep) {
+#pragma unroll
+        for (int j = 0; j < kChunks; ++j) store_chunk(j, wn[j], mn[j], vn[j]);
+    } else {
+        // Pass 1 read every load of the row before the barrier, so the stores
+        // below cannot overtake a load of the same address.
+#pragma unroll
+        for (int b0 = 0; b0 < kChunks; b0 += kBatch) {
+            float w4[kBatch][4], m4[kBatch][4], v4[kBatch][4];
+            step_batch(b0, [&](int j, int e, float w, float m, float v) __attribute__((always_inline)) {
+                w4[j - b0][e] = w;
+                m4[j - b0][e] = m;
+                v4[j - b0][e] = v;
+            });
+#pragma unroll
+            for (int jb = 0; jb < kBatch; ++jb) store_chunk(b0 + jb, w4[jb], m4[jb], v4[jb]);
         }
     }
 }
@@ -311,8 +391,9 @@ __global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
 // Coupled update: the blend of the clipped own and partner gradients (a row
 // missing from the partner's active set contributes zero).
 struct PairGrad {
+    // two float4 gradient loads per chunk: half the plain batch on wide rows
     template <int kThreads, int kChunks>
-    static constexpr int batch() { return plain_batch<kThreads, kChunks>(); }
+    static constexpr int batch() { return kThreads >= 1024 ? (kChunks >= 8 ? 2 : 4) : kChunks; }
     struct Raw {
         float4 own, part;
     };
@@ -460,7 +541,8 @@ struct CkParams {
 // live -> checkpoint (save) or back (restore); a restore also rebuilds the
 // row's live bf16 weights from the restored values, as the write-back does.
 // Lane l takes chunks l, l + 256, ...; it issues the loads of 4 chunks before
-// its stores.  The row's s and its slot's t are copied by lane 0.
+// its stores.  The row's s and its slot's t and moment exponents are copied
+// by lane 0.
 template <bool kRestore>
 __global__ __launch_bounds__(kCkThreads) void k_rows_copy(const CkParams p) {
     const int64_t wg = blockIdx.x;
@@ -487,9 +569,13 @@ __global__ __launch_bounds__(kCkThreads) void k_rows_copy(const CkParams p) {
         if (kRestore) {
             M.s[r] = s_row;
             M.t[sl] = M.ck_t[k];
+            M.mv_exp[2 * sl] = M.ck_mv_exp[2 * k];
+            M.mv_exp[2 * sl + 1] = M.ck_mv_exp[2 * k + 1];
         } else {
             M.ck_s[k] = M.s[r];
             M.ck_t[k] = M.t[sl];
+            M.ck_mv_exp[2 * k] = M.mv_exp[2 * sl];
+            M.ck_mv_exp[2 * k + 1] = M.mv_exp[2 * sl + 1];
         }
     }
     // One 8-column chunk in registers.  The four chunks of a batch are named
@@ -699,7 +785,7 @@ int check_mat(const sft_upd_mat &m, const char *who) {
     SFT_CHECK(m.n_active <= m.R && m.n_active <= m.n_slots, SFT_ECAPACITY,
               "%s: n_active=%lld exceeds R or n_slots", who, (long long)m.n_active);
     if (m.n_active == 0) return SFT_OK;
-    SFT_CHECK(m.active_rows && m.slot && m.G && m.q && m.s && m.delta && m.m && m.v && m.t,
+    SFT_CHECK(m.active_rows && m.slot && m.G && m.q && m.s && m.delta && m.m && m.v && m.t && m.mv_exp,
               SFT_EINVAL, "%s: null device pointer", who);
     SFT_CHECK(sft::aligned16(m.G) && sft::aligned16(m.q) && sft::aligned16(m.delta) &&
                   sft::aligned16(m.m) && sft::aligned16(m.v) &&
@@ -743,6 +829,7 @@ UpdMatDev make_mat(const sft_upd_mat &m, int64_t row_begin) {
     d.m = m.m;
     d.v = m.v;
     d.t = m.t;
+    d.mv_exp = m.mv_exp;
     d.w_live = m.w_live;
     d.C = m.C;
     d.n_active = m.n_active;
@@ -1041,8 +1128,8 @@ int rows_copy(const sft_ckpt_mat *mats, int32_t n_mats, void *stream, bool resto
         SFT_CHECK(m.C % 8 == 0, SFT_ESHAPE, "%s: matrix %d: C=%lld is not a multiple of 8", who, i,
                   (long long)m.C);
         if (m.n_rows == 0) continue;
-        SFT_CHECK(m.rows && m.slot && m.q && m.s && m.delta && m.m && m.v && m.t && m.ck_q && m.ck_s &&
-                      m.ck_delta && m.ck_m && m.ck_v && m.ck_t,
+        SFT_CHECK(m.rows && m.slot && m.q && m.s && m.delta && m.m && m.v && m.t && m.mv_exp && m.ck_q &&
+                      m.ck_s && m.ck_delta && m.ck_m && m.ck_v && m.ck_t && m.ck_mv_exp,
                   SFT_EINVAL, "%s: matrix %d: null device pointer", who, i);
         SFT_CHECK(sft::aligned16(m.q) && sft::aligned16(m.delta) && sft::aligned16(m.m) && sft::aligned16(m.v) &&
                       sft::aligned16(m.ck_q) && sft::aligned16(m.ck_delta) && sft::aligned16(m.ck_m) &&

@@ -34,9 +34,10 @@ def test_memory_model_matches_page_example():
 
 
 def test_update_bytes_per_element():
-    # 24 bytes per active element with the fused write-back, 22 without
-    assert acc.update_work([(1, 1)]).bytes == 24 + 8
-    assert acc.update_work([(1, 1)], fused_writeback=False).bytes == 22 + 8
+    # 24 bytes per active element with the fused write-back, 22 without; per
+    # row the scale (read + write 8) and the two moment exponents (read + write 4)
+    assert acc.update_work([(1, 1)]).bytes == 24 + 12
+    assert acc.update_work([(1, 1)], fused_writeback=False).bytes == 22 + 12
 
 
 def test_masked_dw_work_llama_layer():
@@ -57,10 +58,11 @@ def test_masked_dw_work_llama_layer():
 def test_coupled_update_bytes():
     # one pair of 64-column matrices: 3 rows listed by a, 2 by b, 1 by both.
     # Per listed row element: read g 4, q 1, delta 4, m 2, v 2; write q 1,
-    # delta 4, m 2, v 2, live bf16 2 (24 in all); per row s read + write (8);
-    # a shared row also reads the partner's fp32 gradient row.
+    # delta 4, m 2, v 2, live bf16 2 (24 in all); per row s and the moment
+    # exponents read + write (12); a shared row also reads the partner's fp32
+    # gradient row.
     w = acc.coupled_update_work([(64, 3, 1), (64, 2, 1)])
-    assert w.bytes == (3 + 2) * 64 * 24 + (3 + 2) * 8 + 2 * 64 * 4
+    assert w.bytes == (3 + 2) * 64 * 24 + (3 + 2) * 12 + 2 * 64 * 4
 
 
 def test_writeback_and_embedding_bytes():
@@ -72,10 +74,11 @@ def test_writeback_and_embedding_bytes():
 
 def test_checkpoint_bytes():
     # 3 rows of 16 columns: q 1 + delta 4 + m 2 + v 2 read and written per
-    # element, s and t read and written per row; a restore writes bf16 too
-    assert acc.checkpoint_work([(16, 3)]).bytes == 3 * 16 * 18 + 3 * 16
-    assert acc.checkpoint_work([(16, 3)], restore=True).bytes == 3 * 16 * 20 + 3 * 16
-    assert acc.checkpoint_work([(16, 3)], restore=True, live=False).bytes == 3 * 16 * 18 + 3 * 16
+    # element, s, t and the two moment exponents read and written per row; a
+    # restore writes bf16 too
+    assert acc.checkpoint_work([(16, 3)]).bytes == 3 * 16 * 18 + 3 * 20
+    assert acc.checkpoint_work([(16, 3)], restore=True).bytes == 3 * 16 * 20 + 3 * 20
+    assert acc.checkpoint_work([(16, 3)], restore=True, live=False).bytes == 3 * 16 * 18 + 3 * 20
 
 
 def test_leaf_bytes():

@@ -5,13 +5,18 @@ configuration the benchmark times: q, k, v, o 4096x4096, gate and up
 seven masked dW products in one call (q/k/v and gate/up sharing their input),
 then the sparse update with fused write-back of all seven in one call.
 
-The oracle cannot afford every row at this size, so it checks a seeded
-sample of active rows of every matrix: their dW rows element by element
-(same tolerance as the small cases), and their whole update (q, s, delta, m,
-v, t and the live bf16 row) bit for bit, given the GPU's dW.  Rows outside
-the active set are checked bit-unchanged on a sample.  Method:
+Every active row of the 1% layer (425 rows) is checked: its dW row element
+by element against the oracle (same tolerance as the small cases; the
+oracle's rows are shared out over host threads), and its whole update (q, s,
+delta, m, v, t, the moment exponents and the live bf16 row) bit for bit,
+given the GPU's dW.  The end-to-end gate then runs the benchmark's fused call
+from a mid-run state and compares it with the oracle's own dW fed to the
+oracle's update, within the bounds of tests/gpu_helpers.update_gate (q' flips
+only at .5 ties, each reported).  Rows outside the active set are checked
+bit-unchanged on a sample.  The other workloads (adversarial coupled layer,
+embedding, densities, token shares) check sampled rows.  Method:
 "Sparse-First Fine-Tuning: Full-Weight Training at the Cost of the Active
-Set", sections 2.1-2.3.
+Set", sections 2.1-2.4.
 """
 import numpy as np
 import pytest
@@ -19,13 +24,15 @@ import torch
 
 import oracle
 from sparse_full_weight_amd import _lib, synth
-from tests.gpu_helpers import adam_dev, bf16_dev, dev, dw_close, host_u16
+from tests.gpu_helpers import (adam_dev, bf16_dev, dev, dw_close, host_u16, oracle_dw_threads, u16_dev,
+                               update_gate)
 
 pytestmark = pytest.mark.gpu
 
 T = 4096
 DENSITY = 0.01
-ROWS_PER_MAT = 4          # sampled active rows per matrix
+ROWS_PER_MAT = 4          # sampled active rows per matrix (the workloads beyond the 1% layer)
+HP = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
 
 
 def _layer(seed):
@@ -53,8 +60,19 @@ def layer():
     return _layer(7000)
 
 
+@pytest.fixture(scope="module")
+def layer_oracle_dw(layer):
+    """The oracle's dW of every active row of every matrix of the 1% layer."""
+    X, mats = layer
+    out = {}
+    for name, m in mats.items():
+        plan = _lib.sft_plan_rows(m["mask"])
+        out[name] = oracle_dw_threads(m["dY"], X[m["group"]], plan.active_rows)
+    return out
+
+
 @pytest.mark.parametrize("layout", [_lib.SFT_DW_PACKED, _lib.SFT_DW_TILES], ids=["packed", "tiles"])
-def test_llama7b_layer_dw_and_update_sampled(gpu_lib, layer, layout):
+def test_llama7b_layer_dw_and_update_all_rows(gpu_lib, layer, layer_oracle_dw, layout):
     X, mats = layer
     rng = synth.rng(7777)
     Xd = {g: bf16_dev(x) for g, x in X.items()}
@@ -74,17 +92,17 @@ def test_llama7b_layer_dw_and_update_sampled(gpu_lib, layer, layout):
     _lib.sft_masked_dw(groups, ws)
     torch.cuda.synchronize()
 
-    # dW: sampled active rows of every matrix against the fp64 oracle
+    # dW: every active row of every matrix against the fp64 oracle
     G_host = {}
+    total = 0
     for name, m in mats.items():
         plan = gpu[name]["plan"]
         got = gpu[name]["out"].cpu().numpy()
         assert np.all(np.isnan(got[plan.n_active:])), "write past the last active row"
         G_host[name] = got[:plan.n_active]
-        pick = np.sort(rng.choice(plan.n_active, size=ROWS_PER_MAT, replace=False))
-        pick[-1] = plan.n_active - 1                      # the last active row, always
-        want = oracle.masked_dw(m["dY"], X[m["group"]], plan.active_rows[pick])
-        dw_close(G_host[name][pick], want)
+        dw_close(G_host[name], layer_oracle_dw[name])
+        total += plan.n_active
+    assert total == 425
 
     # update with fused write-back of all seven matrices in one call, fresh moments
     hp = adam_dev()
@@ -92,16 +110,9 @@ def test_llama7b_layer_dw_and_update_sampled(gpu_lib, layer, layout):
     for name, m in mats.items():
         plan = gpu[name]["plan"]
         n = plan.n_active
-        st = {"q": dev(m["q"]), "s": dev(m["s"]), "delta": dev(m["delta"]),
-              "m": torch.zeros((n, m["C"]), dtype=torch.int16, device="cuda"),
-              "v": torch.zeros((n, m["C"]), dtype=torch.int16, device="cuda"),
-              "t": torch.zeros(n, dtype=torch.int32, device="cuda"),
-              "w": torch.zeros((m["R"], m["C"]), dtype=torch.int16, device="cuda"),
-              "slot": dev(np.arange(n, dtype=np.int32)),
-              "fresh": dev(np.ones(n, np.uint8))}
+        st = _dev_state(m, n)
         dev_state[name] = st
-        upd.append(_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], gpu[name]["dplan"].active_rows,
-                               st["slot"], gpu[name]["out"][:n], n, st["fresh"], st["w"]))
+        upd.append(_upd(st, gpu[name]["dplan"].active_rows, gpu[name]["out"][:n], n))
     _lib.sft_sparse_update(upd, hp)
     torch.cuda.synchronize()
 
@@ -109,32 +120,66 @@ def test_llama7b_layer_dw_and_update_sampled(gpu_lib, layer, layout):
         plan = gpu[name]["plan"]
         n, C = plan.n_active, m["C"]
         st = dev_state[name]
-        pick = np.sort(rng.choice(n, size=ROWS_PER_MAT, replace=False))
-        rows = plan.active_rows[pick]
-        # oracle on the sampled rows only: a state holding just those rows
-        sub = oracle.MatState(m["q"][rows].copy(), m["s"][rows].copy(), m["delta"][rows].copy(),
-                              np.zeros((pick.size, C), np.uint16), np.zeros((pick.size, C), np.uint16),
-                              np.zeros(pick.size, np.int32), np.zeros((pick.size, C), np.uint16))
-        oracle.sparse_update(sub, G_host[name][pick], np.arange(pick.size, dtype=np.int32),
-                             np.arange(pick.size, dtype=np.int32), np.ones(pick.size, np.uint8),
-                             lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+        rows = plan.active_rows
+        pos = np.arange(n)
+        # oracle on the active rows: a state holding just those rows
+        sub = _sub_state(m, rows, C)
+        oracle.sparse_update(sub, G_host[name], pos.astype(np.int32), pos.astype(np.int32), np.ones(n, np.uint8),
+                             **HP)
+        _assert_rows(st, rows, pos, sub, name)
+        # inactive rows: bit-unchanged state, untouched live weights
         q = st["q"].cpu().numpy()
         s = st["s"].cpu().numpy()
         delta = st["delta"].cpu().numpy()
-        assert np.array_equal(q[rows], sub.q), name
-        assert np.array_equal(s[rows].view(np.uint32), sub.s.view(np.uint32)), name
-        assert np.array_equal(delta[rows].view(np.uint32), sub.delta.view(np.uint32)), name
-        assert np.array_equal(host_u16(st["m"])[pick], sub.m), name
-        assert np.array_equal(host_u16(st["v"])[pick], sub.v), name
-        assert np.array_equal(st["t"].cpu().numpy()[pick], sub.t), name
-        assert np.array_equal(host_u16(st["w"])[rows], sub.w_live), name
-        # inactive rows: bit-unchanged state, untouched live weights
         idle = np.setdiff1d(np.arange(m["R"]), plan.active_rows)
         idle = idle[rng.choice(idle.size, size=min(64, idle.size), replace=False)]
         assert np.array_equal(q[idle], m["q"][idle]), name
         assert np.array_equal(s[idle].view(np.uint32), m["s"][idle].view(np.uint32)), name
         assert np.array_equal(delta[idle].view(np.uint32), m["delta"][idle].view(np.uint32)), name
         assert not host_u16(st["w"])[idle].any(), name
+
+
+def test_llama7b_layer_end_to_end_gate(gpu_lib, layer, layer_oracle_dw):
+    """The benchmark's fused call (masked dW of all seven matrices with the
+    update and write-back fused in) from a mid-run state, against the
+    oracle's dW fed to the oracle's update, on every active row: the
+    end-to-end bounds of update_gate; every q' flip is printed with its
+    distance to the .5 tie."""
+    X, mats = layer
+    Xd = {g: bf16_dev(x) for g, x in X.items()}
+    groups, upd, states, plans = [], [], {}, {}
+    for gname, members in synth.LLAMA7B_GROUPS:
+        ms = []
+        for name in members:
+            m = mats[name]
+            plan = _lib.sft_plan_rows(m["mask"])
+            plans[name] = plan
+            n = plan.n_active
+            dplan = plan.to_device()
+            out = torch.zeros((n, m["C"]), dtype=torch.float32, device="cuda")
+            ms.append(_lib.DwMat(bf16_dev(m["dY"]), dplan, out))
+            st = _dev_state(m, n, mid_run_seed=7050 + list(mats).index(name))
+            states[name] = st
+            upd.append(_upd(st, dplan.active_rows, out, n))
+        groups.append(_lib.DwGroup(Xd[gname], ms, _lib.SFT_DW_PACKED))
+    ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device="cuda")
+    _lib.sft_masked_dw_update(groups, ws, upd, adam_dev())
+    torch.cuda.synchronize()
+    reports = []
+    for name, m in mats.items():
+        plan = plans[name]
+        n, C = plan.n_active, m["C"]
+        pos = np.arange(n, dtype=np.int32)
+        want = _sub_state(m, plan.active_rows, C, mid_run_seed=7050 + list(mats).index(name))
+        oracle.sparse_update(want, layer_oracle_dw[name], pos, pos, np.zeros(n, np.uint8), **HP)
+        got = _host_sub(states[name], plan.active_rows, pos)
+        reports.append(update_gate(got, want, pos, pos, name, layer_oracle_dw[name]))
+    for r in reports:
+        print(f"[gate] {r['what']}: {r['rows']} rows, {r['flips']} q' flips "
+              f"(tie distances in ulps: {[round(d, 2) for d in r['flip_tie_dist_ulp']]}), "
+              f"max |dw'|/s' {r['max_w_err_over_s']:.2e}; m, v at {r['max_m_err_of_bound']:.2f}, "
+              f"{r['max_v_err_of_bound']:.2f} of their bounds, {r['m_beyond_one_unit']} and "
+              f"{r['v_beyond_one_unit']} elements beyond one fp16 unit", flush=True)
 
 
 @pytest.mark.parametrize("layout", [_lib.SFT_DW_PACKED, _lib.SFT_DW_TILES], ids=["packed", "tiles"])
@@ -158,8 +203,7 @@ def test_llama7b_layer_fused_update_matches_two_calls(gpu_lib, layer, layout):
                 ms.append(_lib.DwMat(bf16_dev(m["dY"]), dplan, out))
                 st = _dev_state(m, n)
                 states[name] = st
-                upd.append(_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], dplan.active_rows,
-                                       st["slot"], out, n, st["fresh"], st["w"]))
+                upd.append(_upd(st, dplan.active_rows, out, n))
             groups.append(_lib.DwGroup(Xd[gname], ms, layout))
         ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device="cuda")
         hp = adam_dev()
@@ -173,19 +217,34 @@ def test_llama7b_layer_fused_update_matches_two_calls(gpu_lib, layer, layout):
 
     a, b = run(True), run(False)
     for name in mats:
-        for key in ("q", "s", "delta", "m", "v", "t", "w"):
+        for key in ("q", "s", "delta", "m", "v", "t", "e", "w"):
             x, y = a[name][key], b[name][key]
             if x.dtype == torch.float32:
                 x, y = x.view(torch.int32), y.view(torch.int32)
             assert torch.equal(x, y), f"{name} {key}"
 
 
-def _sub_state(m, rows, C):
-    """Oracle state holding only the given rows (fresh moments)."""
+def _sub_state(m, rows, C, mid_run_seed=None, pos=None, n_slots=None):
+    """Oracle state holding only the given rows (slot k = row k): fresh
+    moments, or the mid-run moments `_dev_state` draws with the same seed
+    for n_slots slots, taken at slots `pos` (default: 0, 1, ...)."""
     n = rows.size
-    return oracle.MatState(m["q"][rows].copy(), m["s"][rows].copy(), m["delta"][rows].copy(),
-                           np.zeros((n, C), np.uint16), np.zeros((n, C), np.uint16), np.zeros(n, np.int32),
-                           np.zeros((n, C), np.uint16))
+    if mid_run_seed is None:
+        mm, vv, t, e = synth.moments(n, C, 0, mid_run=False)
+    else:
+        pos = np.arange(n) if pos is None else np.asarray(pos)
+        mm, vv, t, e = synth.moments(n if n_slots is None else n_slots, C, mid_run_seed, mid_run=True)
+        mm, vv, t, e = mm[pos], vv[pos], t[pos], e[pos]
+    return oracle.MatState(m["q"][rows].copy(), m["s"][rows].copy(), m["delta"][rows].copy(), mm, vv, t,
+                           np.zeros((n, C), np.uint16), e=e)
+
+
+def _host_sub(st, rows, pos):
+    """Host copy of a GPU state's rows `rows` and moment slots `pos`, shaped as
+    _sub_state (row k = rows[k], slot k = pos[k])."""
+    return oracle.MatState(st["q"].cpu().numpy()[rows], st["s"].cpu().numpy()[rows],
+                           st["delta"].cpu().numpy()[rows], host_u16(st["m"])[pos], host_u16(st["v"])[pos],
+                           st["t"].cpu().numpy()[pos], host_u16(st["w"])[rows], e=st["e"].cpu().numpy()[pos])
 
 
 def _assert_rows(st, rows, pos, sub, what):
@@ -195,16 +254,28 @@ def _assert_rows(st, rows, pos, sub, what):
     assert np.array_equal(st["delta"].cpu().numpy()[rows].view(np.uint32), sub.delta.view(np.uint32)), what
     assert np.array_equal(host_u16(st["m"])[pos], sub.m), what
     assert np.array_equal(host_u16(st["v"])[pos], sub.v), what
+    assert np.array_equal(st["t"].cpu().numpy()[pos], sub.t), what
+    assert np.array_equal(st["e"].cpu().numpy()[pos], sub.e), what
     assert np.array_equal(host_u16(st["w"])[rows], sub.w_live), what
 
 
-def _dev_state(m, n):
-    return {"q": dev(m["q"]), "s": dev(m["s"]), "delta": dev(m["delta"]),
-            "m": torch.zeros((n, m["C"]), dtype=torch.int16, device="cuda"),
-            "v": torch.zeros((n, m["C"]), dtype=torch.int16, device="cuda"),
-            "t": torch.zeros(n, dtype=torch.int32, device="cuda"),
-            "w": torch.zeros((m["R"], m["C"]), dtype=torch.int16, device="cuda"),
-            "slot": dev(np.arange(n, dtype=np.int32)), "fresh": dev(np.ones(n, np.uint8))}
+def _dev_state(m, n, mid_run_seed=None):
+    """GPU state of a matrix with n moment slots: fresh (zero moments, every
+    row flagged fresh) or the seeded mid-run moments of `_sub_state`."""
+    if mid_run_seed is None:
+        mm, vv, t, e = synth.moments(n, m["C"], 0, mid_run=False)
+        fresh = np.ones(n, np.uint8)
+    else:
+        mm, vv, t, e = synth.moments(n, m["C"], mid_run_seed, mid_run=True)
+        fresh = np.zeros(n, np.uint8)
+    return {"q": dev(m["q"]), "s": dev(m["s"]), "delta": dev(m["delta"]), "m": u16_dev(mm), "v": u16_dev(vv),
+            "t": dev(t), "e": dev(e), "w": torch.zeros((m["R"], m["C"]), dtype=torch.int16, device="cuda"),
+            "slot": dev(np.arange(n, dtype=np.int32)), "fresh": dev(fresh)}
+
+
+def _upd(st, active_rows, G, n):
+    return _lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], st["e"], active_rows,
+                       st["slot"], G, n, st["fresh"], st["w"])
 
 
 def test_llama7b_adversarial_one_row_per_tile_coupled(gpu_lib, layer):
@@ -215,18 +286,7 @@ def test_llama7b_adversarial_one_row_per_tile_coupled(gpu_lib, layer):
     import math
     X, base = layer
     rng = synth.rng(7100)
-    mats = {}
-    for mi, name in enumerate(synth.LLAMA7B):
-        mats[name] = dict(base[name])
-        rows = synth.one_per_tile_rows(base[name]["R"], 7200 + mi)
-        mats[name]["rows"] = rows
-    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
-    for a, b in pairs:
-        ra, rb = mats[a]["rows"].copy(), mats[b]["rows"].copy()
-        rb[::2] = ra[::2]                       # same row in every other tile
-        mats[b]["rows"] = rb
-    for name, m in mats.items():
-        m["mask"] = synth.mask_from_rows(m["R"], m["rows"])
+    mats, pairs = _adversarial_mats(base)
 
     groups, gpu = [], {}
     for gname, members in synth.LLAMA7B_GROUPS:
@@ -255,9 +315,7 @@ def test_llama7b_adversarial_one_row_per_tile_coupled(gpu_lib, layer):
     st = {name: _dev_state(m, gpu[name]["plan"].n_active) for name, m in mats.items()}
 
     def upd(name):
-        s_ = st[name]
-        return _lib.UpdMat(s_["q"], s_["s"], s_["delta"], s_["m"], s_["v"], s_["t"], gpu[name]["dplan"].active_rows,
-                           s_["slot"], gpu[name]["out"], gpu[name]["plan"].n_active, s_["fresh"], s_["w"])
+        return _upd(st[name], gpu[name]["dplan"].active_rows, gpu[name]["out"], gpu[name]["plan"].n_active)
     _lib.sft_coupled_update([_lib.Pair(upd(a), upd(b), a_own, a_cross) for a, b in pairs], hp)
     _lib.sft_sparse_update([upd("down")], hp)
     torch.cuda.synchronize()
@@ -281,9 +339,9 @@ def test_llama7b_adversarial_one_row_per_tile_coupled(gpu_lib, layer):
         for side, (name, sub, inside, idx) in enumerate([(a, sa, in_a, ia), (b, sb, in_b, ib)]):
             rows = S[inside]
             got = {k: v for k, v in st[name].items()}
-            sub_rows = oracle.MatState(sub.q[inside], sub.s[inside], sub.delta[inside],
-                                       sub.m[np.nonzero(inside)[0]], sub.v[np.nonzero(inside)[0]],
-                                       sub.t[np.nonzero(inside)[0]], sub.w_live[inside])
+            k = np.nonzero(inside)[0]
+            sub_rows = oracle.MatState(sub.q[inside], sub.s[inside], sub.delta[inside], sub.m[k], sub.v[k],
+                                       sub.t[k], sub.w_live[inside], e=sub.e[k])
             _assert_rows(got, rows, idx[inside], sub_rows, f"{name} (pair {a},{b})")
             untouched = S[~inside]
             assert np.array_equal(got["q"].cpu().numpy()[untouched], mats[name]["q"][untouched])
@@ -298,6 +356,128 @@ def test_llama7b_adversarial_one_row_per_tile_coupled(gpu_lib, layer):
                          np.arange(pick.size, dtype=np.int32), np.ones(pick.size, np.uint8),
                          lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd)
     _assert_rows(st["down"], rows, pick, sub, "down")
+
+
+def _adversarial_mats(base):
+    """One active row in every 32-row tile of every matrix (seeded offsets);
+    a pair's second matrix shares the first one's row in every other tile."""
+    mats = {}
+    for mi, name in enumerate(synth.LLAMA7B):
+        mats[name] = dict(base[name])
+        mats[name]["rows"] = synth.one_per_tile_rows(base[name]["R"], 7200 + mi)
+    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
+    for a, b in pairs:
+        rb = mats[b]["rows"].copy()
+        rb[::2] = mats[a]["rows"][::2]
+        mats[b]["rows"] = rb
+    for m in mats.values():
+        m["mask"] = synth.mask_from_rows(m["R"], m["rows"])
+    return mats, pairs
+
+
+def test_llama7b_adversarial_coupled_step_end_to_end_gate(gpu_lib, layer):
+    """The adversarial workload as one step, as the benchmark times it: one
+    active row in every 32-row tile, packed dW of all seven matrices, the
+    coupled update of (gate, up), (q, o), (k, v) at coupling strength 0.6 with
+    the mixing coefficients the schedule gives at its first step, weight decay
+    0.01 cos(28.4 deg), and the plain update of down, from a mid-run state.
+    Against the oracle's dW fed to the oracle's coupled and plain updates on
+    a seeded quarter of each pair's union rows (both sides) and of down's
+    rows: the end-to-end bounds of update_gate, every q' flip reported."""
+    import math
+    X, base = layer
+    mats, pairs = _adversarial_mats(base)
+    rng = synth.rng(7150)
+    helix = _lib.Helix()
+    helix.step(6.17)
+    a_own, a_cross = helix.coupling(0.6, 0.0)
+    assert a_own == 1.0 and 0.0 < a_cross < 0.3
+    wd = float(np.float32(0.01 * math.cos(math.radians(28.4))))
+    groups, gpu = [], {}
+    for gname, members in synth.LLAMA7B_GROUPS:
+        ms = []
+        for name in members:
+            m = mats[name]
+            plan = _lib.sft_plan_rows(m["mask"])
+            out = torch.empty((plan.n_active, m["C"]), dtype=torch.float32, device="cuda")
+            gpu[name] = {"plan": plan, "dplan": plan.to_device(), "out": out,
+                         "seed": 7160 + list(mats).index(name)}
+            gpu[name]["st"] = _dev_state(m, plan.n_active, mid_run_seed=gpu[name]["seed"])
+            ms.append(_lib.DwMat(bf16_dev(m["dY"]), gpu[name]["dplan"], out))
+        groups.append(_lib.DwGroup(bf16_dev(X[gname]), ms, _lib.SFT_DW_PACKED))
+    ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device="cuda")
+    hp = adam_dev(weight_decay=wd)
+
+    def upd(name):
+        g = gpu[name]
+        return _upd(g["st"], g["dplan"].active_rows, g["out"], g["plan"].n_active)
+    _lib.sft_masked_dw(groups, ws)
+    _lib.sft_coupled_update([_lib.Pair(upd(a), upd(b), a_own, a_cross) for a, b in pairs], hp)
+    _lib.sft_sparse_update([upd("down")], hp)
+    torch.cuda.synchronize()
+
+    def side(name, S):
+        """Positions of rows S in the matrix's active list (-1 where inactive)."""
+        act = gpu[name]["plan"].active_rows
+        i = np.searchsorted(act, S)
+        hit = (i < act.size) & (act[np.minimum(i, act.size - 1)] == S)
+        return np.where(hit, i, -1)
+
+    kw = dict(HP, weight_decay=wd)
+    reports = []
+    for a, b in pairs:
+        union = np.union1d(gpu[a]["plan"].active_rows, gpu[b]["plan"].active_rows)
+        S = np.sort(rng.choice(union, size=union.size // 4, replace=False)).astype(np.int32)
+        pa, pb = side(a, S), side(b, S)
+        ins = {a: pa >= 0, b: pb >= 0}
+        assert ins[a].any() and ins[b].any() and (ins[a] & ins[b]).any() and (ins[a] ^ ins[b]).any()
+        C = mats[a]["C"]
+        # both sides' oracle states hold every sampled row (row i = S[i]); a
+        # side's active rows are the positions of its own rows in S, so the
+        # pair's rows line up by position as they do by row on the GPU
+        subs, grads, local = {}, {}, {}
+        for name, p in ((a, pa), (b, pb)):
+            local[name] = np.nonzero(ins[name])[0].astype(np.int32)
+            subs[name] = _sub_state(mats[name], S, C, gpu[name]["seed"], pos=p[ins[name]],
+                                    n_slots=gpu[name]["plan"].n_active)
+            grads[name] = oracle_dw_threads(mats[name]["dY"], X[mats[name]["group"]], S[ins[name]])
+        na, nb = local[a].size, local[b].size
+        oracle.coupled_update(subs[a], grads[a], local[a], np.arange(na, dtype=np.int32), np.zeros(na, np.uint8),
+                              subs[b], grads[b], local[b], np.arange(nb, dtype=np.int32), np.zeros(nb, np.uint8),
+                              a_own=a_own, a_cross=a_cross, **kw)
+        for name, p in ((a, pa), (b, pb)):
+            li = local[name]
+            sub = subs[name]
+            want = oracle.MatState(sub.q[li], sub.s[li], sub.delta[li], sub.m, sub.v, sub.t, sub.w_live[li], e=sub.e)
+            got = _host_sub(gpu[name]["st"], S[li], p[li])
+            k = np.arange(li.size)
+            # the blended gradient the pair's update saw, from the oracle's dW
+            gi = grads[name]
+            other = b if name == a else a
+            go = np.zeros_like(gi)
+            pos_other = {int(r): j for j, r in enumerate(S[ins[other]])}
+            for j, r in enumerate(S[li]):
+                if int(r) in pos_other:
+                    go[j] = grads[other][pos_other[int(r)]]
+            blend = np.abs(a_own * gi.astype(np.float64)) + np.abs(a_cross * go.astype(np.float64))
+            reports.append(update_gate(got, want, k, k, f"{name} (pair {a}, {b})", blend))
+            untouched = S[~ins[name]]
+            assert np.array_equal(gpu[name]["st"]["q"].cpu().numpy()[untouched], mats[name]["q"][untouched])
+            assert not host_u16(gpu[name]["st"]["w"])[untouched].any()
+    plan = gpu["down"]["plan"]
+    pick = np.sort(rng.choice(plan.n_active, size=plan.n_active // 4, replace=False))
+    rows = plan.active_rows[pick]
+    sub = _sub_state(mats["down"], rows, mats["down"]["C"], gpu["down"]["seed"], pos=pick, n_slots=plan.n_active)
+    g = oracle_dw_threads(mats["down"]["dY"], X["down"], rows)
+    k = np.arange(pick.size, dtype=np.int32)
+    oracle.sparse_update(sub, g, k, k, np.zeros(k.size, np.uint8), **kw)
+    reports.append(update_gate(_host_sub(gpu["down"]["st"], rows, pick), sub, k, k, "down (plain)", g))
+    for r in reports:
+        print(f"[gate] {r['what']}: {r['rows']} rows, {r['flips']} q' flips "
+              f"(tie distances in ulps: {[round(d, 2) for d in r['flip_tie_dist_ulp']]}), "
+              f"max |dw'|/s' {r['max_w_err_over_s']:.2e}; m, v at {r['max_m_err_of_bound']:.2f}, "
+              f"{r['max_v_err_of_bound']:.2f} of their bounds, {r['m_beyond_one_unit']} and "
+              f"{r['v_beyond_one_unit']} elements beyond one fp16 unit", flush=True)
 
 
 def test_embedding_32000x4096_conductor_gradient_update(gpu_lib):
@@ -326,8 +506,7 @@ def test_embedding_32000x4096_conductor_gradient_update(gpu_lib):
     m = {"q": q, "s": s, "delta": delta, "R": V, "C": d}
     st = _dev_state(m, plan.n_active)
     dplan = plan.to_device()
-    _lib.sft_sparse_update([_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], dplan.active_rows,
-                                        st["slot"], dev(G), plan.n_active, st["fresh"], st["w"])], adam_dev())
+    _lib.sft_sparse_update([_upd(st, dplan.active_rows, dev(G), plan.n_active)], adam_dev())
     torch.cuda.synchronize()
     pick = np.sort(synth.rng(7330).choice(plan.n_active, size=6, replace=False))
     rows = plan.active_rows[pick]
@@ -418,8 +597,7 @@ def _check_step(layer, density, tokens, seed):
                 ms.append(_lib.DwMat(bf16_dev(m["dY"]), dplan, out))
                 st = _dev_state(m, n)
                 states[name] = st
-                upd.append(_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], dplan.active_rows,
-                                       st["slot"], out, n, st["fresh"], st["w"]))
+                upd.append(_upd(st, dplan.active_rows, out, n))
             groups.append(_lib.DwGroup(Xd[gname], ms, _lib.SFT_DW_PACKED))
         ws = torch.zeros(max(_lib.sft_masked_dw_workspace(groups) // 4, 1), dtype=torch.int32, device="cuda")
         hp = adam_dev()
@@ -434,7 +612,7 @@ def _check_step(layer, density, tokens, seed):
     a, _ = run(True)
     b, G = run(False)
     for name in mats:
-        for key in ("q", "s", "delta", "m", "v", "t", "w"):
+        for key in ("q", "s", "delta", "m", "v", "t", "e", "w"):
             x, y = a[name][key], b[name][key]
             if x.dtype == torch.float32:
                 x, y = x.view(torch.int32), y.view(torch.int32)

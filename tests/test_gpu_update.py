@@ -287,3 +287,56 @@ def test_coupled_update_driven_by_the_schedule(gpu_lib):
                               a_cross=float(np.float32(a_cross)), clip_a=1.0, clip_b=1.0, weight_decay=0.0, **HP)
         assert_state_equal(ma.to_state(), wa, f"step {step} A")
         assert_state_equal(mb.to_state(), wb, f"step {step} B")
+
+
+def test_binding_rejects_mismatched_tensors(gpu_lib):
+    """The binding checks every tensor's dtype and shape before the library
+    sees the pointers (the kernels trust the sizes)."""
+    st, rows, slot, fresh, G = _case(64, 32, 4, 6, 1600, True)
+    m = GpuMat(st, G, rows, slot, fresh)
+    ok = m.upd()
+    bad_cases = [
+        ("m", m.m[:, :16], ValueError),                                   # wrong width
+        ("v", m.v[:3], ValueError),                                       # slot count disagrees with m
+        ("t", m.t[:2], ValueError),
+        ("mv_exp", m.e[:, :1].contiguous(), ValueError),
+        ("G", m.G.to(torch.float64), TypeError),                          # wrong dtype
+        ("G", m.G[:2], ValueError),                                       # fewer rows than n_active
+        ("delta", m.delta[:, :16].contiguous(), ValueError),
+        ("s", m.s[:10], ValueError),
+        ("active_rows", m.rows.to(torch.int64), TypeError),
+        ("q", m.q.to(torch.int16), TypeError),
+        ("w_live", m.w_live.to(torch.float32), TypeError),
+    ]
+    import dataclasses
+    for field, value, exc in bad_cases:
+        bad = dataclasses.replace(ok, **{field: value})
+        with pytest.raises(exc):
+            _lib.sft_sparse_update([bad], adam_dev(**HP))
+    _lib.sft_sparse_update([ok], adam_dev(**HP))       # the unchanged matrix still runs
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("gmag", [1e-5, 3e4], ids=["tiny", "huge"])
+@pytest.mark.parametrize("C", [264, 20000], ids=["C264", "C20000"])
+def test_scaled_moments_over_many_steps_at_extreme_gradients(gpu_lib, gmag, C):
+    """Forty steps with gradients far below and far above fp16's range (the
+    moments stored as scaled fp16 rows, their exponents moving step by step;
+    at 20000 columns through the wide rows' two passes): bit-exact with the
+    oracle after every fifth step."""
+    st, rows, slot, fresh, _ = _case(24, C, 5, 7, 1700 + C, False)
+    m = GpuMat(st, np.zeros((rows.size, C), np.float32), rows, slot, fresh)
+    want = st.copy()
+    hp = adam_dev(**HP)
+    for step in range(40):
+        Gs = (synth.gradient_rows(rows.size, C, 1.0, 1710 + step) * np.float32(gmag)).astype(np.float32)
+        m.G.copy_(dev(Gs))
+        _lib.sft_sparse_update([m.upd()], hp)
+        oracle.sparse_update(want, Gs, rows, slot, fresh if step == 0 else None, **HP)
+        if step == 0:
+            m.fresh = None
+        if step % 5 == 4:
+            torch.cuda.synchronize()
+            assert_state_equal(m.to_state(), want, f"step {step}")
+    mo, vo = want.moments()
+    assert np.all(np.isfinite(vo[slot])) and np.all(vo[slot] > 0)
