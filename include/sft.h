@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 11
+#define SFT_ABI_VERSION 12
 
 enum {
     SFT_OK = 0,
@@ -465,6 +465,25 @@ int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *h
  */
 int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes,
                          const sft_upd_mat *mats, int32_t n_mats, const sft_adam *hp, void *stream);
+
+/*
+ * sft_masked_dw_update for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call with the workspace taken from a scratch array
+ * the library holds on each device (sft_noalloc_scratch_bytes() bytes, 96 MiB,
+ * held until the process ends; its address is looked up once per device on
+ * the first call there).  The call allocates nothing.  It uses the current
+ * device's array; `stream` must belong to the current device.  Every call on
+ * one device shares that array: calls that overlap on one device (different
+ * streams, or host threads) race, so order them on one stream.  Results are
+ * bit-identical to sft_masked_dw_update.
+ * Errors: those of sft_masked_dw_update; SFT_ECAPACITY when the groups need
+ * more workspace (sft_masked_dw_workspace) than the array holds; SFT_EHIP
+ * if the array's address cannot be found.
+ */
+size_t sft_noalloc_scratch_bytes(void);
+int sft_masked_dw_update_noalloc(const sft_dw_group *groups, int32_t n_groups, const sft_upd_mat *mats,
+                                 int32_t n_mats, const sft_adam *hp, void *stream);
 
 /*
  * A coupled pair (section 2.4: gate-up, query-output, key-value).  a and b

@@ -35,6 +35,7 @@ EXPORTS = (
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
     "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
     "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma",
+    "sft_noalloc_scratch_bytes", "sft_masked_dw_update_noalloc",
 )
 
 
@@ -150,6 +151,10 @@ def lib() -> C.CDLL:
         L.sft_coupled_update.argtypes = [C.POINTER(CPair), i32, C.POINTER(CAdam), p]
         L.sft_masked_dw_update.argtypes = [C.POINTER(CDwGroup), i32, p, C.c_size_t, C.POINTER(CUpdMat), i32,
                                            C.POINTER(CAdam), p]
+        L.sft_masked_dw_update_noalloc.argtypes = [C.POINTER(CDwGroup), i32, C.POINTER(CUpdMat), i32,
+                                                    C.POINTER(CAdam), p]
+        L.sft_noalloc_scratch_bytes.argtypes = []
+        L.sft_noalloc_scratch_bytes.restype = C.c_size_t
         L.sft_masked_writeback.argtypes = [p, p, p, i64, i64, p, i64, p, p]
         L.sft_masked_writeback_many.argtypes = [C.POINTER(CWbMat), i32, p]
         L.sft_rewind_init.argtypes = [C.POINTER(CRewind)]
@@ -170,7 +175,7 @@ def lib() -> C.CDLL:
         L.sft_helix_coupling.argtypes = [C.POINTER(CHelix), C.c_double, C.c_double, C.POINTER(C.c_double),
                                          C.POINTER(C.c_double)]
         for n in EXPORTS[2:]:
-            if n not in ("sft_masked_dw_workspace", "sft_leaf_grad_workspace"):
+            if n not in ("sft_masked_dw_workspace", "sft_leaf_grad_workspace", "sft_noalloc_scratch_bytes"):
                 getattr(L, n).restype = C.c_int
         _lib = L
     return _lib
@@ -482,6 +487,19 @@ def sft_masked_dw_update(groups: Sequence[DwGroup], ws, mats: Sequence[UpdMat], 
     h = hp.c()
     _check(lib().sft_masked_dw_update(arr, len(groups), _dev(ws), nbytes, u, len(mats), C.byref(h),
                                       _stream(stream)))
+
+
+def sft_masked_dw_update_noalloc(groups: Sequence[DwGroup], mats: Sequence[UpdMat], hp: Adam, stream=None) -> None:
+    """sft_masked_dw_update with the library's per-device scratch array as the
+    workspace: the call allocates nothing (calls overlapping on one device race)."""
+    arr, keep = _c_groups(groups)
+    ua = (CUpdMat * max(len(mats), 1))(*[m.c() for m in mats])
+    h = hp.c()
+    _check(lib().sft_masked_dw_update_noalloc(arr, len(groups), ua, len(mats), C.byref(h), _stream(stream)))
+
+
+def sft_noalloc_scratch_bytes() -> int:
+    return lib().sft_noalloc_scratch_bytes()
 
 
 @dataclass

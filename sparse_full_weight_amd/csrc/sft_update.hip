@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <numeric>
 #include <vector>
@@ -1057,6 +1058,58 @@ int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws,
             return rc;
     }
     return SFT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The allocation-free variant's workspace: one array per device, held for the
+// life of the process.  Host code never passes `scratch` itself to a kernel
+// (in host code the name stands for a host-side shadow); it passes the device
+// address hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = size_t(96) << 20;
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+
+int scratch_address(void **out, const char *who) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    SFT_CHECK(e == hipSuccess, SFT_EHIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+    SFT_CHECK(dev >= 0 && dev < kScratchDevices, SFT_ENOTSUP, "%s: device %d beyond the %d supported", who, dev,
+              kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        SFT_CHECK(r == hipSuccess && ptr, SFT_EHIP, "%s: hipGetSymbolAddress of the scratch array failed: %s", who,
+                  hipGetErrorString(r));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sft_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int sft_masked_dw_update_noalloc(const sft_dw_group *groups, int32_t n_groups, const sft_upd_mat *mats,
+                                 int32_t n_mats, const sft_adam *hp, void *stream) {
+    sft::clear_error();
+    const size_t need = sft_masked_dw_workspace(groups, n_groups);
+    if (need == static_cast<size_t>(-1)) return SFT_EINVAL;   // message set by the size call
+    SFT_CHECK(need <= kScratchBytes, SFT_ECAPACITY,
+              "sft_masked_dw_update_noalloc: the groups need %zu workspace bytes, above the %zu-byte scratch "
+              "array; use sft_masked_dw_update with a workspace", need, kScratchBytes);
+    void *ws = nullptr;
+    if (int rc = scratch_address(&ws, "sft_masked_dw_update_noalloc")) return rc;
+    return sft_masked_dw_update(groups, n_groups, ws, kScratchBytes, mats, n_mats, hp, stream);
 }
 
 int sft_masked_writeback(const int8_t *q, const float *s, const float *delta, int64_t R, int64_t C,
