@@ -115,3 +115,27 @@ def test_channel_weight_modulation_bounds_and_periods():
         h.rotation = float(R)
         p, m = h.weights()
         assert 0.9 - 1e-12 <= p <= 1.1 + 1e-12 and 0.95 - 1e-12 <= m <= 1.05 + 1e-12
+
+
+def test_descent_channel_dominates_at_equal_exposure():
+    """Section 2.8: the two channels have unequal weights, 1.833 to 1, so that
+    descent stays dominant.  At equal exposure of the two channels (phase 90
+    degrees, e = 1/2) and unmodulated channel weights, the cross term must
+    take less than half of the coupling strength; with the weights the other
+    way round it would take more.  Pins the direction of M : mu."""
+    h = hx.Helix(mod_plus=0.0, mod_minus=0.0)
+    h.rotation = 90.0
+    b = 0.6
+    a_own, a_cross = h.coupling(b)
+    assert a_own == 1.0
+    assert a_cross < b / 2
+    swapped = hx.Helix(M=1.0, mu=1.833, mod_plus=0.0, mod_minus=0.0)
+    swapped.rotation = 90.0
+    assert swapped.coupling(b)[1] > b / 2
+    # over a whole turn at stride 1 the cross term averages below half of b too
+    h = hx.Helix(mod_plus=0.0, mod_minus=0.0)
+    vals = []
+    for _ in range(10):
+        vals.append(h.coupling(b)[1])
+        h.step(5.0)
+    assert sum(vals) / len(vals) < b / 2
