@@ -442,9 +442,21 @@ typedef struct {
  *
  * Section 2.4 / Kingma-Ba Adam with bias correction: fp32 moments decoded
  * from the stored scaled fp16 rows drive the step, the new moments are
- * stored as scaled fp16 rows (exponents from the new rows' maxima); the step
- * is lr * mhat / (sqrt(vhat) + eps); decoupled weight decay
- * (w * (1 - lr*lambda)) is applied before the step when lambda != 0.
+ * stored as scaled fp16 rows (exponents from the new rows' maxima).  The step
+ * is lr * mhat / (sqrt(vhat) + eps) with mhat = m / (1 - beta1^t) and
+ * vhat = v / (1 - beta2^t).  Reading of the rounding order: the two bias
+ * corrections are per-row factors, k1 = lr / bc1 and k2 = 1 / sqrt(bc2)
+ * (fp32, bc1 and bc2 as below), applied as multiplications, which is the
+ * reordering Kingma and Ba themselves give for an efficient step: per
+ * element u = (k1 * m) / (sqrt(v) * k2 + eps), one division and one square
+ * root.  Decoupled weight decay multiplies w by (1 - lr*lambda) before the
+ * step (by 1, exactly, when lambda = 0).
+ *
+ * Requantisation reading: q' = clamp(rint(w' * r), -127, 127) with r = 1/s'
+ * the row's reciprocal scale (fp32); only if r overflows (s' below 2^-128)
+ * does the row divide, q' = rint(w' / s').  Either way q' is a nearest code of
+ * w'/s' (to within the reciprocal's rounding near a .5 tie) and
+ * delta' = w' - s'*q' stays exact.
  */
 static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_adam *hp,
                        float *wnew, float *mnew, float *vnew)
@@ -456,9 +468,13 @@ static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_ad
     int32_t step = (fresh ? 0 : M->t[sl]) + 1;
     float bc1 = (float)(1.0 - pow((double)hp->beta1, (double)step));
     float bc2 = (float)(1.0 - pow((double)hp->beta2, (double)step));
+    float k1 = hp->lr / bc1;               /* per-row factors of the bias corrections */
+    float sbc2 = sqrtf(bc2);
+    float k2 = 1.0f / sbc2;
     float c1 = 1.0f - hp->beta1;
     float c2 = 1.0f - hp->beta2;
-    float decay = 1.0f - hp->lr * hp->weight_decay;
+    float lrwd = hp->lr * hp->weight_decay;
+    float decay = 1.0f - lrwd;
     float s_old = M->s[r];
     int em_old = fresh ? 0 : M->mv_exp[2 * sl];
     int ev_old = fresh ? 0 : M->mv_exp[2 * sl + 1];
@@ -479,12 +495,12 @@ static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_ad
         float v = v_a + v_b;
         mnew[c] = m;
         vnew[c] = v;
-        float mhat = m / bc1;
-        float vhat = v / bc2;
-        float denom = sqrtf(vhat) + hp->eps;
-        float ratio = mhat / denom;
-        float u = hp->lr * ratio;
-        float w1 = hp->weight_decay != 0.0f ? w * decay : w;
+        float sv = sqrtf(v);
+        float sk = sv * k2;
+        float den = sk + hp->eps;
+        float num = k1 * m;
+        float u = num / den;
+        float w1 = w * decay;
         wnew[c] = w1 - u;
     }
     M->t[sl] = step;
@@ -511,12 +527,15 @@ static void update_row(oracle_mat *M, int64_t k, const float *g, const oracle_ad
         if (fabsf(wnew[c]) > amax)
             amax = fabsf(wnew[c]);
     float s_new = amax / 127.0f;
+    float rs = s_new != 0.0f ? 1.0f / s_new : 0.0f;
+    int by_division = s_new != 0.0f && isinf(rs);
     M->s[r] = s_new;
     for (int64_t c = 0; c < C; ++c) {
         int64_t e = r * C + c;
         float qf = 0.0f;
         if (s_new != 0.0f) {
-            qf = rintf(wnew[c] / s_new);
+            float x = by_division ? wnew[c] / s_new : wnew[c] * rs;
+            qf = rintf(x);
             if (qf > 127.0f)
                 qf = 127.0f;
             if (qf < -127.0f)
