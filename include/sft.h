@@ -432,10 +432,12 @@ typedef struct sft_upd_mat {
  * (section 2.3; section 2.4's plain Adam step for unpaired matrices).  Per
  * active row: rebuild w = fl(fl(s*q) + delta) in registers, take the Adam step
  * (fp32 moments decoded from the stored scaled fp16 rows, new moments stored
- * as scaled fp16 rows with new exponents, bias correction from the table,
- * step lr*mhat/(sqrt(vhat)+eps),
- * decoupled weight decay first when weight_decay != 0), then requantise the
- * row: s' = max|w'|/127, q' = clamp(rint(w'/s'), -127, 127),
+ * as scaled fp16 rows with new exponents; the step lr*mhat/(sqrt(vhat)+eps)
+ * with the bias corrections bc1, bc2 from the table applied as the per-row
+ * factors k1 = lr/bc1 and k2 = 1/sqrt(bc2): u = (k1*m)/(sqrt(v)*k2 + eps);
+ * decoupled weight decay first, w*(1 - lr*weight_decay)), then requantise
+ * the row: s' = max|w'|/127, q' = clamp(rint(w' * (1/s')), -127, 127) (a
+ * row whose reciprocal scale overflows divides by s'),
  * delta' = w' - s'*q' (exact, so s'*q' + delta' rebuilds w'); a row with
  * s' = 0 stores q' = 0, delta' = w'.  With w_live set, the row's live weights
  * are rewritten as bf16(w') in the same pass.  Rows not listed are neither

@@ -196,6 +196,10 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
     const int32_t ti = min(step, hp.t_max);
     const float bc1 = valid ? hp.bc1[ti] : 1.0f;
     const float bc2 = valid ? hp.bc2[ti] : 1.0f;
+    // the bias corrections as per-row factors: u = (k1*m) / (sqrt(v)*k2 + eps)
+    const float k1 = hp.lr / bc1;
+    const float sbc2 = __builtin_sqrtf(bc2);
+    const float k2 = 1.0f / sbc2;
 
     // Wide rows on 1024-lane workgroups go in batches of chunks (registers).
     constexpr int kBatch = Grad::template batch<kThreads, kChunks>();
@@ -250,12 +254,12 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
                     const float v_a = hp.beta2 * v_old;
                     const float v_b = hp.c2 * gg;
                     const float v = v_a + v_b;
-                    const float mhat = m / bc1;
-                    const float vhat = v / bc2;
-                    const float denom = __builtin_sqrtf(vhat) + hp.eps;
-                    const float ratio = mhat / denom;
-                    const float u = hp.lr * ratio;
-                    const float w1 = hp.wd != 0.0f ? w * hp.decay : w;
+                    const float sv = __builtin_sqrtf(v);
+                    const float sk = sv * k2;
+                    const float den = sk + hp.eps;
+                    const float num = k1 * m;
+                    const float u = num / den;
+                    const float w1 = w * hp.decay;   // decay = 1 - lr*lambda (1 exactly without decay)
                     fn(j, e, w1 - u, m, v);
                 }
             }
@@ -286,12 +290,16 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
         M.mv_exp[2 * sl + 1] = static_cast<int8_t>(ev);
     }
 
-    // pass 2
+    // pass 2: codes by the reciprocal scale (a row whose reciprocal overflows
+    // divides; an all-zero row keeps zero codes), uniform per row
+    const float rs = s_new != 0.0f ? 1.0f / s_new : 0.0f;
+    const int mode = s_new == 0.0f ? 0 : (__builtin_isinf(rs) ? 2 : 1);
     int8_t *qout = M.q + r * C;
     float *dout = M.delta + r * C;
     uint16_t *wl = M.w_live ? M.w_live + r * C : nullptr;
-    auto store_chunk = [&](int j, const float (&w4)[4], const float (&m4)[4], const float (&v4)[4])
+    auto store_chunk = [&](auto mode_tag, int j, const float (&w4)[4], const float (&m4)[4], const float (&v4)[4])
         __attribute__((always_inline)) {
+        constexpr int kMode = decltype(mode_tag)::value;
         const int64_t c = 4 * (static_cast<int64_t>(lt) + static_cast<int64_t>(j) * kLanes);
         if (c >= C) return;
         float qf[4], d[4];
@@ -299,8 +307,9 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float qq = 0.0f;
-            if (s_new != 0.0f) {
-                qq = __builtin_rintf(w4[e] / s_new);
+            if constexpr (kMode != 0) {
+                const float x = kMode == 1 ? w4[e] * rs : w4[e] / s_new;
+                qq = __builtin_rintf(x);
                 qq = fminf(fmaxf(qq, -127.0f), 127.0f);
             }
             const float sq = s_new * qq;
@@ -319,24 +328,29 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
         *reinterpret_cast<ushort4 *>(mrow + c) = make_ushort4(mo[0], mo[1], mo[2], mo[3]);
         *reinterpret_cast<ushort4 *>(vrow + c) = make_ushort4(vo[0], vo[1], vo[2], vo[3]);
     };
-    if constexpr (kKeep) {
+    auto pass2 = [&](auto mode_tag) __attribute__((always_inline)) {
+        if constexpr (kKeep) {
 #pragma unroll
-        for (int j = 0; j < kChunks; ++j) store_chunk(j, wn[j], mn[j], vn[j]);
-    } else {
-        // Pass 1 read every load of the row before the barrier, so the stores
-        // below cannot overtake a load of the same address.
+            for (int j = 0; j < kChunks; ++j) store_chunk(mode_tag, j, wn[j], mn[j], vn[j]);
+        } else {
+            // Pass 1 read every load of the row before the barrier, so the
+            // stores below cannot overtake a load of the same address.
 #pragma unroll
-        for (int b0 = 0; b0 < kChunks; b0 += kBatch) {
-            float w4[kBatch][4], m4[kBatch][4], v4[kBatch][4];
-            step_batch(b0, [&](int j, int e, float w, float m, float v) __attribute__((always_inline)) {
-                w4[j - b0][e] = w;
-                m4[j - b0][e] = m;
-                v4[j - b0][e] = v;
-            });
+            for (int b0 = 0; b0 < kChunks; b0 += kBatch) {
+                float w4[kBatch][4], m4[kBatch][4], v4[kBatch][4];
+                step_batch(b0, [&](int j, int e, float w, float m, float v) __attribute__((always_inline)) {
+                    w4[j - b0][e] = w;
+                    m4[j - b0][e] = m;
+                    v4[j - b0][e] = v;
+                });
 #pragma unroll
-            for (int jb = 0; jb < kBatch; ++jb) store_chunk(b0 + jb, w4[jb], m4[jb], v4[jb]);
+                for (int jb = 0; jb < kBatch; ++jb) store_chunk(mode_tag, b0 + jb, w4[jb], m4[jb], v4[jb]);
+            }
         }
-    }
+    };
+    if (mode == 1) pass2(std::integral_constant<int, 1>{});
+    else if (mode == 0) pass2(std::integral_constant<int, 0>{});
+    else pass2(std::integral_constant<int, 2>{});
 }
 
 // Plain update: the gradient is the matrix's own dW row.
