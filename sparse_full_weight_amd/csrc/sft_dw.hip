@@ -158,14 +158,20 @@ __device__ __forceinline__ int2 tile_pos(const DwGroupDev &G, int32_t t) {
 // ---------------------------------------------------------------- gather
 
 // One workgroup per (packed tile, 64 tokens) (measured faster than 128 or
-// 256: more waves in flight for the scattered 2-byte reads).  Thread (row i, token t%8)
-// loads one bf16 per 8 tokens; the block is transposed through LDS and
-// written as 16-byte runs of 8 tokens.  Rows without a source, tokens past T
-// and the padding up to Tp are zero.
+// 256: more waves in flight for the scattered reads).  When the tile's 32
+// rows are one run of consecutive dY columns starting on a 16-byte boundary
+// (whole tiles, and packed rows of a clustered mask), each token's 32 values
+// are 64 contiguous bytes: four lanes load them with 16-byte loads (one load
+// per thread) into a [token][row] LDS block.  Otherwise thread (row i, token
+// t%8) loads one bf16 per 8 tokens into a [row][token] block.  Either block is
+// then written as 16-byte runs of 8 tokens of one row.  Rows without a
+// source, tokens past T and the padding up to Tp are zero.
 __global__ __launch_bounds__(256) void k_dw_gather(const DwParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t tile_t[32][kGatherTokens + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t tile_r[kGatherTokens][32];
     __shared__ const uint16_t *s_src[32];
     __shared__ int64_t s_pitch[32];
+    __shared__ int32_t s_run;
     const int32_t gp = blockIdx.x;
     int gi = 0;
     while (gi + 1 < p.n_groups && gp >= p.g[gi + 1].ptile_begin) ++gi;
@@ -203,8 +209,40 @@ __global__ __launch_bounds__(256) void k_dw_gather(const DwParams p) {
         s_src[tid] = src;
         s_pitch[tid] = pitch;
         if (blockIdx.y == 0) G.rowmap[pt * 32 + tid] = code;
+        // one run: every row present, rows consecutive columns of one matrix,
+        // the first on a 16-byte boundary (and so every token's 64 bytes)
+        const uint16_t *src0 = reinterpret_cast<const uint16_t *>(
+            __shfl(reinterpret_cast<uintptr_t>(src), 0, 32));
+        const int64_t pitch0 = __shfl(pitch, 0, 32);
+        const bool mine = src && src == src0 + tid && pitch == pitch0;
+        const bool all = __all(mine ? 1 : 0);   // lanes 32..63 of wave 0 are inactive here
+        if (tid == 0)
+            s_run = all && (reinterpret_cast<uintptr_t>(src0) & 15u) == 0 && (pitch0 & 7) == 0;
     }
     __syncthreads();
+    uint16_t *dst = G.at + (static_cast<int64_t>(pt) * (G.Tp / 8) + t0 / 8) * 256;
+    if (s_run) {
+        static_assert(kGatherTokens * 4 == 256, "four lanes per token");
+        const int tk = tid >> 2, part = tid & 3;
+        const int64_t t = t0 + tk;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < G.T) v = *reinterpret_cast<const uint4 *>(s_src[0] + t * s_pitch[0] + 8 * part);
+        *reinterpret_cast<uint4 *>(&tile_r[tk][8 * part]) = v;
+        __syncthreads();
+        const int oct = tid >> 5, r = tid & 31;
+        if (t0 + 8 * oct < G.Tp) {
+            uint16_t o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = tile_r[8 * oct + e][r];
+            uint4 pack;
+            pack.x = o[0] | (static_cast<uint32_t>(o[1]) << 16);
+            pack.y = o[2] | (static_cast<uint32_t>(o[3]) << 16);
+            pack.z = o[4] | (static_cast<uint32_t>(o[5]) << 16);
+            pack.w = o[6] | (static_cast<uint32_t>(o[7]) << 16);
+            *reinterpret_cast<uint4 *>(dst + (oct * 32 + r) * 8) = pack;
+        }
+        return;
+    }
     const int i = tid & 31, tt = tid >> 5;
     const uint16_t *src = s_src[i];
     const int64_t pitch = s_pitch[i];
@@ -217,7 +255,6 @@ __global__ __launch_bounds__(256) void k_dw_gather(const DwParams p) {
 #pragma unroll
     for (int q = 0; q < kGatherTokens / 8; ++q) tile_t[i][8 * q + tt] = v[q];
     __syncthreads();
-    uint16_t *dst = G.at + (static_cast<int64_t>(pt) * (G.Tp / 8) + t0 / 8) * 256;
 #pragma unroll
     for (int u = 0; u < kGatherTokens / 64; ++u) {
         const int gidx = tid + 256 * u;
