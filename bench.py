@@ -81,14 +81,6 @@ def parse_args():
 
 
 # ---------------------------------------------------------------------- workloads
-def _mask_plan(R, k, seed, clustered=True):
-    """Row-tracker mask with exactly k hot rows (clustered in 32-row tiles)."""
-    from sparse_full_weight_amd import _lib, synth
-    hot = synth.clustered_rows(R, k, seed)
-    mag = synth.tracker_magnitudes(R, hot, seed + 1)
-    return _lib.sft_plan_rows(_lib.sft_tracker_window(np.zeros(R, np.float32), mag))
-
-
 def layer_buffers(T, seed, dev="cuda", shapes=None, groups=None):
     """Activations, output gradients and resident state of one layer, drawn
     on the device (torch's seeded generator)."""
@@ -131,26 +123,37 @@ class Layer:
         X, bufs = buffers if buffers is not None else layer_buffers(T, seed, dev, self.shapes, self.groups_def)
         self.X = X
         self.mats = {}
-        host_chunks, offsets, off = [], {}, 0
-        for mi, (name, (R, C)) in enumerate(self.shapes.items()):
+        # the step's plan: one sft_plan_layer call over the seven matrices'
+        # tracker windows, written into pinned host memory for one upload
+        names = list(self.shapes)
+        Rs = [self.shapes[n][0] for n in names]
+        self.mags = []
+        for mi, name in enumerate(names):
+            R = Rs[mi]
             if rows is not None:
-                plan = _lib.sft_plan_rows(synth.mask_from_rows(R, rows[name]))
+                self.mags.append(synth.mask_from_rows(R, rows[name]).astype(np.float32))
             else:
-                plan = _mask_plan(R, round(density * R), seed + 10 * mi + 1)
-            row_slot = np.full(R, -1, np.int32)
-            slot, fresh = _lib.sft_slots_update(row_slot, plan.n_active, plan.active_rows)
-            fresh[:] = 0          # steady state: the moments already exist
-            parts = {"rows": plan.active_rows, "tiles": plan.active_tiles,
-                     "abits": plan.active_bits.view(np.int32), "first": plan.tile_first, "slot": slot,
-                     "fresh": np.frombuffer(np.pad(fresh, (0, (-fresh.size) % 4)).tobytes(), np.int32)}
-            offsets[name] = {}
-            for key, arr in parts.items():
-                offsets[name][key] = (off, arr.size)
-                host_chunks.append(arr.astype(np.int32, copy=False))
-                off += arr.size
+                hot = synth.clustered_rows(R, round(density * R), seed + 10 * mi + 1)
+                self.mags.append(synth.tracker_magnitudes(R, hot, seed + 10 * mi + 2))
+        words = _lib.LayerPlanner(Rs, Rs).words
+        self.plan_host = torch.zeros(max(words, 1), dtype=torch.int32).pin_memory()
+        self.planner = _lib.LayerPlanner(Rs, Rs, self.plan_host.data_ptr(), words)
+        mplans = self.planner.plan(self.mags)
+        host = self.plan_host.numpy()
+        offsets = {}
+        for mi, name in enumerate(names):
+            mp = mplans[mi]
+            o = mp.off
+            sec = lambda k, n: host[o[k]:o[k] + n].copy()   # noqa: E731
+            plan = _lib.Plan(Rs[mi], np.zeros(0, np.uint32), sec("rows", mp.n_active), sec("tiles", mp.n_active_tiles),
+                             sec("bits", mp.n_active_tiles).view(np.uint32), sec("first", mp.n_active_tiles))
+            # steady state: the moments already exist (no fresh rows)
+            host[o["fresh"]:o["fresh"] + (mp.n_active + 3) // 4] = 0
+            offsets[name] = {"rows": (o["rows"], mp.n_active), "tiles": (o["tiles"], mp.n_active_tiles),
+                             "abits": (o["bits"], mp.n_active_tiles), "first": (o["first"], mp.n_active_tiles),
+                             "slot": (o["slot"], mp.n_active), "fresh": (o["fresh"], (mp.n_active + 3) // 4)}
             self.mats[name] = dict(bufs[name], plan=plan)
-        packed = np.concatenate(host_chunks) if host_chunks else np.zeros(1, np.int32)
-        self.plan_host = torch.from_numpy(packed).pin_memory()
+        self.plan_len = self.planner.length
         self.plan_dev = torch.empty_like(self.plan_host, device=dev)
         self.plan_dev.copy_(self.plan_host)
         bc1, bc2 = _lib.sft_bias_table(0.9, 0.999, 20000)
@@ -194,7 +197,8 @@ class Layer:
         self.fused_call = _lib.prepare_masked_dw_update(groups, self.ws, upd, self.hp)
 
     def upload_plan(self):
-        self.plan_dev.copy_(self.plan_host, non_blocking=True)
+        n = self.plan_len
+        self.plan_dev[:n].copy_(self.plan_host[:n], non_blocking=True)
 
     def n_active(self):
         return int(sum(m["plan"].n_active for m in self.mats.values()))
@@ -330,30 +334,45 @@ def _hbm(work_bytes, ms):
 
 
 # ---------------------------------------------------------------------- host side
-def host_plan_us(density: float, reps: int = 30):
-    """The a1 host calls of one layer timed alone (C calls only: the row
-    tracker's window, the row plan and the moment slots of the seven
-    matrices), median over `reps` repetitions; the magnitudes are drawn
-    before the clock starts."""
+def host_plan_us(density: float, reps: int = 50):
+    """The a1 host work of one layer timed alone: one sft_plan_layer call
+    (the row tracker's window, the row plan and the moment slots of the seven
+    matrices, written into pinned memory), median over `reps` repetitions.
+    Each repetition starts from the state of a run in progress -- charges from
+    an earlier window of the same hot rows, and those rows holding slots --
+    restored before the clock starts; the magnitudes are drawn beforehand."""
+    import torch
+
     from sparse_full_weight_amd import _lib, synth
-    inputs = []
-    for mi, (name, (R, C)) in enumerate(synth.LLAMA7B.items()):
-        mag = synth.tracker_magnitudes(R, synth.clustered_rows(R, round(density * R), 7 + mi), 8 + mi)
-        inputs.append((R, mag))
+    names = list(synth.LLAMA7B)
+    Rs = [synth.LLAMA7B[n][0] for n in names]
+    mags = []
+    for mi, R in enumerate(Rs):
+        hot = synth.clustered_rows(R, round(density * R), 7 + mi)
+        mags.append(synth.tracker_magnitudes(R, hot, 8 + mi))
+    words = _lib.LayerPlanner(Rs, Rs).words
+    pinned = torch.zeros(words, dtype=torch.int32).pin_memory()
+    pl = _lib.LayerPlanner(Rs, Rs, pinned.data_ptr(), words)
+    # an earlier window of the same hot rows (no background): those rows now
+    # hold charges and slots, and the timed window keeps exactly them active
+    pl.plan([np.where(m >= 0.1, m, np.float32(0)).astype(np.float32) for m in mags])
+    ch0 = [c.copy() for c in pl.charge]
+    rs0 = [r.copy() for r in pl.row_slot]
+    pl.bind(mags)
     times = []
     for _ in range(reps):
-        chs = [np.zeros(R, np.float32) for R, _ in inputs]
-        slots = [np.full(R, -1, np.int32) for R, _ in inputs]
+        for i in range(len(Rs)):
+            pl.charge[i][:] = ch0[i]
+            pl.row_slot[i][:] = rs0[i]
         t0 = time.perf_counter()
-        for (R, mag), ch, rs in zip(inputs, chs, slots):
-            mask = _lib.sft_tracker_window(ch, mag)
-            plan = _lib.sft_plan_rows(mask)
-            _lib.sft_slots_update(rs, plan.n_active, plan.active_rows)
+        pl.step()
         times.append((time.perf_counter() - t0) * 1e6)
     return {"median_us": round(float(np.median(times)), 1), "p10_us": round(float(np.percentile(times, 10)), 1),
             "p90_us": round(float(np.percentile(times, 90)), 1), "reps": reps,
-            "calls": "sft_tracker_window + sft_plan_rows + sft_slots_update on the 7 matrices (42,496 rows), "
-                     "through the ctypes binding"}
+            "n_active": int(sum(int(np.count_nonzero(r >= 0)) for r in pl.row_slot)),
+            "calls": "one sft_plan_layer call over the 7 matrices (42,496 rows): tracker windows, row plans and "
+                     "moment slots into pinned memory, through the ctypes binding (magnitude arrays bound once, "
+                     "refilled in place by a training loop)"}
 
 
 def host_info():
@@ -762,7 +781,10 @@ def main():
             L.fused_call(stream)
 
     def step(i):
-        # the step: this step's plan to the device, then the masked dW and update
+        # the step: this step's plan to the device, then the masked dW and
+        # update, in one stream.  (Copying the next step's plan on a second
+        # stream during this step measured slower: the cross-stream waits
+        # cost more than the copy.)
         L = layers[i % len(layers)]
         L.upload_plan()
         call(L)
@@ -848,8 +870,9 @@ def main():
         "config": {"workload": "llama7b_layer_masked_step", "tokens": args.tokens, "density": args.density,
                    "matrices": {k: list(v) for k, v in synth.LLAMA7B.items()}, "active_rows": n_act,
                    "active_tiles": n_tiles, "ring_layers": args.layers, "dw_layout": args.layout,
-                   "step": ("the step's packed plan copied host -> device (a few KB, pinned), then masked dW "
-                            "(7 matrices) + sparse update with fused write-back (7 matrices), "
+                   "step": ("the step's packed plan (one sft_plan_layer output, a few KB, pinned) copied host -> "
+                            "device, then masked dW (7 matrices) + sparse update with fused write-back "
+                            "(7 matrices), "
                             + ("two calls" if args.unfused else
                                "one call: sft_masked_dw_update, the split tiles' fix-up done by the update")
                             + "; activations, gradients and state resident in HBM"),

@@ -10,7 +10,9 @@
  *                                                                     sft_tracker_window,
  *                                                                     sft_plan_rows,
  *                                                                     sft_plan_embedding,
- *                                                                     sft_slots_update
+ *                                                                     sft_slots_update,
+ *                                                                     sft_plan_layer (all
+ *                                                                     three, per layer)
  *   2. the masked weight gradient dW = dY^T X, skipping 32-row tiles with no
  *      active row (section 2.2);                                  -> sft_masked_dw,
  *                                                                     sft_embedding_dw
@@ -33,6 +35,8 @@
  *                                                                     sft_rewind_observe,
  *                                                                     sft_rows_save,
  *                                                                     sft_rows_restore
+ *   Measurement probes (sustained bandwidth and matrix-core rate) are
+ *   declared apart, in sft_probe.h.
  *   The element-sparse variant of the blog post "SparseLeaf: synaptic sparse
  *   fine-tuning" (K selected connections of a frozen weight train their own
  *   increments): their gradients and their Adam step.
@@ -74,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 12
+#define SFT_ABI_VERSION 13
 
 enum {
     SFT_OK = 0,
@@ -143,6 +147,10 @@ typedef struct sft_plan {
 int sft_plan_rows(const uint8_t *active, sft_plan *plan);
 
 /*
+ * The embedding's masked backward pass needs, per active row, the token
+ * positions that looked it up (section 2.2: the embedding's input is one-hot,
+ * so a row's gradient sums dY over its token's positions; section 2.1: the
+ * conductor's mask chooses the rows).
  * Token positions of the active embedding rows, as CSR: the positions t with
  * tokens[t] == plan->active_rows[k] are positions[row_ptr[k] .. row_ptr[k+1]),
  * ascending.  row_ptr has n_active + 1 entries; positions has capacity
@@ -166,6 +174,50 @@ int sft_plan_embedding(const sft_plan *plan, const int32_t *tokens, int64_t n_to
 int sft_slots_update(int32_t *row_slot, int64_t rows, int64_t n_slots,
                      const int32_t *active_rows, int64_t n_active, int32_t *slot,
                      uint8_t *fresh);
+
+/*
+ * One step's host plan of the matrices of a layer in one call: section 2.1
+ * (the CPU derives every mask once per step, a step ahead of the GPU, and
+ * ships them in one transfer), section 2.2 (32-row tiles) and section 2.3
+ * (moment slots of the active rows).  For each matrix, in order: the row
+ * tracker's window over the matrix's output magnitudes (exactly
+ * sft_tracker_window), the row plan of the resulting mask (exactly
+ * sft_plan_rows) and its moment slots (exactly sft_slots_update).  The
+ * results go one after another into `packed`, host int32 words meant for a
+ * single copy to the device; each matrix's sections start on a 16-byte
+ * boundary of `packed`, at the word offsets returned in its entry:
+ *   off_rows   active rows [n_active]
+ *   off_tiles  active tiles [n_active_tiles]
+ *   off_bits   their row bits [n_active_tiles] (uint32)
+ *   off_first  index of each active tile's first active row [n_active_tiles]
+ *   off_slot   moment slot of each active row [n_active]
+ *   off_fresh  fresh flags, one byte per active row (uint8, zero-padded to
+ *              whole words)
+ * packed must be 16-byte aligned and hold sft_plan_layer_words(mats)
+ * words; *packed_len receives the words used.  Every input is checked and
+ * every mask formed before any state changes: on an error no charge, row
+ * slot or packed word has been written.
+ * Errors: SFT_EINVAL (null arrays, bad sizes, a negative or non-finite
+ * magnitude, a row_slot entry outside [-1, n_slots)), SFT_EALIGN,
+ * SFT_ECAPACITY (packed too small, or more active rows than slots).
+ */
+typedef struct sft_layer_mat {
+    int64_t rows;              /* in: R, below 2^31                          */
+    int64_t n_slots;           /* in: moment slots of the matrix             */
+    float *charge;             /* in/out [rows]: the row tracker's charge    */
+    const float *magnitude;    /* in [rows]: this window's output magnitudes */
+    int32_t *row_slot;         /* in/out [rows]: row -> slot (-1 = none)     */
+    int64_t n_active;          /* out */
+    int64_t n_active_tiles;    /* out */
+    int64_t off_rows, off_tiles, off_bits, off_first, off_slot, off_fresh;   /* out, in words */
+} sft_layer_mat;
+
+/* Words of `packed` that sft_plan_layer needs for these matrices (only
+ * `rows` is read), or -1 for a bad argument. */
+int64_t sft_plan_layer_words(const sft_layer_mat *mats, int32_t n_mats);
+
+int sft_plan_layer(sft_layer_mat *mats, int32_t n_mats, int32_t *packed, int64_t packed_cap,
+                   int64_t *packed_len);
 
 /*
  * Adam bias corrections (section 2.4: Adam with its bias correction):
@@ -342,6 +394,8 @@ typedef struct sft_dw_group {
 } sft_dw_group;
 
 /*
+ * Section 2.2 (only active 32-row tiles reach the matrix cores, so the
+ * scratch scales with the active rows, never with R).
  * Workspace bytes sft_masked_dw needs for these groups: the gathered dY
  * columns of the active rows (the matrix-core operand, token-contiguous),
  * their output map, and the split-K partial rows when the token axis is
@@ -499,6 +553,9 @@ int sft_masked_dw_update_noalloc(const sft_dw_group *groups, int32_t n_groups, c
  * weights a_own/a_cross come from the caller's phase schedule; clip points to
  * a device float[2] {clipA, clipB}, or is NULL for {1, 1}.
  */
+/* The union of the two row lists is never formed: each matrix's rows are
+ * updated by their own workgroups, which find the partner's row (if any) by a
+ * binary search of the partner's ascending active_rows on the device. */
 typedef struct sft_pair {
     sft_upd_mat a, b;
     float a_own, a_cross;
@@ -677,30 +734,6 @@ typedef struct sft_leaf_vec {
 
 int sft_leaf_adam(const sft_leaf_vec *vecs, int32_t n_vecs, int32_t step, const sft_adam *hp,
                   void *stream);
-
-/* ======================================================================= */
-/* measurement probes                                                        */
-/* ======================================================================= */
-
-/*
- * What this device sustains, measured beside the published peaks that the
- * kernels' roofline fractions use.  Each launches sft_probe_grid()
- * workgroups of 256 lanes (8 per CU) and returns without synchronising.
- *   sft_probe_read: streams `bytes` (a multiple of 16, 16-byte aligned) with
- *     16-byte non-temporal loads and writes one XOR per lane to sink
- *     [sft_probe_grid() * 256] (the XOR of sink equals the XOR of the buffer's
- *     32-bit words);
- *   sft_probe_copy: copies `bytes` from src to dst the same way;
- *   sft_probe_mfma: each wave issues 4 * iters v_mfma_f32_32x32x16_bf16 on
- *     register operands (every input 1/16) and writes each lane's sum to out
- *     [sft_probe_grid() * 256], which equals 4 * iters (iters < 2^22 keeps it
- *     exact); work = sft_probe_grid() * 4 waves * 4 * iters * 32768 FLOP.
- * Errors: SFT_EINVAL (null or unaligned pointers, bad sizes), SFT_EHIP.
- */
-int sft_probe_grid(void);
-int sft_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
-int sft_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
-int sft_probe_mfma(int64_t iters, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ EXPORTS = (
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
     "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
     "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma",
-    "sft_noalloc_scratch_bytes", "sft_masked_dw_update_noalloc",
+    "sft_noalloc_scratch_bytes", "sft_masked_dw_update_noalloc", "sft_plan_layer_words", "sft_plan_layer",
 )
 
 
@@ -50,6 +50,13 @@ class CPlan(C.Structure):
     _fields_ = [("rows", C.c_int64), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
                 ("tile_bits", C.c_void_p), ("active_rows", C.c_void_p), ("active_tiles", C.c_void_p),
                 ("active_bits", C.c_void_p), ("tile_first", C.c_void_p)]
+
+
+class CLayerMat(C.Structure):
+    _fields_ = [("rows", C.c_int64), ("n_slots", C.c_int64), ("charge", C.c_void_p), ("magnitude", C.c_void_p),
+                ("row_slot", C.c_void_p), ("n_active", C.c_int64), ("n_active_tiles", C.c_int64),
+                ("off_rows", C.c_int64), ("off_tiles", C.c_int64), ("off_bits", C.c_int64),
+                ("off_first", C.c_int64), ("off_slot", C.c_int64), ("off_fresh", C.c_int64)]
 
 
 class CDwMat(C.Structure):
@@ -142,6 +149,9 @@ def lib() -> C.CDLL:
         L.sft_plan_rows.argtypes = [p, C.POINTER(CPlan)]
         L.sft_plan_embedding.argtypes = [C.POINTER(CPlan), p, i64, p, p, i64, C.POINTER(C.c_int64)]
         L.sft_slots_update.argtypes = [p, i64, i64, p, i64, p, p]
+        L.sft_plan_layer_words.argtypes = [C.POINTER(CLayerMat), i32]
+        L.sft_plan_layer_words.restype = i64
+        L.sft_plan_layer.argtypes = [C.POINTER(CLayerMat), i32, p, i64, C.POINTER(C.c_int64)]
         L.sft_bias_table.argtypes = [f32, f32, i32, p, p]
         L.sft_masked_dw_workspace.argtypes = [C.POINTER(CDwGroup), i32]
         L.sft_masked_dw_workspace.restype = C.c_size_t
@@ -338,6 +348,96 @@ def sft_slots_update(row_slot: np.ndarray, n_slots: int, active_rows: np.ndarray
     _check(lib().sft_slots_update(_np_ptr(row_slot), row_slot.size, n_slots, _np_ptr(active_rows),
                                   active_rows.size, _np_ptr(slot), _np_ptr(fresh)))
     return slot[:active_rows.size].copy(), fresh[:active_rows.size].copy()
+
+
+@dataclass
+class LayerMatPlan:
+    """One matrix's part of a layer plan: counts, and the word offsets of its
+    sections in the packed buffer."""
+    n_active: int
+    n_active_tiles: int
+    off: dict
+
+
+class LayerPlanner:
+    """sft_plan_layer over a fixed list of matrices: holds each matrix's
+    tracker charge and row -> slot map across steps, and the packed host
+    buffer the plans are written to (a numpy array, or the address and word
+    capacity of a caller's buffer, such as pinned memory)."""
+
+    SECTIONS = ("rows", "tiles", "bits", "first", "slot", "fresh")
+
+    def __init__(self, rows, n_slots, packed_ptr: int | None = None, packed_words: int | None = None):
+        self.n = len(rows)
+        assert len(n_slots) == self.n
+        self.charge = [np.zeros(int(R), np.float32) for R in rows]
+        self.row_slot = [np.full(int(R), -1, np.int32) for R in rows]
+        self.c = (CLayerMat * max(self.n, 1))()
+        for i, R in enumerate(rows):
+            self.c[i].rows = int(R)
+            self.c[i].n_slots = int(n_slots[i])
+            self.c[i].charge = _np_ptr(self.charge[i])
+            self.c[i].row_slot = _np_ptr(self.row_slot[i])
+        self.words = int(lib().sft_plan_layer_words(self.c, self.n))
+        if self.words < 0:
+            raise ValueError("sft_plan_layer_words: bad matrix list")
+        if packed_ptr is None:
+            buf = np.zeros(self.words + 8, np.int32)      # 16-byte aligned view below
+            start = (-buf.ctypes.data % 16) // 4
+            self.packed = buf[start:start + max(self.words, 1)]
+            self._ptr, self._cap = self.packed.ctypes.data, self.words
+        else:
+            if packed_words is None or packed_words < self.words:
+                raise ValueError(f"packed buffer holds {packed_words} words, {self.words} needed")
+            self.packed = None
+            self._ptr, self._cap = int(packed_ptr), int(packed_words)
+        self._mags = [None] * self.n
+        self.length = 0
+
+    def bind(self, magnitudes) -> None:
+        """Point the matrices at their magnitude arrays (float32, one per
+        matrix, kept alive here); a loop that refills them in place binds
+        once and calls step()."""
+        assert len(magnitudes) == self.n
+        for i, mag in enumerate(magnitudes):
+            mag = np.ascontiguousarray(mag, np.float32)
+            if mag.shape != (self.c[i].rows,):
+                raise ValueError(f"magnitudes[{i}] has shape {mag.shape}, want ({self.c[i].rows},)")
+            self._mags[i] = mag
+            self.c[i].magnitude = _np_ptr(mag)
+        self._bound = True
+
+    def step(self) -> int:
+        """One sft_plan_layer call over the bound magnitudes; returns the
+        words written."""
+        if not getattr(self, "_bound", False):
+            raise ValueError("LayerPlanner.step: bind() the magnitudes first")
+        n = C.c_int64()
+        _check(lib().sft_plan_layer(self.c, self.n, self._ptr, self._cap, C.byref(n)))
+        self.length = int(n.value)
+        return self.length
+
+    def results(self) -> list[LayerMatPlan]:
+        return [LayerMatPlan(self.c[i].n_active, self.c[i].n_active_tiles,
+                             {k: getattr(self.c[i], "off_" + k) for k in self.SECTIONS}) for i in range(self.n)]
+
+    def plan(self, magnitudes) -> list[LayerMatPlan]:
+        """One step: the tracker window of every matrix over `magnitudes`,
+        its row plan and moment slots, written into the packed buffer."""
+        self.bind(magnitudes)
+        self.step()
+        return self.results()
+
+    def section(self, mp: LayerMatPlan, name: str) -> np.ndarray:
+        """A matrix's section of the numpy packed buffer (rows, tiles, bits,
+        first, slot as int32; fresh as uint8)."""
+        assert self.packed is not None
+        o = mp.off[name]
+        if name == "fresh":
+            return self.packed[o:o + (mp.n_active + 3) // 4].view(np.uint8)[:mp.n_active]
+        n = mp.n_active if name in ("rows", "slot") else mp.n_active_tiles
+        a = self.packed[o:o + n]
+        return a.view(np.uint32) if name == "bits" else a
 
 
 def sft_bias_table(beta1: float, beta2: float, t_max: int):

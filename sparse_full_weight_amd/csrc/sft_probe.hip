@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include "sft_internal.h"
+#include "sft_probe.h"
 
 namespace {
 

@@ -8,6 +8,7 @@ Fine-Tuning: Full-Weight Training at the Cost of the Active Set", sections
 tiles).
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -21,9 +22,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "sft.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(sft_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(sft_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -125,3 +128,88 @@ def test_host_calls_reject_bad_input_before_writing():
     with pytest.raises(_lib.SftError):
         _lib.sft_bias_table(1.0, 0.9, 10)
     assert "beta" in _lib.lib().sft_last_error().decode()
+
+
+def _layer_case(step, shapes, density=0.01, seed=2400):
+    """Magnitudes of one window per matrix: clustered hot rows that drift
+    from step to step."""
+    mags = []
+    for i, R in enumerate(shapes):
+        if R == 0:
+            mags.append(np.zeros(0, np.float32))
+            continue
+        hot = synth.clustered_rows(R, max(1, round(density * R)), seed + 10 * i + step)
+        mags.append(synth.tracker_magnitudes(R, hot, seed + 10 * i + 5 + step))
+    return mags
+
+
+def test_plan_layer_matches_oracle_over_steps():
+    """sft_plan_layer equals the oracle's tracker window, row plan and moment
+    slots of each matrix, step after step (charges and slots carried), with
+    the sections where the offsets say; matrices of ragged sizes, an empty
+    one, and slot pools both larger than the rows and only as large as
+    needed (the staged path)."""
+    shapes = [4096, 4096, 4096, 4096, 11008, 11008, 4096, 33, 0, 1000]
+    slots = [R for R in shapes[:7]] + [40, 0, 900]
+    pl = _lib.LayerPlanner(shapes, slots)
+    ch_o = [np.zeros(R, np.float32) for R in shapes]
+    rs_o = [np.full(R, -1, np.int32) for R in shapes]
+    for step in range(5):
+        mags = _layer_case(step, shapes)
+        got = pl.plan(mags)
+        offs = sorted(o for mp in got for o in mp.off.values())
+        assert all(o % 4 == 0 for o in offs) and pl.length <= pl.words
+        for i, R in enumerate(shapes):
+            act = oracle.tracker_window(ch_o[i], mags[i])
+            assert np.array_equal(pl.charge[i].view(np.uint32), ch_o[i].view(np.uint32)), (step, i)
+            want = oracle.plan_rows(act)
+            slot, fresh = oracle.slots_update(rs_o[i], slots[i], want["active_rows"])
+            mp = got[i]
+            assert np.array_equal(pl.section(mp, "rows"), want["active_rows"]), (step, i)
+            assert np.array_equal(pl.section(mp, "tiles"), want["active_tiles"]), (step, i)
+            assert np.array_equal(pl.section(mp, "bits"), want["bits"][want["active_tiles"]]), (step, i)
+            first = np.searchsorted(want["active_rows"], 32 * want["active_tiles"]).astype(np.int32)
+            assert np.array_equal(pl.section(mp, "first"), first), (step, i)
+            assert np.array_equal(pl.section(mp, "slot"), slot) and np.array_equal(pl.section(mp, "fresh"), fresh)
+            assert np.array_equal(pl.row_slot[i], rs_o[i]), (step, i)
+
+
+def test_plan_layer_checks_everything_before_writing():
+    shapes = [4096, 11008, 64]
+    pl = _lib.LayerPlanner(shapes, [4096, 11008, 2])
+    mags = _layer_case(0, shapes)
+    mags[2] = np.zeros(64, np.float32)
+    pl.plan(mags)
+    before = ([c.copy() for c in pl.charge], [r.copy() for r in pl.row_slot], pl.packed.copy())
+
+    def unchanged():
+        return (all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(pl.charge, before[0]))
+                and all(np.array_equal(a, b) for a, b in zip(pl.row_slot, before[1]))
+                and np.array_equal(pl.packed, before[2]))
+
+    bad = _layer_case(1, shapes)
+    bad[2] = np.zeros(64, np.float32)
+    bad[1] = bad[1].copy()
+    bad[1][77] = np.nan                                   # a bad magnitude in the second matrix
+    with pytest.raises(_lib.SftError) as e:
+        pl.plan(bad)
+    assert e.value.code == _lib.SFT_EINVAL and unchanged()
+    full = _layer_case(1, shapes)
+    full[2] = np.ones(64, np.float32)                      # 64 active rows, 2 slots
+    with pytest.raises(_lib.SftError) as e:
+        pl.plan(full)
+    assert e.value.code == _lib.SFT_ECAPACITY and unchanged()
+    pl.row_slot[0][5] = 4096                               # a slot outside the pool
+    with pytest.raises(_lib.SftError) as e:
+        pl.plan(_layer_case(1, shapes))
+    assert e.value.code == _lib.SFT_EINVAL
+    pl.row_slot[0][5] = before[1][0][5]
+    small = _lib.LayerPlanner(shapes, [4096, 11008, 2], packed_ptr=pl.packed.ctypes.data, packed_words=pl.words)
+    small._cap = pl.words - 1                             # one word short
+    with pytest.raises(_lib.SftError) as e:
+        small.plan(mags)
+    assert e.value.code == _lib.SFT_ECAPACITY
+    small._cap, small._ptr = pl.words, pl.packed.ctypes.data + 4
+    with pytest.raises(_lib.SftError) as e:
+        small.plan(mags)
+    assert e.value.code == _lib.SFT_EALIGN and unchanged()
