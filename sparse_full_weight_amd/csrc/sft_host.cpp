@@ -218,16 +218,24 @@ int sft_conductor_window(float *ch, int64_t rows, const int32_t *tokens, int64_t
     SFT_CHECK(n_tokens == 0 || tokens, SFT_EINVAL, "conductor: null tokens");
     // Hit counts are exact in fp32 up to 2^24 tokens per window.
     SFT_CHECK(n_tokens <= (int64_t(1) << 24), SFT_ENOTSUP, "conductor: window over 2^24 tokens");
-    std::vector<float> hits(static_cast<size_t>(rows), 0.0f);
+    static thread_local std::vector<float> hits_tls;
+    std::vector<float> &hits = hits_tls;
+    hits.assign(static_cast<size_t>(rows), 0.0f);
     for (int64_t i = 0; i < n_tokens; ++i) {
         const int32_t tok = tokens[i];
         SFT_CHECK(tok >= 0 && tok < rows, SFT_EINVAL, "conductor: token %d at %lld out of [0, %lld)",
                   tok, (long long)i, (long long)rows);
     }
-    for (int64_t i = 0; i < n_tokens; ++i) hits[tokens[i]] += 1.0f;
+    // counts are exact in fp32 (at most 2^24), so the running maximum of the
+    // incremented counts is the window's busiest row
+    float *const h = hits.data();
     float busiest = 0.0f;
-    for (float h : hits) busiest = std::max(busiest, h);
-    charge_update(ch, rows, hits.data(), busiest, active);
+    for (int64_t i = 0; i < n_tokens; ++i) {
+        const float c = h[tokens[i]] + 1.0f;
+        h[tokens[i]] = c;
+        busiest = std::max(busiest, c);
+    }
+    charge_update(ch, rows, h, busiest, active);
     return SFT_OK;
 }
 
@@ -380,9 +388,13 @@ int sft_plan_embedding(const sft_plan *plan, const int32_t *tokens, int64_t n_to
     SFT_CHECK(na == 0 || plan->active_rows, SFT_EINVAL, "plan_embedding: null active_rows");
     // Row -> position in the active list (-1 = inactive), then a counting sort
     // of the token positions by row; a stable pass keeps positions ascending.
-    std::vector<int32_t> index(static_cast<size_t>(rows), -1);
+    static thread_local std::vector<int32_t> index_tls;
+    static thread_local std::vector<int64_t> count_tls, fill_tls;
+    std::vector<int32_t> &index = index_tls;
+    std::vector<int64_t> &count = count_tls;
+    index.assign(static_cast<size_t>(rows), -1);
     for (int64_t k = 0; k < na; ++k) index[plan->active_rows[k]] = static_cast<int32_t>(k);
-    std::vector<int64_t> count(static_cast<size_t>(na) + 1, 0);
+    count.assign(static_cast<size_t>(na) + 1, 0);
     for (int64_t t = 0; t < n_tokens; ++t) {
         const int32_t tok = tokens[t];
         SFT_CHECK(tok >= 0 && tok < rows, SFT_EINVAL, "plan_embedding: token %d out of range", tok);
@@ -394,7 +406,8 @@ int sft_plan_embedding(const sft_plan *plan, const int32_t *tokens, int64_t n_to
               (long long)positions_cap);
     SFT_CHECK(count[na] == 0 || positions, SFT_EINVAL, "plan_embedding: null positions");
     for (int64_t k = 0; k <= na; ++k) row_ptr[k] = static_cast<int32_t>(count[k]);
-    std::vector<int64_t> fill(count.begin(), count.end() - 1);
+    std::vector<int64_t> &fill = fill_tls;
+    fill.assign(count.begin(), count.end() - 1);
     for (int64_t t = 0; t < n_tokens; ++t) {
         const int32_t k = index[tokens[t]];
         if (k >= 0) positions[fill[k]++] = static_cast<int32_t>(t);

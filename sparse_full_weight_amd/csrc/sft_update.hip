@@ -179,27 +179,35 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
     const int lt = static_cast<int>(threadIdx.x) % kLanes;
     __shared__ float red[3][kThreads / 64];
     const int64_t C = valid ? M.C : 0;
-    const int64_t r = valid ? M.rows[k] : 0;
-    const int64_t sl = valid ? M.slot[k] : 0;
-    const bool fresh = (valid && M.fresh) ? M.fresh[k] != 0 : false;
-    const float s_old = valid ? M.s[r] : 0.0f;
-    const int32_t t_old = (fresh || !valid) ? 0 : M.t[sl];
-    const int em_old = (fresh || !valid) ? 0 : static_cast<int>(M.mv_exp[2 * sl]);
-    const int ev_old = (fresh || !valid) ? 0 : static_cast<int>(M.mv_exp[2 * sl + 1]);
+    // The row's bookkeeping in two rounds of independent loads, none under a
+    // branch (a missing second row of a pair reads the list's first entry
+    // and ignores it): the row, its slot and fresh flag; then its scale, the
+    // slot's step count and moment exponents.  The bias corrections, which
+    // need the step count, are first used after the row's data loads have
+    // gone out.
+    const int64_t kk = valid ? k : 0;
+    const int64_t r_ld = M.rows[kk];
+    const int64_t sl_ld = M.slot[kk];
+    const uint8_t fresh_ld = M.fresh ? M.fresh[kk] : uint8_t(0);
+    const int64_t r = valid ? r_ld : 0;
+    const int64_t sl = valid ? sl_ld : 0;
+    const bool fresh = valid && fresh_ld != 0;
+    const float s_ld = M.s[r];
+    const int32_t t_ld = M.t[sl];
+    const int8_t em_ld = M.mv_exp[2 * sl], ev_ld = M.mv_exp[2 * sl + 1];
+    const float s_old = valid ? s_ld : 0.0f;
+    const int32_t t_old = (fresh || !valid) ? 0 : t_ld;
+    const int em_old = (fresh || !valid) ? 0 : static_cast<int>(em_ld);
+    const int ev_old = (fresh || !valid) ? 0 : static_cast<int>(ev_ld);
     const float dec_m = pow2f(-em_old), dec_v = pow2f(-ev_old);
     const int8_t *__restrict__ qrow = M.q + r * C;
     const float *__restrict__ drow = M.delta + r * C;
     uint16_t *mrow = M.m + sl * C;
     uint16_t *vrow = M.v + sl * C;
 
-    const int32_t step = t_old + 1;
-    const int32_t ti = min(step, hp.t_max);
-    const float bc1 = valid ? hp.bc1[ti] : 1.0f;
-    const float bc2 = valid ? hp.bc2[ti] : 1.0f;
-    // the bias corrections as per-row factors: u = (k1*m) / (sqrt(v)*k2 + eps)
-    const float k1 = hp.lr / bc1;
-    const float sbc2 = __builtin_sqrtf(bc2);
-    const float k2 = 1.0f / sbc2;
+    // (the step count, and with it the bias corrections, is used only after
+    // the row's data loads: in-order waits would otherwise hold them back)
+    auto new_step = [&]() __attribute__((always_inline)) { return t_old + 1; };
 
     // Wide rows on 1024-lane workgroups go in batches of chunks (registers).
     constexpr int kBatch = Grad::template batch<kThreads, kChunks>();
@@ -229,6 +237,13 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
                 }
             }
         }
+        // the bias corrections as per-row factors: u = (k1*m) / (sqrt(v)*k2 + eps)
+        const int32_t ti = min(new_step(), hp.t_max);
+        const float bc1 = valid ? hp.bc1[ti] : 1.0f;
+        const float bc2 = valid ? hp.bc2[ti] : 1.0f;
+        const float k1 = hp.lr / bc1;
+        const float sbc2 = __builtin_sqrtf(bc2);
+        const float k2 = 1.0f / sbc2;
 #pragma unroll
         for (int jb = 0; jb < kBatch; ++jb) {
             const int j = b0 + jb;
@@ -285,7 +300,7 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
     const float enc_m = pow2f(em), enc_v = pow2f(ev);
     if (lt == 0 && valid) {
         M.s[r] = s_new;
-        M.t[sl] = step;
+        M.t[sl] = new_step();
         M.mv_exp[2 * sl] = static_cast<int8_t>(em);
         M.mv_exp[2 * sl + 1] = static_cast<int8_t>(ev);
     }
@@ -435,15 +450,27 @@ struct PairGrad {
     }
 };
 
-// Index of `row` in an ascending list, or -1.
-__device__ __forceinline__ int64_t find_row(const int32_t *rows, int64_t n, int64_t row) {
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (rows[mid] < row) lo = mid + 1;
-        else hi = mid;
+// Index of `row` in an ascending list of distinct rows, or -1, found by the
+// 64 lanes of a wave together (every lane of the wave gets the answer): each
+// round reads 64 evenly spaced entries of the remaining range and keeps the
+// stretch between the last entry <= row and the next, so a list of up to
+// 64^m entries takes m dependent loads.  Called with the whole wave active.
+__device__ __forceinline__ int64_t find_row_wave(const int32_t *rows, int64_t n, int64_t row) {
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    int64_t lo = 0, hi = n;   // row, if listed, is in [lo, hi)
+    while (hi - lo > 64) {
+        const int64_t step = (hi - lo + 63) / 64;
+        const int64_t idx = lo + lane * step;
+        const bool le = idx < hi && rows[idx] <= row;
+        const int cnt = __popcll(__ballot(le));   // a prefix of the lanes (the list ascends)
+        if (cnt == 0) return -1;
+        lo = lo + static_cast<int64_t>(cnt - 1) * step;
+        hi = min(hi, lo + step);
     }
-    return (lo < n && rows[lo] == row) ? lo : -1;
+    const int64_t idx = lo + lane;
+    const bool hit = idx < hi && rows[idx] == row;
+    const uint64_t b = __ballot(hit);
+    return b ? lo + __ffsll(static_cast<unsigned long long>(b)) - 1 : -1;
 }
 
 template <int kThreads, int kChunks>
@@ -458,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void k_coupled_update(const PairParams p)
         const int64_t k = (wg - M.row_begin) * kPer + static_cast<int>(threadIdx.x) / (kThreads / kPer);
         const bool valid = k < M.n_active;
         const int64_t r = valid ? M.rows[k] : 0;
-        const int64_t pk = valid ? find_row(S.prow, S.pn, r) : -1;
+        const int64_t pk = valid ? find_row_wave(S.prow, S.pn, r) : -1;
         const float clip_a = S.clip ? S.clip[0] : 1.0f;
         const float clip_b = S.clip ? S.clip[1] : 1.0f;
         PairGrad gr;
