@@ -77,6 +77,9 @@ def parse_args():
                     help="skip the probes of the HBM and matrix-core rates this device sustains")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--skip-probe", action="store_true",
+                    help="run only masked dW calls with 0..16 active tiles of 128 (the skipped-tile traffic "
+                         "evidence, under the HBM counters)")
     return ap.parse_args()
 
 
@@ -761,6 +764,41 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 3}), flush=True)
 
 
+SKIP_PROBE_TILES = (0, 1, 2, 4, 8, 16)
+SKIP_PROBE_CALLS = 3
+
+
+def skip_probe():
+    """Masked dW of one 4096 x 4096 matrix (T = 4096, whole-tile layout) with
+    0, 1, 2, 4, 8 and 16 of its 128 row tiles active (every 8th tile), each
+    called SKIP_PROBE_CALLS times in that order: run under rocprofv3's
+    FETCH_SIZE / WRITE_SIZE counters, the dispatches show what a skipped tile
+    costs (none is launched for an all-skipped call)."""
+    import torch
+
+    from sparse_full_weight_amd import _lib, synth
+    T, R, C = 4096, 4096, 4096
+    X = synth.normal_bf16_device((T, C), 1.0, 71, "cuda")
+    dY = synth.normal_bf16_device((T, R), 0.01, 72, "cuda")
+    out = []
+    for k in SKIP_PROBE_TILES:
+        mask = np.zeros(R, np.uint8)
+        for t in range(k):
+            mask[32 * 8 * t: 32 * 8 * t + 32] = 1
+        plan = _lib.sft_plan_rows(mask)
+        dW = torch.empty((max(plan.n_active, 1), C), dtype=torch.float32, device="cuda")
+        groups = [_lib.DwGroup(X, [_lib.DwMat(dY, plan.to_device("cuda"), dW[:plan.n_active])], _lib.SFT_DW_TILES)]
+        nbytes = _lib.sft_masked_dw_workspace(groups)
+        ws = torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(SKIP_PROBE_CALLS):
+            _lib.sft_masked_dw(groups, ws)
+        torch.cuda.synchronize()
+        out.append({"active_tiles": k, "active_rows": plan.n_active, "calls": SKIP_PROBE_CALLS})
+        print(f"[skip-probe] {k} active tiles done", file=sys.stderr, flush=True)
+    print(json.dumps({"skip_probe": out, "T": T, "R": R, "C": C}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -770,6 +808,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.skip_probe:
+        skip_probe()
         return
     torch.cuda.set_device(0)
     print(f"[bench] building {args.layers} layers (T={args.tokens}, density={args.density})", file=sys.stderr,

@@ -22,7 +22,11 @@ support:
   the 1024 SIMDs' busy cycles; the fractions divide by those counts.  With
   ``SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS`` collected too it
   adds the LDS's busy fraction (the 256 CUs' LDS cycles) and the bank-conflict
-  cycles per LDS instruction.
+  cycles per LDS instruction;
+* ``skip``: HBM bytes per masked-dW call against the number of active 32-row
+  tiles, from ``FETCH_SIZE`` / ``WRITE_SIZE`` runs of ``bench.py
+  --skip-probe`` (calls with 0, 1, 2, 4, 8, 16 active tiles of 128, three
+  each, in that order), scaled like ``counters``.
 
 Usage:
   python -m sparse_full_weight_amd.profsum stats <kernel_stats.csv> --cmd "<command>" > out.txt
@@ -30,6 +34,8 @@ Usage:
       --copy-fetch <dir> --copy-write <dir> --cmd "<commands>" > out.txt
   python -m sparse_full_weight_amd.profsum units --runs <dir> [<dir> ...] --kernel k_masked_dw \\
       --label "<workload>" ... --cmd "<commands>" > out.txt
+  python -m sparse_full_weight_amd.profsum skip --fetch <dir> --write <dir> \\
+      --copy-fetch <dir> --copy-write <dir> --cmd "<commands>" > out.txt
 (each <dir> holds the ``*_counter_collection.csv`` of one run).
 """
 from __future__ import annotations
@@ -98,17 +104,20 @@ def _counter(dirname: str, counter: str) -> dict:
     return per
 
 
+def _copy_kib(per) -> float:
+    """Average counter value (KiB) of the 1 GiB copies of a calibration run."""
+    vals = [v for k, vs in per.items() if "copyBuffer" in k or "copy" in short(k).lower() for v in vs]
+    vals = [v for v in vals if v > 1024]     # the 1 GiB copies, not small blits
+    return sum(vals) / len(vals)
+
+
 def counters(fetch: str, write: str, copy_fetch: str, copy_write: str, cmd: str) -> str:
     f = _counter(fetch, "FETCH_SIZE")
     w = _counter(write, "WRITE_SIZE")
     cf = _counter(copy_fetch, "FETCH_SIZE")
     cw = _counter(copy_write, "WRITE_SIZE")
 
-    def copy_kib(per):
-        vals = [v for k, vs in per.items() if "copyBuffer" in k or "copy" in short(k).lower() for v in vs]
-        vals = [v for v in vals if v > 1024]     # the 1 GiB copies, not small blits
-        return sum(vals) / len(vals)
-
+    copy_kib = _copy_kib
     f_scale = (COPY_BYTES / 1024) / copy_kib(cf)
     w_scale = (COPY_BYTES / 1024) / copy_kib(cw)
 
@@ -181,6 +190,66 @@ def units(groups, labels, kernel: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def _dispatches(dirname: str, counter: str) -> list:
+    """(dispatch id, short kernel name, value) of every dispatch of a run."""
+    rows = []
+    for path in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), short(r["Kernel_Name"]), float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def skip(fetch: str, write: str, copy_fetch: str, copy_write: str, tiles, calls: int, T: int, cmd: str) -> str:
+    """Per-call HBM traffic of the masked-dW kernels against the number of
+    active 32-row tiles (the skipped-tile probe: configurations in order,
+    `calls` calls each; a configuration without active tiles launches
+    nothing)."""
+    f_scale = (COPY_BYTES / 1024) / _copy_kib(_counter(copy_fetch, "FETCH_SIZE"))
+    w_scale = (COPY_BYTES / 1024) / _copy_kib(_counter(copy_write, "WRITE_SIZE"))
+    fd = [d for d in _dispatches(fetch, "FETCH_SIZE") if d[1] in DW_KERNELS]
+    wd = [d for d in _dispatches(write, "WRITE_SIZE") if d[1] in DW_KERNELS]
+    live = [k for k in tiles if k > 0]
+    out = ["# HBM traffic of masked-dW calls against active 32-row tiles (4096 x 4096 matrix, 128 tiles)",
+           f"# commands: {cmd}", "",
+           f"calibration: FETCH_SIZE x{f_scale:.4f}, WRITE_SIZE x{w_scale:.4f} (a 1 GiB device copy)",
+           f"dispatches: {len(fd)} FETCH and {len(wd)} WRITE records for {len(live)} configurations with active "
+           f"tiles x {calls} calls; the configuration with 0 active tiles launched no kernel"
+           if 0 in tiles else f"dispatches: {len(fd)}", ""]
+    out.append(f"{'tiles':>5s} {'gather read MB':>15s} {'dY columns MB':>14s} {'product read MB':>16s} "
+               f"{'product write MB':>17s} {'fix-up read MB':>15s}")
+    # the dispatches of one call: gather, product and (if any tile was cut) fix-up
+    calls_f, calls_w = [], []
+    for dl, acc in ((fd, calls_f), (wd, calls_w)):
+        cur = None
+        for _, k, v in dl:
+            if k == "k_dw_gather":
+                cur = {}
+                acc.append(cur)
+            if cur is not None:
+                cur[k] = cur.get(k, 0.0) + v
+    if len(calls_f) != len(live) * calls or len(calls_w) != len(live) * calls:
+        raise SystemExit(f"expected {len(live) * calls} calls, found {len(calls_f)} / {len(calls_w)}")
+    rec = []
+    for i, k in enumerate(live):
+        cf = calls_f[i * calls:(i + 1) * calls]
+        cw = calls_w[i * calls:(i + 1) * calls]
+
+        def mean(cs, name, scale):
+            return sum(c.get(name, 0.0) for c in cs) / len(cs) * 1024 * scale
+
+        g = mean(cf, "k_dw_gather", f_scale)
+        pr = mean(cf, "k_masked_dw", f_scale)
+        pw = mean(cw, "k_masked_dw", w_scale)
+        fx = mean(cf, "k_dw_fixup", f_scale)
+        dy = k * 32 * T * 2
+        rec.append({"tiles": k, "gather_read": round(g), "dY_bytes": dy, "product_read": round(pr),
+                    "product_write": round(pw), "fixup_read": round(fx)})
+        out.append(f"{k:5d} {g / 1e6:15.3f} {dy / 1e6:14.3f} {pr / 1e6:16.2f} {pw / 1e6:17.2f} {fx / 1e6:15.2f}")
+    out.append("skip-json: " + json.dumps(rec))
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str) -> dict | None:
     """The traffic record of a counters summary, or None if missing."""
     try:
@@ -202,6 +271,13 @@ def main(argv=None):
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         b.add_argument("--" + k, required=True)
     b.add_argument("--cmd", required=True)
+    d = sub.add_parser("skip")
+    for k in ("fetch", "write", "copy-fetch", "copy-write"):
+        d.add_argument("--" + k, required=True)
+    d.add_argument("--tiles", default="0,1,2,4,8,16")
+    d.add_argument("--calls", type=int, default=3)
+    d.add_argument("--tokens", type=int, default=4096)
+    d.add_argument("--cmd", required=True)
     c = sub.add_parser("units")
     c.add_argument("--runs", nargs="+", action="append", required=True,
                    help="run directories of one workload (repeat the flag per workload)")
@@ -211,6 +287,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(stats(args.csv, args.cmd))
+    elif args.what == "skip":
+        sys.stdout.write(skip(args.fetch, args.write, args.copy_fetch, args.copy_write,
+                              [int(x) for x in args.tiles.split(",")], args.calls, args.tokens, args.cmd))
     elif args.what == "units":
         if len(args.runs) != len(args.label):
             raise SystemExit("one --label per --runs")

@@ -49,3 +49,40 @@ def test_units_lds_columns(tmp_path):
                    (k, "SQ_LDS_BANK_CONFLICT", 300.0), (k, "SQ_INSTS_LDS", 100.0)])
     row = [ln for ln in profsum.units([[a]], ["leaf"], "k_leaf_grad", "c").splitlines() if ln.startswith("leaf")][0]
     assert row.split()[-2:] == ["0.400", "3.00"]
+
+
+def _write_dispatches(dirname, rows):
+    os.makedirs(dirname, exist_ok=True)
+    with open(os.path.join(dirname, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_skip_groups_calls_by_gather_and_scales(tmp_path):
+    """Calls start at each gather dispatch; configurations follow in order;
+    values are per call and scaled by the copy calibration (here x2 for
+    FETCH_SIZE, x1 for WRITE_SIZE)."""
+    g = "(anonymous namespace)::k_dw_gather((anonymous namespace)::DwParams)"
+    p = "(anonymous namespace)::k_masked_dw((anonymous namespace)::DwParams)"
+    x = "(anonymous namespace)::k_dw_fixup((anonymous namespace)::DwParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    gib = (1 << 30) / 1024
+    fetch, write = [], []
+    for tiles in (1, 2):
+        for _ in range(2):
+            fetch += [(g, "FETCH_SIZE", 100.0 * tiles), (p, "FETCH_SIZE", 1000.0), (x, "FETCH_SIZE", 10.0)]
+            write += [(g, "WRITE_SIZE", 5.0), (p, "WRITE_SIZE", 50.0 * tiles), (x, "WRITE_SIZE", 1.0)]
+    d = {n: str(tmp_path / n) for n in ("f", "w", "cf", "cw")}
+    _write_dispatches(d["f"], fetch)
+    _write_dispatches(d["w"], write)
+    _write_run(d["cf"], [(copy, "FETCH_SIZE", gib / 2)])
+    _write_run(d["cw"], [(copy, "WRITE_SIZE", gib)])
+    text = profsum.skip(d["f"], d["w"], d["cf"], d["cw"], [0, 1, 2], 2, 4096, "cmd")
+    import json
+    rec = json.loads(text.split("skip-json: ")[1])
+    assert [r["tiles"] for r in rec] == [1, 2]
+    assert rec[0]["gather_read"] == 100 * 1024 * 2 and rec[1]["gather_read"] == 200 * 1024 * 2
+    assert rec[1]["product_write"] == 100 * 1024 and rec[0]["fixup_read"] == 10 * 1024 * 2
+    assert "0 active tiles launched no kernel" in text
