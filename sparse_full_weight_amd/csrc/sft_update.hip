@@ -101,6 +101,27 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// Wave-uniform copy of a value every lane of the wave holds alike (a row's
+// address: a wavefront never spans two rows).
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// A raw buffer over the `bytes` bytes at p (the same for every lane of the
+// wave): loads at or past the end read zero and touch no memory.  The row
+// loads below go through such buffers, with no branch around them, so that
+// the compiler's waits can count them one chunk at a time.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buf(const void *p, int64_t bytes) {
+    void *u = reinterpret_cast<void *>(uniform64(reinterpret_cast<uint64_t>(p)));
+    const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+    return __builtin_amdgcn_make_buffer_rsrc(u, static_cast<short>(0), n, 0x00020000);
+}
+__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, int64_t byte_off) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<uint32_t>(byte_off), 0, 0));
+}
+
 // Largest values over the workgroup (three non-negative floats at once), via
 // the integer order of their bit patterns: wave64 shuffles, then one LDS word
 // per wave and value.  The workgroup may hold several rows of kLanes lanes
@@ -179,41 +200,70 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
     const int lt = static_cast<int>(threadIdx.x) % kLanes;
     __shared__ float red[3][kThreads / 64];
     const int64_t C = valid ? M.C : 0;
-    // The row's bookkeeping in two rounds of independent loads, none under a
-    // branch (a missing second row of a pair reads the list's first entry
-    // and ignores it): the row, its slot and fresh flag; then its scale, the
-    // slot's step count and moment exponents.  The bias corrections, which
-    // need the step count, are first used after the row's data loads have
-    // gone out.
+    // The row's bookkeeping, none of it under a branch (a missing second row
+    // of a pair reads the list's first entry and ignores it): the row and its
+    // slot address the row's data; the fresh flag, the row's scale and the
+    // slot's step count and moment exponents are loaded next but first used
+    // after the row's data loads have gone out (the waits count loads in
+    // issue order, so a use before them would hold them back).  A fresh
+    // row's stored moments are loaded like any other and replaced by zeros.
     const int64_t kk = valid ? k : 0;
     const int64_t r_ld = M.rows[kk];
     const int64_t sl_ld = M.slot[kk];
-    const uint8_t fresh_ld = M.fresh ? M.fresh[kk] : uint8_t(0);
     const int64_t r = valid ? r_ld : 0;
     const int64_t sl = valid ? sl_ld : 0;
-    const bool fresh = valid && fresh_ld != 0;
+    // The fresh flag and the exponents are read per lane, at an index plus a
+    // lane count that is zero in every lane: as vector values they are not
+    // moved to scalar registers, and so not waited for, where they are
+    // loaded.  The scale, the step count and the bias corrections of both
+    // cases (a continuing row's step t + 1, a fresh row's step 1) come
+    // through scalar loads, which have a counter of their own.
+    const int64_t z = static_cast<int64_t>(__builtin_amdgcn_mbcnt_lo(0u, 0u));
+    // (no list of fresh flags: an empty buffer, which reads zero, not a branch)
+    const uint8_t fresh_ld = static_cast<uint8_t>(__builtin_amdgcn_raw_buffer_load_b8(
+        row_buf(M.fresh, M.fresh ? M.n_active : 0), static_cast<uint32_t>(kk + z), 0, 0));
+    const int8_t em_ld = M.mv_exp[2 * sl + z], ev_ld = M.mv_exp[2 * sl + 1 + z];
     const float s_ld = M.s[r];
     const int32_t t_ld = M.t[sl];
-    const int8_t em_ld = M.mv_exp[2 * sl], ev_ld = M.mv_exp[2 * sl + 1];
-    const float s_old = valid ? s_ld : 0.0f;
-    const int32_t t_old = (fresh || !valid) ? 0 : t_ld;
-    const int em_old = (fresh || !valid) ? 0 : static_cast<int>(em_ld);
-    const int ev_old = (fresh || !valid) ? 0 : static_cast<int>(ev_ld);
-    const float dec_m = pow2f(-em_old), dec_v = pow2f(-ev_old);
+    // (a fresh row's slot holds a stale count: keep the index inside the table)
+    const int32_t ti_cont = t_ld < 0 ? 1 : (t_ld < hp.t_max ? t_ld + 1 : hp.t_max);
+    const float bc1_cont = hp.bc1[ti_cont], bc2_cont = hp.bc2[ti_cont];
+    const float bc1_fresh = hp.bc1[1], bc2_fresh = hp.bc2[1];
     const int8_t *__restrict__ qrow = M.q + r * C;
     const float *__restrict__ drow = M.delta + r * C;
     uint16_t *mrow = M.m + sl * C;
     uint16_t *vrow = M.v + sl * C;
 
-    // (the step count, and with it the bias corrections, is used only after
-    // the row's data loads: in-order waits would otherwise hold them back)
-    auto new_step = [&]() __attribute__((always_inline)) { return t_old + 1; };
+    struct RowState {
+        float s_old, dec_m, dec_v, k1, k2;
+        int32_t step;
+    };
+    auto row_state = [&]() __attribute__((always_inline)) {
+        const bool fresh = valid && fresh_ld != 0;
+        RowState rs;
+        rs.s_old = valid ? s_ld : 0.0f;
+        const int32_t t_old = (fresh || !valid) ? 0 : t_ld;
+        rs.dec_m = pow2f((fresh || !valid) ? 0 : -static_cast<int>(em_ld));
+        rs.dec_v = pow2f((fresh || !valid) ? 0 : -static_cast<int>(ev_ld));
+        rs.step = t_old + 1;
+        // the bias corrections as per-row factors: u = (k1*m) / (sqrt(v)*k2 + eps)
+        const float bc1 = !valid ? 1.0f : (fresh ? bc1_fresh : bc1_cont);
+        const float bc2 = !valid ? 1.0f : (fresh ? bc2_fresh : bc2_cont);
+        rs.k1 = hp.lr / bc1;
+        const float sbc2 = __builtin_sqrtf(bc2);
+        rs.k2 = 1.0f / sbc2;
+        return rs;
+    };
 
     // Wide rows on 1024-lane workgroups go in batches of chunks (registers).
     constexpr int kBatch = Grad::template batch<kThreads, kChunks>();
     static_assert(kChunks % kBatch == 0, "batch");
     float wn[kKept][4], mn[kKept][4], vn[kKept][4];
     float amax = 0.0f, mmax = 0.0f, vmax = 0.0f;
+
+    // The row's buffers: columns past C (or a whole missing row) read as zero.
+    const __amdgpu_buffer_rsrc_t bq = row_buf(qrow, C), bd = row_buf(drow, 4 * C);
+    const __amdgpu_buffer_rsrc_t bm = row_buf(mrow, 2 * C), bv = row_buf(vrow, 2 * C);
 
     // Loads and Adam step of chunks [b0, b0 + kBatch): fn(j, e, w', m, v) per element.
     auto step_batch = [&](int b0, auto &&fn) __attribute__((always_inline)) {
@@ -225,25 +275,15 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
         for (int jb = 0; jb < kBatch; ++jb) {
             const int j = b0 + jb;
             const int64_t c = 4 * (static_cast<int64_t>(lt) + static_cast<int64_t>(j) * kLanes);
-            mv[jb] = make_ushort4(0, 0, 0, 0);
-            vv[jb] = make_ushort4(0, 0, 0, 0);
-            if (c < C) {
-                graw[jb] = gr.load(c);
-                qv[jb] = *reinterpret_cast<const char4 *>(qrow + c);
-                dv[jb] = *reinterpret_cast<const float4 *>(drow + c);
-                if (!fresh) {
-                    mv[jb] = *reinterpret_cast<const ushort4 *>(mrow + c);
-                    vv[jb] = *reinterpret_cast<const ushort4 *>(vrow + c);
-                }
-            }
+            graw[jb] = gr.load(c);
+            qv[jb] = __builtin_bit_cast(char4, __builtin_amdgcn_raw_buffer_load_b32(bq, static_cast<uint32_t>(c), 0, 0));
+            dv[jb] = ld_f4(bd, 4 * c);
+            mv[jb] = __builtin_bit_cast(ushort4, __builtin_amdgcn_raw_buffer_load_b64(bm, static_cast<uint32_t>(2 * c), 0, 0));
+            vv[jb] = __builtin_bit_cast(ushort4, __builtin_amdgcn_raw_buffer_load_b64(bv, static_cast<uint32_t>(2 * c), 0, 0));
         }
-        // the bias corrections as per-row factors: u = (k1*m) / (sqrt(v)*k2 + eps)
-        const int32_t ti = min(new_step(), hp.t_max);
-        const float bc1 = valid ? hp.bc1[ti] : 1.0f;
-        const float bc2 = valid ? hp.bc2[ti] : 1.0f;
-        const float k1 = hp.lr / bc1;
-        const float sbc2 = __builtin_sqrtf(bc2);
-        const float k2 = 1.0f / sbc2;
+        const RowState rs = row_state();
+        const float s_old = rs.s_old, dec_m = rs.dec_m, dec_v = rs.dec_v, k1 = rs.k1, k2 = rs.k2;
+        const bool zero_mv = !valid || fresh_ld != 0;   // a fresh row's moments start from zero
 #pragma unroll
         for (int jb = 0; jb < kBatch; ++jb) {
             const int j = b0 + jb;
@@ -254,8 +294,10 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
                 const float qf[4] = {static_cast<float>(qv[jb].x), static_cast<float>(qv[jb].y),
                                      static_cast<float>(qv[jb].z), static_cast<float>(qv[jb].w)};
                 const float df[4] = {dv[jb].x, dv[jb].y, dv[jb].z, dv[jb].w};
-                const uint16_t mh[4] = {mv[jb].x, mv[jb].y, mv[jb].z, mv[jb].w};
-                const uint16_t vh[4] = {vv[jb].x, vv[jb].y, vv[jb].z, vv[jb].w};
+                const ushort4 mz = zero_mv ? make_ushort4(0, 0, 0, 0) : mv[jb];
+                const ushort4 vz = zero_mv ? make_ushort4(0, 0, 0, 0) : vv[jb];
+                const uint16_t mh[4] = {mz.x, mz.y, mz.z, mz.w};
+                const uint16_t vh[4] = {vz.x, vz.y, vz.z, vz.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float sq = s_old * qf[e];
@@ -300,7 +342,7 @@ __device__ __forceinline__ void update_row(const UpdMatDev &M, int64_t k, bool v
     const float enc_m = pow2f(em), enc_v = pow2f(ev);
     if (lt == 0 && valid) {
         M.s[r] = s_new;
-        M.t[sl] = new_step();
+        M.t[sl] = row_state().step;
         M.mv_exp[2 * sl] = static_cast<int8_t>(em);
         M.mv_exp[2 * sl + 1] = static_cast<int8_t>(ev);
     }
@@ -394,8 +436,8 @@ struct OwnGrad {
     template <int kThreads, int kChunks>
     static constexpr int batch() { return plain_batch<kThreads, kChunks>(); }
     typedef float4 Raw;
-    const float *row;
-    __device__ __forceinline__ Raw load(int64_t c) const { return *reinterpret_cast<const float4 *>(row + c); }
+    __amdgpu_buffer_rsrc_t row;   // the dW row (C floats; empty for a missing row)
+    __device__ __forceinline__ Raw load(int64_t c) const { return ld_f4(row, 4 * c); }
     __device__ __forceinline__ void combine(const Raw &x, int64_t, float *g) const {
         g[0] = x.x;
         g[1] = x.y;
@@ -414,7 +456,8 @@ __global__ __launch_bounds__(kThreads) void k_sparse_update(const UpdParams p) {
         constexpr int kPer = decltype(per)::value;
         const int64_t k = (wg - M.row_begin) * kPer + static_cast<int>(threadIdx.x) / (kThreads / kPer);
         const bool valid = k < M.n_active;
-        update_row<kThreads, kChunks, kPer>(M, k, valid, p.hp, OwnGrad{M.G + (valid ? k : 0) * M.C});
+        update_row<kThreads, kChunks, kPer>(M, k, valid, p.hp,
+                                            OwnGrad{row_buf(M.G + (valid ? k : 0) * M.C, valid ? 4 * M.C : 0)});
     });
 }
 
@@ -427,13 +470,13 @@ struct PairGrad {
     struct Raw {
         float4 own, part;
     };
-    const float *own_row;
-    const float *part_row;   // null: the partner's row is inactive
+    __amdgpu_buffer_rsrc_t own_row;
+    __amdgpu_buffer_rsrc_t part_row;   // empty: the partner's row is inactive (reads zero)
     float c_self, c_part, a_own, a_cross;
     __device__ __forceinline__ Raw load(int64_t c) const {
         Raw x;
-        x.own = *reinterpret_cast<const float4 *>(own_row + c);
-        x.part = part_row ? *reinterpret_cast<const float4 *>(part_row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        x.own = ld_f4(own_row, 4 * c);
+        x.part = ld_f4(part_row, 4 * c);
         return x;
     }
     __device__ __forceinline__ void combine(const Raw &x, int64_t, float *g) const {
@@ -489,8 +532,8 @@ __global__ __launch_bounds__(kThreads) void k_coupled_update(const PairParams p)
         const float clip_a = S.clip ? S.clip[0] : 1.0f;
         const float clip_b = S.clip ? S.clip[1] : 1.0f;
         PairGrad gr;
-        gr.own_row = M.G + (valid ? k : 0) * M.C;
-        gr.part_row = pk >= 0 ? S.pG + pk * M.C : nullptr;
+        gr.own_row = row_buf(M.G + (valid ? k : 0) * M.C, valid ? 4 * M.C : 0);
+        gr.part_row = row_buf(pk >= 0 ? S.pG + pk * M.C : M.G, pk >= 0 ? 4 * M.C : 0);
         gr.c_self = S.self_is_b ? clip_b : clip_a;
         gr.c_part = S.self_is_b ? clip_a : clip_b;
         gr.a_own = S.a_own;
@@ -680,15 +723,19 @@ __global__ __launch_bounds__(kCkThreads) void k_rows_copy(const CkParams p) {
 // slices | first-slot-odd << 16), built per workgroup; the slices are
 // `stride` apart (team slicing: one per team).
 struct FusedGrad {
-    // (up to four partial loads per chunk)
+    // (four partial loads per chunk)
     template <int kThreads, int kChunks>
     static constexpr int batch() { return kThreads >= 1024 ? 2 : kChunks; }
     struct Raw {
         float4 x[4];
+        int32_t n, v0, cl;   // partial rows of the chunk's column block, their first slice, column in the block
+        bool odd;
     };
     const float *part;
     const float *dw_row;      // the row in dW_act
-    const int2 *tab;          // LDS
+    int64_t row_bytes;        // its bytes (0 for a missing row)
+    int64_t cols;             // its columns (0 for a missing row)
+    const int2 *tab;          // LDS, entries for the column blocks below cols only
     int64_t slot_floats;
     int32_t bn, prow, stride;
     __device__ __forceinline__ const float *slot_row(int32_t v0, int32_t i, bool odd) const {
@@ -696,37 +743,44 @@ struct FusedGrad {
         const int64_t slot = (i == 0 && odd) ? 2 * sv + 1 : 2 * sv;
         return part + slot * slot_floats + static_cast<int64_t>(prow) * bn;
     }
+    // A wave's 64 lanes take 256 consecutive columns starting on a multiple
+    // of 256 (4 columns a lane), and the product's output tiles are 256
+    // columns wide (bn), so the chunk's column block, and with it every
+    // partial row's address, is the same across the wave.  A block that
+    // starts at or past the row's end has no table entry: it reads nothing
+    // (every buffer empty, based at the partial array).
     __device__ __forceinline__ Raw load(int64_t c) const {
-        const int nb = static_cast<int>(c / bn), cl = static_cast<int>(c - static_cast<int64_t>(nb) * bn);
-        const int2 t = tab[nb];
-        const int n = t.y & 0xFFFF;
-        const bool odd = (t.y >> 16) != 0;
+        const int nb = static_cast<int>(c / bn);
+        const bool in = static_cast<int64_t>(nb) * bn < cols;
         Raw r;
-        if (n == 1) {
-            r.x[0] = *reinterpret_cast<const float4 *>(dw_row + c);
-        } else {
+        r.cl = static_cast<int>(c - static_cast<int64_t>(nb) * bn);
+        const int2 t = in ? tab[nb] : make_int2(0, 0);
+        r.v0 = __builtin_amdgcn_readfirstlane(t.x);
+        const int32_t ty = __builtin_amdgcn_readfirstlane(t.y);
+        r.n = ty & 0xFFFF;
+        r.odd = (ty >> 16) != 0;
+        // one slice covered the tile: the dW row itself; else the partial rows
+        const bool whole = r.n == 1;
+        r.x[0] = ld_f4(row_buf(whole ? dw_row : slot_row(r.v0, 0, r.odd), whole ? row_bytes : (in ? 4 * bn : 0)),
+                       whole ? 4 * c : 4 * r.cl);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < n) r.x[i] = *reinterpret_cast<const float4 *>(slot_row(t.x, i, odd) + cl);
-        }
+        for (int i = 1; i < 4; ++i)
+            r.x[i] = ld_f4(row_buf(slot_row(r.v0, i, false), i < r.n ? 4 * bn : 0), 4 * r.cl);
         return r;
     }
-    __device__ __forceinline__ void combine(const Raw &r, int64_t c, float *g) const {
-        const int nb = static_cast<int>(c / bn), cl = static_cast<int>(c - static_cast<int64_t>(nb) * bn);
-        const int2 t = tab[nb];
-        const int n = t.y & 0xFFFF;
+    __device__ __forceinline__ void combine(const Raw &r, int64_t, float *g) const {
         float4 sum = r.x[0];
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
-            if (i < n) {
+            if (i < r.n) {
                 sum.x += r.x[i].x;
                 sum.y += r.x[i].y;
                 sum.z += r.x[i].z;
                 sum.w += r.x[i].w;
             }
         }
-        for (int i = 4; i < n; ++i) {
-            const float4 y = *reinterpret_cast<const float4 *>(slot_row(t.x, i, false) + cl);
+        for (int i = 4; i < r.n; ++i) {
+            const float4 y = *reinterpret_cast<const float4 *>(slot_row(r.v0, i, false) + r.cl);
             sum.x += y.x;
             sum.y += y.y;
             sum.z += y.z;
@@ -807,6 +861,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_update(const FusedParams p) 
         FusedGrad gr;
         gr.part = S.part;
         gr.dw_row = S.dW + kk * M.C;
+        gr.row_bytes = valid ? 4 * M.C : 0;
+        gr.cols = valid ? M.C : 0;
         gr.tab = tab[sub];
         gr.slot_floats = S.slot_floats;
         gr.bn = S.bn;
