@@ -340,3 +340,43 @@ def test_scaled_moments_over_many_steps_at_extreme_gradients(gpu_lib, gmag, C):
             assert_state_equal(m.to_state(), want, f"step {step}")
     mo, vo = want.moments()
     assert np.all(np.isfinite(vo[slot])) and np.all(vo[slot] > 0)
+
+
+def test_fresh_rows_ignore_stale_slot_contents(gpu_lib):
+    """A fresh row's slot still holds what its previous owner left (or
+    garbage): step counts below zero and past the bias table, NaN and
+    infinite fp16 moments, extreme exponents.  The update reads them (its
+    loads are unconditional) but must start the row from zero moments and
+    step 1, bit for bit like the oracle; a step count that is never a valid
+    table index must not be used as one.  Plain and coupled update, 256- and
+    1024-lane launches."""
+    hp = adam_dev(**HP, t_max=100)
+    for C, seed in ((512, 3100), (11008, 3101)):
+        st, rows, slot, _, G = _case(96, C, 40, 48, seed, True)
+        fresh = np.ones(rows.size, np.uint8)
+        fresh[::3] = 0                                     # a third continue from their stored state
+        g = synth.rng(seed + 1)
+        stale = np.array([-7, -2 ** 31, 2 ** 31 - 1, 101, 5000], np.int32)
+        for i in np.nonzero(fresh)[0]:
+            s = slot[i]
+            st.t[s] = stale[i % stale.size]
+            st.m[s, : C // 2] = 0x7E00                     # NaN
+            st.v[s, C // 2:] = 0x7C00                      # +inf
+            st.e[s] = (-128, 127)
+        st.t[slot[fresh == 0]] = np.minimum(st.t[slot[fresh == 0]], 90)
+        gm = GpuMat(st, G, rows, slot, fresh)
+        _lib.sft_sparse_update([gm.upd()], hp)
+        torch.cuda.synchronize()
+        want = st.copy()
+        oracle.sparse_update(want, G, rows, slot, fresh, **HP)
+        assert_state_equal(gm.to_state(), want, f"plain C={C}")
+        # coupled: the same state on both sides of a pair, partner rows shifted by one
+        a_st, b_st = st.copy(), st.copy()
+        ga, gb = GpuMat(a_st, G, rows, slot, fresh), GpuMat(b_st, G[::-1].copy(), rows, slot, fresh)
+        _lib.sft_coupled_update([_lib.Pair(ga.upd(), gb.upd(), 1.0, 0.25, None)], hp)
+        torch.cuda.synchronize()
+        wa, wb = a_st.copy(), b_st.copy()
+        oracle.coupled_update(wa, G, rows, slot, fresh, wb, G[::-1].copy(), rows, slot, fresh,
+                              a_own=1.0, a_cross=0.25, **HP)
+        assert_state_equal(ga.to_state(), wa, f"coupled a C={C}")
+        assert_state_equal(gb.to_state(), wb, f"coupled b C={C}")
