@@ -723,11 +723,13 @@ __global__ __launch_bounds__(kCkThreads) void k_rows_copy(const CkParams p) {
 // slices | first-slot-odd << 16), built per workgroup; the slices are
 // `stride` apart (team slicing: one per team).
 struct FusedGrad {
-    // (four partial loads per chunk)
+    // (two partial rows per chunk loaded with the row; a block cut more ways
+    // adds the rest from memory while the step combines them, which keeps a
+    // 1024-lane batch of four chunks within the registers)
     template <int kThreads, int kChunks>
-    static constexpr int batch() { return kThreads >= 1024 ? 2 : kChunks; }
+    static constexpr int batch() { return kThreads >= 1024 ? (kChunks >= 8 ? 2 : 4) : kChunks; }
     struct Raw {
-        float4 x[4];
+        float4 x[2];
         int32_t n, v0, cl;   // partial rows of the chunk's column block, their first slice, column in the block
         bool odd;
     };
@@ -763,23 +765,18 @@ struct FusedGrad {
         const bool whole = r.n == 1;
         r.x[0] = ld_f4(row_buf(whole ? dw_row : slot_row(r.v0, 0, r.odd), whole ? row_bytes : (in ? 4 * bn : 0)),
                        whole ? 4 * c : 4 * r.cl);
-#pragma unroll
-        for (int i = 1; i < 4; ++i)
-            r.x[i] = ld_f4(row_buf(slot_row(r.v0, i, false), i < r.n ? 4 * bn : 0), 4 * r.cl);
+        r.x[1] = ld_f4(row_buf(slot_row(r.v0, 1, false), 1 < r.n ? 4 * bn : 0), 4 * r.cl);
         return r;
     }
     __device__ __forceinline__ void combine(const Raw &r, int64_t, float *g) const {
         float4 sum = r.x[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) {
-            if (i < r.n) {
-                sum.x += r.x[i].x;
-                sum.y += r.x[i].y;
-                sum.z += r.x[i].z;
-                sum.w += r.x[i].w;
-            }
+        if (1 < r.n) {
+            sum.x += r.x[1].x;
+            sum.y += r.x[1].y;
+            sum.z += r.x[1].z;
+            sum.w += r.x[1].w;
         }
-        for (int i = 4; i < r.n; ++i) {
+        for (int i = 2; i < r.n; ++i) {
             const float4 y = *reinterpret_cast<const float4 *>(slot_row(r.v0, i, false) + r.cl);
             sum.x += y.x;
             sum.y += y.y;
