@@ -453,13 +453,118 @@ def cpu_baseline(L0: "Layer", threads: int):
     one_ms, one_done, total, one_s = run(8, 1)
     many_ms, many_done, _, many_s = run(2, threads)
     info = host_info()
+    configs = cpu_configs(L0, threads, many_ms, total)
     return {"value": round(many_ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
             "sample": (f"every 2nd active row of each of the 7 matrices of one layer ({many_done} of {total} rows: "
                        f"masked dW rows + their update, {many_s:.1f} s on {threads} threads), scaled to the "
                        f"whole layer"),
             "single_thread": {"value": round(one_ms, 1), "unit": "ms", "cores": 1,
                               "sample": f"every 8th active row ({one_done} of {total} rows, {one_s:.1f} s), scaled"},
-            "host": info}
+            "configs": configs, "host": info}
+
+
+def cpu_configs(L0: "Layer", threads: int, layer_ms: float, layer_rows: int):
+    """The oracle on the other configurations, on the same host threads:
+    the 512 x 512 projection at T = 256 (51 rows) and the 32000 x 4096
+    embedding step (conductor over four windows, plan, scatter-gradient and
+    the update of its rows) in full; the one-row-per-tile layer (cfg 5: its
+    masked dW rows, the coupled update of the three pairs, the plain update of
+    down) on every 16th row of each matrix, scaled; and the 32-layer model step
+    at 0.5/1/2/5% rows, extrapolated from the 1% layer's measured time per
+    active row (labelled as such)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import torch
+
+    from sparse_full_weight_amd import synth
+    out = {}
+    # cfg 1
+    T, R, C = 256, 512, 512
+    X = synth.normal_bf16((T, C), 1.0, 11)
+    dY = synth.normal_bf16((T, R), 0.01, 12)
+    rows = synth.clustered_rows(R, round(0.10 * R), 13).astype(np.int32)
+    q, s_, d_ = synth.quant_state(R, C, 15)
+    t0 = time.perf_counter()
+    mask = oracle.tracker_window(np.zeros(R, np.float32), synth.tracker_magnitudes(R, rows, 14))
+    act = oracle.plan_rows(mask)["active_rows"]
+    G = oracle.masked_dw(dY, X, act)
+    k = np.arange(act.size, dtype=np.int32)
+    st = oracle.MatState(q[act], s_[act], d_[act], np.zeros((act.size, C), np.uint16),
+                         np.zeros((act.size, C), np.uint16), np.zeros(act.size, np.int32),
+                         np.zeros((act.size, C), np.uint16))
+    oracle.sparse_update(st, G, k, k, None, **HP)
+    out["cfg1_small_projection_step"] = {"value": round((time.perf_counter() - t0) * 1e3, 2), "unit": "ms",
+                                         "cores": 1, "sample": f"whole step ({act.size} rows)"}
+    # cfg 2
+    V, dd, Tb = 32000, 4096, 8 * 512
+    windows = [synth.zipf_tokens(Tb, V, 1.1, 5100 + w) for w in range(4)]
+    dYe = synth.normal_bf16((Tb, dd), 0.01, 5110)
+    t0 = time.perf_counter()
+    ch = np.zeros(V, np.float32)
+    for w in windows:
+        mask = oracle.conductor_window(ch, w)
+    act = oracle.plan_rows(mask)["active_rows"]
+    Ge = oracle.embedding_dw(dYe, windows[-1], act)
+    k = np.arange(act.size, dtype=np.int32)
+    st = oracle.MatState(np.zeros((act.size, dd), np.int8), np.full(act.size, 1e-3, np.float32),
+                         np.zeros((act.size, dd), np.float32), np.zeros((act.size, dd), np.uint16),
+                         np.zeros((act.size, dd), np.uint16), np.zeros(act.size, np.int32),
+                         np.zeros((act.size, dd), np.uint16))
+    oracle.sparse_update(st, Ge, k, k, None, **HP)
+    out["cfg2_embedding_step"] = {"value": round((time.perf_counter() - t0) * 1e3, 2), "unit": "ms", "cores": 1,
+                                  "sample": f"whole step ({act.size} rows, 4 conductor windows)"}
+    # cfg 5, sampled on the host threads
+    host = {}
+    for gname, members in L0.groups_def:
+        Xb = L0.X[gname].view(torch.int16).cpu().numpy().view(np.uint16)
+        for name in members:
+            m = L0.mats[name]
+            host[name] = (Xb, m["dY"].view(torch.int16).cpu().numpy().view(np.uint16), m["C"])
+    pairs = [("gate", "up"), ("q", "o"), ("k", "v")]
+    adv = {name: synth.one_per_tile_rows(L0.mats[name]["R"], 9100 + mi) for mi, name in enumerate(L0.mats)}
+    for a, b in pairs:
+        adv[b][::2] = adv[a][::2]
+    every = 16
+    jobs, done, total = [], 0, 0
+    for name in L0.mats:
+        sample = adv[name][::every].astype(np.int32)
+        total += adv[name].size
+        done += sample.size
+        jobs += [(name, part) for part in np.array_split(sample, 4 * threads) if part.size]
+
+    def work(name, rws):
+        Xb, dYm, Cm = host[name]
+        Gm = oracle.masked_dw(dYm, Xb, rws)
+        kk = np.arange(rws.size, dtype=np.int32)
+        z = np.zeros((rws.size, Cm), np.uint16)
+        sm = oracle.MatState(np.zeros((rws.size, Cm), np.int8), np.full(rws.size, 1e-3, np.float32),
+                             np.zeros((rws.size, Cm), np.float32), z.copy(), z.copy(), np.zeros(rws.size, np.int32),
+                             z.copy())
+        other = oracle.MatState(np.zeros((rws.size, Cm), np.int8), np.full(rws.size, 1e-3, np.float32),
+                                np.zeros((rws.size, Cm), np.float32), z.copy(), z.copy(), np.zeros(rws.size, np.int32),
+                                z.copy())
+        oracle.coupled_update(sm, Gm, kk, kk, None, other, Gm, kk, kk, None, a_own=1.0, a_cross=0.0318, **HP)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda j: work(*j), jobs))
+    dt = time.perf_counter() - t0
+    out["cfg5_adversarial_coupled_step"] = {
+        "value": round(dt * total / done * 1e3, 1), "unit": "ms", "cores": threads,
+        "sample": (f"every {every}th active row of each matrix ({done} of {total} rows: masked dW rows and a coupled "
+                   f"update of each sampled row with itself as partner, {dt:.1f} s), scaled")}
+    # cfg 4, extrapolated
+    per_row = layer_ms / layer_rows
+    emb = out["cfg2_embedding_step"]["value"]
+    ext = {}
+    for dens in (0.005, 0.01, 0.02, 0.05):
+        n = sum(round(dens * Rm) for Rm, _ in synth.LLAMA7B.values())
+        ext[str(dens)] = round(32 * n * per_row + emb, 1)
+    out["cfg4_model_step_extrapolated"] = {
+        "value": ext, "unit": "ms", "cores": threads,
+        "sample": ("32 layers x the 1% layer's oracle time per active row x the density's active rows, plus the "
+                   "embedding step: extrapolated, not run")}
+    return out
 
 
 # ---------------------------------------------------------------------- other workloads
