@@ -172,9 +172,12 @@ def units(groups, labels, kernel: str, cmd: str) -> str:
     """groups: per workload, the run directories whose counters it combines."""
     out = [f"# unit activity of {kernel} from rocprofv3 counters", f"# commands: {cmd}",
            f"# fractions: TA and TD busy cycles / ({CUS} CUs x active cycles per XCD), MFMA busy cycles / "
-           f"({SIMDS} SIMDs x active cycles per XCD), active cycles per XCD = GRBM_GUI_ACTIVE / {XCDS}", "",
+           f"({SIMDS} SIMDs x active cycles per XCD), VALU busy = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) / "
+           f"({SIMDS} SIMDs x active cycles per XCD), active cycles per XCD = GRBM_GUI_ACTIVE / {XCDS}; "
+           f"VALU inst/wave = SQ_INSTS_VALU / SQ_WAVES", "",
            f"{'workload':28s} {'cycles/XCD':>11s} {'TA busy':>8s} {'TD busy':>8s} {'MFMA busy':>10s} "
-           f"{'L2 read latency (cyc)':>22s} {'LDS busy':>9s} {'conflict cyc/LDS inst':>22s}"]
+           f"{'L2 read latency (cyc)':>22s} {'LDS busy':>9s} {'conflict cyc/LDS inst':>22s} {'VALU busy':>9s} "
+           f"{'VALU inst/wave':>15s}"]
     for label, dirs in zip(labels, groups):
         v: dict = {}
         for d in dirs:
@@ -185,8 +188,13 @@ def units(groups, labels, kernel: str, cmd: str) -> str:
                if v.get("TCP_TCC_READ_REQ_sum") else f"{'-':>22s}")
         conf = (f"{v['SQ_LDS_BANK_CONFLICT'] / v['SQ_INSTS_LDS']:22.2f}"
                 if v.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in v else f"{'-':>22s}")
+        valu = (f"{4.0 * v['SQ_ACTIVE_INST_VALU'] / (SIMDS * g):9.3f}" if "SQ_ACTIVE_INST_VALU" in v and g
+                else f"{'-':>9s}")
+        ipw = (f"{v['SQ_INSTS_VALU'] / v['SQ_WAVES']:15.0f}" if v.get("SQ_WAVES") and "SQ_INSTS_VALU" in v
+               else f"{'-':>15s}")
         out.append(f"{label:28s} {g:11.0f} {frac('TA_TA_BUSY_sum', CUS)} {frac('TD_TD_BUSY_sum', CUS)} "
-                   f"{frac('SQ_VALU_MFMA_BUSY_CYCLES', SIMDS):>10s} {lat} {frac('SQ_LDS_IDX_ACTIVE', CUS):>9s} {conf}")
+                   f"{frac('SQ_VALU_MFMA_BUSY_CYCLES', SIMDS):>10s} {lat} {frac('SQ_LDS_IDX_ACTIVE', CUS):>9s} {conf} "
+                   f"{valu} {ipw}")
     return "\n".join(out) + "\n"
 
 
