@@ -965,6 +965,29 @@ int dispatch(int64_t maxC, int64_t n_wg, const Params &p, hipStream_t stream) {
     return Launch<1024, 16>::go(n_wg, p, stream);
 }
 
+// Launches of a list of matrices sorted widest first: at most `per_launch`
+// matrices each; and when the matrices of at most 4096 columns have more
+// than two rows per CU, they take launches of their own: their 256-lane
+// workgroups then share CUs several at a time, and the load and store phases
+// of different rows interleave, where as 1024-lane workgroups beside wide rows
+// each CU would run one row (or pair) at a time in lock step.  Returns the
+// first index of each launch, and the end.
+std::vector<int32_t> launch_cuts(const std::vector<int64_t> &width, const std::vector<int64_t> &rows,
+                                 int32_t per_launch) {
+    const int32_t n = static_cast<int32_t>(width.size());
+    int64_t narrow = 0;
+    for (int32_t i = 0; i < n; ++i)
+        if (width[i] <= 256 * 4 * 4) narrow += rows[i];
+    const bool split = narrow > 2 * int64_t(sft::num_cus());
+    std::vector<int32_t> cuts;
+    for (int32_t i = 0; i < n; ++i) {
+        const bool boundary = i > 0 && split && width[i - 1] > 256 * 4 * 4 && width[i] <= 256 * 4 * 4;
+        if (i == 0 || boundary || i - cuts.back() == per_launch) cuts.push_back(i);
+    }
+    cuts.push_back(n);
+    return cuts;
+}
+
 int launch_status(const char *who) {
     const hipError_t e = hipGetLastError();
     SFT_CHECK(e == hipSuccess, SFT_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -1011,14 +1034,21 @@ int sft_sparse_update(const sft_upd_mat *mats, int32_t n_mats, const sft_adam *h
     std::vector<int32_t> order(static_cast<size_t>(n_mats));
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return mats[x].C > mats[y].C; });
-    // Matrices go out in batches of kMaxMats per launch (kernel-argument table).
-    for (int32_t base = 0; base < n_mats; base += kMaxMats) {
+    // Matrices go out in batches of kMaxMats per launch (kernel-argument table),
+    // narrow ones apart when they are many (launch_cuts).
+    std::vector<int64_t> wid, nr;
+    for (const int32_t i : order) {
+        wid.push_back(mats[i].C);
+        nr.push_back(mats[i].n_active);
+    }
+    const std::vector<int32_t> cuts = launch_cuts(wid, nr, kMaxMats);
+    for (size_t ci = 0; ci + 1 < cuts.size(); ++ci) {
         UpdParams p{};
         p.hp = a;
         int64_t n_wg = 0, maxC = 0;
         int32_t n = 0;
         UpdMatDev *list[kMaxMats];
-        for (int32_t oi = base; oi < std::min(n_mats, base + kMaxMats); ++oi) {
+        for (int32_t oi = cuts[ci]; oi < cuts[ci + 1]; ++oi) {
             const int32_t i = order[static_cast<size_t>(oi)];
             if (mats[i].n_active == 0) continue;
             p.mat[n] = make_mat(mats[i], 0);
@@ -1071,8 +1101,21 @@ int sft_coupled_update(const sft_pair *pairs, int32_t n_pairs, const sft_adam *h
     std::iota(order.begin(), order.end(), 0);
     auto width = [&](int32_t k) { return (k & 1) ? pairs[k >> 1].b.C : pairs[k >> 1].a.C; };
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return width(x) > width(y); });
+    // narrow sides apart when they are many (as launch_cuts does)
+    std::vector<int64_t> wid, nr;
     for (const int32_t k : order) {
+        wid.push_back(width(k));
+        nr.push_back((k & 1) ? pairs[k >> 1].b.n_active : pairs[k >> 1].a.n_active);
+    }
+    const std::vector<int32_t> cuts = launch_cuts(wid, nr, static_cast<int32_t>(order.size()) + 1);
+    size_t next_cut = 1;
+    for (size_t oi = 0; oi < order.size(); ++oi) {
+        const int32_t k = order[oi];
         const sft_pair &pr = pairs[k >> 1];
+        if (next_cut + 1 < cuts.size() && static_cast<int32_t>(oi) == cuts[next_cut]) {
+            ++next_cut;
+            if (int rc = flush()) return rc;
+        }
         {
             const int side = k & 1;
             const sft_upd_mat &self = side ? pr.b : pr.a;
@@ -1129,13 +1172,19 @@ int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws,
     std::vector<int32_t> order(static_cast<size_t>(n_mats));
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return mats[x].C > mats[y].C; });
-    for (int32_t base = 0; base < n_mats; base += kMaxFused) {
+    std::vector<int64_t> wid, nr;
+    for (const int32_t i : order) {
+        wid.push_back(mats[i].C);
+        nr.push_back(mats[i].n_active);
+    }
+    const std::vector<int32_t> cuts = launch_cuts(wid, nr, kMaxFused);
+    for (size_t ci = 0; ci + 1 < cuts.size(); ++ci) {
         FusedParams p{};
         p.hp = a;
         int64_t n_wg = 0, maxC = 0;
         int32_t n = 0;
         UpdMatDev *list[kMaxFused];
-        for (int32_t oi = base; oi < std::min(n_mats, base + kMaxFused); ++oi) {
+        for (int32_t oi = cuts[ci]; oi < cuts[ci + 1]; ++oi) {
             const int32_t i = order[static_cast<size_t>(oi)];
             if (mats[i].n_active == 0) continue;
             p.mat[n] = make_mat(mats[i], 0);
