@@ -39,6 +39,7 @@ constexpr int kLeafMats = 16;                        // matrices per launch (ker
 constexpr int kLeafStageWords = 16384;               // 64 KB of LDS: one dword = one column of two tokens
 constexpr int kLeafMaxPairs = 4;                     // token pairs staged at once
 constexpr int kLeafSlots = 4;                        // 16-byte chunk pairs a lane stages per batch
+constexpr int kLeafAccs[] = {12, 16, 20, 24, 28};    // coordinates per lane and pass the kernel is built for
 
 struct LeafMatDev {
     const uint16_t *D;
@@ -293,12 +294,14 @@ int check_leaf(const sft_leaf_mat *mats, int32_t n_mats, int64_t T, const char *
     return SFT_OK;
 }
 
-// Decomposition: coordinates per pass kAcc*1024 (kAcc 16 when every matrix
-// has at most 16384 coordinates, else 28, the most that fit the 128
-// registers of a 1024-lane workgroup without spilling); token ranges per matrix in
-// proportion to its share of the work (tokens x (staged row length / 4 +
-// coordinates)), about one workgroup per CU in all, each range at least one
-// LDS batch long.
+// Decomposition: coordinates per pass kAcc*1024, kAcc one of kLeafAccs (28
+// is the most that fit the 128 registers of a 1024-lane workgroup without
+// spilling), the one with the least work over the launch: every lane works
+// all kAcc of its coordinate slots whether or not they hold a coordinate, so
+// a matrix costs passes x kAcc slots per token pair, plus its staging; token
+// ranges per matrix in proportion to that cost (passes x (staged row length
+// / 4 + kAcc*1024) per token), about one workgroup per CU in all, each range
+// at least one LDS batch long.
 LeafPlan leaf_plan(const sft_leaf_mat *mats, int32_t n_mats, int64_t T) {
     LeafPlan plan;
     const int cus = sft::num_cus();
@@ -308,19 +311,25 @@ LeafPlan leaf_plan(const sft_leaf_mat *mats, int32_t n_mats, int64_t T) {
         LeafParams p{};
         p.T = T;
         std::vector<int32_t> idx;
-        int64_t kmax = 0;
         while (i < n_mats && static_cast<int32_t>(idx.size()) < kLeafMats) {
-            if (mats[i].K > 0) {
-                idx.push_back(i);
-                kmax = std::max<int64_t>(kmax, mats[i].K);
-            }
+            if (mats[i].K > 0) idx.push_back(i);
             ++i;
         }
         if (idx.empty()) break;
-        const int acc = kmax <= 16 * kLeafThreads ? 16 : 28;
+        // a matrix's work per token for kAcc a: passes x (staging + slots)
+        auto work = [&](const sft_leaf_mat &L, int a) {
+            const int64_t pp = int64_t(a) * kLeafThreads, passes = (L.K + pp - 1) / pp;
+            return double(passes) * (double(L.m + L.n) / 4.0 + double(pp));
+        };
+        int acc = kLeafAccs[0];
+        double best = -1.0;
+        for (int a : kLeafAccs) {
+            double w = 0.0;
+            for (int32_t j : idx) w += work(mats[j], a);
+            if (best < 0.0 || w < best) best = w, acc = a;
+        }
         const int64_t per_pass = int64_t(acc) * kLeafThreads;
-        double cost = 0.0;
-        for (int32_t j : idx) cost += double(mats[j].m + mats[j].n) / 4.0 + double(mats[j].K);
+        const double cost = best;
         int64_t wgs = 0, coords = 0;
         for (int32_t j : idx) {
             const sft_leaf_mat &L = mats[j];
@@ -346,7 +355,7 @@ LeafPlan leaf_plan(const sft_leaf_mat *mats, int32_t n_mats, int64_t T) {
                 for (int64_t u = 0; u < ux; ++u) d.slot[q++] = pr | (1 << 8) | int32_t(u << 16);
             }
             for (; q < kLeafSlots; ++q) d.slot[q] = -1;
-            const double share = (double(L.m + L.n) / 4.0 + double(L.K)) / cost;
+            const double share = work(L, acc) / cost;
             int64_t S = static_cast<int64_t>(share * cus / d.P + 0.5);
             S = std::max<int64_t>(1, std::min<int64_t>(S, (T + 2 * tp - 1) / (2 * tp)));
             d.S = static_cast<int32_t>(S);
@@ -392,10 +401,13 @@ int sft_leaf_grad(const sft_leaf_mat *mats, int32_t n_mats, int64_t T, void *ws,
                                                       reinterpret_cast<uintptr_t>(p.mat[j].part));
         if (T > 0) {
             const dim3 grid(static_cast<uint32_t>(plan.wgs[l]));
-            if (plan.acc[l] == 16)
-                hipLaunchKernelGGL(k_leaf_grad<16>, grid, dim3(kLeafThreads), 0, st, p);
-            else
-                hipLaunchKernelGGL(k_leaf_grad<28>, grid, dim3(kLeafThreads), 0, st, p);
+            switch (plan.acc[l]) {
+                case 12: hipLaunchKernelGGL(k_leaf_grad<12>, grid, dim3(kLeafThreads), 0, st, p); break;
+                case 16: hipLaunchKernelGGL(k_leaf_grad<16>, grid, dim3(kLeafThreads), 0, st, p); break;
+                case 20: hipLaunchKernelGGL(k_leaf_grad<20>, grid, dim3(kLeafThreads), 0, st, p); break;
+                case 24: hipLaunchKernelGGL(k_leaf_grad<24>, grid, dim3(kLeafThreads), 0, st, p); break;
+                default: hipLaunchKernelGGL(k_leaf_grad<28>, grid, dim3(kLeafThreads), 0, st, p); break;
+            }
             hipError_t e = hipGetLastError();
             SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_leaf_grad: launch failed: %s", hipGetErrorString(e));
         } else {
