@@ -25,7 +25,7 @@ rows, the adversarial one-row-per-tile layer with the coupled update, and the
 separate calls of the path; the oracle timed on the host on one thread and on
 several; the a1 host calls timed alone.
 
-Prints one JSON line (rank 0).  ``--gpus`` above 1 is refused: this build
+Prints one JSON line (rank 0).  ``--gpus`` above 1 is refused: the benchmark
 measures one GPU.
 """
 from __future__ import annotations
@@ -907,8 +907,9 @@ def skip_probe():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path would shard over token positions; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would shard over "
+              "token positions: each GPU the masked dW of its own tokens, then one reduce-scatter of the active rows)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_calibration:
