@@ -61,6 +61,18 @@ def test_leaf_grad_matches_oracle():
         _close(g, oracle.leaf_grad(D, X, rows, cols))
 
 
+@pytest.mark.parametrize("K,width", [(10000, 12), (15000, 16), (19000, 20), (23000, 24), (27000, 28)])
+def test_leaf_grad_every_kernel_width(K, width):
+    # one 256 x 256 matrix per call: the planner takes the width (coordinates
+    # per lane and pass, of 12, 16, 20, 24, 28) with the least slot work, which
+    # for (width - 4) * 1024 < K <= width * 1024 is `width` (one pass; the
+    # next smaller width would take two)
+    case = _case(70, 256, 256, K, 200 + width)
+    got, _, _ = _run([case])
+    D, X, rows, cols = case
+    _close(got[0], oracle.leaf_grad(D, X, rows, cols))
+
+
 def test_leaf_grad_integer_inputs_bit_exact():
     T = 257
     cases = [_case(T, 96, 72, 2000, 50, integer=True), _case(T, 512, 520, 36000, 60, integer=True)]
