@@ -311,13 +311,11 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// 16 bytes per lane from a raw buffer [base, base + size) at byte offset
-// voff into LDS at lds + 16*lane; offsets at or beyond size read as zero.
-// keep: an ordinary cached load (X that other M-blocks read again soon);
-// otherwise non-temporal (X read once).
-__device__ __forceinline__ void dma16_buf(const uint8_t *base, int32_t size, uint32_t voff, void *lds, bool keep) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), static_cast<short>(0), size, 0x00020000);
+// 16 bytes per lane from buffer r at byte offset voff into LDS at lds +
+// 16*lane; offsets at or beyond the buffer's size read as zero.  keep: an
+// ordinary cached load (X that other M-blocks read again soon); otherwise
+// non-temporal (X read once).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds, bool keep) {
     if (keep)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(lds), 16, voff, 0, 0, 0);
     else
@@ -343,6 +341,10 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 // the X copies of chunk j+3 into the stage chunk j-1 used.  Segment epilogues
 // store unconditionally too (masked-off lanes write to a per-wave sink), so
 // the compiler's own waits stay exact as well.
+//
+// kKeep: the cache policy of the launch's X copies, when every group has the
+// same (0 non-temporal, 1 cached), or 2: each group's own (a branch per copy).
+template <int kKeep>
 __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     __shared__ int32_t codes[kMaxSegs][kMaxTiles * 32];
     __shared__ DwGroupDev gs[kMaxGroups];   // the group table, indexable at run time
@@ -457,11 +459,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // advances by one chunk per chunk (scalar work); rows past T fall beyond
     // its size and columns past C get an offset beyond any size, so the range
     // check turns them into zeros.
+    // The next segment's first chunk is kept in a register (a chunk only
+    // compares against it), and a chunk's copies share one buffer resource.
     int sx = 0;
     const uint8_t *x_base = nullptr;
     int64_t x_rem = 0, x_stride = 0;
-    int32_t x_j0 = 0;
-    bool x_keep = false;
+    int32_t x_j0 = 0, x_next = 0;
+    bool x_keep = kKeep == 1;
     uint32_t x_voff[kCopiesX];
     auto describe_x = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
@@ -471,7 +475,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         x_rem = static_cast<int64_t>(uniform64(static_cast<uint64_t>((G.T - r0) * C * 2 - c0 * 2)));
         x_stride = static_cast<int64_t>(uniform64(static_cast<uint64_t>(kBK * C * 2)));
         x_j0 = __builtin_amdgcn_readfirstlane(S.j0);
-        x_keep = __builtin_amdgcn_readfirstlane(G.keep_x) != 0;
+        x_next = __builtin_amdgcn_readfirstlane(sg + 1 < nseg ? segs[sg + 1].j0 : J);
+        if constexpr (kKeep == 2) x_keep = __builtin_amdgcn_readfirstlane(G.keep_x) != 0;
 #pragma unroll
         for (int k = 0; k < kCopiesX; ++k) {
             const int row_in = 2 * (wave + 8 * k) + (lane >> 5);
@@ -480,16 +485,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         }
     };
     auto advance_x = [&](int32_t jx) __attribute__((always_inline)) {
-        if (jx < J && sx + 1 < nseg && jx >= segs[sx + 1].j0) {
+        if (jx >= x_next && jx < J) {
             ++sx;
             describe_x(sx);
         }
     };
-    auto issue_x = [&](int32_t jx, int k, uint8_t *stage) __attribute__((always_inline)) {
+    // the buffer resource of chunk jx's X (size 0 past the slice)
+    auto x_rsrc = [&](int32_t jx) __attribute__((always_inline)) {
         const int64_t off = static_cast<int64_t>(jx - x_j0) * x_stride;
         const int64_t rem = jx < J ? x_rem - off : 0;
         const int32_t size = static_cast<int32_t>(rem <= 0 ? 0 : (rem > 0x7fffffff ? 0x7fffffff : rem));
-        dma16_buf(x_base + (jx < J ? off : 0), size, x_voff[k], stage + (wave + 8 * k) * 1024, x_keep);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(x_base + (jx < J ? off : 0)),
+                                                 static_cast<short>(0), size, 0x00020000);
+    };
+    auto issue_x = [&](__amdgpu_buffer_rsrc_t r, int k, uint8_t *stage) __attribute__((always_inline)) {
+        dma16(r, x_voff[k], stage + (wave + 8 * k) * 1024, x_keep);
     };
 
     // ---- wave layout: wave w takes packed tile w/2 of the M-block and the
@@ -504,18 +514,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // instructions every chunk) but touches no memory.
     int sa = 0;
     const uint16_t *a_base = nullptr;
-    int32_t a_j0 = 0;
+    int32_t a_j0 = 0, a_next = 0;
     bool a_live = false;
     auto describe_a = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
+        a_next = __builtin_amdgcn_readfirstlane(sg + 1 < nseg ? segs[sg + 1].j0 : J);
         a_live = tw < S.mt;
         a_base = reinterpret_cast<const uint16_t *>(uniform64(reinterpret_cast<uint64_t>(
             G.at + (static_cast<int64_t>(S.p0 + (a_live ? tw : 0)) * (G.Tp / 8) + 8 * static_cast<int64_t>(S.k0)) * 256)));
         a_j0 = __builtin_amdgcn_readfirstlane(S.j0);
     };
     auto issue_a = [&](int32_t ja, bf16x8 (&buf)[4]) __attribute__((always_inline)) {
-        if (ja < J && sa + 1 < nseg && ja >= segs[sa + 1].j0) {
+        if (ja >= a_next && ja < J) {
             ++sa;
             describe_a(sa);
         }
@@ -572,6 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         issue_a(jj + kAAhead, ab[(U + kAAhead) % (kAAhead + 1)]);
         const int32_t jx = jj + kXAhead;
         advance_x(jx);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc(jx);
         auto bfrag = [&](int kk, bf16x8 (&b)[4]) __attribute__((always_inline)) {
             const int r0 = 16 * kk + trow;
 #pragma unroll
@@ -583,23 +595,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         };
         // The X copies are issued on every path (only the MFMA work is
         // conditional), so the compiler's count of operations in flight is
-        // exact; they sit between k-steps to overlap the matrix cores.
-        bf16x8 bc[4], bn[4];
-        if (active) bfrag(0, bc);
+        // exact; they sit between k-steps to overlap the matrix cores.  The
+        // fragments alternate between two register sets (k-step kk reads set
+        // kk%2 while set (kk+1)%2 fills), with no copies between them.
+        bf16x8 bf[2][4];
+        if (active) bfrag(0, bf[0]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if (active) {
-                if (kk < 3) bfrag(kk + 1, bn);
+                if (kk < 3) bfrag(kk + 1, bf[(kk + 1) & 1]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[c], a[kk], acc[c], 0, 0, 0);
-                if (kk < 3) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) bc[c] = bn[c];
-                }
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[kk & 1][c], a[kk], acc[c], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            issue_x(jx, kk, st_dma);
+            issue_x(xr, kk, st_dma);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -669,8 +679,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         constexpr int S = decltype(s_tag)::value;
         issue_a(S, ab[S]);
         advance_x(S);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc(S);
 #pragma unroll
-        for (int k = 0; k < kCopiesX; ++k) issue_x(S, k, xstage<S>());
+        for (int k = 0; k < kCopiesX; ++k) issue_x(xr, k, xstage<S>());
     };
     static_assert(kXAhead == 3, "prologue order");
     prologue(ic<0>{});
@@ -1108,6 +1119,20 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
     return plan;
 }
 
+// The product with its X copies' cache policy fixed when every group of the
+// launch has the same one.
+void launch_product(const DwParams &p, hipStream_t st) {
+    bool any = false, all = true;
+    for (int32_t g = 0; g < p.n_groups; ++g) {
+        any = any || p.g[g].keep_x;
+        all = all && p.g[g].keep_x;
+    }
+    const dim3 grid(static_cast<uint32_t>(p.n_wg)), block(kThreads);
+    if (!any) hipLaunchKernelGGL(k_masked_dw<0>, grid, block, 0, st, p);
+    else if (all) hipLaunchKernelGGL(k_masked_dw<1>, grid, block, 0, st, p);
+    else hipLaunchKernelGGL(k_masked_dw<2>, grid, block, 0, st, p);
+}
+
 void bind_workspace(Plan &plan, void *ws) {
     uint8_t *base = static_cast<uint8_t *>(ws);
     for (Launch &L : plan.launches) {
@@ -1191,7 +1216,7 @@ int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, s
                        dim3(256), 0, st, L.p);
     hipError_t e = hipGetLastError();
     SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: gather launch failed: %s", hipGetErrorString(e));
-    hipLaunchKernelGGL(k_masked_dw, dim3(static_cast<uint32_t>(L.p.n_wg)), dim3(kThreads), 0, st, L.p);
+    launch_product(L.p, st);
     e = hipGetLastError();
     SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
     *done = true;
@@ -1229,7 +1254,7 @@ int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t
                            dim3(256), 0, st, L.p);
         hipError_t e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: gather launch failed: %s", hipGetErrorString(e));
-        hipLaunchKernelGGL(k_masked_dw, dim3(static_cast<uint32_t>(L.p.n_wg)), dim3(kThreads), 0, st, L.p);
+        launch_product(L.p, st);
         e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
         hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(L.out_tiles), kMaxTiles), dim3(256), 0, st,
