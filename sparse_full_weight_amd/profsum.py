@@ -215,8 +215,9 @@ def skip(fetch: str, write: str, copy_fetch: str, copy_write: str, tiles, calls:
     nothing)."""
     f_scale = (COPY_BYTES / 1024) / _copy_kib(_counter(copy_fetch, "FETCH_SIZE"))
     w_scale = (COPY_BYTES / 1024) / _copy_kib(_counter(copy_write, "WRITE_SIZE"))
-    fd = [d for d in _dispatches(fetch, "FETCH_SIZE") if d[1] in DW_KERNELS]
-    wd = [d for d in _dispatches(write, "WRITE_SIZE") if d[1] in DW_KERNELS]
+    # (a kernel's template instances count as the kernel)
+    fd = [(i, kernel_of(k, DW_KERNELS), v) for i, k, v in _dispatches(fetch, "FETCH_SIZE") if kernel_of(k, DW_KERNELS)]
+    wd = [(i, kernel_of(k, DW_KERNELS), v) for i, k, v in _dispatches(write, "WRITE_SIZE") if kernel_of(k, DW_KERNELS)]
     live = [k for k in tiles if k > 0]
     out = ["# HBM traffic of masked-dW calls against active 32-row tiles (4096 x 4096 matrix, 128 tiles)",
            f"# commands: {cmd}", "",

@@ -65,7 +65,8 @@ def test_skip_groups_calls_by_gather_and_scales(tmp_path):
     values are per call and scaled by the copy calibration (here x2 for
     FETCH_SIZE, x1 for WRITE_SIZE)."""
     g = "(anonymous namespace)::k_dw_gather((anonymous namespace)::DwParams)"
-    p = "(anonymous namespace)::k_masked_dw((anonymous namespace)::DwParams)"
+    # (the product as one of its template instances, as rocprofv3 names it)
+    p = "void (anonymous namespace)::k_masked_dw<0>((anonymous namespace)::DwParams)"
     x = "(anonymous namespace)::k_dw_fixup((anonymous namespace)::DwParams)"
     copy = "__amd_rocclr_copyBuffer"
     gib = (1 << 30) / 1024
@@ -85,6 +86,7 @@ def test_skip_groups_calls_by_gather_and_scales(tmp_path):
     assert [r["tiles"] for r in rec] == [1, 2]
     assert rec[0]["gather_read"] == 100 * 1024 * 2 and rec[1]["gather_read"] == 200 * 1024 * 2
     assert rec[1]["product_write"] == 100 * 1024 and rec[0]["fixup_read"] == 10 * 1024 * 2
+    assert rec[0]["product_read"] == 1000 * 1024 * 2
     assert "0 active tiles launched no kernel" in text
 
 
