@@ -930,6 +930,8 @@ int validate(const sft_dw_group *groups, int32_t n_groups) {
                   "sft_masked_dw: group %d has T=%lld C=%lld", gi, (long long)g.T, (long long)g.C);
         SFT_CHECK(g.C % 8 == 0, SFT_ESHAPE, "sft_masked_dw: C=%lld is not a multiple of 8", (long long)g.C);
         SFT_CHECK(g.T * g.C < (int64_t(1) << 31), SFT_ENOTSUP, "sft_masked_dw: group %d: T*C reaches 2^31", gi);
+        // (a chunk's X copy offsets, up to 63 rows of C columns, stay 32-bit)
+        SFT_CHECK(g.C <= (int64_t(1) << 24), SFT_ENOTSUP, "sft_masked_dw: group %d: C above 2^24", gi);
         SFT_CHECK(g.X && sft::aligned16(g.X), g.X ? SFT_EALIGN : SFT_EINVAL,
                   "sft_masked_dw: group %d X null or not 16-byte aligned", gi);
         for (int32_t mi = 0; mi < g.n_mats; ++mi) {

@@ -219,6 +219,20 @@ def test_dw_rejects_bad_shapes(gpu_lib):
     assert e.value.code == _lib.SFT_ESHAPE
 
 
+def test_dw_rejects_c_beyond_2_24(gpu_lib):
+    # one token of 2^24 + 8 columns: T*C is fine, C itself is past the limit
+    T, R, C = 1, 32, (1 << 24) + 8
+    X = torch.zeros((T, C), dtype=torch.bfloat16, device="cuda")
+    plan = _lib.sft_plan_rows(_mask_rows(R, [0]))
+    out = torch.zeros((1, C), dtype=torch.float32, device="cuda")
+    g = [_lib.DwGroup(X, [_lib.DwMat(bf16_dev(synth.normal_bf16((T, R), 0.01, 3)), plan.to_device(), out)])]
+    with pytest.raises(_lib.SftError):
+        _lib.sft_masked_dw_workspace(g)
+    with pytest.raises(_lib.SftError) as e:
+        _lib.sft_masked_dw(g, None)
+    assert e.value.code == _lib.SFT_ENOTSUP
+
+
 # ------------------------------------------------------------------ embedding
 
 
