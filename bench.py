@@ -16,7 +16,12 @@ Active Set", sections 2.1-2.6.
 
 Steps cycle through a ring of distinct layers (like the layers of one model
 step), so that every step reads its inputs from HBM rather than from the
-256 MB last-level cache.
+256 MB last-level cache.  The layers' steps are independent of each other,
+so consecutive layers alternate between two streams (both of the default
+priority; a layer always on the same one): one layer's launches fill the
+CUs the other's leave idle while it starts, drains and runs its update.  The
+same steps on one stream are reported beside the value
+(``ms_per_step_one_stream``).
 
 Besides the headline, the JSON line carries (``rows``) the other workloads
 timed as steps: the 512x512 projection (10% rows), the whole 7B-shaped model
@@ -72,6 +77,11 @@ def parse_args():
                     help="time only the other calls (prints their JSON object), for profiling them apart "
                          "from the layer step")
     ap.add_argument("--no-model", action="store_true", help="skip the 32-layer model step")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="every step on one stream (no overlap of consecutive layers)")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="only the warm-up and the K timed steps (prints their ms per step), for kernel traces of "
+                         "the step schedule")
     ap.add_argument("--model-steps", type=int, default=10)
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probes of the HBM and matrix-core rates this device sustains")
@@ -318,6 +328,43 @@ def timed_blocks(fn, K: int, block: int, stream):
     torch.cuda.synchronize()
     per = [evs[b].elapsed_time(evs[b + 1]) / block for b in range(n_blocks)]
     return evs[0].elapsed_time(evs[-1]) / K, per
+
+
+def timed_blocks_lanes(fn, K: int, block: int, lanes):
+    """timed_blocks over several streams: fn(i) may enqueue on any of `lanes`.
+    The other lanes wait for the start event on lanes[0] and are joined back
+    into it (an event wait) before each block's event, so every block's
+    interval covers all of its work."""
+    import torch
+    main, others = lanes[0], lanes[1:]
+    block = max(1, min(block, K))
+    n_blocks = max(1, K // block)
+    K = n_blocks * block
+    evs = [_ev() for _ in range(n_blocks + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(main)
+    for s in others:
+        s.wait_event(evs[0])
+    for b in range(n_blocks):
+        for j in range(block):
+            fn(b * block + j)
+        for s in others:
+            e = torch.cuda.Event()
+            e.record(s)
+            main.wait_event(e)
+        evs[b + 1].record(main)
+    torch.cuda.synchronize()
+    per = [evs[b].elapsed_time(evs[b + 1]) / block for b in range(n_blocks)]
+    return evs[0].elapsed_time(evs[-1]) / K, per
+
+
+# The streams the layer steps alternate over (set by main; one stream when
+# --one-stream).  A layer's launches always go to the same one.
+LANES = None
+
+
+def lane(L):
+    return LANES[L.idx % len(LANES)]
 
 
 def _stats(per):
@@ -580,11 +627,41 @@ def leaf_support(m: int, n: int, seed: int):
     return (flat // n).astype(np.int32), (flat % n).astype(np.int32)
 
 
+def _warm(fn, calls: int, seconds: float):
+    """Untimed calls of fn(i): at least `calls`, and for at least `seconds`
+    (after a pause on the host the first steps run slower, more so with the
+    lanes overlapping)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < calls or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def _ring_step_ms(ring, fn, K, stream, block=10):
+    """fn(L, st) enqueues layer L's step on st; the ring's layers alternate
+    over the lanes."""
+    import torch
+
+    def one(i):
+        L = ring[i % len(ring)]
+        st = lane(L)
+        with torch.cuda.stream(st):
+            fn(L, st)
+    _warm(one, 5, 0.1)
+    return timed_blocks_lanes(one, K, block, LANES)
+
+
+def _ring_serial_ms(ring, fn, K, stream, block=10):
+    """fn(L) enqueues one call of layer L on `stream`; the ring's calls one
+    after the other (a call's own duration)."""
     for i in range(5):
         fn(ring[i % len(ring)])
-    mean, per = timed_blocks(lambda i: fn(ring[i % len(ring)]), K, block, stream)
-    return mean, per
+    return timed_blocks(lambda i: fn(ring[i % len(ring)]), K, block, stream)
 
 
 def small_projection_step(K, stream):
@@ -594,9 +671,9 @@ def small_projection_step(K, stream):
     groups = (("x", ("w",)),)
     ring = [Layer(300 + i, 256, 0.10, 8000, "packed", shapes=shapes, groups=groups) for i in range(4)]
 
-    def fn(L):
+    def fn(L, st):
         L.upload_plan()
-        L.fused_call(stream)
+        L.fused_call(st)
     mean, per = _ring_step_ms(ring, fn, K, stream)
     work = ring[0].dw_work().bytes + ring[0].upd_work().bytes
     return dict(_hbm(work, mean), **_stats(per), active_rows=ring[0].n_active(), tokens=256,
@@ -661,7 +738,8 @@ def model_step(T, K, stream, densities=(0.005, 0.01, 0.02, 0.05), n_layers=32):
     """The whole 7B-shaped model: 32 layers with distinct activations,
     gradients and state, and the 32000 x 4096 embedding; fresh seeded masks
     per layer at each density.  One step = every layer's plan upload and fused
-    call, then the embedding's plan upload, scatter-gradient and update."""
+    call (consecutive layers on alternate lanes), then the embedding's plan
+    upload, scatter-gradient and update."""
     import torch
     t0 = time.perf_counter()
     bufs = [layer_buffers(T, 11000 + 100 * i) for i in range(n_layers)]
@@ -677,12 +755,13 @@ def model_step(T, K, stream, densities=(0.005, 0.01, 0.02, 0.05), n_layers=32):
 
         def step(_):
             for L in layers:
-                L.upload_plan()
-                L.fused_call(stream)
+                st = lane(L)
+                with torch.cuda.stream(st):
+                    L.upload_plan()
+                L.fused_call(st)
             emb.step(stream)
-        for i in range(2):
-            step(i)
-        mean, per = timed_blocks(step, K, 1, stream)
+        _warm(step, 2, 0.3)
+        mean, per = timed_blocks_lanes(step, K, 1, LANES)
         work = sum(L.dw_work().bytes + L.upd_work().bytes for L in layers) + emb.work()
         out[f"{density:g}"] = dict(_hbm(work, mean), **_stats(per),
                                    ms_per_layer=round(mean / n_layers, 5),
@@ -788,14 +867,15 @@ def other_rows(L0: "Layer", K: int, stream, with_model=True, model_steps=10):
     del leaf, lvecs, lws
 
     # ---- the layer step at the model's other row densities (0.5%, 2%, 5%),
-    # plan upload included, over a ring of 3 layers at each density
+    # plan upload included, over a ring of 4 layers at each density (two on
+    # each lane)
     sweep = {}
     for density in (0.005, 0.02, 0.05):
-        ring = [Layer(100 + i, L0.T, density, 6000, "packed") for i in range(3)]
+        ring = [Layer(100 + i, L0.T, density, 6000, "packed") for i in range(4)]
 
-        def fn(L):
+        def fn(L, st):
             L.upload_plan()
-            L.fused_call(stream)
+            L.fused_call(st)
         mean, per = _ring_step_ms(ring, fn, K, stream)
         work = ring[0].dw_work().bytes + ring[0].upd_work().bytes
         sweep[f"{density:g}"] = dict(_hbm(work, mean), **_stats(per), active_rows=ring[0].n_active())
@@ -809,14 +889,14 @@ def other_rows(L0: "Layer", K: int, stream, with_model=True, model_steps=10):
     share = {}
     for n_gpu in (2, 4, 8):
         T = L0.T // n_gpu
-        ring = [Layer(200 + i, T, L0.density, 7000, "packed") for i in range(3)]
+        ring = [Layer(200 + i, T, L0.density, 7000, "packed") for i in range(4)]
         dw_b, up_b = ring[0].dw_work().bytes, ring[0].upd_work().bytes
 
-        def fn(L):
+        def fn(L, st):
             L.upload_plan()
-            L.fused_call(stream)
+            L.fused_call(st)
         mean, _ = _ring_step_ms(ring, fn, K, stream)
-        dw_ms, _ = _ring_step_ms(ring, lambda L: L.dw_call(stream), K, stream)
+        dw_ms, _ = _ring_serial_ms(ring, lambda L: L.dw_call(stream), K, stream)
         share[f"T{T}"] = dict(_hbm(dw_b + up_b, mean), n_gpus_sharing=n_gpu, tokens=T, masked_dw=_hbm(dw_b, dw_ms))
         del ring
         torch.cuda.empty_cache()
@@ -928,29 +1008,36 @@ def main():
 
     from sparse_full_weight_amd import synth
     stream = torch.cuda.current_stream()
+    global LANES
+    LANES = (stream,) if args.one_stream else (stream, torch.cuda.Stream())
     if args.rows_only:
         print(json.dumps({"rows": other_rows(layers[0], min(args.steps, 100), stream, not args.no_model,
                                              args.model_steps)}), flush=True)
         return
 
-    def call(L):
+    def call(L, st):
         if args.unfused:
-            L.dw_call(stream)
-            L.upd_call(stream)
+            L.dw_call(st)
+            L.upd_call(st)
         else:
-            L.fused_call(stream)
+            L.fused_call(st)
 
-    def step(i):
+    def step(i, lanes=None):
         # the step: this step's plan to the device, then the masked dW and
-        # update, in one stream.  (Copying the next step's plan on a second
-        # stream during this step measured slower: the cross-stream waits
-        # cost more than the copy.)
+        # update, on the layer's lane.  (Copying the next step's plan on
+        # another stream during this step, ordered by events, measured slower:
+        # the cross-stream waits cost more than the copy.)
         L = layers[i % len(layers)]
-        L.upload_plan()
-        call(L)
+        st = lane(L) if lanes is None else lanes[0]
+        with torch.cuda.stream(st):
+            L.upload_plan()
+        call(L, st)
 
-    def step_resident(i):
-        call(layers[i % len(layers)])
+    def step_resident(i, lanes=None):
+        L = layers[i % len(layers)]
+        call(L, lane(L) if lanes is None else lanes[0])
+
+    one = (stream,)
 
     # Untimed: about 0.1 s of steps so that the clocks have settled, then the
     # W warmup steps.
@@ -966,8 +1053,14 @@ def main():
     K = args.steps
     # The timed loop: K whole steps back to back, with an event pair around the
     # run and an event every `block` steps (between steps, never inside one).
-    ms_per_step, per_block = timed_blocks(step, K, args.block, stream)
-    ms_resident, per_block_res = timed_blocks(step_resident, K, args.block, stream)
+    ms_per_step, per_block = timed_blocks_lanes(step, K, args.block, LANES)
+    if args.steps_only:
+        print(json.dumps({"ms_per_step": round(ms_per_step, 5), "steps": K, "lanes": len(LANES)}), flush=True)
+        return
+    ms_resident, per_block_res = timed_blocks_lanes(step_resident, K, args.block, LANES)
+    # the same steps with every layer on one stream
+    ms_one, per_one = timed_blocks_lanes(lambda i: step(i, one), K, args.block, one)
+    ms_one_res, _ = timed_blocks_lanes(lambda i: step_resident(i, one), K, args.block, one)
 
     # Per-call durations, each timed over its own back-to-back run of K calls
     # on the same stream and inputs (the masked-dW call is the gather, product
@@ -1035,10 +1128,16 @@ def main():
                             "(7 matrices), "
                             + ("two calls" if args.unfused else
                                "one call: sft_masked_dw_update, the split tiles' fix-up done by the update")
-                            + "; activations, gradients and state resident in HBM"),
+                            + "; activations, gradients and state resident in HBM; consecutive layers' steps "
+                              "alternate between the lanes (streams of the default priority, a layer always on "
+                              "the same one), so one layer's step overlaps the next one's"),
+                   "lanes": len(LANES),
                    "step_stats": _stats(per_block),
                    "ms_per_step_plan_resident": round(ms_resident, 5),
                    "step_stats_plan_resident": _stats(per_block_res),
+                   "ms_per_step_one_stream": round(ms_one, 5),
+                   "step_stats_one_stream": _stats(per_one),
+                   "ms_per_step_one_stream_plan_resident": round(ms_one_res, 5),
                    "step_GB_s": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
                    "hbm_roofline_ms": round((dw.bytes + up.bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 5)},
         "roofline": {"bound": "hbm", "kernel": "sft_masked_dw (k_dw_gather + k_masked_dw + k_dw_fixup)",

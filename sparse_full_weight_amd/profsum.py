@@ -26,7 +26,12 @@ support:
 * ``skip``: HBM bytes per masked-dW call against the number of active 32-row
   tiles, from ``FETCH_SIZE`` / ``WRITE_SIZE`` runs of ``bench.py
   --skip-probe`` (calls with 0, 1, 2, 4, 8, 16 active tiles of 128, three
-  each, in that order), scaled like ``counters``.
+  each, in that order), scaled like ``counters``;
+* ``overlap``: how much kernels of a ``--kernel-trace`` run ran at the same
+  time (from ``*_kernel_trace.csv``): the span from the first start to the
+  last end, the time at least one kernel ran, the time two or more did, and
+  the sum of all durations, over the dispatches of this library's kernels
+  (plus the plan copies) from the named dispatch on.
 
 Usage:
   python -m sparse_full_weight_amd.profsum stats <kernel_stats.csv> --cmd "<command>" > out.txt
@@ -36,6 +41,7 @@ Usage:
       --label "<workload>" ... --cmd "<commands>" > out.txt
   python -m sparse_full_weight_amd.profsum skip --fetch <dir> --write <dir> \\
       --copy-fetch <dir> --copy-write <dir> --cmd "<commands>" > out.txt
+  python -m sparse_full_weight_amd.profsum overlap <kernel_trace.csv> --cmd "<command>" > out.txt
 (each <dir> holds the ``*_counter_collection.csv`` of one run).
 """
 from __future__ import annotations
@@ -270,6 +276,39 @@ def read_traffic(path: str) -> dict | None:
     return None
 
 
+def _ours(name: str) -> bool:
+    s = short(name)
+    return s.startswith("k_") or s.startswith("__amd_rocclr_copyBuffer")
+
+
+def overlap(path: str, cmd: str, first: int = 0) -> str:
+    """Concurrency of the trace's kernels (dispatch id >= first): span, busy
+    time (union of the intervals), time with two or more running, and the
+    sum of the durations, all in microseconds."""
+    rows = [r for r in csv.DictReader(open(path)) if _ours(r["Kernel_Name"]) and int(r["Dispatch_Id"]) >= first]
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows)
+    ev = sorted([(a, 1) for a, _ in iv] + [(b, -1) for _, b in iv], key=lambda e: (e[0], e[1]))
+    busy = multi = 0
+    depth, last = 0, None
+    for t, d in ev:
+        if last is not None:
+            if depth >= 1:
+                busy += t - last
+            if depth >= 2:
+                multi += t - last
+        depth += d
+        last = t
+    span = (iv[-1][1] - iv[0][0]) if iv else 0
+    total = sum(b - a for a, b in iv)
+    out = ["# kernel concurrency from a rocprofv3 kernel trace", f"# command: {cmd}", "",
+           f"dispatches: {len(iv)} (this library's kernels and the plan copies, from dispatch {first} on)",
+           f"span from first start to last end: {span / 1e3:.1f} us",
+           f"time with at least one kernel running: {busy / 1e3:.1f} us",
+           f"time with two or more running: {multi / 1e3:.1f} us ({(multi / busy if busy else 0):.3f} of the busy time)",
+           f"sum of the kernels' durations: {total / 1e3:.1f} us ({(total / busy if busy else 0):.3f} x the busy time)"]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -293,12 +332,18 @@ def main(argv=None):
     c.add_argument("--label", action="append", required=True)
     c.add_argument("--kernel", default="k_masked_dw")
     c.add_argument("--cmd", required=True)
+    o = sub.add_parser("overlap")
+    o.add_argument("csv")
+    o.add_argument("--first", type=int, default=0, help="first dispatch id to count")
+    o.add_argument("--cmd", required=True)
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(stats(args.csv, args.cmd))
     elif args.what == "skip":
         sys.stdout.write(skip(args.fetch, args.write, args.copy_fetch, args.copy_write,
                               [int(x) for x in args.tiles.split(",")], args.calls, args.tokens, args.cmd))
+    elif args.what == "overlap":
+        sys.stdout.write(overlap(args.csv, args.cmd, args.first))
     elif args.what == "units":
         if len(args.runs) != len(args.label):
             raise SystemExit("one --label per --runs")

@@ -97,3 +97,26 @@ def test_units_valu_columns(tmp_path):
                    (k, "SQ_INSTS_VALU", 5000.0), (k, "SQ_WAVES", 10.0)])
     row = [ln for ln in profsum.units([[a]], ["upd"], "k_fused_update", "c").splitlines() if ln.startswith("upd")][0]
     assert row.split()[-2:] == ["0.300", "500"]
+
+
+def test_overlap_counts_concurrent_time(tmp_path):
+    # three kernels: [0, 10) and [5, 20) overlap for 5 us, [30, 35) alone;
+    # another library's kernel is not counted
+    path = str(tmp_path / "kt.csv")
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i, (k, a, b) in enumerate([("void (anonymous namespace)::k_masked_dw<0>(x)", 0, 10000),
+                                       ("(anonymous namespace)::k_fused_update<1024, 4>(y)", 5000, 20000),
+                                       ("__amd_rocclr_copyBuffer", 30000, 35000),
+                                       ("at::native::elementwise_kernel", 0, 99000)]):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Start_Timestamp": a, "End_Timestamp": b})
+    text = profsum.overlap(path, "cmd")
+    assert "dispatches: 3" in text
+    assert "span from first start to last end: 35.0 us" in text
+    assert "time with at least one kernel running: 25.0 us" in text
+    assert "time with two or more running: 5.0 us (0.200 of the busy time)" in text
+    assert "sum of the kernels' durations: 30.0 us (1.200 x the busy time)" in text
+    # from dispatch 2 on: the first kernel is left out
+    assert "time with two or more running: 0.0 us" in profsum.overlap(path, "cmd", first=2)
+
