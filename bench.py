@@ -17,10 +17,10 @@ Active Set", sections 2.1-2.6.
 Steps cycle through a ring of distinct layers (like the layers of one model
 step), so that every step reads its inputs from HBM rather than from the
 256 MB last-level cache.  The layers' steps are independent of each other,
-so consecutive layers alternate between two streams (both of the default
-priority; a layer always on the same one): one layer's launches fill the
-CUs the other's leave idle while it starts, drains and runs its update.  The
-same steps on one stream are reported beside the value
+so consecutive layers alternate between three streams, the lanes (all of the
+default priority; layer i always on lane i mod 3): one layer's launches fill
+the CUs the others leave idle while they start, drain and run their updates.
+The same steps on one stream are reported beside the value
 (``ms_per_step_one_stream``).
 
 Besides the headline, the JSON line carries (``rows``) the other workloads
@@ -77,8 +77,9 @@ def parse_args():
                     help="time only the other calls (prints their JSON object), for profiling them apart "
                          "from the layer step")
     ap.add_argument("--no-model", action="store_true", help="skip the 32-layer model step")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="every step on one stream (no overlap of consecutive layers)")
+    ap.add_argument("--lanes", type=int, default=3,
+                    help="streams the layers' steps alternate over (layer i on lane i mod lanes); 1: one stream")
+    ap.add_argument("--one-stream", action="store_true", help="the same as --lanes 1")
     ap.add_argument("--steps-only", action="store_true",
                     help="only the warm-up and the K timed steps (prints their ms per step), for kernel traces of "
                          "the step schedule")
@@ -669,7 +670,7 @@ def small_projection_step(K, stream):
     two clustered tiles): plan upload, masked dW and update in one call."""
     shapes = {"w": (512, 512)}
     groups = (("x", ("w",)),)
-    ring = [Layer(300 + i, 256, 0.10, 8000, "packed", shapes=shapes, groups=groups) for i in range(4)]
+    ring = [Layer(300 + i, 256, 0.10, 8000, "packed", shapes=shapes, groups=groups) for i in range(6)]
 
     def fn(L, st):
         L.upload_plan()
@@ -867,11 +868,11 @@ def other_rows(L0: "Layer", K: int, stream, with_model=True, model_steps=10):
     del leaf, lvecs, lws
 
     # ---- the layer step at the model's other row densities (0.5%, 2%, 5%),
-    # plan upload included, over a ring of 4 layers at each density (two on
-    # each lane)
+    # plan upload included, over a ring of 6 layers at each density (spread
+    # evenly over the lanes)
     sweep = {}
     for density in (0.005, 0.02, 0.05):
-        ring = [Layer(100 + i, L0.T, density, 6000, "packed") for i in range(4)]
+        ring = [Layer(100 + i, L0.T, density, 6000, "packed") for i in range(6)]
 
         def fn(L, st):
             L.upload_plan()
@@ -889,7 +890,7 @@ def other_rows(L0: "Layer", K: int, stream, with_model=True, model_steps=10):
     share = {}
     for n_gpu in (2, 4, 8):
         T = L0.T // n_gpu
-        ring = [Layer(200 + i, T, L0.density, 7000, "packed") for i in range(4)]
+        ring = [Layer(200 + i, T, L0.density, 7000, "packed") for i in range(6)]
         dw_b, up_b = ring[0].dw_work().bytes, ring[0].upd_work().bytes
 
         def fn(L, st):
@@ -1009,7 +1010,8 @@ def main():
     from sparse_full_weight_amd import synth
     stream = torch.cuda.current_stream()
     global LANES
-    LANES = (stream,) if args.one_stream else (stream, torch.cuda.Stream())
+    n_lanes = 1 if args.one_stream else max(1, args.lanes)
+    LANES = (stream,) + tuple(torch.cuda.Stream() for _ in range(n_lanes - 1))
     if args.rows_only:
         print(json.dumps({"rows": other_rows(layers[0], min(args.steps, 100), stream, not args.no_model,
                                              args.model_steps)}), flush=True)
