@@ -61,7 +61,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--block", type=int, default=10,
+    ap.add_argument("--block", type=int, default=12,
                     help="steps between the timing events whose block means give the median and percentiles")
     ap.add_argument("--layers", type=int, default=6, help="ring of distinct layers cycled by the steps")
     ap.add_argument("--density", type=float, default=0.01)
@@ -210,9 +210,11 @@ class Layer:
         # the update matrices follow the groups' matrices in order
         self.fused_call = _lib.prepare_masked_dw_update(groups, self.ws, upd, self.hp)
 
-    def upload_plan(self):
-        n = self.plan_len
-        self.plan_dev[:n].copy_(self.plan_host[:n], non_blocking=True)
+    def upload_plan(self, stream=None):
+        # one kernel on the stream reads the pinned plan over the bus
+        # (sft_plan_upload)
+        from sparse_full_weight_amd import _lib
+        _lib.sft_plan_upload(self.plan_dev, self.plan_host, 4 * self.plan_len, stream)
 
     def n_active(self):
         return int(sum(m["plan"].n_active for m in self.mats.values()))
@@ -291,11 +293,12 @@ class Embedding:
             [_lib.UpdMat(st["q"], st["s"], st["delta"], st["m"], st["v"], st["t"], st["e"], rows_d, slot_d,
                          self.G[:n], n, None, st["w"])], hp)
 
-    def upload_plan(self):
-        self.plan_dev.copy_(self.plan_host, non_blocking=True)
+    def upload_plan(self, stream=None):
+        from sparse_full_weight_amd import _lib
+        _lib.sft_plan_upload(self.plan_dev, self.plan_host, None, stream)
 
     def step(self, stream):
-        self.upload_plan()
+        self.upload_plan(stream)
         self.emb_call(stream)
         self.upd_call(stream)
 
@@ -315,47 +318,40 @@ def timed_blocks(fn, K: int, block: int, stream):
     """K calls of fn(i) back to back on `stream`, with an event pair around
     the whole run and an event between every `block` calls.  Returns the mean
     ms per call over all K and the block means (ms per call)."""
-    import torch
-    block = max(1, min(block, K))
-    n_blocks = max(1, K // block)
-    K = n_blocks * block
-    evs = [_ev() for _ in range(n_blocks + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for b in range(n_blocks):
-        for j in range(block):
-            fn(b * block + j)
-        evs[b + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[b].elapsed_time(evs[b + 1]) / block for b in range(n_blocks)]
-    return evs[0].elapsed_time(evs[-1]) / K, per
+    return timed_blocks_lanes(fn, K, block, (stream,))
 
 
 def timed_blocks_lanes(fn, K: int, block: int, lanes):
-    """timed_blocks over several streams: fn(i) may enqueue on any of `lanes`.
-    The other lanes wait for the start event on lanes[0] and are joined back
-    into it (an event wait) before each block's event, so every block's
-    interval covers all of its work."""
+    """Exactly K calls of fn(i) (i = 0..K-1), which may enqueue on any of
+    `lanes`, with an event pair around the whole run on lanes[0] and an event
+    after every `block` calls (the last block may be shorter).  The other
+    lanes wait for the start event, and are joined back into lanes[0] (an
+    event wait) before each block's event, so that every block's interval
+    covers all of its work.  Returns the mean ms per call over all K and the
+    means of the full blocks (ms per call)."""
     import torch
     main, others = lanes[0], lanes[1:]
+    K = max(1, K)
     block = max(1, min(block, K))
-    n_blocks = max(1, K // block)
-    K = n_blocks * block
-    evs = [_ev() for _ in range(n_blocks + 1)]
+    bounds = list(range(0, K, block)) + [K]
+    evs = [_ev() for _ in bounds]
     torch.cuda.synchronize()
     evs[0].record(main)
     for s in others:
         s.wait_event(evs[0])
-    for b in range(n_blocks):
-        for j in range(block):
-            fn(b * block + j)
+    for b in range(len(bounds) - 1):
+        for i in range(bounds[b], bounds[b + 1]):
+            fn(i)
         for s in others:
             e = torch.cuda.Event()
             e.record(s)
             main.wait_event(e)
         evs[b + 1].record(main)
     torch.cuda.synchronize()
-    per = [evs[b].elapsed_time(evs[b + 1]) / block for b in range(n_blocks)]
+    per = [evs[b].elapsed_time(evs[b + 1]) / block for b in range(len(bounds) - 1)
+           if bounds[b + 1] - bounds[b] == block]
+    if not per:
+        per = [evs[0].elapsed_time(evs[-1]) / K]
     return evs[0].elapsed_time(evs[-1]) / K, per
 
 
@@ -643,7 +639,7 @@ def _warm(fn, calls: int, seconds: float):
     torch.cuda.synchronize()
 
 
-def _ring_step_ms(ring, fn, K, stream, block=10):
+def _ring_step_ms(ring, fn, K, stream, block=12):
     """fn(L, st) enqueues layer L's step on st; the ring's layers alternate
     over the lanes."""
     import torch

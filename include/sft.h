@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SFT_ABI_VERSION 13
+#define SFT_ABI_VERSION 14
 
 enum {
     SFT_OK = 0,
@@ -218,6 +218,19 @@ int64_t sft_plan_layer_words(const sft_layer_mat *mats, int32_t n_mats);
 
 int sft_plan_layer(sft_layer_mat *mats, int32_t n_mats, int32_t *packed, int64_t packed_cap,
                    int64_t *packed_len);
+
+/*
+ * Section 2.6 and Figure 2 (the step's masks go to the GPU once per step):
+ * copies `bytes` bytes of a plan in pinned host memory (`src`, allocated by
+ * hipHostMalloc or an allocator built on it, such as torch's pin_memory) to
+ * device memory `dst`, by a kernel on `stream` that reads the host buffer
+ * over the bus.  Asynchronous like a copy on the stream: src must stay
+ * unchanged until the stream has passed the call.  bytes is a multiple of 4
+ * (plans are int32 words); dst and src are 16-byte aligned.
+ * Errors: SFT_EINVAL (null, or src not pinned host memory), SFT_ESHAPE
+ * (bytes % 4), SFT_EALIGN, SFT_ENOTSUP (bytes >= 2^31), SFT_EHIP.
+ */
+int sft_plan_upload(void *dst, const void *src, size_t bytes, void *stream);
 
 /*
  * Adam bias corrections (section 2.4: Adam with its bias correction):

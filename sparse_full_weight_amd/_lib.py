@@ -36,6 +36,7 @@ EXPORTS = (
     "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
     "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma",
     "sft_noalloc_scratch_bytes", "sft_masked_dw_update_noalloc", "sft_plan_layer_words", "sft_plan_layer",
+    "sft_plan_upload",
 )
 
 
@@ -153,6 +154,7 @@ def lib() -> C.CDLL:
         L.sft_plan_layer_words.restype = i64
         L.sft_plan_layer.argtypes = [C.POINTER(CLayerMat), i32, p, i64, C.POINTER(C.c_int64)]
         L.sft_bias_table.argtypes = [f32, f32, i32, p, p]
+        L.sft_plan_upload.argtypes = [p, p, C.c_size_t, p]
         L.sft_masked_dw_workspace.argtypes = [C.POINTER(CDwGroup), i32]
         L.sft_masked_dw_workspace.restype = C.c_size_t
         L.sft_masked_dw.argtypes = [C.POINTER(CDwGroup), i32, p, C.c_size_t, p]
@@ -348,6 +350,21 @@ def sft_slots_update(row_slot: np.ndarray, n_slots: int, active_rows: np.ndarray
     _check(lib().sft_slots_update(_np_ptr(row_slot), row_slot.size, n_slots, _np_ptr(active_rows),
                                   active_rows.size, _np_ptr(slot), _np_ptr(fresh)))
     return slot[:active_rows.size].copy(), fresh[:active_rows.size].copy()
+
+
+def sft_plan_upload(dst, src, nbytes: int | None = None, stream=None) -> None:
+    """Section 2.6 / Figure 2: the first nbytes (default: all of src) of a
+    pinned host tensor src copied to the GPU tensor dst by a kernel on the
+    stream (asynchronous; src must stay unchanged until the stream has
+    passed the call)."""
+    if src.is_cuda or not src.is_pinned():
+        raise TypeError("src must be a pinned host tensor")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size() or n > dst.numel() * dst.element_size():
+        raise ValueError(f"{n} bytes exceed src or dst")
+    _check(lib().sft_plan_upload(_dev(dst), src.data_ptr(), n, _stream(stream)))
 
 
 @dataclass

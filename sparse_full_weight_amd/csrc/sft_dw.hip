@@ -28,11 +28,15 @@
 //      waves share a packed tile, each taking four of its eight 32-column
 //      blocks.  The launch is persistent and
 //      stream-K: one 8-wave workgroup per CU takes an equal slice of the
-//      (output tile, chunk) iteration space.
+//      (output tile, chunk) iteration space; or, where the tiles line up with
+//      the CUs, tile-aligned slices, team slices (groups of three or more
+//      M-blocks), or narrow whole tiles (128 columns x 128-token chunks, one
+//      tile per workgroup, no partial sums at all).
 //   3. Fix-up.  Output tiles cut by slice boundaries leave partial sums in
 //      scratch; this kernel adds them in slice order (deterministic; the
 //      kernel boundary orders the stores, so no device-scope fence is needed
-//      -- such a fence writes back and invalidates an XCD's L2).
+//      -- such a fence writes back and invalidates an XCD's L2).  Narrow
+//      launches have nothing to add and skip it.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -52,6 +56,10 @@ typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
 constexpr int kBN = 256;             // columns per output tile: 8 MFMA column blocks of 32
 constexpr int kMaxTiles = 4;         // packed tiles per M-block
 constexpr int kBK = 64;              // tokens per chunk: 4 MFMA k-steps of 16
+// Narrow output tiles (launches where every workgroup takes one whole tile):
+// 128 columns, chunks of 128 tokens (the same 32 KB of X a chunk).
+constexpr int kBNn = 128, kBKn = 128;
+static_assert(kBK * kBN == kBKn * kBNn, "one X stage size for both tile shapes");
 constexpr int kRound = 4;            // chunks per pipeline round (segments are whole rounds)
 constexpr int kThreads = 512;        // 8 waves
 constexpr int kXStages = 4;          // X ring depth
@@ -93,7 +101,7 @@ struct DwGroupDev {
     uint16_t *at;           // gathered operand [n_ptiles][Tp/8][32][8] bf16
     int32_t *rowmap;        // [n_ptiles*32]: (matrix << 24) | row of dW_act, or -1
     int64_t T, C;
-    int32_t Tp;             // tokens rounded up to whole rounds (multiple of 512)
+    int32_t Tp;             // tokens rounded up to whole rounds (of 256 tokens; 512 for narrow tiles)
     int32_t layout;
     int32_t mat_begin, n_mats;
     int32_t n_rows, n_ptiles, n_mblk, n_nblk, chunks;
@@ -113,6 +121,7 @@ struct DwParams {
     int32_t n_wg;           // slices (= workgroups of the product)
     int32_t xcd_blocked;    // neighbouring slices on one XCD (else slice = workgroup index)
     int32_t teams;          // team slicing (per group) instead of slices of the iteration space
+    int32_t narrow;         // narrow output tiles, one whole tile per workgroup (no partial sums)
     int64_t iters;          // total (output tile, chunk) iterations, a multiple of kRound
     float *part;            // [2 * n_wg] partial tiles of kSlotFloats
     int32_t part_rows;      // partial tiles row-major (1) or in MFMA fragment order (0)
@@ -344,8 +353,20 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 //
 // kKeep: the cache policy of the launch's X copies, when every group has the
 // same (0 non-temporal, 1 cached), or 2: each group's own (a branch per copy).
-template <int kKeep>
+//
+// kNarrow: output tile = (M-block, 128 columns), a chunk is 128 tokens, and
+// every workgroup takes one whole tile (never a partial slot).  The two waves
+// of a packed tile then split each chunk's tokens (64 each) rather than its
+// columns, so each loads only its own half of the operand; at the end they
+// add their sums through LDS and store the tile straight into dW_act.  Odd
+// workgroups start halfway along the token axis and wrap (two segments of the
+// one tile), so that the launch reads two token ranges at a time.
+template <int kKeep, int kNarrow>
 __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
+    constexpr int BN = kNarrow ? kBNn : kBN;   // columns per output tile
+    constexpr int BK = kNarrow ? kBKn : kBK;   // tokens per chunk
+    constexpr int kRowLanes = BN / 8;          // 16-byte column groups (lanes) per X row
+    constexpr int kCopyRows = 64 / kRowLanes;  // X rows per wave copy
     __shared__ int32_t codes[kMaxSegs][kMaxTiles * 32];
     __shared__ DwGroupDev gs[kMaxGroups];   // the group table, indexable at run time
     __shared__ float *outp[kMaxMats];
@@ -443,6 +464,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             j += sg.len;
             it = end;
         }
+        if constexpr (kNarrow) {
+            // odd workgroups: the second half of the tile's token axis first
+            if ((v & 1) && n == 1 && segs[0].len >= 2 * kRound) {
+                Seg a = segs[0], b = segs[0];
+                const int32_t h = (a.len / kRound / 2) * kRound;
+                a.k0 = h;
+                a.len = b.len - h;
+                b.k0 = 0;
+                b.j0 = a.len;
+                b.len = h;
+                if (lane == 0) {
+                    segs[0] = a;
+                    segs[1] = b;
+                }
+                n = 2;
+            }
+        }
         if (lane == 0) s_nseg = n;
     }
     __syncthreads();
@@ -451,11 +489,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int32_t J = segs[nseg - 1].j0 + segs[nseg - 1].len;
     float *const sink = p.sink + (v * 8 + wave) * 16;
 
-    // ---- X copies.  A chunk is 64 token rows x 256 columns (512 bytes a
-    // row); copy k (k = 0..3) of a wave holds rows 2q, 2q+1, q = wave + 8k.
-    // Lane slot l%32 of row 2q + l/32 holds the 16-byte column group
-    // (l%32) ^ 2*(row%4) (a swizzle that makes the transposing reads of 4
-    // consecutive rows hit distinct banks).  The buffer resource's base
+    // ---- X copies.  A chunk is BK token rows x BN columns (64 x 256, 512
+    // bytes a row; narrow 128 x 128, 256 bytes a row); copy k (k = 0..3) of a
+    // wave holds the kCopyRows rows from kCopyRows*q, q = wave + 8k.  Lane slot
+    // l%kRowLanes of row kCopyRows*q + l/kRowLanes holds the 16-byte column
+    // group (l%kRowLanes) ^ 2*(row%4) (a swizzle that makes the transposing
+    // reads of 4 consecutive rows hit distinct banks).  The buffer resource's base
     // advances by one chunk per chunk (scalar work); rows past T fall beyond
     // its size and columns past C get an offset beyond any size, so the range
     // check turns them into zeros.
@@ -470,17 +509,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     auto describe_x = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
-        const int64_t C = G.C, c0 = static_cast<int64_t>(S.nb) * kBN, r0 = static_cast<int64_t>(S.k0) * kBK;
+        const int64_t C = G.C, c0 = static_cast<int64_t>(S.nb) * BN, r0 = static_cast<int64_t>(S.k0) * BK;
         x_base = reinterpret_cast<const uint8_t *>(uniform64(reinterpret_cast<uint64_t>(G.X + r0 * C + c0)));
         x_rem = static_cast<int64_t>(uniform64(static_cast<uint64_t>((G.T - r0) * C * 2 - c0 * 2)));
-        x_stride = static_cast<int64_t>(uniform64(static_cast<uint64_t>(kBK * C * 2)));
+        x_stride = static_cast<int64_t>(uniform64(static_cast<uint64_t>(BK * C * 2)));
         x_j0 = __builtin_amdgcn_readfirstlane(S.j0);
         x_next = __builtin_amdgcn_readfirstlane(sg + 1 < nseg ? segs[sg + 1].j0 : J);
         if constexpr (kKeep == 2) x_keep = __builtin_amdgcn_readfirstlane(G.keep_x) != 0;
 #pragma unroll
         for (int k = 0; k < kCopiesX; ++k) {
-            const int row_in = 2 * (wave + 8 * k) + (lane >> 5);
-            const int grp = (lane & 31) ^ (2 * (row_in & 3));
+            const int row_in = kCopyRows * (wave + 8 * k) + lane / kRowLanes;
+            const int grp = (lane % kRowLanes) ^ (2 * (row_in & 3));
             x_voff[k] = (c0 + 8 * grp < C) ? static_cast<uint32_t>((row_in * C + 8 * grp) * 2) : kOutside;
         }
     };
@@ -503,12 +542,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     };
 
     // ---- wave layout: wave w takes packed tile w/2 of the M-block and the
-    // column half w%2 (four 32-column blocks); waves past the M-block's tiles
-    // only copy.
+    // column half w%2 (four 32-column blocks); narrow: all four column blocks
+    // of the tile and the token half w%2 of each chunk.  Waves past the
+    // M-block's tiles only copy.
     const int tw = wave >> 1, ch = wave & 1;
 
-    // ---- dY operand: 4 KB per (packed tile, chunk); k-step kk is the 1 KB
-    // at 512*kk elements, lane l's 16 bytes at 8*l.  Loads go through a buffer
+    // ---- dY operand: 4 KB per (packed tile, 64 tokens); k-step kk is the
+    // 1 KB at 512*kk elements, lane l's 16 bytes at 8*l.  A narrow chunk's
+    // wave loads the 4 KB of its token half.  Loads go through a buffer
     // resource whose size is 0 for waves without a tile and for chunks past
     // the slice: the load is still issued (every wave issues the same memory
     // instructions every chunk) but touches no memory.
@@ -522,7 +563,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         a_next = __builtin_amdgcn_readfirstlane(sg + 1 < nseg ? segs[sg + 1].j0 : J);
         a_live = tw < S.mt;
         a_base = reinterpret_cast<const uint16_t *>(uniform64(reinterpret_cast<uint64_t>(
-            G.at + (static_cast<int64_t>(S.p0 + (a_live ? tw : 0)) * (G.Tp / 8) + 8 * static_cast<int64_t>(S.k0)) * 256)));
+            G.at + (static_cast<int64_t>(S.p0 + (a_live ? tw : 0)) * (G.Tp / 8) + (BK / 8) * static_cast<int64_t>(S.k0)) * 256 +
+            (kNarrow ? 2048 * ch : 0))));
         a_j0 = __builtin_amdgcn_readfirstlane(S.j0);
     };
     auto issue_a = [&](int32_t ja, bf16x8 (&buf)[4]) __attribute__((always_inline)) {
@@ -531,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             describe_a(sa);
         }
         const bool live = a_live && ja < J;
-        const uint16_t *base = a_base + (live ? static_cast<int64_t>(ja - a_j0) * 2048 : 0);
+        const uint16_t *base = a_base + (live ? static_cast<int64_t>(ja - a_j0) * (BK / 8) * 256 : 0);
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(base), static_cast<short>(0), live ? 4096 : 0, 0x00020000);
 #pragma unroll
@@ -549,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     int xo[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int cb = 4 * ch + c;
+        const int cb = kNarrow ? c : 4 * ch + c;
         xo[c] = 8 * ((4 * cb + (xcp >> 3)) ^ (2 * (s16 >> 2))) + (xcp & 7);
     }
 
@@ -585,11 +627,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         advance_x(jx);
         const __amdgpu_buffer_rsrc_t xr = x_rsrc(jx);
         auto bfrag = [&](int kk, bf16x8 (&b)[4]) __attribute__((always_inline)) {
-            const int r0 = 16 * kk + trow;
+            const int r0 = (kNarrow ? 64 * ch : 0) + 16 * kk + trow;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const short4v lo = lds_tr16(X + r0 * kBN + xo[c]);
-                const short4v hi = lds_tr16(X + (r0 + 4) * kBN + xo[c]);
+                const short4v lo = lds_tr16(X + r0 * BN + xo[c]);
+                const short4v hi = lds_tr16(X + (r0 + 4) * BN + xo[c]);
                 b[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         };
@@ -656,6 +698,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
             for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
     };
 
+    // Narrow epilogue (the workgroup's one tile): waves 2t and 2t+1 summed
+    // tile t over the two token halves of every chunk.  Once every copy has
+    // landed the X ring is free: each wave leaves its 32 x 128 partial there
+    // row-major (16 KB; the 16-byte groups of row r swizzled by r%16, so that
+    // the writes of a fragment and the reads of a row hit distinct banks), and
+    // after a barrier wave 2t+h adds the two partials of rows 16h..16h+15 and
+    // stores them two rows (1 KB) an instruction.  Two addends: the sum does
+    // not depend on which wave adds.
+    auto epilogue_narrow = [&](int sg) __attribute__((always_inline)) {
+        const Seg &S = segs[sg];
+        const DwGroupDev &G = gs[S.g];
+        SFT_WAIT_VMCNT(0);
+        __syncthreads();
+        auto region = [&](int w) __attribute__((always_inline)) {
+            uint8_t *st = w < 2 ? xstage<0>() : w < 4 ? xstage<1>() : w < 6 ? xstage<2>() : xstage<3>();
+            return reinterpret_cast<float *>(st) + (w & 1) * (32 * kBNn);
+        };
+        {
+            float *const mine = region(wave);
+            const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int g = 8 * c + 2 * a + h;
+                    *reinterpret_cast<f32x4 *>(mine + r * kBNn + 4 * (g ^ (r & 15))) =
+                        f32x4{acc[c][4 * a], acc[c][4 * a + 1], acc[c][4 * a + 2], acc[c][4 * a + 3]};
+                }
+        }
+        __syncthreads();
+        const float *const p0 = region(2 * tw), *const p1 = region(2 * tw + 1);
+        const int64_t c0 = static_cast<int64_t>(S.nb) * BN;
+        const int g = lane & 31;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * ch + 2 * i + (lane >> 5);
+            const int o = r * kBNn + 4 * (g ^ (r & 15));
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(p0 + o);
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(p1 + o);
+            const int32_t code = tw < S.mt ? codes[sg][tw * 32 + r] : -1;
+            if (code >= 0 && c0 + 4 * g < G.C) {
+                float *dst = outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C + c0 + 4 * g;
+                *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(reinterpret_cast<uintptr_t>(dst)) = x + y;
+            }
+        }
+    };
+
     // ---- the output map of the slice's first four segments (thread t: entry
     // t%128 of segment t/128), loaded ahead of the prologue so that the wait
     // for it covers these loads only; written to LDS behind the prologue, and
@@ -711,8 +800,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         for (int32_t jq = j0 + kRound; jq < j0 + len; jq += kRound) round4(jq, active, 0);
         epilogue(sg);
     };
-    segment(0, ic<1>{});
-    for (int sg = 1; sg < nseg; ++sg) segment(sg, ic<0>{});
+    if constexpr (kNarrow) {
+        // one tile (the host plans narrow launches that way), in one or two
+        // segments
+        const bool active = tw < segs[0].mt;
+        round4(0, active, 0);
+        for (int32_t jq = kRound; jq < J; jq += kRound) round4(jq, active, 0);
+        epilogue_narrow(0);
+        return;
+    } else {
+        segment(0, ic<1>{});
+        for (int sg = 1; sg < nseg; ++sg) segment(sg, ic<0>{});
+    }
     // Copies past the slice are still in flight (they write zeros to LDS):
     // drain them before the workgroup's LDS can be handed to another (the
     // last epilogue's stores, issued after them, may stay in flight).
@@ -972,6 +1071,35 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         int32_t nm = 0, ptiles = 0;
         int64_t iters = 0, otiles = 0, min_chunks = INT64_MAX;
         size_t at = 0;
+        // Output-tile geometry of the launch's groups: wide (256 columns,
+        // 64-token chunks) or narrow (128 columns, 128-token chunks).
+        auto lay = [&](bool narrow) {
+            const int64_t bn = narrow ? kBNn : kBN, bk = narrow ? kBKn : kBK;
+            iters = otiles = 0;
+            min_chunks = INT64_MAX;
+            at = 0;
+            L.at_off.clear();
+            L.map_off.clear();
+            L.gather_blocks = 0;
+            for (int32_t g = 0; g < p.n_groups; ++g) {
+                DwGroupDev &d = p.g[g];
+                d.n_nblk = static_cast<int32_t>((d.C + bn - 1) / bn);
+                d.chunks = static_cast<int32_t>(((d.T + kRound * bk - 1) / (kRound * bk)) * kRound);
+                d.Tp = static_cast<int32_t>(d.chunks * bk);
+                d.it_begin = iters;
+                d.otile_begin = otiles;
+                const int64_t ot = int64_t(d.n_mblk) * d.n_nblk;
+                otiles += ot;
+                iters += ot * d.chunks;
+                min_chunks = std::min<int64_t>(min_chunks, d.chunks);
+                L.at_off.push_back(at);
+                at += round256(size_t(d.n_ptiles) * 32 * size_t(d.Tp) * 2);
+                L.map_off.push_back(at);
+                at += round256(size_t(d.n_ptiles) * 32 * 4);
+                L.gather_blocks = std::max(L.gather_blocks, d.Tp / kGatherTokens);
+            }
+            p.narrow = narrow ? 1 : 0;
+        };
         while (gi < n_groups && p.n_groups < kMaxGroups) {
             const sft_dw_group &g = groups[gi];
             if (!group_live(g)) {
@@ -1008,25 +1136,12 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             d.n_rows = static_cast<int32_t>(rows);
             d.n_ptiles = static_cast<int32_t>((rows + 31) / 32);
             d.n_mblk = (d.n_ptiles + kMaxTiles - 1) / kMaxTiles;
-            d.n_nblk = static_cast<int32_t>((g.C + kBN - 1) / kBN);
             d.nb_major = d.n_mblk >= 3 ? 1 : 0;
-            d.chunks = static_cast<int32_t>(((g.T + kRound * kBK - 1) / (kRound * kBK)) * kRound);
-            d.Tp = d.chunks * kBK;
             d.ptile_begin = ptiles;
             ptiles += d.n_ptiles;
-            d.it_begin = iters;
-            d.otile_begin = otiles;
-            const int64_t ot = int64_t(d.n_mblk) * d.n_nblk;
-            otiles += ot;
-            iters += ot * d.chunks;
-            min_chunks = std::min<int64_t>(min_chunks, d.chunks);
-            L.at_off.push_back(at);
-            at += round256(size_t(d.n_ptiles) * 32 * size_t(d.Tp) * 2);
-            L.map_off.push_back(at);
-            at += round256(size_t(d.n_ptiles) * 32 * 4);
-            L.gather_blocks = std::max(L.gather_blocks, d.Tp / kGatherTokens);
         }
         if (p.n_groups == 0) break;
+        lay(false);
         if (iters >= (int64_t(1) << 31)) {
             plan.too_big = true;
             break;
@@ -1088,10 +1203,32 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         p.teams = teams ? 1 : 0;
         for (int32_t g = 0; g < p.n_groups; ++g)
             p.g[g].keep_x = teams ? (p.g[g].n_mblk >= 2) : p.g[g].nb_major;
+        // Narrow tiles when one workgroup per narrow tile keeps at least half
+        // of the CUs busy: each workgroup then takes one whole tile over the
+        // whole token axis, with no partial sums and no fix-up (the tile
+        // halves of the wide shape leave every tile in two partial slots, 16
+        // bytes per element written and read again, where narrow tiles write
+        // the 4-byte result once; at 0.5% rows, 182 narrow tiles measured
+        // faster than stream-K over all 256 CUs).  Every tile must have the
+        // same rounds.
+        if (!teams) {
+            int64_t n_ot = 0;
+            bool same = true;
+            for (int32_t g = 0; g < p.n_groups; ++g) {
+                const DwGroupDev &d = p.g[g];
+                n_ot += int64_t(d.n_mblk) * ((d.C + kBNn - 1) / kBNn);
+                same = same && (d.T + kRound * kBKn - 1) / (kRound * kBKn) ==
+                                   (p.g[0].T + kRound * kBKn - 1) / (kRound * kBKn);
+            }
+            if (same && n_ot <= cus && 2 * n_ot >= int64_t(cus)) {
+                lay(true);
+                P = otiles;
+            }
+        }
         int64_t rt = p.g[0].chunks / kRound;
         for (int32_t g = 1; g < p.n_groups; ++g)
             if (p.g[g].chunks / kRound != rt) rt = 0;
-        for (int64_t f = rt; f >= 1 && !teams; --f) {
+        for (int64_t f = rt; f >= 1 && !teams && !p.narrow; --f) {
             if (rt % f || f * otiles > cus) continue;
             if (4 * f * otiles >= 3 * int64_t(cus)) P = f * otiles;
             break;
@@ -1113,7 +1250,8 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         L.out_tiles = otiles;
         L.gather_tiles = ptiles;
         L.at_bytes = at;
-        plan.part_bytes = std::max(plan.part_bytes, round256(size_t(2 * P) * size_t(kSlotFloats) * sizeof(float)));
+        if (!p.narrow)
+            plan.part_bytes = std::max(plan.part_bytes, round256(size_t(2 * P) * size_t(kSlotFloats) * sizeof(float)));
         plan.sink_bytes = std::max(plan.sink_bytes, round256(size_t(P) * 8 * 16 * sizeof(float)));
         plan.at_bytes = std::max(plan.at_bytes, at);
         plan.launches.push_back(L);
@@ -1130,9 +1268,15 @@ void launch_product(const DwParams &p, hipStream_t st) {
         all = all && p.g[g].keep_x;
     }
     const dim3 grid(static_cast<uint32_t>(p.n_wg)), block(kThreads);
-    if (!any) hipLaunchKernelGGL(k_masked_dw<0>, grid, block, 0, st, p);
-    else if (all) hipLaunchKernelGGL(k_masked_dw<1>, grid, block, 0, st, p);
-    else hipLaunchKernelGGL(k_masked_dw<2>, grid, block, 0, st, p);
+    if (p.narrow) {
+        if (!any) hipLaunchKernelGGL((k_masked_dw<0, 1>), grid, block, 0, st, p);
+        else if (all) hipLaunchKernelGGL((k_masked_dw<1, 1>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_masked_dw<2, 1>), grid, block, 0, st, p);
+    } else {
+        if (!any) hipLaunchKernelGGL((k_masked_dw<0, 0>), grid, block, 0, st, p);
+        else if (all) hipLaunchKernelGGL((k_masked_dw<1, 0>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_masked_dw<2, 0>), grid, block, 0, st, p);
+    }
 }
 
 void bind_workspace(Plan &plan, void *ws) {
@@ -1166,8 +1310,9 @@ int num_cus() {
 }
 
 int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream,
-                       DwRowSrc *src, bool *done) {
+                       DwRowSrc *src, bool *done, bool *whole) {
     *done = false;
+    *whole = false;
     if (int rc = validate(groups, n_groups)) return rc;
     Plan plan = make_plan(groups, n_groups);
     SFT_CHECK(!plan.too_big, SFT_ENOTSUP, "sft_masked_dw: a launch beyond 2^31 (tile, chunk) iterations");
@@ -1222,6 +1367,7 @@ int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, s
     e = hipGetLastError();
     SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
     *done = true;
+    *whole = L.p.narrow != 0;
     return SFT_OK;
 }
 
@@ -1259,6 +1405,7 @@ int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t
         launch_product(L.p, st);
         e = hipGetLastError();
         SFT_CHECK(e == hipSuccess, SFT_EHIP, "sft_masked_dw: launch failed: %s", hipGetErrorString(e));
+        if (L.p.narrow) continue;   // whole tiles only: nothing to add up
         hipLaunchKernelGGL(k_dw_fixup, dim3(static_cast<uint32_t>(L.out_tiles), kMaxTiles), dim3(256), 0, st,
                            L.p);
         e = hipGetLastError();

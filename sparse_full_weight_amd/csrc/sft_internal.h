@@ -45,9 +45,10 @@ struct DwRowSrc {
 // Gather and product of sft_masked_dw without the fix-up, partial tiles
 // row-major; src[i] describes the i-th matrix of the groups in order (part
 // null for matrices with no active row).  Sets *done = false and launches
-// nothing when the call needs more than one launch.
+// nothing when the call needs more than one launch.  Sets *whole when the
+// launch wrote every tile whole into dW_act (no partial sums to add).
 int masked_dw_partials(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream,
-                       DwRowSrc *src, bool *done);
+                       DwRowSrc *src, bool *done, bool *whole);
 
 }  // namespace sft
 

@@ -1162,12 +1162,14 @@ int sft_masked_dw_update(const sft_dw_group *groups, int32_t n_groups, void *ws,
         }
     }
     std::vector<sft::DwRowSrc> src(static_cast<size_t>(total));
-    bool done = false;
-    if (int rc = sft::masked_dw_partials(groups, n_groups, ws, ws_bytes, stream, src.data(), &done)) return rc;
+    bool done = false, whole = false;
+    if (int rc = sft::masked_dw_partials(groups, n_groups, ws, ws_bytes, stream, src.data(), &done, &whole))
+        return rc;
     if (!done) {   // the product needs more than one launch: the two calls
         if (int rc = sft_masked_dw(groups, n_groups, ws, ws_bytes, stream)) return rc;
         return sft_sparse_update(mats, n_mats, hp, stream);
     }
+    if (whole) return sft_sparse_update(mats, n_mats, hp, stream);   // dW_act holds every row whole
     const AdamDev a = make_adam(*hp);
     std::vector<int32_t> order(static_cast<size_t>(n_mats));
     std::iota(order.begin(), order.end(), 0);

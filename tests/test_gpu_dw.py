@@ -148,14 +148,42 @@ def test_dw_long_token_axis_split(gpu_lib, layout):
 
 
 @LAYOUTS
-def test_dw_tile_aligned_half_slices(gpu_lib, layout):
-    # 100 output tiles of 2 rounds: 200 workgroups each take exactly half a
-    # tile (slices aligned to the tiles)
-    T, R, C = 512, 96, 100 * 256
+def test_dw_tile_aligned_quarter_slices(gpu_lib, layout):
+    # 50 output tiles of 4 rounds: 200 workgroups each take exactly a quarter
+    # of a 256-column tile (slices aligned to the tiles, four partial sums a
+    # tile); the 128-column shape would have 100 tiles, too few for half of
+    # 256 CUs
+    T, R, C = 1024, 96, 50 * 256
     X = synth.normal_bf16((T, C), 1.0, 1601)
     dY = synth.normal_bf16((T, R), 0.01, 1602)
     mask = _mask_rows(R, synth.clustered_rows(R, 40, 1603))
     _check([(X, [(dY, mask)])], repeat=2, layout=layout)
+
+
+@LAYOUTS
+def test_dw_narrow_whole_tiles(gpu_lib, layout):
+    # 200 output tiles of 128 columns (the last one ragged), each one
+    # workgroup's over a ragged token axis (700 of 1024 padded tokens; odd
+    # workgroups start halfway and wrap); three packed tiles, so two of the
+    # eight waves only copy
+    T, R, C = 700, 96, 199 * 128 + 40
+    X = synth.normal_bf16((T, C), 1.0, 1621)
+    dY = synth.normal_bf16((T, R), 0.01, 1622)
+    mask = _mask_rows(R, synth.clustered_rows(R, 70, 1623))
+    _check([(X, [(dY, mask)])], repeat=2, layout=layout)
+
+
+@LAYOUTS
+def test_dw_narrow_tiles_two_groups_exact(gpu_lib, layout):
+    # 128-column tiles over two groups (100 tiles of a 4-tile M-block and 94
+    # of a 1-tile one; 1000 and 600 tokens, one round count) on small
+    # integers: the two token halves' sums add exactly, so the result is the
+    # exact product
+    g1 = (synth.integer_bf16((1000, 100 * 128), -3, 3, 1631),
+          [(synth.integer_bf16((1000, 128), -3, 3, 1632), _mask_rows(128, synth.clustered_rows(128, 100, 1633)))])
+    g2 = (synth.integer_bf16((600, 12000), -3, 3, 1634),
+          [(synth.integer_bf16((600, 64), -3, 3, 1635), _mask_rows(64, synth.clustered_rows(64, 20, 1636)))])
+    _check([g1, g2], exact=True, layout=layout)
 
 
 @LAYOUTS

@@ -97,8 +97,16 @@ def test_fused_wide_and_narrow_rows(gpu_lib):
 
 @LAYOUTS
 def test_fused_tile_aligned_slices(gpu_lib, layout):
-    # 100 output tiles of 2 rounds, each cut in half by the slices
-    case = _case([(512, 100 * 256, [(96, 40)])], 2350)
+    # 50 output tiles of 4 rounds, each cut in quarters by the slices (too few
+    # 128-column tiles for the whole-tile shape)
+    case = _case([(1024, 50 * 256, [(96, 40)])], 2350)
+    _check_equal(case, layout)
+
+
+@LAYOUTS
+def test_fused_narrow_whole_tiles(gpu_lib, layout):
+    # 200 whole 128-column tiles: no partial sums, the update reads dW_act
+    case = _case([(700, 199 * 128 + 40, [(96, 70)])], 2360)
     _check_equal(case, layout)
 
 
