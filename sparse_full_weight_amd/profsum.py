@@ -93,7 +93,8 @@ def stats(path: str, cmd: str) -> str:
                    f"{float(r['MaxNs']) / 1e3:9.2f}")
         if kernel_of(r["Name"], DW_KERNELS):
             dw_sum += avg
-    out += ["", f"sft_masked_dw call (k_dw_gather + k_masked_dw + k_dw_fixup), sum of averages: {dw_sum:.2f} us"]
+    out += ["", f"sft_masked_dw call (k_dw_gather + k_masked_dw, + k_dw_fixup where it ran), "
+                f"sum of averages: {dw_sum:.2f} us"]
     return "\n".join(out) + "\n"
 
 
