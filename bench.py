@@ -1086,6 +1086,20 @@ def main():
     traffic = None
     if rec and rec.get("sft_dw_sha256") == profsum.source_hash("sft_dw.hip"):
         traffic = rec["masked_dw_call_bytes"]
+    # HBM bytes a step touches (the dW call and the update kernel the step
+    # ran, from the same counters; both sources unchanged since), against the
+    # step time
+    step_traffic = None
+    if (traffic is not None and rec.get("sft_update_sha256") == profsum.source_hash("sft_update.hip")
+            and not args.unfused):
+        ks = rec["kernels"]
+        # split tiles (a fix-up ran) make the step's update the fused kernel
+        upd = "k_fused_update" if "k_dw_fixup" in ks else "k_sparse_update"
+        if upd in ks:
+            b = traffic + ks[upd]["read_bytes"] + ks[upd]["write_bytes"]
+            gbs = b / (ms_per_step * 1e-3) / 1e9
+            step_traffic = {"bytes": b, "update_kernel": upd, "GB_s": round(gbs, 1),
+                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     print("[bench] timing the a1 host calls", file=sys.stderr, flush=True)
     host_plan = host_plan_us(args.density)
@@ -1137,6 +1151,7 @@ def main():
                    "step_stats_one_stream": _stats(per_one),
                    "ms_per_step_one_stream_plan_resident": round(ms_one_res, 5),
                    "step_GB_s": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "step_traffic": step_traffic,
                    "hbm_roofline_ms": round((dw.bytes + up.bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 5)},
         "roofline": {"bound": "hbm", "kernel": ("sft_masked_dw (k_dw_gather + k_masked_dw, + k_dw_fixup where the "
                                                 "launch splits tiles; the 1% layer's narrow tiles split none)"),
