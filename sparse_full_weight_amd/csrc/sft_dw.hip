@@ -31,7 +31,9 @@
 //      (output tile, chunk) iteration space; or, where the tiles line up with
 //      the CUs, tile-aligned slices, team slices (groups of three or more
 //      M-blocks), or narrow whole tiles (128 columns x 128-token chunks, one
-//      tile per workgroup, no partial sums at all).
+//      tile per workgroup, no partial sums at all; a group of 5 to 8 packed
+//      tiles there takes 64-column tiles with one wave per packed tile, all
+//      its tiles in one M-block).
 //   3. Fix-up.  Output tiles cut by slice boundaries leave partial sums in
 //      scratch; this kernel adds them in slice order (deterministic; the
 //      kernel boundary orders the stores, so no device-scope fence is needed
@@ -60,6 +62,11 @@ constexpr int kBK = 64;              // tokens per chunk: 4 MFMA k-steps of 16
 // 128 columns, chunks of 128 tokens (the same 32 KB of X a chunk).
 constexpr int kBNn = 128, kBKn = 128;
 static_assert(kBK * kBN == kBKn * kBNn, "one X stage size for both tile shapes");
+// Narrow tiles of one wave per packed tile (a group of 5 to 8 packed tiles in
+// a narrow launch): 64 columns, the same 128-token chunks (16 KB of X a
+// chunk), all of the group's packed tiles in one M-block, so its X is read
+// once.
+constexpr int kBNw = 64, kMaxTilesW = 8;
 constexpr int kRound = 4;            // chunks per pipeline round (segments are whole rounds)
 constexpr int kThreads = 512;        // 8 waves
 constexpr int kXStages = 4;          // X ring depth
@@ -110,6 +117,7 @@ struct DwGroupDev {
     int32_t keep_x;         // X copies allocate in L2 (other M-blocks read the same X soon)
     int32_t wg_begin;       // team slicing: first slice of the group's teams
     int32_t n_team;         // team slicing: teams of n_mblk slices each
+    int32_t wt;             // narrow launch, one wave per packed tile: 64-column tiles, M-blocks of up to 8 tiles
     int64_t it_begin;       // first global iteration of this group
     int64_t otile_begin;    // first output tile (launch numbering)
 };
@@ -361,18 +369,24 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 // add their sums through LDS and store the tile straight into dW_act.  Odd
 // workgroups start halfway along the token axis and wrap (two segments of the
 // one tile), so that the launch reads two token ranges at a time.
+//
+// kWt (narrow launches only, chosen per workgroup by its group's wt flag):
+// output tile = (M-block of up to 8 packed tiles, 64 columns), a chunk is 128
+// tokens; wave w takes packed tile w over the whole chunk (all 128 tokens,
+// both 32-column blocks) and stores its 32 x 64 sums straight into dW_act.
+// Against two M-blocks of 128-column tiles this reads the group's X once.
+__shared__ int32_t codes[kMaxSegs][kMaxTiles * 32];
+__shared__ DwGroupDev gs[kMaxGroups];   // the group table, indexable at run time
+__shared__ float *outp[kMaxMats];
+__shared__ Seg segs[kMaxSegs];
+__shared__ int32_t s_nseg;
+static_assert(kMaxTilesW * 32 <= kMaxSegs * kMaxTiles * 32, "output map of an 8-tile M-block");
+
+template <int kKeep, int kNarrow, int kWt>
+__device__ __forceinline__ void masked_dw_body(const DwParams &p, const int64_t v, const int nseg);
+
 template <int kKeep, int kNarrow>
 __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
-    constexpr int BN = kNarrow ? kBNn : kBN;   // columns per output tile
-    constexpr int BK = kNarrow ? kBKn : kBK;   // tokens per chunk
-    constexpr int kRowLanes = BN / 8;          // 16-byte column groups (lanes) per X row
-    constexpr int kCopyRows = 64 / kRowLanes;  // X rows per wave copy
-    __shared__ int32_t codes[kMaxSegs][kMaxTiles * 32];
-    __shared__ DwGroupDev gs[kMaxGroups];   // the group table, indexable at run time
-    __shared__ float *outp[kMaxMats];
-    __shared__ Seg segs[kMaxSegs];
-    __shared__ int32_t s_nseg;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
@@ -486,6 +500,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     __syncthreads();
     const int nseg = s_nseg;
     if (nseg == 0) return;   // an idle slice (team slicing pads the grid to whole XCDs)
+    if constexpr (kNarrow) {
+        if (__builtin_amdgcn_readfirstlane(gs[segs[0].g].wt)) masked_dw_body<kKeep, 1, 1>(p, v, nseg);
+        else masked_dw_body<kKeep, 1, 0>(p, v, nseg);
+    } else {
+        masked_dw_body<kKeep, 0, 0>(p, v, nseg);
+    }
+}
+
+template <int kKeep, int kNarrow, int kWt>
+__device__ __forceinline__ void masked_dw_body(const DwParams &p, const int64_t v, const int nseg) {
+    static_assert(!kWt || kNarrow, "one wave per tile only in narrow launches");
+    constexpr int BN = kWt ? kBNw : kNarrow ? kBNn : kBN;   // columns per output tile
+    constexpr int BK = kNarrow ? kBKn : kBK;                // tokens per chunk
+    constexpr int kRowLanes = BN / 8;          // 16-byte column groups (lanes) per X row
+    constexpr int kCopyRows = 64 / kRowLanes;  // X rows per wave copy
+    // per wave and chunk: operand loads (1 KB each), X copies (1 KB each),
+    // 32-column blocks and 16-token k-steps
+    constexpr int LA = kWt ? 8 : kLoadsA, CX = kWt ? 2 : kCopiesX, NC = kWt ? 2 : 4, KS = kWt ? 8 : 4;
+    static_assert(CX * 8 * 1024 == BK * BN * 2 && KS % CX == 0, "a chunk's X is its waves' copies");
+    constexpr int IF = (kXAhead - 1) * (LA + CX);   // loads in flight while chunk j is consumed
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int32_t J = segs[nseg - 1].j0 + segs[nseg - 1].len;
     float *const sink = p.sink + (v * 8 + wave) * 16;
 
@@ -505,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     int64_t x_rem = 0, x_stride = 0;
     int32_t x_j0 = 0, x_next = 0;
     bool x_keep = kKeep == 1;
-    uint32_t x_voff[kCopiesX];
+    uint32_t x_voff[CX];
     auto describe_x = [&](int sg) __attribute__((always_inline)) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
@@ -517,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         x_next = __builtin_amdgcn_readfirstlane(sg + 1 < nseg ? segs[sg + 1].j0 : J);
         if constexpr (kKeep == 2) x_keep = __builtin_amdgcn_readfirstlane(G.keep_x) != 0;
 #pragma unroll
-        for (int k = 0; k < kCopiesX; ++k) {
+        for (int k = 0; k < CX; ++k) {
             const int row_in = kCopyRows * (wave + 8 * k) + lane / kRowLanes;
             const int grp = (lane % kRowLanes) ^ (2 * (row_in & 3));
             x_voff[k] = (c0 + 8 * grp < C) ? static_cast<uint32_t>((row_in * C + 8 * grp) * 2) : kOutside;
@@ -545,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // column half w%2 (four 32-column blocks); narrow: all four column blocks
     // of the tile and the token half w%2 of each chunk.  Waves past the
     // M-block's tiles only copy.
-    const int tw = wave >> 1, ch = wave & 1;
+    const int tw = kWt ? wave : wave >> 1, ch = kWt ? 0 : wave & 1;
 
     // ---- dY operand: 4 KB per (packed tile, 64 tokens); k-step kk is the
     // 1 KB at 512*kk elements, lane l's 16 bytes at 8*l.  A narrow chunk's
@@ -564,10 +601,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         a_live = tw < S.mt;
         a_base = reinterpret_cast<const uint16_t *>(uniform64(reinterpret_cast<uint64_t>(
             G.at + (static_cast<int64_t>(S.p0 + (a_live ? tw : 0)) * (G.Tp / 8) + (BK / 8) * static_cast<int64_t>(S.k0)) * 256 +
-            (kNarrow ? 2048 * ch : 0))));
+            (kNarrow && !kWt ? 2048 * ch : 0))));
         a_j0 = __builtin_amdgcn_readfirstlane(S.j0);
     };
-    auto issue_a = [&](int32_t ja, bf16x8 (&buf)[4]) __attribute__((always_inline)) {
+    auto issue_a = [&](int32_t ja, bf16x8 (&buf)[LA]) __attribute__((always_inline)) {
         if (ja >= a_next && ja < J) {
             ++sa;
             describe_a(sa);
@@ -575,9 +612,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         const bool live = a_live && ja < J;
         const uint16_t *base = a_base + (live ? static_cast<int64_t>(ja - a_j0) * (BK / 8) * 256 : 0);
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(base), static_cast<short>(0), live ? 4096 : 0, 0x00020000);
+            const_cast<uint16_t *>(base), static_cast<short>(0), live ? 1024 * LA : 0, 0x00020000);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < LA; ++kk)
             buf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane + 1024 * kk, 0, 0));
     };
 
@@ -588,9 +625,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int s16 = lane & 15;
     const int trow = 8 * (lane >> 5) + (s16 >> 2);
     const int xcp = ((lane >> 4) & 1) * 16 + 4 * (s16 & 3);   // column inside a 32-column block
-    int xo[4];
+    int xo[NC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int cb = kNarrow ? c : 4 * ch + c;
         xo[c] = 8 * ((4 * cb + (xcp >> 3)) ^ (2 * (s16 >> 2))) + (xcp & 7);
     }
@@ -599,26 +636,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // block, so lane l register r holds column 8*(r/4) + 4*(l/32) + r%4 of the
     // block for packed row l%32: four consecutive columns per register quad,
     // stored as one float4.
-    floatx16 acc[4];
+    floatx16 acc[NC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
     auto wait_vm = [](int n) __attribute__((always_inline)) {
-        if (n == kInFlight) SFT_WAIT_VMCNT(kInFlight);
-        else SFT_WAIT_VMCNT(kInFlight + kEpiStores);
+        if (n == IF) SFT_WAIT_VMCNT(IF);
+        else SFT_WAIT_VMCNT(IF + kEpiStores);
     };
 
     // One chunk, u = jj mod 4 (a constant): reads stage u and A buffer u; the
     // operand loads and copies of chunk jj+3 go to buffer (u+3)%4 and stage
     // (u+3)%4 (chunk jj-1's), one copy after each k-step.
-    bf16x8 ab[kAAhead + 1][4];
+    bf16x8 ab[kAAhead + 1][LA];
     auto step = [&](auto u_tag, int32_t jj, int n_wait, bool active) __attribute__((always_inline)) {
         constexpr int U = decltype(u_tag)::value;
         const uint16_t *X = reinterpret_cast<const uint16_t *>(xstage<U>());
         uint8_t *st_dma = xstage<(U + kXAhead) % kXStages>();
-        const bf16x8 (&a)[4] = ab[U % (kAAhead + 1)];
+        const bf16x8 (&a)[LA] = ab[U % (kAAhead + 1)];
         SFT_WAIT_LGKM0();
         wait_vm(n_wait);
         __builtin_amdgcn_s_barrier();
@@ -626,10 +663,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         const int32_t jx = jj + kXAhead;
         advance_x(jx);
         const __amdgpu_buffer_rsrc_t xr = x_rsrc(jx);
-        auto bfrag = [&](int kk, bf16x8 (&b)[4]) __attribute__((always_inline)) {
-            const int r0 = (kNarrow ? 64 * ch : 0) + 16 * kk + trow;
+        auto bfrag = [&](int kk, bf16x8 (&b)[NC]) __attribute__((always_inline)) {
+            const int r0 = (kNarrow && !kWt ? 64 * ch : 0) + 16 * kk + trow;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 const short4v lo = lds_tr16(X + r0 * BN + xo[c]);
                 const short4v hi = lds_tr16(X + (r0 + 4) * BN + xo[c]);
                 b[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -640,28 +677,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         // exact; they sit between k-steps to overlap the matrix cores.  The
         // fragments alternate between two register sets (k-step kk reads set
         // kk%2 while set (kk+1)%2 fills), with no copies between them.
-        bf16x8 bf[2][4];
+        // Copy k follows k-step k*KS/CX (every k-step; one wave per tile:
+        // k-steps 0 and 4 of 8).
+        bf16x8 bf[2][NC];
         if (active) bfrag(0, bf[0]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KS; ++kk) {
             if (active) {
-                if (kk < 3) bfrag(kk + 1, bf[(kk + 1) & 1]);
+                if (kk < KS - 1) bfrag(kk + 1, bf[(kk + 1) & 1]);
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < NC; ++c)
                     acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[kk & 1][c], a[kk], acc[c], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            issue_x(xr, kk, st_dma);
-            __builtin_amdgcn_sched_barrier(0);
+            if (kk % (KS / CX) == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue_x(xr, kk / (KS / CX), st_dma);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
-    static_assert(kCopiesX == 4 && kRound == kXStages, "one copy per k-step; stages rotate once a round");
+    static_assert(LA == KS && kRound == kXStages, "one operand load per k-step; stages rotate once a round");
     // A round of 4 chunks; the first three wait for `extra` more operations.
     auto round4 = [&](int32_t jq, bool active, int extra) __attribute__((always_inline)) {
-        step(ic<0>{}, jq + 0, kInFlight + extra, active);
-        step(ic<1>{}, jq + 1, kInFlight + extra, active);
-        step(ic<2>{}, jq + 2, kInFlight + extra, active);
-        step(ic<3>{}, jq + 3, kInFlight, active);
+        step(ic<0>{}, jq + 0, IF + extra, active);
+        step(ic<1>{}, jq + 1, IF + extra, active);
+        step(ic<2>{}, jq + 2, IF + extra, active);
+        step(ic<3>{}, jq + 3, IF, active);
     };
 
     // Segment epilogue: every wave issues 16 float4 stores (masked-off lanes
@@ -671,6 +712,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // 16 bytes at 16*l, so each of those stores is one contiguous kilobyte;
     // or, for an update that reads its rows from the slots, row-major.
     auto epilogue = [&](int sg) __attribute__((always_inline)) {
+      if constexpr (!kNarrow) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
         const int h = lane >> 5;
@@ -696,6 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+      }
     };
 
     // Narrow epilogue (the workgroup's one tile): waves 2t and 2t+1 summed
@@ -707,6 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     // stores them two rows (1 KB) an instruction.  Two addends: the sum does
     // not depend on which wave adds.
     auto epilogue_narrow = [&](int sg) __attribute__((always_inline)) {
+      if constexpr (kNarrow && !kWt) {
         const Seg &S = segs[sg];
         const DwGroupDev &G = gs[S.g];
         SFT_WAIT_VMCNT(0);
@@ -743,13 +787,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
                 *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(reinterpret_cast<uintptr_t>(dst)) = x + y;
             }
         }
+      }
+    };
+
+    // One wave per tile: wave w holds packed tile w's 32 x 64 sums over the
+    // whole token axis; each lane stores 4 consecutive columns of its row at
+    // a time (a row's 64 columns in 8 stores of lane pairs) straight into
+    // dW_act.  No wave adds another's sums.
+    auto epilogue_wt = [&](int sg) __attribute__((always_inline)) {
+      if constexpr (kWt) {
+        const Seg &S = segs[sg];
+        const DwGroupDev &G = gs[S.g];
+        SFT_WAIT_VMCNT(0);   // the copies past the slice (zeros into LDS) land before the workgroup ends
+        const int h = lane >> 5;
+        const int32_t code = tw < S.mt ? (&codes[0][0])[tw * 32 + (lane & 31)] : -1;
+        const int64_t c0 = static_cast<int64_t>(S.nb) * BN;
+        if (code >= 0) {
+            float *const row = outp[code >> 24] + static_cast<int64_t>(code & 0xFFFFFF) * G.C;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int64_t col = c0 + 32 * c + 8 * a + 4 * h;
+                    if (col < G.C)
+                        *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(
+                            reinterpret_cast<uintptr_t>(row + col)) =
+                            f32x4{acc[c][4 * a], acc[c][4 * a + 1], acc[c][4 * a + 2], acc[c][4 * a + 3]};
+                }
+        }
+      }
     };
 
     // ---- the output map of the slice's first four segments (thread t: entry
-    // t%128 of segment t/128), loaded ahead of the prologue so that the wait
+    // t%128 of segment t/128; one wave per tile: entry t of the one tile's
+    // map, up to 8 packed tiles), loaded ahead of the prologue so that the wait
     // for it covers these loads only; written to LDS behind the prologue, and
     // read only by epilogues, after the first chunk's barrier.
-    const int csg = tid >> 7, crow = tid & 127;
+    const int csg = kWt ? 0 : tid >> 7, crow = kWt ? tid : tid & 127;
     int32_t cval = -1;
     if (csg < nseg) {
         const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[csg].g);
@@ -770,7 +844,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         advance_x(S);
         const __amdgpu_buffer_rsrc_t xr = x_rsrc(S);
 #pragma unroll
-        for (int k = 0; k < kCopiesX; ++k) issue_x(xr, k, xstage<S>());
+        for (int k = 0; k < CX; ++k) issue_x(xr, k, xstage<S>());
     };
     static_assert(kXAhead == 3, "prologue order");
     prologue(ic<0>{});
@@ -778,8 +852,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     prologue(ic<2>{});
 
     static_assert(kThreads / (kMaxTiles * 32) == 4 && kMaxSegs >= 4, "four segments' output map per pass");
-    codes[csg][crow] = cval;
-    if (nseg > 4) {   // rare: slices across more than four output tiles
+    if constexpr (kWt) {
+        if (tid < kMaxTilesW * 32) (&codes[0][0])[tid] = cval;
+    } else {
+        codes[csg][crow] = cval;
+    }
+    if (!kNarrow && nseg > 4) {   // rare: slices across more than four output tiles
         for (int sg = 4; sg < nseg; ++sg) {
             const int32_t gsg = __builtin_amdgcn_readfirstlane(segs[sg].g);
             const int32_t *map = gs[gsg].rowmap + segs[sg].p0 * 32;
@@ -806,7 +884,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
         const bool active = tw < segs[0].mt;
         round4(0, active, 0);
         for (int32_t jq = kRound; jq < J; jq += kRound) round4(jq, active, 0);
-        epilogue_narrow(0);
+        if constexpr (kWt) epilogue_wt(0);
+        else epilogue_narrow(0);
         return;
     } else {
         segment(0, ic<1>{});
@@ -1060,6 +1139,11 @@ int validate(const sft_dw_group *groups, int32_t n_groups) {
 // Launch decomposition, shared by the workspace query and the launch.
 // Workspace: [partial slots][store sink][gathered operands + row maps of one
 // launch] (launches run in stream order, so they reuse the last region).
+// A group of 5 to 8 packed tiles in a narrow launch takes one M-block of
+// 64-column tiles, one wave per packed tile (its X read once), instead of two
+// M-blocks of 128-column tiles.
+bool wave_tiles(const DwGroupDev &d) { return d.n_ptiles > kMaxTiles && d.n_ptiles <= kMaxTilesW; }
+
 Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
     Plan plan;
     const int cus = sft::num_cus();
@@ -1074,7 +1158,7 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         // Output-tile geometry of the launch's groups: wide (256 columns,
         // 64-token chunks) or narrow (128 columns, 128-token chunks).
         auto lay = [&](bool narrow) {
-            const int64_t bn = narrow ? kBNn : kBN, bk = narrow ? kBKn : kBK;
+            const int64_t bk = narrow ? kBKn : kBK;
             iters = otiles = 0;
             min_chunks = INT64_MAX;
             at = 0;
@@ -1083,6 +1167,9 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             L.gather_blocks = 0;
             for (int32_t g = 0; g < p.n_groups; ++g) {
                 DwGroupDev &d = p.g[g];
+                d.wt = narrow && wave_tiles(d) ? 1 : 0;
+                d.n_mblk = d.wt ? 1 : (d.n_ptiles + kMaxTiles - 1) / kMaxTiles;
+                const int64_t bn = d.wt ? kBNw : narrow ? kBNn : kBN;
                 d.n_nblk = static_cast<int32_t>((d.C + bn - 1) / bn);
                 d.chunks = static_cast<int32_t>(((d.T + kRound * bk - 1) / (kRound * bk)) * kRound);
                 d.Tp = static_cast<int32_t>(d.chunks * bk);
@@ -1216,7 +1303,7 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             bool same = true;
             for (int32_t g = 0; g < p.n_groups; ++g) {
                 const DwGroupDev &d = p.g[g];
-                n_ot += int64_t(d.n_mblk) * ((d.C + kBNn - 1) / kBNn);
+                n_ot += wave_tiles(d) ? (d.C + kBNw - 1) / kBNw : int64_t(d.n_mblk) * ((d.C + kBNn - 1) / kBNn);
                 same = same && (d.T + kRound * kBKn - 1) / (kRound * kBKn) ==
                                    (p.g[0].T + kRound * kBKn - 1) / (kRound * kBKn);
             }

@@ -187,6 +187,36 @@ def test_dw_narrow_tiles_two_groups_exact(gpu_lib, layout):
 
 
 @LAYOUTS
+@pytest.mark.parametrize("n_tiles", [5, 7, 8])
+def test_dw_narrow_wave_per_tile(gpu_lib, layout, n_tiles):
+    # 5-8 packed tiles in a narrow launch: one M-block of 64-column tiles,
+    # one wave per packed tile (151 tiles, the last one ragged; 700 of 1024
+    # padded tokens, odd workgroups start halfway and wrap); rows spread over
+    # exactly n_tiles 32-row tiles, so both layouts take this shape
+    T, R, C = 700, 8 * 32, 150 * 64 + 40
+    rng = np.random.default_rng(1640 + n_tiles)
+    rows = []
+    for t in range(n_tiles):
+        rows += list(32 * t + np.sort(rng.choice(32, 31 if t % 2 else 32, replace=False)))
+    X = synth.normal_bf16((T, C), 1.0, 1641)
+    dY = synth.normal_bf16((T, R), 0.01, 1642)
+    _check([(X, [(dY, _mask_rows(R, rows))])], repeat=2, layout=layout)
+
+
+@LAYOUTS
+def test_dw_narrow_wave_per_tile_beside_narrow_exact(gpu_lib, layout):
+    # the 1% layer's shape in small: a group of 7 packed tiles over two
+    # matrices (64 tiles of 64 columns) beside a 2-tile group (64 tiles of 128
+    # columns) in one narrow launch, on small integers (exact products)
+    g1 = (synth.integer_bf16((1000, 4096), -3, 3, 1651),
+          [(synth.integer_bf16((1000, 128), -3, 3, 1652), _mask_rows(128, list(range(0, 128)))),
+           (synth.integer_bf16((1000, 160), -3, 3, 1653), _mask_rows(160, list(range(0, 90)) + [100, 127]))])
+    g2 = (synth.integer_bf16((600, 8192), -3, 3, 1654),
+          [(synth.integer_bf16((600, 64), -3, 3, 1655), _mask_rows(64, synth.clustered_rows(64, 40, 1656)))])
+    _check([g1, g2], exact=True, layout=layout)
+
+
+@LAYOUTS
 def test_dw_one_tile_per_workgroup(gpu_lib, layout):
     # 200 output tiles of one round: every workgroup computes one whole tile
     # (no partial sums at all)
