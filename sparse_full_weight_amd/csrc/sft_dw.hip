@@ -117,7 +117,8 @@ struct DwGroupDev {
     int32_t keep_x;         // X copies allocate in L2 (other M-blocks read the same X soon)
     int32_t wg_begin;       // team slicing: first slice of the group's teams
     int32_t n_team;         // team slicing: teams of n_mblk slices each
-    int32_t wt;             // narrow launch, one wave per packed tile: 64-column tiles, M-blocks of up to 8 tiles
+    int32_t wt;             // narrow launch, one wave per packed tile and M-blocks of up to 8 tiles: 1: 64-column
+                            // tiles, 2: 128-column tiles (0: two waves per packed tile, M-blocks of up to 4)
     int64_t it_begin;       // first global iteration of this group
     int64_t otile_begin;    // first output tile (launch numbering)
 };
@@ -501,7 +502,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int nseg = s_nseg;
     if (nseg == 0) return;   // an idle slice (team slicing pads the grid to whole XCDs)
     if constexpr (kNarrow) {
-        if (__builtin_amdgcn_readfirstlane(gs[segs[0].g].wt)) masked_dw_body<kKeep, 1, 1>(p, v, nseg);
+        const int32_t wt = __builtin_amdgcn_readfirstlane(gs[segs[0].g].wt);
+        if (wt == 1) masked_dw_body<kKeep, 1, 1>(p, v, nseg);
+        else if (wt == 2) masked_dw_body<kKeep, 1, 2>(p, v, nseg);
         else masked_dw_body<kKeep, 1, 0>(p, v, nseg);
     } else {
         masked_dw_body<kKeep, 0, 0>(p, v, nseg);
@@ -511,13 +514,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
 template <int kKeep, int kNarrow, int kWt>
 __device__ __forceinline__ void masked_dw_body(const DwParams &p, const int64_t v, const int nseg) {
     static_assert(!kWt || kNarrow, "one wave per tile only in narrow launches");
-    constexpr int BN = kWt ? kBNw : kNarrow ? kBNn : kBN;   // columns per output tile
+    constexpr int BN = kWt == 1 ? kBNw : kNarrow ? kBNn : kBN;   // columns per output tile
     constexpr int BK = kNarrow ? kBKn : kBK;                // tokens per chunk
     constexpr int kRowLanes = BN / 8;          // 16-byte column groups (lanes) per X row
     constexpr int kCopyRows = 64 / kRowLanes;  // X rows per wave copy
     // per wave and chunk: operand loads (1 KB each), X copies (1 KB each),
     // 32-column blocks and 16-token k-steps
-    constexpr int LA = kWt ? 8 : kLoadsA, CX = kWt ? 2 : kCopiesX, NC = kWt ? 2 : 4, KS = kWt ? 8 : 4;
+    // (a wide tile's two waves of a packed tile split its columns)
+    constexpr int LA = kWt ? 8 : kLoadsA, CX = BK * BN * 2 / (8 * 1024), NC = kNarrow ? BN / 32 : BN / 64,
+                  KS = kWt ? 8 : 4;
     static_assert(CX * 8 * 1024 == BK * BN * 2 && KS % CX == 0, "a chunk's X is its waves' copies");
     constexpr int IF = (kXAhead - 1) * (LA + CX);   // loads in flight while chunk j is consumed
     const int tid = threadIdx.x;
@@ -1139,10 +1144,47 @@ int validate(const sft_dw_group *groups, int32_t n_groups) {
 // Launch decomposition, shared by the workspace query and the launch.
 // Workspace: [partial slots][store sink][gathered operands + row maps of one
 // launch] (launches run in stream order, so they reuse the last region).
-// A group of 5 to 8 packed tiles in a narrow launch takes one M-block of
-// 64-column tiles, one wave per packed tile (its X read once), instead of two
-// M-blocks of 128-column tiles.
-bool wave_tiles(const DwGroupDev &d) { return d.n_ptiles > kMaxTiles && d.n_ptiles <= kMaxTilesW; }
+// Shapes of a group in a narrow launch (DwGroupDev::wt): 0, M-blocks of up
+// to 4 packed tiles and 128-column tiles, two waves per packed tile; 1 and 2,
+// M-blocks of up to 8 packed tiles, one wave per packed tile, over 64 or 128
+// columns.  Returns the group's output tiles (= workgroups) in that shape.
+int64_t narrow_tiles(const DwGroupDev &d, int wt) {
+    const int64_t mb = wt ? (d.n_ptiles + kMaxTilesW - 1) / kMaxTilesW : (d.n_ptiles + kMaxTiles - 1) / kMaxTiles;
+    const int64_t bn = wt == 1 ? kBNw : kBNn;
+    return mb * ((d.C + bn - 1) / bn);
+}
+
+// Narrow shapes for the launch's groups: groups of up to 4 packed tiles take
+// shape 0, the others shape 1 (their X read once per 8 packed tiles, with as
+// many workgroups as two 4-tile M-blocks of 128 columns); while the tiles
+// outnumber the CUs, the shape-1 group with the most tiles moves to shape 2
+// (half its workgroups, each with twice the columns).  A narrow launch needs
+// every group on the same rounds and between half the CUs and all of them
+// busy; where a group has 3 or more M-blocks of 4 packed tiles (team slicing
+// otherwise), also two rounds of workgroups that keep at least 70% of the
+// CUs busy over both (5% rows: 374 tiles, measured faster than team slices).
+// Returns false if no such assignment exists.
+bool narrow_shapes(const DwParams &p, int cus, int32_t *wt) {
+    int64_t n = 0;
+    bool same = true, many = false;
+    for (int32_t g = 0; g < p.n_groups; ++g) {
+        const DwGroupDev &d = p.g[g];
+        wt[g] = d.n_ptiles > kMaxTiles ? 1 : 0;
+        n += narrow_tiles(d, wt[g]);
+        many = many || d.n_ptiles > (kTeamMblk - 1) * kMaxTiles;
+        same = same && (d.T + kRound * kBKn - 1) / (kRound * kBKn) ==
+                           (p.g[0].T + kRound * kBKn - 1) / (kRound * kBKn);
+    }
+    while (n > cus) {
+        int32_t best = -1;
+        for (int32_t g = 0; g < p.n_groups; ++g)
+            if (wt[g] == 1 && (best < 0 || narrow_tiles(p.g[g], 1) > narrow_tiles(p.g[best], 1))) best = g;
+        if (best < 0) break;
+        n += narrow_tiles(p.g[best], 2) - narrow_tiles(p.g[best], 1);
+        wt[best] = 2;
+    }
+    return same && ((n <= cus && 2 * n >= int64_t(cus)) || (many && n <= 2 * cus && 10 * n >= 14 * int64_t(cus)));
+}
 
 Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
     Plan plan;
@@ -1157,6 +1199,7 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         size_t at = 0;
         // Output-tile geometry of the launch's groups: wide (256 columns,
         // 64-token chunks) or narrow (128 columns, 128-token chunks).
+        int32_t wt_of[kMaxGroups] = {};
         auto lay = [&](bool narrow) {
             const int64_t bk = narrow ? kBKn : kBK;
             iters = otiles = 0;
@@ -1167,9 +1210,10 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
             L.gather_blocks = 0;
             for (int32_t g = 0; g < p.n_groups; ++g) {
                 DwGroupDev &d = p.g[g];
-                d.wt = narrow && wave_tiles(d) ? 1 : 0;
-                d.n_mblk = d.wt ? 1 : (d.n_ptiles + kMaxTiles - 1) / kMaxTiles;
-                const int64_t bn = d.wt ? kBNw : narrow ? kBNn : kBN;
+                d.wt = narrow ? wt_of[g] : 0;
+                d.n_mblk = d.wt ? (d.n_ptiles + kMaxTilesW - 1) / kMaxTilesW : (d.n_ptiles + kMaxTiles - 1) / kMaxTiles;
+                d.nb_major = !narrow && d.n_mblk >= 3 ? 1 : 0;
+                const int64_t bn = d.wt == 1 ? kBNw : narrow ? kBNn : kBN;
                 d.n_nblk = static_cast<int32_t>((d.C + bn - 1) / bn);
                 d.chunks = static_cast<int32_t>(((d.T + kRound * bk - 1) / (kRound * bk)) * kRound);
                 d.Tp = static_cast<int32_t>(d.chunks * bk);
@@ -1256,8 +1300,19 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         // a team is then added, while the CUs last, to the group whose
         // members have the most rounds each (never more teams than rounds).
         int64_t P = 0;
+        // Narrow whole tiles first, when the groups' shapes keep at least half
+        // of the CUs busy with one workgroup per tile: each workgroup then takes
+        // one whole tile over the whole token axis, with no partial sums and no
+        // fix-up (the tile halves of the wide shape leave every tile in two
+        // partial slots, 16 bytes per element written and read again, where
+        // narrow tiles write the 4-byte result once; at 0.5% rows, 182 narrow
+        // tiles measured faster than stream-K over all 256 CUs).
+        if (narrow_shapes(p, cus, wt_of)) {
+            lay(true);
+            P = otiles;
+        }
         bool teams = false;
-        for (int32_t g = 0; g < p.n_groups; ++g) teams = teams || p.g[g].n_mblk >= kTeamMblk;
+        for (int32_t g = 0; g < p.n_groups && !p.narrow; ++g) teams = teams || p.g[g].n_mblk >= kTeamMblk;
         if (teams) {
             int64_t T[kMaxGroups], Qg[kMaxGroups], tot = 0;
             for (int32_t g = 0; g < p.n_groups; ++g) {
@@ -1290,28 +1345,6 @@ Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
         p.teams = teams ? 1 : 0;
         for (int32_t g = 0; g < p.n_groups; ++g)
             p.g[g].keep_x = teams ? (p.g[g].n_mblk >= 2) : p.g[g].nb_major;
-        // Narrow tiles when one workgroup per narrow tile keeps at least half
-        // of the CUs busy: each workgroup then takes one whole tile over the
-        // whole token axis, with no partial sums and no fix-up (the tile
-        // halves of the wide shape leave every tile in two partial slots, 16
-        // bytes per element written and read again, where narrow tiles write
-        // the 4-byte result once; at 0.5% rows, 182 narrow tiles measured
-        // faster than stream-K over all 256 CUs).  Every tile must have the
-        // same rounds.
-        if (!teams) {
-            int64_t n_ot = 0;
-            bool same = true;
-            for (int32_t g = 0; g < p.n_groups; ++g) {
-                const DwGroupDev &d = p.g[g];
-                n_ot += wave_tiles(d) ? (d.C + kBNw - 1) / kBNw : int64_t(d.n_mblk) * ((d.C + kBNn - 1) / kBNn);
-                same = same && (d.T + kRound * kBKn - 1) / (kRound * kBKn) ==
-                                   (p.g[0].T + kRound * kBKn - 1) / (kRound * kBKn);
-            }
-            if (same && n_ot <= cus && 2 * n_ot >= int64_t(cus)) {
-                lay(true);
-                P = otiles;
-            }
-        }
         int64_t rt = p.g[0].chunks / kRound;
         for (int32_t g = 1; g < p.n_groups; ++g)
             if (p.g[g].chunks / kRound != rt) rt = 0;

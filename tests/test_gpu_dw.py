@@ -216,6 +216,59 @@ def test_dw_narrow_wave_per_tile_beside_narrow_exact(gpu_lib, layout):
     _check([g1, g2], exact=True, layout=layout)
 
 
+def _tile_rows(tiles, seed, drop=(1, 3)):
+    """Rows of the given 32-row tiles, all but a row or two of some, so that
+    both layouts see exactly those tiles."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i, t in enumerate(tiles):
+        keep = 32 - drop[i % len(drop)] if i % 2 else 32
+        rows += list(32 * t + np.sort(rng.choice(32, keep, replace=False)))
+    return rows
+
+
+@LAYOUTS
+def test_dw_narrow_wave_per_tile_128_columns(gpu_lib, layout):
+    # 8 packed tiles over 19240 columns: one wave per tile over 64 columns
+    # would need 301 workgroups, so the group takes 128-column tiles (151,
+    # the last one ragged) with one wave per packed tile over all 128 tokens
+    # of a chunk; ragged token axis, odd workgroups start halfway
+    T, R, C = 700, 256, 150 * 128 + 40
+    X = synth.normal_bf16((T, C), 1.0, 1661)
+    dY = synth.normal_bf16((T, R), 0.01, 1662)
+    _check([(X, [(dY, _mask_rows(R, _tile_rows(range(8), 1663)))])], repeat=2, layout=layout)
+
+
+@LAYOUTS
+def test_dw_narrow_three_shapes_exact(gpu_lib, layout):
+    # one narrow launch with all three whole-tile shapes, on small integers
+    # (exact products): 14 packed tiles over two matrices (two M-blocks of 7,
+    # 128-column tiles, one wave per packed tile: 64 workgroups), 8 tiles
+    # (one M-block of 64-column tiles: 64) and 3 tiles over 11008 columns
+    # (two waves per packed tile: 86)
+    T = 600
+    ga = (synth.integer_bf16((T, 4096), -3, 3, 1671),
+          [(synth.integer_bf16((T, 320), -3, 3, 1672), _mask_rows(320, _tile_rows([0, 2, 3, 5, 6, 8, 9], 1673))),
+           (synth.integer_bf16((T, 256), -3, 3, 1674), _mask_rows(256, _tile_rows([0, 1, 2, 4, 5, 6, 7], 1675)))])
+    gb = (synth.integer_bf16((T, 4096), -3, 3, 1676),
+          [(synth.integer_bf16((T, 256), -3, 3, 1677), _mask_rows(256, _tile_rows(range(8), 1678)))])
+    gc = (synth.integer_bf16((T, 11008), -3, 3, 1679),
+          [(synth.integer_bf16((T, 128), -3, 3, 1680), _mask_rows(128, _tile_rows([0, 1, 3], 1681)))])
+    _check([ga, gb, gc], exact=True, layout=layout)
+
+
+@LAYOUTS
+def test_dw_narrow_two_rounds(gpu_lib, layout):
+    # 9 packed tiles (3 M-blocks of 4 would take team slices) over 23040
+    # columns: two M-blocks of 128-column tiles, one wave per packed tile,
+    # 360 whole tiles, so two rounds of workgroups (more tiles than CUs);
+    # ragged token axis
+    T, R, C = 200, 320, 180 * 128
+    X = synth.normal_bf16((T, C), 1.0, 1691)
+    dY = synth.normal_bf16((T, R), 0.01, 1692)
+    _check([(X, [(dY, _mask_rows(R, _tile_rows([0, 1, 2, 4, 5, 6, 7, 8, 9], 1693)))])], repeat=2, layout=layout)
+
+
 @LAYOUTS
 def test_dw_one_tile_per_workgroup(gpu_lib, layout):
     # 200 output tiles of one round: every workgroup computes one whole tile
@@ -361,12 +414,13 @@ def test_dw_many_mblocks_column_major_tiles(gpu_lib, layout):
 
 @LAYOUTS
 def test_dw_team_slices_cut_tiles(gpu_lib, layout):
-    # a group of three or more M-blocks puts the launch on team slicing: a
-    # 5-M-block and a 2-M-block group (packed; more in the tile layout), 8
-    # column blocks each, 4096 tokens (16 rounds a tile), share the CUs in
-    # teams of 3-4 rounds, so most tiles are cut at ragged rounds into up to
-    # five partial sums added by the fix-up; repeated for determinism
-    T, C = 4096, 2000
+    # a group of three or more M-blocks puts the launch on team slicing (too
+    # few columns for whole narrow tiles): a 5-M-block and a 2-M-block group
+    # (packed; more in the tile layout), 6 column blocks each, 4096 tokens
+    # (16 rounds a tile), share the CUs in teams of 3-4 rounds, so most tiles
+    # are cut at ragged rounds into up to five partial sums added by the
+    # fix-up; repeated for determinism
+    T, C = 4096, 1496
     X1 = synth.normal_bf16((T, C), 1.0, 2100)
     mats1 = [(synth.normal_bf16((T, R), 0.01, 2101 + i), _mask_rows(R, synth.clustered_rows(R, k, 2110 + i)))
              for i, (R, k) in enumerate([(900, 330), (600, 200)])]

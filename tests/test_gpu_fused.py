@@ -110,6 +110,14 @@ def test_fused_narrow_whole_tiles(gpu_lib, layout):
     _check_equal(case, layout)
 
 
+def test_fused_narrow_wave_per_tile(gpu_lib):
+    # a group of 7 packed tiles (one M-block of 64-column tiles, one wave per
+    # packed tile) beside a 2-tile group of 128-column tiles, one narrow
+    # launch: the update reads dW_act
+    case = _case([(1000, 4096, [(512, 110), (512, 110)]), (600, 8192, [(256, 40)])], 2370)
+    _check_equal(case, _lib.SFT_DW_PACKED)
+
+
 def test_fused_falls_back_beyond_one_launch(gpu_lib):
     # ten groups need two product launches: the call runs the two calls
     case = _case([(128, 64 + 8 * i, [(40 + 13 * i, 5 + i)]) for i in range(10)], 2400)
@@ -164,9 +172,10 @@ def test_fused_many_mblocks(gpu_lib, layout):
 @LAYOUTS
 def test_fused_team_slices_cut_tiles(gpu_lib, layout):
     # team slicing with tiles cut at ragged rounds (5- and 2-M-block groups,
-    # 16 rounds a tile, teams of 3-4 rounds): the update adds each cut tile's
-    # partial rows, one slice per team, in the fix-up's order
-    case = _case([(4096, 2000, [(900, 330), (600, 200)]), (4096, 2000, [(512, 200)])], 2800)
+    # too few columns for whole narrow tiles, 16 rounds a tile, teams of 3-4
+    # rounds): the update adds each cut tile's partial rows, one slice per
+    # team, in the fix-up's order
+    case = _case([(4096, 1496, [(900, 330), (600, 200)]), (4096, 1496, [(512, 200)])], 2800)
     _check_equal(case, layout)
 
 
