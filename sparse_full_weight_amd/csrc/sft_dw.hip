@@ -31,9 +31,9 @@
 //      (output tile, chunk) iteration space; or, where the tiles line up with
 //      the CUs, tile-aligned slices, team slices (groups of three or more
 //      M-blocks), or narrow whole tiles (128 columns x 128-token chunks, one
-//      tile per workgroup, no partial sums at all; a group of 5 to 8 packed
-//      tiles there takes 64-column tiles with one wave per packed tile, all
-//      its tiles in one M-block).
+//      tile per workgroup, no partial sums at all; a group of more than 4
+//      packed tiles there takes M-blocks of up to 8 with one wave per packed
+//      tile, over 64 or 128 columns).
 //   3. Fix-up.  Output tiles cut by slice boundaries leave partial sums in
 //      scratch; this kernel adds them in slice order (deterministic; the
 //      kernel boundary orders the stores, so no device-scope fence is needed
@@ -62,10 +62,10 @@ constexpr int kBK = 64;              // tokens per chunk: 4 MFMA k-steps of 16
 // 128 columns, chunks of 128 tokens (the same 32 KB of X a chunk).
 constexpr int kBNn = 128, kBKn = 128;
 static_assert(kBK * kBN == kBKn * kBNn, "one X stage size for both tile shapes");
-// Narrow tiles of one wave per packed tile (a group of 5 to 8 packed tiles in
-// a narrow launch): 64 columns, the same 128-token chunks (16 KB of X a
-// chunk), all of the group's packed tiles in one M-block, so its X is read
-// once.
+// Narrow tiles of one wave per packed tile (a group of more than 4 packed
+// tiles in a narrow launch): M-blocks of up to 8 packed tiles, the same
+// 128-token chunks, over 64 columns (16 KB of X a chunk; as many workgroups as
+// two 4-tile M-blocks of 128 columns, and the X read once) or 128.
 constexpr int kBNw = 64, kMaxTilesW = 8;
 constexpr int kRound = 4;            // chunks per pipeline round (segments are whole rounds)
 constexpr int kThreads = 512;        // 8 waves
@@ -372,10 +372,10 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 // one tile), so that the launch reads two token ranges at a time.
 //
 // kWt (narrow launches only, chosen per workgroup by its group's wt flag):
-// output tile = (M-block of up to 8 packed tiles, 64 columns), a chunk is 128
-// tokens; wave w takes packed tile w over the whole chunk (all 128 tokens,
-// both 32-column blocks) and stores its 32 x 64 sums straight into dW_act.
-// Against two M-blocks of 128-column tiles this reads the group's X once.
+// output tile = (M-block of up to 8 packed tiles, 64 columns for kWt 1 or 128
+// for kWt 2), a chunk is 128 tokens; wave w takes packed tile w over the
+// whole chunk (all 128 tokens, every 32-column block of the tile) and stores
+// its 32-row sums straight into dW_act.
 __shared__ int32_t codes[kMaxSegs][kMaxTiles * 32];
 __shared__ DwGroupDev gs[kMaxGroups];   // the group table, indexable at run time
 __shared__ float *outp[kMaxMats];
@@ -795,10 +795,10 @@ __device__ __forceinline__ void masked_dw_body(const DwParams &p, const int64_t 
       }
     };
 
-    // One wave per tile: wave w holds packed tile w's 32 x 64 sums over the
+    // One wave per tile: wave w holds packed tile w's 32 x BN sums over the
     // whole token axis; each lane stores 4 consecutive columns of its row at
-    // a time (a row's 64 columns in 8 stores of lane pairs) straight into
-    // dW_act.  No wave adds another's sums.
+    // a time (a lane pair covers 8 columns a store) straight into dW_act.  No
+    // wave adds another's sums.
     auto epilogue_wt = [&](int sg) __attribute__((always_inline)) {
       if constexpr (kWt) {
         const Seg &S = segs[sg];
