@@ -32,6 +32,12 @@ page's equations are lost; the readings taken here are:
      input: the page's elliptic-curve walk is not specified), a_own = 1 and
      a_cross = b mu w- (1 - e) / (M w+ e + mu w- (1 - e)), M : mu = 1.833 : 1;
   7. all arithmetic in double precision.
+
+Parity unpinned: the page prints none of these formulas' values, so readings
+1-6 are checked only by their invariants (closed forms of the trend, the
+ladder's moves, the turn's sweep of the blend from 0 to b, the bounds of the
+weights) and by section 2.8's statement that the 1.833 : 1 weighting keeps
+descent dominant, not by a printed number.
 """
 from __future__ import annotations
 
