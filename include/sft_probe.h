@@ -9,6 +9,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sft.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -32,6 +34,22 @@ int sft_probe_grid(void);
 int sft_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 int sft_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 int sft_probe_mfma(int64_t iters, float *out, void *stream);
+
+/*
+ * How sft_masked_dw would launch these groups (host only: nothing runs on the
+ * device and no device pointer is read; the groups' pointers need only be
+ * non-null where sft_masked_dw requires them).  cus: the compute units to
+ * plan for (0: this device's count).  Writes, for each product launch in
+ * order, its kind (0 stream-K slices, 1 slices aligned to the output tiles,
+ * 2 team slices, 3 narrow whole tiles), its workgroups with work, its group
+ * count, then per group the narrow tile shape (0 two waves per packed tile,
+ * 1 one wave per packed tile over 64 columns, 2 over 128 columns; 0 outside
+ * narrow launches), its M-blocks and its column blocks; at most `cap` values
+ * go to out.  Returns the number of values (more than cap if out was too
+ * short), or an error code (< 0): SFT_EINVAL (bad groups or arguments),
+ * SFT_ENOTSUP (a launch beyond 2^31 iterations).
+ */
+int sft_probe_dw_plan(const sft_dw_group *groups, int32_t n_groups, int32_t cus, int32_t *out, int32_t cap);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ EXPORTS = (
     "sft_masked_writeback_many",
     "sft_rewind_init", "sft_rewind_observe", "sft_rows_save", "sft_rows_restore",
     "sft_leaf_grad_workspace", "sft_leaf_grad", "sft_leaf_adam", "sft_helix_init", "sft_helix_step",
-    "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma",
+    "sft_helix_coupling", "sft_probe_grid", "sft_probe_read", "sft_probe_copy", "sft_probe_mfma", "sft_probe_dw_plan",
     "sft_noalloc_scratch_bytes", "sft_masked_dw_update_noalloc", "sft_plan_layer_words", "sft_plan_layer",
     "sft_plan_upload",
 )
@@ -181,6 +181,7 @@ def lib() -> C.CDLL:
         L.sft_probe_read.argtypes = [p, C.c_size_t, p, p]
         L.sft_probe_copy.argtypes = [p, p, C.c_size_t, p]
         L.sft_probe_mfma.argtypes = [i64, p, p]
+        L.sft_probe_dw_plan.argtypes = [C.POINTER(CDwGroup), i32, i32, p, i32]
         L.sft_helix_init.argtypes = [C.POINTER(CHelix)]
         L.sft_helix_step.argtypes = [C.POINTER(CHelix), C.c_double, i32, C.POINTER(C.c_int32),
                                      C.POINTER(C.c_double)]
@@ -953,3 +954,38 @@ def prepare_probe_copy(src, dst) -> Prepared:
 
 def prepare_probe_mfma(iters: int, out) -> Prepared:
     return Prepared(lib().sft_probe_mfma, (int(iters), _dev(out)), (out,))
+
+
+DW_LAUNCH_KINDS = {0: "stream-k", 1: "aligned", 2: "teams", 3: "narrow"}
+
+
+def sft_probe_dw_plan(groups, cus: int = 0) -> list:
+    """How sft_masked_dw would launch groups of host row plans (no device
+    work): groups = [(T, C, layout, [Plan, ...]), ...] with each matrix's
+    Plan from sft_plan_rows.  Returns one dict per product launch: kind,
+    workgroups, and per group (shape, M-blocks, column blocks)."""
+    dummy = np.zeros(8, np.float32)          # stands in for X, dY and dW_act: never read
+    if dummy.ctypes.data % 16:
+        dummy = np.zeros(12, np.float32)[2:10]
+    ptr = dummy.ctypes.data
+    keep, arr = [], (CDwGroup * max(len(groups), 1))()
+    for i, (T, Cc, layout, plans) in enumerate(groups):
+        mats = (CDwMat * max(len(plans), 1))()
+        for j, pl in enumerate(plans):
+            mats[j] = CDwMat(ptr, pl.rows, _np_ptr(pl.active_rows), _np_ptr(pl.active_tiles),
+                             _np_ptr(pl.active_bits), _np_ptr(pl.tile_first), pl.n_active, pl.n_active_tiles, ptr)
+        keep.append(mats)
+        arr[i] = CDwGroup(ptr, T, Cc, len(plans), layout, mats)
+    out = np.zeros(1024, np.int32)
+    n = lib().sft_probe_dw_plan(arr, len(groups), cus, _np_ptr(out), out.size)
+    if n < 0:
+        raise SftError(n, lib().sft_last_error().decode())
+    assert n <= out.size, "plan description longer than its buffer"
+    v, i, res = out[:n].tolist(), 0, []
+    while i < n:
+        kind, wg, ng = v[i:i + 3]
+        i += 3
+        res.append({"kind": DW_LAUNCH_KINDS[kind], "workgroups": wg,
+                    "groups": [tuple(v[i + 3 * g:i + 3 * g + 3]) for g in range(ng)]})
+        i += 3 * ng
+    return res

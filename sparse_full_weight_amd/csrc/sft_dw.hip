@@ -1186,9 +1186,8 @@ bool narrow_shapes(const DwParams &p, int cus, int32_t *wt) {
     return same && ((n <= cus && 2 * n >= int64_t(cus)) || (many && n <= 2 * cus && 10 * n >= 14 * int64_t(cus)));
 }
 
-Plan make_plan(const sft_dw_group *groups, int32_t n_groups) {
+Plan make_plan(const sft_dw_group *groups, int32_t n_groups, int cus = sft::num_cus()) {
     Plan plan;
-    const int cus = sft::num_cus();
     int32_t gi = 0;
     while (gi < n_groups) {
         Launch L;
@@ -1504,6 +1503,31 @@ size_t sft_masked_dw_workspace(const sft_dw_group *groups, int32_t n_groups) {
         return static_cast<size_t>(-1);
     }
     return plan.ws_bytes();
+}
+
+int sft_probe_dw_plan(const sft_dw_group *groups, int32_t n_groups, int32_t cus, int32_t *out, int32_t cap) {
+    sft::clear_error();
+    SFT_CHECK(cus >= 0 && cap >= 0 && (cap == 0 || out), SFT_EINVAL, "sft_probe_dw_plan: bad arguments");
+    if (int rc = validate(groups, n_groups)) return rc;
+    const Plan plan = cus ? make_plan(groups, n_groups, cus) : make_plan(groups, n_groups);
+    SFT_CHECK(!plan.too_big, SFT_ENOTSUP, "sft_probe_dw_plan: a launch beyond 2^31 (tile, chunk) iterations");
+    int32_t n = 0;
+    auto put = [&](int64_t x) {
+        if (n < cap) out[n] = static_cast<int32_t>(x);
+        ++n;
+    };
+    for (const Launch &L : plan.launches) {
+        const DwParams &p = L.p;
+        put(p.narrow ? 3 : p.teams ? 2 : p.xcd_blocked ? 0 : 1);
+        put(p.n_wg);
+        put(p.n_groups);
+        for (int32_t g = 0; g < p.n_groups; ++g) {
+            put(p.g[g].wt);
+            put(p.g[g].n_mblk);
+            put(p.g[g].n_nblk);
+        }
+    }
+    return n;
 }
 
 int sft_masked_dw(const sft_dw_group *groups, int32_t n_groups, void *ws, size_t ws_bytes, void *stream) {
