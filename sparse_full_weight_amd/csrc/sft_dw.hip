@@ -502,10 +502,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_masked_dw(const DwParams p) {
     const int nseg = s_nseg;
     if (nseg == 0) return;   // an idle slice (team slicing pads the grid to whole XCDs)
     if constexpr (kNarrow) {
+        // kNarrow 2: the launch has 128-column one-wave tiles, whose body
+        // needs more registers than the others (252 against 204 VGPRs), so
+        // it is compiled into this instantiation only
         const int32_t wt = __builtin_amdgcn_readfirstlane(gs[segs[0].g].wt);
-        if (wt == 1) masked_dw_body<kKeep, 1, 1>(p, v, nseg);
-        else if (wt == 2) masked_dw_body<kKeep, 1, 2>(p, v, nseg);
-        else masked_dw_body<kKeep, 1, 0>(p, v, nseg);
+        if (wt == 1) {
+            masked_dw_body<kKeep, 1, 1>(p, v, nseg);
+        } else if constexpr (kNarrow == 2) {
+            if (wt == 2) masked_dw_body<kKeep, 1, 2>(p, v, nseg);
+            else masked_dw_body<kKeep, 1, 0>(p, v, nseg);
+        } else {
+            masked_dw_body<kKeep, 1, 0>(p, v, nseg);
+        }
     } else {
         masked_dw_body<kKeep, 0, 0>(p, v, nseg);
     }
@@ -1387,7 +1395,13 @@ void launch_product(const DwParams &p, hipStream_t st) {
         all = all && p.g[g].keep_x;
     }
     const dim3 grid(static_cast<uint32_t>(p.n_wg)), block(kThreads);
-    if (p.narrow) {
+    bool wide_wt = false;
+    for (int32_t g = 0; g < p.n_groups; ++g) wide_wt = wide_wt || p.g[g].wt == 2;
+    if (p.narrow && wide_wt) {
+        if (!any) hipLaunchKernelGGL((k_masked_dw<0, 2>), grid, block, 0, st, p);
+        else if (all) hipLaunchKernelGGL((k_masked_dw<1, 2>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((k_masked_dw<2, 2>), grid, block, 0, st, p);
+    } else if (p.narrow) {
         if (!any) hipLaunchKernelGGL((k_masked_dw<0, 1>), grid, block, 0, st, p);
         else if (all) hipLaunchKernelGGL((k_masked_dw<1, 1>), grid, block, 0, st, p);
         else hipLaunchKernelGGL((k_masked_dw<2, 1>), grid, block, 0, st, p);
