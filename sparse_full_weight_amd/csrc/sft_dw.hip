@@ -369,7 +369,8 @@ __device__ __forceinline__ short4v lds_tr16(const uint16_t *p) {
 // columns, so each loads only its own half of the operand; at the end they
 // add their sums through LDS and store the tile straight into dW_act.  Odd
 // workgroups start halfway along the token axis and wrap (two segments of the
-// one tile), so that the launch reads two token ranges at a time.
+// one tile), so that the launch reads two token ranges at a time.  kNarrow 2
+// is the same with the 128-column one-wave body compiled in (kWt below).
 //
 // kWt (narrow launches only, chosen per workgroup by its group's wt flag):
 // output tile = (M-block of up to 8 packed tiles, 64 columns for kWt 1 or 128
