@@ -270,6 +270,21 @@ def test_dw_narrow_two_rounds(gpu_lib, layout):
 
 
 @LAYOUTS
+def test_dw_narrow_one_wave_two_mblocks_64_columns(gpu_lib, layout):
+    # 10 packed tiles over 8192 columns: two M-blocks of 5 with one wave per
+    # packed tile over 64 columns (256 whole tiles, every CU), ragged tokens;
+    # the planner's choice is checked first so the case keeps its shape
+    T, R, C = 300, 320, 8192
+    rows = _tile_rows(range(10), 1695)
+    plan = _lib.sft_plan_rows(_mask_rows(R, rows))
+    got = _lib.sft_probe_dw_plan([(T, C, layout, [plan])], 256)
+    assert got == [{"kind": "narrow", "workgroups": 256, "groups": [(1, 2, 128)]}]
+    X = synth.normal_bf16((T, C), 1.0, 1696)
+    dY = synth.normal_bf16((T, R), 0.01, 1697)
+    _check([(X, [(dY, _mask_rows(R, rows))])], repeat=2, layout=layout)
+
+
+@LAYOUTS
 def test_dw_one_tile_per_workgroup(gpu_lib, layout):
     # 200 output tiles of one round: every workgroup computes one whole tile
     # (no partial sums at all)
