@@ -65,6 +65,21 @@ def test_noalloc_call_equals_the_workspace_call_twice_in_a_row(gpu_lib):
             assert_state_equal(a, b, f"{what}, matrix {i}")
 
 
+def test_noalloc_call_on_narrow_whole_tiles(gpu_lib):
+    # narrow whole tiles (no partial rows): 7 packed tiles over 8192 columns
+    # take one wave per packed tile over 64 columns (128 tiles), then a
+    # smaller call on 4 packed tiles over 8192 columns (stream-K slices)
+    narrow = _case(600, [(512, 8192), (512, 8192)], 110 / 512, 9300)
+    small = _case(300, [(256, 8192)], 0.45, 9400)
+    shape = [(600, 8192, _lib.SFT_DW_PACKED, [p for _, p, _, _ in narrow[1]])]
+    assert _lib.sft_probe_dw_plan(shape, 256)[0]["kind"] == "narrow"
+    for what, case in (("first (narrow) call", narrow), ("second (smaller) call", small)):
+        want = _run(case, noalloc=False)
+        got = _run(case, noalloc=True)
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert_state_equal(a, b, f"{what}, matrix {i}")
+
+
 def test_noalloc_call_rejects_groups_beyond_the_scratch_array(gpu_lib):
     T, R, C = 1 << 18, 2048, 8
     X = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
